@@ -1,0 +1,320 @@
+"""Pins of the CPU oracle against closed forms, invariants, brute force and
+finite differences.  Each test would fail under a plausible slip in the oracle
+(a dropped term, a wrong sign or index, a transposed operand)."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import gpt, optim, decode
+from oracle.configs import ORACLE_CONFIGS
+
+TINY = gpt.Spec(n_layer=2, d_model=16, n_head=2, d_ff=24, vocab=11, n_pos=9,
+                mlp_gated=False, tied_head=False, has_bias=True, batch=2, seq=7,
+                lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
+                lr_schedule="constant", total_steps=10)
+TINY_ROPE = TINY.replace(n_pos=0, mlp_gated=True, tied_head=True, has_bias=False)
+
+
+def rand_params(s, seed=0, scale=0.3):
+    """Random (non-init-like) parameters so that every term of the gradient is non-trivial."""
+    g = np.random.default_rng(seed)
+    out = {}
+    for name, shape, kind in gpt.param_layout(s):
+        a = g.standard_normal(shape) * scale
+        if kind == "ones":
+            a = 1.0 + a
+        out[name] = a
+    return out
+
+
+def rand_tokens(s, seed=1):
+    return np.random.default_rng(seed).integers(0, s.vocab, size=(s.batch, s.seq + 1))
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+def test_layernorm_closed_form():
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    y, (xhat, rstd) = gpt.layer_norm(x, np.ones(4), np.zeros(4))
+    # mean 2.5, biased variance 1.25
+    expect = (x - 2.5) / math.sqrt(1.25 + 1e-5)
+    np.testing.assert_allclose(y, expect, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(rstd[0, 0], 1 / math.sqrt(1.25 + 1e-5), rtol=1e-15)
+    # gain/bias act elementwise
+    g, b = np.array([1.0, -2.0, 0.5, 3.0]), np.array([0.1, 0.2, 0.3, 0.4])
+    y2, _ = gpt.layer_norm(x, g, b)
+    np.testing.assert_allclose(y2, expect * g + b, atol=1e-15)
+
+
+def test_layernorm_invariants_and_backward_orthogonality():
+    rng = np.random.default_rng(3)
+    d = 37
+    x = rng.standard_normal((5, d)) * 3 + 1
+    y, cache = gpt.layer_norm(x, np.ones(d), np.zeros(d))
+    xhat, rstd = cache
+    var = x.var(axis=-1)
+    np.testing.assert_allclose(xhat.sum(-1), 0, atol=1e-12)
+    np.testing.assert_allclose((xhat ** 2).sum(-1), d * var / (var + 1e-5), rtol=1e-12)
+    g = rng.standard_normal(d)
+    dy = rng.standard_normal((5, d))
+    dx, _, _ = gpt.layer_norm_backward(dy, cache, g)
+    # the input gradient is orthogonal to 1 (shift invariance); against xhat it leaves
+    # only the eps term: dx.xhat = rstd * (gy.xhat) * eps / (var + eps)
+    np.testing.assert_allclose(dx.sum(-1), 0, atol=1e-10)
+    gy_xhat = (g * dy * xhat).sum(-1)
+    np.testing.assert_allclose((dx * xhat).sum(-1),
+                               rstd[:, 0] * gy_xhat * 1e-5 / (var + 1e-5), rtol=1e-6, atol=1e-13)
+
+
+# ---------------------------------------------------------------- GELU
+
+def test_gelu_values():
+    assert gpt.gelu(np.array(0.0)) == 0.0
+    assert gpt.gelu_grad(np.array(0.0)) == 0.5
+    # GELU(1) = Phi(1) = 0.8413447460685429 (standard normal CDF table value)
+    assert abs(gpt.gelu(np.array(1.0)) - 0.8413447460685429) < 1e-15
+    # GELU(-x) = GELU(x) - x
+    x = np.linspace(-4, 4, 17)
+    np.testing.assert_allclose(gpt.gelu(-x), gpt.gelu(x) - x, atol=1e-14)
+    # derivative by central differences
+    h = 1e-6
+    np.testing.assert_allclose(gpt.gelu_grad(x), (gpt.gelu(x + h) - gpt.gelu(x - h)) / (2 * h), atol=1e-8)
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_properties():
+    rng = np.random.default_rng(4)
+    T, dh = 12, 8
+    cos, sin = gpt.rope_tables(T, dh)
+    q = rng.standard_normal((T, dh))
+    k = rng.standard_normal((T, dh))
+    rq, rk = gpt.rope(q, cos, sin), gpt.rope(k, cos, sin)
+    # position 0 is the identity
+    np.testing.assert_allclose(rq[0], q[0], atol=1e-15)
+    # norm preserving
+    np.testing.assert_allclose(np.linalg.norm(rq, axis=-1), np.linalg.norm(q, axis=-1), rtol=1e-13)
+    # inverse after forward is the identity
+    np.testing.assert_allclose(gpt.rope_inverse(rq, cos, sin), q, atol=1e-14)
+    # <R_t a, R_s b> depends only on t - s: shift both positions by 3
+    a, b = q[0], k[0]
+    A = gpt.rope(np.tile(a, (T, 1)), cos, sin)
+    Bm = gpt.rope(np.tile(b, (T, 1)), cos, sin)
+    np.testing.assert_allclose(A[5] @ Bm[2], A[8] @ Bm[5], rtol=1e-12)
+    np.testing.assert_allclose(A[7] @ Bm[7], a @ b, rtol=1e-12)
+    # the first pair rotates by exactly t radians (theta_0 = 1)
+    e = np.zeros(dh); e[0] = 1.0
+    E = gpt.rope(np.tile(e, (T, 1)), cos, sin)
+    np.testing.assert_allclose(E[3, 0], math.cos(3.0), atol=1e-15)
+    np.testing.assert_allclose(E[3, dh // 2], math.sin(3.0), atol=1e-15)
+
+
+# ---------------------------------------------------------------- attention
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(5)
+    T, dh = 9, 4
+    v = rng.standard_normal((T, dh))
+    # T = 1: the output is v itself
+    o, _ = gpt.causal_attention(rng.standard_normal((1, dh)), rng.standard_normal((1, dh)), v[:1])
+    np.testing.assert_allclose(o, v[:1], atol=1e-15)
+    # q = 0: uniform weights over the causal prefix -> running mean of v
+    o, p = gpt.causal_attention(np.zeros((T, dh)), rng.standard_normal((T, dh)), v)
+    running_mean = np.cumsum(v, axis=0) / np.arange(1, T + 1)[:, None]
+    np.testing.assert_allclose(o, running_mean, atol=1e-14)
+    assert np.all(np.triu(p, 1) == 0)
+
+
+def test_attention_backward_brute_force():
+    rng = np.random.default_rng(6)
+    T, dh = 5, 3
+    q, k, v, w = (rng.standard_normal((T, dh)) for _ in range(4))
+    f = lambda q, k, v: (gpt.causal_attention(q, k, v)[0] * w).sum()
+    o, p = gpt.causal_attention(q, k, v)
+    dq, dk, dv = gpt.causal_attention_backward(w, q, k, v, p)
+    h = 1e-6
+    for X, dX in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            args_p = [Xp if Y is X else Y for Y in (q, k, v)]
+            args_m = [Xm if Y is X else Y for Y in (q, k, v)]
+            num[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        np.testing.assert_allclose(dX, num, atol=1e-8)
+
+
+# ---------------------------------------------------------------- cross-entropy / loss
+
+@pytest.mark.parametrize("spec", [TINY, TINY_ROPE], ids=["learned-pos", "rope-gated-tied"])
+def test_zero_head_gives_ln_vocab(spec):
+    P = rand_params(spec)
+    if spec.tied_head:
+        # a zero head cannot be tied to a non-zero embedding: zero the final LN instead
+        P["lnf.g"] = np.zeros_like(P["lnf.g"])
+        P["lnf.b"] = np.zeros_like(P["lnf.b"])
+    else:
+        P["w_lm"] = np.zeros_like(P["w_lm"])
+    loss, cache = gpt.forward(spec, P, rand_tokens(spec))
+    assert loss == pytest.approx(math.log(spec.vocab), abs=1e-14)
+
+
+def test_dlogits_rows_sum_to_zero_and_dominant_row():
+    s = TINY
+    P = rand_params(s)
+    loss, cache = gpt.forward(s, P, rand_tokens(s))
+    dz = np.exp(cache["logp"])
+    dz[np.arange(dz.shape[0]), cache["tgt"]] -= 1
+    np.testing.assert_allclose(dz.sum(axis=1), 0, atol=1e-14)
+    # a logit row dominated by its target gives loss -> 0
+    z = np.full((1, 7), -50.0)
+    z[0, 3] = 50.0
+    logp, lse = gpt.log_softmax_rows(z)
+    assert -logp[0, 3] < 1e-40 + 1e-30
+
+
+def test_causal_invariant_logits():
+    s = TINY
+    P = rand_params(s)
+    seq = np.random.default_rng(7).integers(0, s.vocab, size=9)
+    z1 = gpt.sequence_logits(s, P, seq)
+    seq2 = seq.copy()
+    seq2[5:] = (seq2[5:] + 3) % s.vocab
+    z2 = gpt.sequence_logits(s, P, seq2)
+    assert np.array_equal(z1[:5], z2[:5])          # bit-identical before the change
+    assert not np.allclose(z1[5:], z2[5:])
+    s2 = TINY_ROPE
+    P2 = rand_params(s2)
+    a = gpt.sequence_logits(s2, P2, seq)
+    b = gpt.sequence_logits(s2, P2, seq2)
+    assert np.array_equal(a[:5], b[:5])
+
+
+# ---------------------------------------------------------------- full backward
+
+def _fd_check(spec, seed, n_coords=12, h_rel=1e-6):
+    P = rand_params(spec, seed)
+    tok = rand_tokens(spec, seed + 1)
+    loss, grads = gpt.loss_and_grads(spec, P, tok)
+    rng = np.random.default_rng(seed + 2)
+    worst = 0.0
+    for name, shape, _ in gpt.param_layout(spec):
+        flat = P[name].reshape(-1)
+        idxs = rng.choice(flat.size, size=min(n_coords, flat.size), replace=False)
+        for i in idxs:
+            h = h_rel * max(1.0, abs(flat[i]))
+            old = flat[i]
+            flat[i] = old + h
+            lp, _ = gpt.forward(spec, P, tok, keep=False)
+            flat[i] = old - h
+            lm, _ = gpt.forward(spec, P, tok, keep=False)
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            an = grads[name].reshape(-1)[i]
+            if abs(fd) < 1e-9 and abs(an) < 1e-9:
+                continue
+            rel = abs(fd - an) / max(abs(fd), abs(an), 1e-8)
+            worst = max(worst, rel)
+            assert rel < 1e-3, (name, int(i), fd, an)
+    return worst
+
+
+def test_backward_finite_differences_learned_positions():
+    assert _fd_check(TINY, 10) < 2e-4
+
+
+def test_backward_finite_differences_rope_gated_tied():
+    assert _fd_check(TINY_ROPE, 20) < 2e-4
+
+
+def test_backward_finite_differences_c1_shape():
+    # the tiny fp32 workload's own shapes, at its seeded N(0, 0.02) init scale
+    s = ORACLE_CONFIGS["c1"].replace(batch=1, seq=16)
+    P = rand_params(s, 30, scale=0.05)
+    for name, shape, kind in gpt.param_layout(s):
+        if kind == "ones":
+            P[name] = 1.0 + 0.05 * np.random.default_rng(1).standard_normal(shape)
+    tok = rand_tokens(s, 31)
+    loss, grads = gpt.loss_and_grads(s, P, tok)
+    rng = np.random.default_rng(32)
+    for name in ("wte", "wpe", "h0.w_qkv", "h1.b_fc", "h1.w_proj", "lnf.g", "w_lm", "h0.ln1.b"):
+        flat = P[name].reshape(-1)
+        for i in rng.choice(flat.size, size=4, replace=False):
+            h = 1e-6 * max(1.0, abs(flat[i]))
+            old = flat[i]
+            flat[i] = old + h
+            lp, _ = gpt.forward(s, P, tok, keep=False)
+            flat[i] = old - h
+            lm, _ = gpt.forward(s, P, tok, keep=False)
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            an = grads[name].reshape(-1)[i]
+            if abs(fd) < 1e-10 and abs(an) < 1e-10:
+                continue
+            assert abs(fd - an) / max(abs(fd), abs(an), 1e-8) < 1e-3, (name, i, fd, an)
+
+
+# ---------------------------------------------------------------- AdamW
+
+def test_adamw_scalar_closed_form():
+    # constant g and lr: m_hat = g, v_hat = g^2 at every t, so
+    # p_t = (1-a)^t p0 - c (1 - (1-a)^t) / a  with a = lr*wd, c = lr*g/(|g|+eps)
+    lr, wd, b1, b2, eps = 1e-2, 0.1, 0.9, 0.95, 1e-8
+    for g0 in (0.37, -2.5):
+        p, m, v = np.array([1.3]), np.zeros(1), np.zeros(1)
+        for t in range(1, 51):
+            optim.adamw_update(p, np.array([g0]), m, v, t, lr, b1, b2, eps, wd)
+            a = lr * wd
+            c = lr * g0 / (abs(g0) + eps)
+            expect = (1 - a) ** t * 1.3 - c * (1 - (1 - a) ** t) / a
+            assert p[0] == pytest.approx(expect, rel=1e-12, abs=1e-14)
+    # g = 0: pure geometric decay
+    p, m, v = np.array([2.0]), np.zeros(1), np.zeros(1)
+    for t in range(1, 11):
+        optim.adamw_update(p, np.zeros(1), m, v, t, lr, b1, b2, eps, wd)
+    assert p[0] == pytest.approx(2.0 * (1 - lr * wd) ** 10, rel=1e-14)
+
+
+def test_lr_schedule():
+    s = ORACLE_CONFIGS["c3"]
+    assert optim.lr_at(s, 0) == pytest.approx(6e-4, rel=1e-15)
+    assert optim.lr_at(s, 2000) == pytest.approx(3e-4, rel=1e-12)
+    assert optim.lr_at(s, 4000) == pytest.approx(0.0, abs=1e-18)
+    # a short run uses the long schedule: step 99 of 4000 is still near the peak
+    assert optim.lr_at(s, 99) == pytest.approx(6e-4 * 0.5 * (1 + math.cos(math.pi * 99 / 4000)))
+    assert optim.lr_at(ORACLE_CONFIGS["c1"], 7) == 1e-3
+
+
+# ---------------------------------------------------------------- decode oracle
+
+def test_teacher_forced_matches_greedy_recompute():
+    s = TINY.replace(n_pos=6)
+    P = rand_params(s, 40)
+    prompt = [1, 5, 2]
+    gen = decode.greedy(s, P, prompt, n_new=11, n_ctx=6, keep=3)
+    z = decode.teacher_forced_logits(s, P, prompt, gen, n_ctx=6, keep=3)
+    assert [decode.argmax_lowest(r) for r in z] == gen
+    # brute force: replay the window rule token by token with a full recompute
+    ctx = list(prompt)
+    for i, tok in enumerate(gen):
+        zz = gpt.sequence_logits(s, P, ctx)[-1]
+        np.testing.assert_allclose(z[i], zz, atol=1e-13)
+        ctx.append(tok)
+        if len(ctx) > 6:
+            ctx = ctx[-3:]
+
+
+def test_window_rule_segments():
+    segs = list(decode.windows([7, 8], [1, 2, 3, 4, 5], n_ctx=4, keep=2))
+    # ctx [7,8] -> predict 1 (row 1), ctx [7,8,1] -> 2 (row 2), ctx [7,8,1,2] -> 3 (row 3),
+    # append 3 overflows -> restart from [2,3]; predict 4 (row 1), [2,3,4] -> 5 (row 2)
+    assert segs[0] == ([7, 8, 1, 2], [(1, 0), (2, 1), (3, 2)])
+    assert segs[1] == ([2, 3, 4, 5], [(1, 3), (2, 4)])
+
+
+def test_argmax_tie_lowest_id():
+    assert decode.argmax_lowest(np.array([0.5, 2.0, 1.0, 2.0])) == 1
+    assert decode.top2_margin(np.array([0.5, 2.0, 1.0, 2.0])) == 0.0
