@@ -1,0 +1,208 @@
+/*
+ * ofa.h -- C ABI of libofa.so: one GPT training step (embedding, causal
+ * multi-head attention, MLP, LayerNorm, softmax cross-entropy forward and
+ * backward, fused AdamW) and batch-1 greedy decode that reads the live,
+ * changing weights, on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page title, section):
+ *  - "Open Flapping Airplanes ... A100 reproduction", "What ran": training runs
+ *    the forward pass, the backward pass and the weight update; serving is
+ *    autoregressive generation from the changing model; initial weights are
+ *    generated on the host ("Reproduce the run": PyTorch on the CPU only made
+ *    the initial weights).
+ *  - same page, "A longer run exposed a scheduler overflow": a 32-bit task
+ *    budget wrapped; counter widths must be consistent.  Every counter, ticket
+ *    and budget behind this ABI is 64-bit.
+ *  - "How one persistent kernel runs three jobs": one persistent kernel; work
+ *    is claimed through ticket counters; a finished phase fences its writes
+ *    and then increments a counter, and dependents acquire-read that counter;
+ *    forward releases backward and one token releases the next, with no host
+ *    launch in between; static partitions of the compute units.
+ *  - "Coppelius training on the RTX 3090", "Channel health": each invocation
+ *    reports an error notifier, a host status block and a finite loss.
+ *
+ * Memory ownership.  All device memory is the caller's.  The caller passes one
+ * device workspace of ofa_workspace_bytes() bytes to ofa_create(); the library
+ * carves it and never allocates or frees device memory for model state.  The
+ * handle owns only host-side state (the config, the phase tables, the error
+ * string and a small pinned staging area).  The caller frees the workspace
+ * after ofa_destroy().
+ *
+ * Synchronisation.  Every call enqueues work on the HIP stream given to
+ * ofa_create() and returns without waiting, except where stated.  Device
+ * results are valid once the caller has synchronised that stream.  The device
+ * status block is read back by ofa_status_sync(); a non-zero device status
+ * makes every later call return that status.
+ *
+ * Errors.  No call throws.  Each returns an ofa_status; on failure
+ * ofa_last_error(h) returns a message owned by the handle (valid until the
+ * next call on that handle).
+ *
+ * Thread safety: one handle must not be used by two host threads at once.
+ */
+#ifndef OFA_H
+#define OFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ofa_handle ofa_handle;   /* opaque, owned by the library */
+
+typedef enum {
+  OFA_OK = 0,
+  OFA_E_ARG = -1,        /* invalid argument or configuration */
+  OFA_E_HIP = -2,        /* a HIP runtime call failed (code kept in the handle) */
+  OFA_E_NONFINITE = -3,  /* a step produced a non-finite loss */
+  OFA_E_TIMEOUT = -4,    /* a device-side wait exceeded its watchdog deadline */
+  OFA_E_OVERFLOW = -5,   /* a requested budget does not fit its counters */
+  OFA_E_STATE = -6       /* call not valid in the handle's current state */
+} ofa_status;
+
+typedef enum { OFA_FP32 = 0, OFA_BF16 = 1 } ofa_precision;
+typedef enum { OFA_LR_CONSTANT = 0, OFA_LR_COSINE = 1 } ofa_lr_schedule;
+typedef enum { OFA_EXEC_PERSISTENT = 0, OFA_EXEC_LAUNCH_PER_PHASE = 1 } ofa_exec_mode;
+
+/* Model, optimizer and execution configuration (plain values, no pointers). */
+typedef struct {
+  int32_t n_layer, d_model, n_head, d_ff, vocab;
+  int32_t n_pos;          /* learned position-table length; 0 = rotary positions */
+  int32_t mlp_gated;      /* 1 = GELU(h Wg^T) * (h Wu^T); 0 = GELU(h W1^T + b1) */
+  int32_t tied_head;      /* 1 = logits use the token-embedding table */
+  int32_t has_bias;       /* 1 = every linear layer has a bias */
+  int32_t batch, seq;     /* one step trains on batch x seq positions */
+  int32_t precision;      /* ofa_precision */
+  float lr, beta1, beta2, eps, weight_decay;
+  int32_t lr_schedule;    /* ofa_lr_schedule; cosine decays to 0 at total_steps */
+  int32_t total_steps;
+  int32_t train_cus;      /* persistent mode: compute units given to training */
+  int32_t serve_cus;      /* compute units given to decode (0 = no serve role) */
+  int32_t decode_window;  /* positions held by the decode context (<= n_pos if n_pos) */
+  int32_t prompt_len;     /* tokens kept when the decode context restarts */
+  int32_t restart_every;  /* co-resident decode: restart from the prompt every N tokens */
+  int32_t exec_mode;      /* ofa_exec_mode */
+  uint64_t debug_counter_base;  /* start value of every ticket/phase counter (tests) */
+  int32_t debug_flags;          /* OFA_DEBUG_* bits (tests only) */
+  int32_t reserved[7];          /* must be zero */
+} ofa_config;
+
+#define OFA_DEBUG_SHUFFLE_TICKETS 1  /* persistent mode: permute tile order inside a phase */
+#define OFA_DEBUG_SHORT_WATCHDOG  2  /* device waits give up after ~1 ms instead of ~10 s */
+
+/* Size in bytes of the device workspace ofa_create() needs for cfg; 0 if cfg is
+ * invalid (ofa_validate_config() says why). */
+size_t ofa_workspace_bytes(const ofa_config *cfg);
+
+/* Checks cfg without touching the GPU.  On OFA_E_ARG, writes a message into
+ * msg (NUL-terminated, at most msg_len bytes) when msg is not NULL. */
+ofa_status ofa_validate_config(const ofa_config *cfg, char *msg, size_t msg_len);
+
+/* Number of parameters (fp32 scalars) of the model cfg describes. */
+int64_t ofa_param_count(const ofa_config *cfg);
+
+/* Canonical parameter layout: tensor i (0 <= i < ofa_param_tensor_count) starts
+ * at flat offset *offset, has *numel scalars and init kind *kind
+ * (0 = N(0, 0.02), 1 = zeros, 2 = ones).  name receives a NUL-terminated
+ * tensor name (at most name_len bytes). */
+int32_t ofa_param_tensor_count(const ofa_config *cfg);
+ofa_status ofa_param_tensor(const ofa_config *cfg, int32_t i, int64_t *offset, int64_t *numel,
+                            int32_t *kind, char *name, size_t name_len);
+
+/* Creates a handle.  dev_workspace: device pointer to ws_bytes >= the size
+ * ofa_workspace_bytes(cfg) returns, 256-byte aligned.  dev_init_params: device
+ * pointer to ofa_param_count(cfg) fp32 scalars in canonical order; they are
+ * copied (the caller may free them after the stream synchronises).
+ * hip_stream: the hipStream_t all work of this handle is ordered on (NULL =
+ * the default stream).  Enqueues initialisation work; *out receives the handle. */
+ofa_status ofa_create(const ofa_config *cfg, void *dev_workspace, size_t ws_bytes,
+                      const float *dev_init_params, void *hip_stream, ofa_handle **out);
+
+/* Runs n_steps >= 1 training steps.  dev_tokens: device int32
+ * [n_steps][batch][seq+1]; step s trains inputs tokens[s][:, :seq] on targets
+ * tokens[s][:, 1:].  dev_losses: device fp32 [n_steps], receives each step's
+ * mean cross-entropy.  Every token must lie in [0, vocab) (checked on the
+ * device; a bad token sets OFA_E_ARG in the status block and the step is
+ * skipped).  The learning rate of each step follows the step count kept in
+ * the handle.  Persistent mode runs all n_steps in one kernel launch. */
+ofa_status ofa_train_step(ofa_handle *h, const int32_t *dev_tokens, int32_t n_steps,
+                          float *dev_losses);
+
+/* Makes the current weights visible to decode as version v+1; *version_out
+ * (host pointer, may be NULL) receives v+1. */
+ofa_status ofa_publish_weights(ofa_handle *h, uint64_t *version_out);
+
+/* Batch-1 greedy decode with the latest published weights.
+ * dev_prompt: device int32 [n_prompt]; n_prompt > 0 starts a new context from
+ * this prompt (n_prompt <= decode_window); n_prompt == 0 continues the previous
+ * context.  Generates n_new tokens into dev_tokens_out (device int32 [n_new]).
+ * dev_logits_out (device fp32 [n_new][vocab], may be NULL) receives the logits
+ * each token was chosen from.  dev_versions_out (device uint64 [n_new], may be
+ * NULL) receives the weight version each token read.  When the context would
+ * exceed decode_window positions it restarts from its most recent prompt_len
+ * tokens at positions 0..prompt_len-1. */
+ofa_status ofa_decode_token(ofa_handle *h, const int32_t *dev_prompt, int32_t n_prompt,
+                            int32_t n_new, int32_t *dev_tokens_out, float *dev_logits_out,
+                            uint64_t *dev_versions_out);
+
+/* Co-resident mode (train_cus > 0 and serve_cus > 0): one persistent launch
+ * trains n_steps steps on the train partition while the serve partition decodes
+ * continuously, restarting from dev_prompt every restart_every tokens and
+ * acquiring the newest published version at every token.  Generated tokens go
+ * round-robin into dev_tokens_out[ring_len], their versions into
+ * dev_versions_out[ring_len] (may be NULL); *dev_n_generated (device uint64)
+ * receives the count.  Training publishes after every AdamW update. */
+ofa_status ofa_train_and_serve(ofa_handle *h, const int32_t *dev_tokens, int32_t n_steps,
+                               float *dev_losses, const int32_t *dev_prompt, int32_t n_prompt,
+                               int32_t *dev_tokens_out, uint64_t *dev_versions_out,
+                               int32_t ring_len, uint64_t *dev_n_generated);
+
+/* Copies the fp32 master weights to / from dev_params (device fp32
+ * [ofa_param_count]).  ofa_set_params also refreshes the compute copy. */
+ofa_status ofa_get_params(ofa_handle *h, float *dev_params);
+ofa_status ofa_set_params(ofa_handle *h, const float *dev_params);
+
+/* Copies the gradient of the most recent step (device fp32 [ofa_param_count]). */
+ofa_status ofa_get_grads(ofa_handle *h, float *dev_grads);
+
+/* Statistics of the last completed call, filled on the host after a stream
+ * synchronisation (this call synchronises the stream). */
+typedef struct {
+  int32_t status;           /* device status block: 0 or an ofa_status */
+  int32_t err_phase;        /* phase index that raised it, -1 if none */
+  int64_t err_step;         /* step that raised it */
+  int64_t err_info;         /* extra detail (offending value) */
+  uint64_t tickets_claimed; /* tickets handed out in the last persistent launch */
+  uint64_t steps_done;      /* training steps completed since create */
+  uint64_t version;         /* latest published weight version */
+  double last_call_ms;      /* device time of the last train/decode call (hip events) */
+  int32_t n_phases;         /* phases of one training step */
+  int32_t n_tiles_step;     /* tiles of one training step */
+  int32_t grid;             /* workgroups of the last persistent launch */
+  int32_t reserved[5];
+} ofa_stats;
+
+ofa_status ofa_status_sync(ofa_handle *h, ofa_stats *out);
+
+/* Per-phase device timestamps of the last training step run in launch-per-phase
+ * or persistent mode: for phase i, t[2i] = first tile start, t[2i+1] = last tile
+ * end, in device clock ticks (100 MHz).  n: capacity in pairs.  Synchronises. */
+ofa_status ofa_phase_times(ofa_handle *h, uint64_t *host_t, int32_t n, int32_t *n_out,
+                           char *names, size_t name_stride);
+
+/* 64-bit task budget = iterations x tasks_per_unit; OFA_E_OVERFLOW if the
+ * product does not fit 63 bits.  Host-only helper (the budget rule of the
+ * scheduler). */
+ofa_status ofa_task_budget(uint64_t iterations, uint64_t tasks_per_unit, uint64_t *out);
+
+const char *ofa_last_error(const ofa_handle *h);
+const char *ofa_status_string(ofa_status s);
+
+ofa_status ofa_destroy(ofa_handle *h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OFA_H */

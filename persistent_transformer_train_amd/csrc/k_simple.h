@@ -1,0 +1,660 @@
+// k_simple.h -- the training-step task functions in their plain form: each
+// one processes one tile with 256 threads.  These are the fp32 path and the
+// fallback-free reference-quality versions of the bandwidth-bound steps; the
+// dense contractions additionally have MFMA versions (k_mfma.h).
+//
+// What each step computes follows the kernel families of "Coppelius training
+// on the RTX 3090" ("Where a step's time goes"): gather, layernorm-forward,
+// layernorm-backward, layernorm-parameters, attention-forward, attention-key,
+// attention-query, qk-rope, inverse-rope-qkv, gated-gelu-forward/-backward,
+// cross-entropy(-backward), loss-target-gather, embedding-scatter, adamw.
+#pragma once
+#include "ofa_dev.h"
+
+namespace ofa {
+
+__device__ __forceinline__ int token_at(const StepCtx* sc, int b, int t, int T, int V,
+                                        const TaskCtx& tc) {
+  int tok = sc->tokens[(int64_t)b * (T + 1) + t];
+  if (tok < 0 || tok >= V) {
+    raise_status(tc.status, -1 /*OFA_E_ARG*/, tc.phase, tc.step, tok);
+    tok = 0;
+  }
+  return tok;
+}
+
+// ---------------------------------------------------------------- embedding gather
+
+__device__ void task_embed(const EmbedArgs& a, int tile, const TaskCtx& tc) {
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  const int BT = a.B * a.T;
+  const int r0 = tile * a.rows_per_tile;
+  const int r1 = min(r0 + a.rows_per_tile, BT);
+  for (int r = r0 + w; r < r1; r += kWaves) {
+    int b = r / a.T, t = r % a.T;
+    int tok = token_at(tc.sc, b, t, a.T, a.V, tc);
+    const float* e = a.wte + (int64_t)tok * a.d;
+    const float* p = a.wpe ? a.wpe + (int64_t)t * a.d : nullptr;
+    float* x = a.x + (int64_t)r * a.d;
+    for (int j = l; j < a.d; j += kWave) x[j] = e[j] + (p ? p[j] : 0.f);
+  }
+}
+
+// ---------------------------------------------------------------- LayerNorm
+
+constexpr int kMaxDPerLane = 16;   // d <= 1024
+
+__device__ void task_ln_fwd(const LnFwdArgs& a, int tile) {
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  const int r0 = tile * a.rows_per_tile;
+  const int r1 = min(r0 + a.rows_per_tile, a.rows);
+  const int nj = (a.d + kWave - 1) / kWave;
+  for (int r = r0 + w; r < r1; r += kWaves) {
+    const float* x = a.x + (int64_t)r * a.d;
+    float v[kMaxDPerLane];
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxDPerLane; ++c) {
+      int j = l + c * kWave;
+      v[c] = (c < nj && j < a.d) ? x[j] : 0.f;
+      s += v[c];
+    }
+    float mean = wave_sum(s) / a.d;
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxDPerLane; ++c) {
+      int j = l + c * kWave;
+      float dv = (c < nj && j < a.d) ? v[c] - mean : 0.f;
+      q += dv * dv;
+    }
+    float var = wave_sum(q) / a.d;
+    float rstd = 1.0f / sqrtf(var + 1e-5f);
+#pragma unroll
+    for (int c = 0; c < kMaxDPerLane; ++c) {
+      int j = l + c * kWave;
+      if (c < nj && j < a.d) stf(a.y, (int64_t)r * a.d + j, a.y_dt, (v[c] - mean) * rstd * a.g[j] + a.b[j]);
+    }
+    if (l == 0) {
+      a.mean[r] = mean;
+      a.rstd[r] = rstd;
+    }
+  }
+}
+
+// dx = rstd * (gy - mean(gy) - xhat * mean(gy*xhat)), gy = g*dy; dx_out = dx_in + dx.
+// Column partial sums of the tile (fixed order): dy*xhat, dy, dx_out.
+__device__ void task_ln_bwd(const LnBwdArgs& a, int tile, char* smem) {
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  const int r0 = tile * a.rows_per_tile;
+  const int r1 = min(r0 + a.rows_per_tile, a.rows);
+  const int nj = (a.d + kWave - 1) / kWave;
+  float pg[kMaxDPerLane], pb[kMaxDPerLane], px[kMaxDPerLane];
+#pragma unroll
+  for (int c = 0; c < kMaxDPerLane; ++c) pg[c] = pb[c] = px[c] = 0.f;
+  for (int r = r0 + w; r < r1; r += kWaves) {
+    const float* x = a.x + (int64_t)r * a.d;
+    const float* dy = a.dy + (int64_t)r * a.d;
+    const float mean = a.mean[r], rstd = a.rstd[r];
+    float xh[kMaxDPerLane], gy[kMaxDPerLane], dyv[kMaxDPerLane];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxDPerLane; ++c) {
+      int j = l + c * kWave;
+      bool ok = c < nj && j < a.d;
+      xh[c] = ok ? (x[j] - mean) * rstd : 0.f;
+      dyv[c] = ok ? dy[j] : 0.f;
+      gy[c] = ok ? dyv[c] * a.g[j] : 0.f;
+      s1 += gy[c];
+      s2 += gy[c] * xh[c];
+    }
+    const float m1 = wave_sum(s1) / a.d, m2 = wave_sum(s2) / a.d;
+#pragma unroll
+    for (int c = 0; c < kMaxDPerLane; ++c) {
+      int j = l + c * kWave;
+      if (c < nj && j < a.d) {
+        float dx = rstd * (gy[c] - m1 - xh[c] * m2);
+        int64_t idx = (int64_t)r * a.d + j;
+        float out = (a.dx_in ? a.dx_in[idx] : 0.f) + dx;
+        a.dx_out[idx] = out;
+        if (a.dx_lp) stf(a.dx_lp, idx, a.lp_dt, out);
+        pg[c] += dyv[c] * xh[c];
+        pb[c] += dyv[c];
+        px[c] += out;
+      }
+    }
+  }
+  // combine the four waves in a fixed order
+  float* red = (float*)smem;   // [kWaves][3][d]
+#pragma unroll
+  for (int c = 0; c < kMaxDPerLane; ++c) {
+    int j = l + c * kWave;
+    if (c < nj && j < a.d) {
+      red[(w * 3 + 0) * a.d + j] = pg[c];
+      red[(w * 3 + 1) * a.d + j] = pb[c];
+      red[(w * 3 + 2) * a.d + j] = px[c];
+    }
+  }
+  __syncthreads();
+  float* out = a.partials + (int64_t)tile * 3 * a.d;
+  for (int i = threadIdx.x; i < 3 * a.d; i += kThreads) {
+    float s = 0.f;
+    for (int ww = 0; ww < kWaves; ++ww) s += red[ww * 3 * a.d + i];
+    out[i] = s;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- column sums
+
+__device__ void task_colsum(const ColsumArgs& a, int tile) {
+  const int r0 = tile * a.rows_per_tile;
+  const int r1 = min(r0 + a.rows_per_tile, a.rows);
+  float* out = a.partials + (int64_t)tile * a.cols;
+  for (int c = threadIdx.x; c < a.cols; c += kThreads) {
+    float s = 0.f;
+    for (int r = r0; r < r1; ++r) s += ldf(a.src, (int64_t)r * a.ld + c, a.dt);
+    out[c] = s;
+  }
+}
+
+__device__ void task_colred(const ColredArgs& a, int tile) {
+  const int c0 = tile * a.cols_per_tile;
+  const int c1 = min(c0 + a.cols_per_tile, a.cols);
+  for (int c = c0 + (int)threadIdx.x; c < c1; c += kThreads) {
+    for (int k = 0; k < a.n_vec; ++k) {
+      float* o = a.out[k];
+      if (!o) continue;
+      float s = 0.f;
+      for (int p = 0; p < a.n_parts; ++p) s += a.partials[((int64_t)p * a.n_vec + k) * a.cols + c];
+      o[c] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- plain GEMM
+// 64x64 tile, BK = 16, each thread computes 4x4 outputs.  Operands of any
+// layout / dtype; accumulation in fp32.
+
+struct GemmSmemSimple {
+  float As[16][64 + 4];
+  float Bs[16][64 + 4];
+};
+
+__device__ __forceinline__ float gemm_a(const GemmArgs& g, int m, int k) {
+  if (m >= g.M || k >= g.K) return 0.f;
+  int64_t i = g.a_kmajor ? (int64_t)m * g.lda + k : (int64_t)k * g.lda + m;
+  return ldf(g.A, i, g.a_dt);
+}
+__device__ __forceinline__ float gemm_b(const GemmArgs& g, int k, int n) {
+  if (n >= g.N || k >= g.K) return 0.f;
+  int64_t i = g.b_kmajor ? (int64_t)n * g.ldb + k : (int64_t)k * g.ldb + n;
+  return ldf(g.B, i, g.b_dt);
+}
+
+__device__ __noinline__ void gemm_epilogue(const GemmArgs& g, int m, int n, float acc) {
+  if (m >= g.M || n >= g.N) return;
+  float v = acc + (g.bias ? g.bias[n] : 0.f);
+  int64_t ci = (int64_t)m * g.ldc + n;
+  switch (g.epi) {
+    case EPI_STORE:
+      stf(g.C, ci, g.c_dt, v);
+      break;
+    case EPI_RESID:
+      ((float*)g.C)[ci] = g.resid[(int64_t)m * g.ldres + n] + v;
+      break;
+    case EPI_GELU:
+      stf(g.C, ci, g.c_dt, v);
+      stf(g.aux, (int64_t)m * g.ldaux + n, g.aux_dt, gelu_f(v));
+      break;
+    case EPI_DGELU: {
+      float u = ldf(g.aux, (int64_t)m * g.ldaux + n, g.aux_dt);
+      stf(g.C, ci, g.c_dt, v * gelu_grad_f(u));
+    } break;
+    case EPI_DGEGLU: {
+      int64_t ai = (int64_t)m * g.ldaux + n;
+      float gt = ldf(g.aux, ai, g.aux_dt);
+      float up = ldf(g.aux, ai + g.aux_off, g.aux_dt);
+      stf(g.C, ci, g.c_dt, v * up * gelu_grad_f(gt));
+      stf(g.C, ci + g.aux_off, g.c_dt, v * gelu_f(gt));
+    } break;
+  }
+}
+
+__device__ void task_gemm_simple(const GemmArgs& g, int tile, char* smem) {
+  GemmSmemSimple& s = *(GemmSmemSimple*)smem;
+  const int tm = tile / g.tiles_n, tn = tile % g.tiles_n;
+  const int m0 = tm * 64, n0 = tn * 64;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = 0; k0 < g.K; k0 += 16) {
+    // each thread loads 4 elements of each operand
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int idx = threadIdx.x + e * kThreads;   // 0..1023
+      int kk, mm;
+      if (g.a_kmajor) { mm = idx / 16; kk = idx % 16; } else { kk = idx / 64; mm = idx % 64; }
+      s.As[kk][mm] = gemm_a(g, m0 + mm, k0 + kk);
+      int nn;
+      if (g.b_kmajor) { nn = idx / 16; kk = idx % 16; } else { kk = idx / 64; nn = idx % 64; }
+      s.Bs[kk][nn] = gemm_b(g, k0 + kk, n0 + nn);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = s.As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = s.Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gemm_epilogue(g, m0 + ty * 4 + i, n0 + tx * 4 + j, acc[i][j]);
+}
+
+// ---------------------------------------------------------------- RoPE (rotate-half)
+
+__device__ void task_rope(const RopeArgs& a, int tile, bool inverse) {
+  const int BT = a.B * a.T;
+  const int half = a.dh / 2;
+  const int r0 = tile * a.rows_per_tile;
+  const int r1 = min(r0 + a.rows_per_tile, BT);
+  const int per_row = 2 * a.H * half;   // q and k, every head, every pair
+  for (int idx = threadIdx.x; idx < (r1 - r0) * per_row; idx += kThreads) {
+    int r = r0 + idx / per_row;
+    int rem = idx % per_row;
+    int part = rem / (a.H * half);          // 0 = q, 1 = k
+    int h = (rem / half) % a.H;
+    int i = rem % half;
+    int t = r % a.T + a.pos0;
+    double theta = pow(10000.0, -2.0 * i / a.dh);
+    double ang = (double)t * theta;
+    float c = (float)cos(ang), sn = (float)sin(ang);
+    if (inverse) sn = -sn;
+    int64_t base = (int64_t)r * a.ld + part * a.d + h * a.dh;
+    float x1 = ldf(a.qkv, base + i, a.dt), x2 = ldf(a.qkv, base + i + half, a.dt);
+    stf(a.qkv, base + i, a.dt, x1 * c - x2 * sn);
+    stf(a.qkv, base + i + half, a.dt, x1 * sn + x2 * c);
+  }
+}
+
+// ---------------------------------------------------------------- gated GELU forward
+
+__device__ void task_geglu_fwd(const GegluArgs& a, int tile) {
+  const int r0 = tile * a.rows_per_tile;
+  const int r1 = min(r0 + a.rows_per_tile, a.rows);
+  for (int64_t idx = threadIdx.x; idx < (int64_t)(r1 - r0) * a.F; idx += kThreads) {
+    int r = r0 + (int)(idx / a.F), f = (int)(idx % a.F);
+    float g = ldf(a.gu, (int64_t)r * 2 * a.F + f, a.dt);
+    float up = ldf(a.gu, (int64_t)r * 2 * a.F + a.F + f, a.dt);
+    stf(a.a, (int64_t)r * a.F + f, a.dt, gelu_f(g) * up);
+  }
+}
+
+// ---------------------------------------------------------------- attention (plain)
+// One wavefront per query row (forward, dQ) or key row (dK, dV).  Rows of a
+// tile share one (b, h).  Scores live in LDS, 4 bytes per key.
+
+struct AttnIdx { int b, h, t; };
+
+__device__ __forceinline__ AttnIdx attn_row(const AttnArgs& a, int tile, int i) {
+  const int nblk = (a.T + a.block - 1) / a.block;
+  int bh = tile / nblk, blk = tile % nblk;
+  AttnIdx r;
+  r.b = bh / a.H;
+  r.h = bh % a.H;
+  r.t = blk * a.block + i;
+  return r;
+}
+
+__device__ void task_attn_fwd_simple(const AttnArgs& a, int tile, char* smem) {
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  float* qs = (float*)smem + w * (64 + a.T);   // q (64) then scores (T)
+  float* sc = qs + 64;
+  const float scale = 1.0f / sqrtf((float)a.dh);
+  const int64_t ld = 3 * (int64_t)a.d;
+  for (int i = w; i < a.block; i += kWaves) {
+    AttnIdx r = attn_row(a, tile, i);
+    if (r.t >= a.T) break;
+    const int64_t row_q = ((int64_t)r.b * a.T + r.t) * ld + r.h * a.dh;
+    if (l < a.dh) qs[l] = ldf(a.qkv, row_q + l, a.dt) * scale;
+    wave_sync();
+    float mx = -INFINITY;
+    for (int s0 = 0; s0 <= r.t; s0 += kWave) {
+      int s = s0 + l;
+      float v = -INFINITY;
+      if (s <= r.t) {
+        const int64_t row_k = ((int64_t)r.b * a.T + s) * ld + a.d + r.h * a.dh;
+        float acc = 0.f;
+        for (int j = 0; j < a.dh; ++j) acc += qs[j] * ldf(a.qkv, row_k + j, a.dt);
+        v = acc;
+        sc[s] = v;
+      }
+      mx = fmaxf(mx, v);
+    }
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int s = l; s <= r.t; s += kWave) {
+      float p = expf(sc[s] - mx);
+      sc[s] = p;
+      sum += p;
+    }
+    sum = wave_sum(sum);
+    wave_sync();
+    const float inv = 1.0f / sum;
+    if (l < a.dh) {
+      float acc = 0.f;
+      for (int s = 0; s <= r.t; ++s) {
+        const int64_t row_v = ((int64_t)r.b * a.T + s) * ld + 2 * a.d + r.h * a.dh;
+        acc += sc[s] * ldf(a.qkv, row_v + l, a.dt);
+      }
+      stf(a.o, ((int64_t)r.b * a.T + r.t) * a.d + r.h * a.dh + l, a.dt, acc * inv);
+    }
+    if (l == 0) a.lse[((int64_t)r.b * a.H + r.h) * a.T + r.t] = mx + logf(sum);
+    wave_sync();
+  }
+}
+
+// D[b,h,t] = sum_j dO[b,t,h,j] * O[b,t,h,j]; one wave per (row, head)
+__device__ void task_attn_prep(const AttnArgs& a, int tile) {
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  const int BT = a.B * a.T;
+  const int per_tile = a.block;   // rows per tile
+  const int r0 = tile * per_tile, r1 = min(r0 + per_tile, BT);
+  for (int item = w; item < (r1 - r0) * a.H; item += kWaves) {
+    int r = r0 + item / a.H, h = item % a.H;
+    float s = 0.f;
+    for (int j = l; j < a.dh; j += kWave) {
+      int64_t i = (int64_t)r * a.d + h * a.dh + j;
+      s += ldf(a.dout, i, a.dt) * ldf(a.o, i, a.dt);
+    }
+    s = wave_sum(s);
+    int b = r / a.T, t = r % a.T;
+    if (l == 0) a.dsum[((int64_t)b * a.H + h) * a.T + t] = s;
+  }
+}
+
+// key row s: dV_s = sum_{t>=s} P_ts dO_t;  dK_s = scale * sum_{t>=s} dS_ts q_t
+__device__ void task_attn_bwd_kv_simple(const AttnArgs& a, int tile, char* smem) {
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  float* ks = (float*)smem + w * (2 * 64 + 2 * 64);
+  float* vs = ks + 64;
+  float* ps = vs + 64;
+  float* dss = ps + 64;
+  const float scale = 1.0f / sqrtf((float)a.dh);
+  const int64_t ld = 3 * (int64_t)a.d;
+  for (int i = w; i < a.block; i += kWaves) {
+    AttnIdx r = attn_row(a, tile, i);
+    if (r.t >= a.T) break;
+    const int s = r.t;
+    const int64_t rs = ((int64_t)r.b * a.T + s) * ld + r.h * a.dh;
+    if (l < a.dh) {
+      ks[l] = ldf(a.qkv, rs + a.d + l, a.dt);
+      vs[l] = ldf(a.qkv, rs + 2 * a.d + l, a.dt);
+    }
+    wave_sync();
+    float dk = 0.f, dv = 0.f;
+    for (int t0 = s; t0 < a.T; t0 += kWave) {
+      int t = t0 + l;
+      float p = 0.f, ds = 0.f;
+      if (t < a.T) {
+        const int64_t rq = ((int64_t)r.b * a.T + t) * ld + r.h * a.dh;
+        const int64_t ro = ((int64_t)r.b * a.T + t) * a.d + r.h * a.dh;
+        float qk = 0.f, dpv = 0.f;
+        for (int j = 0; j < a.dh; ++j) {
+          qk += ldf(a.qkv, rq + j, a.dt) * ks[j];
+          dpv += ldf(a.dout, ro + j, a.dt) * vs[j];
+        }
+        const int64_t st = ((int64_t)r.b * a.H + r.h) * a.T + t;
+        p = expf(qk * scale - a.lse[st]);
+        ds = p * (dpv - a.dsum[st]);
+      }
+      ps[l] = p;
+      dss[l] = ds;
+      wave_sync();
+      if (l < a.dh) {
+        const int n = min(kWave, a.T - t0);
+        for (int u = 0; u < n; ++u) {
+          const int64_t tt = (int64_t)r.b * a.T + t0 + u;
+          dv += ps[u] * ldf(a.dout, tt * a.d + r.h * a.dh + l, a.dt);
+          dk += dss[u] * ldf(a.qkv, tt * ld + r.h * a.dh + l, a.dt);
+        }
+      }
+      wave_sync();
+    }
+    if (l < a.dh) {
+      stf(a.dqkv, rs + a.d + l, a.dt, dk * scale);
+      stf(a.dqkv, rs + 2 * a.d + l, a.dt, dv);
+    }
+    wave_sync();
+  }
+}
+
+// query row t: dQ_t = scale * sum_{s<=t} dS_ts k_s
+__device__ void task_attn_bwd_q_simple(const AttnArgs& a, int tile, char* smem) {
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  float* qs = (float*)smem + w * (3 * 64);
+  float* dos = qs + 64;
+  float* dss = dos + 64;
+  const float scale = 1.0f / sqrtf((float)a.dh);
+  const int64_t ld = 3 * (int64_t)a.d;
+  for (int i = w; i < a.block; i += kWaves) {
+    AttnIdx r = attn_row(a, tile, i);
+    if (r.t >= a.T) break;
+    const int t = r.t;
+    const int64_t rq = ((int64_t)r.b * a.T + t) * ld + r.h * a.dh;
+    const int64_t ro = ((int64_t)r.b * a.T + t) * a.d + r.h * a.dh;
+    if (l < a.dh) {
+      qs[l] = ldf(a.qkv, rq + l, a.dt);
+      dos[l] = ldf(a.dout, ro + l, a.dt);
+    }
+    wave_sync();
+    const int64_t st = ((int64_t)r.b * a.H + r.h) * a.T + t;
+    const float lse = a.lse[st], D = a.dsum[st];
+    float dq = 0.f;
+    for (int s0 = 0; s0 <= t; s0 += kWave) {
+      int s = s0 + l;
+      float ds = 0.f;
+      if (s <= t) {
+        const int64_t rk = ((int64_t)r.b * a.T + s) * ld + r.h * a.dh;
+        float qk = 0.f, dpv = 0.f;
+        for (int j = 0; j < a.dh; ++j) {
+          qk += qs[j] * ldf(a.qkv, rk + a.d + j, a.dt);
+          dpv += dos[j] * ldf(a.qkv, rk + 2 * a.d + j, a.dt);
+        }
+        float p = expf(qk * scale - lse);
+        ds = p * (dpv - D);
+      }
+      dss[l] = ds;
+      wave_sync();
+      if (l < a.dh) {
+        const int n = min(kWave, t - s0 + 1);
+        for (int u = 0; u < n; ++u) {
+          const int64_t rk = ((int64_t)r.b * a.T + s0 + u) * ld + a.d + r.h * a.dh;
+          dq += dss[u] * ldf(a.qkv, rk + l, a.dt);
+        }
+      }
+      wave_sync();
+    }
+    if (l < a.dh) stf(a.dqkv, rq + l, a.dt, dq * scale);
+    wave_sync();
+  }
+}
+
+// ---------------------------------------------------------------- cross-entropy
+// One row per tile.  loss_r = logsumexp(z) - z[y];  dz = (softmax(z) - onehot(y)) / rows.
+
+__device__ void task_ce(const CeArgs& a, int tile, const TaskCtx& tc, char* smem) {
+  float* red = (float*)smem;
+  const int r = tile;
+  const int b = r / a.T, t = r % a.T;
+  const int y = token_at(tc.sc, b, t + 1, a.T, a.V, tc);
+  const float* z = a.logits + (int64_t)r * a.V;
+  float mx = -INFINITY;
+  for (int v = threadIdx.x; v < a.V; v += kThreads) mx = fmaxf(mx, z[v]);
+  mx = block_max(mx, red);
+  float s = 0.f;
+  for (int v = threadIdx.x; v < a.V; v += kThreads) s += expf(z[v] - mx);
+  s = block_sum(s, red + kWaves);
+  const float lse = mx + logf(s);
+  for (int v = threadIdx.x; v < a.V; v += kThreads) {
+    float p = expf(z[v] - lse);
+    stf(a.dz, (int64_t)r * a.V + v, a.dt, (p - (v == y ? 1.f : 0.f)) * a.inv_rows);
+  }
+  if (threadIdx.x == 0) a.loss_rows[r] = lse - z[y];
+}
+
+// mean of the per-row losses, fixed summation order; flags a non-finite loss
+__device__ void task_loss(const LossArgs& a, const TaskCtx& tc, char* smem) {
+  float* red = (float*)smem;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < a.rows; i += kThreads) s += (double)a.loss_rows[i];
+  s = wave_sum_d(s);
+  int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  double* dred = (double*)red;
+  __syncthreads();
+  if (l == 0) dred[w] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int i = 0; i < kWaves; ++i) tot += dred[i];
+    float loss = (float)(tot / a.rows);
+    if (tc.sc->loss_out) *tc.sc->loss_out = loss;
+    if (!isfinite(loss)) raise_status(tc.status, -3 /*OFA_E_NONFINITE*/, tc.phase, tc.step, 0);
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- embedding backward
+// EMB_SORT (one tile): sort positions by (token, position) with a bitonic sort
+// in LDS, so that every token's positions form one run in increasing position
+// order.  For each token present, first[tok] = tag << 32 | start << 16 | count.
+
+__device__ void task_emb_sort(const EmbSortArgs& a, const TaskCtx& tc, char* smem) {
+  uint64_t* keys = (uint64_t*)smem;
+  int n = 1;
+  while (n < a.BT) n <<= 1;
+  const int T1 = a.T + 1;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    uint64_t k = ~0ull;
+    if (i < a.BT) {
+      int tok = tc.sc->tokens[(int64_t)(i / a.T) * T1 + i % a.T];
+      if (tok < 0 || tok >= a.V) tok = 0;   // reported by the embedding gather
+      k = ((uint64_t)(uint32_t)tok << 32) | (uint32_t)i;
+    }
+    keys[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += kThreads) {
+        int ixj = i ^ j;
+        if (ixj > i) {
+          uint64_t x = keys[i], y = keys[ixj];
+          bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < a.BT; i += kThreads) {
+    uint64_t k = keys[i];
+    uint32_t tok = (uint32_t)(k >> 32);
+    a.sorted[i] = (int32_t)(k & 0xffffffffu);
+    if (i == 0 || (uint32_t)(keys[i - 1] >> 32) != tok) {
+      int e = i + 1;
+      while (e < a.BT && (uint32_t)(keys[e] >> 32) == tok) ++e;
+      a.first[tok] = (tc.sc->tag << 32) | ((uint64_t)i << 16) | (uint64_t)(e - i);
+    }
+  }
+  __syncthreads();
+}
+
+// rows of d wte: fixed-order sum over the token's positions (or zero); then rows of d wpe
+__device__ void task_emb_bwd(const EmbBwdArgs& a, int tile, const TaskCtx& tc) {
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  const int nj = (a.d + kWave - 1) / kWave;
+  if (tile < a.v_tiles) {
+    const int v0 = tile * a.rows_per_tile, v1 = min(v0 + a.rows_per_tile, a.V);
+    for (int v = v0 + w; v < v1; v += kWaves) {
+      float acc[kMaxDPerLane];
+#pragma unroll
+      for (int c = 0; c < kMaxDPerLane; ++c) acc[c] = 0.f;
+      const uint64_t f = a.first[v];
+      const bool present = (f >> 32) == (tc.sc->tag & 0xffffffffu);
+      if (present) {
+        const int start = (int)((f >> 16) & 0xffff), cnt = (int)(f & 0xffff);
+        for (int k = start; k < start + cnt; ++k) {
+          const float* row = a.dx0 + (int64_t)a.sorted[k] * a.d;
+#pragma unroll
+          for (int c = 0; c < kMaxDPerLane; ++c) {
+            int j = l + c * kWave;
+            if (c < nj && j < a.d) acc[c] += row[j];
+          }
+        }
+      }
+      if (!present && a.accumulate) continue;
+      float* out = a.dwte + (int64_t)v * a.d;
+#pragma unroll
+      for (int c = 0; c < kMaxDPerLane; ++c) {
+        int j = l + c * kWave;
+        if (c < nj && j < a.d) out[j] = (a.accumulate ? out[j] : 0.f) + acc[c];
+      }
+    }
+  } else {
+    const int t0 = (tile - a.v_tiles) * a.rows_per_tile, t1 = min(t0 + a.rows_per_tile, a.n_pos);
+    for (int t = t0 + w; t < t1; t += kWaves) {
+      for (int j = l; j < a.d; j += kWave) {
+        float s = 0.f;
+        if (t < a.T)
+          for (int b = 0; b < a.B; ++b) s += a.dx0[((int64_t)b * a.T + t) * a.d + j];
+        a.dwpe[(int64_t)t * a.d + j] = s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- AdamW
+// p <- p(1 - lr wd); m <- b1 m + (1-b1) g; v <- b2 v + (1-b2) g^2;
+// p <- p - lr (m/bc1) / (sqrt(v/bc2) + eps); compute copy <- p.
+
+__device__ void task_adamw(const AdamArgs& a, int tile, const TaskCtx& tc) {
+  const float lr = tc.sc->lr, bc1 = tc.sc->bc1, bc2 = tc.sc->bc2;
+  const int64_t i0 = (int64_t)tile * a.per_tile;
+  const int64_t i1 = min(i0 + (int64_t)a.per_tile, a.n);
+  const float decay = 1.0f - lr * a.wd;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += kThreads) {
+    float g = a.g[i];
+    float p = a.p[i] * decay;
+    float m = a.beta1 * a.m[i] + (1.0f - a.beta1) * g;
+    float v = a.beta2 * a.v[i] + (1.0f - a.beta2) * g * g;
+    p -= lr * (m / bc1) / (sqrtf(v / bc2) + a.eps);
+    a.p[i] = p;
+    a.m[i] = m;
+    a.v[i] = v;
+    if (a.wc) stf(a.wc, i, a.wc_dt, p);
+  }
+}
+
+__device__ void task_copy(const CopyArgs& a, int tile) {
+  const int64_t i0 = (int64_t)tile * a.per_tile;
+  const int64_t i1 = min(i0 + (int64_t)a.per_tile, a.n);
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += kThreads) stf(a.dst, i, a.dst_dt, ldf(a.src, i, a.src_dt));
+}
+
+}  // namespace ofa

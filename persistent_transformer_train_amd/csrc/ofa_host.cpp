@@ -1,0 +1,1307 @@
+// ofa_host.cpp -- libofa.so: the C ABI declared in include/ofa.h.
+//
+// Host responsibilities: validate the configuration, lay out the parameters
+// and carve the caller's workspace, build the phase tables ("programs") of a
+// training step and of a decode position, and run them with one of the two
+// executors (one launch per phase, or the persistent kernel).  The host never
+// touches model data: every step of the method runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/ofa.h"
+#include "ofa_launch.h"
+#include "ofa_types.h"
+
+using namespace ofa;
+
+namespace {
+
+constexpr int kMaxSteps = 8192;        // training steps per call
+constexpr int kMaxDecInst = 1 << 16;   // decode positions per call
+constexpr size_t kAlign = 256;
+constexpr size_t kMiscBytes = 4096;    // one Phase (offset 0) and the DecIO block (offset 2048)
+constexpr size_t kMiscDecIO = 2048;
+
+// ---------------------------------------------------------------- parameter layout
+
+struct TensorDesc {
+  std::string name;
+  int64_t off = 0, numel = 0;
+  int kind = 0;   // 0 normal, 1 zeros, 2 ones
+};
+
+struct LayerOff {
+  int64_t ln1_g = -1, ln1_b = -1, w_qkv = -1, b_qkv = -1, w_o = -1, b_o = -1, ln2_g = -1, ln2_b = -1;
+  int64_t w_fc = -1, b_fc = -1, w_proj = -1, b_proj = -1, w_gate = -1, w_up = -1, w_down = -1;
+};
+
+struct Layout {
+  std::vector<TensorDesc> t;
+  int64_t total = 0;
+  int64_t wte = -1, wpe = -1, lnf_g = -1, lnf_b = -1, w_lm = -1;
+  std::vector<LayerOff> layer;
+};
+
+Layout make_layout(const ofa_config& c) {
+  Layout L;
+  const int64_t d = c.d_model, F = c.d_ff, V = c.vocab;
+  auto add = [&](const std::string& n, int64_t numel, int kind) {
+    TensorDesc td;
+    td.name = n;
+    td.off = L.total;
+    td.numel = numel;
+    td.kind = kind;
+    L.t.push_back(td);
+    L.total += numel;
+    return td.off;
+  };
+  L.wte = add("wte", V * d, 0);
+  if (c.n_pos) L.wpe = add("wpe", (int64_t)c.n_pos * d, 0);
+  for (int l = 0; l < c.n_layer; ++l) {
+    std::string p = "h" + std::to_string(l) + ".";
+    LayerOff o;
+    o.ln1_g = add(p + "ln1.g", d, 2);
+    o.ln1_b = add(p + "ln1.b", d, 1);
+    o.w_qkv = add(p + "w_qkv", 3 * d * d, 0);
+    if (c.has_bias) o.b_qkv = add(p + "b_qkv", 3 * d, 1);
+    o.w_o = add(p + "w_o", d * d, 0);
+    if (c.has_bias) o.b_o = add(p + "b_o", d, 1);
+    o.ln2_g = add(p + "ln2.g", d, 2);
+    o.ln2_b = add(p + "ln2.b", d, 1);
+    if (c.mlp_gated) {
+      o.w_gate = add(p + "w_gate", F * d, 0);
+      o.w_up = add(p + "w_up", F * d, 0);
+      o.w_down = add(p + "w_down", d * F, 0);
+    } else {
+      o.w_fc = add(p + "w_fc", F * d, 0);
+      if (c.has_bias) o.b_fc = add(p + "b_fc", F, 1);
+      o.w_proj = add(p + "w_proj", d * F, 0);
+      if (c.has_bias) o.b_proj = add(p + "b_proj", d, 1);
+    }
+    L.layer.push_back(o);
+  }
+  L.lnf_g = add("lnf.g", d, 2);
+  L.lnf_b = add("lnf.b", d, 1);
+  if (!c.tied_head) L.w_lm = add("w_lm", V * d, 0);
+  return L;
+}
+
+std::string validate(const ofa_config& c) {
+  char buf[256];
+  auto bad = [&](const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    return std::string(buf);
+  };
+  if (c.n_layer < 1 || c.n_layer > 64) return bad("n_layer %d out of [1, 64]", c.n_layer);
+  if (c.n_head < 1 || c.d_model < 1 || c.d_model % c.n_head) return bad("d_model %d not divisible by n_head %d", c.d_model, c.n_head);
+  const int dh = c.d_model / c.n_head;
+  if (dh > 64 || dh % 2 || 256 % dh) return bad("head dim %d unsupported (even, divides 256, <= 64)", dh);
+  if (c.d_model > 1024 || c.d_model % 8) return bad("d_model %d must be a multiple of 8 and <= 1024", c.d_model);
+  if (c.d_ff < 8 || c.d_ff % 8) return bad("d_ff %d must be a positive multiple of 8", c.d_ff);
+  if (c.vocab < 2 || c.vocab % 8) return bad("vocab %d must be a multiple of 8 (>= 8)", c.vocab);
+  if (c.n_pos < 0) return bad("n_pos < 0");
+  if (c.batch < 1 || c.seq < 1) return bad("batch/seq must be >= 1");
+  if (c.n_pos && c.seq > c.n_pos) return bad("seq %d exceeds the position table (%d)", c.seq, c.n_pos);
+  if (c.seq > 4096) return bad("seq %d > 4096", c.seq);
+  if ((int64_t)c.batch * c.seq > 8192) return bad("batch*seq %d exceeds 8192 (embedding sort)", c.batch * c.seq);
+  if ((int64_t)c.batch * c.seq % 8 && c.precision == OFA_BF16)
+    return bad("batch*seq must be a multiple of 8 in bf16 mode");
+  if (c.precision != OFA_FP32 && c.precision != OFA_BF16) return bad("precision %d unknown", c.precision);
+  if (c.precision == OFA_BF16 && dh != 64) return bad("bf16 mode needs head dim 64 (got %d)", dh);
+  if (c.mlp_gated && c.has_bias) return bad("gated MLP has no biases in this model family");
+  if (c.n_pos == 0 && dh % 2) return bad("rotary positions need an even head dim");
+  if (!(c.lr >= 0) || !(c.beta1 >= 0 && c.beta1 < 1) || !(c.beta2 >= 0 && c.beta2 < 1) || !(c.eps > 0))
+    return bad("optimizer hyper-parameters out of range");
+  if (c.lr_schedule != OFA_LR_CONSTANT && c.lr_schedule != OFA_LR_COSINE) return bad("lr_schedule unknown");
+  if (c.lr_schedule == OFA_LR_COSINE && c.total_steps < 1) return bad("cosine schedule needs total_steps >= 1");
+  if (c.exec_mode != OFA_EXEC_PERSISTENT && c.exec_mode != OFA_EXEC_LAUNCH_PER_PHASE) return bad("exec_mode unknown");
+  const int win = c.decode_window ? c.decode_window : (c.n_pos ? c.n_pos : c.seq);
+  if (win < 2 || (c.n_pos && win > c.n_pos)) return bad("decode_window %d invalid", win);
+  if (win > 8192) return bad("decode_window %d > 8192", win);
+  const int keep = c.prompt_len ? c.prompt_len : 1;
+  if (keep < 1 || keep > win) return bad("prompt_len %d invalid for window %d", keep, win);
+  if (c.train_cus < 0 || c.serve_cus < 0) return bad("negative CU count");
+  for (int r : c.reserved)
+    if (r) return bad("reserved fields must be zero");
+  return "";
+}
+
+// ---------------------------------------------------------------- workspace carving
+
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    size_t o = off;
+    off += bytes;
+    return o;
+  }
+};
+
+struct Carve {
+  // offsets (bytes) into the workspace
+  size_t p, g, m, v, wc, serve, xres, ln_mean, ln_rstd, h, qkv, o, lse, mlp1, mlp2, logits, dz, loss_rows;
+  size_t dxres, dxlp, dln, dmlp, dout, dsum, dqkv, ln_part, cs_fc, cs_qkv, esorted, efirst;
+  size_t sched, status, times, inst_end, steps, published;
+  size_t kv, ctx_tok, dstate, dx, dq, dvo, dmlp_v, dlogits, dsteps, dtimes, misc;
+  size_t total;
+  int n_slots;
+  int ln_tiles, cs_tiles;
+};
+
+struct Dims {
+  int64_t B, T, BT, d, H, dh, F, V, L, P, win, keep, mlp1_cols;
+  int lp_dt;
+  size_t lp;   // bytes per low-precision element
+};
+
+Dims dims_of(const ofa_config& c, const Layout& lay) {
+  Dims D;
+  D.B = c.batch;
+  D.T = c.seq;
+  D.BT = D.B * D.T;
+  D.d = c.d_model;
+  D.H = c.n_head;
+  D.dh = D.d / D.H;
+  D.F = c.d_ff;
+  D.V = c.vocab;
+  D.L = c.n_layer;
+  D.P = lay.total;
+  D.win = c.decode_window ? c.decode_window : (c.n_pos ? c.n_pos : c.seq);
+  D.keep = c.prompt_len ? c.prompt_len : 1;
+  D.mlp1_cols = c.mlp_gated ? 2 * D.F : D.F;
+  D.lp_dt = c.precision == OFA_BF16 ? DT_BF16 : DT_F32;
+  D.lp = c.precision == OFA_BF16 ? 2 : 4;
+  return D;
+}
+
+constexpr int kLnRows = 16;     // rows per LayerNorm tile
+constexpr int kCsRows = 64;     // rows per column-sum tile
+
+Carve carve(const ofa_config& c, const Layout& lay) {
+  Dims D = dims_of(c, lay);
+  Carve w;
+  Bump b;
+  const size_t f4 = 4, lp = D.lp;
+  const bool bf = c.precision == OFA_BF16;
+  const int64_t R = 2 * D.L + 1;   // residual points
+  w.n_slots = (c.train_cus > 0 && c.serve_cus > 0) ? 2 : 1;
+  w.ln_tiles = (int)((D.BT + kLnRows - 1) / kLnRows);
+  w.cs_tiles = (int)((D.BT + kCsRows - 1) / kCsRows);
+  w.p = b.take(D.P * f4);
+  w.g = b.take(D.P * f4);
+  w.m = b.take(D.P * f4);
+  w.v = b.take(D.P * f4);
+  w.wc = bf ? b.take(D.P * lp) : w.p;
+  w.serve = b.take(D.P * lp * w.n_slots);
+  w.xres = b.take(R * D.BT * D.d * f4);
+  w.ln_mean = b.take(R * D.BT * f4);
+  w.ln_rstd = b.take(R * D.BT * f4);
+  w.h = b.take(R * D.BT * D.d * lp);
+  w.qkv = b.take(D.L * D.BT * 3 * D.d * lp);
+  w.o = b.take(D.L * D.BT * D.d * lp);
+  w.lse = b.take(D.L * D.B * D.H * D.T * f4);
+  w.mlp1 = b.take(D.L * D.BT * D.mlp1_cols * lp);
+  w.mlp2 = b.take(D.L * D.BT * D.F * lp);
+  w.logits = b.take(D.BT * D.V * f4);
+  w.dz = b.take(D.BT * D.V * lp);
+  w.loss_rows = b.take(D.BT * f4);
+  w.dxres = b.take(R * D.BT * D.d * f4);
+  w.dxlp = bf ? b.take(R * D.BT * D.d * lp) : w.dxres;
+  w.dln = b.take(R * D.BT * D.d * f4);
+  w.dmlp = b.take(D.L * D.BT * D.mlp1_cols * lp);
+  w.dout = b.take(D.L * D.BT * D.d * lp);
+  w.dsum = b.take(D.L * D.B * D.H * D.T * f4);
+  w.dqkv = b.take(D.L * D.BT * 3 * D.d * lp);
+  w.ln_part = b.take(R * w.ln_tiles * 3 * D.d * f4);
+  w.cs_fc = b.take(D.L * w.cs_tiles * D.F * f4);
+  w.cs_qkv = b.take(D.L * w.cs_tiles * 3 * D.d * f4);
+  w.esorted = b.take(D.BT * 4);
+  w.efirst = b.take(D.V * 8);
+  w.sched = b.take(sizeof(Sched));
+  w.status = b.take(sizeof(DevStatus));
+  w.times = b.take(kMaxPhases * sizeof(PhaseTime));
+  w.dtimes = b.take(kMaxPhases * sizeof(PhaseTime));
+  w.inst_end = b.take(kMaxSteps * 8);
+  w.steps = b.take(kMaxSteps * sizeof(StepCtx));
+  w.published = b.take(64);
+  w.kv = b.take(D.L * 2 * D.H * D.win * D.dh * lp);
+  w.ctx_tok = b.take(D.win * 4);
+  w.dstate = b.take(sizeof(DecState));
+  w.dx = b.take(R * D.d * f4);
+  w.dq = b.take(D.d * f4);
+  w.dvo = b.take(D.L * D.d * f4);
+  w.dmlp_v = b.take(D.L * D.F * f4);
+  w.dlogits = b.take(D.V * f4);
+  w.dsteps = b.take((size_t)kMaxDecInst * sizeof(StepCtx));
+  w.misc = b.take(kMiscBytes);
+  w.total = (b.off + kAlign - 1) / kAlign * kAlign;
+  return w;
+}
+
+template <typename T>
+T* at(char* ws, size_t off) { return (T*)(ws + off); }
+
+}  // namespace
+
+// ---------------------------------------------------------------- the handle
+
+struct ofa_handle {
+  ofa_config cfg{};
+  Layout lay;
+  Dims D{};
+  Carve cw{};
+  hipStream_t stream = nullptr;
+  char* ws = nullptr;
+  int n_cu = 0;
+  std::vector<Phase> train;        // one training step
+  std::vector<Phase> dec;          // one decode position (with head)
+  Phase* d_train = nullptr;        // device copies (inside the pinned-upload area)
+  Phase* d_dec = nullptr;
+  std::vector<char> phase_names;   // for phase_times
+  std::vector<std::string> train_names;
+  StepCtx* h_steps = nullptr;      // pinned staging
+  StepCtx* h_dsteps = nullptr;
+  char* h_misc = nullptr;          // pinned staging for the misc block
+  hipEvent_t ev_upload = nullptr, ev_t0 = nullptr, ev_t1 = nullptr;
+  bool upload_pending = false;
+  uint64_t steps_done = 0;
+  uint64_t version = 0;
+  int sticky = 0;
+  int last_grid = 0;
+  uint64_t last_tickets = 0;
+  double last_ms = 0;
+  std::string err;
+  int hip_err = 0;
+  // decode host mirror of the context rule
+  int64_t dec_ctx_len = 0, dec_processed = 0;
+  bool dec_started = false;
+  void* d_alloc = nullptr;         // library-owned device memory for phase tables (small)
+};
+
+namespace {
+
+ofa_status fail(ofa_handle* h, ofa_status s, const char* fmt, ...) {
+  if (h) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    h->err = buf;
+  }
+  return s;
+}
+
+#define HIP_TRY(h, expr)                                                                   \
+  do {                                                                                     \
+    hipError_t _e = (expr);                                                                \
+    if (_e != hipSuccess) {                                                                \
+      (h)->hip_err = (int)_e;                                                              \
+      return fail((h), OFA_E_HIP, "%s failed: %s", #expr, hipGetErrorString(_e));          \
+    }                                                                                      \
+  } while (0)
+
+// ---------------------------------------------------------------- program builders
+
+struct Builder {
+  std::vector<Phase>* out;
+  std::vector<std::string>* names;
+  int add(Op op, int n_tiles, const char* name, std::initializer_list<int> deps = {}) {
+    Phase p;
+    memset(&p, 0, sizeof p);
+    p.op = op;
+    p.n_tiles = n_tiles;
+    for (int i = 0; i < kMaxDeps; ++i) p.dep[i] = -1;
+    int i = 0;
+    for (int d : deps)
+      if (i < kMaxDeps) p.dep[i++] = d;
+    p.dep_prev = -1;
+    out->push_back(p);
+    if (names) names->push_back(name);
+    return (int)out->size() - 1;
+  }
+  Phase& operator[](int i) { return (*out)[i]; }
+};
+
+int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t lda, int a_km, int a_dt,
+              const void* B, int64_t ldb, int b_km, int b_dt, void* C, int64_t ldc, int c_dt, int epi) {
+  GemmArgs g;
+  memset(&g, 0, sizeof g);
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.A = A;
+  g.lda = lda;
+  g.a_kmajor = a_km;
+  g.a_dt = a_dt;
+  g.B = B;
+  g.ldb = ldb;
+  g.b_kmajor = b_km;
+  g.b_dt = b_dt;
+  g.C = C;
+  g.ldc = ldc;
+  g.c_dt = c_dt;
+  g.epi = epi;
+  const bool mfma = h->cfg.precision == OFA_BF16 && a_dt == DT_BF16 && b_dt == DT_BF16;
+  g.impl = mfma ? GEMM_MFMA : GEMM_SIMPLE;
+  g.bm = mfma ? 128 : 64;
+  g.bn = mfma ? 128 : 64;
+  g.tiles_m = cdiv(M, g.bm);
+  g.tiles_n = cdiv(N, g.bn);
+  return g;
+}
+
+void build_train(ofa_handle* h) {
+  const ofa_config& c = h->cfg;
+  const Dims& D = h->D;
+  const Carve& w = h->cw;
+  char* ws = h->ws;
+  h->train.clear();
+  h->train_names.clear();
+  Builder b{&h->train, &h->train_names};
+  const int lp = D.lp_dt;
+  const int64_t BT = D.BT, d = D.d, F = D.F, V = D.V, L = D.L;
+  float* P = at<float>(ws, w.p);
+  float* G = at<float>(ws, w.g);
+  char* WC = ws + w.wc;   // compute weights (lp)
+  auto wc = [&](int64_t off) -> const void* { return WC + off * D.lp; };
+  auto pf = [&](int64_t off) -> float* { return off < 0 ? nullptr : P + off; };
+  auto gf = [&](int64_t off) -> float* { return off < 0 ? nullptr : G + off; };
+  float* xres = at<float>(ws, w.xres);
+  auto X = [&](int i) { return xres + (int64_t)i * BT * d; };
+  auto Hh = [&](int i) -> void* { return ws + w.h + (size_t)i * BT * d * D.lp; };
+  auto MEAN = [&](int i) { return at<float>(ws, w.ln_mean) + (int64_t)i * BT; };
+  auto RSTD = [&](int i) { return at<float>(ws, w.ln_rstd) + (int64_t)i * BT; };
+  auto QKV = [&](int l) -> void* { return ws + w.qkv + (size_t)l * BT * 3 * d * D.lp; };
+  auto O = [&](int l) -> void* { return ws + w.o + (size_t)l * BT * d * D.lp; };
+  auto LSE = [&](int l) { return at<float>(ws, w.lse) + (int64_t)l * D.B * D.H * D.T; };
+  auto M1 = [&](int l) -> void* { return ws + w.mlp1 + (size_t)l * BT * D.mlp1_cols * D.lp; };
+  auto M2 = [&](int l) -> void* { return ws + w.mlp2 + (size_t)l * BT * F * D.lp; };
+  auto DX = [&](int i) { return at<float>(ws, w.dxres) + (int64_t)i * BT * d; };
+  auto DXLP = [&](int i) -> void* { return ws + w.dxlp + (size_t)i * BT * d * D.lp; };
+  auto DLN = [&](int i) { return at<float>(ws, w.dln) + (int64_t)i * BT * d; };
+  auto DM = [&](int l) -> void* { return ws + w.dmlp + (size_t)l * BT * D.mlp1_cols * D.lp; };
+  auto DOUT = [&](int l) -> void* { return ws + w.dout + (size_t)l * BT * d * D.lp; };
+  auto DSUM = [&](int l) { return at<float>(ws, w.dsum) + (int64_t)l * D.B * D.H * D.T; };
+  auto DQKV = [&](int l) -> void* { return ws + w.dqkv + (size_t)l * BT * 3 * d * D.lp; };
+  auto LNP = [&](int i) { return at<float>(ws, w.ln_part) + (int64_t)i * w.ln_tiles * 3 * d; };
+  auto CSF = [&](int l) { return at<float>(ws, w.cs_fc) + (int64_t)l * w.cs_tiles * F; };
+  auto CSQ = [&](int l) { return at<float>(ws, w.cs_qkv) + (int64_t)l * w.cs_tiles * 3 * d; };
+  const int lnt = w.ln_tiles;
+  const int attn_block = 16;
+  const int attn_tiles = (int)(D.B * D.H * cdiv(D.T, attn_block));
+
+  auto ln_fwd = [&](int i, int dep, const char* nm) {
+    int p = b.add(OP_LN_FWD, lnt, nm, {dep});
+    LnFwdArgs& a = b[p].a.lnf;
+    a.x = X(i);
+    a.g = nullptr;
+    a.y = Hh(i);
+    a.mean = MEAN(i);
+    a.rstd = RSTD(i);
+    a.rows = (int)BT;
+    a.d = (int)d;
+    a.y_dt = lp;
+    a.rows_per_tile = kLnRows;
+    return p;
+  };
+  auto set_ln_params = [&](int p, int64_t g_off, int64_t b_off) {
+    b[p].a.lnf.g = pf(g_off);
+    b[p].a.lnf.b = pf(b_off);
+  };
+  auto gemm_phase = [&](const GemmArgs& g, std::initializer_list<int> deps, const char* nm) {
+    int p = b.add(OP_GEMM, g.tiles_m * g.tiles_n, nm, deps);
+    b[p].a.gemm = g;
+    return p;
+  };
+  auto attn_args = [&](int l) {
+    AttnArgs a;
+    memset(&a, 0, sizeof a);
+    a.qkv = QKV(l);
+    a.o = O(l);
+    a.lse = LSE(l);
+    a.dout = DOUT(l);
+    a.dsum = DSUM(l);
+    a.dqkv = DQKV(l);
+    a.B = (int)D.B;
+    a.T = (int)D.T;
+    a.H = (int)D.H;
+    a.dh = (int)D.dh;
+    a.d = (int)d;
+    a.dt = lp;
+    a.block = attn_block;
+    a.impl = 0;
+    return a;
+  };
+  auto rope_args = [&](void* buf) {
+    RopeArgs r;
+    memset(&r, 0, sizeof r);
+    r.qkv = buf;
+    r.ld = 3 * d;
+    r.B = (int)D.B;
+    r.T = (int)D.T;
+    r.H = (int)D.H;
+    r.dh = (int)D.dh;
+    r.d = (int)d;
+    r.dt = lp;
+    r.rows_per_tile = 16;
+    r.pos0 = 0;
+    return r;
+  };
+
+  // ---- forward
+  int p_emb = b.add(OP_EMBED, cdiv(BT, 16), "embed");
+  {
+    EmbedArgs& a = b[p_emb].a.emb;
+    a.wte = pf(h->lay.wte);
+    a.wpe = pf(h->lay.wpe);
+    a.x = X(0);
+    a.B = (int)D.B;
+    a.T = (int)D.T;
+    a.d = (int)d;
+    a.V = (int)V;
+    a.rows_per_tile = 16;
+  }
+  int p_sort = b.add(OP_EMB_SORT, 1, "emb_sort");
+  {
+    EmbSortArgs& a = b[p_sort].a.esort;
+    a.sorted = at<int32_t>(ws, w.esorted);
+    a.first = at<uint64_t>(ws, w.efirst);
+    a.BT = (int)BT;
+    a.T = (int)D.T;
+    a.V = (int)V;
+  }
+  int last_x = p_emb;
+  for (int l = 0; l < L; ++l) {
+    const LayerOff& lo = h->lay.layer[l];
+    int p_ln1 = ln_fwd(2 * l, last_x, "ln1");
+    set_ln_params(p_ln1, lo.ln1_g, lo.ln1_b);
+    GemmArgs g = gemm(h, (int)BT, (int)(3 * d), (int)d, Hh(2 * l), d, 1, lp, wc(lo.w_qkv), d, 1, lp, QKV(l), 3 * d, lp,
+                      EPI_STORE);
+    g.bias = pf(lo.b_qkv);
+    int p_qkv = gemm_phase(g, {p_ln1}, "qkv");
+    int p_pre_attn = p_qkv;
+    if (c.n_pos == 0) {
+      int p = b.add(OP_ROPE, cdiv(BT, 16), "rope", {p_qkv});
+      b[p].a.rope = rope_args(QKV(l));
+      p_pre_attn = p;
+    }
+    int p_att = b.add(OP_ATTN_FWD, attn_tiles, "attn_fwd", {p_pre_attn});
+    b[p_att].a.attn = attn_args(l);
+    g = gemm(h, (int)BT, (int)d, (int)d, O(l), d, 1, lp, wc(lo.w_o), d, 1, lp, X(2 * l + 1), d, DT_F32, EPI_RESID);
+    g.bias = pf(lo.b_o);
+    g.resid = X(2 * l);
+    g.ldres = d;
+    int p_o = gemm_phase(g, {p_att, last_x}, "attn_out");
+    int p_ln2 = ln_fwd(2 * l + 1, p_o, "ln2");
+    set_ln_params(p_ln2, lo.ln2_g, lo.ln2_b);
+    int p_down;
+    if (c.mlp_gated) {
+      g = gemm(h, (int)BT, (int)(2 * F), (int)d, Hh(2 * l + 1), d, 1, lp, wc(lo.w_gate), d, 1, lp, M1(l), 2 * F, lp,
+               EPI_STORE);
+      int p_gu = gemm_phase(g, {p_ln2}, "gate_up");
+      int p_gg = b.add(OP_GEGLU_FWD, cdiv(BT, 16), "geglu", {p_gu});
+      GegluArgs& ga = b[p_gg].a.geglu;
+      ga.gu = M1(l);
+      ga.a = M2(l);
+      ga.rows = (int)BT;
+      ga.F = (int)F;
+      ga.dt = lp;
+      ga.rows_per_tile = 16;
+      g = gemm(h, (int)BT, (int)d, (int)F, M2(l), F, 1, lp, wc(lo.w_down), F, 1, lp, X(2 * l + 2), d, DT_F32,
+               EPI_RESID);
+      g.resid = X(2 * l + 1);
+      g.ldres = d;
+      p_down = gemm_phase(g, {p_gg, p_o}, "down");
+    } else {
+      g = gemm(h, (int)BT, (int)F, (int)d, Hh(2 * l + 1), d, 1, lp, wc(lo.w_fc), d, 1, lp, M1(l), F, lp, EPI_GELU);
+      g.bias = pf(lo.b_fc);
+      g.aux = M2(l);
+      g.ldaux = F;
+      g.aux_dt = lp;
+      int p_fc = gemm_phase(g, {p_ln2}, "fc");
+      g = gemm(h, (int)BT, (int)d, (int)F, M2(l), F, 1, lp, wc(lo.w_proj), F, 1, lp, X(2 * l + 2), d, DT_F32,
+               EPI_RESID);
+      g.bias = pf(lo.b_proj);
+      g.resid = X(2 * l + 1);
+      g.ldres = d;
+      p_down = gemm_phase(g, {p_fc, p_o}, "proj");
+    }
+    last_x = p_down;
+  }
+  int p_lnf = ln_fwd(2 * (int)L, last_x, "lnf");
+  set_ln_params(p_lnf, h->lay.lnf_g, h->lay.lnf_b);
+  const int64_t w_lm = c.tied_head ? h->lay.wte : h->lay.w_lm;
+  GemmArgs g = gemm(h, (int)BT, (int)V, (int)d, Hh(2 * L), d, 1, lp, wc(w_lm), d, 1, lp, at<float>(ws, w.logits), V,
+                    DT_F32, EPI_STORE);
+  int p_head = gemm_phase(g, {p_lnf}, "lm_head");
+  int p_ce = b.add(OP_CE, (int)BT, "cross_entropy", {p_head});
+  {
+    CeArgs& a = b[p_ce].a.ce;
+    a.logits = at<float>(ws, w.logits);
+    a.dz = ws + w.dz;
+    a.loss_rows = at<float>(ws, w.loss_rows);
+    a.rows = (int)BT;
+    a.V = (int)V;
+    a.T = (int)D.T;
+    a.dt = lp;
+    a.inv_rows = 1.0f / (float)BT;
+  }
+  int p_loss = b.add(OP_LOSS, 1, "loss", {p_ce});
+  b[p_loss].a.loss.loss_rows = at<float>(ws, w.loss_rows);
+  b[p_loss].a.loss.rows = (int)BT;
+
+  // ---- backward
+  void* dz = ws + w.dz;
+  g = gemm(h, (int)BT, (int)d, (int)V, dz, V, 1, lp, wc(w_lm), d, 0, lp, DLN(2 * L), d, DT_F32, EPI_STORE);
+  int p_head_dx = gemm_phase(g, {p_ce}, "lm_head_dx");
+  g = gemm(h, (int)V, (int)d, (int)BT, dz, V, 0, lp, Hh(2 * L), d, 0, lp, gf(w_lm), d, DT_F32, EPI_STORE);
+  int p_head_dw = gemm_phase(g, {p_ce}, "lm_head_dw");
+  auto ln_bwd = [&](int i, int64_t g_off, int dx_in_idx, std::initializer_list<int> deps, const char* nm) {
+    int p = b.add(OP_LN_BWD, lnt, nm, deps);
+    LnBwdArgs& a = b[p].a.lnb;
+    a.dy = DLN(i);
+    a.x = X(i);
+    a.mean = MEAN(i);
+    a.rstd = RSTD(i);
+    a.g = pf(g_off);
+    a.dx_in = dx_in_idx >= 0 ? DX(dx_in_idx) : nullptr;
+    a.dx_out = DX(i);
+    a.dx_lp = c.precision == OFA_BF16 ? DXLP(i) : nullptr;
+    a.lp_dt = lp;
+    a.partials = LNP(i);
+    a.rows = (int)BT;
+    a.d = (int)d;
+    a.rows_per_tile = kLnRows;
+    return p;
+  };
+  auto ln_red = [&](int i, int dep, float* og, float* ob, float* ores, const char* nm) {
+    int p = b.add(OP_COLRED, cdiv(d, 256), nm, {dep});
+    ColredArgs& a = b[p].a.cr;
+    a.partials = LNP(i);
+    a.out[0] = og;
+    a.out[1] = ob;
+    a.out[2] = ores;
+    a.n_parts = lnt;
+    a.n_vec = 3;
+    a.cols = (int)d;
+    a.cols_per_tile = 256;
+    return p;
+  };
+  auto colsum = [&](const void* src, int64_t ld, int cols, float* part, float* out, int dep, const char* nm) {
+    int p = b.add(OP_COLSUM, w.cs_tiles, nm, {dep});
+    ColsumArgs& a = b[p].a.cs;
+    a.src = src;
+    a.ld = ld;
+    a.partials = part;
+    a.rows = (int)BT;
+    a.cols = cols;
+    a.rows_per_tile = kCsRows;
+    a.dt = lp;
+    int q = b.add(OP_COLRED, cdiv(cols, 256), "bias_grad", {p});
+    ColredArgs& r = b[q].a.cr;
+    r.partials = part;
+    r.out[0] = out;
+    r.n_parts = w.cs_tiles;
+    r.n_vec = 1;
+    r.cols = cols;
+    r.cols_per_tile = 256;
+    return q;
+  };
+  int p_lnf_b = ln_bwd(2 * (int)L, h->lay.lnf_g, -1, {p_head_dx}, "lnf_bwd");
+  // colsum(dx at the last residual point) is the last MLP output bias gradient
+  float* last_bias = c.has_bias ? gf(h->lay.layer[L - 1].b_proj) : nullptr;
+  ln_red(2 * (int)L, p_lnf_b, gf(h->lay.lnf_g), gf(h->lay.lnf_b), last_bias, "lnf_params");
+  int cur_dx = p_lnf_b;   // phase that produced dx at the current residual point
+  for (int l = (int)L - 1; l >= 0; --l) {
+    const LayerOff& lo = h->lay.layer[l];
+    const int ri = 2 * l + 2;   // residual point after the MLP
+    void* dxo = DXLP(ri);
+    int p_mdx, p_mdw2;
+    if (c.mlp_gated) {
+      g = gemm(h, (int)BT, (int)F, (int)d, dxo, d, 1, lp, wc(lo.w_down), F, 0, lp, DM(l), 2 * F, lp, EPI_DGEGLU);
+      g.aux = M1(l);
+      g.ldaux = 2 * F;
+      g.aux_dt = lp;
+      g.aux_off = (int)F;
+      int p_ddx = gemm_phase(g, {cur_dx}, "down_dx");
+      g = gemm(h, (int)d, (int)F, (int)BT, dxo, d, 0, lp, M2(l), F, 0, lp, gf(lo.w_down), F, DT_F32, EPI_STORE);
+      gemm_phase(g, {cur_dx}, "down_dw");
+      g = gemm(h, (int)BT, (int)d, (int)(2 * F), DM(l), 2 * F, 1, lp, wc(lo.w_gate), d, 0, lp, DLN(2 * l + 1), d,
+               DT_F32, EPI_STORE);
+      p_mdx = gemm_phase(g, {p_ddx}, "gate_up_dx");
+      g = gemm(h, (int)(2 * F), (int)d, (int)BT, DM(l), 2 * F, 0, lp, Hh(2 * l + 1), d, 0, lp, gf(lo.w_gate), d,
+               DT_F32, EPI_STORE);
+      p_mdw2 = gemm_phase(g, {p_ddx}, "gate_up_dw");
+    } else {
+      g = gemm(h, (int)BT, (int)F, (int)d, dxo, d, 1, lp, wc(lo.w_proj), F, 0, lp, DM(l), F, lp, EPI_DGELU);
+      g.aux = M1(l);
+      g.ldaux = F;
+      g.aux_dt = lp;
+      int p_pdx = gemm_phase(g, {cur_dx}, "proj_dx");
+      g = gemm(h, (int)d, (int)F, (int)BT, dxo, d, 0, lp, M2(l), F, 0, lp, gf(lo.w_proj), F, DT_F32, EPI_STORE);
+      gemm_phase(g, {cur_dx}, "proj_dw");
+      g = gemm(h, (int)BT, (int)d, (int)F, DM(l), F, 1, lp, wc(lo.w_fc), d, 0, lp, DLN(2 * l + 1), d, DT_F32,
+               EPI_STORE);
+      p_mdx = gemm_phase(g, {p_pdx}, "fc_dx");
+      g = gemm(h, (int)F, (int)d, (int)BT, DM(l), F, 0, lp, Hh(2 * l + 1), d, 0, lp, gf(lo.w_fc), d, DT_F32,
+               EPI_STORE);
+      p_mdw2 = gemm_phase(g, {p_pdx}, "fc_dw");
+      if (c.has_bias) colsum(DM(l), F, (int)F, CSF(l), gf(lo.b_fc), p_pdx, "fc_bias_sum");
+    }
+    (void)p_mdw2;
+    int p_ln2b = ln_bwd(2 * l + 1, lo.ln2_g, ri, {p_mdx}, "ln2_bwd");
+    ln_red(2 * l + 1, p_ln2b, gf(lo.ln2_g), gf(lo.ln2_b), c.has_bias ? gf(lo.b_o) : nullptr, "ln2_params");
+    void* dxm = DXLP(2 * l + 1);
+    g = gemm(h, (int)BT, (int)d, (int)d, dxm, d, 1, lp, wc(lo.w_o), d, 0, lp, DOUT(l), d, lp, EPI_STORE);
+    int p_odx = gemm_phase(g, {p_ln2b}, "attn_out_dx");
+    g = gemm(h, (int)d, (int)d, (int)BT, dxm, d, 0, lp, O(l), d, 0, lp, gf(lo.w_o), d, DT_F32, EPI_STORE);
+    gemm_phase(g, {p_ln2b}, "attn_out_dw");
+    int p_prep = b.add(OP_ATTN_PREP, cdiv(BT, 16), "attn_prep", {p_odx});
+    b[p_prep].a.attn = attn_args(l);
+    b[p_prep].a.attn.block = 16;
+    int p_kv = b.add(OP_ATTN_BWD_KV, attn_tiles, "attn_bwd_kv", {p_prep});
+    b[p_kv].a.attn = attn_args(l);
+    int p_q = b.add(OP_ATTN_BWD_Q, attn_tiles, "attn_bwd_q", {p_prep});
+    b[p_q].a.attn = attn_args(l);
+    int p_dqkv = p_q;
+    if (c.n_pos == 0) {
+      int p = b.add(OP_ROPE_BWD, cdiv(BT, 16), "rope_bwd", {p_kv, p_q});
+      b[p].a.rope = rope_args(DQKV(l));
+      p_dqkv = p;
+    }
+      g = gemm(h, (int)BT, (int)d, (int)(3 * d), DQKV(l), 3 * d, 1, lp, wc(lo.w_qkv), d, 0, lp, DLN(2 * l), d, DT_F32,
+             EPI_STORE);
+    int p_qdx = gemm_phase(g, {p_dqkv, p_kv}, "qkv_dx");
+    g = gemm(h, (int)(3 * d), (int)d, (int)BT, DQKV(l), 3 * d, 0, lp, Hh(2 * l), d, 0, lp, gf(lo.w_qkv), d, DT_F32,
+             EPI_STORE);
+    gemm_phase(g, {p_dqkv, p_kv}, "qkv_dw");
+    if (c.has_bias) colsum(DQKV(l), 3 * d, (int)(3 * d), CSQ(l), gf(lo.b_qkv), p_dqkv, "qkv_bias_sum");
+    int p_ln1b = ln_bwd(2 * l, lo.ln1_g, 2 * l + 1, {p_qdx}, "ln1_bwd");
+    float* prev_bias = (c.has_bias && l > 0) ? gf(h->lay.layer[l - 1].b_proj) : nullptr;
+    ln_red(2 * l, p_ln1b, gf(lo.ln1_g), gf(lo.ln1_b), prev_bias, "ln1_params");
+    cur_dx = p_ln1b;
+  }
+  int v_rows = 64;
+  int v_tiles = cdiv(V, v_rows);
+  int pos_tiles = c.n_pos ? cdiv(c.n_pos, v_rows) : 0;
+  int p_eb = b.add(OP_EMB_BWD, v_tiles + pos_tiles, "emb_bwd", {cur_dx, p_sort, p_head_dw});
+  {
+    EmbBwdArgs& a = b[p_eb].a.ebwd;
+    a.dx0 = DX(0);
+    a.sorted = at<int32_t>(ws, w.esorted);
+    a.first = at<uint64_t>(ws, w.efirst);
+    a.dwte = gf(h->lay.wte);
+    a.dwpe = gf(h->lay.wpe);
+    a.B = (int)D.B;
+    a.T = (int)D.T;
+    a.d = (int)d;
+    a.V = (int)V;
+    a.n_pos = c.n_pos;
+    a.accumulate = c.tied_head ? 1 : 0;
+    a.rows_per_tile = v_rows;
+    a.v_tiles = v_tiles;
+  }
+  const int adam_chunk = 16384;
+  int p_adam = b.add(OP_ADAMW, cdiv(D.P, adam_chunk), "adamw", {-2});
+  {
+    AdamArgs& a = b[p_adam].a.adam;
+    a.p = P;
+    a.g = G;
+    a.m = at<float>(ws, w.m);
+    a.v = at<float>(ws, w.v);
+    a.wc = c.precision == OFA_BF16 ? (void*)(ws + w.wc) : nullptr;
+    a.wc_dt = lp;
+    a.n = D.P;
+    a.per_tile = adam_chunk;
+    a.beta1 = c.beta1;
+    a.beta2 = c.beta2;
+    a.eps = c.eps;
+    a.wd = c.weight_decay;
+  }
+  // the next step's forward overwrites activations this step's backward reads
+  b[p_emb].dep_prev = p_adam;
+  b[p_sort].dep_prev = p_adam;
+  // tile prefix sums
+  int acc = 0;
+  for (auto& ph : h->train) {
+    ph.tile_base = acc;
+    acc += ph.n_tiles;
+    ph.lds_bytes = (int)phase_lds_bytes(ph);
+  }
+}
+
+// decode program for one position (head phases skip themselves when the
+// instance has no head)
+void build_decode(ofa_handle* h) {
+  const ofa_config& c = h->cfg;
+  const Dims& D = h->D;
+  const Carve& w = h->cw;
+  char* ws = h->ws;
+  h->dec.clear();
+  Builder b{&h->dec, nullptr};
+  const int lp = D.lp_dt;
+  const int64_t d = D.d, F = D.F, V = D.V;
+  char* S = ws + w.serve;   // slot 0
+  auto sw = [&](int64_t off) -> const void* { return off < 0 ? nullptr : S + off * D.lp; };
+  float* dx = at<float>(ws, w.dx);
+  auto XV = [&](int i) { return dx + (int64_t)i * d; };
+  DecState* st = at<DecState>(ws, w.dstate);
+  const int64_t slot_bytes = w.n_slots > 1 ? D.P * D.lp : 0;
+  int p_emb = b.add(OP_DEC_EMBED, 1, "dec_embed");
+  {
+    DecEmbedArgs& a = b[p_emb].a.dembed;
+    a.wte = sw(h->lay.wte);
+    a.wpe = sw(h->lay.wpe);
+    a.ctx_tok = at<int32_t>(ws, w.ctx_tok);
+    a.x = XV(0);
+    a.st = st;
+    a.published = at<uint64_t>(ws, w.published);
+    a.slot_bytes = slot_bytes;
+    a.d = (int)d;
+    a.V = (int)V;
+    a.w_dt = lp;
+  }
+  auto gemv = [&](int dep, const void* W, const void* bias, const float* xin, const void* lg, const void* lb, float* y,
+                  int N, int K, int epi, int rpt) {
+    int n_rows = epi == DEPI_GEGLU ? (int)F : N;
+    int p = b.add(OP_DEC_GEMV, cdiv(n_rows, rpt), "dec_gemv", {dep});
+    DecGemvArgs& a = b[p].a.dgemv;
+    a.W = W;
+    a.bias = bias;
+    a.xin = xin;
+    a.ln_g = lg;
+    a.ln_b = lb;
+    a.y = y;
+    a.st = st;
+    a.N = N;
+    a.K = K;
+    a.w_dt = lp;
+    a.kv_dt = lp;
+    a.epi = epi;
+    a.rows_per_tile = rpt;
+    a.d = (int)d;
+    a.H = (int)D.H;
+    a.dh = (int)D.dh;
+    a.cap = (int)D.win;
+    a.rope = c.n_pos == 0;
+    a.F = (int)F;
+    a.io = at<DecIO>(ws, w.misc + kMiscDecIO);
+    return p;
+  };
+  int last = p_emb;
+  for (int l = 0; l < D.L; ++l) {
+    const LayerOff& lo = h->lay.layer[l];
+    void* kv = ws + w.kv + (size_t)l * 2 * D.H * D.win * D.dh * D.lp;
+    int p_qkv = gemv(last, sw(lo.w_qkv), sw(lo.b_qkv), XV(2 * l), sw(lo.ln1_g), sw(lo.ln1_b), at<float>(ws, w.dq),
+                     (int)(3 * d), (int)d, DEPI_QKV, (int)D.dh);
+    b[p_qkv].a.dgemv.kv = kv;
+    int p_att = b.add(OP_DEC_ATTN, (int)D.H, "dec_attn", {p_qkv});
+    {
+      DecAttnArgs& a = b[p_att].a.dattn;
+      a.q = at<float>(ws, w.dq);
+      a.kv = kv;
+      a.o = at<float>(ws, w.dvo) + l * d;
+      a.H = (int)D.H;
+      a.dh = (int)D.dh;
+      a.cap = (int)D.win;
+      a.kv_dt = lp;
+    }
+    int p_o = gemv(p_att, sw(lo.w_o), sw(lo.b_o), at<float>(ws, w.dvo) + l * d, nullptr, nullptr, XV(2 * l + 1),
+                   (int)d, (int)d, DEPI_RESID, 16);
+    b[p_o].a.dgemv.resid = XV(2 * l);
+    float* act = at<float>(ws, w.dmlp_v) + l * F;
+    int p_fc;
+    if (c.mlp_gated)
+      p_fc = gemv(p_o, sw(lo.w_gate), nullptr, XV(2 * l + 1), sw(lo.ln2_g), sw(lo.ln2_b), act, (int)(2 * F), (int)d,
+                  DEPI_GEGLU, 16);
+    else
+      p_fc = gemv(p_o, sw(lo.w_fc), sw(lo.b_fc), XV(2 * l + 1), sw(lo.ln2_g), sw(lo.ln2_b), act, (int)F, (int)d,
+                  DEPI_GELU, 16);
+    int p_pr = gemv(p_fc, sw(c.mlp_gated ? lo.w_down : lo.w_proj), sw(lo.b_proj), act, nullptr, nullptr,
+                    XV(2 * l + 2), (int)d, (int)F, DEPI_RESID, 16);
+    b[p_pr].a.dgemv.resid = XV(2 * l + 1);
+    last = p_pr;
+  }
+  const int64_t w_lm = c.tied_head ? h->lay.wte : h->lay.w_lm;
+  int p_lm = gemv(last, sw(w_lm), nullptr, XV(2 * (int)D.L), sw(h->lay.lnf_g), sw(h->lay.lnf_b),
+                  at<float>(ws, w.dlogits), (int)V, (int)d, DEPI_LOGITS, 16);
+  int p_am = b.add(OP_DEC_ARGMAX, 1, "dec_argmax", {p_lm});
+  {
+    DecArgmaxArgs& a = b[p_am].a.dargmax;
+    a.logits = at<float>(ws, w.dlogits);
+    a.ctx_tok = at<int32_t>(ws, w.ctx_tok);
+    a.st = st;
+    a.io = at<DecIO>(ws, w.misc + kMiscDecIO);
+    a.V = (int)V;
+    a.cap = (int)D.win;
+    a.keep = (int)D.keep;
+  }
+  b[p_emb].dep_prev = p_am;
+  int acc = 0;
+  for (auto& ph : h->dec) {
+    ph.tile_base = acc;
+    acc += ph.n_tiles;
+    ph.lds_bytes = (int)phase_lds_bytes(ph);
+  }
+}
+
+double lr_at(const ofa_config& c, uint64_t step) {
+  if (c.lr_schedule == OFA_LR_COSINE)
+    return c.lr * 0.5 * (1.0 + std::cos(M_PI * (double)step / (double)c.total_steps));
+  return c.lr;
+}
+
+ofa_status check_sticky(ofa_handle* h) {
+  if (h->sticky) return fail(h, (ofa_status)h->sticky, "an earlier call left device status %d", h->sticky);
+  return OFA_OK;
+}
+
+ofa_status upload(ofa_handle* h, void* dst, const void* src, size_t bytes) {
+  HIP_TRY(h, hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, h->stream));
+  return OFA_OK;
+}
+
+// waits until the previous upload from the pinned staging area has been consumed
+ofa_status staging_ready(ofa_handle* h) {
+  if (h->upload_pending) {
+    HIP_TRY(h, hipEventSynchronize(h->ev_upload));
+    h->upload_pending = false;
+  }
+  return OFA_OK;
+}
+
+ofa_status mark_upload(ofa_handle* h) {
+  HIP_TRY(h, hipEventRecord(h->ev_upload, h->stream));
+  h->upload_pending = true;
+  return OFA_OK;
+}
+
+ofa_status run_launch_per_phase(ofa_handle* h, const std::vector<Phase>& prog, const Phase* d_prog,
+                                const StepCtx* d_ctx, int64_t n_inst, int64_t step0, bool dec_head_gate) {
+  DevStatus* st = at<DevStatus>(h->ws, h->cw.status);
+  PhaseTime* tm = at<PhaseTime>(h->ws, dec_head_gate ? h->cw.dtimes : h->cw.times);
+  for (int64_t s = 0; s < n_inst; ++s) {
+    const bool head = dec_head_gate ? (h->h_dsteps[s].head & 1) != 0 : true;
+    for (size_t i = 0; i < prog.size(); ++i) {
+      if (dec_head_gate && !head && (prog[i].op == OP_DEC_ARGMAX || (prog[i].op == OP_DEC_GEMV &&
+                                                                     prog[i].a.dgemv.epi == DEPI_LOGITS)))
+        continue;
+      HIP_TRY(h, launch_phase(prog[i], d_prog, (int)i, d_ctx + s, st, tm, step0 + s, h->stream));
+    }
+  }
+  return OFA_OK;
+}
+
+}  // namespace
+
+// =====================================================================  C ABI
+
+static ofa_status publish(ofa_handle* h);
+static ofa_status copy_flat(ofa_handle* h, const void* src, int sdt, void* dst, int ddt, int64_t n);
+
+extern "C" {
+
+ofa_status ofa_validate_config(const ofa_config* cfg, char* msg, size_t msg_len) {
+  if (!cfg) return OFA_E_ARG;
+  std::string e = validate(*cfg);
+  if (e.empty()) return OFA_OK;
+  if (msg && msg_len) {
+    strncpy(msg, e.c_str(), msg_len - 1);
+    msg[msg_len - 1] = 0;
+  }
+  return OFA_E_ARG;
+}
+
+size_t ofa_workspace_bytes(const ofa_config* cfg) {
+  if (!cfg || !validate(*cfg).empty()) return 0;
+  Layout L = make_layout(*cfg);
+  return carve(*cfg, L).total;
+}
+
+int64_t ofa_param_count(const ofa_config* cfg) {
+  if (!cfg || !validate(*cfg).empty()) return -1;
+  return make_layout(*cfg).total;
+}
+
+int32_t ofa_param_tensor_count(const ofa_config* cfg) {
+  if (!cfg || !validate(*cfg).empty()) return -1;
+  return (int32_t)make_layout(*cfg).t.size();
+}
+
+ofa_status ofa_param_tensor(const ofa_config* cfg, int32_t i, int64_t* offset, int64_t* numel, int32_t* kind,
+                            char* name, size_t name_len) {
+  if (!cfg || !validate(*cfg).empty()) return OFA_E_ARG;
+  Layout L = make_layout(*cfg);
+  if (i < 0 || i >= (int32_t)L.t.size()) return OFA_E_ARG;
+  const TensorDesc& t = L.t[i];
+  if (offset) *offset = t.off;
+  if (numel) *numel = t.numel;
+  if (kind) *kind = t.kind;
+  if (name && name_len) {
+    strncpy(name, t.name.c_str(), name_len - 1);
+    name[name_len - 1] = 0;
+  }
+  return OFA_OK;
+}
+
+ofa_status ofa_task_budget(uint64_t iterations, uint64_t tasks_per_unit, uint64_t* out) {
+  if (!out) return OFA_E_ARG;
+  if (tasks_per_unit && iterations > (uint64_t)INT64_MAX / tasks_per_unit) return OFA_E_OVERFLOW;
+  *out = iterations * tasks_per_unit;
+  return OFA_OK;
+}
+
+const char* ofa_status_string(ofa_status s) {
+  switch (s) {
+    case OFA_OK: return "ok";
+    case OFA_E_ARG: return "invalid argument";
+    case OFA_E_HIP: return "HIP runtime error";
+    case OFA_E_NONFINITE: return "non-finite value";
+    case OFA_E_TIMEOUT: return "device wait timed out";
+    case OFA_E_OVERFLOW: return "budget overflow";
+    case OFA_E_STATE: return "invalid state";
+  }
+  return "unknown";
+}
+
+const char* ofa_last_error(const ofa_handle* h) { return h ? h->err.c_str() : "null handle"; }
+
+ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_bytes, const float* dev_init_params,
+                      void* hip_stream, ofa_handle** out) {
+  if (!cfg || !out || !dev_workspace || !dev_init_params) return OFA_E_ARG;
+  *out = nullptr;
+  if (!validate(*cfg).empty()) return OFA_E_ARG;
+  if ((uintptr_t)dev_workspace % kAlign) return OFA_E_ARG;
+  ofa_handle* h = new ofa_handle();
+  h->cfg = *cfg;
+  h->lay = make_layout(*cfg);
+  h->D = dims_of(*cfg, h->lay);
+  h->cw = carve(*cfg, h->lay);
+  if (ws_bytes < h->cw.total) {
+    delete h;
+    return OFA_E_ARG;
+  }
+  h->ws = (char*)dev_workspace;
+  h->stream = (hipStream_t)hip_stream;
+  *out = h;
+  static bool kernels_ready = false;
+  if (!kernels_ready) {
+    HIP_TRY(h, init_kernels());
+    kernels_ready = true;
+  }
+  int dev = 0;
+  HIP_TRY(h, hipGetDevice(&dev));
+  HIP_TRY(h, hipDeviceGetAttribute(&h->n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  if (h->cfg.train_cus > h->n_cu || h->cfg.serve_cus > h->n_cu || h->cfg.train_cus + h->cfg.serve_cus > h->n_cu)
+    return fail(h, OFA_E_ARG, "CU partition %d + %d exceeds the device's %d CUs", h->cfg.train_cus,
+                h->cfg.serve_cus, h->n_cu);
+  HIP_TRY(h, hipHostMalloc((void**)&h->h_steps, sizeof(StepCtx) * kMaxSteps, hipHostMallocDefault));
+  HIP_TRY(h, hipHostMalloc((void**)&h->h_dsteps, sizeof(StepCtx) * kMaxDecInst, hipHostMallocDefault));
+  HIP_TRY(h, hipHostMalloc((void**)&h->h_misc, kMiscBytes, hipHostMallocDefault));
+  HIP_TRY(h, hipEventCreateWithFlags(&h->ev_upload, hipEventDisableTiming));
+  HIP_TRY(h, hipEventCreate(&h->ev_t0));
+  HIP_TRY(h, hipEventCreate(&h->ev_t1));
+  build_train(h);
+  build_decode(h);
+  if (h->train.size() > (size_t)kMaxPhases || h->dec.size() > (size_t)kMaxPhases)
+    return fail(h, OFA_E_ARG, "program too long");
+  // phase tables live in a small library-owned device buffer
+  size_t tbytes = (h->train.size() + h->dec.size()) * sizeof(Phase);
+  HIP_TRY(h, hipMalloc(&h->d_alloc, tbytes));
+  h->d_train = (Phase*)h->d_alloc;
+  h->d_dec = h->d_train + h->train.size();
+  HIP_TRY(h, hipMemcpy(h->d_train, h->train.data(), h->train.size() * sizeof(Phase), hipMemcpyHostToDevice));
+  HIP_TRY(h, hipMemcpy(h->d_dec, h->dec.data(), h->dec.size() * sizeof(Phase), hipMemcpyHostToDevice));
+  // state
+  char* ws = h->ws;
+  const Carve& w = h->cw;
+  const size_t P = h->D.P;
+  HIP_TRY(h, hipMemcpyAsync(ws + w.p, dev_init_params, P * 4, hipMemcpyDeviceToDevice, h->stream));
+  HIP_TRY(h, launch_fill_u32(at<uint32_t>(ws, w.m), 0, (int64_t)P, h->stream));
+  HIP_TRY(h, launch_fill_u32(at<uint32_t>(ws, w.v), 0, (int64_t)P, h->stream));
+  HIP_TRY(h, launch_fill_u32(at<uint32_t>(ws, w.g), 0, (int64_t)P, h->stream));
+  HIP_TRY(h, launch_fill_u64(at<uint64_t>(ws, w.efirst), 0, h->D.V, h->stream));
+  HIP_TRY(h, launch_fill_u32((uint32_t*)at<DevStatus>(ws, w.status), 0, sizeof(DevStatus) / 4, h->stream));
+  HIP_TRY(h, launch_fill_u64(at<uint64_t>(ws, w.published), 0, 8, h->stream));
+  HIP_TRY(h, launch_fill_u32((uint32_t*)at<DecState>(ws, w.dstate), 0, sizeof(DecState) / 4, h->stream));
+  ofa_status s = ofa_set_params(h, at<float>(ws, w.p));
+  if (s != OFA_OK) return s;
+  h->version = 0;   // the initial weights are version 0
+  return publish(h);
+}
+
+ofa_status ofa_destroy(ofa_handle* h) {
+  if (!h) return OFA_E_ARG;
+  (void)hipStreamSynchronize(h->stream);
+  if (h->h_steps) (void)hipHostFree(h->h_steps);
+  if (h->h_dsteps) (void)hipHostFree(h->h_dsteps);
+  if (h->h_misc) (void)hipHostFree(h->h_misc);
+  if (h->ev_upload) (void)hipEventDestroy(h->ev_upload);
+  if (h->ev_t0) (void)hipEventDestroy(h->ev_t0);
+  if (h->ev_t1) (void)hipEventDestroy(h->ev_t1);
+  if (h->d_alloc) (void)hipFree(h->d_alloc);
+  delete h;
+  return OFA_OK;
+}
+
+// copy / cast a flat range with one COPY phase launched on its own
+static ofa_status copy_flat(ofa_handle* h, const void* src, int sdt, void* dst, int ddt, int64_t n) {
+  // small helper program: built on the fly into the staging slot after the phase tables
+  Phase p;
+  memset(&p, 0, sizeof p);
+  p.op = OP_COPY;
+  const int per = 65536;
+  p.n_tiles = cdiv(n, per);
+  p.a.copy.src = src;
+  p.a.copy.dst = dst;
+  p.a.copy.n = n;
+  p.a.copy.src_dt = sdt;
+  p.a.copy.dst_dt = ddt;
+  p.a.copy.per_tile = per;
+  for (int i = 0; i < kMaxDeps; ++i) p.dep[i] = -1;
+  p.dep_prev = -1;
+  static_assert(sizeof(Phase) <= kMiscDecIO, "misc block too small");
+  Phase* d_p = (Phase*)(h->ws + h->cw.misc);
+  ofa_status s = staging_ready(h);
+  if (s != OFA_OK) return s;
+  memcpy(h->h_misc, &p, sizeof p);
+  s = upload(h, d_p, h->h_misc, sizeof p);
+  if (s != OFA_OK) return s;
+  HIP_TRY(h, launch_phase(p, d_p, 0, nullptr, at<DevStatus>(h->ws, h->cw.status), nullptr, 0, h->stream));
+  return mark_upload(h);
+}
+
+ofa_status ofa_set_params(ofa_handle* h, const float* dev_params) {
+  if (!h || !dev_params) return OFA_E_ARG;
+  char* ws = h->ws;
+  const int64_t P = h->D.P;
+  if ((const char*)dev_params != ws + h->cw.p)
+    HIP_TRY(h, hipMemcpyAsync(ws + h->cw.p, dev_params, P * 4, hipMemcpyDeviceToDevice, h->stream));
+  if (h->cfg.precision == OFA_BF16) return copy_flat(h, ws + h->cw.p, DT_F32, ws + h->cw.wc, DT_BF16, P);
+  return OFA_OK;
+}
+
+ofa_status ofa_get_params(ofa_handle* h, float* dev_params) {
+  if (!h || !dev_params) return OFA_E_ARG;
+  HIP_TRY(h, hipMemcpyAsync(dev_params, h->ws + h->cw.p, h->D.P * 4, hipMemcpyDeviceToDevice, h->stream));
+  return OFA_OK;
+}
+
+ofa_status ofa_get_grads(ofa_handle* h, float* dev_grads) {
+  if (!h || !dev_grads) return OFA_E_ARG;
+  HIP_TRY(h, hipMemcpyAsync(dev_grads, h->ws + h->cw.g, h->D.P * 4, hipMemcpyDeviceToDevice, h->stream));
+  return OFA_OK;
+}
+
+// serve copy <- compute weights, then the published version number
+static ofa_status publish(ofa_handle* h) {
+  char* ws = h->ws;
+  ofa_status s = copy_flat(h, ws + h->cw.wc, h->D.lp_dt, ws + h->cw.serve, h->D.lp_dt, h->D.P);
+  if (s != OFA_OK) return s;
+  HIP_TRY(h, launch_fill_u64(at<uint64_t>(ws, h->cw.published), h->version, 1, h->stream));
+  return OFA_OK;
+}
+
+ofa_status ofa_publish_weights(ofa_handle* h, uint64_t* version_out) {
+  if (!h) return OFA_E_ARG;
+  ofa_status s = check_sticky(h);
+  if (s != OFA_OK) return s;
+  h->version += 1;
+  s = publish(h);
+  if (s != OFA_OK) return s;
+  if (version_out) *version_out = h->version;
+  return OFA_OK;
+}
+
+ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_steps, float* dev_losses) {
+  if (!h || !dev_tokens || !dev_losses || n_steps < 1) return fail(h, OFA_E_ARG, "bad arguments");
+  if (n_steps > kMaxSteps) return fail(h, OFA_E_ARG, "n_steps %d > %d", n_steps, kMaxSteps);
+  ofa_status s = check_sticky(h);
+  if (s != OFA_OK) return s;
+  const ofa_config& c = h->cfg;
+  s = staging_ready(h);
+  if (s != OFA_OK) return s;
+  const int64_t per = h->D.B * (h->D.T + 1);
+  for (int i = 0; i < n_steps; ++i) {
+    StepCtx& sc = h->h_steps[i];
+    memset(&sc, 0, sizeof sc);
+    const uint64_t t = h->steps_done + i + 1;
+    sc.tokens = dev_tokens + per * i;
+    sc.loss_out = dev_losses + i;
+    sc.lr = (float)lr_at(c, t - 1);
+    sc.bc1 = (float)(1.0 - std::pow((double)c.beta1, (double)t));
+    sc.bc2 = (float)(1.0 - std::pow((double)c.beta2, (double)t));
+    sc.step_in_call = i;
+    sc.tag = t;
+  }
+  StepCtx* d_steps = at<StepCtx>(h->ws, h->cw.steps);
+  s = upload(h, d_steps, h->h_steps, sizeof(StepCtx) * n_steps);
+  if (s != OFA_OK) return s;
+  s = mark_upload(h);
+  if (s != OFA_OK) return s;
+  const int np = (int)h->train.size();
+  // phase times: t0 <- max, t1 <- 0
+  PhaseTime* tm = at<PhaseTime>(h->ws, h->cw.times);
+  HIP_TRY(h, launch_fill_pairs((uint64_t*)tm, ~0ull, 0ull, np, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
+  if (c.exec_mode == OFA_EXEC_LAUNCH_PER_PHASE) {
+    s = run_launch_per_phase(h, h->train, h->d_train, d_steps, n_steps, (int64_t)h->steps_done, false);
+    if (s != OFA_OK) return s;
+  } else {
+    Sched* sc = at<Sched>(h->ws, h->cw.sched);
+    const uint64_t base = c.debug_counter_base;
+    HIP_TRY(h, launch_fill_u64(&sc->ticket, base, 1, h->stream));
+    HIP_TRY(h, launch_fill_u64(&sc->base, base, 1, h->stream));
+    HIP_TRY(h, launch_fill_u64(&sc->abort, 0, 2, h->stream));
+    HIP_TRY(h, launch_fill_u64(sc->done, base, np, h->stream));
+    HIP_TRY(h, launch_fill_u64(at<uint64_t>(h->ws, h->cw.inst_end), 0, n_steps, h->stream));
+    PersistParams pp;
+    memset(&pp, 0, sizeof pp);
+    pp.phases = h->d_train;
+    pp.n_phases = np;
+    pp.tiles_per_inst = h->train.back().tile_base + h->train.back().n_tiles;
+    pp.n_inst = n_steps;
+    pp.steps = d_steps;
+    pp.sched = sc;
+    pp.status = at<DevStatus>(h->ws, h->cw.status);
+    pp.times = tm;
+    pp.inst_end = at<uint64_t>(h->ws, h->cw.inst_end);
+    pp.watchdog_ticks = (c.debug_flags & OFA_DEBUG_SHORT_WATCHDOG) ? 100000ull : 1000000000ull;
+    pp.shuffle = (c.debug_flags & OFA_DEBUG_SHUFFLE_TICKETS) ? 1 : 0;
+    int occ = persistent_occupancy();
+    if (occ < 1) return fail(h, OFA_E_HIP, "persistent kernel does not fit a CU");
+    int cus = c.train_cus > 0 ? c.train_cus : h->n_cu;
+    int grid = cus * occ;
+    h->last_grid = grid;
+    HIP_TRY(h, launch_persistent(pp, grid, h->stream));
+  }
+  HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
+  h->steps_done += n_steps;
+  return OFA_OK;
+}
+
+ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_prompt, int32_t n_new,
+                            int32_t* dev_tokens_out, float* dev_logits_out, uint64_t* dev_versions_out) {
+  if (!h || n_new < 1 || !dev_tokens_out || n_prompt < 0) return fail(h, OFA_E_ARG, "bad arguments");
+  ofa_status s = check_sticky(h);
+  if (s != OFA_OK) return s;
+  const Dims& D = h->D;
+  if (n_prompt > D.win) return fail(h, OFA_E_ARG, "prompt %d longer than the window %d", n_prompt, (int)D.win);
+  if (n_prompt == 0 && !h->dec_started) return fail(h, OFA_E_STATE, "no context to continue");
+  char* ws = h->ws;
+  DecState* st = at<DecState>(ws, h->cw.dstate);
+  if (n_prompt > 0) {
+    if (!dev_prompt) return fail(h, OFA_E_ARG, "null prompt");
+    HIP_TRY(h, hipMemcpyAsync(ws + h->cw.ctx_tok, dev_prompt, n_prompt * 4, hipMemcpyDeviceToDevice, h->stream));
+    // ctx_len = n_prompt, n_gen = 0 (DecState: version, w_delta, ctx_len, n_gen)
+    HIP_TRY(h, launch_fill_u32((uint32_t*)&st->ctx_len, (uint32_t)n_prompt, 1, h->stream));
+    HIP_TRY(h, launch_fill_u32((uint32_t*)&st->n_gen, 0, 1, h->stream));
+    h->dec_ctx_len = n_prompt;
+    h->dec_processed = 0;
+    h->dec_started = true;
+  }
+  // schedule: positions to process before every emitted token (mirror of the device rule)
+  s = staging_ready(h);
+  if (s != OFA_OK) return s;
+  int64_t n_inst = 0;
+  for (int i = 0; i < n_new; ++i) {
+    for (int64_t p = h->dec_processed; p < h->dec_ctx_len; ++p) {
+      if (n_inst >= kMaxDecInst - 64) return fail(h, OFA_E_ARG, "decode call too long");
+      StepCtx& sc = h->h_dsteps[n_inst++];
+      memset(&sc, 0, sizeof sc);
+      sc.pos = (int)p;
+      sc.head = (p == h->dec_ctx_len - 1 ? 1 : 0) | (p == h->dec_processed ? 2 : 0);
+      sc.gen_idx = i;
+    }
+    h->dec_processed = h->dec_ctx_len;
+    if (h->dec_ctx_len + 1 > D.win) {
+      h->dec_ctx_len = D.keep;
+      h->dec_processed = 0;
+    } else {
+      h->dec_ctx_len += 1;
+    }
+  }
+  StepCtx* d_dsteps = at<StepCtx>(ws, h->cw.dsteps);
+  s = upload(h, d_dsteps, h->h_dsteps, sizeof(StepCtx) * n_inst);
+  if (s != OFA_OK) return s;
+  // outputs of this call
+  DecIO io{dev_tokens_out, dev_versions_out, dev_logits_out};
+  memcpy(h->h_misc + kMiscDecIO, &io, sizeof io);
+  s = upload(h, h->ws + h->cw.misc + kMiscDecIO, h->h_misc + kMiscDecIO, sizeof io);
+  if (s != OFA_OK) return s;
+  s = mark_upload(h);
+  if (s != OFA_OK) return s;
+  HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
+  s = run_launch_per_phase(h, h->dec, h->d_dec, d_dsteps, n_inst, 0, true);
+  if (s != OFA_OK) return s;
+  HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
+  return OFA_OK;
+}
+
+ofa_status ofa_train_and_serve(ofa_handle* h, const int32_t*, int32_t, float*, const int32_t*, int32_t, int32_t*,
+                               uint64_t*, int32_t, uint64_t*) {
+  return fail(h, OFA_E_STATE, "co-resident mode is not available in this build");
+}
+
+ofa_status ofa_status_sync(ofa_handle* h, ofa_stats* out) {
+  if (!h) return OFA_E_ARG;
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  DevStatus ds;
+  HIP_TRY(h, hipMemcpy(&ds, h->ws + h->cw.status, sizeof ds, hipMemcpyDeviceToHost));
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, h->ev_t0, h->ev_t1) == hipSuccess) h->last_ms = ms;
+  if (ds.code && !h->sticky) {
+    h->sticky = ds.code;
+    h->err = std::string("device status: ") + ofa_status_string((ofa_status)ds.code) +
+             " (phase " + std::to_string(ds.phase) + ", step " + std::to_string(ds.step) + ", info " +
+             std::to_string(ds.info) + ")";
+  }
+  if (out) {
+    memset(out, 0, sizeof *out);
+    out->status = ds.code;
+    out->err_phase = ds.code ? ds.phase : -1;
+    out->err_step = ds.step;
+    out->err_info = ds.info;
+    Sched sc;
+    HIP_TRY(h, hipMemcpy(&sc, h->ws + h->cw.sched, 32, hipMemcpyDeviceToHost));
+    out->tickets_claimed = sc.ticket - h->cfg.debug_counter_base;
+    out->steps_done = h->steps_done;
+    out->version = h->version;
+    out->last_call_ms = h->last_ms;
+    out->n_phases = (int32_t)h->train.size();
+    out->n_tiles_step = h->train.back().tile_base + h->train.back().n_tiles;
+    out->grid = h->last_grid;
+  }
+  return ds.code ? (ofa_status)ds.code : OFA_OK;
+}
+
+ofa_status ofa_phase_times(ofa_handle* h, uint64_t* host_t, int32_t n, int32_t* n_out, char* names,
+                           size_t name_stride) {
+  if (!h || !host_t || !n_out) return OFA_E_ARG;
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  int np = std::min<int>(n, (int)h->train.size());
+  HIP_TRY(h, hipMemcpy(host_t, h->ws + h->cw.times, np * sizeof(PhaseTime), hipMemcpyDeviceToHost));
+  if (names && name_stride)
+    for (int i = 0; i < np; ++i) {
+      strncpy(names + i * name_stride, h->train_names[i].c_str(), name_stride - 1);
+      names[i * name_stride + name_stride - 1] = 0;
+    }
+  *n_out = np;
+  return OFA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,300 @@
+// ofa_kernels.hip -- the two executors of a phase table.
+//
+// 1. launch per phase: phase_kernel<OP> runs every tile of one phase; stream
+//    order supplies the dependencies.  Used for debugging and per-kernel
+//    profiles.
+// 2. persistent: one cooperative launch; every workgroup loops claiming 64-bit
+//    tickets from one counter.  Ticket t names (instance, phase, tile) in
+//    program order, so a workgroup only ever waits on tiles with smaller
+//    tickets, all of which are already held by running workgroups: the loop
+//    cannot deadlock.  A finished tile is published with a release increment
+//    of its phase's completion counter; a dependent tile acquire-reads the
+//    counters it needs.  This is the claim / fence-then-count / acquire-wait
+//    scheme of "How one persistent kernel runs three jobs" (review page,
+//    section of the same name), with every counter 64-bit after the 32-bit
+//    budget overflow described on the A100 reproduction page ("A longer run
+//    exposed a scheduler overflow").
+#include <hip/hip_runtime.h>
+
+#include "k_simple.h"
+#include "k_mfma.h"
+#include "k_decode.h"
+#include "ofa_launch.h"
+
+namespace ofa {
+
+// ---------------------------------------------------------------- dispatch
+
+template <int OP>
+__device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCtx& tc, char* smem) {
+  if constexpr (OP == OP_EMBED) task_embed(ph.a.emb, tile, tc);
+  else if constexpr (OP == OP_LN_FWD) task_ln_fwd(ph.a.lnf, tile);
+  else if constexpr (OP == OP_GEMM) {
+    if (ph.a.gemm.impl == GEMM_MFMA) task_gemm_mfma(ph.a.gemm, tile, smem);
+    else task_gemm_simple(ph.a.gemm, tile, smem);
+  }
+  else if constexpr (OP == OP_ROPE) task_rope(ph.a.rope, tile, false);
+  else if constexpr (OP == OP_ATTN_FWD) {
+    task_attn_fwd_simple(ph.a.attn, tile, smem);
+  }
+  else if constexpr (OP == OP_GEGLU_FWD) task_geglu_fwd(ph.a.geglu, tile);
+  else if constexpr (OP == OP_CE) task_ce(ph.a.ce, tile, tc, smem);
+  else if constexpr (OP == OP_LOSS) task_loss(ph.a.loss, tc, smem);
+  else if constexpr (OP == OP_LN_BWD) task_ln_bwd(ph.a.lnb, tile, smem);
+  else if constexpr (OP == OP_COLSUM) task_colsum(ph.a.cs, tile);
+  else if constexpr (OP == OP_COLRED) task_colred(ph.a.cr, tile);
+  else if constexpr (OP == OP_ATTN_PREP) task_attn_prep(ph.a.attn, tile);
+  else if constexpr (OP == OP_ATTN_BWD_KV) {
+    task_attn_bwd_kv_simple(ph.a.attn, tile, smem);
+  }
+  else if constexpr (OP == OP_ATTN_BWD_Q) {
+    task_attn_bwd_q_simple(ph.a.attn, tile, smem);
+  }
+  else if constexpr (OP == OP_ROPE_BWD) task_rope(ph.a.rope, tile, true);
+  else if constexpr (OP == OP_EMB_SORT) task_emb_sort(ph.a.esort, tc, smem);
+  else if constexpr (OP == OP_EMB_BWD) task_emb_bwd(ph.a.ebwd, tile, tc);
+  else if constexpr (OP == OP_ADAMW) task_adamw(ph.a.adam, tile, tc);
+  else if constexpr (OP == OP_COPY) task_copy(ph.a.copy, tile);
+  else if constexpr (OP == OP_DEC_EMBED) task_dec_embed(ph.a.dembed, tile, tc);
+  else if constexpr (OP == OP_DEC_GEMV) task_dec_gemv(ph.a.dgemv, tile, tc, smem);
+  else if constexpr (OP == OP_DEC_ATTN) task_dec_attn(ph.a.dattn, tile, tc, smem);
+  else if constexpr (OP == OP_DEC_ARGMAX) task_dec_argmax(ph.a.dargmax, tile, tc, smem);
+}
+
+__device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& tc, char* smem) {
+  switch (ph.op) {
+#define OFA_CASE(X) case X: run_task<X>(ph, tile, tc, smem); break;
+    OFA_CASE(OP_EMBED) OFA_CASE(OP_LN_FWD) OFA_CASE(OP_GEMM) OFA_CASE(OP_ROPE)
+    OFA_CASE(OP_ATTN_FWD) OFA_CASE(OP_GEGLU_FWD) OFA_CASE(OP_CE) OFA_CASE(OP_LOSS)
+    OFA_CASE(OP_LN_BWD) OFA_CASE(OP_COLSUM) OFA_CASE(OP_COLRED) OFA_CASE(OP_ATTN_PREP)
+    OFA_CASE(OP_ATTN_BWD_KV) OFA_CASE(OP_ATTN_BWD_Q) OFA_CASE(OP_ROPE_BWD) OFA_CASE(OP_EMB_SORT)
+    OFA_CASE(OP_EMB_BWD) OFA_CASE(OP_ADAMW) OFA_CASE(OP_COPY) OFA_CASE(OP_DEC_EMBED)
+    OFA_CASE(OP_DEC_GEMV) OFA_CASE(OP_DEC_ATTN) OFA_CASE(OP_DEC_ARGMAX)
+#undef OFA_CASE
+    default: break;
+  }
+}
+
+// ---------------------------------------------------------------- executor 1: one launch per phase
+
+template <int OP>
+__global__ __launch_bounds__(kThreads) void phase_kernel(const Phase* phases, int idx, const StepCtx* sc,
+                                                         DevStatus* status, PhaseTime* times, int64_t step) {
+  extern __shared__ __align__(16) char smem[];
+  const Phase& ph = phases[idx];
+  TaskCtx tc{sc, status, idx, step};
+  const uint64_t t0 = now_ticks();
+  for (int tile = blockIdx.x; tile < ph.n_tiles; tile += gridDim.x) run_task<OP>(ph, tile, tc, smem);
+  if (times && threadIdx.x == 0) {
+    atomicMin((unsigned long long*)&times[idx].t0, (unsigned long long)t0);
+    atomicMax((unsigned long long*)&times[idx].t1, (unsigned long long)now_ticks());
+  }
+}
+
+// ---------------------------------------------------------------- executor 2: persistent
+
+__device__ __forceinline__ bool wait_count(const uint64_t* ctr, uint64_t need, const PersistParams& p,
+                                           const TaskCtx& tc) {
+  const uint64_t start = now_ticks();
+  int spins = 0;
+  while (ld_acquire(ctr) < need) {
+    if (ld_relaxed(&p.sched->abort)) return false;
+    if (++spins > 64) {
+      __builtin_amdgcn_s_sleep(2);
+      if ((spins & 255) == 0 && now_ticks() - start > p.watchdog_ticks) {
+        raise_status(p.status, -4 /*OFA_E_TIMEOUT*/, tc.phase, tc.step, (int64_t)need);
+        st_release(&p.sched->abort, 1);
+        return false;
+      }
+    }
+  }
+  return true;
+}
+
+__global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
+  extern __shared__ __align__(16) char smem[];
+  __shared__ uint64_t s_ticket;
+  __shared__ int s_ok;
+  const uint64_t base = p.sched->base;
+  const uint64_t total = (uint64_t)p.n_inst * (uint64_t)p.tiles_per_inst;
+  for (;;) {
+    if (threadIdx.x == 0) s_ticket = add_relaxed(&p.sched->ticket, 1) - base;
+    __syncthreads();
+    const uint64_t t = s_ticket;
+    if (t >= total) break;
+    const int64_t inst = (int64_t)(t / (uint64_t)p.tiles_per_inst);
+    const int r = (int)(t % (uint64_t)p.tiles_per_inst);
+    // phase owning tile r: last phase whose tile_base <= r
+    int lo = 0, hi = p.n_phases - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (p.phases[mid].tile_base <= r) lo = mid; else hi = mid - 1;
+    }
+    const int pi = lo;
+    const Phase& ph = p.phases[pi];
+    int tile = r - ph.tile_base;
+    if (p.shuffle && ph.n_tiles > 1) {
+      // reversal after a rotation: a permutation of the phase's tiles
+      const int rot = (int)(((uint64_t)inst * 977u + 31u) % (uint64_t)ph.n_tiles);
+      tile = ph.n_tiles - 1 - (tile + rot) % ph.n_tiles;
+    }
+    TaskCtx tc{p.steps + inst, p.status, pi, inst};
+    // wait for dependencies (thread 0), then acquire for the whole workgroup
+    if (threadIdx.x == 0) {
+      bool ok = true;
+      for (int d = 0; d < kMaxDeps && ok; ++d) {
+        int q = ph.dep[d];
+        if (q == -2) {
+          for (int qq = 0; qq < pi && ok; ++qq)
+            ok = wait_count(&p.sched->done[qq], base + (uint64_t)(inst + 1) * p.phases[qq].n_tiles, p, tc);
+        } else if (q >= 0) {
+          ok = wait_count(&p.sched->done[q], base + (uint64_t)(inst + 1) * p.phases[q].n_tiles, p, tc);
+        }
+      }
+      if (ok && ph.dep_prev >= 0 && inst > 0)
+        ok = wait_count(&p.sched->done[ph.dep_prev], base + (uint64_t)inst * p.phases[ph.dep_prev].n_tiles, p, tc);
+      s_ok = ok ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_ok) break;
+    fence_acquire_agent();
+    const uint64_t t0 = now_ticks();
+    run_any(ph, tile, tc, smem);
+    // publish: every thread's writes are complete and visible at agent scope
+    // before the completion counter moves
+    fence_release_agent();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      add_release(&p.sched->done[pi], 1);
+      if (p.times) {
+        atomicMin((unsigned long long*)&p.times[pi].t0, (unsigned long long)t0);
+        atomicMax((unsigned long long*)&p.times[pi].t1, (unsigned long long)now_ticks());
+      }
+      if (p.inst_end) atomicMax((unsigned long long*)&p.inst_end[inst], (unsigned long long)now_ticks());
+    }
+  }
+  if (threadIdx.x == 0) add_relaxed(&p.sched->exited, 1);
+}
+
+// ---------------------------------------------------------------- small utility kernels
+
+__global__ void fill_u64_kernel(uint64_t* p, uint64_t v, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+__global__ void fill_pairs_kernel(uint64_t* p, uint64_t a, uint64_t b, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    p[2 * i] = a;
+    p[2 * i + 1] = b;
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+static size_t lds_for(const Phase& ph) {
+  switch (ph.op) {
+    case OP_GEMM: return ph.a.gemm.impl == GEMM_MFMA ? gemm_mfma_lds_bytes() : sizeof(GemmSmemSimple);
+    case OP_LN_BWD: return (size_t)kWaves * 3 * ph.a.lnb.d * sizeof(float);
+    case OP_ATTN_FWD:
+      return (size_t)kWaves * (64 + ph.a.attn.T) * sizeof(float);
+    case OP_ATTN_BWD_KV:
+      return (size_t)kWaves * 256 * sizeof(float);
+    case OP_ATTN_BWD_Q:
+      return (size_t)kWaves * 192 * sizeof(float);
+    case OP_CE: case OP_LOSS: return 64;
+    case OP_EMB_SORT: {
+      int n = 1;
+      while (n < ph.a.esort.BT) n <<= 1;
+      return (size_t)n * sizeof(uint64_t);
+    }
+    case OP_DEC_GEMV: return dec_gemv_lds_bytes(ph.a.dgemv);
+    case OP_DEC_ATTN: return dec_attn_lds_bytes(ph.a.dattn);
+    case OP_DEC_ARGMAX: return 2048;
+    default: return 0;
+  }
+}
+
+size_t phase_lds_bytes(const Phase& ph) { return lds_for(ph); }
+
+static constexpr size_t kPersistLds = 96 * 1024;
+size_t persistent_lds_bytes() { return kPersistLds; }
+
+template <int OP>
+static hipError_t set_attr() {
+  return hipFuncSetAttribute((const void*)phase_kernel<OP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             160 * 1024);
+}
+
+hipError_t init_kernels() {
+  hipError_t e = hipSuccess;
+#define OFA_ATTR(X) if (e == hipSuccess) e = set_attr<X>();
+  OFA_ATTR(OP_EMBED) OFA_ATTR(OP_LN_FWD) OFA_ATTR(OP_GEMM) OFA_ATTR(OP_ROPE) OFA_ATTR(OP_ATTN_FWD)
+  OFA_ATTR(OP_GEGLU_FWD) OFA_ATTR(OP_CE) OFA_ATTR(OP_LOSS) OFA_ATTR(OP_LN_BWD) OFA_ATTR(OP_COLSUM)
+  OFA_ATTR(OP_COLRED) OFA_ATTR(OP_ATTN_PREP) OFA_ATTR(OP_ATTN_BWD_KV) OFA_ATTR(OP_ATTN_BWD_Q)
+  OFA_ATTR(OP_ROPE_BWD) OFA_ATTR(OP_EMB_SORT) OFA_ATTR(OP_EMB_BWD) OFA_ATTR(OP_ADAMW) OFA_ATTR(OP_COPY)
+  OFA_ATTR(OP_DEC_EMBED) OFA_ATTR(OP_DEC_GEMV) OFA_ATTR(OP_DEC_ATTN) OFA_ATTR(OP_DEC_ARGMAX)
+#undef OFA_ATTR
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)persistent_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kPersistLds);
+  return e;
+}
+
+int persistent_occupancy() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, persistent_kernel, kThreads, kPersistLds) != hipSuccess)
+    return 0;
+  return n;
+}
+
+hipError_t launch_phase(const Phase& h, const Phase* d_phases, int idx, const StepCtx* d_sc, DevStatus* st,
+                        PhaseTime* tm, int64_t step, hipStream_t s) {
+  if (h.n_tiles <= 0) return hipSuccess;
+  const int grid = h.n_tiles;
+  const size_t lds = lds_for(h);
+  switch (h.op) {
+#define OFA_LAUNCH(X) \
+  case X: hipLaunchKernelGGL(phase_kernel<X>, dim3(grid), dim3(kThreads), lds, s, d_phases, idx, d_sc, st, tm, step); break;
+    OFA_LAUNCH(OP_EMBED) OFA_LAUNCH(OP_LN_FWD) OFA_LAUNCH(OP_GEMM) OFA_LAUNCH(OP_ROPE)
+    OFA_LAUNCH(OP_ATTN_FWD) OFA_LAUNCH(OP_GEGLU_FWD) OFA_LAUNCH(OP_CE) OFA_LAUNCH(OP_LOSS)
+    OFA_LAUNCH(OP_LN_BWD) OFA_LAUNCH(OP_COLSUM) OFA_LAUNCH(OP_COLRED) OFA_LAUNCH(OP_ATTN_PREP)
+    OFA_LAUNCH(OP_ATTN_BWD_KV) OFA_LAUNCH(OP_ATTN_BWD_Q) OFA_LAUNCH(OP_ROPE_BWD) OFA_LAUNCH(OP_EMB_SORT)
+    OFA_LAUNCH(OP_EMB_BWD) OFA_LAUNCH(OP_ADAMW) OFA_LAUNCH(OP_COPY) OFA_LAUNCH(OP_DEC_EMBED)
+    OFA_LAUNCH(OP_DEC_GEMV) OFA_LAUNCH(OP_DEC_ATTN) OFA_LAUNCH(OP_DEC_ARGMAX)
+#undef OFA_LAUNCH
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_persistent(const PersistParams& p, int grid, hipStream_t s) {
+  void* args[] = {(void*)&p};
+  return hipLaunchCooperativeKernel((const void*)persistent_kernel, dim3(grid), dim3(kThreads), args,
+                                    kPersistLds, s);
+}
+
+hipError_t launch_fill_u64(uint64_t* p, uint64_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int grid = (int)std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(grid), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int grid = (int)std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_pairs(uint64_t* p, uint64_t a, uint64_t b, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int grid = (int)std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_pairs_kernel, dim3(grid), dim3(256), 0, s, p, a, b, n);
+  return hipGetLastError();
+}
+
+}  // namespace ofa

@@ -1,0 +1,37 @@
+// ofa_launch.h -- host-side entry points of the device code (ofa_kernels.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "ofa_types.h"
+
+namespace ofa {
+
+// Everything the persistent kernel reads; passed by value.
+struct PersistParams {
+  const Phase* phases;       // one program instance's phase table
+  int32_t n_phases;
+  int32_t tiles_per_inst;    // sum of n_tiles over the phases
+  int64_t n_inst;            // instances (training steps) to run
+  const StepCtx* steps;      // [n_inst]
+  Sched* sched;
+  DevStatus* status;
+  PhaseTime* times;          // [n_phases] (nullable)
+  uint64_t* inst_end;        // [n_inst] device time each instance finished (nullable)
+  uint64_t watchdog_ticks;   // a wait longer than this raises OFA_E_TIMEOUT
+  int32_t shuffle;           // debug: permute tiles inside a phase
+};
+
+hipError_t init_kernels();
+size_t phase_lds_bytes(const Phase& ph);   // dynamic LDS a phase needs
+size_t persistent_lds_bytes();             // dynamic LDS of the persistent kernel
+int persistent_occupancy();                // workgroups per CU for the persistent kernel
+
+hipError_t launch_phase(const Phase& host_ph, const Phase* dev_phases, int idx, const StepCtx* dev_sc,
+                        DevStatus* status, PhaseTime* times, int64_t step, hipStream_t s);
+hipError_t launch_persistent(const PersistParams& p, int grid, hipStream_t s);
+hipError_t launch_fill_u64(uint64_t* p, uint64_t v, int64_t n, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
+// p[2i] = a, p[2i+1] = b for i < n_pairs
+hipError_t launch_fill_pairs(uint64_t* p, uint64_t a, uint64_t b, int64_t n_pairs, hipStream_t s);
+
+}  // namespace ofa

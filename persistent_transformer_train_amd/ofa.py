@@ -1,0 +1,212 @@
+"""Thin ctypes binding of libofa.so (include/ofa.h), same names as the C ABI.
+
+Argument marshalling only: every step of the method runs in the HIP kernels of
+the library.  PyTorch is used for device memory and the stream.  Importing this
+module fails loudly when libofa.so has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libofa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m persistent_transformer_train_amd.build` "
+        "(there is no CPU or PyTorch fallback)")
+
+_lib = C.CDLL(LIB_PATH)
+
+OFA_OK, OFA_E_ARG, OFA_E_HIP, OFA_E_NONFINITE, OFA_E_TIMEOUT, OFA_E_OVERFLOW, OFA_E_STATE = 0, -1, -2, -3, -4, -5, -6
+OFA_DEBUG_SHUFFLE_TICKETS, OFA_DEBUG_SHORT_WATCHDOG = 1, 2
+
+
+class ofa_config(C.Structure):
+    _fields_ = [
+        ("n_layer", C.c_int32), ("d_model", C.c_int32), ("n_head", C.c_int32), ("d_ff", C.c_int32),
+        ("vocab", C.c_int32), ("n_pos", C.c_int32),
+        ("mlp_gated", C.c_int32), ("tied_head", C.c_int32), ("has_bias", C.c_int32),
+        ("batch", C.c_int32), ("seq", C.c_int32), ("precision", C.c_int32),
+        ("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+        ("weight_decay", C.c_float),
+        ("lr_schedule", C.c_int32), ("total_steps", C.c_int32),
+        ("train_cus", C.c_int32), ("serve_cus", C.c_int32),
+        ("decode_window", C.c_int32), ("prompt_len", C.c_int32), ("restart_every", C.c_int32),
+        ("exec_mode", C.c_int32),
+        ("debug_counter_base", C.c_uint64), ("debug_flags", C.c_int32),
+        ("reserved", C.c_int32 * 7),
+    ]
+
+
+class ofa_stats(C.Structure):
+    _fields_ = [
+        ("status", C.c_int32), ("err_phase", C.c_int32), ("err_step", C.c_int64), ("err_info", C.c_int64),
+        ("tickets_claimed", C.c_uint64), ("steps_done", C.c_uint64), ("version", C.c_uint64),
+        ("last_call_ms", C.c_double), ("n_phases", C.c_int32), ("n_tiles_step", C.c_int32),
+        ("grid", C.c_int32), ("reserved", C.c_int32 * 5),
+    ]
+
+
+_H = C.c_void_p
+_P = C.c_void_p
+_sig = {
+    "ofa_workspace_bytes": (C.c_size_t, [C.POINTER(ofa_config)]),
+    "ofa_validate_config": (C.c_int, [C.POINTER(ofa_config), C.c_char_p, C.c_size_t]),
+    "ofa_param_count": (C.c_int64, [C.POINTER(ofa_config)]),
+    "ofa_param_tensor_count": (C.c_int32, [C.POINTER(ofa_config)]),
+    "ofa_param_tensor": (C.c_int, [C.POINTER(ofa_config), C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_int64),
+                                   C.POINTER(C.c_int32), C.c_char_p, C.c_size_t]),
+    "ofa_create": (C.c_int, [C.POINTER(ofa_config), _P, C.c_size_t, _P, _P, C.POINTER(_H)]),
+    "ofa_train_step": (C.c_int, [_H, _P, C.c_int32, _P]),
+    "ofa_publish_weights": (C.c_int, [_H, C.POINTER(C.c_uint64)]),
+    "ofa_decode_token": (C.c_int, [_H, _P, C.c_int32, C.c_int32, _P, _P, _P]),
+    "ofa_train_and_serve": (C.c_int, [_H, _P, C.c_int32, _P, _P, C.c_int32, _P, _P, C.c_int32, _P]),
+    "ofa_get_params": (C.c_int, [_H, _P]),
+    "ofa_set_params": (C.c_int, [_H, _P]),
+    "ofa_get_grads": (C.c_int, [_H, _P]),
+    "ofa_status_sync": (C.c_int, [_H, C.POINTER(ofa_stats)]),
+    "ofa_phase_times": (C.c_int, [_H, C.POINTER(C.c_uint64), C.c_int32, C.POINTER(C.c_int32), C.c_char_p,
+                                  C.c_size_t]),
+    "ofa_task_budget": (C.c_int, [C.c_uint64, C.c_uint64, C.POINTER(C.c_uint64)]),
+    "ofa_last_error": (C.c_char_p, [_H]),
+    "ofa_status_string": (C.c_char_p, [C.c_int]),
+    "ofa_destroy": (C.c_int, [_H]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+    globals()[_name] = _f
+
+EXPORTED = tuple(_sig)
+
+
+class OfaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ofa_status_string(code).decode()} ({code}): {msg}")
+        self.code = code
+
+
+def make_config(d: dict) -> ofa_config:
+    c = ofa_config()
+    for k, v in d.items():
+        setattr(c, k, v)
+    return c
+
+
+def layout(cfg: ofa_config):
+    """[(name, offset, numel, kind)] of the canonical parameter layout."""
+    n = ofa_param_tensor_count(C.byref(cfg))
+    if n < 0:
+        buf = C.create_string_buffer(256)
+        ofa_validate_config(C.byref(cfg), buf, 256)
+        raise OfaError(OFA_E_ARG, buf.value.decode())
+    out = []
+    off, numel, kind = C.c_int64(), C.c_int64(), C.c_int32()
+    name = C.create_string_buffer(64)
+    kinds = {0: "normal", 1: "zeros", 2: "ones"}
+    for i in range(n):
+        ofa_param_tensor(C.byref(cfg), i, C.byref(off), C.byref(numel), C.byref(kind), name, 64)
+        out.append((name.value.decode(), off.value, numel.value, kinds[kind.value]))
+    return out
+
+
+class Handle:
+    """One model on one GPU: owns the torch-allocated workspace and the ofa handle."""
+
+    def __init__(self, cfg_dict: dict, init_params, device="cuda:0"):
+        import torch
+        self.torch = torch
+        self.cfg_dict = dict(cfg_dict)
+        self.cfg = make_config(cfg_dict)
+        buf = C.create_string_buffer(256)
+        if ofa_validate_config(C.byref(self.cfg), buf, 256) != OFA_OK:
+            raise OfaError(OFA_E_ARG, buf.value.decode())
+        self.device = torch.device(device)
+        self.n_params = ofa_param_count(C.byref(self.cfg))
+        ws_bytes = ofa_workspace_bytes(C.byref(self.cfg))
+        self.ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=self.device)
+        base = self.ws.data_ptr()
+        self.ws_ptr = (base + 255) // 256 * 256
+        self.ws_bytes = ws_bytes
+        init = torch.as_tensor(init_params, dtype=torch.float32).to(self.device).contiguous()
+        assert init.numel() == self.n_params, (init.numel(), self.n_params)
+        self.stream = torch.cuda.current_stream(self.device)
+        self.h = _H()
+        rc = ofa_create(C.byref(self.cfg), self.ws_ptr, ws_bytes, init.data_ptr(), self.stream.cuda_stream,
+                        C.byref(self.h))
+        if rc != OFA_OK:
+            msg = ofa_last_error(self.h).decode() if self.h.value else "create failed"
+            raise OfaError(rc, msg)
+        self.sync()
+        del init
+
+    # -- calls ---------------------------------------------------------------
+    def _check(self, rc):
+        if rc != OFA_OK:
+            raise OfaError(rc, ofa_last_error(self.h).decode())
+
+    def train_step(self, tokens, losses):
+        """tokens: int32 cuda [n][B][T+1]; losses: float32 cuda [n]."""
+        assert tokens.dtype == self.torch.int32 and tokens.is_cuda and tokens.is_contiguous()
+        assert losses.dtype == self.torch.float32 and losses.is_cuda and losses.numel() >= tokens.shape[0]
+        self._check(ofa_train_step(self.h, tokens.data_ptr(), tokens.shape[0], losses.data_ptr()))
+
+    def publish(self) -> int:
+        v = C.c_uint64()
+        self._check(ofa_publish_weights(self.h, C.byref(v)))
+        return v.value
+
+    def decode(self, prompt, n_new, tokens_out, logits_out=None, versions_out=None):
+        n_prompt = 0 if prompt is None else prompt.numel()
+        self._check(ofa_decode_token(self.h, 0 if prompt is None else prompt.data_ptr(), n_prompt, n_new,
+                                     tokens_out.data_ptr(), 0 if logits_out is None else logits_out.data_ptr(),
+                                     0 if versions_out is None else versions_out.data_ptr()))
+
+    def get_params(self):
+        out = self.torch.empty(self.n_params, dtype=self.torch.float32, device=self.device)
+        self._check(ofa_get_params(self.h, out.data_ptr()))
+        return out
+
+    def set_params(self, p):
+        p = p.to(self.device, self.torch.float32).contiguous()
+        self._check(ofa_set_params(self.h, p.data_ptr()))
+        self.sync()
+
+    def get_grads(self):
+        out = self.torch.empty(self.n_params, dtype=self.torch.float32, device=self.device)
+        self._check(ofa_get_grads(self.h, out.data_ptr()))
+        return out
+
+    def sync(self) -> ofa_stats:
+        st = ofa_stats()
+        rc = ofa_status_sync(self.h, C.byref(st))
+        self.last_stats = st
+        self._check(rc)
+        return st
+
+    def phase_times(self):
+        n = 512
+        t = (C.c_uint64 * (2 * n))()
+        names = C.create_string_buffer(32 * n)
+        n_out = C.c_int32()
+        self._check(ofa_phase_times(self.h, t, n, C.byref(n_out), names, 32))
+        out = []
+        for i in range(n_out.value):
+            nm = names.raw[32 * i:32 * (i + 1)].split(b"\0", 1)[0].decode()
+            out.append((nm, t[2 * i], t[2 * i + 1]))
+        return out
+
+    def close(self):
+        if self.h:
+            ofa_destroy(self.h)
+            self.h = _H()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
