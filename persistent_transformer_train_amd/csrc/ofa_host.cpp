@@ -112,8 +112,8 @@ std::string validate(const ofa_config& c) {
   if (c.n_pos < 0) return bad("n_pos < 0");
   if (c.batch < 1 || c.seq < 1) return bad("batch/seq must be >= 1");
   if (c.n_pos && c.seq > c.n_pos) return bad("seq %d exceeds the position table (%d)", c.seq, c.n_pos);
-  if (c.seq > 4096) return bad("seq %d > 4096", c.seq);
-  if ((int64_t)c.batch * c.seq > 8192) return bad("batch*seq %d exceeds 8192 (embedding sort)", c.batch * c.seq);
+  if (c.seq > 2048) return bad("seq %d > 2048", c.seq);
+  if ((int64_t)c.batch * c.seq > 4096) return bad("batch*seq %d exceeds 4096 (embedding sort)", c.batch * c.seq);
   if ((int64_t)c.batch * c.seq % 8 && c.precision == OFA_BF16)
     return bad("batch*seq must be a multiple of 8 in bf16 mode");
   if (c.precision != OFA_FP32 && c.precision != OFA_BF16) return bad("precision %d unknown", c.precision);
@@ -127,7 +127,7 @@ std::string validate(const ofa_config& c) {
   if (c.exec_mode != OFA_EXEC_PERSISTENT && c.exec_mode != OFA_EXEC_LAUNCH_PER_PHASE) return bad("exec_mode unknown");
   const int win = c.decode_window ? c.decode_window : (c.n_pos ? c.n_pos : c.seq);
   if (win < 2 || (c.n_pos && win > c.n_pos)) return bad("decode_window %d invalid", win);
-  if (win > 8192) return bad("decode_window %d > 8192", win);
+  if (win > 4096) return bad("decode_window %d > 4096", win);
   const int keep = c.prompt_len ? c.prompt_len : 1;
   if (keep < 1 || keep > win) return bad("prompt_len %d invalid for window %d", keep, win);
   if (c.train_cus < 0 || c.serve_cus < 0) return bad("negative CU count");
@@ -275,6 +275,7 @@ struct ofa_handle {
   char* h_misc = nullptr;          // pinned staging for the misc block
   hipEvent_t ev_upload = nullptr, ev_t0 = nullptr, ev_t1 = nullptr;
   bool upload_pending = false;
+  bool timed = false;              // ev_t0 / ev_t1 bracket a recorded call
   uint64_t steps_done = 0;
   uint64_t version = 0;
   int sticky = 0;
@@ -307,6 +308,7 @@ ofa_status fail(ofa_handle* h, ofa_status s, const char* fmt, ...) {
   do {                                                                                     \
     hipError_t _e = (expr);                                                                \
     if (_e != hipSuccess) {                                                                \
+      (void)hipGetLastError();                                                             \
       (h)->hip_err = (int)_e;                                                              \
       return fail((h), OFA_E_HIP, "%s failed: %s", #expr, hipGetErrorString(_e));          \
     }                                                                                      \
@@ -601,8 +603,9 @@ void build_train(ofa_handle* h) {
     a.cols_per_tile = 256;
     return p;
   };
-  auto colsum = [&](const void* src, int64_t ld, int cols, float* part, float* out, int dep, const char* nm) {
-    int p = b.add(OP_COLSUM, w.cs_tiles, nm, {dep});
+  auto colsum = [&](const void* src, int64_t ld, int cols, float* part, float* out, int dep, int dep2,
+                    const char* nm) {
+    int p = b.add(OP_COLSUM, w.cs_tiles, nm, {dep, dep2});
     ColsumArgs& a = b[p].a.cs;
     a.src = src;
     a.ld = ld;
@@ -660,7 +663,7 @@ void build_train(ofa_handle* h) {
       g = gemm(h, (int)F, (int)d, (int)BT, DM(l), F, 0, lp, Hh(2 * l + 1), d, 0, lp, gf(lo.w_fc), d, DT_F32,
                EPI_STORE);
       p_mdw2 = gemm_phase(g, {p_pdx}, "fc_dw");
-      if (c.has_bias) colsum(DM(l), F, (int)F, CSF(l), gf(lo.b_fc), p_pdx, "fc_bias_sum");
+      if (c.has_bias) colsum(DM(l), F, (int)F, CSF(l), gf(lo.b_fc), p_pdx, -1, "fc_bias_sum");
     }
     (void)p_mdw2;
     int p_ln2b = ln_bwd(2 * l + 1, lo.ln2_g, ri, {p_mdx}, "ln2_bwd");
@@ -689,7 +692,7 @@ void build_train(ofa_handle* h) {
     g = gemm(h, (int)(3 * d), (int)d, (int)BT, DQKV(l), 3 * d, 0, lp, Hh(2 * l), d, 0, lp, gf(lo.w_qkv), d, DT_F32,
              EPI_STORE);
     gemm_phase(g, {p_dqkv, p_kv}, "qkv_dw");
-    if (c.has_bias) colsum(DQKV(l), 3 * d, (int)(3 * d), CSQ(l), gf(lo.b_qkv), p_dqkv, "qkv_bias_sum");
+    if (c.has_bias) colsum(DQKV(l), 3 * d, (int)(3 * d), CSQ(l), gf(lo.b_qkv), p_dqkv, p_kv, "qkv_bias_sum");
     int p_ln1b = ln_bwd(2 * l, lo.ln1_g, 2 * l + 1, {p_qdx}, "ln1_bwd");
     float* prev_bias = (c.has_bias && l > 0) ? gf(h->lay.layer[l - 1].b_proj) : nullptr;
     ln_red(2 * l, p_ln1b, gf(lo.ln1_g), gf(lo.ln1_b), prev_bias, "ln1_params");
@@ -1003,6 +1006,9 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
     HIP_TRY(h, init_kernels());
     kernels_ready = true;
   }
+  // the sort of the embedding backward keeps batch*seq 64-bit keys in LDS
+  if ((size_t)h->D.BT * 8 + 64 > persistent_lds_bytes())
+    return fail(h, OFA_E_ARG, "batch*seq %lld needs more LDS than the device allows", (long long)h->D.BT);
   int dev = 0;
   HIP_TRY(h, hipGetDevice(&dev));
   HIP_TRY(h, hipDeviceGetAttribute(&h->n_cu, hipDeviceAttributeMultiprocessorCount, dev));
@@ -1019,6 +1025,11 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
   build_decode(h);
   if (h->train.size() > (size_t)kMaxPhases || h->dec.size() > (size_t)kMaxPhases)
     return fail(h, OFA_E_ARG, "program too long");
+  for (const auto* prog : {&h->train, &h->dec})
+    for (const Phase& ph : *prog)
+      if ((size_t)ph.lds_bytes > persistent_lds_bytes() || (size_t)ph.lds_bytes > lds_limit_bytes())
+        return fail(h, OFA_E_ARG, "phase op %d needs %d bytes of LDS (> %zu)", ph.op, ph.lds_bytes,
+                    persistent_lds_bytes());
   // phase tables live in a small library-owned device buffer
   size_t tbytes = (h->train.size() + h->dec.size()) * sizeof(Phase);
   HIP_TRY(h, hipMalloc(&h->d_alloc, tbytes));
@@ -1190,6 +1201,7 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
     HIP_TRY(h, launch_persistent(pp, grid, h->stream));
   }
   HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
+  h->timed = true;
   h->steps_done += n_steps;
   return OFA_OK;
 }
@@ -1249,6 +1261,7 @@ ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_
   s = run_launch_per_phase(h, h->dec, h->d_dec, d_dsteps, n_inst, 0, true);
   if (s != OFA_OK) return s;
   HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
+  h->timed = true;
   return OFA_OK;
 }
 
@@ -1263,7 +1276,10 @@ ofa_status ofa_status_sync(ofa_handle* h, ofa_stats* out) {
   DevStatus ds;
   HIP_TRY(h, hipMemcpy(&ds, h->ws + h->cw.status, sizeof ds, hipMemcpyDeviceToHost));
   float ms = 0.f;
-  if (hipEventElapsedTime(&ms, h->ev_t0, h->ev_t1) == hipSuccess) h->last_ms = ms;
+  if (h->timed) {
+    if (hipEventElapsedTime(&ms, h->ev_t0, h->ev_t1) == hipSuccess) h->last_ms = ms;
+    (void)hipGetLastError();
+  }
   if (ds.code && !h->sticky) {
     h->sticky = ds.code;
     h->err = std::string("device status: ") + ofa_status_string((ofa_status)ds.code) +

@@ -219,40 +219,29 @@ static size_t lds_for(const Phase& ph) {
 
 size_t phase_lds_bytes(const Phase& ph) { return lds_for(ph); }
 
-static constexpr size_t kPersistLds = 96 * 1024;
-size_t persistent_lds_bytes() { return kPersistLds; }
+// Every phase is sized to fit the default 64 KB dynamic-LDS window, so no
+// kernel needs a raised attribute.
+static constexpr size_t g_lds_limit = 60 * 1024;
+static constexpr size_t g_persist_lds = 60 * 1024;
+size_t persistent_lds_bytes() { return g_persist_lds; }
 
-template <int OP>
-static hipError_t set_attr() {
-  return hipFuncSetAttribute((const void*)phase_kernel<OP>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             160 * 1024);
-}
+hipError_t init_kernels() { return hipSuccess; }
 
-hipError_t init_kernels() {
-  hipError_t e = hipSuccess;
-#define OFA_ATTR(X) if (e == hipSuccess) e = set_attr<X>();
-  OFA_ATTR(OP_EMBED) OFA_ATTR(OP_LN_FWD) OFA_ATTR(OP_GEMM) OFA_ATTR(OP_ROPE) OFA_ATTR(OP_ATTN_FWD)
-  OFA_ATTR(OP_GEGLU_FWD) OFA_ATTR(OP_CE) OFA_ATTR(OP_LOSS) OFA_ATTR(OP_LN_BWD) OFA_ATTR(OP_COLSUM)
-  OFA_ATTR(OP_COLRED) OFA_ATTR(OP_ATTN_PREP) OFA_ATTR(OP_ATTN_BWD_KV) OFA_ATTR(OP_ATTN_BWD_Q)
-  OFA_ATTR(OP_ROPE_BWD) OFA_ATTR(OP_EMB_SORT) OFA_ATTR(OP_EMB_BWD) OFA_ATTR(OP_ADAMW) OFA_ATTR(OP_COPY)
-  OFA_ATTR(OP_DEC_EMBED) OFA_ATTR(OP_DEC_GEMV) OFA_ATTR(OP_DEC_ATTN) OFA_ATTR(OP_DEC_ARGMAX)
-#undef OFA_ATTR
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void*)persistent_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kPersistLds);
-  return e;
-}
+size_t lds_limit_bytes() { return g_lds_limit; }
 
 int persistent_occupancy() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, persistent_kernel, kThreads, kPersistLds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, persistent_kernel, kThreads, g_persist_lds) != hipSuccess) {
+    (void)hipGetLastError();
     return 0;
+  }
   return n;
 }
 
 hipError_t launch_phase(const Phase& h, const Phase* d_phases, int idx, const StepCtx* d_sc, DevStatus* st,
                         PhaseTime* tm, int64_t step, hipStream_t s) {
   if (h.n_tiles <= 0) return hipSuccess;
+  (void)hipGetLastError();   // report this launch's error, not a stale one
   const int grid = h.n_tiles;
   const size_t lds = lds_for(h);
   switch (h.op) {
@@ -271,14 +260,16 @@ hipError_t launch_phase(const Phase& h, const Phase* d_phases, int idx, const St
 }
 
 hipError_t launch_persistent(const PersistParams& p, int grid, hipStream_t s) {
+  (void)hipGetLastError();
   void* args[] = {(void*)&p};
   return hipLaunchCooperativeKernel((const void*)persistent_kernel, dim3(grid), dim3(kThreads), args,
-                                    kPersistLds, s);
+                                    g_persist_lds, s);
 }
 
 hipError_t launch_fill_u64(uint64_t* p, uint64_t v, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   int grid = (int)std::min<int64_t>((n + 255) / 256, 1024);
+  (void)hipGetLastError();
   hipLaunchKernelGGL(fill_u64_kernel, dim3(grid), dim3(256), 0, s, p, v, n);
   return hipGetLastError();
 }
@@ -286,6 +277,7 @@ hipError_t launch_fill_u64(uint64_t* p, uint64_t v, int64_t n, hipStream_t s) {
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   int grid = (int)std::min<int64_t>((n + 255) / 256, 1024);
+  (void)hipGetLastError();
   hipLaunchKernelGGL(fill_u32_kernel, dim3(grid), dim3(256), 0, s, p, v, n);
   return hipGetLastError();
 }
@@ -293,6 +285,7 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
 hipError_t launch_fill_pairs(uint64_t* p, uint64_t a, uint64_t b, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   int grid = (int)std::min<int64_t>((n + 255) / 256, 1024);
+  (void)hipGetLastError();
   hipLaunchKernelGGL(fill_pairs_kernel, dim3(grid), dim3(256), 0, s, p, a, b, n);
   return hipGetLastError();
 }

@@ -1,0 +1,111 @@
+"""GPU parity of batch-1 greedy decode against the oracle's full recomputation.
+
+Teacher forcing: the oracle recomputes the logits along the GPU's own token
+sequence; the GPU token must equal the oracle argmax wherever the oracle's
+top-2 margin exceeds 1e-2.  Small windows force the context-restart rule.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_common import cfg_of, init_of, log, spec_from_cfg, stream_of
+from oracle import decode, gpt
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def run_decode(name, n_new, exec_mode=1, publish=True, **kw):
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of(name, exec_mode=exec_mode, **kw)
+    init = init_of(name, cfg)
+    h = ofa.Handle(cfg, init)
+    if publish:
+        v = h.publish()
+        assert v == 1
+    stream = stream_of(name, cfg)
+    keep = cfg["prompt_len"]
+    prompt = stream.prompt(keep)
+    toks = torch.zeros(n_new, dtype=torch.int32, device="cuda")
+    logits = torch.zeros(n_new, cfg["vocab"], dtype=torch.float32, device="cuda")
+    vers = torch.zeros(n_new, dtype=torch.int64, device="cuda")
+    h.decode(torch.from_numpy(prompt).cuda(), n_new, toks, logits, vers)
+    h.sync()
+    return h, cfg, init, prompt, toks.cpu().numpy(), logits.cpu().numpy(), vers.cpu().numpy()
+
+
+def check_against_oracle(cfg, params_flat, prompt, toks, logits, dtype, logit_tol):
+    s = spec_from_cfg(cfg)
+    P = gpt.unflatten(s, np.asarray(params_flat, np.float64))
+    win = cfg["decode_window"]
+    keep = cfg["prompt_len"]
+    z = decode.teacher_forced_logits(s, P, prompt, toks, win, keep, dtype=dtype)
+    checked = 0
+    for i in range(len(toks)):
+        if decode.top2_margin(z[i]) > 1e-2:
+            assert toks[i] == decode.argmax_lowest(z[i]), (i, toks[i], decode.argmax_lowest(z[i]))
+            checked += 1
+    err = np.abs(logits - z).max()
+    log(f"decode: {checked}/{len(toks)} tokens checked, max |logit err| {err:.3g}")
+    assert err <= logit_tol
+    return checked
+
+
+@pytest.mark.parametrize("window", [64, 24])
+def test_c1_fp32_decode(window):
+    n_new = 60
+    h, cfg, init, prompt, toks, logits, vers = run_decode("c1", n_new, decode_window=window)
+    assert np.all(vers == 1)
+    checked = check_against_oracle(cfg, init, prompt, toks, logits, np.float64, 1e-4)
+    assert checked >= n_new // 2
+    # continuing the context gives the same tokens as one longer call
+    h.close()
+
+
+def test_c1_decode_continue_matches_single_call():
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of("c1", exec_mode=1, decode_window=24)
+    h = ofa.Handle(cfg, init_of("c1", cfg))
+    prompt = torch.from_numpy(stream_of("c1", cfg).prompt(cfg["prompt_len"])).cuda()
+    a = torch.zeros(40, dtype=torch.int32, device="cuda")
+    h.decode(prompt, 40, a)
+    b1 = torch.zeros(17, dtype=torch.int32, device="cuda")
+    b2 = torch.zeros(23, dtype=torch.int32, device="cuda")
+    h.decode(prompt, 17, b1)
+    h.decode(None, 23, b2)
+    h.sync()
+    assert np.array_equal(a.cpu().numpy(), np.concatenate([b1.cpu().numpy(), b2.cpu().numpy()]))
+    h.close()
+
+
+@pytest.mark.parametrize("name", ["m2", "m3"])
+def test_bf16_mini_decode(name):
+    # bf16 weights and KV cache: the oracle uses the same bf16-rounded weights
+    n_new = 100
+    h, cfg, init, prompt, toks, logits, vers = run_decode(name, n_new)
+    w_bf16 = torch.tensor(init).to(torch.bfloat16).to(torch.float32).numpy()
+    checked = check_against_oracle(cfg, w_bf16, prompt, toks, logits, np.float64, 5e-2)
+    assert checked >= n_new // 4
+    h.close()
+
+
+def test_decode_after_training_reads_published_weights():
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of("c1", exec_mode=0, decode_window=32)
+    h = ofa.Handle(cfg, init_of("c1", cfg))
+    stream = stream_of("c1", cfg)
+    losses = torch.zeros(3, dtype=torch.float32, device="cuda")
+    h.train_step(torch.from_numpy(stream.batches(0, 3)).cuda(), losses)
+    v = h.publish()
+    assert v == 1
+    trained = h.get_params().cpu().numpy()
+    h.train_step(torch.from_numpy(stream.batches(3, 2)).cuda(), losses)   # not published
+    prompt = stream.prompt(cfg["prompt_len"])
+    toks = torch.zeros(30, dtype=torch.int32, device="cuda")
+    logits = torch.zeros(30, cfg["vocab"], dtype=torch.float32, device="cuda")
+    vers = torch.zeros(30, dtype=torch.int64, device="cuda")
+    h.decode(torch.from_numpy(prompt).cuda(), 30, toks, logits, vers)
+    h.sync()
+    assert np.all(vers.cpu().numpy() == 1)
+    check_against_oracle(cfg, trained, prompt, toks.cpu().numpy(), logits.cpu().numpy(), np.float64, 1e-4)
+    h.close()

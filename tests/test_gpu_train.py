@@ -1,0 +1,166 @@
+"""GPU parity of the training step against the CPU oracle, through the C ABI.
+
+fp32 mode: per-step loss within 1e-4 relative of the fp64 oracle, gradients
+element by element.  bf16 mode: loss within 2e-2 absolute of the oracle's own
+fp32 trajectory over 100 steps, whole-gradient cosine >= 0.999.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_common import cfg_of, cosine, init_of, log, spec_from_cfg, stream_of
+from oracle import gpt, optim
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+PER_PHASE, PERSISTENT = 1, 0
+
+
+def gpu_run(name, n_steps, exec_mode, **kw):
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of(name, exec_mode=exec_mode, **kw)
+    stream = stream_of(name, cfg)
+    init = init_of(name, cfg)
+    h = ofa.Handle(cfg, init)
+    toks = torch.from_numpy(stream.batches(0, n_steps)).cuda()
+    losses = torch.zeros(n_steps, dtype=torch.float32, device="cuda")
+    h.train_step(toks, losses)
+    h.sync()
+    return h, cfg, stream, init, losses.cpu().numpy()
+
+
+def oracle_losses(cfg, stream, init, n_steps, dtype):
+    tr = optim.Trainer(spec_from_cfg(cfg), init, dtype=dtype)
+    return np.array([tr.step(stream.batch(s)) for s in range(n_steps)]), tr
+
+
+@pytest.mark.parametrize("exec_mode", [PER_PHASE, PERSISTENT], ids=["per_phase", "persistent"])
+def test_c1_fp32_loss_trajectory(exec_mode):
+    log(f"c1 fp32 10 steps exec_mode={exec_mode}")
+    h, cfg, stream, init, gl = gpu_run("c1", 10, exec_mode)
+    ol, _ = oracle_losses(cfg, stream, init, 10, np.float64)
+    log("gpu", gl, "\noracle", ol)
+    assert np.all(np.isfinite(gl))
+    rel = np.abs(gl - ol) / np.abs(ol)
+    assert rel.max() <= 1e-4, rel
+    assert gl[-1] < gl[0]
+    h.close()
+
+
+@pytest.mark.parametrize("exec_mode", [PER_PHASE, PERSISTENT], ids=["per_phase", "persistent"])
+def test_c1_fp32_gradients_elementwise(exec_mode):
+    h, cfg, stream, init, gl = gpu_run("c1", 1, exec_mode)
+    g_gpu = h.get_grads().cpu().numpy().astype(np.float64)
+    p_gpu = h.get_params().cpu().numpy()
+    s = spec_from_cfg(cfg)
+    P = gpt.unflatten(s, np.asarray(init, np.float64))
+    loss, grads = gpt.loss_and_grads(s, P, stream.batch(0))
+    g_or = gpt.flatten(s, grads)
+    scale = np.abs(g_or).max()
+    err = np.abs(g_gpu - g_or)
+    log("max abs grad err", err.max(), "grad scale", scale)
+    assert err.max() <= 1e-4 * scale + 1e-7
+    # the AdamW update of the first step, element by element, applied by the oracle
+    # to the GPU's own gradient (Adam's first step is sign-like: where |g| ~ eps a
+    # 1e-7 gradient difference moves the update by up to lr)
+    p_exp = np.asarray(init, np.float64).copy()
+    m = np.zeros_like(p_exp)
+    v = np.zeros_like(p_exp)
+    optim.adamw_update(p_exp, g_gpu, m, v, 1, optim.lr_at(s, 0), s.beta1, s.beta2, s.eps, s.weight_decay)
+    err_p = np.abs(p_gpu - p_exp).max()
+    log("max abs param err after AdamW", err_p)
+    assert err_p <= 1e-7
+    h.close()
+
+
+@pytest.mark.parametrize("name", ["m2", "m3"])
+@pytest.mark.parametrize("exec_mode", [PER_PHASE, PERSISTENT], ids=["per_phase", "persistent"])
+def test_bf16_mini_loss_100_steps(name, exec_mode):
+    log(f"{name} bf16 100 steps exec_mode={exec_mode}")
+    h, cfg, stream, init, gl = gpu_run(name, 100, exec_mode)
+    ol, _ = oracle_losses(cfg, stream, init, 100, np.float32)
+    d = np.abs(gl - ol)
+    log(f"{name}: max |dloss| {d.max():.4g} first {gl[0]:.4f}/{ol[0]:.4f} last {gl[-1]:.4f}/{ol[-1]:.4f}")
+    assert np.all(np.isfinite(gl))
+    assert d.max() <= 2e-2
+    assert gl[-1] < gl[0]
+    h.close()
+
+
+@pytest.mark.parametrize("name", ["m2", "m3"])
+def test_bf16_mini_gradient_cosine(name):
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of(name, exec_mode=PERSISTENT)
+    stream = stream_of(name, cfg)
+    init = init_of(name, cfg)
+    h = ofa.Handle(cfg, init)
+    s = spec_from_cfg(cfg)
+    losses = torch.zeros(10, dtype=torch.float32, device="cuda")
+    for step in (0, 9):
+        if step == 9:   # 9 more steps, then compare at the GPU's own weights
+            h.train_step(torch.from_numpy(stream.batches(1, 8)).cuda(), losses)
+            h.sync()
+        p_now = h.get_params().cpu().numpy().astype(np.float64)
+        tok = torch.from_numpy(stream.batches(step, 1)).cuda()
+        h.train_step(tok, losses)
+        h.sync()
+        g_gpu = h.get_grads().cpu().numpy()
+        loss, grads = gpt.loss_and_grads(s, gpt.unflatten(s, p_now), stream.batch(step))
+        g_or = gpt.flatten(s, grads)
+        cos = cosine(g_gpu, g_or)
+        per = {n: cosine(g_gpu[o:o + k], g_or[o:o + k]) for n, o, k, _ in ofa.layout(h.cfg)}
+        worst = min(per.items(), key=lambda kv: kv[1])
+        log(f"{name} step {step + 1}: grad cosine {cos:.6f}, worst tensor {worst}")
+        assert cos >= 0.999
+        assert worst[1] >= 0.99
+    h.close()
+
+
+def test_determinism_and_shuffled_tickets():
+    from persistent_transformer_train_amd import ofa
+    runs = []
+    for flags in (0, 0, ofa.OFA_DEBUG_SHUFFLE_TICKETS):
+        h, *_, gl = gpu_run("m3", 5, PERSISTENT, debug_flags=flags)
+        runs.append((gl.tobytes(), h.get_params().cpu().numpy().tobytes()))
+        h.close()
+    assert runs[0] == runs[1]
+    assert runs[0] == runs[2]
+
+
+def test_persistent_equals_per_phase_bitwise():
+    h1, *_, g1 = gpu_run("m2", 3, PERSISTENT)
+    p1 = h1.get_params().cpu().numpy()
+    h2, *_, g2 = gpu_run("m2", 3, PER_PHASE)
+    p2 = h2.get_params().cpu().numpy()
+    assert g1.tobytes() == g2.tobytes()
+    assert p1.tobytes() == p2.tobytes()
+    h1.close()
+    h2.close()
+
+
+def test_counter_base_near_2_pow_32():
+    # every counter starts just below 2^32: a 32-bit counter would wrap inside the run
+    h, cfg, stream, init, gl = gpu_run("c1", 3, PERSISTENT, debug_counter_base=2 ** 32 - 10)
+    ol, _ = oracle_losses(cfg, stream, init, 3, np.float64)
+    assert np.abs(gl - ol).max() / abs(ol[0]) <= 1e-4
+    assert h.last_stats.tickets_claimed >= 3 * h.last_stats.n_tiles_step
+    h.close()
+
+
+def test_bad_token_reports_arg_error():
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of("c1", exec_mode=PERSISTENT)
+    h = ofa.Handle(cfg, init_of("c1", cfg))
+    tok = np.zeros((1, cfg["batch"], cfg["seq"] + 1), np.int32)
+    tok[0, 1, 5] = cfg["vocab"] + 7
+    losses = torch.zeros(1, dtype=torch.float32, device="cuda")
+    h.train_step(torch.from_numpy(tok).cuda(), losses)
+    with pytest.raises(ofa.OfaError) as e:
+        h.sync()
+    assert e.value.code == ofa.OFA_E_ARG
+    assert h.last_stats.err_info == cfg["vocab"] + 7
+    # the handle stays in the error state
+    with pytest.raises(ofa.OfaError):
+        h.train_step(torch.from_numpy(tok).cuda(), losses)
+    h.close()
