@@ -1,0 +1,180 @@
+"""Benchmark: training tokens/s of the 162M GPT step (forward, backward, AdamW)
+on one MI355X, plus batch-1 greedy decode tokens/s of the same model.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--exec-mode persistent|per_phase]
+
+Prints ONE JSON line.  Workload: the 162M GPT-2-small-shaped model (12 layers,
+width 768, 12 heads, MLP 3072, learned positions 512, vocabulary 50,304, untied
+head) on 8 x 512 = 4,096 synthetic tokens per step (seeded order-2 Markov
+chain), bf16 operands with fp32 master weights -- the shape of the 162M run on
+the "Open Flapping Airplanes ... A100 reproduction" page ("What ran").  Inputs
+are resident in HBM before the timed region starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15   # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12    # MI355X HBM3E, bytes/s
+
+
+def model_flops_per_step(c: dict) -> dict:
+    """Algorithmic FLOPs of one training step: 6 * matmul params * tokens + causal attention."""
+    d, F, V, L, B, T, H = c["d_model"], c["d_ff"], c["vocab"], c["n_layer"], c["batch"], c["seq"], c["n_head"]
+    mlp = (3 if c["mlp_gated"] else 2) * d * F
+    matmul_params = L * (4 * d * d + mlp) + V * d
+    tokens = B * T
+    gemm = 6.0 * matmul_params * tokens
+    dh = d // H
+    attn_fwd = L * B * H * 2.0 * T * T * dh   # QK^T and PV over the causal half
+    return {"gemm": gemm, "attention": 3.0 * attn_fwd, "total": gemm + 3.0 * attn_fwd,
+            "matmul_params": matmul_params}
+
+
+def decode_bytes_per_token(c: dict, ctx: float) -> float:
+    """Weights read per decoded token (bf16) + KV cache read at context length ctx."""
+    d, F, V, L = c["d_model"], c["d_ff"], c["vocab"], c["n_layer"]
+    per_layer = (3 * d * d + 3 * d) + (d * d + d) + 2 * d + (2 * d * F + F + d) + 2 * d
+    weights = L * per_layer + V * d + 2 * d + (c["n_pos"] and d)   # blocks + head + lnf + one wte/wpe row
+    kv = L * 2 * d * ctx
+    return 2.0 * (weights + kv)
+
+
+def cpu_baseline(cfg: dict) -> dict:
+    """The oracle (numpy fp64, untuned) on a bounded sample: one full training step of
+    the same model at batch 1 (512 of the step's 4,096 tokens)."""
+    from oracle import gpt, optim
+    from persistent_transformer_train_amd import configs, synth
+    spec = gpt.Spec(n_layer=cfg["n_layer"], d_model=cfg["d_model"], n_head=cfg["n_head"], d_ff=cfg["d_ff"],
+                    vocab=cfg["vocab"], n_pos=cfg["n_pos"], mlp_gated=bool(cfg["mlp_gated"]),
+                    tied_head=bool(cfg["tied_head"]), has_bias=bool(cfg["has_bias"]), batch=1, seq=cfg["seq"],
+                    lr=cfg["lr"], beta1=cfg["beta1"], beta2=cfg["beta2"], eps=cfg["eps"],
+                    weight_decay=cfg["weight_decay"],
+                    lr_schedule="cosine" if cfg["lr_schedule"] == configs.LR_COSINE else "constant",
+                    total_steps=cfg["total_steps"])
+    lay = gpt.param_layout(spec)
+    init = synth.init_params([(int(np.prod(sh)), k) for _, sh, k in lay], 3)
+    stream = synth.TokenStream("markov2", 3, cfg["vocab"], 1, cfg["seq"])
+    tr = optim.Trainer(spec, init, dtype=np.float64)
+    t0 = time.perf_counter()
+    tr.step(stream.batch(0))
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(cfg["seq"] / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one fp64 training step (fwd+bwd+AdamW) of the same model at batch 1 "
+                      f"({cfg['seq']} tokens), {dt:.2f} s, numpy BLAS threads = affinity cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--exec-mode", choices=["persistent", "per_phase"], default="persistent")
+    ap.add_argument("--decode-tokens", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(collectives and sharding are design-only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from persistent_transformer_train_amd import configs, ofa, synth
+
+    cfg = configs.get("c3", exec_mode=0 if args.exec_mode == "persistent" else 1)
+    lay = ofa.layout(ofa.make_config(cfg))
+    init = synth.init_params([(n, k) for _, _, n, k in lay], 3)
+    stream = synth.TokenStream("markov2", 3, cfg["vocab"], cfg["batch"], cfg["seq"])
+    h = ofa.Handle(cfg, init)
+    BT = cfg["batch"] * cfg["seq"]
+    W, K = args.warmup, args.steps
+    toks_w = torch.from_numpy(stream.batches(0, max(W, 1))).cuda()
+    toks_k = torch.from_numpy(stream.batches(W, K)).cuda()
+    losses = torch.zeros(max(W, K, 1), dtype=torch.float32, device="cuda")
+    if W:
+        h.train_step(toks_w, losses)
+        h.sync()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    h.train_step(toks_k, losses)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = h.sync()
+    kernel_ms = st.last_call_ms   # HIP events around the launch(es) on the handle's stream
+    ls = losses[:K].cpu().numpy()
+    assert np.all(np.isfinite(ls)), ls
+
+    fl = model_flops_per_step(cfg)
+    value = K * BT / elapsed
+    achieved = fl["total"] * K / (kernel_ms / 1e3)
+    out = {
+        "metric": "train tokens/s for 162M GPT step (fwd+bwd+AdamW); batch-1 decode tokens/s",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / 24772.0, 3),
+        "baseline_ref": "24,772 tokens/s: A100 SXM4 40 GB, 85 training SMs (A100 reproduction page, "
+                        "'Measured results' table); context only, another machine",
+        "dtype": "bf16",
+        "data": "synthetic (seeded order-2 Markov chain, Zipf(1.1) transitions); random N(0,0.02) init",
+        "config": {"workload": "162M GPT-2-small-shaped training step: 12 layers, width 768, 12 heads, "
+                               "MLP 3072 GELU, 512 learned positions, vocab 50304, untied head; bf16 operands, "
+                               "fp32 master weights and AdamW state",
+                   "global_batch": cfg["batch"], "seq_len": cfg["seq"], "tokens_per_step": BT,
+                   "executor": args.exec_mode, "params": int(ofa.ofa_param_count(ofa.make_config(cfg)))},
+        "roofline": {"bound": "mfma", "kernel": "persistent_kernel" if args.exec_mode == "persistent"
+                     else "all phase kernels", "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4), "traffic": None,
+                     "flops_per_step": fl["total"], "kernel_ms_per_step": round(kernel_ms / K, 4)},
+        "losses": [float(ls[0]), float(ls[-1])],
+    }
+
+    if not args.no_decode and args.decode_tokens > 1:
+        # c4: greedy decode of the frozen seeded weights (version 0, published at create)
+        dcfg = cfg
+        prompt = torch.from_numpy(stream.prompt(dcfg["prompt_len"])).cuda()
+        n = args.decode_tokens
+        toks = torch.zeros(n, dtype=torch.int32, device="cuda")
+        h.decode(prompt, 1, toks)        # prefill of the prompt + first token (not timed)
+        h.sync()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h.decode(None, n - 1, toks[1:])
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        h.sync()
+        rate = (n - 1) / dt
+        avg_ctx = (dcfg["prompt_len"] + dcfg["decode_window"]) / 2
+        bpt = decode_bytes_per_token(dcfg, avg_ctx)
+        out["decode"] = {"metric": "batch-1 greedy decode tokens/s", "value": round(rate, 1), "unit": "tokens/s",
+                         "tokens": n - 1, "prompt": dcfg["prompt_len"], "window": dcfg["decode_window"],
+                         "cus": "all (launch per phase)",
+                         "roofline": {"bound": "hbm", "achieved": round(bpt * rate / 1e9, 1),
+                                      "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                      "frac": round(bpt * rate / PEAK_HBM, 4), "bytes_per_token": bpt}}
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    h.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
