@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libofa.so")
 ROOT = os.path.dirname(PKG)
 
 SOURCES = ["ofa_kernels.hip", "ofa_host.cpp"]
-HEADERS = ["ofa_types.h", "ofa_dev.h", "ofa_launch.h", "k_simple.h", "k_mfma.h", "k_decode.h"]
+HEADERS = ["ofa_types.h", "ofa_dev.h", "ofa_launch.h", "k_simple.h", "k_mfma.h", "k_attn.h", "k_decode.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

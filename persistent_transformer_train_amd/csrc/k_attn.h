@@ -1,0 +1,341 @@
+// k_attn.h -- causal attention on the gfx950 matrix cores (bf16 operands,
+// fp32 accumulation, head dim 64): forward with an online softmax that saves
+// the row log-sum-exp, and the backward split the way the RTX 3090 page's
+// profile splits it ("Where a step's time goes": attention-forward,
+// attention-key, attention-query): a key-side pass producing dK and dV and a
+// query-side pass producing dQ, both recomputing the probabilities from the
+// saved log-sum-exp (no atomics, so results are deterministic).
+//
+// MFMA layout facts used throughout (v_mfma_f32_32x32x16_bf16, 64 lanes):
+//  * operand A (M x K): lane l supplies row l%32, eight k values of its half
+//    g = l/32; operand B (K x N): lane l supplies column l%32, same k slots.
+//  * accumulator element r of lane l is C[row(r, l)][l%32] with
+//    row(r, l) = 8*(r/4) + 4*(l/32) + r%4.
+// A 32 x 32 accumulator fed back as a B operand over a 16-wide k chunk c
+// holds, in slot i of half g, the k index 16c + 8*(i/4) + 4g + i%4 (the same
+// formula as row()).  The partner A operand is then read with that same
+// permutation ("kperm" fragments), so no register shuffle is needed.
+#pragma once
+#include "k_mfma.h"
+
+namespace ofa {
+
+constexpr int kAP = 72;   // LDS pitch (bf16 elements) of a 64-wide block: 144 bytes
+
+__device__ __forceinline__ int acc_row(int r, int lane) { return ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3); }
+
+__device__ __forceinline__ bf16x8_t frag16(const uint16_t* base, int row, int k) {
+  return __builtin_bit_cast(bf16x8_t, *(const uint4*)(base + row * kAP + k));
+}
+
+// A fragment over k chunk c (16 wide) with the accumulator's k permutation
+__device__ __forceinline__ bf16x8_t frag_kperm(const uint16_t* base, int row, int c, int g) {
+  const uint16_t* p = base + row * kAP + 16 * c + 4 * g;
+  uint2 a = *(const uint2*)p;
+  uint2 b = *(const uint2*)(p + 8);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// eight fp32 values (accumulator elements 8c..8c+7) -> bf16 B operand
+__device__ __forceinline__ bf16x8_t pack_bf16(const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// 64 rows x 64 head dims (bf16, row stride ld) -> LDS as [row][dh] and/or [dh][row]
+__device__ __forceinline__ void attn_load_block(const uint16_t* g, int64_t ld, int row0, int nvalid,
+                                                uint16_t* lds_n, uint16_t* lds_t) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = threadIdx.x + i * kThreads;   // 512 chunks of 8
+    const int r = c >> 3, ch = (c & 7) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < nvalid) v = *(const uint4*)(g + (int64_t)(row0 + r) * ld + ch);
+    if (lds_n) *(uint4*)(lds_n + r * kAP + ch) = v;
+    if (lds_t) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lds_t[(ch + j) * kAP + r] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+    }
+  }
+}
+
+// B-operand fragments of one wave's 32 rows (row stride ld) for the four 16-wide dh chunks
+__device__ __forceinline__ void attn_row_frags(bf16x8_t f[4], const uint16_t* g, int64_t ld, int row, bool valid,
+                                               int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (valid) v = *(const uint4*)(g + (int64_t)row * ld + 16 * kk + 8 * (lane >> 5));
+    f[kk] = __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+__host__ __device__ constexpr size_t attn_mfma_lds_bytes() { return 4 * 64 * kAP * 2 + 2 * 64 * 4; }
+
+// ---------------------------------------------------------------- forward
+// tile = (b, h, block of 128 queries), largest blocks first; wave w owns 32 queries.
+
+__device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
+  uint16_t* Ks = (uint16_t*)smem;        // [64 keys][dh]
+  uint16_t* Vt = Ks + 64 * kAP;          // [dh][64 keys]
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, g = lane >> 5;
+  const int BH = a.B * a.H, nqb = (a.T + 127) / 128;
+  const int qblk = nqb - 1 - tile / BH, bh = tile % BH, b = bh / a.H, h = bh % a.H;
+  const int64_t ld = 3 * (int64_t)a.d;
+  const uint16_t* base = (const uint16_t*)a.qkv + (int64_t)b * a.T * ld + h * a.dh;
+  const int q0 = qblk * 128, qw = q0 + 32 * w, q = qw + (lane & 31);
+  const float scale = 1.0f / sqrtf((float)a.dh);
+  bf16x8_t qf[4];
+  attn_row_frags(qf, base, ld, q, q < a.T, lane);
+  f32x16_t oacc[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) oacc[0][e] = oacc[1][e] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+  const int kend = min(q0 + 128, a.T);
+  const int nkb = (kend + 63) / 64;
+  for (int kb = 0; kb < nkb; ++kb) {
+    __syncthreads();
+    attn_load_block(base + a.d, ld, kb * 64, min(64, a.T - kb * 64), Ks, nullptr);
+    attn_load_block(base + 2 * a.d, ld, kb * 64, min(64, a.T - kb * 64), nullptr, Vt);
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kbase = kb * 64 + sub * 32;
+      if (kbase > qw + 31 || kbase >= a.T) continue;   // wave-uniform: causal / past the end
+      f32x16_t s;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(Ks, sub * 32 + (lane & 31), 16 * kk + 8 * g), qf[kk], s,
+                                                    0, 0, 0);
+      // s[r]: key kbase + acc_row(r), query q
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbase + acc_row(r, lane);
+        const float v = (key <= q && key < a.T) ? s[r] * scale : -INFINITY;
+        s[r] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mnew = fmaxf(m, mx);
+      const float alpha = (m == -INFINITY) ? 0.f : expf(m - mnew);
+      float p[16], rs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = (s[r] == -INFINITY) ? 0.f : expf(s[r] - mnew);
+        rs += p[r];
+      }
+      rs += __shfl_xor(rs, 32, 64);
+      lsum = lsum * alpha + rs;
+      m = mnew;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        oacc[0][e] *= alpha;
+        oacc[1][e] *= alpha;
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8_t pb = pack_bf16(p + 8 * c);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm(Vt + sub * 32, db * 32 + (lane & 31), c, g),
+                                                             pb, oacc[db], 0, 0, 0);
+      }
+    }
+  }
+  if (q < a.T) {
+    const float inv = 1.0f / lsum;
+    uint16_t* o = (uint16_t*)a.o + ((int64_t)b * a.T + q) * a.d + h * a.dh;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int j = db * 32 + acc_row(4 * rg, lane);   // 4 consecutive head dims
+        uint32_t w0 = (uint32_t)f2bf(oacc[db][4 * rg] * inv) | ((uint32_t)f2bf(oacc[db][4 * rg + 1] * inv) << 16);
+        uint32_t w1 = (uint32_t)f2bf(oacc[db][4 * rg + 2] * inv) | ((uint32_t)f2bf(oacc[db][4 * rg + 3] * inv) << 16);
+        *(uint2*)(o + j) = make_uint2(w0, w1);
+      }
+    if (g == 0) a.lse[((int64_t)b * a.H + h) * a.T + q] = m + logf(lsum);
+  }
+}
+
+// ---------------------------------------------------------------- backward, key side
+// tile = (b, h, block of 128 keys), most work first; wave w owns 32 keys.
+// S = Q K^T with lanes on keys: P, dP and dS come out as B operands for
+// dV^T += dO^T P and dK^T += Q^T dS.
+
+__device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
+  uint16_t* Qs = (uint16_t*)smem;        // [64 q][dh]
+  uint16_t* Qt = Qs + 64 * kAP;          // [dh][64 q]
+  uint16_t* Ds = Qt + 64 * kAP;          // dO [64 q][dh]
+  uint16_t* Dt = Ds + 64 * kAP;          // dO^T [dh][64 q]
+  float* lse_s = (float*)(Dt + 64 * kAP);
+  float* dd_s = lse_s + 64;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, g = lane >> 5;
+  const int BH = a.B * a.H;
+  const int kblk = tile / BH, bh = tile % BH, b = bh / a.H, h = bh % a.H;
+  const int64_t ld = 3 * (int64_t)a.d;
+  const uint16_t* base = (const uint16_t*)a.qkv + (int64_t)b * a.T * ld + h * a.dh;
+  const uint16_t* dob = (const uint16_t*)a.dout + (int64_t)b * a.T * a.d + h * a.dh;
+  const float* lse = a.lse + ((int64_t)b * a.H + h) * a.T;
+  const float* dsum = a.dsum + ((int64_t)b * a.H + h) * a.T;
+  const int k0 = kblk * 128, kw = k0 + 32 * w, key = kw + (lane & 31);
+  const float scale = 1.0f / sqrtf((float)a.dh);
+  bf16x8_t kf[4], vf[4];
+  attn_row_frags(kf, base + a.d, ld, key, key < a.T, lane);
+  attn_row_frags(vf, base + 2 * a.d, ld, key, key < a.T, lane);
+  f32x16_t dk[2], dv[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) dk[0][e] = dk[1][e] = dv[0][e] = dv[1][e] = 0.f;
+  const int nqb = (a.T + 63) / 64;
+  for (int qb = k0 / 64; qb < nqb; ++qb) {
+    const int q0 = qb * 64, nv = min(64, a.T - q0);
+    __syncthreads();
+    attn_load_block(base, ld, q0, nv, Qs, Qt);
+    attn_load_block(dob, a.d, q0, nv, Ds, Dt);
+    if (threadIdx.x < 64) {
+      const int qq = q0 + threadIdx.x;
+      lse_s[threadIdx.x] = qq < a.T ? lse[qq] : INFINITY;
+      dd_s[threadIdx.x] = qq < a.T ? dsum[qq] : 0.f;
+    }
+    __syncthreads();
+    if (kw >= a.T) continue;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int qs0 = q0 + sub * 32;
+      if (qs0 + 31 < kw || qs0 >= a.T) continue;   // every query of the chunk precedes the wave's keys
+      f32x16_t s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(Qs, sub * 32 + (lane & 31), 16 * kk + 8 * g), kf[kk], s,
+                                                    0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(Ds, sub * 32 + (lane & 31), 16 * kk + 8 * g), vf[kk],
+                                                     dp, 0, 0, 0);
+      }
+      // s[r], dp[r]: query qs0 + acc_row(r), key `key`
+      float p[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = sub * 32 + acc_row(r, lane);
+        const int qq = q0 + ql;
+        const float pv = (key <= qq && qq < a.T) ? expf(s[r] * scale - lse_s[ql]) : 0.f;
+        p[r] = pv;
+        ds[r] = pv * (dp[r] - dd_s[ql]);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8_t pb = pack_bf16(p + 8 * c), sb = pack_bf16(ds + 8 * c);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm(Dt + sub * 32, db * 32 + (lane & 31), c, g), pb,
+                                                           dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm(Qt + sub * 32, db * 32 + (lane & 31), c, g), sb,
+                                                           dk[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (key < a.T) {
+    uint16_t* out = (uint16_t*)a.dqkv + ((int64_t)b * a.T + key) * ld + h * a.dh;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int j = db * 32 + acc_row(4 * rg, lane);
+        uint32_t k0w = (uint32_t)f2bf(dk[db][4 * rg] * scale) | ((uint32_t)f2bf(dk[db][4 * rg + 1] * scale) << 16);
+        uint32_t k1w = (uint32_t)f2bf(dk[db][4 * rg + 2] * scale) | ((uint32_t)f2bf(dk[db][4 * rg + 3] * scale) << 16);
+        *(uint2*)(out + a.d + j) = make_uint2(k0w, k1w);
+        uint32_t v0w = (uint32_t)f2bf(dv[db][4 * rg]) | ((uint32_t)f2bf(dv[db][4 * rg + 1]) << 16);
+        uint32_t v1w = (uint32_t)f2bf(dv[db][4 * rg + 2]) | ((uint32_t)f2bf(dv[db][4 * rg + 3]) << 16);
+        *(uint2*)(out + 2 * a.d + j) = make_uint2(v0w, v1w);
+      }
+  }
+}
+
+// ---------------------------------------------------------------- backward, query side
+// tile = (b, h, block of 128 queries), largest first; wave w owns 32 queries.
+// S^T = K Q^T with lanes on queries: dS^T comes out as the B operand of dQ^T += K^T dS^T.
+
+__device__ void task_attn_bwd_q_mfma(const AttnArgs& a, int tile, char* smem) {
+  uint16_t* Ks = (uint16_t*)smem;        // [64 keys][dh]
+  uint16_t* Vs = Ks + 64 * kAP;          // [64 keys][dh]
+  uint16_t* Kt = Vs + 64 * kAP;          // [dh][64 keys]
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, g = lane >> 5;
+  const int BH = a.B * a.H, nqb = (a.T + 127) / 128;
+  const int qblk = nqb - 1 - tile / BH, bh = tile % BH, b = bh / a.H, h = bh % a.H;
+  const int64_t ld = 3 * (int64_t)a.d;
+  const uint16_t* base = (const uint16_t*)a.qkv + (int64_t)b * a.T * ld + h * a.dh;
+  const uint16_t* dob = (const uint16_t*)a.dout + (int64_t)b * a.T * a.d + h * a.dh;
+  const int q0 = qblk * 128, qw = q0 + 32 * w, q = qw + (lane & 31);
+  const bool qv = q < a.T;
+  const float scale = 1.0f / sqrtf((float)a.dh);
+  bf16x8_t qf[4], df[4];
+  attn_row_frags(qf, base, ld, q, qv, lane);
+  attn_row_frags(df, dob, a.d, q, qv, lane);
+  const int64_t st = ((int64_t)b * a.H + h) * a.T + (qv ? q : 0);
+  const float lse_q = qv ? a.lse[st] : 0.f, d_q = qv ? a.dsum[st] : 0.f;
+  f32x16_t dq[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) dq[0][e] = dq[1][e] = 0.f;
+  const int kend = min(q0 + 128, a.T);
+  const int nkb = (kend + 63) / 64;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int nv = min(64, a.T - kb * 64);
+    __syncthreads();
+    attn_load_block(base + a.d, ld, kb * 64, nv, Ks, Kt);
+    attn_load_block(base + 2 * a.d, ld, kb * 64, nv, Vs, nullptr);
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kbase = kb * 64 + sub * 32;
+      if (kbase > qw + 31 || kbase >= a.T) continue;
+      f32x16_t s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(Ks, sub * 32 + (lane & 31), 16 * kk + 8 * g), qf[kk], s,
+                                                    0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag16(Vs, sub * 32 + (lane & 31), 16 * kk + 8 * g), df[kk],
+                                                     dp, 0, 0, 0);
+      }
+      // s[r], dp[r]: key kbase + acc_row(r), query q
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbase + acc_row(r, lane);
+        const float pv = (key <= q && key < a.T && qv) ? expf(s[r] * scale - lse_q) : 0.f;
+        ds[r] = pv * (dp[r] - d_q);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8_t sb = pack_bf16(ds + 8 * c);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm(Kt + sub * 32, db * 32 + (lane & 31), c, g), sb,
+                                                           dq[db], 0, 0, 0);
+      }
+    }
+  }
+  if (qv) {
+    uint16_t* out = (uint16_t*)a.dqkv + ((int64_t)b * a.T + q) * ld + h * a.dh;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int j = db * 32 + acc_row(4 * rg, lane);
+        uint32_t w0 = (uint32_t)f2bf(dq[db][4 * rg] * scale) | ((uint32_t)f2bf(dq[db][4 * rg + 1] * scale) << 16);
+        uint32_t w1 = (uint32_t)f2bf(dq[db][4 * rg + 2] * scale) | ((uint32_t)f2bf(dq[db][4 * rg + 3] * scale) << 16);
+        *(uint2*)(out + j) = make_uint2(w0, w1);
+      }
+  }
+}
+
+}  // namespace ofa

@@ -403,7 +403,9 @@ void build_train(ofa_handle* h) {
   auto CSF = [&](int l) { return at<float>(ws, w.cs_fc) + (int64_t)l * w.cs_tiles * F; };
   auto CSQ = [&](int l) { return at<float>(ws, w.cs_qkv) + (int64_t)l * w.cs_tiles * 3 * d; };
   const int lnt = w.ln_tiles;
-  const int attn_block = 16;
+  // bf16 with 64-wide heads runs the MFMA attention (128 rows per tile), else the plain one
+  const int attn_impl = (c.precision == OFA_BF16 && D.dh == 64) ? 1 : 0;
+  const int attn_block = attn_impl ? 128 : 16;
   const int attn_tiles = (int)(D.B * D.H * cdiv(D.T, attn_block));
 
   auto ln_fwd = [&](int i, int dep, const char* nm) {
@@ -445,7 +447,7 @@ void build_train(ofa_handle* h) {
     a.d = (int)d;
     a.dt = lp;
     a.block = attn_block;
-    a.impl = 0;
+    a.impl = attn_impl;
     return a;
   };
   auto rope_args = [&](void* buf) {

@@ -18,6 +18,7 @@
 
 #include "k_simple.h"
 #include "k_mfma.h"
+#include "k_attn.h"
 #include "k_decode.h"
 #include "ofa_launch.h"
 
@@ -35,7 +36,8 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   }
   else if constexpr (OP == OP_ROPE) task_rope(ph.a.rope, tile, false);
   else if constexpr (OP == OP_ATTN_FWD) {
-    task_attn_fwd_simple(ph.a.attn, tile, smem);
+    if (ph.a.attn.impl == 1) task_attn_fwd_mfma(ph.a.attn, tile, smem);
+    else task_attn_fwd_simple(ph.a.attn, tile, smem);
   }
   else if constexpr (OP == OP_GEGLU_FWD) task_geglu_fwd(ph.a.geglu, tile);
   else if constexpr (OP == OP_CE) task_ce(ph.a.ce, tile, tc, smem);
@@ -45,10 +47,12 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   else if constexpr (OP == OP_COLRED) task_colred(ph.a.cr, tile);
   else if constexpr (OP == OP_ATTN_PREP) task_attn_prep(ph.a.attn, tile);
   else if constexpr (OP == OP_ATTN_BWD_KV) {
-    task_attn_bwd_kv_simple(ph.a.attn, tile, smem);
+    if (ph.a.attn.impl == 1) task_attn_bwd_kv_mfma(ph.a.attn, tile, smem);
+    else task_attn_bwd_kv_simple(ph.a.attn, tile, smem);
   }
   else if constexpr (OP == OP_ATTN_BWD_Q) {
-    task_attn_bwd_q_simple(ph.a.attn, tile, smem);
+    if (ph.a.attn.impl == 1) task_attn_bwd_q_mfma(ph.a.attn, tile, smem);
+    else task_attn_bwd_q_simple(ph.a.attn, tile, smem);
   }
   else if constexpr (OP == OP_ROPE_BWD) task_rope(ph.a.rope, tile, true);
   else if constexpr (OP == OP_EMB_SORT) task_emb_sort(ph.a.esort, tc, smem);
@@ -199,11 +203,11 @@ static size_t lds_for(const Phase& ph) {
     case OP_GEMM: return ph.a.gemm.impl == GEMM_MFMA ? gemm_mfma_lds_bytes() : sizeof(GemmSmemSimple);
     case OP_LN_BWD: return (size_t)kWaves * 3 * ph.a.lnb.d * sizeof(float);
     case OP_ATTN_FWD:
-      return (size_t)kWaves * (64 + ph.a.attn.T) * sizeof(float);
+      return ph.a.attn.impl == 1 ? attn_mfma_lds_bytes() : (size_t)kWaves * (64 + ph.a.attn.T) * sizeof(float);
     case OP_ATTN_BWD_KV:
-      return (size_t)kWaves * 256 * sizeof(float);
+      return ph.a.attn.impl == 1 ? attn_mfma_lds_bytes() : (size_t)kWaves * 256 * sizeof(float);
     case OP_ATTN_BWD_Q:
-      return (size_t)kWaves * 192 * sizeof(float);
+      return ph.a.attn.impl == 1 ? attn_mfma_lds_bytes() : (size_t)kWaves * 192 * sizeof(float);
     case OP_CE: case OP_LOSS: return 64;
     case OP_EMB_SORT: {
       int n = 1;
