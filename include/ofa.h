@@ -181,7 +181,8 @@ typedef struct {
   int32_t n_phases;         /* phases of one training step */
   int32_t n_tiles_step;     /* tiles of one training step */
   int32_t grid;             /* workgroups of the last persistent launch */
-  int32_t reserved[5];
+  int32_t n_tickets_step;   /* tickets of one training step (persistent executor) */
+  int32_t reserved[4];
 } ofa_stats;
 
 ofa_status ofa_status_sync(ofa_handle *h, ofa_stats *out);

@@ -146,28 +146,34 @@ __device__ void task_ln_bwd(const LnBwdArgs& a, int tile, char* smem) {
 
 // ---------------------------------------------------------------- column sums
 
+// tile = (row chunk, block of 256 columns); partials[row chunk][col]
 __device__ void task_colsum(const ColsumArgs& a, int tile) {
-  const int r0 = tile * a.rows_per_tile;
+  const int ncb = (a.cols + kThreads - 1) / kThreads;
+  const int rc = tile / ncb, cb = tile % ncb;
+  const int r0 = rc * a.rows_per_tile;
   const int r1 = min(r0 + a.rows_per_tile, a.rows);
-  float* out = a.partials + (int64_t)tile * a.cols;
-  for (int c = threadIdx.x; c < a.cols; c += kThreads) {
-    float s = 0.f;
-    for (int r = r0; r < r1; ++r) s += ldf(a.src, (int64_t)r * a.ld + c, a.dt);
-    out[c] = s;
-  }
+  const int c = cb * kThreads + threadIdx.x;
+  if (c >= a.cols) return;
+  float s = 0.f;
+  for (int r = r0; r < r1; ++r) s += ldf(a.src, (int64_t)r * a.ld + c, a.dt);
+  a.partials[(int64_t)rc * a.cols + c] = s;
 }
 
-__device__ void task_colred(const ColredArgs& a, int tile) {
-  const int c0 = tile * a.cols_per_tile;
-  const int c1 = min(c0 + a.cols_per_tile, a.cols);
-  for (int c = c0 + (int)threadIdx.x; c < c1; c += kThreads) {
-    for (int k = 0; k < a.n_vec; ++k) {
-      float* o = a.out[k];
-      if (!o) continue;
-      float s = 0.f;
-      for (int p = 0; p < a.n_parts; ++p) s += a.partials[((int64_t)p * a.n_vec + k) * a.cols + c];
-      o[c] = s;
-    }
+// tile = block of 64 columns; four groups of 64 threads each sum every fourth
+// partial in order, then the groups combine in a fixed order
+__device__ void task_colred(const ColredArgs& a, int tile, char* smem) {
+  float* red = (float*)smem;   // [4][64]
+  const int c = tile * 64 + (threadIdx.x & 63), grp = threadIdx.x >> 6;
+  for (int k = 0; k < a.n_vec; ++k) {
+    float* o = a.out[k];
+    if (!o) continue;   // uniform across the workgroup
+    float s = 0.f;
+    if (c < a.cols)
+      for (int p = grp; p < a.n_parts; p += 4) s += a.partials[((int64_t)p * a.n_vec + k) * a.cols + c];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    if (grp == 0 && c < a.cols) o[c] = ((red[threadIdx.x] + red[64 + threadIdx.x]) + red[128 + threadIdx.x]) + red[192 + threadIdx.x];
+    __syncthreads();
   }
 }
 

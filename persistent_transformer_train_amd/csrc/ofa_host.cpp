@@ -366,6 +366,23 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
   return g;
 }
 
+// tile and ticket prefix sums; a ticket groups tiles so that a large phase
+// hands out at most ~512 tickets (each ticket costs one release fence)
+constexpr int kTicketsPerPhase = 512;
+
+void finish_program(std::vector<Phase>& prog) {
+  int tiles = 0, tickets = 0;
+  for (auto& ph : prog) {
+    ph.tile_base = tiles;
+    tiles += ph.n_tiles;
+    ph.per_ticket = std::max(1, cdiv(ph.n_tiles, kTicketsPerPhase));
+    ph.n_tickets = cdiv(ph.n_tiles, ph.per_ticket);
+    ph.ticket_base = tickets;
+    tickets += ph.n_tickets;
+    ph.lds_bytes = (int)phase_lds_bytes(ph);
+  }
+}
+
 void build_train(ofa_handle* h) {
   const ofa_config& c = h->cfg;
   const Dims& D = h->D;
@@ -593,7 +610,7 @@ void build_train(ofa_handle* h) {
     return p;
   };
   auto ln_red = [&](int i, int dep, float* og, float* ob, float* ores, const char* nm) {
-    int p = b.add(OP_COLRED, cdiv(d, 256), nm, {dep});
+    int p = b.add(OP_COLRED, cdiv(d, 64), nm, {dep});
     ColredArgs& a = b[p].a.cr;
     a.partials = LNP(i);
     a.out[0] = og;
@@ -602,12 +619,12 @@ void build_train(ofa_handle* h) {
     a.n_parts = lnt;
     a.n_vec = 3;
     a.cols = (int)d;
-    a.cols_per_tile = 256;
+    a.cols_per_tile = 64;
     return p;
   };
   auto colsum = [&](const void* src, int64_t ld, int cols, float* part, float* out, int dep, int dep2,
                     const char* nm) {
-    int p = b.add(OP_COLSUM, w.cs_tiles, nm, {dep, dep2});
+    int p = b.add(OP_COLSUM, w.cs_tiles * cdiv(cols, 256), nm, {dep, dep2});
     ColsumArgs& a = b[p].a.cs;
     a.src = src;
     a.ld = ld;
@@ -616,14 +633,14 @@ void build_train(ofa_handle* h) {
     a.cols = cols;
     a.rows_per_tile = kCsRows;
     a.dt = lp;
-    int q = b.add(OP_COLRED, cdiv(cols, 256), "bias_grad", {p});
+    int q = b.add(OP_COLRED, cdiv(cols, 64), "bias_grad", {p});
     ColredArgs& r = b[q].a.cr;
     r.partials = part;
     r.out[0] = out;
     r.n_parts = w.cs_tiles;
     r.n_vec = 1;
     r.cols = cols;
-    r.cols_per_tile = 256;
+    r.cols_per_tile = 64;
     return q;
   };
   int p_lnf_b = ln_bwd(2 * (int)L, h->lay.lnf_g, -1, {p_head_dx}, "lnf_bwd");
@@ -740,13 +757,7 @@ void build_train(ofa_handle* h) {
   // the next step's forward overwrites activations this step's backward reads
   b[p_emb].dep_prev = p_adam;
   b[p_sort].dep_prev = p_adam;
-  // tile prefix sums
-  int acc = 0;
-  for (auto& ph : h->train) {
-    ph.tile_base = acc;
-    acc += ph.n_tiles;
-    ph.lds_bytes = (int)phase_lds_bytes(ph);
-  }
+  finish_program(h->train);
 }
 
 // decode program for one position (head phases skip themselves when the
@@ -856,12 +867,7 @@ void build_decode(ofa_handle* h) {
     a.keep = (int)D.keep;
   }
   b[p_emb].dep_prev = p_am;
-  int acc = 0;
-  for (auto& ph : h->dec) {
-    ph.tile_base = acc;
-    acc += ph.n_tiles;
-    ph.lds_bytes = (int)phase_lds_bytes(ph);
-  }
+  finish_program(h->dec);
 }
 
 double lr_at(const ofa_config& c, uint64_t step) {
@@ -1186,7 +1192,7 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
     memset(&pp, 0, sizeof pp);
     pp.phases = h->d_train;
     pp.n_phases = np;
-    pp.tiles_per_inst = h->train.back().tile_base + h->train.back().n_tiles;
+    pp.tickets_per_inst = h->train.back().ticket_base + h->train.back().n_tickets;
     pp.n_inst = n_steps;
     pp.steps = d_steps;
     pp.sched = sc;
@@ -1303,6 +1309,7 @@ ofa_status ofa_status_sync(ofa_handle* h, ofa_stats* out) {
     out->n_phases = (int32_t)h->train.size();
     out->n_tiles_step = h->train.back().tile_base + h->train.back().n_tiles;
     out->grid = h->last_grid;
+    out->n_tickets_step = h->train.back().ticket_base + h->train.back().n_tickets;
   }
   return ds.code ? (ofa_status)ds.code : OFA_OK;
 }

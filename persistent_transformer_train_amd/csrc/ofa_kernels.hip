@@ -44,7 +44,7 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   else if constexpr (OP == OP_LOSS) task_loss(ph.a.loss, tc, smem);
   else if constexpr (OP == OP_LN_BWD) task_ln_bwd(ph.a.lnb, tile, smem);
   else if constexpr (OP == OP_COLSUM) task_colsum(ph.a.cs, tile);
-  else if constexpr (OP == OP_COLRED) task_colred(ph.a.cr, tile);
+  else if constexpr (OP == OP_COLRED) task_colred(ph.a.cr, tile, smem);
   else if constexpr (OP == OP_ATTN_PREP) task_attn_prep(ph.a.attn, tile);
   else if constexpr (OP == OP_ATTN_BWD_KV) {
     if (ph.a.attn.impl == 1) task_attn_bwd_kv_mfma(ph.a.attn, tile, smem);
@@ -97,79 +97,90 @@ __global__ __launch_bounds__(kThreads) void phase_kernel(const Phase* phases, in
 
 // ---------------------------------------------------------------- executor 2: persistent
 
+// Polls a completion counter with relaxed loads (the caller issues one
+// acquire fence once every wait has succeeded).  Gives up when the scheduler
+// aborts or when the watchdog deadline passes.
 __device__ __forceinline__ bool wait_count(const uint64_t* ctr, uint64_t need, const PersistParams& p,
                                            const TaskCtx& tc) {
+  if (ld_relaxed(ctr) >= need) return true;
   const uint64_t start = now_ticks();
-  int spins = 0;
-  while (ld_acquire(ctr) < need) {
+  for (int spins = 0;; ++spins) {
+    if (ld_relaxed(ctr) >= need) return true;
     if (ld_relaxed(&p.sched->abort)) return false;
-    if (++spins > 64) {
-      __builtin_amdgcn_s_sleep(2);
-      if ((spins & 255) == 0 && now_ticks() - start > p.watchdog_ticks) {
-        raise_status(p.status, -4 /*OFA_E_TIMEOUT*/, tc.phase, tc.step, (int64_t)need);
-        st_release(&p.sched->abort, 1);
-        return false;
-      }
+    __builtin_amdgcn_s_sleep(1);
+    if ((spins & 63) == 63 && now_ticks() - start > p.watchdog_ticks) {
+      raise_status(p.status, -4 /*OFA_E_TIMEOUT*/, tc.phase, tc.step, (int64_t)need);
+      st_release(&p.sched->abort, 1);
+      return false;
     }
   }
-  return true;
 }
 
-__global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
+__global__ __launch_bounds__(kThreads, 2) void persistent_kernel(PersistParams p) {
   extern __shared__ __align__(16) char smem[];
   __shared__ uint64_t s_ticket;
   __shared__ int s_ok;
+  __shared__ int64_t s_all_checked;   // instance whose every phase this workgroup saw complete
   const uint64_t base = p.sched->base;
-  const uint64_t total = (uint64_t)p.n_inst * (uint64_t)p.tiles_per_inst;
+  const uint64_t total = (uint64_t)p.n_inst * (uint64_t)p.tickets_per_inst;
+  if (threadIdx.x == 0) s_all_checked = -1;
   for (;;) {
     if (threadIdx.x == 0) s_ticket = add_relaxed(&p.sched->ticket, 1) - base;
     __syncthreads();
     const uint64_t t = s_ticket;
     if (t >= total) break;
-    const int64_t inst = (int64_t)(t / (uint64_t)p.tiles_per_inst);
-    const int r = (int)(t % (uint64_t)p.tiles_per_inst);
-    // phase owning tile r: last phase whose tile_base <= r
+    const int64_t inst = (int64_t)(t / (uint64_t)p.tickets_per_inst);
+    const int r = (int)(t % (uint64_t)p.tickets_per_inst);
+    // phase owning ticket r: last phase whose ticket_base <= r
     int lo = 0, hi = p.n_phases - 1;
     while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (p.phases[mid].tile_base <= r) lo = mid; else hi = mid - 1;
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.phases[mid].ticket_base <= r) lo = mid; else hi = mid - 1;
     }
     const int pi = lo;
     const Phase& ph = p.phases[pi];
-    int tile = r - ph.tile_base;
-    if (p.shuffle && ph.n_tiles > 1) {
-      // reversal after a rotation: a permutation of the phase's tiles
-      const int rot = (int)(((uint64_t)inst * 977u + 31u) % (uint64_t)ph.n_tiles);
-      tile = ph.n_tiles - 1 - (tile + rot) % ph.n_tiles;
-    }
+    const int j = r - ph.ticket_base;
+    int tile0 = j * ph.per_ticket;
+    const int tile1 = min(tile0 + ph.per_ticket, ph.n_tiles);
     TaskCtx tc{p.steps + inst, p.status, pi, inst};
-    // wait for dependencies (thread 0), then acquire for the whole workgroup
+    // wait for the dependencies (thread 0), then one acquire for the workgroup
     if (threadIdx.x == 0) {
       bool ok = true;
       for (int d = 0; d < kMaxDeps && ok; ++d) {
-        int q = ph.dep[d];
+        const int q = ph.dep[d];
         if (q == -2) {
-          for (int qq = 0; qq < pi && ok; ++qq)
-            ok = wait_count(&p.sched->done[qq], base + (uint64_t)(inst + 1) * p.phases[qq].n_tiles, p, tc);
+          if (s_all_checked != inst) {
+            for (int qq = 0; qq < pi && ok; ++qq)
+              ok = wait_count(&p.sched->done[qq], base + (uint64_t)(inst + 1) * p.phases[qq].n_tiles, p, tc);
+            if (ok) s_all_checked = inst;
+          }
         } else if (q >= 0) {
           ok = wait_count(&p.sched->done[q], base + (uint64_t)(inst + 1) * p.phases[q].n_tiles, p, tc);
         }
       }
       if (ok && ph.dep_prev >= 0 && inst > 0)
         ok = wait_count(&p.sched->done[ph.dep_prev], base + (uint64_t)inst * p.phases[ph.dep_prev].n_tiles, p, tc);
+      if (ok) fence_acquire_agent();
       s_ok = ok ? 1 : 0;
     }
     __syncthreads();
     if (!s_ok) break;
-    fence_acquire_agent();
     const uint64_t t0 = now_ticks();
-    run_any(ph, tile, tc, smem);
-    // publish: every thread's writes are complete and visible at agent scope
-    // before the completion counter moves
-    fence_release_agent();
+    for (int tile = tile0; tile < tile1; ++tile) {
+      int tl = tile;
+      if (p.shuffle && ph.n_tiles > 1) {
+        // reversal after a rotation: a permutation of the phase's tiles
+        const int rot = (int)(((uint64_t)inst * 977u + 31u) % (uint64_t)ph.n_tiles);
+        tl = ph.n_tiles - 1 - (tile + rot) % ph.n_tiles;
+      }
+      run_any(ph, tl, tc, smem);
+    }
+    // publish: the barrier makes every wave's stores complete; one agent-scope
+    // release fence then makes them visible before the counter moves
     __syncthreads();
     if (threadIdx.x == 0) {
-      add_release(&p.sched->done[pi], 1);
+      fence_release_agent();
+      add_relaxed(&p.sched->done[pi], (uint64_t)(tile1 - tile0));
       if (p.times) {
         atomicMin((unsigned long long*)&p.times[pi].t0, (unsigned long long)t0);
         atomicMax((unsigned long long*)&p.times[pi].t1, (unsigned long long)now_ticks());
@@ -209,6 +220,7 @@ static size_t lds_for(const Phase& ph) {
     case OP_ATTN_BWD_Q:
       return ph.a.attn.impl == 1 ? attn_mfma_lds_bytes() : (size_t)kWaves * 192 * sizeof(float);
     case OP_CE: case OP_LOSS: return 64;
+    case OP_COLRED: return 4 * 64 * sizeof(float);
     case OP_EMB_SORT: {
       int n = 1;
       while (n < ph.a.esort.BT) n <<= 1;

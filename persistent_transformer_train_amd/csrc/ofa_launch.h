@@ -10,7 +10,7 @@ namespace ofa {
 struct PersistParams {
   const Phase* phases;       // one program instance's phase table
   int32_t n_phases;
-  int32_t tiles_per_inst;    // sum of n_tiles over the phases
+  int32_t tickets_per_inst;  // sum of n_tickets over the phases
   int64_t n_inst;            // instances (training steps) to run
   const StepCtx* steps;      // [n_inst]
   Sched* sched;

@@ -250,10 +250,14 @@ struct Phase {
   int32_t op;
   int32_t n_tiles;
   int32_t tile_base;          // first tile of this phase inside one program instance
-  int32_t dep[kMaxDeps];      // phases of the same instance that must be complete (-1 = none)
+  int32_t dep[kMaxDeps];      // phases of the same instance that must be complete
+                              // (-1 = none, -2 = every earlier phase)
   int32_t dep_prev;           // phase of the previous instance that must be complete (-1 = none)
   int32_t lds_bytes;
-  int32_t pad[7];
+  int32_t per_ticket;         // persistent executor: tiles claimed by one ticket
+  int32_t n_tickets;          // ceil(n_tiles / per_ticket)
+  int32_t ticket_base;        // first ticket of this phase inside one program instance
+  int32_t pad[4];
   PhaseArgs a;
 };
 

@@ -46,7 +46,7 @@ class ofa_stats(C.Structure):
         ("status", C.c_int32), ("err_phase", C.c_int32), ("err_step", C.c_int64), ("err_info", C.c_int64),
         ("tickets_claimed", C.c_uint64), ("steps_done", C.c_uint64), ("version", C.c_uint64),
         ("last_call_ms", C.c_double), ("n_phases", C.c_int32), ("n_tiles_step", C.c_int32),
-        ("grid", C.c_int32), ("reserved", C.c_int32 * 5),
+        ("grid", C.c_int32), ("n_tickets_step", C.c_int32), ("reserved", C.c_int32 * 4),
     ]
 
 

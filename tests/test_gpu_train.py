@@ -144,7 +144,7 @@ def test_counter_base_near_2_pow_32():
     h, cfg, stream, init, gl = gpu_run("c1", 3, PERSISTENT, debug_counter_base=2 ** 32 - 10)
     ol, _ = oracle_losses(cfg, stream, init, 3, np.float64)
     assert np.abs(gl - ol).max() / abs(ol[0]) <= 1e-4
-    assert h.last_stats.tickets_claimed >= 3 * h.last_stats.n_tiles_step
+    assert h.last_stats.tickets_claimed >= 3 * h.last_stats.n_tickets_step
     h.close()
 
 
