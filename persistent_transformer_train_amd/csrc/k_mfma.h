@@ -108,36 +108,70 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* lds, int row, int k
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-// fast epilogues (plain store with optional bias, residual add) inline; the
-// GELU family goes through the shared element-wise epilogue
+// Epilogue through LDS: the waves park their accumulators in LDS (fp32,
+// [rows][128]), then all 256 threads walk the tile (thread -> column, rows in
+// steps of two), so each epilogue variant is one small loop with coalesced
+// stores and no per-element branching.  In bf16 mode every low-precision
+// operand of an epilogue (C, aux) is bf16.
+template <int EPI, bool CF32>
+__device__ __forceinline__ void epi_tile(const GemmArgs& g, const float* cst, int rows, int row0, int n0) {
+  const int c = threadIdx.x & 127, col = n0 + c;
+  if (col >= g.N) return;
+  const float bias = g.bias ? g.bias[col] : 0.f;
+  const int rend = min(rows, g.M - row0);
+  for (int r = threadIdx.x >> 7; r < rend; r += 2) {
+    const int row = row0 + r;
+    const float v = cst[r * 128 + c] + bias;
+    const int64_t ci = (int64_t)row * g.ldc + col;
+    if constexpr (EPI == EPI_STORE) {
+      if constexpr (CF32) ((float*)g.C)[ci] = v;
+      else ((uint16_t*)g.C)[ci] = f2bf(v);
+    } else if constexpr (EPI == EPI_RESID) {
+      ((float*)g.C)[ci] = g.resid[(int64_t)row * g.ldres + col] + v;
+    } else if constexpr (EPI == EPI_GELU) {
+      ((uint16_t*)g.C)[ci] = f2bf(v);
+      ((uint16_t*)g.aux)[(int64_t)row * g.ldaux + col] = f2bf(gelu_f(v));
+    } else if constexpr (EPI == EPI_DGELU) {
+      const float u = bf2f(((const uint16_t*)g.aux)[(int64_t)row * g.ldaux + col]);
+      ((uint16_t*)g.C)[ci] = f2bf(v * gelu_grad_f(u));
+    } else {   // EPI_DGEGLU
+      const int64_t ai = (int64_t)row * g.ldaux + col;
+      const float gt = bf2f(((const uint16_t*)g.aux)[ai]);
+      const float up = bf2f(((const uint16_t*)g.aux)[ai + g.aux_off]);
+      ((uint16_t*)g.C)[ci] = f2bf(v * up * gelu_grad_f(gt));
+      ((uint16_t*)g.C)[ci + g.aux_off] = f2bf(v * gelu_f(gt));
+    }
+  }
+}
+
+// `pass_rows` = 128 when the LDS holds the whole tile, 64 otherwise (two passes).
 __device__ __forceinline__ void gemm_mfma_epilogue(const GemmArgs& g, const f32x16_t (&acc)[2][2], int m0, int n0,
-                                                   int wm, int wn, int lane) {
-  const bool fast = g.epi == EPI_STORE || g.epi == EPI_RESID;
+                                                   int wm, int wn, int lane, float* cst, int pass_rows) {
+  for (int pass = 0; pass < 128 / pass_rows; ++pass) {
+    const int rbase = pass * pass_rows;
+    __syncthreads();
+    if (wm >= rbase && wm < rbase + pass_rows) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + wn + j * 32 + (lane & 31);
-    const bool cok = col < g.N;
-    const float bias = (g.bias && cok) ? g.bias[col] : 0.f;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        if (!cok || row >= g.M) continue;
-        if (fast) {
-          float v = acc[i][j][e] + bias;
-          const int64_t ci = (int64_t)row * g.ldc + col;
-          if (g.epi == EPI_RESID) {
-            ((float*)g.C)[ci] = g.resid[(int64_t)row * g.ldres + col] + v;
-          } else if (g.c_dt == DT_BF16) {
-            ((uint16_t*)g.C)[ci] = f2bf(v);
-          } else {
-            ((float*)g.C)[ci] = v;
+          for (int e = 0; e < 16; ++e) {
+            const int r = wm - rbase + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+            cst[r * 128 + wn + j * 32 + (lane & 31)] = acc[i][j][e];
           }
-        } else {
-          gemm_epilogue(g, row, col, acc[i][j][e]);
-        }
-      }
+    }
+    __syncthreads();
+    const int row0 = m0 + rbase;
+    switch (g.epi) {
+      case EPI_STORE:
+        if (g.c_dt == DT_F32) epi_tile<EPI_STORE, true>(g, cst, pass_rows, row0, n0);
+        else epi_tile<EPI_STORE, false>(g, cst, pass_rows, row0, n0);
+        break;
+      case EPI_RESID: epi_tile<EPI_RESID, true>(g, cst, pass_rows, row0, n0); break;
+      case EPI_GELU: epi_tile<EPI_GELU, false>(g, cst, pass_rows, row0, n0); break;
+      case EPI_DGELU: epi_tile<EPI_DGELU, false>(g, cst, pass_rows, row0, n0); break;
+      default: epi_tile<EPI_DGEGLU, false>(g, cst, pass_rows, row0, n0); break;
     }
   }
 }
@@ -194,7 +228,166 @@ __device__ void task_gemm_mfma(const GemmArgs& g, int tile, char* smem) {
       __syncthreads();
     }
   }
-  gemm_mfma_epilogue(g, acc, m0, n0, wm, wn, lane);
+  gemm_mfma_epilogue(g, acc, m0, n0, wm, wn, lane, (float*)smem, 64);
+}
+
+// ============================================================================
+// GEMM tile, pipelined version (K a multiple of 64; every strided operand's
+// contiguous dimension a multiple of 8).
+//
+// Operands stay in their memory layout in LDS: a k-contiguous operand as
+// [128 rows][64 k], a row-contiguous operand as [64 k][128 rows], both with
+// 16-byte chunks XOR-swizzled so that fragment reads avoid bank conflicts.
+// Global -> LDS copies use the direct-to-LDS loads of gfx950 into a two-stage
+// ring: the next k slice is in flight while the current one is multiplied.
+// Fragments of a k-contiguous operand are one 16-byte LDS read; fragments of
+// a row-contiguous operand are two transposing 8-byte reads
+// (ds_read_b64_tr_b16): within each group of 16 lanes, lane 4g+e receives
+// element e of the 4-element pieces addressed by lanes g, g+4, g+8, g+12, so
+// lane r addressing k row k0 + r/4 at columns c0 + 4*(r%4) makes every lane
+// receive four consecutive k of one column.
+// ============================================================================
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int kP3BK = 64;
+constexpr int kP3Stage = 128 * kP3BK;   // elements of one operand stage
+
+struct GemmSmemP3 {
+  uint16_t a[2][kP3Stage];
+  uint16_t b[2][kP3Stage];
+};
+
+__host__ __device__ constexpr size_t gemm_p3_lds_bytes() { return sizeof(GemmSmemP3); }
+
+// Issue the direct-to-LDS copy of one operand's (128 rows x 64 k) slice.
+// Wave w issues the 64-lane instructions w, w+4, w+8, w+12 (16 per slice);
+// lane L of instruction i fills physical 16-byte chunk p = 64 i + L.
+template <bool KMAJOR>
+__device__ __forceinline__ void p3_issue(const uint16_t* base, int64_t ld, int r0, int R, int k0, uint16_t* stage,
+                                         int wave, int lane) {
+  const uint16_t* src[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int p = (wave + 4 * q) * 64 + lane;
+    if (KMAJOR) {
+      // physical chunk p = 8 r + (c ^ (r & 7)): row r, logical k chunk c
+      const int r = p >> 3, c = (p & 7) ^ (r & 7);
+      const int rr = min(r0 + r, R - 1);   // rows past the end: any valid row (their outputs are dropped)
+      src[q] = base + (int64_t)rr * ld + k0 + c * 8;
+    } else {
+      // physical chunk p = 16 k + (c ^ 2(k & 7)): k row k, logical row chunk c
+      const int k = p >> 4, c = (p & 15) ^ (2 * (k & 7));
+      const int col = min(r0 + c * 8, R - 8);
+      src[q] = base + (int64_t)(k0 + k) * ld + col;
+    }
+  }
+  // The copies are issued as inline assembly so that the compiler does not
+  // track them: its own tracking would wait for every outstanding copy
+  // (gfx9 counts loads and copies on one counter) before any LDS read.  The
+  // waits are explicit (p3_wait_barrier).
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void_t*)(stage + (wave + 4 * q) * 64 * 8));   // wave-uniform
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src[q]), "s"(lds) : "memory", "m0");
+  }
+}
+
+// wait until at most N of this wave's vector-memory operations are
+// outstanding, then join the workgroup barrier
+template <int N>
+__device__ __forceinline__ void p3_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// this wave's LDS reads are complete, then join the workgroup barrier
+__device__ __forceinline__ void p3_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+__device__ __forceinline__ bf16x8_t p3_frag_k(const uint16_t* stage, int row, int kc) {
+  const int pc = kc ^ (row & 7);
+  return __builtin_bit_cast(bf16x8_t, *(const uint4*)(stage + row * kP3BK + pc * 8));
+}
+
+// fragment of rows rbase..rbase+31 (lane -> row rbase + lane%32), k16 chunk kk,
+// from a [64 k][128 rows] stage
+__device__ __forceinline__ bf16x8_t p3_frag_t(const uint16_t* stage, int rbase, int kk, int lane) {
+  const int G = lane >> 4, r = lane & 15;
+  const int col = rbase + 16 * (G & 1) + 4 * (r & 3);
+  const int c = col >> 3, sub = (col >> 2) & 1;
+  i16x4_t v[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int kr = kk * 16 + 8 * (G >> 1) + 4 * t + (r >> 2);
+    const int pc = c ^ (2 * (kr & 7));
+    v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(stage + kr * 128 + pc * 8 + sub * 4));
+  }
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  i16x8_t w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+template <bool AKM, bool BKM>
+__device__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
+  GemmSmemP3& s = *(GemmSmemP3*)smem;
+  const int tm = tile / g.tiles_n, tn = tile % g.tiles_n;
+  const int m0 = tm * kMBM, n0 = tn * kMBN;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const uint16_t* A = (const uint16_t*)g.A;
+  const uint16_t* B = (const uint16_t*)g.B;
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = g.K / kP3BK;
+  __syncthreads();   // the previous tile's readers are done with the ring
+  p3_issue<AKM>(A, g.lda, m0, g.M, 0, s.a[0], w, lane);
+  p3_issue<BKM>(B, g.ldb, n0, g.N, 0, s.b[0], w, lane);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      p3_issue<AKM>(A, g.lda, m0, g.M, (kt + 1) * kP3BK, s.a[cur ^ 1], w, lane);
+      p3_issue<BKM>(B, g.ldb, n0, g.N, (kt + 1) * kP3BK, s.b[cur ^ 1], w, lane);
+      p3_wait_barrier<8>();   // this slice has landed in every wave; the next one stays in flight
+    } else {
+      p3_wait_barrier<0>();
+    }
+    const uint16_t* sa = s.a[cur];
+    const uint16_t* sb = s.b[cur];
+#pragma unroll
+    for (int kk = 0; kk < kP3BK / 16; ++kk) {
+      bf16x8_t af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = AKM ? p3_frag_k(sa, wm + i * 32 + (lane & 31), 2 * kk + (lane >> 5)) : p3_frag_t(sa, wm + i * 32, kk, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = BKM ? p3_frag_k(sb, wn + j * 32 + (lane & 31), 2 * kk + (lane >> 5)) : p3_frag_t(sb, wn + j * 32, kk, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    p3_lds_barrier();   // every wave is done with this slice before it is refilled
+  }
+  gemm_mfma_epilogue(g, acc, m0, n0, wm, wn, lane, (float*)smem, 128);
+}
+
+__device__ void task_gemm_p3(const GemmArgs& g, int tile, char* smem) {
+  if (g.a_kmajor) {
+    if (g.b_kmajor) gemm_p3<true, true>(g, tile, smem); else gemm_p3<true, false>(g, tile, smem);
+  } else {
+    if (g.b_kmajor) gemm_p3<false, true>(g, tile, smem); else gemm_p3<false, false>(g, tile, smem);
+  }
 }
 
 }  // namespace ofa

@@ -197,7 +197,7 @@ __device__ __forceinline__ float gemm_b(const GemmArgs& g, int k, int n) {
   return ldf(g.B, i, g.b_dt);
 }
 
-__device__ __noinline__ void gemm_epilogue(const GemmArgs& g, int m, int n, float acc) {
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, int m, int n, float acc) {
   if (m >= g.M || n >= g.N) return;
   float v = acc + (g.bias ? g.bias[n] : 0.f);
   int64_t ci = (int64_t)m * g.ldc + n;

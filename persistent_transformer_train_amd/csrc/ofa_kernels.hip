@@ -31,7 +31,8 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   if constexpr (OP == OP_EMBED) task_embed(ph.a.emb, tile, tc);
   else if constexpr (OP == OP_LN_FWD) task_ln_fwd(ph.a.lnf, tile);
   else if constexpr (OP == OP_GEMM) {
-    if (ph.a.gemm.impl == GEMM_MFMA) task_gemm_mfma(ph.a.gemm, tile, smem);
+    if (ph.a.gemm.impl == GEMM_P3) task_gemm_p3(ph.a.gemm, tile, smem);
+    else if (ph.a.gemm.impl == GEMM_MFMA) task_gemm_mfma(ph.a.gemm, tile, smem);
     else task_gemm_simple(ph.a.gemm, tile, smem);
   }
   else if constexpr (OP == OP_ROPE) task_rope(ph.a.rope, tile, false);
@@ -95,6 +96,23 @@ __global__ __launch_bounds__(kThreads) void phase_kernel(const Phase* phases, in
   }
 }
 
+// one kernel per GEMM implementation, so each gets its own register budget
+template <int IMPL>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const Phase* phases, int idx, PhaseTime* times) {
+  extern __shared__ __align__(16) char smem[];
+  const Phase& ph = phases[idx];
+  const uint64_t t0 = now_ticks();
+  for (int tile = blockIdx.x; tile < ph.n_tiles; tile += gridDim.x) {
+    if constexpr (IMPL == GEMM_P3) task_gemm_p3(ph.a.gemm, tile, smem);
+    else if constexpr (IMPL == GEMM_MFMA) task_gemm_mfma(ph.a.gemm, tile, smem);
+    else task_gemm_simple(ph.a.gemm, tile, smem);
+  }
+  if (times && threadIdx.x == 0) {
+    atomicMin((unsigned long long*)&times[idx].t0, (unsigned long long)t0);
+    atomicMax((unsigned long long*)&times[idx].t1, (unsigned long long)now_ticks());
+  }
+}
+
 // ---------------------------------------------------------------- executor 2: persistent
 
 // Polls a completion counter with relaxed loads (the caller issues one
@@ -127,7 +145,9 @@ __global__ __launch_bounds__(kThreads, 2) void persistent_kernel(PersistParams p
   for (;;) {
     if (threadIdx.x == 0) s_ticket = add_relaxed(&p.sched->ticket, 1) - base;
     __syncthreads();
-    const uint64_t t = s_ticket;
+    // wave-uniform copy, so the phase table is read with scalar loads
+    const uint64_t t = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(s_ticket >> 32)) << 32) |
+                       (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)s_ticket);
     if (t >= total) break;
     const int64_t inst = (int64_t)(t / (uint64_t)p.tickets_per_inst);
     const int r = (int)(t % (uint64_t)p.tickets_per_inst);
@@ -164,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 2) void persistent_kernel(PersistParams p
       s_ok = ok ? 1 : 0;
     }
     __syncthreads();
-    if (!s_ok) break;
+    if (!__builtin_amdgcn_readfirstlane(s_ok)) break;
     const uint64_t t0 = now_ticks();
     for (int tile = tile0; tile < tile1; ++tile) {
       int tl = tile;
@@ -211,7 +231,9 @@ __global__ void fill_pairs_kernel(uint64_t* p, uint64_t a, uint64_t b, int64_t n
 
 static size_t lds_for(const Phase& ph) {
   switch (ph.op) {
-    case OP_GEMM: return ph.a.gemm.impl == GEMM_MFMA ? gemm_mfma_lds_bytes() : sizeof(GemmSmemSimple);
+    case OP_GEMM:
+      return ph.a.gemm.impl == GEMM_P3 ? gemm_p3_lds_bytes()
+             : ph.a.gemm.impl == GEMM_MFMA ? gemm_mfma_lds_bytes() : sizeof(GemmSmemSimple);
     case OP_LN_BWD: return (size_t)kWaves * 3 * ph.a.lnb.d * sizeof(float);
     case OP_ATTN_FWD:
       return ph.a.attn.impl == 1 ? attn_mfma_lds_bytes() : (size_t)kWaves * (64 + ph.a.attn.T) * sizeof(float);
@@ -235,13 +257,29 @@ static size_t lds_for(const Phase& ph) {
 
 size_t phase_lds_bytes(const Phase& ph) { return lds_for(ph); }
 
-// Every phase is sized to fit the default 64 KB dynamic-LDS window, so no
-// kernel needs a raised attribute.
-static constexpr size_t g_lds_limit = 60 * 1024;
-static constexpr size_t g_persist_lds = 60 * 1024;
+// Dynamic LDS: every phase fits 64 KB.  The pipelined GEMM uses exactly
+// 64 KB, which together with the kernels' own static LDS needs the raised
+// per-kernel limit; without it that GEMM is not used.
+static size_t g_lds_limit = 60 * 1024;
+static size_t g_persist_lds = 60 * 1024;
+static bool g_p3_ok = false;
 size_t persistent_lds_bytes() { return g_persist_lds; }
+bool gemm_p3_available() { return g_p3_ok; }
 
-hipError_t init_kernels() { return hipSuccess; }
+hipError_t init_kernels() {
+  const int want = 64 * 1024 + 1024;
+  hipError_t e1 = hipFuncSetAttribute((const void*)gemm_kernel<GEMM_P3>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  hipError_t e2 = hipFuncSetAttribute((const void*)persistent_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      want);
+  (void)hipGetLastError();
+  if (e1 == hipSuccess && e2 == hipSuccess) {
+    g_p3_ok = true;
+    g_lds_limit = 64 * 1024;
+    g_persist_lds = 64 * 1024;
+  }
+  return hipSuccess;
+}
 
 size_t lds_limit_bytes() { return g_lds_limit; }
 
@@ -260,6 +298,15 @@ hipError_t launch_phase(const Phase& h, const Phase* d_phases, int idx, const St
   (void)hipGetLastError();   // report this launch's error, not a stale one
   const int grid = h.n_tiles;
   const size_t lds = lds_for(h);
+  if (h.op == OP_GEMM) {
+    if (h.a.gemm.impl == GEMM_P3)
+      hipLaunchKernelGGL(gemm_kernel<GEMM_P3>, dim3(grid), dim3(kThreads), lds, s, d_phases, idx, tm);
+    else if (h.a.gemm.impl == GEMM_MFMA)
+      hipLaunchKernelGGL(gemm_kernel<GEMM_MFMA>, dim3(grid), dim3(kThreads), lds, s, d_phases, idx, tm);
+    else
+      hipLaunchKernelGGL(gemm_kernel<GEMM_SIMPLE>, dim3(grid), dim3(kThreads), lds, s, d_phases, idx, tm);
+    return hipGetLastError();
+  }
   switch (h.op) {
 #define OFA_LAUNCH(X) \
   case X: hipLaunchKernelGGL(phase_kernel<X>, dim3(grid), dim3(kThreads), lds, s, d_phases, idx, d_sc, st, tm, step); break;

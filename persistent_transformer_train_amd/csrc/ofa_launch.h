@@ -25,6 +25,7 @@ hipError_t init_kernels();
 size_t phase_lds_bytes(const Phase& ph);   // dynamic LDS a phase needs
 size_t persistent_lds_bytes();             // dynamic LDS of the persistent kernel
 size_t lds_limit_bytes();                  // dynamic LDS a per-phase kernel may use
+bool gemm_p3_available();                  // the pipelined GEMM tile can be launched
 int persistent_occupancy();                // workgroups per CU for the persistent kernel
 
 hipError_t launch_phase(const Phase& host_ph, const Phase* dev_phases, int idx, const StepCtx* dev_sc,

@@ -74,7 +74,7 @@ def test_c1_fp32_gradients_elementwise(exec_mode):
     h.close()
 
 
-@pytest.mark.parametrize("name", ["m2", "m3"])
+@pytest.mark.parametrize("name", ["m2", "m3", "m3b"])
 @pytest.mark.parametrize("exec_mode", [PER_PHASE, PERSISTENT], ids=["per_phase", "persistent"])
 def test_bf16_mini_loss_100_steps(name, exec_mode):
     log(f"{name} bf16 100 steps exec_mode={exec_mode}")
@@ -88,7 +88,7 @@ def test_bf16_mini_loss_100_steps(name, exec_mode):
     h.close()
 
 
-@pytest.mark.parametrize("name", ["m2", "m3"])
+@pytest.mark.parametrize("name", ["m2", "m3", "m3b"])
 def test_bf16_mini_gradient_cosine(name):
     from persistent_transformer_train_amd import ofa
     cfg = cfg_of(name, exec_mode=PERSISTENT)
@@ -164,3 +164,30 @@ def test_bad_token_reports_arg_error():
     with pytest.raises(ofa.OfaError):
         h.train_step(torch.from_numpy(tok).cuda(), losses)
     h.close()
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_full_size_first_step(name):
+    """Full-size workloads in the launch configuration bench.py times (persistent
+    executor): the first step's loss against the oracle's fp32 forward and the
+    whole-gradient cosine against the oracle's fp32 backward, same init, same tokens."""
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of(name, exec_mode=PERSISTENT)
+    stream = stream_of(name, cfg)
+    init = init_of(name, cfg)
+    h = ofa.Handle(cfg, init)
+    losses = torch.zeros(1, dtype=torch.float32, device="cuda")
+    h.train_step(torch.from_numpy(stream.batches(0, 1)).cuda(), losses)
+    h.sync()
+    g_gpu = h.get_grads().cpu().numpy()
+    h.close()
+    s = spec_from_cfg(cfg)
+    log(f"{name}: oracle fp32 forward+backward")
+    loss, grads = gpt.loss_and_grads(s, gpt.unflatten(s, np.asarray(init, np.float32)), stream.batch(0),
+                                     dtype=np.float32)
+    g_or = gpt.flatten(s, grads, dtype=np.float32)
+    cos = cosine(g_gpu, g_or)
+    gl = float(losses.cpu().numpy()[0])
+    log(f"{name}: loss gpu {gl:.5f} oracle {float(loss):.5f}; grad cosine {cos:.6f}")
+    assert abs(gl - float(loss)) <= 2e-2
+    assert cos >= 0.999
