@@ -22,91 +22,7 @@ namespace ofa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kMBM = 128, kMBN = 128, kMBK = 64;
-constexpr int kMPitch = kMBK + 8;   // bf16 elements per LDS row: 144 bytes, conflict-free 16-byte row reads
-
-struct GemmSmemMfma {
-  uint16_t a[kMBM * kMPitch];
-  uint16_t b[kMBN * kMPitch];
-};
-
-__host__ __device__ constexpr size_t gemm_mfma_lds_bytes() { return sizeof(GemmSmemMfma); }
-
-// Registers holding one operand's next (128 rows x 64 k) slice: 4 x 16 bytes per thread.
-struct OpStage {
-  uint4 v[4];
-};
-
-__device__ __forceinline__ uint4 ld16_rows(const uint16_t* p, int r, int R) {
-  // 8 consecutive rows-contiguous elements starting at row index r (bounds R)
-  if (r + 8 <= R) return *(const uint4*)p;
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (r + e < R) w[e >> 1] |= (uint32_t)p[e] << (16 * (e & 1));
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// Load rows r0..r0+127, k0..k0+63 of an operand.
-// kmajor: element (r, k) at base[r*ld + k]: thread c reads row c/8, k chunk (c%8)*8.
-// otherwise element (r, k) at base[k*ld + r]: thread c reads k rows k0+2*(c%32) and +1,
-// row chunk (c/32)*8, so that the transposing LDS writes of a wavefront hit
-// consecutive dwords.
-__device__ __forceinline__ void mfma_load(OpStage& st, const uint16_t* base, int64_t ld, bool kmajor,
-                                          int r0, int R, int k0, int K) {
-  if (kmajor) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = threadIdx.x + i * kThreads;   // 1024 chunks
-      const int r = r0 + (c >> 3), k = k0 + (c & 7) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < R && k < K) v = *(const uint4*)(base + (int64_t)r * ld + k);   // K % 8 == 0
-      st.v[i] = v;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = threadIdx.x + i * kThreads;   // 512 (k pair, row chunk) items
-      const int k = k0 + 2 * (c & 31), r = r0 + (c >> 5) * 8;
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-      if (r < R) {
-        if (k < K) v0 = ld16_rows(base + (int64_t)k * ld + r, r, R);
-        if (k + 1 < K) v1 = ld16_rows(base + (int64_t)(k + 1) * ld + r, r, R);
-      }
-      st.v[2 * i] = v0;
-      st.v[2 * i + 1] = v1;
-    }
-  }
-}
-
-__device__ __forceinline__ void mfma_store(const OpStage& st, uint16_t* lds, bool kmajor) {
-  if (kmajor) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      *(uint4*)(lds + (c >> 3) * kMPitch + (c & 7) * 8) = st.v[i];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int kp = c & 31, r = (c >> 5) * 8;
-      const uint4 a = st.v[2 * i], b = st.v[2 * i + 1];
-      const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t lo = (wa[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-        const uint32_t hi = (wb[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-        *(uint32_t*)(lds + (r + j) * kMPitch + 2 * kp) = lo | (hi << 16);
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* lds, int row, int k) {
-  uint4 u = *(const uint4*)(lds + row * kMPitch + k);
-  return __builtin_bit_cast(bf16x8_t, u);
-}
+constexpr int kMBM = 128, kMBN = 128;   // output tile
 
 // Epilogue through LDS: the waves park their accumulators in LDS (fp32,
 // [rows][128]), then all 256 threads walk the tile (thread -> column, rows in
@@ -176,64 +92,9 @@ __device__ __forceinline__ void gemm_mfma_epilogue(const GemmArgs& g, const f32x
   }
 }
 
-__device__ void task_gemm_mfma(const GemmArgs& g, int tile, char* smem) {
-  GemmSmemMfma& s = *(GemmSmemMfma*)smem;
-  const int tm = tile / g.tiles_n, tn = tile % g.tiles_n;
-  const int m0 = tm * kMBM, n0 = tn * kMBN;
-  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
-  const uint16_t* A = (const uint16_t*)g.A;
-  const uint16_t* B = (const uint16_t*)g.B;
-
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  OpStage sa, sb;
-  const int nk = (g.K + kMBK - 1) / kMBK;
-  mfma_load(sa, A, g.lda, g.a_kmajor, m0, g.M, 0, g.K);
-  mfma_load(sb, B, g.ldb, g.b_kmajor, n0, g.N, 0, g.K);
-  __syncthreads();   // the previous tile's readers are done with the LDS
-  mfma_store(sa, s.a, g.a_kmajor);
-  mfma_store(sb, s.b, g.b_kmajor);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      mfma_load(sa, A, g.lda, g.a_kmajor, m0, g.M, (kt + 1) * kMBK, g.K);
-      mfma_load(sb, B, g.ldb, g.b_kmajor, n0, g.N, (kt + 1) * kMBK, g.K);
-    }
-#pragma unroll
-    for (int kk = 0; kk < kMBK; kk += 16) {
-      const int kf = kk + (lane >> 5) * 8;
-      bf16x8_t af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = lds_frag(s.a, wm + i * 32 + (lane & 31), kf);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = lds_frag(s.b, wn + j * 32 + (lane & 31), kf);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      __syncthreads();
-      mfma_store(sa, s.a, g.a_kmajor);
-      mfma_store(sb, s.b, g.b_kmajor);
-      __syncthreads();
-    }
-  }
-  gemm_mfma_epilogue(g, acc, m0, n0, wm, wn, lane, (float*)smem, 64);
-}
-
 // ============================================================================
-// GEMM tile, pipelined version (K a multiple of 64; every strided operand's
-// contiguous dimension a multiple of 8).
+// GEMM tile, pipelined version (K a multiple of 8; every row-contiguous
+// operand's contiguous dimension a multiple of 8).
 //
 // Operands stay in their memory layout in LDS: a k-contiguous operand as
 // [128 rows][64 k], a row-contiguous operand as [64 k][128 rows], both with
@@ -288,19 +149,54 @@ __device__ __forceinline__ void p3_issue(const uint16_t* base, int64_t ld, int r
   // track them: its own tracking would wait for every outstanding copy
   // (gfx9 counts loads and copies on one counter) before any LDS read.  The
   // waits are explicit (p3_wait_barrier).
+  // m0 is reserved to the compiler, which does not use it in these kernels
+  // (checked in the generated code); the clobber documents the write.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void_t*)(stage + (wave + 4 * q) * 64 * 8));   // wave-uniform
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src[q]), "s"(lds) : "memory", "m0");
   }
+#pragma clang diagnostic pop
+}
+
+// The last k slice when K is not a multiple of 64: ordinary loads with zero
+// fill (K % 8 == 0, so a 16-byte chunk is either wholly inside or outside),
+// written by ds_write to the same swizzled chunk the copy would have filled.
+template <bool KMAJOR>
+__device__ __forceinline__ void p3_fill_tail(const uint16_t* base, int64_t ld, int r0, int R, int k0, int K,
+                                             uint16_t* stage, int wave, int lane) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int p = (wave + 4 * q) * 64 + lane;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (KMAJOR) {
+      const int r = p >> 3, c = (p & 7) ^ (r & 7);
+      const int rr = min(r0 + r, R - 1), k = k0 + c * 8;
+      if (k < K) v = *(const uint4*)(base + (int64_t)rr * ld + k);
+    } else {
+      const int k = p >> 4, c = (p & 15) ^ (2 * (k & 7));
+      const int col = min(r0 + c * 8, R - 8);
+      if (k0 + k < K) v = *(const uint4*)(base + (int64_t)(k0 + k) * ld + col);
+    }
+    *(uint4*)(stage + p * 8) = v;
+  }
+}
+
+template <bool KMAJOR>
+__device__ __forceinline__ void p3_load(const uint16_t* base, int64_t ld, int r0, int R, int k0, int K, uint16_t* stage,
+                                        int wave, int lane) {
+  if (k0 + kP3BK <= K) p3_issue<KMAJOR>(base, ld, r0, R, k0, stage, wave, lane);
+  else p3_fill_tail<KMAJOR>(base, ld, r0, R, k0, K, stage, wave, lane);
 }
 
 // wait until at most N of this wave's vector-memory operations are
 // outstanding, then join the workgroup barrier
 template <int N>
 __device__ __forceinline__ void p3_wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
 // this wave's LDS reads are complete, then join the workgroup barrier
@@ -347,15 +243,15 @@ __device__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = g.K / kP3BK;
+  const int nk = (g.K + kP3BK - 1) / kP3BK;
   __syncthreads();   // the previous tile's readers are done with the ring
-  p3_issue<AKM>(A, g.lda, m0, g.M, 0, s.a[0], w, lane);
-  p3_issue<BKM>(B, g.ldb, n0, g.N, 0, s.b[0], w, lane);
+  p3_load<AKM>(A, g.lda, m0, g.M, 0, g.K, s.a[0], w, lane);
+  p3_load<BKM>(B, g.ldb, n0, g.N, 0, g.K, s.b[0], w, lane);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
-      p3_issue<AKM>(A, g.lda, m0, g.M, (kt + 1) * kP3BK, s.a[cur ^ 1], w, lane);
-      p3_issue<BKM>(B, g.ldb, n0, g.N, (kt + 1) * kP3BK, s.b[cur ^ 1], w, lane);
+      p3_load<AKM>(A, g.lda, m0, g.M, (kt + 1) * kP3BK, g.K, s.a[cur ^ 1], w, lane);
+      p3_load<BKM>(B, g.ldb, n0, g.N, (kt + 1) * kP3BK, g.K, s.b[cur ^ 1], w, lane);
       p3_wait_barrier<8>();   // this slice has landed in every wave; the next one stays in flight
     } else {
       p3_wait_barrier<0>();

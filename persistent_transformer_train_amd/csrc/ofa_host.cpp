@@ -357,11 +357,12 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
   g.ldc = ldc;
   g.c_dt = c_dt;
   g.epi = epi;
-  const bool mfma = h->cfg.precision == OFA_BF16 && a_dt == DT_BF16 && b_dt == DT_BF16;
-  // the pipelined tile needs whole 64-wide k slices and 8-aligned contiguous row dimensions
-  const bool p3 = mfma && gemm_p3_available() && K % 64 == 0 && (a_km || M % 8 == 0) && (b_km || N % 8 == 0) &&
-                  M >= 8 && N >= 8;
-  g.impl = p3 ? GEMM_P3 : mfma ? GEMM_MFMA : GEMM_SIMPLE;
+  // bf16 operands take the matrix-core tile; its shape limits (K, and the
+  // contiguous dimension of a row-contiguous operand, multiples of 8) hold for
+  // every bf16 configuration the validator accepts
+  const bool mfma = h->cfg.precision == OFA_BF16 && a_dt == DT_BF16 && b_dt == DT_BF16 && gemm_p3_available() &&
+                    K % 8 == 0 && (a_km || M % 8 == 0) && (b_km || N % 8 == 0) && M >= 8 && N >= 8;
+  g.impl = mfma ? GEMM_P3 : GEMM_SIMPLE;
   g.bm = mfma ? 128 : 64;
   g.bn = mfma ? 128 : 64;
   g.tiles_m = cdiv(M, g.bm);

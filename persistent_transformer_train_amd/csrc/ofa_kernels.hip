@@ -32,7 +32,6 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   else if constexpr (OP == OP_LN_FWD) task_ln_fwd(ph.a.lnf, tile);
   else if constexpr (OP == OP_GEMM) {
     if (ph.a.gemm.impl == GEMM_P3) task_gemm_p3(ph.a.gemm, tile, smem);
-    else if (ph.a.gemm.impl == GEMM_MFMA) task_gemm_mfma(ph.a.gemm, tile, smem);
     else task_gemm_simple(ph.a.gemm, tile, smem);
   }
   else if constexpr (OP == OP_ROPE) task_rope(ph.a.rope, tile, false);
@@ -104,7 +103,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Phase* phases, int
   const uint64_t t0 = now_ticks();
   for (int tile = blockIdx.x; tile < ph.n_tiles; tile += gridDim.x) {
     if constexpr (IMPL == GEMM_P3) task_gemm_p3(ph.a.gemm, tile, smem);
-    else if constexpr (IMPL == GEMM_MFMA) task_gemm_mfma(ph.a.gemm, tile, smem);
     else task_gemm_simple(ph.a.gemm, tile, smem);
   }
   if (times && threadIdx.x == 0) {
@@ -134,7 +132,7 @@ __device__ __forceinline__ bool wait_count(const uint64_t* ctr, uint64_t need, c
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void persistent_kernel(PersistParams p) {
+__global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
   extern __shared__ __align__(16) char smem[];
   __shared__ uint64_t s_ticket;
   __shared__ int s_ok;
@@ -232,8 +230,7 @@ __global__ void fill_pairs_kernel(uint64_t* p, uint64_t a, uint64_t b, int64_t n
 static size_t lds_for(const Phase& ph) {
   switch (ph.op) {
     case OP_GEMM:
-      return ph.a.gemm.impl == GEMM_P3 ? gemm_p3_lds_bytes()
-             : ph.a.gemm.impl == GEMM_MFMA ? gemm_mfma_lds_bytes() : sizeof(GemmSmemSimple);
+      return ph.a.gemm.impl == GEMM_P3 ? gemm_p3_lds_bytes() : sizeof(GemmSmemSimple);
     case OP_LN_BWD: return (size_t)kWaves * 3 * ph.a.lnb.d * sizeof(float);
     case OP_ATTN_FWD:
       return ph.a.attn.impl == 1 ? attn_mfma_lds_bytes() : (size_t)kWaves * (64 + ph.a.attn.T) * sizeof(float);
@@ -301,8 +298,6 @@ hipError_t launch_phase(const Phase& h, const Phase* d_phases, int idx, const St
   if (h.op == OP_GEMM) {
     if (h.a.gemm.impl == GEMM_P3)
       hipLaunchKernelGGL(gemm_kernel<GEMM_P3>, dim3(grid), dim3(kThreads), lds, s, d_phases, idx, tm);
-    else if (h.a.gemm.impl == GEMM_MFMA)
-      hipLaunchKernelGGL(gemm_kernel<GEMM_MFMA>, dim3(grid), dim3(kThreads), lds, s, d_phases, idx, tm);
     else
       hipLaunchKernelGGL(gemm_kernel<GEMM_SIMPLE>, dim3(grid), dim3(kThreads), lds, s, d_phases, idx, tm);
     return hipGetLastError();

@@ -54,7 +54,7 @@ enum Epi : int32_t {
   EPI_DGEGLU = 4,  // aux = [g | up] (ld ldaux, up at +aux_off); C[:, n] = acc*up*GELU'(g), C[:, n+aux_off] = acc*GELU(g)
 };
 
-enum GemmImpl : int32_t { GEMM_SIMPLE = 0, GEMM_MFMA = 1, GEMM_P3 = 2 };
+enum GemmImpl : int32_t { GEMM_SIMPLE = 0, GEMM_P3 = 2 };
 
 struct GemmArgs {
   const void* A;
