@@ -116,9 +116,11 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 constexpr int kP3BK = 64;
 constexpr int kP3Stage = 128 * kP3BK;   // elements of one operand stage
 
+constexpr int kP3Stages = 3;            // k slices resident in the LDS ring (two in flight)
+
 struct GemmSmemP3 {
-  uint16_t a[2][kP3Stage];
-  uint16_t b[2][kP3Stage];
+  uint16_t a[kP3Stages][kP3Stage];
+  uint16_t b[kP3Stages][kP3Stage];
 };
 
 __host__ __device__ constexpr size_t gemm_p3_lds_bytes() { return sizeof(GemmSmemP3); }
@@ -228,7 +230,10 @@ __device__ __forceinline__ bf16x8_t p3_frag_t(const uint16_t* stage, int rbase, 
 template <bool AKM, bool BKM>
 __device__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
   GemmSmemP3& s = *(GemmSmemP3*)smem;
-  const int tm = tile / g.tiles_n, tn = tile % g.tiles_n;
+  // tile order: with tile_order = 1 the M index runs fastest, so tiles that run
+  // at the same time share the B panel (used when B is the larger operand)
+  const int tm = g.tile_order ? tile % g.tiles_m : tile / g.tiles_n;
+  const int tn = g.tile_order ? tile / g.tiles_m : tile % g.tiles_n;
   const int m0 = tm * kMBM, n0 = tn * kMBN;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
@@ -245,14 +250,24 @@ __device__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
 
   const int nk = (g.K + kP3BK - 1) / kP3BK;
   __syncthreads();   // the previous tile's readers are done with the ring
-  p3_load<AKM>(A, g.lda, m0, g.M, 0, g.K, s.a[0], w, lane);
-  p3_load<BKM>(B, g.ldb, n0, g.N, 0, g.K, s.b[0], w, lane);
+  // prologue: slices 0 and 1 in flight
+#pragma unroll
+  for (int q = 0; q < kP3Stages - 1; ++q)
+    if (q < nk) {
+      p3_load<AKM>(A, g.lda, m0, g.M, q * kP3BK, g.K, s.a[q], w, lane);
+      p3_load<BKM>(B, g.ldb, n0, g.N, q * kP3BK, g.K, s.b[q], w, lane);
+    }
+  int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      p3_load<AKM>(A, g.lda, m0, g.M, (kt + 1) * kP3BK, g.K, s.a[cur ^ 1], w, lane);
-      p3_load<BKM>(B, g.ldb, n0, g.N, (kt + 1) * kP3BK, g.K, s.b[cur ^ 1], w, lane);
-      p3_wait_barrier<8>();   // this slice has landed in every wave; the next one stays in flight
+    // slice kt+2 goes into the buffer slice kt-1 used (everyone left it at the last barrier)
+    const int ahead = kt + kP3Stages - 1;
+    if (ahead < nk) {
+      const int buf = cur == 0 ? kP3Stages - 1 : cur - 1;
+      p3_load<AKM>(A, g.lda, m0, g.M, ahead * kP3BK, g.K, s.a[buf], w, lane);
+      p3_load<BKM>(B, g.ldb, n0, g.N, ahead * kP3BK, g.K, s.b[buf], w, lane);
+      p3_wait_barrier<16>();   // slice kt landed in every wave; kt+1 and kt+2 stay in flight
+    } else if (kt + 1 < nk) {
+      p3_wait_barrier<8>();
     } else {
       p3_wait_barrier<0>();
     }
@@ -274,6 +289,7 @@ __device__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     p3_lds_barrier();   // every wave is done with this slice before it is refilled
+    cur = cur + 1 == kP3Stages ? 0 : cur + 1;
   }
   gemm_mfma_epilogue(g, acc, m0, n0, wm, wn, lane, (float*)smem, 128);
 }

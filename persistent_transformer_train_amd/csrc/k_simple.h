@@ -228,7 +228,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, int m, int n, f
 
 __device__ void task_gemm_simple(const GemmArgs& g, int tile, char* smem) {
   GemmSmemSimple& s = *(GemmSmemSimple*)smem;
-  const int tm = tile / g.tiles_n, tn = tile % g.tiles_n;
+  const int tm = g.tile_order ? tile % g.tiles_m : tile / g.tiles_n;
+  const int tn = g.tile_order ? tile / g.tiles_m : tile % g.tiles_n;
   const int m0 = tm * 64, n0 = tn * 64;
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
   float acc[4][4];
@@ -507,16 +508,36 @@ __device__ void task_ce(const CeArgs& a, int tile, const TaskCtx& tc, char* smem
   const int b = r / a.T, t = r % a.T;
   const int y = token_at(tc.sc, b, t + 1, a.T, a.V, tc);
   const float* z = a.logits + (int64_t)r * a.V;
+  // V % 8 == 0 and rows are 16-byte aligned: float4 loads, two in flight per thread
+  const float4* z4 = (const float4*)z;
+  const int n4 = a.V / 4;
   float mx = -INFINITY;
-  for (int v = threadIdx.x; v < a.V; v += kThreads) mx = fmaxf(mx, z[v]);
+  for (int i = threadIdx.x; i < n4; i += kThreads) {
+    const float4 v = z4[i];
+    mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+  }
   mx = block_max(mx, red);
   float s = 0.f;
-  for (int v = threadIdx.x; v < a.V; v += kThreads) s += expf(z[v] - mx);
+  for (int i = threadIdx.x; i < n4; i += kThreads) {
+    const float4 v = z4[i];
+    s += (expf(v.x - mx) + expf(v.y - mx)) + (expf(v.z - mx) + expf(v.w - mx));
+  }
   s = block_sum(s, red + kWaves);
   const float lse = mx + logf(s);
-  for (int v = threadIdx.x; v < a.V; v += kThreads) {
-    float p = expf(z[v] - lse);
-    stf(a.dz, (int64_t)r * a.V + v, a.dt, (p - (v == y ? 1.f : 0.f)) * a.inv_rows);
+  for (int i = threadIdx.x; i < n4; i += kThreads) {
+    const float4 v = z4[i];
+    float p[4] = {expf(v.x - lse), expf(v.y - lse), expf(v.z - lse), expf(v.w - lse)};
+    const int v0 = 4 * i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = (p[e] - (v0 + e == y ? 1.f : 0.f)) * a.inv_rows;
+    const int64_t o = (int64_t)r * a.V + v0;
+    if (a.dt == DT_BF16) {
+      const uint32_t w0 = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
+      const uint32_t w1 = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
+      *(uint2*)((uint16_t*)a.dz + o) = make_uint2(w0, w1);
+    } else {
+      *(float4*)((float*)a.dz + o) = make_float4(p[0], p[1], p[2], p[3]);
+    }
   }
   if (threadIdx.x == 0) a.loss_rows[r] = lse - z[y];
 }
@@ -639,17 +660,50 @@ __device__ void task_emb_bwd(const EmbBwdArgs& a, int tile, const TaskCtx& tc) {
 // p <- p(1 - lr wd); m <- b1 m + (1-b1) g; v <- b2 v + (1-b2) g^2;
 // p <- p - lr (m/bc1) / (sqrt(v/bc2) + eps); compute copy <- p.
 
+__device__ __forceinline__ void adamw_one(float& p, float& m, float& v, float g, float decay, float lr, float bc1,
+                                          float bc2, const AdamArgs& a) {
+  p *= decay;
+  m = a.beta1 * m + (1.0f - a.beta1) * g;
+  v = a.beta2 * v + (1.0f - a.beta2) * g * g;
+  p -= lr * (m / bc1) / (sqrtf(v / bc2) + a.eps);
+}
+
+// per_tile is a multiple of 1024 and n of 8 (checked on the host): float4 access,
+// the tail of the last tile element-wise
 __device__ void task_adamw(const AdamArgs& a, int tile, const TaskCtx& tc) {
   const float lr = tc.sc->lr, bc1 = tc.sc->bc1, bc2 = tc.sc->bc2;
   const int64_t i0 = (int64_t)tile * a.per_tile;
   const int64_t i1 = min(i0 + (int64_t)a.per_tile, a.n);
   const float decay = 1.0f - lr * a.wd;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += kThreads) {
-    float g = a.g[i];
-    float p = a.p[i] * decay;
-    float m = a.beta1 * a.m[i] + (1.0f - a.beta1) * g;
-    float v = a.beta2 * a.v[i] + (1.0f - a.beta2) * g * g;
-    p -= lr * (m / bc1) / (sqrtf(v / bc2) + a.eps);
+  const int64_t n4 = (i1 - i0) / 4;
+  float4* P = (float4*)(a.p + i0);
+  float4* M = (float4*)(a.m + i0);
+  float4* Vv = (float4*)(a.v + i0);
+  const float4* G = (const float4*)(a.g + i0);
+  for (int64_t j = threadIdx.x; j < n4; j += kThreads) {
+    float4 p = P[j], m = M[j], v = Vv[j];
+    const float4 g = G[j];
+    adamw_one(p.x, m.x, v.x, g.x, decay, lr, bc1, bc2, a);
+    adamw_one(p.y, m.y, v.y, g.y, decay, lr, bc1, bc2, a);
+    adamw_one(p.z, m.z, v.z, g.z, decay, lr, bc1, bc2, a);
+    adamw_one(p.w, m.w, v.w, g.w, decay, lr, bc1, bc2, a);
+    P[j] = p;
+    M[j] = m;
+    Vv[j] = v;
+    if (a.wc) {
+      const int64_t e = i0 + 4 * j;
+      if (a.wc_dt == DT_BF16) {
+        const uint32_t w0 = (uint32_t)f2bf(p.x) | ((uint32_t)f2bf(p.y) << 16);
+        const uint32_t w1 = (uint32_t)f2bf(p.z) | ((uint32_t)f2bf(p.w) << 16);
+        *(uint2*)((uint16_t*)a.wc + e) = make_uint2(w0, w1);
+      } else {
+        *(float4*)((float*)a.wc + e) = p;
+      }
+    }
+  }
+  for (int64_t i = i0 + 4 * n4 + threadIdx.x; i < i1; i += kThreads) {
+    float p = a.p[i], m = a.m[i], v = a.v[i];
+    adamw_one(p, m, v, a.g[i], decay, lr, bc1, bc2, a);
     a.p[i] = p;
     a.m[i] = m;
     a.v[i] = v;

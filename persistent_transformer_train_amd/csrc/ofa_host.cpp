@@ -367,6 +367,8 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
   g.bn = mfma ? 128 : 64;
   g.tiles_m = cdiv(M, g.bm);
   g.tiles_n = cdiv(N, g.bn);
+  // walk the smaller operand fastest so the larger one is streamed about once
+  g.tile_order = (int64_t)N > (int64_t)M ? 1 : 0;
   return g;
 }
 

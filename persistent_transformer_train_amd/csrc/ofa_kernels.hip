@@ -264,7 +264,7 @@ size_t persistent_lds_bytes() { return g_persist_lds; }
 bool gemm_p3_available() { return g_p3_ok; }
 
 hipError_t init_kernels() {
-  const int want = 64 * 1024 + 1024;
+  const int want = (int)gemm_p3_lds_bytes() + 2048;
   hipError_t e1 = hipFuncSetAttribute((const void*)gemm_kernel<GEMM_P3>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, want);
   hipError_t e2 = hipFuncSetAttribute((const void*)persistent_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -272,8 +272,8 @@ hipError_t init_kernels() {
   (void)hipGetLastError();
   if (e1 == hipSuccess && e2 == hipSuccess) {
     g_p3_ok = true;
-    g_lds_limit = 64 * 1024;
-    g_persist_lds = 64 * 1024;
+    g_lds_limit = gemm_p3_lds_bytes();
+    g_persist_lds = gemm_p3_lds_bytes();
   }
   return hipSuccess;
 }

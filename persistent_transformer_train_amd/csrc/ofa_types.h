@@ -73,6 +73,7 @@ struct GemmArgs {
   int32_t tiles_m, tiles_n;
   int32_t aux_off;
   int32_t bm, bn;     // tile shape (rows of C, columns of C)
+  int32_t tile_order; // 0: N index fastest; 1: M index fastest
 };
 
 struct LnFwdArgs {
