@@ -75,6 +75,37 @@ def cpu_baseline(cfg: dict) -> dict:
                       f"({cfg['seq']} tokens), {dt:.2f} s, numpy BLAS threads = affinity cores"}
 
 
+def bench_decode(init, stream, args) -> dict:
+    """Batch-1 greedy decode of the frozen seeded weights (version 0, published at
+    create) on the serve CUs: a 32-token prompt, then decode_tokens tokens; the
+    first call (prompt prefill + first token) is not timed."""
+    import torch
+    from persistent_transformer_train_amd import configs, ofa
+    dcfg = configs.get("c4", exec_mode=0 if args.exec_mode == "persistent" else 1)
+    h = ofa.Handle(dcfg, init)
+    prompt = torch.from_numpy(stream.prompt(dcfg["prompt_len"])).cuda()
+    n = args.decode_tokens
+    toks = torch.zeros(n, dtype=torch.int32, device="cuda")
+    h.decode(prompt, 1, toks)
+    h.sync()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    h.decode(None, n - 1, toks[1:])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = h.sync()
+    h.close()
+    rate = (n - 1) / dt
+    avg_ctx = (dcfg["prompt_len"] + dcfg["decode_window"]) / 2
+    bpt = decode_bytes_per_token(dcfg, avg_ctx)
+    return {"metric": "batch-1 greedy decode tokens/s", "value": round(rate, 1), "unit": "tokens/s",
+            "tokens": n - 1, "prompt": dcfg["prompt_len"], "window": dcfg["decode_window"],
+            "cus": dcfg["serve_cus"] if args.exec_mode == "persistent" else "all (launch per phase)",
+            "kernel_ms": round(st.last_call_ms, 3),
+            "roofline": {"bound": "hbm", "achieved": round(bpt * rate / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s", "frac": round(bpt * rate / PEAK_HBM, 4), "bytes_per_token": bpt}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,33 +177,12 @@ def main():
         "losses": [float(ls[0]), float(ls[-1])],
     }
 
+    h.close()
     if not args.no_decode and args.decode_tokens > 1:
-        # c4: greedy decode of the frozen seeded weights (version 0, published at create)
-        dcfg = cfg
-        prompt = torch.from_numpy(stream.prompt(dcfg["prompt_len"])).cuda()
-        n = args.decode_tokens
-        toks = torch.zeros(n, dtype=torch.int32, device="cuda")
-        h.decode(prompt, 1, toks)        # prefill of the prompt + first token (not timed)
-        h.sync()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        h.decode(None, n - 1, toks[1:])
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-        h.sync()
-        rate = (n - 1) / dt
-        avg_ctx = (dcfg["prompt_len"] + dcfg["decode_window"]) / 2
-        bpt = decode_bytes_per_token(dcfg, avg_ctx)
-        out["decode"] = {"metric": "batch-1 greedy decode tokens/s", "value": round(rate, 1), "unit": "tokens/s",
-                         "tokens": n - 1, "prompt": dcfg["prompt_len"], "window": dcfg["decode_window"],
-                         "cus": "all (launch per phase)",
-                         "roofline": {"bound": "hbm", "achieved": round(bpt * rate / 1e9, 1),
-                                      "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                                      "frac": round(bpt * rate / PEAK_HBM, 4), "bytes_per_token": bpt}}
+        out["decode"] = bench_decode(init, stream, args)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
-    h.close()
     print(json.dumps(out), flush=True)
 
 

@@ -91,6 +91,7 @@ typedef struct {
 
 #define OFA_DEBUG_SHUFFLE_TICKETS 1  /* persistent mode: permute tile order inside a phase */
 #define OFA_DEBUG_SHORT_WATCHDOG  2  /* device waits give up after ~1 ms instead of ~10 s */
+#define OFA_DEBUG_TRACE           4  /* persistent mode: per (instance, phase) timestamps, see ofa_trace */
 
 /* Size in bytes of the device workspace ofa_create() needs for cfg; 0 if cfg is
  * invalid (ofa_validate_config() says why). */
@@ -192,6 +193,23 @@ ofa_status ofa_status_sync(ofa_handle *h, ofa_stats *out);
  * end, in device clock ticks (100 MHz).  n: capacity in pairs.  Synchronises. */
 ofa_status ofa_phase_times(ofa_handle *h, uint64_t *host_t, int32_t n, int32_t *n_out,
                            char *names, size_t name_stride);
+
+/* The same for the decode program of the last decode call (summed over its
+ * positions: first tile start and last tile end of each phase). */
+ofa_status ofa_decode_phase_times(ofa_handle *h, uint64_t *host_t, int32_t n, int32_t *n_out,
+                                  char *names, size_t name_stride);
+
+/* Phase trace of the last persistent call (needs OFA_DEBUG_TRACE in the config;
+ * the workspace then holds the trace).  For instance i < OFA_TRACE_INSTANCES and
+ * phase p of that call's program, four device times (ticks of 100 MHz) at
+ * t[4(i P + p) + 0..3]: the first and the last time a workgroup started the
+ * phase's work (its dependencies met), the last time one finished the work,
+ * and the last time one had published it (release fence and counter update);
+ * P = *n_phases.  decode != 0 selects the last decode call.  n: capacity in
+ * uint64 words / 2; *n_out: entries written.  Synchronises. */
+#define OFA_TRACE_INSTANCES 1024
+ofa_status ofa_trace(ofa_handle *h, int32_t decode, uint64_t *host_t, int64_t n, int64_t *n_out,
+                     int32_t *n_phases);
 
 /* 64-bit task budget = iterations x tasks_per_unit; OFA_E_OVERFLOW if the
  * product does not fit 63 bits.  Host-only helper (the budget rule of the

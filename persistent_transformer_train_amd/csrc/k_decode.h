@@ -50,102 +50,374 @@ __device__ void task_dec_embed(const DecEmbedArgs& a, int tile, const TaskCtx& t
 
 // ---------------------------------------------------------------- GEMV
 
-__host__ __device__ inline size_t dec_gemv_lds_bytes(const DecGemvArgs& a) {
-  return (size_t)(a.K + 2 * a.rows_per_tile + 64) * sizeof(float);
+// (value, index) maximum over the workgroup: larger value wins, equal values
+// keep the lower index; the result is valid in every thread.  red holds 16
+// words.
+__device__ __forceinline__ void argmax_combine_block(float& bv, int& bi, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    red[w] = bv;
+    ((int*)red)[8 + w] = bi;
+  }
+  __syncthreads();
+  bv = red[0];
+  bi = ((int*)red)[8];
+  for (int i = 1; i < kWaves; ++i) {
+    const float ov = red[i];
+    const int oi = ((int*)red)[8 + i];
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
 }
 
-// dot of one weight row (K elements, dtype w_dt) with the LDS vector xs
-__device__ __forceinline__ float row_dot(const void* Wrow, int K, int w_dt, const float* xs, int lane) {
-  float acc = 0.f;
-  if (w_dt == DT_BF16) {
-    const uint4* p = (const uint4*)Wrow;
-    for (int c = lane; c < K / 8; c += kWave) {
-      uint4 u = p[c];
-      const uint16_t* e = (const uint16_t*)&u;
-      const float* x = xs + c * 8;
+// A ticket covers tiles [t0, t1) of a GEMV; tile t is rows [t R, t R + R) of W
+// (for the gated MLP also rows F + t R ... of the up half, in the second half
+// of the tile buffer).  The weights stream through an LDS ring of n_buf
+// buffers of kDecTile bytes by direct-to-LDS copies; the persistent executor
+// issues the first ones before the ticket's dependencies are met (weights do
+// not depend on them), so weight streaming overlaps the previous phase.  Every
+// tile takes the same number of copies per wave, so every wait count is a
+// constant.  Rows are dot products of lpr lanes (16-byte chunks i, i + lpr, ...)
+// against the LayerNorm'd input held in registers, each group of lpr lanes
+// taking RPG rows per pass and reducing with DPP row operations.
+// LDS: [ring n_buf x kDecTile][x: K fp32][ys: 2 ys_rows fp32][64 fp32 scratch].
+
+constexpr int kDecTile = 32768;                    // bytes of one tile buffer
+constexpr int kDecCopies = kDecTile / (1024 * kWaves);   // copies per wave per tile (8)
+constexpr int kDecMaxChunks = 8;                   // 16-byte chunks of a row per lane
+
+__host__ __device__ inline int dec_tile_rows_all(const DecGemvArgs& a) {
+  return (a.epi == DEPI_GEGLU ? 2 : 1) * a.rows_per_tile;
+}
+
+__host__ __device__ inline size_t dec_gemv_lds_bytes(const DecGemvArgs& a) {
+  return (size_t)a.n_buf * kDecTile + (size_t)(a.K + 2 * a.ys_rows + 64) * sizeof(float);
+}
+
+__device__ __forceinline__ int dec_row_bytes(const DecGemvArgs& a) { return a.K * (a.w_dt == DT_BF16 ? 2 : 4); }
+
+// rows of W a tile of this GEMV covers (output rows; GEGLU: per half)
+__device__ __forceinline__ int dec_tile_rows(const DecGemvArgs& a, int tile) {
+  const int total = a.epi == DEPI_GEGLU ? a.F : a.N;
+  return min(a.rows_per_tile, total - tile * a.rows_per_tile);
+}
+
+// N copies per wave of [src, src + 4 KB N) into dst; reads past `valid` bytes
+// re-read the last valid chunk (nothing is read out of range)
+template <int N>
+__device__ __forceinline__ void dec_copy_n(const char* src, int valid, char* dst) {
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc += bf2f(e[i]) * x[i];
+  for (int j = 0; j < N; ++j) {
+    const int blk = j * kWaves + w;
+    dma16_to_lds(src + min(blk * 1024 + lane * 16, valid - 16), dst + blk * 1024);
+  }
+}
+
+__device__ __forceinline__ void dec_tile_issue(const DecGemvArgs& a, const char* W, int tile, char* ring, int buf) {
+  const int rb = dec_row_bytes(a);
+  const int valid = dec_tile_rows(a, tile) * rb;
+  const int64_t r0 = (int64_t)tile * a.rows_per_tile;
+  char* dst = ring + buf * kDecTile;
+  if (a.epi == DEPI_GEGLU) {
+    dec_copy_n<kDecCopies / 2>(W + r0 * rb, valid, dst);
+    dec_copy_n<kDecCopies / 2>(W + ((int64_t)a.F + r0) * rb, valid, dst + kDecTile / 2);
+  } else {
+    dec_copy_n<kDecCopies>(W + r0 * rb, valid, dst);
+  }
+}
+
+// wait until tile i has landed while `later` (0..3) later tiles stay in flight,
+// then join the workgroup barrier
+__device__ __forceinline__ void dec_wait_tile(int later) {
+  if (later >= 3) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" : : : "memory");
+  else if (later == 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" : : : "memory");
+  else if (later == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" : : : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+}
+static_assert(kDecCopies == 8, "wait counts above assume 8 copies per wave per tile");
+
+// Prefetch before the dependency wait: returns the number of tiles issued.
+__device__ __forceinline__ int dec_gemv_prefetch(const DecGemvArgs& a, int t0, int t1, char* smem, bool allowed) {
+  if (!allowed) return 0;
+  const char* W = (const char*)a.W + a.st->w_delta;
+  const int n = min(a.n_buf, t1 - t0);
+  for (int i = 0; i < n; ++i) dec_tile_issue(a, W, t0 + i, smem, i);
+  return n;
+}
+
+// sum over groups of lpr lanes (16, 32 or 64) with DPP; the sum lands in the
+// group's last lane
+__device__ __forceinline__ float dpp_group_sum(float v, int lpr) {
+#define OFA_SHR(x, n) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + (n), 0xf, 0xf, true))
+  v += OFA_SHR(v, 1);   // row_shr:1
+  v += OFA_SHR(v, 2);   // row_shr:2
+  v += OFA_SHR(v, 4);   // row_shr:4
+  v += OFA_SHR(v, 8);   // row_shr:8 -> lane 15 of each row holds the row's sum
+#undef OFA_SHR
+  if (lpr >= 32)        // row_bcast:15 into rows 1 and 3
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+  if (lpr >= 64)        // row_bcast:31 into rows 2 and 3
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+  return v;
+}
+
+// Dot products of one LDS tile's rows with the input chunks in xr; row rr of
+// the tile (GEGLU: rows R.. are the up half) lands in ys[rr] or ys2[rr - R].
+template <int RPG, bool BF16>
+__device__ __forceinline__ void dec_dot_rows(const DecGemvArgs& a, const char* tilep, int rows,
+                                             const float (&xr)[kDecMaxChunks][8], float* ys, float* ys2) {
+  const int lpr = a.lpr, ng = kThreads / lpr;
+  const int grp = threadIdx.x / lpr, li = threadIdx.x % lpr;
+  const int R = a.rows_per_tile, TR = dec_tile_rows_all(a);
+  const int rb = dec_row_bytes(a);
+  const int nch = rb / 16;
+  const int half = kDecTile / 2;
+  int off[RPG];
+#pragma unroll
+  for (int k = 0; k < RPG; ++k) {
+    const int rr = grp + k * ng;
+    off[k] = (rr < TR && rr % R < rows) ? (rr / R) * half + (rr % R) * rb : 0;
+  }
+  float acc[RPG];
+#pragma unroll
+  for (int k = 0; k < RPG; ++k) acc[k] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kDecMaxChunks; ++j) {
+    const int c = li + j * lpr;
+    if (j * lpr < nch && c < nch) {
+      if constexpr (BF16) {
+        uint4 u[RPG];
+#pragma unroll
+        for (int k = 0; k < RPG; ++k) u[k] = *(const uint4*)(tilep + off[k] + c * 16);
+#pragma unroll
+        for (int k = 0; k < RPG; ++k)
+          acc[k] += bf2f(u[k].x & 0xffff) * xr[j][0] + bf2f(u[k].x >> 16) * xr[j][1] +
+                    bf2f(u[k].y & 0xffff) * xr[j][2] + bf2f(u[k].y >> 16) * xr[j][3] +
+                    bf2f(u[k].z & 0xffff) * xr[j][4] + bf2f(u[k].z >> 16) * xr[j][5] +
+                    bf2f(u[k].w & 0xffff) * xr[j][6] + bf2f(u[k].w >> 16) * xr[j][7];
+      } else {
+        float4 u[RPG];
+#pragma unroll
+        for (int k = 0; k < RPG; ++k) u[k] = *(const float4*)(tilep + off[k] + c * 16);
+#pragma unroll
+        for (int k = 0; k < RPG; ++k)
+          acc[k] += u[k].x * xr[j][0] + u[k].y * xr[j][1] + u[k].z * xr[j][2] + u[k].w * xr[j][3];
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < RPG; ++k) {
+    const float v = dpp_group_sum(acc[k], lpr);
+    const int rr = grp + k * ng;
+    if (li == lpr - 1 && rr < TR && rr % R < rows) {
+      if (rr < R) ys[rr] = v;
+      else ys2[rr - R] = v;
+    }
+  }
+}
+
+__device__ __forceinline__ void dec_tile_dot(const DecGemvArgs& a, const char* tilep, int rows,
+                                             const float (&xr)[kDecMaxChunks][8], float* ys, float* ys2) {
+  const bool bf = a.w_dt == DT_BF16;
+  switch (a.rpg) {
+    case 1: bf ? dec_dot_rows<1, true>(a, tilep, rows, xr, ys, ys2) : dec_dot_rows<1, false>(a, tilep, rows, xr, ys, ys2); break;
+    case 2: bf ? dec_dot_rows<2, true>(a, tilep, rows, xr, ys, ys2) : dec_dot_rows<2, false>(a, tilep, rows, xr, ys, ys2); break;
+    case 4: bf ? dec_dot_rows<4, true>(a, tilep, rows, xr, ys, ys2) : dec_dot_rows<4, false>(a, tilep, rows, xr, ys, ys2); break;
+    default: bf ? dec_dot_rows<8, true>(a, tilep, rows, xr, ys, ys2) : dec_dot_rows<8, false>(a, tilep, rows, xr, ys, ys2); break;
+  }
+}
+
+// Tiles [t0, t1) of one GEMV; tiles [t0, t0 + npre) were issued by the prefetch.
+__device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0, int t1, const TaskCtx& tc,
+                                                    char* smem, int npre) {
+  if (a.epi == DEPI_LOGITS && !(tc.sc->head & 1)) {   // prefill position: no logits needed
+    if (npre) vm_wait_barrier(0);                      // drain the prefetched copies
+    return;
+  }
+  char* ring = smem;
+  float* xs = (float*)(smem + (size_t)a.n_buf * kDecTile);   // [K]
+  float* ys = xs + a.K;                                        // [ys_rows]
+  float* ys2 = ys + a.ys_rows;                                 // [ys_rows] (gated: up half)
+  float* red = ys2 + a.ys_rows;                                // [64]
+  const DecState* st = a.st;
+  // with one weight slot the offset is always 0 (no dependent load)
+  const int64_t wd = a.pre_dep >= 0 ? st->w_delta : 0;
+  const char* W = (const char*)a.W + wd;
+  const int nt = t1 - t0;
+  for (int i = npre; i < min(a.n_buf, nt); ++i) dec_tile_issue(a, W, t0 + i, ring, i);
+  int issued = min(a.n_buf, nt);
+  // per-position values the epilogue needs, read now rather than after the tiles
+  const int pos = tc.sc->pos;
+  const int64_t gen_idx = tc.sc->gen_idx;
+  float* const logits_out = a.epi == DEPI_LOGITS ? a.io->logits_out : nullptr;
+  // everything that does not come from the tiles is read now, in one round trip:
+  // input, LayerNorm parameters, bias and residual of this thread's output rows
+  const void* bias = a.bias ? (const void*)((const char*)a.bias + wd) : nullptr;
+  const int r0 = t0 * a.rows_per_tile;
+  const int nrows = min(nt * a.rows_per_tile, (a.epi == DEPI_GEGLU ? a.F : a.N) - r0);
+  constexpr int kPre = 4;   // rows per thread held in registers (the rest read in the epilogue)
+  float pre_b[kPre], pre_r[kPre];
+#pragma unroll
+  for (int m = 0; m < kPre; ++m) {
+    const int i = threadIdx.x + m * kThreads;
+    pre_b[m] = (bias && i < nrows) ? ldf(bias, r0 + i, a.w_dt) : 0.f;
+    pre_r[m] = (a.epi == DEPI_RESID && i < nrows) ? a.resid[r0 + i] : 0.f;
+  }
+  constexpr int kMaxK = 4;   // input elements per thread (K <= 1024) for the LayerNorm
+  float gv[kMaxK], bv[kMaxK];
+  if (a.ln_g) {
+    const void* g = (const char*)a.ln_g + wd;
+    const void* b = (const char*)a.ln_b + wd;
+#pragma unroll
+    for (int m = 0; m < kMaxK; ++m) {
+      const int j = threadIdx.x + m * kThreads;
+      gv[m] = j < a.K ? ldf(g, j, a.w_dt) : 0.f;
+      bv[m] = j < a.K ? ldf(b, j, a.w_dt) : 0.f;
+    }
+  }
+  float s = 0.f;
+  if (a.attn_part) {
+    // the attention output: per head, the key-range partials rescaled to their
+    // common maximum, summed, and divided by the summed weights
+    const int Wd = a.dh + 2;
+    constexpr int kSplitMax = 8;
+    for (int j = threadIdx.x; j < a.K; j += kThreads) {
+      const float* ph = a.attn_part + (int64_t)(j / a.dh) * a.attn_split * Wd;
+      float mc[kSplitMax], lc[kSplitMax], oc[kSplitMax];
+#pragma unroll
+      for (int c = 0; c < kSplitMax; ++c)   // all loads first: one round trip
+        if (c < a.attn_split) {
+          mc[c] = ph[c * Wd + a.dh];
+          lc[c] = ph[c * Wd + a.dh + 1];
+          oc[c] = ph[c * Wd + j % a.dh];
+        }
+      float m = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < kSplitMax; ++c)
+        if (c < a.attn_split) m = fmaxf(m, mc[c]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int c = 0; c < kSplitMax; ++c)
+        if (c < a.attn_split && mc[c] != -INFINITY) {   // an empty key range adds nothing
+          const float e = expf(mc[c] - m);
+          num += e * oc[c];
+          den += e * lc[c];
+        }
+      const float v = num / den;
+      xs[j] = v;
+      s += v;
     }
   } else {
-    const float4* p = (const float4*)Wrow;
-    for (int c = lane; c < K / 4; c += kWave) {
-      float4 u = p[c];
-      const float* x = xs + c * 4;
-      acc += u.x * x[0] + u.y * x[1] + u.z * x[2] + u.w * x[3];
+    for (int j = threadIdx.x; j < a.K; j += kThreads) {
+      float v = a.xin[j];
+      xs[j] = v;
+      s += v;
     }
   }
-  return wave_sum(acc);
-}
-
-__device__ void task_dec_gemv(const DecGemvArgs& a, int tile, const TaskCtx& tc, char* smem) {
-  if (a.epi == DEPI_LOGITS && !(tc.sc->head & 1)) return;   // prefill position: no logits needed
-  float* xs = (float*)smem;                 // [K]
-  float* ys = xs + a.K;                     // [rows_per_tile] (x2 for gated)
-  float* red = ys + 2 * a.rows_per_tile;    // reduction scratch
-  const DecState* st = a.st;
-  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const size_t esz = a.w_dt == DT_BF16 ? 2 : 4;
-  // input vector, LayerNorm'd when requested (every tile recomputes the statistics)
-  float s = 0.f;
-  for (int j = threadIdx.x; j < a.K; j += kThreads) {
-    float v = a.xin[j];
-    xs[j] = v;
-    s += v;
-  }
   if (a.ln_g) {
-    const float mean = block_sum(s, red) / a.K;
+    const float mean = block_sum2_dpp(s, 0.f, red).x / a.K;
     float q = 0.f;
     for (int j = threadIdx.x; j < a.K; j += kThreads) {
       float dv = xs[j] - mean;
       q += dv * dv;
     }
-    const float rstd = 1.0f / sqrtf(block_sum(q, red + kWaves) / a.K + 1e-5f);
-    const void* g = (const char*)a.ln_g + st->w_delta;
-    const void* b = (const char*)a.ln_b + st->w_delta;
-    for (int j = threadIdx.x; j < a.K; j += kThreads)
-      xs[j] = (xs[j] - mean) * rstd * ldf(g, j, a.w_dt) + ldf(b, j, a.w_dt);
-  }
-  __syncthreads();
-  const char* W = (const char*)a.W + st->w_delta;
-  const void* bias = a.bias ? (const void*)((const char*)a.bias + st->w_delta) : nullptr;
-  const int r0 = tile * a.rows_per_tile;
-  const int nrows = min(a.rows_per_tile, (a.epi == DEPI_GEGLU ? a.F : a.N) - r0);
-  for (int i = w; i < nrows; i += kWaves) {
-    const int n = r0 + i;
-    float v = row_dot(W + (size_t)n * a.K * esz, a.K, a.w_dt, xs, lane);
-    if (bias) v += ldf(bias, n, a.w_dt);
-    float v2 = 0.f;
-    if (a.epi == DEPI_GEGLU) v2 = row_dot(W + (size_t)(n + a.F) * a.K * esz, a.K, a.w_dt, xs, lane);
-    if (lane == 0) {
-      ys[i] = v;
-      ys[a.rows_per_tile + i] = v2;
+    const float rstd = 1.0f / sqrtf(block_sum2_dpp(q, 0.f, red + 2 * kWaves).x / a.K + 1e-5f);
+#pragma unroll
+    for (int m = 0; m < kMaxK; ++m) {
+      const int j = threadIdx.x + m * kThreads;
+      if (j < a.K) xs[j] = (xs[j] - mean) * rstd * gv[m] + bv[m];
     }
   }
   __syncthreads();
-  const int pos = tc.sc->pos;
-  for (int i = threadIdx.x; i < nrows; i += kThreads) {
+  // this lane's input chunks, in registers for the whole ticket
+  float xr[kDecMaxChunks][8];
+  {
+    const int li = threadIdx.x % a.lpr;
+    const bool bf = a.w_dt == DT_BF16;
+    const int nch = dec_row_bytes(a) / 16;
+#pragma unroll
+    for (int j = 0; j < kDecMaxChunks; ++j) {
+      const int c = li + j * a.lpr;
+      float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+      if (c < nch) {
+        if (bf) {
+          lo = *(const float4*)(xs + c * 8);
+          hi = *(const float4*)(xs + c * 8 + 4);
+        } else {
+          lo = *(const float4*)(xs + c * 4);
+        }
+      }
+      xr[j][0] = lo.x; xr[j][1] = lo.y; xr[j][2] = lo.z; xr[j][3] = lo.w;
+      xr[j][4] = hi.x; xr[j][5] = hi.y; xr[j][6] = hi.z; xr[j][7] = hi.w;
+    }
+  }
+  for (int i = 0; i < nt; ++i) {
+    // tile i landed in every wave, and every wave is done with tile i - 1's buffer
+    dec_wait_tile(issued - i - 1);
+    if (a.n_buf > 1 && i >= 1 && issued < nt) {   // refill the buffer tile i - 1 used
+      dec_tile_issue(a, W, t0 + issued, ring, issued % a.n_buf);
+      ++issued;
+    }
+    dec_tile_dot(a, ring + (size_t)(i % a.n_buf) * kDecTile, dec_tile_rows(a, t0 + i), xr,
+                 ys + i * a.rows_per_tile, ys2 + i * a.rows_per_tile);
+    if (a.n_buf == 1 && issued < nt) {   // one buffer: refill once every wave has read it
+      __syncthreads();
+      dec_tile_issue(a, W, t0 + issued, ring, 0);
+      ++issued;
+    }
+  }
+  __syncthreads();
+  // epilogue over the ticket's rows
+  for (int i = threadIdx.x, m = 0; i < nrows; i += kThreads, ++m) {
     const int n = r0 + i;
-    const float v = ys[i];
+    float v = ys[i];
+    float rv = 0.f;
+    if (m < kPre) {
+#pragma unroll
+      for (int q = 0; q < kPre; ++q)
+        if (q == m) {
+          v += pre_b[q];
+          rv = pre_r[q];
+        }
+    } else {
+      if (bias) v += ldf(bias, n, a.w_dt);
+      if (a.epi == DEPI_RESID) rv = a.resid[n];
+    }
     switch (a.epi) {
       case DEPI_STORE: a.y[n] = v; break;
-      case DEPI_RESID: a.y[n] = a.resid[n] + v; break;
+      case DEPI_RESID: a.y[n] = rv + v; break;
       case DEPI_GELU: a.y[n] = gelu_f(v); break;
-      case DEPI_GEGLU: a.y[n] = gelu_f(v) * ys[a.rows_per_tile + i]; break;
+      case DEPI_GEGLU: a.y[n] = gelu_f(v) * ys2[i]; break;
       case DEPI_LOGITS:
         a.y[n] = v;
-        if (a.io->logits_out) a.io->logits_out[(int64_t)tc.sc->gen_idx * a.N + n] = v;
+        if (logits_out) logits_out[gen_idx * a.N + n] = v;
         break;
       case DEPI_QKV: {
-        // a tile covers whole heads of one part (q, k or v): rows_per_tile % dh == 0
+        // a ticket covers whole heads when the rotation is on (host plan)
         const int part = n / a.d, h = (n % a.d) / a.dh, j = n % a.dh;
         float out = v;
         if (a.rope && part < 2) {
-          const int half = a.dh / 2;
-          const int jj = j < half ? j : j - half;
+          const int hl = a.dh / 2;
+          const int jj = j < hl ? j : j - hl;
           const double ang = (double)pos * pow(10000.0, -2.0 * jj / a.dh);
           const float c = (float)cos(ang), sn = (float)sin(ang);
-          const float other = ys[j < half ? i + half : i - half];
-          out = j < half ? v * c - other * sn : other * sn + v * c;
+          const int io = j < hl ? i + hl : i - hl;
+          float other = ys[io];
+          if (bias) other += ldf(bias, r0 + io, a.w_dt);
+          out = j < hl ? v * c - other * sn : other * sn + v * c;
         }
         if (part == 0) {
           a.y[n] = out;
@@ -156,85 +428,198 @@ __device__ void task_dec_gemv(const DecGemvArgs& a, int tile, const TaskCtx& tc,
       } break;
     }
   }
+  if (a.epi == DEPI_LOGITS) {
+    // this ticket's (max, first index): ascending per thread, then lowest index
+    // among equal maxima; a NaN never wins
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = threadIdx.x; i < nrows; i += kThreads)
+      if (ys[i] > bv) {
+        bv = ys[i];
+        bi = r0 + i;
+      }
+    argmax_combine_block(bv, bi, red);
+    if (threadIdx.x == 0) {
+      const int ticket = t0 / a.per_ticket;
+      a.part_val[ticket] = bv;
+      a.part_idx[ticket] = bi;
+    }
+  }
   __syncthreads();
 }
 
-// ---------------------------------------------------------------- attention (one head per tile)
+__device__ void task_dec_gemv(const DecGemvArgs& a, int tile, const TaskCtx& tc, char* smem) {
+  task_dec_gemv_range(a, tile, tile + 1, tc, smem, 0);
+}
+
+// ---------------------------------------------------------------- attention
+// Tile = (head h, key range c of `split`): scores of the query against the
+// cached keys of the range, their maximum m, weights exp(score - m), their sum
+// l and the weighted sum of the values o; the consumer (the output-projection
+// GEMV) rescales the ranges to a common maximum and divides ("flash decoding":
+// the softmax of the whole row, taken in pieces).
+
+__host__ __device__ inline int dec_attn_ept(const DecAttnArgs& a) {
+  return a.kv_dt == DT_BF16 ? 8 : (a.dh % 4 == 0 ? 4 : 2);
+}
 
 __host__ __device__ inline size_t dec_attn_lds_bytes(const DecAttnArgs& a) {
-  return (size_t)(a.cap + a.dh + kThreads + 16) * sizeof(float);
+  const int ept = dec_attn_ept(a);
+  return (size_t)(a.cap + a.dh + (kThreads / (a.dh / ept)) * a.dh + 16) * sizeof(float);
 }
 
-__device__ void task_dec_attn(const DecAttnArgs& a, int tile, const TaskCtx& tc, char* smem) {
-  const int h = tile;
+// elements [e0, e0 + ept) of a cache row, as fp32
+__device__ __forceinline__ void kv_chunk(const void* kv, int64_t e0, int dt, int ept, float* out) {
+  if (dt == DT_BF16) {
+    const uint4 u = *(const uint4*)((const uint16_t*)kv + e0);
+    out[0] = bf2f(u.x & 0xffff); out[1] = bf2f(u.x >> 16); out[2] = bf2f(u.y & 0xffff); out[3] = bf2f(u.y >> 16);
+    out[4] = bf2f(u.z & 0xffff); out[5] = bf2f(u.z >> 16); out[6] = bf2f(u.w & 0xffff); out[7] = bf2f(u.w >> 16);
+  } else if (ept == 4) {
+    const float4 u = *(const float4*)((const float*)kv + e0);
+    out[0] = u.x; out[1] = u.y; out[2] = u.z; out[3] = u.w;
+  } else {
+    const float2 u = *(const float2*)((const float*)kv + e0);
+    out[0] = u.x; out[1] = u.y;
+  }
+}
+
+template <int ept>
+__device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc, char* smem) {
+  constexpr int kKMax = 64 / ept;   // chunks of a key row (head size <= 64)
+  constexpr int kVPre = 4;          // value rows per thread read ahead
+  const int h = tile / a.split, c = tile % a.split;
   const int pos = tc.sc->pos;
-  float* sc = (float*)smem;          // [cap]
-  float* qs = sc + a.cap;            // [dh]
-  float* part = qs + a.dh;           // [kThreads]
-  float* red = part + kThreads;      // [16]
+  const int n_keys = pos + 1;
+  const int cl = (n_keys + a.split - 1) / a.split;
+  const int s0 = min(c * cl, n_keys), s1 = min(s0 + cl, n_keys);
+  float* sc = (float*)smem;                         // [cap]
+  float* qs = sc + a.cap;                           // [dh]
+  float* acc2 = qs + a.dh;                          // [row slots][dh]
+  const int lpr = a.dh / ept, slots = kThreads / lpr;
+  float* red = acc2 + slots * a.dh;                 // [16]
+  float* out = a.part + (int64_t)tile * (a.dh + 2);
   const float scale = 1.0f / sqrtf((float)a.dh);
-  for (int j = threadIdx.x; j < a.dh; j += kThreads) qs[j] = a.q[h * a.dh + j] * scale;
+  const int64_t kbase = (int64_t)h * a.cap * a.dh;
+  const int64_t vbase = ((int64_t)a.H + h) * a.cap * a.dh;
+  const int nkc = a.dh / ept;
+  const int slot = threadIdx.x / lpr, ci = threadIdx.x % lpr;
+  // every load that does not depend on another is issued first: the query, this
+  // thread's first key row and its first value chunks
+  const float qv = threadIdx.x < a.dh ? a.q[h * a.dh + threadIdx.x] : 0.f;
+  const int s_k = s0 + threadIdx.x;
+  float kr[kKMax][ept];
+#pragma unroll
+  for (int j = 0; j < kKMax; ++j)
+    if (j < nkc && s_k < s1) kv_chunk(a.kv, kbase + (int64_t)s_k * a.dh + j * ept, a.kv_dt, ept, kr[j]);
+  float vr[kVPre][ept];
+#pragma unroll
+  for (int m = 0; m < kVPre; ++m) {
+    const int s = s0 + slot + m * slots;
+    if (s < s1) kv_chunk(a.kv, vbase + (int64_t)s * a.dh + ci * ept, a.kv_dt, ept, vr[m]);
+  }
+  if (threadIdx.x < a.dh) qs[threadIdx.x] = qv * scale;
   __syncthreads();
-  const int64_t kbase = ((int64_t)0 * a.H + h) * a.cap * a.dh;
-  const int64_t vbase = ((int64_t)1 * a.H + h) * a.cap * a.dh;
+  if (s0 >= s1) {   // empty range
+    for (int j = threadIdx.x; j < a.dh; j += kThreads) out[j] = 0.f;
+    if (threadIdx.x == 0) {
+      out[a.dh] = -INFINITY;
+      out[a.dh + 1] = 0.f;
+    }
+    __syncthreads();
+    return;
+  }
+  // scores: one thread per key
   float mx = -INFINITY;
-  for (int s = threadIdx.x; s <= pos; s += kThreads) {
+  if (s_k < s1) {
     float acc = 0.f;
-    for (int j = 0; j < a.dh; ++j) acc += qs[j] * ldf(a.kv, kbase + (int64_t)s * a.dh + j, a.kv_dt);
-    sc[s] = acc;
+#pragma unroll
+    for (int j = 0; j < kKMax; ++j)
+      if (j < nkc)
+#pragma unroll
+        for (int e = 0; e < ept; ++e) acc += qs[j * ept + e] * kr[j][e];
+    sc[s_k - s0] = acc;
+    mx = acc;
+  }
+  for (int s = s_k + kThreads; s < s1; s += kThreads) {   // ranges longer than the workgroup
+    float acc = 0.f;
+    for (int j = 0; j < a.dh; j += ept) {
+      float k[8];
+      kv_chunk(a.kv, kbase + (int64_t)s * a.dh + j, a.kv_dt, ept, k);
+#pragma unroll
+      for (int e = 0; e < ept; ++e) acc += qs[j + e] * k[e];
+    }
+    sc[s - s0] = acc;
     mx = fmaxf(mx, acc);
   }
   mx = block_max(mx, red);
   float sum = 0.f;
-  for (int s = threadIdx.x; s <= pos; s += kThreads) {
-    float p = expf(sc[s] - mx);
-    sc[s] = p;
+  for (int s = s0 + threadIdx.x; s < s1; s += kThreads) {
+    const float p = expf(sc[s - s0] - mx);
+    sc[s - s0] = p;
     sum += p;
   }
-  sum = block_sum(sum, red + kWaves);
+  sum = block_sum(sum, red + kWaves);   // ends with a barrier: every weight is in LDS
+  // weighted values: lpr lanes per value row, `slots` rows at a time
+  float o[ept];
+#pragma unroll
+  for (int e = 0; e < ept; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int m = 0; m < kVPre; ++m) {
+    const int s = s0 + slot + m * slots;
+    if (s < s1) {
+      const float p = sc[s - s0];
+#pragma unroll
+      for (int e = 0; e < ept; ++e) o[e] += p * vr[m][e];
+    }
+  }
+  for (int s = s0 + slot + kVPre * slots; s < s1; s += slots) {
+    float v[8];
+    kv_chunk(a.kv, vbase + (int64_t)s * a.dh + ci * ept, a.kv_dt, ept, v);
+    const float p = sc[s - s0];
+#pragma unroll
+    for (int e = 0; e < ept; ++e) o[e] += p * v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < ept; ++e) acc2[slot * a.dh + ci * ept + e] = o[e];
   __syncthreads();
-  const int groups = kThreads / a.dh;   // dh divides 256
-  const int j = threadIdx.x % a.dh, g = threadIdx.x / a.dh;
-  float acc = 0.f;
-  for (int s = g; s <= pos; s += groups) acc += sc[s] * ldf(a.kv, vbase + (int64_t)s * a.dh + j, a.kv_dt);
-  part[threadIdx.x] = acc;
-  __syncthreads();
-  if (threadIdx.x < a.dh) {
-    float o = 0.f;
-    for (int gg = 0; gg < groups; ++gg) o += part[gg * a.dh + threadIdx.x];
-    a.o[h * a.dh + threadIdx.x] = o / sum;
+  for (int j = threadIdx.x; j < a.dh; j += kThreads) {
+    float t = 0.f;
+    for (int q = 0; q < slots; ++q) t += acc2[q * a.dh + j];
+    out[j] = t;
+  }
+  if (threadIdx.x == 0) {
+    out[a.dh] = mx;
+    out[a.dh + 1] = sum;
   }
   __syncthreads();
+}
+
+__device__ void task_dec_attn(const DecAttnArgs& a, int tile, const TaskCtx& tc, char* smem) {
+  switch (dec_attn_ept(a)) {
+    case 8: dec_attn_tile<8>(a, tile, tc, smem); break;
+    case 4: dec_attn_tile<4>(a, tile, tc, smem); break;
+    default: dec_attn_tile<2>(a, tile, tc, smem); break;
+  }
 }
 
 // ---------------------------------------------------------------- argmax + context update
 
 __device__ void task_dec_argmax(const DecArgmaxArgs& a, int tile, const TaskCtx& tc, char* smem) {
   if (!(tc.sc->head & 1)) return;
-  float* bv = (float*)smem;             // [kThreads]
-  int* bi = (int*)(bv + kThreads);      // [kThreads]
+  float* red = (float*)smem;   // [16]
   float best = -INFINITY;
   int idx = 0x7fffffff;
-  for (int v = threadIdx.x; v < a.V; v += kThreads) {
-    float z = a.logits[v];
-    if (z > best) { best = z; idx = v; }   // strided ascending: first max per thread wins ties
-  }
-  bv[threadIdx.x] = best;
-  bi[threadIdx.x] = idx;
-  __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if ((int)threadIdx.x < off) {
-      float ob = bv[threadIdx.x + off];
-      int oi = bi[threadIdx.x + off];
-      if (ob > bv[threadIdx.x] || (ob == bv[threadIdx.x] && oi < bi[threadIdx.x])) {
-        bv[threadIdx.x] = ob;
-        bi[threadIdx.x] = oi;
-      }
+  for (int i = threadIdx.x; i < a.n_part; i += kThreads) {
+    const float z = a.part_val[i];
+    const int zi = a.part_idx[i];
+    if (z > best || (z == best && zi < idx)) {
+      best = z;
+      idx = zi;
     }
-    __syncthreads();
   }
+  argmax_combine_block(best, idx, red);
   if (threadIdx.x == 0) {
-    int y = bi[0];
+    int y = idx;
     if (y < 0 || y >= a.V) {   // every logit was NaN
       raise_status(tc.status, -3 /*OFA_E_NONFINITE*/, tc.phase, tc.step, 0);
       y = 0;

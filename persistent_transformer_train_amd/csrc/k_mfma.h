@@ -110,7 +110,6 @@ __device__ __forceinline__ void gemm_mfma_epilogue(const GemmArgs& g, const f32x
 // ============================================================================
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kP3BK = 64;

@@ -66,6 +66,42 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// wavefront sum with DPP row shifts and broadcasts (no LDS round trips);
+// every lane receives the total
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+#define OFA_DPP(x, ctrl, rmask, bc) \
+  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rmask, 0xf, bc))
+  v += OFA_DPP(v, 0x111, 0xf, true);   // row_shr:1
+  v += OFA_DPP(v, 0x112, 0xf, true);   // row_shr:2
+  v += OFA_DPP(v, 0x114, 0xf, true);   // row_shr:4
+  v += OFA_DPP(v, 0x118, 0xf, true);   // row_shr:8: lane 15 of each row holds the row sum
+  v += OFA_DPP(v, 0x142, 0xa, false);  // row_bcast:15
+  v += OFA_DPP(v, 0x143, 0xc, false);  // row_bcast:31: lane 63 holds the total
+#undef OFA_DPP
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// workgroup sum of a value and of a second one with one barrier pair, fixed
+// order; red must hold 2 kWaves floats
+__device__ __forceinline__ float2 block_sum2_dpp(float a, float b, float* red) {
+  a = wave_sum_dpp(a);
+  b = wave_sum_dpp(b);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    red[w] = a;
+    red[kWaves + w] = b;
+  }
+  __syncthreads();
+  float2 r = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    r.x += red[i];
+    r.y += red[kWaves + i];
+  }
+  return r;
+}
+
 // workgroup sum, fixed order (deterministic); red must hold kWaves floats
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
@@ -126,6 +162,53 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+
+// A wave-uniform copy of a 64-bit value held by the first active lane.  The
+// builtin returns a signed int: each half is taken as unsigned before it is
+// widened, so a low half with bit 31 set is not sign-extended into the high one.
+__device__ __forceinline__ uint64_t readfirstlane_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+// ---------------------------------------------------------------- direct-to-LDS copies
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One wavefront-wide copy from global memory straight into LDS
+// (global_load_lds_dwordx4): lane L's 16 bytes at src land at lds_block + 16 L.
+// lds_block is wave-uniform.  The copy is inline assembly so that the
+// compiler does not track it (it would otherwise wait for every outstanding
+// copy before its own LDS accesses, gfx9 counting loads and copies on one
+// counter); completion is awaited explicitly with vm_wait_barrier.  m0 is
+// reserved to the compiler, which does not use it in these kernels; the
+// clobber documents the write.
+__device__ __forceinline__ void dma16_to_lds(const void* src, const void* lds_block) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds_block);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Wait until at most n of this wave's vector-memory operations are
+// outstanding (n wave-uniform, 0..47; larger values wait for all), then join
+// the workgroup barrier.
+#define OFA_VMW(N) \
+  case N: asm volatile("s_waitcnt vmcnt(" #N ")\n\ts_barrier" : : : "memory"); break;
+__device__ __forceinline__ void vm_wait_barrier(int n) {
+  switch (n) {
+    OFA_VMW(1) OFA_VMW(2) OFA_VMW(3) OFA_VMW(4) OFA_VMW(5) OFA_VMW(6) OFA_VMW(7) OFA_VMW(8)
+    OFA_VMW(9) OFA_VMW(10) OFA_VMW(11) OFA_VMW(12) OFA_VMW(13) OFA_VMW(14) OFA_VMW(15) OFA_VMW(16)
+    OFA_VMW(17) OFA_VMW(18) OFA_VMW(19) OFA_VMW(20) OFA_VMW(21) OFA_VMW(22) OFA_VMW(23) OFA_VMW(24)
+    OFA_VMW(25) OFA_VMW(26) OFA_VMW(27) OFA_VMW(28) OFA_VMW(29) OFA_VMW(30) OFA_VMW(31) OFA_VMW(32)
+    OFA_VMW(33) OFA_VMW(34) OFA_VMW(35) OFA_VMW(36) OFA_VMW(37) OFA_VMW(38) OFA_VMW(39) OFA_VMW(40)
+    OFA_VMW(41) OFA_VMW(42) OFA_VMW(43) OFA_VMW(44) OFA_VMW(45) OFA_VMW(46) OFA_VMW(47)
+    default: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory"); break;
+  }
+}
+#undef OFA_VMW
 
 // first error wins
 __device__ __forceinline__ void raise_status(DevStatus* st, int code, int phase, int64_t step,

@@ -28,6 +28,8 @@ constexpr int kMaxDecInst = 1 << 16;   // decode positions per call
 constexpr size_t kAlign = 256;
 constexpr size_t kMiscBytes = 4096;    // one Phase (offset 0) and the DecIO block (offset 2048)
 constexpr size_t kMiscDecIO = 2048;
+constexpr int kMaxAttnSplit = 8;        // key ranges per head in decode attention
+constexpr int kThreadsHost = 256;       // threads of every workgroup
 
 // ---------------------------------------------------------------- parameter layout
 
@@ -152,8 +154,8 @@ struct Carve {
   // offsets (bytes) into the workspace
   size_t p, g, m, v, wc, serve, xres, ln_mean, ln_rstd, h, qkv, o, lse, mlp1, mlp2, logits, dz, loss_rows;
   size_t dxres, dxlp, dln, dmlp, dout, dsum, dqkv, ln_part, cs_fc, cs_qkv, esorted, efirst;
-  size_t sched, status, times, inst_end, steps, published;
-  size_t kv, ctx_tok, dstate, dx, dq, dvo, dmlp_v, dlogits, dsteps, dtimes, misc;
+  size_t sched, status, times, inst_end, steps, published, trace;
+  size_t kv, ctx_tok, dstate, dx, dq, dapart, dmlp_v, dlogits, dsteps, dtimes, misc, dsched, dpart_v, dpart_i;
   size_t total;
   int n_slots;
   int ln_tiles, cs_tiles;
@@ -240,11 +242,15 @@ Carve carve(const ofa_config& c, const Layout& lay) {
   w.dstate = b.take(sizeof(DecState));
   w.dx = b.take(R * D.d * f4);
   w.dq = b.take(D.d * f4);
-  w.dvo = b.take(D.L * D.d * f4);
+  w.dapart = b.take(D.L * D.H * kMaxAttnSplit * (D.dh + 2) * f4);
   w.dmlp_v = b.take(D.L * D.F * f4);
   w.dlogits = b.take(D.V * f4);
   w.dsteps = b.take((size_t)kMaxDecInst * sizeof(StepCtx));
+  w.dsched = b.take(sizeof(Sched));
+  w.dpart_v = b.take(D.V * f4);
+  w.dpart_i = b.take(D.V * 4);
   w.misc = b.take(kMiscBytes);
+  w.trace = (c.debug_flags & OFA_DEBUG_TRACE) ? b.take((size_t)OFA_TRACE_INSTANCES * kMaxPhases * 32) : 0;
   w.total = (b.off + kAlign - 1) / kAlign * kAlign;
   return w;
 }
@@ -264,12 +270,14 @@ struct ofa_handle {
   hipStream_t stream = nullptr;
   char* ws = nullptr;
   int n_cu = 0;
+  int serve_wgs = 0;               // workgroups that run decode (one per serve CU)
   std::vector<Phase> train;        // one training step
   std::vector<Phase> dec;          // one decode position (with head)
   Phase* d_train = nullptr;        // device copies (inside the pinned-upload area)
   Phase* d_dec = nullptr;
   std::vector<char> phase_names;   // for phase_times
   std::vector<std::string> train_names;
+  std::vector<std::string> dec_names;
   StepCtx* h_steps = nullptr;      // pinned staging
   StepCtx* h_dsteps = nullptr;
   char* h_misc = nullptr;          // pinned staging for the misc block
@@ -280,6 +288,10 @@ struct ofa_handle {
   uint64_t version = 0;
   int sticky = 0;
   int last_grid = 0;
+  bool plan_ok = true;             // every decode GEMV found an LDS plan
+  int trace_n_phases = 0;          // program length of the last traced launch (0 = none)
+  int64_t trace_n_inst = 0;
+  bool trace_dec = false;          // the last traced launch was a decode call
   uint64_t last_tickets = 0;
   double last_ms = 0;
   std::string err;
@@ -381,7 +393,7 @@ void finish_program(std::vector<Phase>& prog) {
   for (auto& ph : prog) {
     ph.tile_base = tiles;
     tiles += ph.n_tiles;
-    ph.per_ticket = std::max(1, cdiv(ph.n_tiles, kTicketsPerPhase));
+    if (ph.per_ticket <= 0) ph.per_ticket = std::max(1, cdiv(ph.n_tiles, kTicketsPerPhase));
     ph.n_tickets = cdiv(ph.n_tiles, ph.per_ticket);
     ph.ticket_base = tickets;
     tickets += ph.n_tickets;
@@ -766,6 +778,50 @@ void build_train(ofa_handle* h) {
   finish_program(h->train);
 }
 
+// Tile plan of a decode GEMV, whose task streams weight tiles through an LDS
+// ring of fixed-size buffers: rows per tile chosen so that each of the G serve
+// workgroups gets one ticket of whole tiles, up to four tiles in flight where
+// the LDS allows.  With the rotation on, a ticket covers whole heads.
+constexpr int kDecTileHost = 32768;   // bytes of one tile buffer (the task's kDecTile)
+
+bool plan_gemv(Phase& ph, int G) {
+  DecGemvArgs& a = ph.a.dgemv;
+  const int64_t rb = (int64_t)a.K * (a.w_dt == DT_BF16 ? 2 : 4);
+  const int halves = a.epi == DEPI_GEGLU ? 2 : 1;
+  const int total = a.epi == DEPI_GEGLU ? a.F : a.N;
+  const bool whole_heads = a.epi == DEPI_QKV && a.rope;
+  const size_t avail = std::min(persistent_lds_bytes(), lds_limit_bytes());
+  const int nch = (int)(rb / 16);
+  if (nch > 64 * 8) return false;                       // a row needs more than 8 chunks per lane
+  const int lpr = nch <= 16 * 8 ? 16 : (nch <= 32 * 8 ? 32 : 64);
+  const int r_max = (int)std::min<int64_t>({(int64_t)kDecTileHost / halves / rb, (int64_t)total,
+                                            (int64_t)8 * (kThreadsHost / lpr) / halves});
+  if (r_max < 1) return false;
+  int R, per;
+  if (whole_heads) {
+    R = (int)a.dh;   // a power of two (the head size divides 256)
+    while (R > r_max) R /= 2;
+    const int rows_wg = cdiv(cdiv(total, G), a.dh) * (int)a.dh;
+    per = cdiv(rows_wg, R);
+  } else {
+    const int rows_wg = cdiv(total, G);
+    per = cdiv(rows_wg, r_max);
+    R = cdiv(rows_wg, per);
+  }
+  a.rows_per_tile = R;
+  a.lpr = lpr;
+  const int per_group = cdiv(halves * R, kThreadsHost / lpr);
+  a.rpg = per_group <= 1 ? 1 : per_group <= 2 ? 2 : per_group <= 4 ? 4 : 8;
+  a.tile_bytes = kDecTileHost;
+  a.ys_rows = (per * R + 3) / 4 * 4;   // keeps the LDS areas after it 16-byte aligned
+  ph.n_tiles = cdiv(total, R);
+  ph.per_ticket = per;
+  a.per_ticket = per;
+  for (a.n_buf = std::min(4, per); a.n_buf >= 1; --a.n_buf)
+    if (phase_lds_bytes(ph) <= avail) return true;
+  return false;
+}
+
 // decode program for one position (head phases skip themselves when the
 // instance has no head)
 void build_decode(ofa_handle* h) {
@@ -774,7 +830,8 @@ void build_decode(ofa_handle* h) {
   const Carve& w = h->cw;
   char* ws = h->ws;
   h->dec.clear();
-  Builder b{&h->dec, nullptr};
+  h->dec_names.clear();
+  Builder b{&h->dec, &h->dec_names};
   const int lp = D.lp_dt;
   const int64_t d = D.d, F = D.F, V = D.V;
   char* S = ws + w.serve;   // slot 0
@@ -797,10 +854,10 @@ void build_decode(ofa_handle* h) {
     a.V = (int)V;
     a.w_dt = lp;
   }
-  auto gemv = [&](int dep, const void* W, const void* bias, const float* xin, const void* lg, const void* lb, float* y,
+  auto gemv = [&](const char* nm, int dep, const void* W, const void* bias, const float* xin, const void* lg, const void* lb, float* y,
                   int N, int K, int epi, int rpt) {
-    int n_rows = epi == DEPI_GEGLU ? (int)F : N;
-    int p = b.add(OP_DEC_GEMV, cdiv(n_rows, rpt), "dec_gemv", {dep});
+    (void)rpt;
+    int p = b.add(OP_DEC_GEMV, 1, nm, {dep});
     DecGemvArgs& a = b[p].a.dgemv;
     a.W = W;
     a.bias = bias;
@@ -822,49 +879,60 @@ void build_decode(ofa_handle* h) {
     a.rope = c.n_pos == 0;
     a.F = (int)F;
     a.io = at<DecIO>(ws, w.misc + kMiscDecIO);
+    a.pre_dep = slot_bytes ? p_emb : -1;
+    if (!plan_gemv(b[p], h->serve_wgs)) h->plan_ok = false;
     return p;
   };
   int last = p_emb;
   for (int l = 0; l < D.L; ++l) {
     const LayerOff& lo = h->lay.layer[l];
     void* kv = ws + w.kv + (size_t)l * 2 * D.H * D.win * D.dh * D.lp;
-    int p_qkv = gemv(last, sw(lo.w_qkv), sw(lo.b_qkv), XV(2 * l), sw(lo.ln1_g), sw(lo.ln1_b), at<float>(ws, w.dq),
+    int p_qkv = gemv("dec_qkv", last, sw(lo.w_qkv), sw(lo.b_qkv), XV(2 * l), sw(lo.ln1_g), sw(lo.ln1_b), at<float>(ws, w.dq),
                      (int)(3 * d), (int)d, DEPI_QKV, (int)D.dh);
     b[p_qkv].a.dgemv.kv = kv;
-    int p_att = b.add(OP_DEC_ATTN, (int)D.H, "dec_attn", {p_qkv});
+    const int split = std::max(1, std::min(kMaxAttnSplit, h->serve_wgs / (int)D.H));
+    float* apart = at<float>(ws, w.dapart) + (int64_t)l * D.H * kMaxAttnSplit * (D.dh + 2);
+    int p_att = b.add(OP_DEC_ATTN, (int)D.H * split, "dec_attn", {p_qkv});
     {
       DecAttnArgs& a = b[p_att].a.dattn;
       a.q = at<float>(ws, w.dq);
       a.kv = kv;
-      a.o = at<float>(ws, w.dvo) + l * d;
+      a.part = apart;
       a.H = (int)D.H;
       a.dh = (int)D.dh;
       a.cap = (int)D.win;
       a.kv_dt = lp;
+      a.split = split;
     }
-    int p_o = gemv(p_att, sw(lo.w_o), sw(lo.b_o), at<float>(ws, w.dvo) + l * d, nullptr, nullptr, XV(2 * l + 1),
+    int p_o = gemv("dec_attn_out", p_att, sw(lo.w_o), sw(lo.b_o), nullptr, nullptr, nullptr, XV(2 * l + 1),
                    (int)d, (int)d, DEPI_RESID, 16);
+    b[p_o].a.dgemv.attn_part = apart;
+    b[p_o].a.dgemv.attn_split = split;
     b[p_o].a.dgemv.resid = XV(2 * l);
     float* act = at<float>(ws, w.dmlp_v) + l * F;
     int p_fc;
     if (c.mlp_gated)
-      p_fc = gemv(p_o, sw(lo.w_gate), nullptr, XV(2 * l + 1), sw(lo.ln2_g), sw(lo.ln2_b), act, (int)(2 * F), (int)d,
+      p_fc = gemv("dec_fc", p_o, sw(lo.w_gate), nullptr, XV(2 * l + 1), sw(lo.ln2_g), sw(lo.ln2_b), act, (int)(2 * F), (int)d,
                   DEPI_GEGLU, 16);
     else
-      p_fc = gemv(p_o, sw(lo.w_fc), sw(lo.b_fc), XV(2 * l + 1), sw(lo.ln2_g), sw(lo.ln2_b), act, (int)F, (int)d,
+      p_fc = gemv("dec_fc", p_o, sw(lo.w_fc), sw(lo.b_fc), XV(2 * l + 1), sw(lo.ln2_g), sw(lo.ln2_b), act, (int)F, (int)d,
                   DEPI_GELU, 16);
-    int p_pr = gemv(p_fc, sw(c.mlp_gated ? lo.w_down : lo.w_proj), sw(lo.b_proj), act, nullptr, nullptr,
+    int p_pr = gemv("dec_proj", p_fc, sw(c.mlp_gated ? lo.w_down : lo.w_proj), sw(lo.b_proj), act, nullptr, nullptr,
                     XV(2 * l + 2), (int)d, (int)F, DEPI_RESID, 16);
     b[p_pr].a.dgemv.resid = XV(2 * l + 1);
     last = p_pr;
   }
   const int64_t w_lm = c.tied_head ? h->lay.wte : h->lay.w_lm;
-  int p_lm = gemv(last, sw(w_lm), nullptr, XV(2 * (int)D.L), sw(h->lay.lnf_g), sw(h->lay.lnf_b),
+  int p_lm = gemv("dec_lm_head", last, sw(w_lm), nullptr, XV(2 * (int)D.L), sw(h->lay.lnf_g), sw(h->lay.lnf_b),
                   at<float>(ws, w.dlogits), (int)V, (int)d, DEPI_LOGITS, 16);
+  b[p_lm].a.dgemv.part_val = at<float>(ws, w.dpart_v);
+  b[p_lm].a.dgemv.part_idx = at<int32_t>(ws, w.dpart_i);
   int p_am = b.add(OP_DEC_ARGMAX, 1, "dec_argmax", {p_lm});
   {
     DecArgmaxArgs& a = b[p_am].a.dargmax;
-    a.logits = at<float>(ws, w.dlogits);
+    a.part_val = at<float>(ws, w.dpart_v);
+    a.part_idx = at<int32_t>(ws, w.dpart_i);
+    a.n_part = cdiv(b[p_lm].n_tiles, b[p_lm].per_ticket);
     a.ctx_tok = at<int32_t>(ws, w.ctx_tok);
     a.st = st;
     a.io = at<DecIO>(ws, w.misc + kMiscDecIO);
@@ -920,6 +988,50 @@ ofa_status run_launch_per_phase(ofa_handle* h, const std::vector<Phase>& prog, c
       HIP_TRY(h, launch_phase(prog[i], d_prog, (int)i, d_ctx + s, st, tm, step0 + s, h->stream));
     }
   }
+  return OFA_OK;
+}
+
+// One persistent launch of n_inst instances of a program on `cus` CUs, with
+// the scheduler block at sched_off (reset here: ticket and counters start at
+// the debug base).
+ofa_status run_persistent(ofa_handle* h, const std::vector<Phase>& prog, const Phase* d_prog, const StepCtx* d_ctx,
+                          int64_t n_inst, size_t sched_off, PhaseTime* times, uint64_t* inst_end, int cus) {
+  const ofa_config& c = h->cfg;
+  const int np = (int)prog.size();
+  Sched* sc = at<Sched>(h->ws, sched_off);
+  const uint64_t base = c.debug_counter_base;
+  HIP_TRY(h, launch_fill_u64(&sc->ticket, base, 1, h->stream));
+  HIP_TRY(h, launch_fill_u64(&sc->base, base, 1, h->stream));
+  HIP_TRY(h, launch_fill_u64(&sc->abort, 0, 2, h->stream));
+  HIP_TRY(h, launch_fill_u64(sc->done, base, np, h->stream));
+  if (inst_end) HIP_TRY(h, launch_fill_u64(inst_end, 0, n_inst, h->stream));
+  PersistParams pp;
+  memset(&pp, 0, sizeof pp);
+  pp.phases = d_prog;
+  pp.n_phases = np;
+  pp.tickets_per_inst = prog.back().ticket_base + prog.back().n_tickets;
+  pp.n_inst = n_inst;
+  pp.steps = d_ctx;
+  pp.sched = sc;
+  pp.status = at<DevStatus>(h->ws, h->cw.status);
+  pp.times = times;
+  pp.inst_end = inst_end;
+  pp.watchdog_ticks = (c.debug_flags & OFA_DEBUG_SHORT_WATCHDOG) ? 100000ull : 1000000000ull;
+  pp.shuffle = (c.debug_flags & OFA_DEBUG_SHUFFLE_TICKETS) ? 1 : 0;
+  h->trace_n_phases = 0;
+  h->trace_dec = sched_off == h->cw.dsched;
+  if (c.debug_flags & OFA_DEBUG_TRACE) {
+    pp.trace = at<uint64_t>(h->ws, h->cw.trace);
+    pp.trace_inst = std::min<int64_t>(n_inst, OFA_TRACE_INSTANCES);
+    HIP_TRY(h, launch_fill_u64(pp.trace, 0, pp.trace_inst * np * 4, h->stream));
+    h->trace_n_phases = np;
+    h->trace_n_inst = pp.trace_inst;
+  }
+  const int occ = persistent_occupancy();
+  if (occ < 1) return fail(h, OFA_E_HIP, "persistent kernel does not fit a CU");
+  const int grid = cus * occ;
+  h->last_grid = grid;
+  HIP_TRY(h, launch_persistent(pp, grid, h->stream));
   return OFA_OK;
 }
 
@@ -1035,8 +1147,13 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
   HIP_TRY(h, hipEventCreateWithFlags(&h->ev_upload, hipEventDisableTiming));
   HIP_TRY(h, hipEventCreate(&h->ev_t0));
   HIP_TRY(h, hipEventCreate(&h->ev_t1));
+  {
+    const int occ = std::max(1, persistent_occupancy());
+    h->serve_wgs = (h->cfg.serve_cus > 0 ? h->cfg.serve_cus : h->n_cu) * occ;
+  }
   build_train(h);
   build_decode(h);
+  if (!h->plan_ok) return fail(h, OFA_E_ARG, "a decode matrix-vector product does not fit the LDS");
   if (h->train.size() > (size_t)kMaxPhases || h->dec.size() > (size_t)kMaxPhases)
     return fail(h, OFA_E_ARG, "program too long");
   for (const auto* prog : {&h->train, &h->dec})
@@ -1187,32 +1304,10 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
     s = run_launch_per_phase(h, h->train, h->d_train, d_steps, n_steps, (int64_t)h->steps_done, false);
     if (s != OFA_OK) return s;
   } else {
-    Sched* sc = at<Sched>(h->ws, h->cw.sched);
-    const uint64_t base = c.debug_counter_base;
-    HIP_TRY(h, launch_fill_u64(&sc->ticket, base, 1, h->stream));
-    HIP_TRY(h, launch_fill_u64(&sc->base, base, 1, h->stream));
-    HIP_TRY(h, launch_fill_u64(&sc->abort, 0, 2, h->stream));
-    HIP_TRY(h, launch_fill_u64(sc->done, base, np, h->stream));
-    HIP_TRY(h, launch_fill_u64(at<uint64_t>(h->ws, h->cw.inst_end), 0, n_steps, h->stream));
-    PersistParams pp;
-    memset(&pp, 0, sizeof pp);
-    pp.phases = h->d_train;
-    pp.n_phases = np;
-    pp.tickets_per_inst = h->train.back().ticket_base + h->train.back().n_tickets;
-    pp.n_inst = n_steps;
-    pp.steps = d_steps;
-    pp.sched = sc;
-    pp.status = at<DevStatus>(h->ws, h->cw.status);
-    pp.times = tm;
-    pp.inst_end = at<uint64_t>(h->ws, h->cw.inst_end);
-    pp.watchdog_ticks = (c.debug_flags & OFA_DEBUG_SHORT_WATCHDOG) ? 100000ull : 1000000000ull;
-    pp.shuffle = (c.debug_flags & OFA_DEBUG_SHUFFLE_TICKETS) ? 1 : 0;
-    int occ = persistent_occupancy();
-    if (occ < 1) return fail(h, OFA_E_HIP, "persistent kernel does not fit a CU");
     int cus = c.train_cus > 0 ? c.train_cus : h->n_cu;
-    int grid = cus * occ;
-    h->last_grid = grid;
-    HIP_TRY(h, launch_persistent(pp, grid, h->stream));
+    s = run_persistent(h, h->train, h->d_train, d_steps, n_steps, h->cw.sched, tm,
+                       at<uint64_t>(h->ws, h->cw.inst_end), cus);
+    if (s != OFA_OK) return s;
   }
   HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
   h->timed = true;
@@ -1271,8 +1366,14 @@ ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_
   if (s != OFA_OK) return s;
   s = mark_upload(h);
   if (s != OFA_OK) return s;
+  PhaseTime* dtm = at<PhaseTime>(ws, h->cw.dtimes);
+  HIP_TRY(h, launch_fill_pairs((uint64_t*)dtm, ~0ull, 0ull, (int64_t)h->dec.size(), h->stream));
   HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
-  s = run_launch_per_phase(h, h->dec, h->d_dec, d_dsteps, n_inst, 0, true);
+  if (h->cfg.exec_mode == OFA_EXEC_LAUNCH_PER_PHASE)
+    s = run_launch_per_phase(h, h->dec, h->d_dec, d_dsteps, n_inst, 0, true);
+  else
+    s = run_persistent(h, h->dec, h->d_dec, d_dsteps, n_inst, h->cw.dsched, dtm, nullptr,
+                       h->serve_wgs / std::max(1, persistent_occupancy()));
   if (s != OFA_OK) return s;
   HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
   h->timed = true;
@@ -1320,19 +1421,44 @@ ofa_status ofa_status_sync(ofa_handle* h, ofa_stats* out) {
   return ds.code ? (ofa_status)ds.code : OFA_OK;
 }
 
-ofa_status ofa_phase_times(ofa_handle* h, uint64_t* host_t, int32_t n, int32_t* n_out, char* names,
-                           size_t name_stride) {
+static ofa_status phase_times_of(ofa_handle* h, const std::vector<std::string>& nm, size_t off, uint64_t* host_t,
+                                 int32_t n, int32_t* n_out, char* names, size_t name_stride) {
   if (!h || !host_t || !n_out) return OFA_E_ARG;
   HIP_TRY(h, hipStreamSynchronize(h->stream));
-  int np = std::min<int>(n, (int)h->train.size());
-  HIP_TRY(h, hipMemcpy(host_t, h->ws + h->cw.times, np * sizeof(PhaseTime), hipMemcpyDeviceToHost));
+  int np = std::min<int>(n, (int)nm.size());
+  HIP_TRY(h, hipMemcpy(host_t, h->ws + off, np * sizeof(PhaseTime), hipMemcpyDeviceToHost));
   if (names && name_stride)
     for (int i = 0; i < np; ++i) {
-      strncpy(names + i * name_stride, h->train_names[i].c_str(), name_stride - 1);
+      strncpy(names + i * name_stride, nm[i].c_str(), name_stride - 1);
       names[i * name_stride + name_stride - 1] = 0;
     }
   *n_out = np;
   return OFA_OK;
+}
+
+ofa_status ofa_phase_times(ofa_handle* h, uint64_t* host_t, int32_t n, int32_t* n_out, char* names,
+                           size_t name_stride) {
+  if (!h) return OFA_E_ARG;
+  return phase_times_of(h, h->train_names, h->cw.times, host_t, n, n_out, names, name_stride);
+}
+
+ofa_status ofa_trace(ofa_handle* h, int32_t decode, uint64_t* host_t, int64_t n, int64_t* n_out, int32_t* n_phases) {
+  if (!h || !host_t || !n_out || !n_phases) return OFA_E_ARG;
+  if (!(h->cfg.debug_flags & OFA_DEBUG_TRACE)) return fail(h, OFA_E_STATE, "tracing is off in this configuration");
+  if (!h->trace_n_phases || h->trace_dec != (decode != 0)) return fail(h, OFA_E_STATE, "no traced call of that kind");
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  const int64_t quads = std::min<int64_t>(n / 2, h->trace_n_inst * h->trace_n_phases);
+  HIP_TRY(h, hipMemcpy(host_t, h->ws + h->cw.trace, quads * 32, hipMemcpyDeviceToHost));
+  for (int64_t i = 0; i < quads; ++i) host_t[4 * i] = ~host_t[4 * i];   // stored complemented
+  *n_out = quads;
+  *n_phases = h->trace_n_phases;
+  return OFA_OK;
+}
+
+ofa_status ofa_decode_phase_times(ofa_handle* h, uint64_t* host_t, int32_t n, int32_t* n_out, char* names,
+                                  size_t name_stride) {
+  if (!h) return OFA_E_ARG;
+  return phase_times_of(h, h->dec_names, h->cw.dtimes, host_t, n, n_out, names, name_stride);
 }
 
 }  // extern "C"

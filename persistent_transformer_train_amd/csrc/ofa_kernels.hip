@@ -26,44 +26,54 @@ namespace ofa {
 
 // ---------------------------------------------------------------- dispatch
 
+// Each task receives a by-value copy of its argument block, read once when the
+// task starts: arguments read through the phase-table reference inside the
+// tasks' loops would be reloaded on every iteration (the compiler cannot rule
+// out that the loop's stores change them), and every such reload waits for all
+// outstanding memory operations, the streaming copies included.
+#define OFA_ARGS(FIELD) const auto a = ph.a.FIELD
 template <int OP>
 __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCtx& tc, char* smem) {
-  if constexpr (OP == OP_EMBED) task_embed(ph.a.emb, tile, tc);
-  else if constexpr (OP == OP_LN_FWD) task_ln_fwd(ph.a.lnf, tile);
+  if constexpr (OP == OP_EMBED) { OFA_ARGS(emb); task_embed(a, tile, tc); }
+  else if constexpr (OP == OP_LN_FWD) { OFA_ARGS(lnf); task_ln_fwd(a, tile); }
   else if constexpr (OP == OP_GEMM) {
     if (ph.a.gemm.impl == GEMM_P3) task_gemm_p3(ph.a.gemm, tile, smem);
     else task_gemm_simple(ph.a.gemm, tile, smem);
   }
-  else if constexpr (OP == OP_ROPE) task_rope(ph.a.rope, tile, false);
+  else if constexpr (OP == OP_ROPE) { OFA_ARGS(rope); task_rope(a, tile, false); }
   else if constexpr (OP == OP_ATTN_FWD) {
-    if (ph.a.attn.impl == 1) task_attn_fwd_mfma(ph.a.attn, tile, smem);
-    else task_attn_fwd_simple(ph.a.attn, tile, smem);
+    OFA_ARGS(attn);
+    if (a.impl == 1) task_attn_fwd_mfma(a, tile, smem);
+    else task_attn_fwd_simple(a, tile, smem);
   }
-  else if constexpr (OP == OP_GEGLU_FWD) task_geglu_fwd(ph.a.geglu, tile);
-  else if constexpr (OP == OP_CE) task_ce(ph.a.ce, tile, tc, smem);
-  else if constexpr (OP == OP_LOSS) task_loss(ph.a.loss, tc, smem);
-  else if constexpr (OP == OP_LN_BWD) task_ln_bwd(ph.a.lnb, tile, smem);
-  else if constexpr (OP == OP_COLSUM) task_colsum(ph.a.cs, tile);
-  else if constexpr (OP == OP_COLRED) task_colred(ph.a.cr, tile, smem);
-  else if constexpr (OP == OP_ATTN_PREP) task_attn_prep(ph.a.attn, tile);
+  else if constexpr (OP == OP_GEGLU_FWD) { OFA_ARGS(geglu); task_geglu_fwd(a, tile); }
+  else if constexpr (OP == OP_CE) { OFA_ARGS(ce); task_ce(a, tile, tc, smem); }
+  else if constexpr (OP == OP_LOSS) { OFA_ARGS(loss); task_loss(a, tc, smem); }
+  else if constexpr (OP == OP_LN_BWD) { OFA_ARGS(lnb); task_ln_bwd(a, tile, smem); }
+  else if constexpr (OP == OP_COLSUM) { OFA_ARGS(cs); task_colsum(a, tile); }
+  else if constexpr (OP == OP_COLRED) { OFA_ARGS(cr); task_colred(a, tile, smem); }
+  else if constexpr (OP == OP_ATTN_PREP) { OFA_ARGS(attn); task_attn_prep(a, tile); }
   else if constexpr (OP == OP_ATTN_BWD_KV) {
-    if (ph.a.attn.impl == 1) task_attn_bwd_kv_mfma(ph.a.attn, tile, smem);
-    else task_attn_bwd_kv_simple(ph.a.attn, tile, smem);
+    OFA_ARGS(attn);
+    if (a.impl == 1) task_attn_bwd_kv_mfma(a, tile, smem);
+    else task_attn_bwd_kv_simple(a, tile, smem);
   }
   else if constexpr (OP == OP_ATTN_BWD_Q) {
-    if (ph.a.attn.impl == 1) task_attn_bwd_q_mfma(ph.a.attn, tile, smem);
-    else task_attn_bwd_q_simple(ph.a.attn, tile, smem);
+    OFA_ARGS(attn);
+    if (a.impl == 1) task_attn_bwd_q_mfma(a, tile, smem);
+    else task_attn_bwd_q_simple(a, tile, smem);
   }
-  else if constexpr (OP == OP_ROPE_BWD) task_rope(ph.a.rope, tile, true);
-  else if constexpr (OP == OP_EMB_SORT) task_emb_sort(ph.a.esort, tc, smem);
-  else if constexpr (OP == OP_EMB_BWD) task_emb_bwd(ph.a.ebwd, tile, tc);
-  else if constexpr (OP == OP_ADAMW) task_adamw(ph.a.adam, tile, tc);
-  else if constexpr (OP == OP_COPY) task_copy(ph.a.copy, tile);
-  else if constexpr (OP == OP_DEC_EMBED) task_dec_embed(ph.a.dembed, tile, tc);
-  else if constexpr (OP == OP_DEC_GEMV) task_dec_gemv(ph.a.dgemv, tile, tc, smem);
-  else if constexpr (OP == OP_DEC_ATTN) task_dec_attn(ph.a.dattn, tile, tc, smem);
-  else if constexpr (OP == OP_DEC_ARGMAX) task_dec_argmax(ph.a.dargmax, tile, tc, smem);
+  else if constexpr (OP == OP_ROPE_BWD) { OFA_ARGS(rope); task_rope(a, tile, true); }
+  else if constexpr (OP == OP_EMB_SORT) { OFA_ARGS(esort); task_emb_sort(a, tc, smem); }
+  else if constexpr (OP == OP_EMB_BWD) { OFA_ARGS(ebwd); task_emb_bwd(a, tile, tc); }
+  else if constexpr (OP == OP_ADAMW) { OFA_ARGS(adam); task_adamw(a, tile, tc); }
+  else if constexpr (OP == OP_COPY) { OFA_ARGS(copy); task_copy(a, tile); }
+  else if constexpr (OP == OP_DEC_EMBED) { OFA_ARGS(dembed); task_dec_embed(a, tile, tc); }
+  else if constexpr (OP == OP_DEC_GEMV) { OFA_ARGS(dgemv); task_dec_gemv(a, tile, tc, smem); }
+  else if constexpr (OP == OP_DEC_ATTN) { OFA_ARGS(dattn); task_dec_attn(a, tile, tc, smem); }
+  else if constexpr (OP == OP_DEC_ARGMAX) { OFA_ARGS(dargmax); task_dec_argmax(a, tile, tc, smem); }
 }
+#undef OFA_ARGS
 
 __device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& tc, char* smem) {
   switch (ph.op) {
@@ -79,6 +89,16 @@ __device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& t
   }
 }
 
+__device__ __noinline__ void run_dec_gemv(const Phase& ph, int t0, int t1, const TaskCtx& tc, char* smem, int npre) {
+  const DecGemvArgs a = ph.a.dgemv;
+  task_dec_gemv_range(a, t0, t1, tc, smem, npre);
+}
+
+__device__ __noinline__ int prefetch_dec_gemv(const Phase& ph, int t0, int t1, char* smem, bool allowed) {
+  const DecGemvArgs a = ph.a.dgemv;
+  return dec_gemv_prefetch(a, t0, t1, smem, allowed);
+}
+
 // ---------------------------------------------------------------- executor 1: one launch per phase
 
 template <int OP>
@@ -88,7 +108,14 @@ __global__ __launch_bounds__(kThreads) void phase_kernel(const Phase* phases, in
   const Phase& ph = phases[idx];
   TaskCtx tc{sc, status, idx, step};
   const uint64_t t0 = now_ticks();
-  for (int tile = blockIdx.x; tile < ph.n_tiles; tile += gridDim.x) run_task<OP>(ph, tile, tc, smem);
+  if constexpr (OP == OP_DEC_GEMV) {
+    // one workgroup per ticket, as the persistent executor hands them out
+    const DecGemvArgs a = ph.a.dgemv;
+    for (int t = blockIdx.x; t < ph.n_tickets; t += gridDim.x)
+      task_dec_gemv_range(a, t * ph.per_ticket, min((t + 1) * ph.per_ticket, ph.n_tiles), tc, smem, 0);
+  } else {
+    for (int tile = blockIdx.x; tile < ph.n_tiles; tile += gridDim.x) run_task<OP>(ph, tile, tc, smem);
+  }
   if (times && threadIdx.x == 0) {
     atomicMin((unsigned long long*)&times[idx].t0, (unsigned long long)t0);
     atomicMax((unsigned long long*)&times[idx].t1, (unsigned long long)now_ticks());
@@ -136,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
   extern __shared__ __align__(16) char smem[];
   __shared__ uint64_t s_ticket;
   __shared__ int s_ok;
+  __shared__ int s_pre;
   __shared__ int64_t s_all_checked;   // instance whose every phase this workgroup saw complete
   const uint64_t base = p.sched->base;
   const uint64_t total = (uint64_t)p.n_inst * (uint64_t)p.tickets_per_inst;
@@ -144,8 +172,7 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
     if (threadIdx.x == 0) s_ticket = add_relaxed(&p.sched->ticket, 1) - base;
     __syncthreads();
     // wave-uniform copy, so the phase table is read with scalar loads
-    const uint64_t t = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(s_ticket >> 32)) << 32) |
-                       (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)s_ticket);
+    const uint64_t t = readfirstlane_u64(s_ticket);
     if (t >= total) break;
     const int64_t inst = (int64_t)(t / (uint64_t)p.tickets_per_inst);
     const int r = (int)(t % (uint64_t)p.tickets_per_inst);
@@ -161,6 +188,24 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
     int tile0 = j * ph.per_ticket;
     const int tile1 = min(tile0 + ph.per_ticket, ph.n_tiles);
     TaskCtx tc{p.steps + inst, p.status, pi, inst};
+    // a decode GEMV starts streaming its weights before its dependencies are
+    // met; with two weight slots only once this token's version is known
+    int npre = 0;
+    if (ph.op == OP_DEC_GEMV) {
+      const DecGemvArgs& a = ph.a.dgemv;
+      bool allow = !(a.epi == DEPI_LOGITS && !(tc.sc->head & 1));
+      if (allow && a.pre_dep >= 0) {
+        if (threadIdx.x == 0) {
+          const bool seen = ld_relaxed(&p.sched->done[a.pre_dep]) >=
+                            base + (uint64_t)(inst + 1) * p.phases[a.pre_dep].n_tiles;
+          if (seen) fence_acquire_agent();
+          s_pre = seen ? 1 : 0;
+        }
+        __syncthreads();
+        allow = __builtin_amdgcn_readfirstlane(s_pre) != 0;
+      }
+      npre = prefetch_dec_gemv(ph, tile0, tile1, smem, allow);
+    }
     // wait for the dependencies (thread 0), then one acquire for the workgroup
     if (threadIdx.x == 0) {
       bool ok = true;
@@ -182,9 +227,18 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
       s_ok = ok ? 1 : 0;
     }
     __syncthreads();
-    if (!__builtin_amdgcn_readfirstlane(s_ok)) break;
+    if (!__builtin_amdgcn_readfirstlane(s_ok)) {
+      if (npre) vm_wait_barrier(0);   // no copy may land in LDS after the exit
+      break;
+    }
     const uint64_t t0 = now_ticks();
-    for (int tile = tile0; tile < tile1; ++tile) {
+    if (p.trace && inst < p.trace_inst && threadIdx.x == 0) {
+      // word 0 keeps the complement of the earliest start, so every word starts at 0 and takes a maximum
+      atomicMax((unsigned long long*)&p.trace[4 * (inst * p.n_phases + pi)], ~(unsigned long long)t0);
+      atomicMax((unsigned long long*)&p.trace[4 * (inst * p.n_phases + pi) + 1], (unsigned long long)t0);
+    }
+    if (ph.op == OP_DEC_GEMV) run_dec_gemv(ph, tile0, tile1, tc, smem, npre);
+    else for (int tile = tile0; tile < tile1; ++tile) {
       int tl = tile;
       if (p.shuffle && ph.n_tiles > 1) {
         // reversal after a rotation: a permutation of the phase's tiles
@@ -197,6 +251,8 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
     // release fence then makes them visible before the counter moves
     __syncthreads();
     if (threadIdx.x == 0) {
+      if (p.trace && inst < p.trace_inst)
+        atomicMax((unsigned long long*)&p.trace[4 * (inst * p.n_phases + pi) + 2], (unsigned long long)now_ticks());
       fence_release_agent();
       add_relaxed(&p.sched->done[pi], (uint64_t)(tile1 - tile0));
       if (p.times) {
@@ -204,6 +260,8 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
         atomicMax((unsigned long long*)&p.times[pi].t1, (unsigned long long)now_ticks());
       }
       if (p.inst_end) atomicMax((unsigned long long*)&p.inst_end[inst], (unsigned long long)now_ticks());
+      if (p.trace && inst < p.trace_inst)
+        atomicMax((unsigned long long*)&p.trace[4 * (inst * p.n_phases + pi) + 3], (unsigned long long)now_ticks());
     }
   }
   if (threadIdx.x == 0) add_relaxed(&p.sched->exited, 1);
@@ -263,17 +321,32 @@ static bool g_p3_ok = false;
 size_t persistent_lds_bytes() { return g_persist_lds; }
 bool gemm_p3_available() { return g_p3_ok; }
 
+// Dynamic LDS of the persistent kernel (and of the kernels whose phases need
+// more than the default): as much of the CU's LDS as one workgroup may hold,
+// at least the pipelined GEMM's ring.  The persistent kernel runs one
+// workgroup per CU in any case (registers), so the LDS is otherwise idle.
 hipError_t init_kernels() {
-  const int want = (int)gemm_p3_lds_bytes() + 2048;
-  hipError_t e1 = hipFuncSetAttribute((const void*)gemm_kernel<GEMM_P3>,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, want);
-  hipError_t e2 = hipFuncSetAttribute((const void*)persistent_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      want);
+  int dev = 0, max_blk = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&max_blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    max_blk = 64 * 1024;
   (void)hipGetLastError();
-  if (e1 == hipSuccess && e2 == hipSuccess) {
+  hipFuncAttributes fa;
+  size_t stat = 2048;
+  if (hipFuncGetAttributes(&fa, (const void*)persistent_kernel) == hipSuccess) stat = fa.sharedSizeBytes;
+  (void)hipGetLastError();
+  size_t want = max_blk > (int)stat ? ((size_t)max_blk - stat) / 1024 * 1024 : 0;
+  if (want < gemm_p3_lds_bytes()) return hipSuccess;   // pipelined GEMM unavailable; small tiles only
+  const void* big[] = {(const void*)gemm_kernel<GEMM_P3>, (const void*)persistent_kernel,
+                       (const void*)phase_kernel<OP_DEC_GEMV>};
+  bool ok = true;
+  for (const void* f : big)
+    ok = ok && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)want) == hipSuccess;
+  (void)hipGetLastError();
+  if (ok) {
     g_p3_ok = true;
-    g_lds_limit = gemm_p3_lds_bytes();
-    g_persist_lds = gemm_p3_lds_bytes();
+    g_lds_limit = want;
+    g_persist_lds = want;
   }
   return hipSuccess;
 }
@@ -293,7 +366,7 @@ hipError_t launch_phase(const Phase& h, const Phase* d_phases, int idx, const St
                         PhaseTime* tm, int64_t step, hipStream_t s) {
   if (h.n_tiles <= 0) return hipSuccess;
   (void)hipGetLastError();   // report this launch's error, not a stale one
-  const int grid = h.n_tiles;
+  const int grid = h.op == OP_DEC_GEMV ? h.n_tickets : h.n_tiles;
   const size_t lds = lds_for(h);
   if (h.op == OP_GEMM) {
     if (h.a.gemm.impl == GEMM_P3)

@@ -19,6 +19,8 @@ struct PersistParams {
   uint64_t* inst_end;        // [n_inst] device time each instance finished (nullable)
   uint64_t watchdog_ticks;   // a wait longer than this raises OFA_E_TIMEOUT
   int32_t shuffle;           // debug: permute tiles inside a phase
+  uint64_t* trace;           // debug: [trace_inst][n_phases] (first start, last end) pairs (nullable)
+  int64_t trace_inst;
 };
 
 hipError_t init_kernels();

@@ -221,17 +221,31 @@ struct DecGemvArgs {
   const DecIO* io;           // DEPI_LOGITS: optional logits copy
   DecState* st;
   int32_t N, K, w_dt, kv_dt, epi, rows_per_tile, d, H, dh, cap, rope, F;
+  // LDS plan: weight tiles stream through a ring of n_buf buffers of tile_bytes
+  // (a multiple of 4 KB) each; ys_rows = rows of the largest ticket
+  int32_t tile_bytes, n_buf, ys_rows;
+  // phase whose completion for the current instance must be seen before the
+  // weights may be prefetched (the token's version acquire), -1 = any time
+  int32_t pre_dep;
+  // DEPI_LOGITS: per-ticket (max, first index) of the logits, for the argmax
+  float* part_val; int32_t* part_idx;
+  int32_t lpr;               // lanes that share one row's dot product (16, 32 or 64)
+  int32_t rpg;               // rows per lane group in one pass over a tile (1, 2, 4 or 8)
+  int32_t per_ticket;        // tiles per ticket (the ticket of tile t is t / per_ticket)
+  // input = the attention partials [H][attn_split][dh + 2] combined (nullable; xin unused then)
+  const float* attn_part; int32_t attn_split;
 };
 
 struct DecAttnArgs {
   const float* q;            // [d]
   const void* kv;            // this layer's cache [2][H][cap][dh]
-  float* o;                  // [d]
-  int32_t H, dh, cap, kv_dt;
+  float* part;               // [H][split][dh + 2]: unnormalised output, running max, sum of weights
+  int32_t H, dh, cap, kv_dt, split;
 };
 
 struct DecArgmaxArgs {
-  const float* logits;
+  const float* part_val; const int32_t* part_idx;   // per-ticket maxima of the LM-head GEMV
+  int32_t n_part;
   int32_t* ctx_tok;
   DecState* st;
   const DecIO* io;

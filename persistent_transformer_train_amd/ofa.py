@@ -21,7 +21,8 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 OFA_OK, OFA_E_ARG, OFA_E_HIP, OFA_E_NONFINITE, OFA_E_TIMEOUT, OFA_E_OVERFLOW, OFA_E_STATE = 0, -1, -2, -3, -4, -5, -6
-OFA_DEBUG_SHUFFLE_TICKETS, OFA_DEBUG_SHORT_WATCHDOG = 1, 2
+OFA_DEBUG_SHUFFLE_TICKETS, OFA_DEBUG_SHORT_WATCHDOG, OFA_DEBUG_TRACE = 1, 2, 4
+OFA_TRACE_INSTANCES = 1024
 
 
 class ofa_config(C.Structure):
@@ -70,6 +71,10 @@ _sig = {
     "ofa_status_sync": (C.c_int, [_H, C.POINTER(ofa_stats)]),
     "ofa_phase_times": (C.c_int, [_H, C.POINTER(C.c_uint64), C.c_int32, C.POINTER(C.c_int32), C.c_char_p,
                                   C.c_size_t]),
+    "ofa_decode_phase_times": (C.c_int, [_H, C.POINTER(C.c_uint64), C.c_int32, C.POINTER(C.c_int32), C.c_char_p,
+                                         C.c_size_t]),
+    "ofa_trace": (C.c_int, [_H, C.c_int32, C.POINTER(C.c_uint64), C.c_int64, C.POINTER(C.c_int64),
+                            C.POINTER(C.c_int32)]),
     "ofa_task_budget": (C.c_int, [C.c_uint64, C.c_uint64, C.POINTER(C.c_uint64)]),
     "ofa_last_error": (C.c_char_p, [_H]),
     "ofa_status_string": (C.c_char_p, [C.c_int]),
@@ -188,17 +193,30 @@ class Handle:
         self._check(rc)
         return st
 
-    def phase_times(self):
+    def phase_times(self, decode: bool = False):
         n = 512
         t = (C.c_uint64 * (2 * n))()
         names = C.create_string_buffer(32 * n)
         n_out = C.c_int32()
-        self._check(ofa_phase_times(self.h, t, n, C.byref(n_out), names, 32))
+        fn = ofa_decode_phase_times if decode else ofa_phase_times
+        self._check(fn(self.h, t, n, C.byref(n_out), names, 32))
         out = []
         for i in range(n_out.value):
             nm = names.raw[32 * i:32 * (i + 1)].split(b"\0", 1)[0].decode()
             out.append((nm, t[2 * i], t[2 * i + 1]))
         return out
+
+    def trace(self, decode: bool = False):
+        """(n_inst, n_phases, 4) device ticks of the last traced persistent call:
+        first start, last start, last task end and last publication of every
+        phase of every instance."""
+        import numpy as np
+        n = OFA_TRACE_INSTANCES * 512
+        buf = (C.c_uint64 * (4 * n))()
+        n_out, n_ph = C.c_int64(), C.c_int32()
+        self._check(ofa_trace(self.h, 1 if decode else 0, buf, 2 * n, C.byref(n_out), C.byref(n_ph)))
+        a = np.frombuffer(buf, dtype=np.uint64, count=4 * n_out.value).copy()
+        return a.reshape(-1, n_ph.value, 4)
 
     def close(self):
         if self.h:

@@ -51,10 +51,14 @@ def check_against_oracle(cfg, params_flat, prompt, toks, logits, dtype, logit_to
     return checked
 
 
+MODES = pytest.mark.parametrize("exec_mode", [1, 0], ids=["per_phase", "persistent"])
+
+
+@MODES
 @pytest.mark.parametrize("window", [64, 24])
-def test_c1_fp32_decode(window):
+def test_c1_fp32_decode(window, exec_mode):
     n_new = 60
-    h, cfg, init, prompt, toks, logits, vers = run_decode("c1", n_new, decode_window=window)
+    h, cfg, init, prompt, toks, logits, vers = run_decode("c1", n_new, exec_mode, decode_window=window)
     assert np.all(vers == 1)
     checked = check_against_oracle(cfg, init, prompt, toks, logits, np.float64, 1e-4)
     assert checked >= n_new // 2
@@ -62,9 +66,10 @@ def test_c1_fp32_decode(window):
     h.close()
 
 
-def test_c1_decode_continue_matches_single_call():
+@MODES
+def test_c1_decode_continue_matches_single_call(exec_mode):
     from persistent_transformer_train_amd import ofa
-    cfg = cfg_of("c1", exec_mode=1, decode_window=24)
+    cfg = cfg_of("c1", exec_mode=exec_mode, decode_window=24)
     h = ofa.Handle(cfg, init_of("c1", cfg))
     prompt = torch.from_numpy(stream_of("c1", cfg).prompt(cfg["prompt_len"])).cuda()
     a = torch.zeros(40, dtype=torch.int32, device="cuda")
@@ -78,11 +83,12 @@ def test_c1_decode_continue_matches_single_call():
     h.close()
 
 
+@MODES
 @pytest.mark.parametrize("name", ["m2", "m3"])
-def test_bf16_mini_decode(name):
+def test_bf16_mini_decode(name, exec_mode):
     # bf16 weights and KV cache: the oracle uses the same bf16-rounded weights
     n_new = 100
-    h, cfg, init, prompt, toks, logits, vers = run_decode(name, n_new)
+    h, cfg, init, prompt, toks, logits, vers = run_decode(name, n_new, exec_mode)
     w_bf16 = torch.tensor(init).to(torch.bfloat16).to(torch.float32).numpy()
     checked = check_against_oracle(cfg, w_bf16, prompt, toks, logits, np.float64, 5e-2)
     assert checked >= n_new // 4
