@@ -26,10 +26,18 @@ __device__ void task_dec_embed(const DecEmbedArgs& a, int tile, const TaskCtx& t
   const int pos = tc.sc->pos;
   if (threadIdx.x == 0) {
     DecState* st = a.st;
+    if (tc.sc->head & 4) {    // restart: the saved prompt becomes the context again
+      const int n = st->prompt_len;
+      for (int i = 0; i < n; ++i) a.ctx_tok[i] = a.prompt[i];
+      st->ctx_len = n;
+    }
     if (tc.sc->head & 2) {    // first position of a token: acquire the newest weights
       uint64_t ver = ld_acquire(a.published);
-      st->version = ver;
       st->w_delta = a.slot_bytes ? (int64_t)(ver & 1) * a.slot_bytes : 0;
+      // release: every read of the previous version's slot (earlier phases,
+      // acquired through the dependency counters) happens before a trainer
+      // that acquires this value overwrites that slot
+      st_release(&st->version, ver);
     }
     int tok = a.ctx_tok[pos];
     if (tok < 0 || tok >= a.V) {
@@ -626,8 +634,11 @@ __device__ void task_dec_argmax(const DecArgmaxArgs& a, int tile, const TaskCtx&
     }
     DecState* st = a.st;
     const int gi = tc.sc->gen_idx;
-    a.io->tokens_out[gi] = y;
-    if (a.io->versions_out) a.io->versions_out[gi] = st->version;
+    const int64_t g = tc.gen_base + gi;   // tokens emitted before this one
+    const int64_t slot = g % a.io->ring_len;
+    a.io->tokens_out[slot] = y;
+    if (a.io->versions_out) a.io->versions_out[slot] = st->version;
+    if (a.io->n_generated) st_release(a.io->n_generated, (uint64_t)(g + 1));
     int L = st->ctx_len;
     if (L + 1 > a.cap) {
       // context full: keep the most recent `keep` tokens (the new one included) at 0..keep-1
@@ -641,6 +652,33 @@ __device__ void task_dec_argmax(const DecArgmaxArgs& a, int tile, const TaskCtx&
     st->n_gen = gi + 1;
   }
   __syncthreads();
+}
+
+// ---------------------------------------------------------------- co-resident training
+
+// The training step about to write serve slot (tag & 1) waits until the
+// decoder has moved to version tag - 1 or later: the slot then holds no
+// version the decoder still reads (version v lives in slot v & 1).  Waits only
+// while co-resident decode runs; gives up on an error elsewhere or after ~10 s.
+__device__ void task_slot_guard(const GuardArgs& a, const TaskCtx& tc) {
+  if (threadIdx.x != 0) return;
+  if (!__hip_atomic_load(&a.st->serving, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+  const uint64_t need = tc.sc->tag - 1;
+  const uint64_t start = now_ticks();
+  for (int spins = 0; ld_acquire(&a.st->version) < need; ++spins) {
+    if (__hip_atomic_load(&tc.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+    __builtin_amdgcn_s_sleep(2);
+    if ((spins & 63) == 63 && now_ticks() - start > 1000000000ull) {
+      raise_status(tc.status, -4 /*OFA_E_TIMEOUT*/, tc.phase, tc.step, (int64_t)need);
+      return;
+    }
+  }
+}
+
+// The step's weights (written to slot tag & 1 by AdamW, complete: this phase
+// depends on it) become version tag.
+__device__ void task_publish(const PublishArgs& a, const TaskCtx& tc) {
+  if (threadIdx.x == 0) st_release(a.published, tc.sc->tag);
 }
 
 }  // namespace ofa

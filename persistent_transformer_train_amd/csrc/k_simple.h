@@ -676,6 +676,8 @@ __device__ void task_adamw(const AdamArgs& a, int tile, const TaskCtx& tc) {
   const int64_t i1 = min(i0 + (int64_t)a.per_tile, a.n);
   const float decay = 1.0f - lr * a.wd;
   const int64_t n4 = (i1 - i0) / 4;
+  // co-resident mode: the serve slot of this step's version
+  void* pub = a.pub ? (void*)((char*)a.pub + (int64_t)(tc.sc->tag & 1) * a.pub_slot_bytes) : nullptr;
   float4* P = (float4*)(a.p + i0);
   float4* M = (float4*)(a.m + i0);
   float4* Vv = (float4*)(a.v + i0);
@@ -690,14 +692,16 @@ __device__ void task_adamw(const AdamArgs& a, int tile, const TaskCtx& tc) {
     P[j] = p;
     M[j] = m;
     Vv[j] = v;
-    if (a.wc) {
+    if (a.wc || pub) {
       const int64_t e = i0 + 4 * j;
       if (a.wc_dt == DT_BF16) {
         const uint32_t w0 = (uint32_t)f2bf(p.x) | ((uint32_t)f2bf(p.y) << 16);
         const uint32_t w1 = (uint32_t)f2bf(p.z) | ((uint32_t)f2bf(p.w) << 16);
-        *(uint2*)((uint16_t*)a.wc + e) = make_uint2(w0, w1);
+        if (a.wc) *(uint2*)((uint16_t*)a.wc + e) = make_uint2(w0, w1);
+        if (pub) *(uint2*)((uint16_t*)pub + e) = make_uint2(w0, w1);
       } else {
-        *(float4*)((float*)a.wc + e) = p;
+        if (a.wc) *(float4*)((float*)a.wc + e) = p;
+        if (pub) *(float4*)((float*)pub + e) = p;
       }
     }
   }
@@ -708,6 +712,7 @@ __device__ void task_adamw(const AdamArgs& a, int tile, const TaskCtx& tc) {
     a.m[i] = m;
     a.v[i] = v;
     if (a.wc) stf(a.wc, i, a.wc_dt, p);
+    if (pub) stf(pub, i, a.wc_dt, p);
   }
 }
 

@@ -228,6 +228,7 @@ struct TaskCtx {
   DevStatus* status;
   int32_t phase;
   int64_t step;
+  int64_t gen_base;   // decode: index of the first token of this instance's schedule period
 };
 
 }  // namespace ofa

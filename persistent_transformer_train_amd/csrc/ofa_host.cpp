@@ -155,7 +155,7 @@ struct Carve {
   size_t p, g, m, v, wc, serve, xres, ln_mean, ln_rstd, h, qkv, o, lse, mlp1, mlp2, logits, dz, loss_rows;
   size_t dxres, dxlp, dln, dmlp, dout, dsum, dqkv, ln_part, cs_fc, cs_qkv, esorted, efirst;
   size_t sched, status, times, inst_end, steps, published, trace;
-  size_t kv, ctx_tok, dstate, dx, dq, dapart, dmlp_v, dlogits, dsteps, dtimes, misc, dsched, dpart_v, dpart_i;
+  size_t kv, ctx_tok, dstate, dx, dq, dapart, dmlp_v, dlogits, dsteps, dtimes, misc, dsched, dpart_v, dpart_i, dprompt;
   size_t total;
   int n_slots;
   int ln_tiles, cs_tiles;
@@ -247,6 +247,7 @@ Carve carve(const ofa_config& c, const Layout& lay) {
   w.dlogits = b.take(D.V * f4);
   w.dsteps = b.take((size_t)kMaxDecInst * sizeof(StepCtx));
   w.dsched = b.take(sizeof(Sched));
+  w.dprompt = b.take(D.win * 4);
   w.dpart_v = b.take(D.V * f4);
   w.dpart_i = b.take(D.V * 4);
   w.misc = b.take(kMiscBytes);
@@ -756,6 +757,13 @@ void build_train(ofa_handle* h) {
     a.v_tiles = v_tiles;
   }
   const int adam_chunk = 16384;
+  // co-resident mode: before AdamW overwrites serve slot (tag & 1) the decoder
+  // must have left the version that slot holds; after it, the step is published
+  const bool coresident = w.n_slots > 1;
+  if (coresident) {
+    int p_guard = b.add(OP_SLOT_GUARD, 1, "slot_guard", {-2});
+    b[p_guard].a.guard.st = at<DecState>(ws, w.dstate);
+  }
   int p_adam = b.add(OP_ADAMW, cdiv(D.P, adam_chunk), "adamw", {-2});
   {
     AdamArgs& a = b[p_adam].a.adam;
@@ -771,6 +779,14 @@ void build_train(ofa_handle* h) {
     a.beta2 = c.beta2;
     a.eps = c.eps;
     a.wd = c.weight_decay;
+    if (coresident) {
+      a.pub = ws + w.serve;
+      a.pub_slot_bytes = D.P * D.lp;
+    }
+  }
+  if (coresident) {
+    int p_pub = b.add(OP_PUBLISH, 1, "publish", {p_adam});
+    b[p_pub].a.publish.published = at<uint64_t>(ws, w.published);
   }
   // the next step's forward overwrites activations this step's backward reads
   b[p_emb].dep_prev = p_adam;
@@ -846,6 +862,7 @@ void build_decode(ofa_handle* h) {
     a.wte = sw(h->lay.wte);
     a.wpe = sw(h->lay.wpe);
     a.ctx_tok = at<int32_t>(ws, w.ctx_tok);
+    a.prompt = at<int32_t>(ws, w.dprompt);
     a.x = XV(0);
     a.st = st;
     a.published = at<uint64_t>(ws, w.published);
@@ -991,48 +1008,103 @@ ofa_status run_launch_per_phase(ofa_handle* h, const std::vector<Phase>& prog, c
   return OFA_OK;
 }
 
-// One persistent launch of n_inst instances of a program on `cus` CUs, with
-// the scheduler block at sched_off (reset here: ticket and counters start at
-// the debug base).
-ofa_status run_persistent(ofa_handle* h, const std::vector<Phase>& prog, const Phase* d_prog, const StepCtx* d_ctx,
-                          int64_t n_inst, size_t sched_off, PhaseTime* times, uint64_t* inst_end, int cus) {
-  const ofa_config& c = h->cfg;
-  const int np = (int)prog.size();
+// Decode schedule (host mirror of the device's context rule): the positions
+// processed before each of n_new emitted tokens, appended to h_dsteps from
+// index *n_inst on; the first position of each token acquires the newest
+// weights, the last one emits.  Advances the handle's context mirror.
+bool dec_schedule(ofa_handle* h, int n_new, int head_extra_first, int64_t* n_inst) {
+  const Dims& D = h->D;
+  for (int i = 0; i < n_new; ++i) {
+    for (int64_t p = h->dec_processed; p < h->dec_ctx_len; ++p) {
+      if (*n_inst >= kMaxDecInst - 64) return false;
+      StepCtx& sc = h->h_dsteps[(*n_inst)++];
+      memset(&sc, 0, sizeof sc);
+      sc.pos = (int)p;
+      sc.head = (p == h->dec_ctx_len - 1 ? 1 : 0) | (p == h->dec_processed ? 2 : 0);
+      if (i == 0 && p == h->dec_processed) sc.head |= head_extra_first;
+      sc.gen_idx = i;
+    }
+    h->dec_processed = h->dec_ctx_len;
+    if (h->dec_ctx_len + 1 > D.win) {
+      h->dec_ctx_len = D.keep;
+      h->dec_processed = 0;
+    } else {
+      h->dec_ctx_len += 1;
+    }
+  }
+  return true;
+}
+
+// Scheduler block reset for one launch: ticket and counters start at the
+// debug base, stop/limit cleared.
+ofa_status reset_sched(ofa_handle* h, size_t sched_off, int n_phases) {
   Sched* sc = at<Sched>(h->ws, sched_off);
-  const uint64_t base = c.debug_counter_base;
+  const uint64_t base = h->cfg.debug_counter_base;
   HIP_TRY(h, launch_fill_u64(&sc->ticket, base, 1, h->stream));
   HIP_TRY(h, launch_fill_u64(&sc->base, base, 1, h->stream));
-  HIP_TRY(h, launch_fill_u64(&sc->abort, 0, 2, h->stream));
-  HIP_TRY(h, launch_fill_u64(sc->done, base, np, h->stream));
-  if (inst_end) HIP_TRY(h, launch_fill_u64(inst_end, 0, n_inst, h->stream));
+  HIP_TRY(h, launch_fill_u64(&sc->abort, 0, 3, h->stream));   // abort, exited, stop
+  HIP_TRY(h, launch_fill_u64(&sc->limit, ~0ull, 1, h->stream));
+  HIP_TRY(h, launch_fill_u64(sc->done, base, n_phases, h->stream));
+  return OFA_OK;
+}
+
+PersistJob make_job(ofa_handle* h, const std::vector<Phase>& prog, const Phase* d_prog, const StepCtx* d_ctx,
+                    int64_t n_inst, size_t sched_off, PhaseTime* times, uint64_t* inst_end, int n_wg) {
+  PersistJob j;
+  memset(&j, 0, sizeof j);
+  j.phases = d_prog;
+  j.n_phases = (int)prog.size();
+  j.tickets_per_inst = prog.back().ticket_base + prog.back().n_tickets;
+  j.n_inst = n_inst;
+  j.steps = d_ctx;
+  j.period = n_inst;
+  j.sched = at<Sched>(h->ws, sched_off);
+  j.times = times;
+  j.inst_end = inst_end;
+  j.n_wg = n_wg;
+  return j;
+}
+
+// One persistent launch of one or two jobs.
+ofa_status launch_jobs(ofa_handle* h, PersistJob* jobs, int n_jobs) {
+  const ofa_config& c = h->cfg;
   PersistParams pp;
   memset(&pp, 0, sizeof pp);
-  pp.phases = d_prog;
-  pp.n_phases = np;
-  pp.tickets_per_inst = prog.back().ticket_base + prog.back().n_tickets;
-  pp.n_inst = n_inst;
-  pp.steps = d_ctx;
-  pp.sched = sc;
+  int grid = 0;
+  h->trace_n_phases = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    pp.job[i] = jobs[i];
+    grid += jobs[i].n_wg;
+  }
+  pp.n_jobs = n_jobs;
   pp.status = at<DevStatus>(h->ws, h->cw.status);
-  pp.times = times;
-  pp.inst_end = inst_end;
+  pp.abort = &pp.job[0].sched->abort;
   pp.watchdog_ticks = (c.debug_flags & OFA_DEBUG_SHORT_WATCHDOG) ? 100000ull : 1000000000ull;
   pp.shuffle = (c.debug_flags & OFA_DEBUG_SHUFFLE_TICKETS) ? 1 : 0;
-  h->trace_n_phases = 0;
-  h->trace_dec = sched_off == h->cw.dsched;
-  if (c.debug_flags & OFA_DEBUG_TRACE) {
-    pp.trace = at<uint64_t>(h->ws, h->cw.trace);
-    pp.trace_inst = std::min<int64_t>(n_inst, OFA_TRACE_INSTANCES);
-    HIP_TRY(h, launch_fill_u64(pp.trace, 0, pp.trace_inst * np * 4, h->stream));
-    h->trace_n_phases = np;
-    h->trace_n_inst = pp.trace_inst;
+  if (n_jobs == 1 && (c.debug_flags & OFA_DEBUG_TRACE)) {
+    PersistJob& j = pp.job[0];
+    j.trace = at<uint64_t>(h->ws, h->cw.trace);
+    j.trace_inst = std::min<int64_t>(j.n_inst, OFA_TRACE_INSTANCES);
+    HIP_TRY(h, launch_fill_u64(j.trace, 0, j.trace_inst * j.n_phases * 4, h->stream));
+    h->trace_n_phases = j.n_phases;
+    h->trace_n_inst = j.trace_inst;
+    h->trace_dec = j.phases == h->d_dec;
   }
-  const int occ = persistent_occupancy();
-  if (occ < 1) return fail(h, OFA_E_HIP, "persistent kernel does not fit a CU");
-  const int grid = cus * occ;
   h->last_grid = grid;
   HIP_TRY(h, launch_persistent(pp, grid, h->stream));
   return OFA_OK;
+}
+
+// One persistent launch of n_inst instances of a program on `cus` CUs.
+ofa_status run_persistent(ofa_handle* h, const std::vector<Phase>& prog, const Phase* d_prog, const StepCtx* d_ctx,
+                          int64_t n_inst, size_t sched_off, PhaseTime* times, uint64_t* inst_end, int cus) {
+  const int occ = persistent_occupancy();
+  if (occ < 1) return fail(h, OFA_E_HIP, "persistent kernel does not fit a CU");
+  ofa_status s = reset_sched(h, sched_off, (int)prog.size());
+  if (s != OFA_OK) return s;
+  if (inst_end) HIP_TRY(h, launch_fill_u64(inst_end, 0, n_inst, h->stream));
+  PersistJob j = make_job(h, prog, d_prog, d_ctx, n_inst, sched_off, times, inst_end, cus * occ);
+  return launch_jobs(h, &j, 1);
 }
 
 }  // namespace
@@ -1262,6 +1334,10 @@ ofa_status ofa_publish_weights(ofa_handle* h, uint64_t* version_out) {
   if (!h) return OFA_E_ARG;
   ofa_status s = check_sticky(h);
   if (s != OFA_OK) return s;
+  if (h->cw.n_slots > 1) {   // co-resident configuration: every training step has published already
+    if (version_out) *version_out = h->version;
+    return OFA_OK;
+  }
   h->version += 1;
   s = publish(h);
   if (s != OFA_OK) return s;
@@ -1312,6 +1388,7 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
   HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
   h->timed = true;
   h->steps_done += n_steps;
+  if (h->cw.n_slots > 1) h->version = h->steps_done;   // co-resident configuration: each step published
   return OFA_OK;
 }
 
@@ -1335,32 +1412,15 @@ ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_
     h->dec_processed = 0;
     h->dec_started = true;
   }
-  // schedule: positions to process before every emitted token (mirror of the device rule)
   s = staging_ready(h);
   if (s != OFA_OK) return s;
   int64_t n_inst = 0;
-  for (int i = 0; i < n_new; ++i) {
-    for (int64_t p = h->dec_processed; p < h->dec_ctx_len; ++p) {
-      if (n_inst >= kMaxDecInst - 64) return fail(h, OFA_E_ARG, "decode call too long");
-      StepCtx& sc = h->h_dsteps[n_inst++];
-      memset(&sc, 0, sizeof sc);
-      sc.pos = (int)p;
-      sc.head = (p == h->dec_ctx_len - 1 ? 1 : 0) | (p == h->dec_processed ? 2 : 0);
-      sc.gen_idx = i;
-    }
-    h->dec_processed = h->dec_ctx_len;
-    if (h->dec_ctx_len + 1 > D.win) {
-      h->dec_ctx_len = D.keep;
-      h->dec_processed = 0;
-    } else {
-      h->dec_ctx_len += 1;
-    }
-  }
+  if (!dec_schedule(h, n_new, 0, &n_inst)) return fail(h, OFA_E_ARG, "decode call too long");
   StepCtx* d_dsteps = at<StepCtx>(ws, h->cw.dsteps);
   s = upload(h, d_dsteps, h->h_dsteps, sizeof(StepCtx) * n_inst);
   if (s != OFA_OK) return s;
   // outputs of this call
-  DecIO io{dev_tokens_out, dev_versions_out, dev_logits_out};
+  DecIO io{dev_tokens_out, dev_versions_out, dev_logits_out, nullptr, (int64_t)n_new};
   memcpy(h->h_misc + kMiscDecIO, &io, sizeof io);
   s = upload(h, h->ws + h->cw.misc + kMiscDecIO, h->h_misc + kMiscDecIO, sizeof io);
   if (s != OFA_OK) return s;
@@ -1380,9 +1440,93 @@ ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_
   return OFA_OK;
 }
 
-ofa_status ofa_train_and_serve(ofa_handle* h, const int32_t*, int32_t, float*, const int32_t*, int32_t, int32_t*,
-                               uint64_t*, int32_t, uint64_t*) {
-  return fail(h, OFA_E_STATE, "co-resident mode is not available in this build");
+ofa_status ofa_train_and_serve(ofa_handle* h, const int32_t* dev_tokens, int32_t n_steps, float* dev_losses,
+                               const int32_t* dev_prompt, int32_t n_prompt, int32_t* dev_tokens_out,
+                               uint64_t* dev_versions_out, int32_t ring_len, uint64_t* dev_n_generated) {
+  if (!h || !dev_tokens || !dev_losses || n_steps < 1 || !dev_prompt || !dev_tokens_out || ring_len < 1)
+    return fail(h, OFA_E_ARG, "bad arguments");
+  const ofa_config& c = h->cfg;
+  if (c.train_cus <= 0 || c.serve_cus <= 0) return fail(h, OFA_E_STATE, "configuration has no CU partition");
+  if (c.exec_mode != OFA_EXEC_PERSISTENT) return fail(h, OFA_E_STATE, "co-resident mode needs the persistent executor");
+  if (n_steps > kMaxSteps) return fail(h, OFA_E_ARG, "n_steps %d > %d", n_steps, kMaxSteps);
+  const Dims& D = h->D;
+  if (n_prompt < 1 || n_prompt > D.win) return fail(h, OFA_E_ARG, "prompt length %d invalid", n_prompt);
+  ofa_status s = check_sticky(h);
+  if (s != OFA_OK) return s;
+  s = staging_ready(h);
+  if (s != OFA_OK) return s;
+  char* ws = h->ws;
+  const Carve& w = h->cw;
+  // training schedule
+  const int64_t per = D.B * (D.T + 1);
+  for (int i = 0; i < n_steps; ++i) {
+    StepCtx& sc = h->h_steps[i];
+    memset(&sc, 0, sizeof sc);
+    const uint64_t t = h->steps_done + i + 1;
+    sc.tokens = dev_tokens + per * i;
+    sc.loss_out = dev_losses + i;
+    sc.lr = (float)lr_at(c, t - 1);
+    sc.bc1 = (float)(1.0 - std::pow((double)c.beta1, (double)t));
+    sc.bc2 = (float)(1.0 - std::pow((double)c.beta2, (double)t));
+    sc.step_in_call = i;
+    sc.tag = t;
+  }
+  // decode: one restart period = the prompt reloaded, then restart_every tokens
+  const int per_gen = c.restart_every > 0 ? c.restart_every : 512;
+  h->dec_ctx_len = n_prompt;
+  h->dec_processed = 0;
+  int64_t period = 0;
+  if (!dec_schedule(h, per_gen, 4, &period)) return fail(h, OFA_E_ARG, "restart period too long");
+  h->dec_started = false;   // the co-resident context is not continued by later decode calls
+  StepCtx* d_steps = at<StepCtx>(ws, w.steps);
+  StepCtx* d_dsteps = at<StepCtx>(ws, w.dsteps);
+  s = upload(h, d_steps, h->h_steps, sizeof(StepCtx) * n_steps);
+  if (s != OFA_OK) return s;
+  s = upload(h, d_dsteps, h->h_dsteps, sizeof(StepCtx) * period);
+  if (s != OFA_OK) return s;
+  DecIO io{dev_tokens_out, dev_versions_out, nullptr, dev_n_generated, (int64_t)ring_len};
+  memcpy(h->h_misc + kMiscDecIO, &io, sizeof io);
+  s = upload(h, ws + w.misc + kMiscDecIO, h->h_misc + kMiscDecIO, sizeof io);
+  if (s != OFA_OK) return s;
+  s = mark_upload(h);
+  if (s != OFA_OK) return s;
+  HIP_TRY(h, hipMemcpyAsync(ws + w.dprompt, dev_prompt, (size_t)n_prompt * 4, hipMemcpyDeviceToDevice, h->stream));
+  // decoder state: prompt length, serving on, version = the newest published
+  DecState* st = at<DecState>(ws, w.dstate);
+  HIP_TRY(h, launch_fill_u32((uint32_t*)&st->prompt_len, (uint32_t)n_prompt, 1, h->stream));
+  HIP_TRY(h, launch_fill_u32((uint32_t*)&st->serving, 1, 1, h->stream));
+  HIP_TRY(h, launch_fill_u64(&st->version, h->version, 1, h->stream));
+  if (dev_n_generated) HIP_TRY(h, launch_fill_u64(dev_n_generated, 0, 1, h->stream));
+  const int occ = persistent_occupancy();
+  if (occ < 1) return fail(h, OFA_E_HIP, "persistent kernel does not fit a CU");
+  PhaseTime* tm = at<PhaseTime>(ws, w.times);
+  PhaseTime* dtm = at<PhaseTime>(ws, w.dtimes);
+  HIP_TRY(h, launch_fill_pairs((uint64_t*)tm, ~0ull, 0ull, (int64_t)h->train.size(), h->stream));
+  HIP_TRY(h, launch_fill_pairs((uint64_t*)dtm, ~0ull, 0ull, (int64_t)h->dec.size(), h->stream));
+  s = reset_sched(h, w.sched, (int)h->train.size());
+  if (s != OFA_OK) return s;
+  s = reset_sched(h, w.dsched, (int)h->dec.size());
+  if (s != OFA_OK) return s;
+  PersistJob jobs[2];
+  // job 0: decode on the serve workgroups, open-ended, stopped by training's end
+  jobs[0] = make_job(h, h->dec, h->d_dec, d_dsteps, (int64_t)1 << 40, w.dsched, dtm, nullptr, c.serve_cus * occ);
+  jobs[0].period = period;
+  jobs[0].gen_per_period = per_gen;
+  jobs[0].open_ended = 1;
+  // job 1: the n_steps training steps on the train workgroups
+  jobs[1] = make_job(h, h->train, h->d_train, d_steps, n_steps, w.sched, tm, at<uint64_t>(ws, w.inst_end),
+                     c.train_cus * occ);
+  jobs[1].raise_stop = &at<Sched>(ws, w.dsched)->stop;
+  HIP_TRY(h, launch_fill_u64(jobs[1].inst_end, 0, n_steps, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
+  s = launch_jobs(h, jobs, 2);
+  if (s != OFA_OK) return s;
+  HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
+  HIP_TRY(h, launch_fill_u32((uint32_t*)&st->serving, 0, 1, h->stream));
+  h->timed = true;
+  h->steps_done += n_steps;
+  h->version = h->steps_done;   // every step published its weights
+  return OFA_OK;
 }
 
 ofa_status ofa_status_sync(ofa_handle* h, ofa_stats* out) {

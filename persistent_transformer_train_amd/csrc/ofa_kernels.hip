@@ -72,6 +72,8 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   else if constexpr (OP == OP_DEC_GEMV) { OFA_ARGS(dgemv); task_dec_gemv(a, tile, tc, smem); }
   else if constexpr (OP == OP_DEC_ATTN) { OFA_ARGS(dattn); task_dec_attn(a, tile, tc, smem); }
   else if constexpr (OP == OP_DEC_ARGMAX) { OFA_ARGS(dargmax); task_dec_argmax(a, tile, tc, smem); }
+  else if constexpr (OP == OP_SLOT_GUARD) { OFA_ARGS(guard); task_slot_guard(a, tc); }
+  else if constexpr (OP == OP_PUBLISH) { OFA_ARGS(publish); task_publish(a, tc); }
 }
 #undef OFA_ARGS
 
@@ -83,7 +85,8 @@ __device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& t
     OFA_CASE(OP_LN_BWD) OFA_CASE(OP_COLSUM) OFA_CASE(OP_COLRED) OFA_CASE(OP_ATTN_PREP)
     OFA_CASE(OP_ATTN_BWD_KV) OFA_CASE(OP_ATTN_BWD_Q) OFA_CASE(OP_ROPE_BWD) OFA_CASE(OP_EMB_SORT)
     OFA_CASE(OP_EMB_BWD) OFA_CASE(OP_ADAMW) OFA_CASE(OP_COPY) OFA_CASE(OP_DEC_EMBED)
-    OFA_CASE(OP_DEC_GEMV) OFA_CASE(OP_DEC_ATTN) OFA_CASE(OP_DEC_ARGMAX)
+    OFA_CASE(OP_DEC_GEMV) OFA_CASE(OP_DEC_ATTN) OFA_CASE(OP_DEC_ARGMAX) OFA_CASE(OP_SLOT_GUARD)
+    OFA_CASE(OP_PUBLISH)
 #undef OFA_CASE
     default: break;
   }
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void phase_kernel(const Phase* phases, in
                                                          DevStatus* status, PhaseTime* times, int64_t step) {
   extern __shared__ __align__(16) char smem[];
   const Phase& ph = phases[idx];
-  TaskCtx tc{sc, status, idx, step};
+  TaskCtx tc{sc, status, idx, step, 0};
   const uint64_t t0 = now_ticks();
   if constexpr (OP == OP_DEC_GEMV) {
     // one workgroup per ticket, as the persistent executor hands them out
@@ -142,18 +145,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Phase* phases, int
 
 // Polls a completion counter with relaxed loads (the caller issues one
 // acquire fence once every wait has succeeded).  Gives up when the scheduler
-// aborts or when the watchdog deadline passes.
+// aborts, when the watchdog deadline passes (an error) or, in an open-ended
+// job, when the instance lies past the job's stopping point (not an error).
 __device__ __forceinline__ bool wait_count(const uint64_t* ctr, uint64_t need, const PersistParams& p,
-                                           const TaskCtx& tc) {
+                                           const PersistJob& J, const TaskCtx& tc) {
   if (ld_relaxed(ctr) >= need) return true;
   const uint64_t start = now_ticks();
   for (int spins = 0;; ++spins) {
     if (ld_relaxed(ctr) >= need) return true;
-    if (ld_relaxed(&p.sched->abort)) return false;
+    if (ld_relaxed(p.abort)) return false;
+    if (J.open_ended && ld_relaxed(&J.sched->limit) <= (uint64_t)tc.step) return false;
     __builtin_amdgcn_s_sleep(1);
     if ((spins & 63) == 63 && now_ticks() - start > p.watchdog_ticks) {
       raise_status(p.status, -4 /*OFA_E_TIMEOUT*/, tc.phase, tc.step, (int64_t)need);
-      st_release(&p.sched->abort, 1);
+      st_release(p.abort, 1);
       return false;
     }
   }
@@ -164,30 +169,37 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
   __shared__ uint64_t s_ticket;
   __shared__ int s_ok;
   __shared__ int s_pre;
+  __shared__ int s_stop;              // this workgroup saw the stop word of its open-ended job
   __shared__ int64_t s_all_checked;   // instance whose every phase this workgroup saw complete
-  const uint64_t base = p.sched->base;
-  const uint64_t total = (uint64_t)p.n_inst * (uint64_t)p.tickets_per_inst;
-  if (threadIdx.x == 0) s_all_checked = -1;
+  const int ji = (p.n_jobs > 1 && (int)blockIdx.x >= p.job[0].n_wg) ? 1 : 0;
+  const PersistJob& J = p.job[ji];
+  const uint64_t base = J.sched->base;
+  const uint64_t total = (uint64_t)J.n_inst * (uint64_t)J.tickets_per_inst;
+  if (threadIdx.x == 0) {
+    s_all_checked = -1;
+    s_stop = 0;
+  }
   for (;;) {
-    if (threadIdx.x == 0) s_ticket = add_relaxed(&p.sched->ticket, 1) - base;
+    if (threadIdx.x == 0) s_ticket = add_relaxed(&J.sched->ticket, 1) - base;
     __syncthreads();
     // wave-uniform copy, so the phase table is read with scalar loads
     const uint64_t t = readfirstlane_u64(s_ticket);
     if (t >= total) break;
-    const int64_t inst = (int64_t)(t / (uint64_t)p.tickets_per_inst);
-    const int r = (int)(t % (uint64_t)p.tickets_per_inst);
+    const int64_t inst = (int64_t)(t / (uint64_t)J.tickets_per_inst);
+    const int r = (int)(t % (uint64_t)J.tickets_per_inst);
     // phase owning ticket r: last phase whose ticket_base <= r
-    int lo = 0, hi = p.n_phases - 1;
+    int lo = 0, hi = J.n_phases - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (p.phases[mid].ticket_base <= r) lo = mid; else hi = mid - 1;
+      if (J.phases[mid].ticket_base <= r) lo = mid; else hi = mid - 1;
     }
     const int pi = lo;
-    const Phase& ph = p.phases[pi];
+    const Phase& ph = J.phases[pi];
     const int j = r - ph.ticket_base;
     int tile0 = j * ph.per_ticket;
     const int tile1 = min(tile0 + ph.per_ticket, ph.n_tiles);
-    TaskCtx tc{p.steps + inst, p.status, pi, inst};
+    const int64_t period_idx = inst / J.period;
+    TaskCtx tc{J.steps + (inst - period_idx * J.period), p.status, pi, inst, period_idx * J.gen_per_period};
     // a decode GEMV starts streaming its weights before its dependencies are
     // met; with two weight slots only once this token's version is known
     int npre = 0;
@@ -196,8 +208,8 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
       bool allow = !(a.epi == DEPI_LOGITS && !(tc.sc->head & 1));
       if (allow && a.pre_dep >= 0) {
         if (threadIdx.x == 0) {
-          const bool seen = ld_relaxed(&p.sched->done[a.pre_dep]) >=
-                            base + (uint64_t)(inst + 1) * p.phases[a.pre_dep].n_tiles;
+          const bool seen = ld_relaxed(&J.sched->done[a.pre_dep]) >=
+                            base + (uint64_t)(inst + 1) * J.phases[a.pre_dep].n_tiles;
           if (seen) fence_acquire_agent();
           s_pre = seen ? 1 : 0;
         }
@@ -205,6 +217,17 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
         allow = __builtin_amdgcn_readfirstlane(s_pre) != 0;
       }
       npre = prefetch_dec_gemv(ph, tile0, tile1, smem, allow);
+    }
+    // An open-ended job stops at an instance boundary once the other job has
+    // finished: the workgroup holding an instance's first ticket checks the
+    // stop word (in the second wave, beside thread 0's dependency wait); if it
+    // is raised the instance becomes the limit (a minimum over such holders) and
+    // is not started.  Every instance below the final limit runs whole: the
+    // limit only decreases and its holders saw no stop.  Tickets of instances at
+    // or past it find their dependencies unmet and leave their wait on the limit.
+    if (J.open_ended && r == 0 && threadIdx.x == kWave && ld_relaxed(&J.sched->stop)) {
+      atomicMin((unsigned long long*)&J.sched->limit, (unsigned long long)inst);
+      s_stop = 1;
     }
     // wait for the dependencies (thread 0), then one acquire for the workgroup
     if (threadIdx.x == 0) {
@@ -214,28 +237,29 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
         if (q == -2) {
           if (s_all_checked != inst) {
             for (int qq = 0; qq < pi && ok; ++qq)
-              ok = wait_count(&p.sched->done[qq], base + (uint64_t)(inst + 1) * p.phases[qq].n_tiles, p, tc);
+              ok = wait_count(&J.sched->done[qq], base + (uint64_t)(inst + 1) * J.phases[qq].n_tiles, p, J, tc);
             if (ok) s_all_checked = inst;
           }
         } else if (q >= 0) {
-          ok = wait_count(&p.sched->done[q], base + (uint64_t)(inst + 1) * p.phases[q].n_tiles, p, tc);
+          ok = wait_count(&J.sched->done[q], base + (uint64_t)(inst + 1) * J.phases[q].n_tiles, p, J, tc);
         }
       }
       if (ok && ph.dep_prev >= 0 && inst > 0)
-        ok = wait_count(&p.sched->done[ph.dep_prev], base + (uint64_t)inst * p.phases[ph.dep_prev].n_tiles, p, tc);
+        ok = wait_count(&J.sched->done[ph.dep_prev], base + (uint64_t)inst * J.phases[ph.dep_prev].n_tiles, p, J,
+                        tc);
       if (ok) fence_acquire_agent();
       s_ok = ok ? 1 : 0;
     }
     __syncthreads();
-    if (!__builtin_amdgcn_readfirstlane(s_ok)) {
+    if (!__builtin_amdgcn_readfirstlane(s_ok) || __builtin_amdgcn_readfirstlane(s_stop)) {
       if (npre) vm_wait_barrier(0);   // no copy may land in LDS after the exit
       break;
     }
     const uint64_t t0 = now_ticks();
-    if (p.trace && inst < p.trace_inst && threadIdx.x == 0) {
+    if (J.trace && inst < J.trace_inst && threadIdx.x == 0) {
       // word 0 keeps the complement of the earliest start, so every word starts at 0 and takes a maximum
-      atomicMax((unsigned long long*)&p.trace[4 * (inst * p.n_phases + pi)], ~(unsigned long long)t0);
-      atomicMax((unsigned long long*)&p.trace[4 * (inst * p.n_phases + pi) + 1], (unsigned long long)t0);
+      atomicMax((unsigned long long*)&J.trace[4 * (inst * J.n_phases + pi)], ~(unsigned long long)t0);
+      atomicMax((unsigned long long*)&J.trace[4 * (inst * J.n_phases + pi) + 1], (unsigned long long)t0);
     }
     if (ph.op == OP_DEC_GEMV) run_dec_gemv(ph, tile0, tile1, tc, smem, npre);
     else for (int tile = tile0; tile < tile1; ++tile) {
@@ -251,20 +275,23 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
     // release fence then makes them visible before the counter moves
     __syncthreads();
     if (threadIdx.x == 0) {
-      if (p.trace && inst < p.trace_inst)
-        atomicMax((unsigned long long*)&p.trace[4 * (inst * p.n_phases + pi) + 2], (unsigned long long)now_ticks());
+      if (J.trace && inst < J.trace_inst)
+        atomicMax((unsigned long long*)&J.trace[4 * (inst * J.n_phases + pi) + 2], (unsigned long long)now_ticks());
       fence_release_agent();
-      add_relaxed(&p.sched->done[pi], (uint64_t)(tile1 - tile0));
-      if (p.times) {
-        atomicMin((unsigned long long*)&p.times[pi].t0, (unsigned long long)t0);
-        atomicMax((unsigned long long*)&p.times[pi].t1, (unsigned long long)now_ticks());
+      add_relaxed(&J.sched->done[pi], (uint64_t)(tile1 - tile0));
+      if (J.times) {
+        atomicMin((unsigned long long*)&J.times[pi].t0, (unsigned long long)t0);
+        atomicMax((unsigned long long*)&J.times[pi].t1, (unsigned long long)now_ticks());
       }
-      if (p.inst_end) atomicMax((unsigned long long*)&p.inst_end[inst], (unsigned long long)now_ticks());
-      if (p.trace && inst < p.trace_inst)
-        atomicMax((unsigned long long*)&p.trace[4 * (inst * p.n_phases + pi) + 3], (unsigned long long)now_ticks());
+      if (J.inst_end) atomicMax((unsigned long long*)&J.inst_end[inst], (unsigned long long)now_ticks());
+      if (J.trace && inst < J.trace_inst)
+        atomicMax((unsigned long long*)&J.trace[4 * (inst * J.n_phases + pi) + 3], (unsigned long long)now_ticks());
     }
   }
-  if (threadIdx.x == 0) add_relaxed(&p.sched->exited, 1);
+  if (threadIdx.x == 0) {
+    // the last workgroup of a job to leave raises the other job's stop word
+    if (add_relaxed(&J.sched->exited, 1) + 1 == (uint64_t)J.n_wg && J.raise_stop) st_release(J.raise_stop, 1);
+  }
 }
 
 // ---------------------------------------------------------------- small utility kernels
@@ -383,7 +410,8 @@ hipError_t launch_phase(const Phase& h, const Phase* d_phases, int idx, const St
     OFA_LAUNCH(OP_LN_BWD) OFA_LAUNCH(OP_COLSUM) OFA_LAUNCH(OP_COLRED) OFA_LAUNCH(OP_ATTN_PREP)
     OFA_LAUNCH(OP_ATTN_BWD_KV) OFA_LAUNCH(OP_ATTN_BWD_Q) OFA_LAUNCH(OP_ROPE_BWD) OFA_LAUNCH(OP_EMB_SORT)
     OFA_LAUNCH(OP_EMB_BWD) OFA_LAUNCH(OP_ADAMW) OFA_LAUNCH(OP_COPY) OFA_LAUNCH(OP_DEC_EMBED)
-    OFA_LAUNCH(OP_DEC_GEMV) OFA_LAUNCH(OP_DEC_ATTN) OFA_LAUNCH(OP_DEC_ARGMAX)
+    OFA_LAUNCH(OP_DEC_GEMV) OFA_LAUNCH(OP_DEC_ATTN) OFA_LAUNCH(OP_DEC_ARGMAX) OFA_LAUNCH(OP_SLOT_GUARD)
+    OFA_LAUNCH(OP_PUBLISH)
 #undef OFA_LAUNCH
     default: return hipErrorInvalidValue;
   }

@@ -6,21 +6,35 @@
 
 namespace ofa {
 
-// Everything the persistent kernel reads; passed by value.
-struct PersistParams {
+// One job of the persistent kernel: a program run instance after instance by
+// its own workgroups, with its own scheduler block.
+struct PersistJob {
   const Phase* phases;       // one program instance's phase table
   int32_t n_phases;
   int32_t tickets_per_inst;  // sum of n_tickets over the phases
-  int64_t n_inst;            // instances (training steps) to run
-  const StepCtx* steps;      // [n_inst]
+  int64_t n_inst;            // instances to run (open-ended jobs: a bound no run reaches)
+  const StepCtx* steps;      // instance i runs steps[i % period]
+  int64_t period;
+  int64_t gen_per_period;    // decode: tokens emitted per period
   Sched* sched;
-  DevStatus* status;
   PhaseTime* times;          // [n_phases] (nullable)
   uint64_t* inst_end;        // [n_inst] device time each instance finished (nullable)
+  uint64_t* trace;           // debug: [trace_inst][n_phases][4] (nullable)
+  int64_t trace_inst;
+  int32_t n_wg;              // workgroups that run this job
+  int32_t open_ended;        // stops at sched->limit once sched->stop is raised
+  uint64_t* raise_stop;      // when this job's last workgroup leaves, this word is raised (nullable)
+};
+
+// Everything the persistent kernel reads; passed by value.  With two jobs,
+// workgroups [0, job[0].n_wg) run job 0 and the rest job 1.
+struct PersistParams {
+  PersistJob job[2];
+  int32_t n_jobs;
+  DevStatus* status;
+  uint64_t* abort;           // shared stop word: any error stops every job
   uint64_t watchdog_ticks;   // a wait longer than this raises OFA_E_TIMEOUT
   int32_t shuffle;           // debug: permute tiles inside a phase
-  uint64_t* trace;           // debug: [trace_inst][n_phases] (first start, last end) pairs (nullable)
-  int64_t trace_inst;
 };
 
 hipError_t init_kernels();

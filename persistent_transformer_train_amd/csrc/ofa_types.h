@@ -41,6 +41,8 @@ enum Op : int32_t {
   OP_DEC_GEMV,     // decode: y = W x (+ epilogue)
   OP_DEC_ATTN,     // decode: one head's attention over the context
   OP_DEC_ARGMAX,   // decode: argmax over the logits, emit the token
+  OP_SLOT_GUARD,   // co-resident training: wait until decode no longer reads the slot AdamW writes
+  OP_PUBLISH,      // co-resident training: release the step's weights as a new version
   OP_COUNT
 };
 
@@ -165,6 +167,17 @@ struct AdamArgs {
   void* wc;             // compute copy (nullable): bf16 or f32
   int64_t n; int32_t per_tile, wc_dt;
   float beta1, beta2, eps, wd;
+  // co-resident mode: the updated weights also go to serve slot (step tag & 1)
+  void* pub; int64_t pub_slot_bytes;
+};
+
+struct DecState;
+struct GuardArgs {            // wait until the decoder reads version >= tag - 1
+  const DecState* st;
+};
+
+struct PublishArgs {          // published = tag (release)
+  uint64_t* published;
 };
 
 struct CopyArgs {
@@ -178,11 +191,12 @@ struct CopyArgs {
 // version the current token acquired.
 
 struct DecState {
-  uint64_t version;          // weight version read by the current token
+  uint64_t version;          // weight version read by the current token (release-stored)
   int64_t w_delta;           // byte offset from slot 0 to the slot being read
   int32_t ctx_len;           // tokens in the context list
   int32_t n_gen;             // tokens emitted in this call
-  int32_t pad[2];
+  int32_t prompt_len;        // co-resident decode: tokens of the saved prompt a restart reloads
+  int32_t serving;           // co-resident decode running (training then guards the slot it writes)
 };
 
 enum DecEpi : int32_t {
@@ -195,14 +209,17 @@ enum DecEpi : int32_t {
 };
 
 struct DecIO {               // per-call output pointers of a decode call
-  int32_t* tokens_out;       // [n_new]
-  uint64_t* versions_out;    // [n_new] (nullable)
-  float* logits_out;         // [n_new][V] (nullable)
+  int32_t* tokens_out;       // [ring_len]: token g goes to g % ring_len
+  uint64_t* versions_out;    // [ring_len] (nullable)
+  float* logits_out;         // [n_new][V] (nullable; step mode only)
+  uint64_t* n_generated;     // tokens emitted so far (nullable)
+  int64_t ring_len;
 };
 
 struct DecEmbedArgs {
   const void* wte; const void* wpe;   // slot-0 pointers (wpe nullable)
-  const int32_t* ctx_tok;
+  int32_t* ctx_tok;
+  const int32_t* prompt;              // saved prompt a restart reloads (co-resident decode)
   float* x;
   DecState* st;
   const uint64_t* published;          // published version (co-resident: slot = version & 1)
@@ -257,6 +274,7 @@ union PhaseArgs {
   EmbedArgs emb; AttnArgs attn; RopeArgs rope; GegluArgs geglu; CeArgs ce;
   LossArgs loss; EmbSortArgs esort; EmbBwdArgs ebwd; AdamArgs adam; CopyArgs copy;
   DecEmbedArgs dembed; DecGemvArgs dgemv; DecAttnArgs dattn; DecArgmaxArgs dargmax;
+  GuardArgs guard; PublishArgs publish;
 };
 
 constexpr int kMaxDeps = 4;
@@ -284,18 +302,23 @@ struct StepCtx {
   int32_t step_in_call;
   uint64_t tag;            // strictly increasing per step across calls
   int32_t pos;             // decode: position this instance processes
-  int32_t head;            // decode: 1 = compute logits and emit a token afterwards
+  int32_t head;            // decode: bit 0 = compute logits and emit a token afterwards,
+                           // bit 1 = first position of a token (acquire the newest weights),
+                           // bit 2 = restart: reload the saved prompt as the context
   int32_t gen_idx;         // decode: index of the emitted token in the call
   int32_t pad;
 };
 
 constexpr int kMaxPhases = 512;
 
-struct Sched {                       // persistent-kernel scheduler block (device)
+struct Sched {                       // persistent-kernel scheduler block of one job (device)
   uint64_t ticket;                   // next ticket to hand out
   uint64_t base;                     // debug counter base (added to every counter)
-  uint64_t abort;                    // non-zero: every role stops
+  uint64_t abort;                    // non-zero: every role stops (the first job's word is shared)
   uint64_t exited;                   // workgroups that left the loop
+  uint64_t stop;                     // open-ended job: raised when the other job has finished
+  uint64_t limit;                    // open-ended job: instances >= limit are not run (~0 = none yet)
+  uint64_t pad[2];
   uint64_t done[kMaxPhases];         // completed tiles per phase, summed over instances
 };
 

@@ -171,6 +171,19 @@ class Handle:
                                      tokens_out.data_ptr(), 0 if logits_out is None else logits_out.data_ptr(),
                                      0 if versions_out is None else versions_out.data_ptr()))
 
+    def train_and_serve(self, tokens, losses, prompt, tokens_ring, versions_ring=None, n_generated=None):
+        """Co-resident mode: train on tokens [n][B][T+1] on the train CUs while the
+        serve CUs decode continuously from prompt (restarting every restart_every
+        tokens); generated tokens go round-robin into tokens_ring, their weight
+        versions into versions_ring, the count into n_generated (uint64 [1])."""
+        assert tokens.dtype == self.torch.int32 and tokens.is_cuda and tokens.is_contiguous()
+        assert losses.dtype == self.torch.float32 and losses.numel() >= tokens.shape[0]
+        assert prompt.dtype == self.torch.int32 and tokens_ring.dtype == self.torch.int32
+        self._check(ofa_train_and_serve(self.h, tokens.data_ptr(), tokens.shape[0], losses.data_ptr(),
+                                        prompt.data_ptr(), prompt.numel(), tokens_ring.data_ptr(),
+                                        0 if versions_ring is None else versions_ring.data_ptr(),
+                                        tokens_ring.numel(), 0 if n_generated is None else n_generated.data_ptr()))
+
     def get_params(self):
         out = self.torch.empty(self.n_params, dtype=self.torch.float32, device=self.device)
         self._check(ofa_get_params(self.h, out.data_ptr()))
