@@ -106,6 +106,40 @@ def bench_decode(init, stream, args) -> dict:
                          "unit": "GB/s", "frac": round(bpt * rate / PEAK_HBM, 4), "bytes_per_token": bpt}}
 
 
+def bench_coresident(init, stream, args) -> dict:
+    """c5: the training step on 208 CUs and batch-1 decode on 48 CUs in one
+    persistent launch; decode restarts from the seeded prompt every 512 tokens
+    and reads the weights each AdamW step publishes.  Both rates over the call."""
+    import torch
+    from persistent_transformer_train_amd import configs, ofa
+    cfg = configs.get("c5")
+    h = ofa.Handle(cfg, init)
+    BT = cfg["batch"] * cfg["seq"]
+    n = args.co_steps
+    toks = torch.from_numpy(stream.batches(0, n)).cuda()
+    losses = torch.zeros(n, dtype=torch.float32, device="cuda")
+    prompt = torch.from_numpy(stream.prompt(cfg["prompt_len"])).cuda()
+    ring = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    vers = torch.zeros(1 << 16, dtype=torch.int64, device="cuda")
+    n_gen = torch.zeros(1, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    h.train_and_serve(toks, losses, prompt, ring, vers, n_gen)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = h.sync()
+    g = int(n_gen.item())
+    v = vers[:min(g, ring.numel())].cpu().numpy()
+    ls = losses.cpu().numpy()
+    h.close()
+    return {"metric": "co-resident train tokens/s and decode tokens/s in one persistent launch",
+            "train_value": round(n * BT / dt, 1), "decode_value": round(g / dt, 1), "unit": "tokens/s",
+            "steps": n, "tokens_generated": g, "seconds": round(dt, 4), "kernel_ms": round(st.last_call_ms, 3),
+            "train_cus": cfg["train_cus"], "serve_cus": cfg["serve_cus"], "restart_every": cfg["restart_every"],
+            "versions_read": [int(v.min()), int(v.max()), int(len(np.unique(v)))] if g else None,
+            "losses": [float(ls[0]), float(ls[-1])]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +149,7 @@ def main():
     ap.add_argument("--decode-tokens", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--co-steps", type=int, default=40, help="co-resident (c5) training steps; 0 = skip")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -180,6 +215,8 @@ def main():
     h.close()
     if not args.no_decode and args.decode_tokens > 1:
         out["decode"] = bench_decode(init, stream, args)
+    if args.co_steps > 0 and args.exec_mode == "persistent":
+        out["coresident"] = bench_coresident(init, stream, args)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
