@@ -41,42 +41,89 @@ __device__ void task_embed(const EmbedArgs& a, int tile, const TaskCtx& tc) {
 }
 
 // ---------------------------------------------------------------- LayerNorm
+// Rows of d floats read as float4 (d is a multiple of 8 and at most 1024, so
+// a lane holds at most four float4 of a row).  Each wave takes two rows at a
+// time so that both rows' loads are in flight together.
 
-constexpr int kMaxDPerLane = 16;   // d <= 1024
+constexpr int kMaxD4 = 4;   // float4 per lane: d <= 1024
+
+__device__ __forceinline__ float4 f4_zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+
+__device__ __forceinline__ void st_row4(void* y, int64_t e, int dt, float4 v) {
+  if (dt == DT_BF16) {
+    const uint32_t w0 = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+    const uint32_t w1 = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    *(uint2*)((uint16_t*)y + e) = make_uint2(w0, w1);
+  } else {
+    *(float4*)((float*)y + e) = v;
+  }
+}
 
 __device__ void task_ln_fwd(const LnFwdArgs& a, int tile) {
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int r0 = tile * a.rows_per_tile;
   const int r1 = min(r0 + a.rows_per_tile, a.rows);
-  const int nj = (a.d + kWave - 1) / kWave;
-  for (int r = r0 + w; r < r1; r += kWaves) {
-    const float* x = a.x + (int64_t)r * a.d;
-    float v[kMaxDPerLane];
-    float s = 0.f;
+  const int n4 = a.d / 4;
+  const float4* __restrict__ x4 = (const float4*)a.x;
+  const float4* __restrict__ g4 = (const float4*)a.g;
+  const float4* __restrict__ b4 = (const float4*)a.b;
+  float4 gv[kMaxD4], bv[kMaxD4];
 #pragma unroll
-    for (int c = 0; c < kMaxDPerLane; ++c) {
-      int j = l + c * kWave;
-      v[c] = (c < nj && j < a.d) ? x[j] : 0.f;
-      s += v[c];
-    }
-    float mean = wave_sum(s) / a.d;
-    float q = 0.f;
+  for (int c = 0; c < kMaxD4; ++c) {
+    const int j = l + c * kWave;
+    gv[c] = j < n4 ? g4[j] : f4_zero();
+    bv[c] = j < n4 ? b4[j] : f4_zero();
+  }
+  for (int r = r0 + w; r < r1; r += 2 * kWaves) {
+    float4 v[2][kMaxD4];
+    float mean[2], rstd[2];
 #pragma unroll
-    for (int c = 0; c < kMaxDPerLane; ++c) {
-      int j = l + c * kWave;
-      float dv = (c < nj && j < a.d) ? v[c] - mean : 0.f;
-      q += dv * dv;
-    }
-    float var = wave_sum(q) / a.d;
-    float rstd = 1.0f / sqrtf(var + 1e-5f);
+    for (int q = 0; q < 2; ++q) {
+      const int rr = r + q * kWaves;
 #pragma unroll
-    for (int c = 0; c < kMaxDPerLane; ++c) {
-      int j = l + c * kWave;
-      if (c < nj && j < a.d) stf(a.y, (int64_t)r * a.d + j, a.y_dt, (v[c] - mean) * rstd * a.g[j] + a.b[j]);
+      for (int c = 0; c < kMaxD4; ++c) {
+        const int j = l + c * kWave;
+        v[q][c] = (rr < r1 && j < n4) ? x4[(int64_t)rr * n4 + j] : f4_zero();
+      }
     }
-    if (l == 0) {
-      a.mean[r] = mean;
-      a.rstd[r] = rstd;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < kMaxD4; ++c) s += (v[q][c].x + v[q][c].y) + (v[q][c].z + v[q][c].w);
+      mean[q] = wave_sum(s) / a.d;
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < kMaxD4; ++c) {
+        if (l + c * kWave < n4) {
+          const float dx = v[q][c].x - mean[q], dy = v[q][c].y - mean[q];
+          const float dz = v[q][c].z - mean[q], dw = v[q][c].w - mean[q];
+          ss += (dx * dx + dy * dy) + (dz * dz + dw * dw);
+        }
+      }
+      rstd[q] = 1.0f / sqrtf(wave_sum(ss) / a.d + 1e-5f);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int rr = r + q * kWaves;
+      if (rr >= r1) break;
+#pragma unroll
+      for (int c = 0; c < kMaxD4; ++c) {
+        const int j = l + c * kWave;
+        if (j < n4) {
+          const float m = mean[q], rs = rstd[q];
+          float4 o;
+          o.x = (v[q][c].x - m) * rs * gv[c].x + bv[c].x;
+          o.y = (v[q][c].y - m) * rs * gv[c].y + bv[c].y;
+          o.z = (v[q][c].z - m) * rs * gv[c].z + bv[c].z;
+          o.w = (v[q][c].w - m) * rs * gv[c].w + bv[c].w;
+          st_row4(a.y, (int64_t)rr * a.d + 4 * j, a.y_dt, o);
+        }
+      }
+      if (l == 0) {
+        a.mean[rr] = mean[q];
+        a.rstd[rr] = rstd[q];
+      }
     }
   }
 }
@@ -87,58 +134,102 @@ __device__ void task_ln_bwd(const LnBwdArgs& a, int tile, char* smem) {
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int r0 = tile * a.rows_per_tile;
   const int r1 = min(r0 + a.rows_per_tile, a.rows);
-  const int nj = (a.d + kWave - 1) / kWave;
-  float pg[kMaxDPerLane], pb[kMaxDPerLane], px[kMaxDPerLane];
+  const int n4 = a.d / 4;
+  const float4* __restrict__ x4 = (const float4*)a.x;
+  const float4* __restrict__ dy4 = (const float4*)a.dy;
+  const float4* __restrict__ in4 = (const float4*)a.dx_in;
+  float4* __restrict__ out4 = (float4*)a.dx_out;
+  float4 gv[kMaxD4], pg[kMaxD4], pb[kMaxD4], px[kMaxD4];
 #pragma unroll
-  for (int c = 0; c < kMaxDPerLane; ++c) pg[c] = pb[c] = px[c] = 0.f;
-  for (int r = r0 + w; r < r1; r += kWaves) {
-    const float* x = a.x + (int64_t)r * a.d;
-    const float* dy = a.dy + (int64_t)r * a.d;
-    const float mean = a.mean[r], rstd = a.rstd[r];
-    float xh[kMaxDPerLane], gy[kMaxDPerLane], dyv[kMaxDPerLane];
-    float s1 = 0.f, s2 = 0.f;
+  for (int c = 0; c < kMaxD4; ++c) {
+    const int j = l + c * kWave;
+    gv[c] = j < n4 ? ((const float4*)a.g)[j] : f4_zero();
+    pg[c] = pb[c] = px[c] = f4_zero();
+  }
+  for (int r = r0 + w; r < r1; r += 2 * kWaves) {
+    float4 xh[2][kMaxD4], dyv[2][kMaxD4], din[2][kMaxD4];
+    float rs[2], m1[2], m2[2];
 #pragma unroll
-    for (int c = 0; c < kMaxDPerLane; ++c) {
-      int j = l + c * kWave;
-      bool ok = c < nj && j < a.d;
-      xh[c] = ok ? (x[j] - mean) * rstd : 0.f;
-      dyv[c] = ok ? dy[j] : 0.f;
-      gy[c] = ok ? dyv[c] * a.g[j] : 0.f;
-      s1 += gy[c];
-      s2 += gy[c] * xh[c];
+    for (int q = 0; q < 2; ++q) {
+      const int rr = r + q * kWaves;
+      const bool okr = rr < r1;
+#pragma unroll
+      for (int c = 0; c < kMaxD4; ++c) {
+        const int j = l + c * kWave;
+        const bool ok = okr && j < n4;
+        const int64_t e = (int64_t)rr * n4 + j;
+        xh[q][c] = ok ? x4[e] : f4_zero();
+        dyv[q][c] = ok ? dy4[e] : f4_zero();
+        din[q][c] = (ok && in4) ? in4[e] : f4_zero();
+      }
     }
-    const float m1 = wave_sum(s1) / a.d, m2 = wave_sum(s2) / a.d;
 #pragma unroll
-    for (int c = 0; c < kMaxDPerLane; ++c) {
-      int j = l + c * kWave;
-      if (c < nj && j < a.d) {
-        float dx = rstd * (gy[c] - m1 - xh[c] * m2);
-        int64_t idx = (int64_t)r * a.d + j;
-        float out = (a.dx_in ? a.dx_in[idx] : 0.f) + dx;
-        a.dx_out[idx] = out;
-        if (a.dx_lp) stf(a.dx_lp, idx, a.lp_dt, out);
-        pg[c] += dyv[c] * xh[c];
-        pb[c] += dyv[c];
-        px[c] += out;
+    for (int q = 0; q < 2; ++q) {
+      const int rr = r + q * kWaves;
+      const float mean = rr < r1 ? a.mean[rr] : 0.f;
+      rs[q] = rr < r1 ? a.rstd[rr] : 0.f;
+      float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < kMaxD4; ++c) {
+        if (l + c * kWave < n4) {
+          float4& h = xh[q][c];
+          h.x = (h.x - mean) * rs[q];
+          h.y = (h.y - mean) * rs[q];
+          h.z = (h.z - mean) * rs[q];
+          h.w = (h.w - mean) * rs[q];
+          const float4 gy = make_float4(dyv[q][c].x * gv[c].x, dyv[q][c].y * gv[c].y, dyv[q][c].z * gv[c].z,
+                                        dyv[q][c].w * gv[c].w);
+          s1 += (gy.x + gy.y) + (gy.z + gy.w);
+          s2 += (gy.x * h.x + gy.y * h.y) + (gy.z * h.z + gy.w * h.w);
+        }
+      }
+      m1[q] = wave_sum(s1) / a.d;
+      m2[q] = wave_sum(s2) / a.d;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int rr = r + q * kWaves;
+      if (rr >= r1) break;
+#pragma unroll
+      for (int c = 0; c < kMaxD4; ++c) {
+        const int j = l + c * kWave;
+        if (j < n4) {
+          const float4 h = xh[q][c], dv = dyv[q][c], g = gv[c];
+          float4 o;
+          o.x = din[q][c].x + rs[q] * (dv.x * g.x - m1[q] - h.x * m2[q]);
+          o.y = din[q][c].y + rs[q] * (dv.y * g.y - m1[q] - h.y * m2[q]);
+          o.z = din[q][c].z + rs[q] * (dv.z * g.z - m1[q] - h.z * m2[q]);
+          o.w = din[q][c].w + rs[q] * (dv.w * g.w - m1[q] - h.w * m2[q]);
+          const int64_t e = (int64_t)rr * n4 + j;
+          out4[e] = o;
+          if (a.dx_lp) st_row4(a.dx_lp, 4 * e, a.lp_dt, o);
+          pg[c].x += dv.x * h.x; pg[c].y += dv.y * h.y; pg[c].z += dv.z * h.z; pg[c].w += dv.w * h.w;
+          pb[c].x += dv.x; pb[c].y += dv.y; pb[c].z += dv.z; pb[c].w += dv.w;
+          px[c].x += o.x; px[c].y += o.y; px[c].z += o.z; px[c].w += o.w;
+        }
       }
     }
   }
   // combine the four waves in a fixed order
-  float* red = (float*)smem;   // [kWaves][3][d]
+  float4* red = (float4*)smem;   // [kWaves][3][n4]
 #pragma unroll
-  for (int c = 0; c < kMaxDPerLane; ++c) {
-    int j = l + c * kWave;
-    if (c < nj && j < a.d) {
-      red[(w * 3 + 0) * a.d + j] = pg[c];
-      red[(w * 3 + 1) * a.d + j] = pb[c];
-      red[(w * 3 + 2) * a.d + j] = px[c];
+  for (int c = 0; c < kMaxD4; ++c) {
+    const int j = l + c * kWave;
+    if (j < n4) {
+      red[(w * 3 + 0) * n4 + j] = pg[c];
+      red[(w * 3 + 1) * n4 + j] = pb[c];
+      red[(w * 3 + 2) * n4 + j] = px[c];
     }
   }
   __syncthreads();
-  float* out = a.partials + (int64_t)tile * 3 * a.d;
-  for (int i = threadIdx.x; i < 3 * a.d; i += kThreads) {
-    float s = 0.f;
-    for (int ww = 0; ww < kWaves; ++ww) s += red[ww * 3 * a.d + i];
+  float4* out = (float4*)(a.partials + (int64_t)tile * 3 * a.d);
+  for (int i = threadIdx.x; i < 3 * n4; i += kThreads) {
+    float4 s = red[i];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) {
+      const float4 t = red[ww * 3 * n4 + i];
+      s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    }
     out[i] = s;
   }
   __syncthreads();
@@ -146,35 +237,113 @@ __device__ void task_ln_bwd(const LnBwdArgs& a, int tile, char* smem) {
 
 // ---------------------------------------------------------------- column sums
 
-// tile = (row chunk, block of 256 columns); partials[row chunk][col]
-__device__ void task_colsum(const ColsumArgs& a, int tile) {
-  const int ncb = (a.cols + kThreads - 1) / kThreads;
+// tile = (row chunk, block of 512 columns).  Thread (g, c8): rows g, g+4, ...
+// of the chunk at columns 8 c8 .. 8 c8 + 7, 16-byte loads, sixteen rows in
+// flight; the four row groups are added in group order through LDS.
+// partials[row chunk][col].  cols is a multiple of 8.
+constexpr int kCsCols = 512;   // columns per column-sum tile
+
+__device__ __forceinline__ void cs_load8(const ColsumArgs& a, int64_t e, float (&v)[8]) {
+  if (a.dt == DT_BF16) {
+    const uint4 p = *(const uint4*)((const uint16_t*)a.src + e);
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+  } else {
+    const float4 p0 = *(const float4*)((const float*)a.src + e);
+    const float4 p1 = *(const float4*)((const float*)a.src + e + 4);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+    v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+  }
+}
+
+__device__ void task_colsum(const ColsumArgs& a, int tile, char* smem) {
+  float* red = (float*)smem;   // [kWaves][kCsCols]
+  const int ncb = (a.cols + kCsCols - 1) / kCsCols;
   const int rc = tile / ncb, cb = tile % ncb;
   const int r0 = rc * a.rows_per_tile;
   const int r1 = min(r0 + a.rows_per_tile, a.rows);
-  const int c = cb * kThreads + threadIdx.x;
-  if (c >= a.cols) return;
-  float s = 0.f;
-  for (int r = r0; r < r1; ++r) s += ldf(a.src, (int64_t)r * a.ld + c, a.dt);
-  a.partials[(int64_t)rc * a.cols + c] = s;
+  const int g = threadIdx.x / 64, c8 = threadIdx.x % 64;
+  const int c = cb * kCsCols + 8 * c8;
+  float s[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s[q] = 0.f;
+  if (c < a.cols) {
+    constexpr int U = 16;
+    for (int rb = r0 + g; rb < r1; rb += 4 * U) {
+      float v[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = rb + 4 * u;
+        if (r < r1) cs_load8(a, (int64_t)r * a.ld + c, v[u]);
+        else
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[u][q] = 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s[q] += v[u][q];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) red[g * kCsCols + 8 * c8 + q] = s[q];
+  __syncthreads();
+  for (int i = threadIdx.x; i < kCsCols; i += kThreads) {
+    const int cc = cb * kCsCols + i;
+    if (cc < a.cols)
+      a.partials[(int64_t)rc * a.cols + cc] =
+          ((red[i] + red[kCsCols + i]) + red[2 * kCsCols + i]) + red[3 * kCsCols + i];
+  }
+  __syncthreads();
 }
 
-// tile = block of 64 columns; four groups of 64 threads each sum every fourth
-// partial in order, then the groups combine in a fixed order
+// tile = (vector k, block of 16 columns).  Sixteen groups of 16 threads: group
+// q sums partials q, q+16, q+32, ... of its column in that order (eight loads
+// in flight); the sixteen group sums are then added in group order.
+constexpr int kCrCols = 16;
+
 __device__ void task_colred(const ColredArgs& a, int tile, char* smem) {
-  float* red = (float*)smem;   // [4][64]
-  const int c = tile * 64 + (threadIdx.x & 63), grp = threadIdx.x >> 6;
-  for (int k = 0; k < a.n_vec; ++k) {
-    float* o = a.out[k];
-    if (!o) continue;   // uniform across the workgroup
-    float s = 0.f;
-    if (c < a.cols)
-      for (int p = grp; p < a.n_parts; p += 4) s += a.partials[((int64_t)p * a.n_vec + k) * a.cols + c];
-    red[threadIdx.x] = s;
-    __syncthreads();
-    if (grp == 0 && c < a.cols) o[c] = ((red[threadIdx.x] + red[64 + threadIdx.x]) + red[128 + threadIdx.x]) + red[192 + threadIdx.x];
-    __syncthreads();
+  float* red = (float*)smem;   // [16 groups][16 columns]
+  const int ncb = (a.cols + kCrCols - 1) / kCrCols;
+  const int k = tile / ncb, cb = tile % ncb;
+  // select among values already in registers: a dynamic index would move the
+  // argument copy to scratch memory
+  float* o0 = (float*)readfirstlane_u64((uint64_t)a.out[0]);
+  float* o1 = (float*)readfirstlane_u64((uint64_t)a.out[1]);
+  float* o2 = (float*)readfirstlane_u64((uint64_t)a.out[2]);
+  float* o = k == 0 ? o0 : (k == 1 ? o1 : o2);
+  if (!o) return;   // uniform across the workgroup
+  const int cl = threadIdx.x & (kCrCols - 1), grp = threadIdx.x / kCrCols;
+  const int c = cb * kCrCols + cl;
+  constexpr int G = kThreads / kCrCols, U = 8;
+  float s = 0.f;
+  if (c < a.cols) {
+    const float* __restrict__ p0 = a.partials + (int64_t)k * a.cols + c;
+    const int64_t stride = (int64_t)a.n_vec * a.cols;
+    for (int p = grp; p < a.n_parts; p += G * U) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pp = p + G * u;
+        v[u] = pp < a.n_parts ? p0[pp * stride] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) s += v[u];
+    }
   }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x < kCrCols && c < a.cols) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < G; ++q) t += red[q * kCrCols + cl];
+    o[c] = t;
+  }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------- plain GEMM
@@ -226,7 +395,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, int m, int n, f
   }
 }
 
-__device__ void task_gemm_simple(const GemmArgs& g, int tile, char* smem) {
+__device__ __forceinline__ void task_gemm_simple(const GemmArgs& g, int tile, char* smem) {
   GemmSmemSimple& s = *(GemmSmemSimple*)smem;
   const int tm = g.tile_order ? tile % g.tiles_m : tile / g.tiles_n;
   const int tn = g.tile_order ? tile / g.tiles_m : tile % g.tiles_n;
@@ -373,13 +542,51 @@ __device__ void task_attn_fwd_simple(const AttnArgs& a, int tile, char* smem) {
   }
 }
 
-// D[b,h,t] = sum_j dO[b,t,h,j] * O[b,t,h,j]; one wave per (row, head)
+// D[b,h,t] = sum_j dO[b,t,h,j] * O[b,t,h,j].  bf16 with 64-wide heads: eight
+// lanes per (row, head), one 16-byte load of each operand per lane, four
+// items per lane in flight; otherwise one wave per (row, head).
 __device__ void task_attn_prep(const AttnArgs& a, int tile) {
-  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int BT = a.B * a.T;
-  const int per_tile = a.block;   // rows per tile
-  const int r0 = tile * per_tile, r1 = min(r0 + per_tile, BT);
-  for (int item = w; item < (r1 - r0) * a.H; item += kWaves) {
+  const int r0 = tile * a.block, r1 = min(r0 + a.block, BT);
+  const int n_items = (r1 - r0) * a.H;
+  if (a.dt == DT_BF16 && a.dh == 64) {
+    const int sub = threadIdx.x & 7, slot = threadIdx.x >> 3;
+    constexpr int S = kThreads / 8, U = 4;
+    const uint16_t* __restrict__ dO = (const uint16_t*)a.dout;
+    const uint16_t* __restrict__ O = (const uint16_t*)a.o;
+    for (int i0 = 0; i0 < n_items; i0 += S * U) {
+      uint4 x[U], y[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int it = i0 + slot + S * u;
+        const int r = r0 + it / a.H, h = it % a.H;
+        const int64_t e = (int64_t)r * a.d + h * 64 + sub * 8;
+        x[u] = it < n_items ? *(const uint4*)(dO + e) : make_uint4(0, 0, 0, 0);
+        y[u] = it < n_items ? *(const uint4*)(O + e) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t xa[4] = {x[u].x, x[u].y, x[u].z, x[u].w}, ya[4] = {y[u].x, y[u].y, y[u].z, y[u].w};
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          s += __uint_as_float(xa[q] << 16) * __uint_as_float(ya[q] << 16) +
+               __uint_as_float(xa[q] & 0xffff0000u) * __uint_as_float(ya[q] & 0xffff0000u);
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        const int it = i0 + slot + S * u;
+        if (sub == 0 && it < n_items) {
+          const int r = r0 + it / a.H, h = it % a.H;
+          const int b = r / a.T, t = r % a.T;
+          a.dsum[((int64_t)b * a.H + h) * a.T + t] = s;
+        }
+      }
+    }
+    return;
+  }
+  const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  for (int item = w; item < n_items; item += kWaves) {
     int r = r0 + item / a.H, h = item % a.H;
     float s = 0.f;
     for (int j = l; j < a.dh; j += kWave) {
@@ -501,15 +708,81 @@ __device__ void task_attn_bwd_q_simple(const AttnArgs& a, int tile, char* smem) 
 
 // ---------------------------------------------------------------- cross-entropy
 // One row per tile.  loss_r = logsumexp(z) - z[y];  dz = (softmax(z) - onehot(y)) / rows.
+// V % 8 == 0 and rows are 16-byte aligned, so the row is read as float4.  A
+// row of up to 256 * NR float4 is read once into registers (all loads in
+// flight together) and reduced from there; longer rows take three passes.
 
-__device__ void task_ce(const CeArgs& a, int tile, const TaskCtx& tc, char* smem) {
-  float* red = (float*)smem;
-  const int r = tile;
-  const int b = r / a.T, t = r % a.T;
-  const int y = token_at(tc.sc, b, t + 1, a.T, a.V, tc);
-  const float* z = a.logits + (int64_t)r * a.V;
-  // V % 8 == 0 and rows are 16-byte aligned: float4 loads, two in flight per thread
-  const float4* z4 = (const float4*)z;
+__device__ __forceinline__ void ce_store(const CeArgs& a, int r, int i, int y, float lse, float4 v) {
+  float p[4] = {expf(v.x - lse), expf(v.y - lse), expf(v.z - lse), expf(v.w - lse)};
+  const int v0 = 4 * i;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = (p[e] - (v0 + e == y ? 1.f : 0.f)) * a.inv_rows;
+  const int64_t o = (int64_t)r * a.V + v0;
+  if (a.dt == DT_BF16) {
+    const uint32_t w0 = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
+    const uint32_t w1 = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
+    *(uint2*)((uint16_t*)a.dz + o) = make_uint2(w0, w1);
+  } else {
+    *(float4*)((float*)a.dz + o) = make_float4(p[0], p[1], p[2], p[3]);
+  }
+}
+
+// exp(x - m) as 2^(x log2(e) - m log2(e)) on the hardware base-2 exponential
+// (one transcendental instruction); ml2 = m * log2(e)
+__device__ __forceinline__ float exp_shift(float x, float ml2) {
+  return __builtin_amdgcn_exp2f(fmaf(x, 1.44269504088896341f, -ml2));
+}
+
+// The row stays in registers: softmax numerators overwrite the logits, so each
+// element takes one exponential.
+template <int NR>
+__device__ __forceinline__ void ce_row_regs(const CeArgs& a, int r, int y, float* red) {
+  const float4* __restrict__ z4 = (const float4*)(a.logits + (int64_t)r * a.V);
+  const int n4 = a.V / 4;
+  float4 v[NR];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    v[u] = i < n4 ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < NR; ++u) mx = fmaxf(mx, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+  mx = block_max(mx, red);
+  const float ml2 = mx * 1.44269504088896341f;
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    v[u].x = exp_shift(v[u].x, ml2);
+    v[u].y = exp_shift(v[u].y, ml2);
+    v[u].z = exp_shift(v[u].z, ml2);
+    v[u].w = exp_shift(v[u].w, ml2);
+    s += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+  }
+  s = block_sum(s, red + kWaves);
+  const float inv_s = 1.0f / s;
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    if (i >= n4) continue;
+    float p[4] = {v[u].x * inv_s, v[u].y * inv_s, v[u].z * inv_s, v[u].w * inv_s};
+    const int v0 = 4 * i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = (p[e] - (v0 + e == y ? 1.f : 0.f)) * a.inv_rows;
+    const int64_t o = (int64_t)r * a.V + v0;
+    if (a.dt == DT_BF16) {
+      const uint32_t w0 = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
+      const uint32_t w1 = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
+      *(uint2*)((uint16_t*)a.dz + o) = make_uint2(w0, w1);
+    } else {
+      *(float4*)((float*)a.dz + o) = make_float4(p[0], p[1], p[2], p[3]);
+    }
+  }
+  if (threadIdx.x == 0) a.loss_rows[r] = mx + logf(s) - a.logits[(int64_t)r * a.V + y];
+}
+
+__device__ __forceinline__ void ce_row_loop(const CeArgs& a, int r, int y, float* red) {
+  const float4* z4 = (const float4*)(a.logits + (int64_t)r * a.V);
   const int n4 = a.V / 4;
   float mx = -INFINITY;
   for (int i = threadIdx.x; i < n4; i += kThreads) {
@@ -524,22 +797,20 @@ __device__ void task_ce(const CeArgs& a, int tile, const TaskCtx& tc, char* smem
   }
   s = block_sum(s, red + kWaves);
   const float lse = mx + logf(s);
-  for (int i = threadIdx.x; i < n4; i += kThreads) {
-    const float4 v = z4[i];
-    float p[4] = {expf(v.x - lse), expf(v.y - lse), expf(v.z - lse), expf(v.w - lse)};
-    const int v0 = 4 * i;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = (p[e] - (v0 + e == y ? 1.f : 0.f)) * a.inv_rows;
-    const int64_t o = (int64_t)r * a.V + v0;
-    if (a.dt == DT_BF16) {
-      const uint32_t w0 = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
-      const uint32_t w1 = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
-      *(uint2*)((uint16_t*)a.dz + o) = make_uint2(w0, w1);
-    } else {
-      *(float4*)((float*)a.dz + o) = make_float4(p[0], p[1], p[2], p[3]);
-    }
-  }
-  if (threadIdx.x == 0) a.loss_rows[r] = lse - z[y];
+  for (int i = threadIdx.x; i < n4; i += kThreads) ce_store(a, r, i, y, lse, z4[i]);
+  if (threadIdx.x == 0) a.loss_rows[r] = lse - a.logits[(int64_t)r * a.V + y];
+}
+
+__device__ __forceinline__ void task_ce(const CeArgs& a, int tile, const TaskCtx& tc, char* smem) {
+  float* red = (float*)smem;
+  const int r = tile;
+  const int b = r / a.T, t = r % a.T;
+  const int y = token_at(tc.sc, b, t + 1, a.T, a.V, tc);
+  const int n4 = a.V / 4;
+  if (n4 <= 4 * kThreads) ce_row_regs<4>(a, r, y, red);
+  else if (n4 <= 16 * kThreads) ce_row_regs<16>(a, r, y, red);
+  else if (n4 <= 52 * kThreads) ce_row_regs<52>(a, r, y, red);
+  else ce_row_loop(a, r, y, red);
 }
 
 // mean of the per-row losses, fixed summation order; flags a non-finite loss
@@ -612,46 +883,103 @@ __device__ void task_emb_sort(const EmbSortArgs& a, const TaskCtx& tc, char* sme
   __syncthreads();
 }
 
-// rows of d wte: fixed-order sum over the token's positions (or zero); then rows of d wpe
+// rows of d wte: fixed-order sum over the token's positions (or zero); then rows of d wpe.
+// Each wave owns consecutive vocabulary rows; one lane per row loads the row's
+// run descriptor up front, rows are written as float4.
 __device__ void task_emb_bwd(const EmbBwdArgs& a, int tile, const TaskCtx& tc) {
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-  const int nj = (a.d + kWave - 1) / kWave;
+  const int n4 = a.d / 4;
   if (tile < a.v_tiles) {
     const int v0 = tile * a.rows_per_tile, v1 = min(v0 + a.rows_per_tile, a.V);
-    for (int v = v0 + w; v < v1; v += kWaves) {
-      float acc[kMaxDPerLane];
+    const int per_wave = (a.rows_per_tile + kWaves - 1) / kWaves;   // <= 64 (host)
+    const int vw = v0 + w * per_wave;
+    const uint32_t tag = (uint32_t)tc.sc->tag;
+    const uint64_t f_l = (l < per_wave && vw + l < v1) ? a.first[vw + l] : 0;
+    for (int i = 0; i < per_wave; ++i) {
+      const int v = vw + i;
+      if (v >= v1) break;
+      const uint64_t f = __shfl(f_l, i);
+      const bool present = (uint32_t)(f >> 32) == tag;
+      if (!present && a.accumulate) continue;
+      float4 acc[kMaxD4];
 #pragma unroll
-      for (int c = 0; c < kMaxDPerLane; ++c) acc[c] = 0.f;
-      const uint64_t f = a.first[v];
-      const bool present = (f >> 32) == (tc.sc->tag & 0xffffffffu);
+      for (int c = 0; c < kMaxD4; ++c) acc[c] = f4_zero();
       if (present) {
-        const int start = (int)((f >> 16) & 0xffff), cnt = (int)(f & 0xffff);
-        for (int k = start; k < start + cnt; ++k) {
-          const float* row = a.dx0 + (int64_t)a.sorted[k] * a.d;
+        // positions in increasing order, eight rows in flight: lane q < 8 fetches
+        // the position index of the batch's q-th row
+        const int start = (int)((f >> 16) & 0xffff), end = start + (int)(f & 0xffff);
+        constexpr int U = 8;
+        for (int k0 = start; k0 < end; k0 += U) {
+          const int pos_l = (l < U && k0 + l < end) ? a.sorted[k0 + l] : -1;
+          float4 x[U][kMaxD4];
 #pragma unroll
-          for (int c = 0; c < kMaxDPerLane; ++c) {
-            int j = l + c * kWave;
-            if (c < nj && j < a.d) acc[c] += row[j];
+          for (int q = 0; q < U; ++q) {
+            const int pos = __shfl(pos_l, q);
+            const float4* row = (const float4*)(a.dx0 + (int64_t)(pos < 0 ? 0 : pos) * a.d);
+#pragma unroll
+            for (int c = 0; c < kMaxD4; ++c) {
+              const int j = l + c * kWave;
+              x[q][c] = (pos >= 0 && j < n4) ? row[j] : f4_zero();
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < U; ++q) {
+            if (k0 + q >= end) break;
+#pragma unroll
+            for (int c = 0; c < kMaxD4; ++c) {
+              acc[c].x += x[q][c].x; acc[c].y += x[q][c].y; acc[c].z += x[q][c].z; acc[c].w += x[q][c].w;
+            }
           }
         }
       }
-      if (!present && a.accumulate) continue;
-      float* out = a.dwte + (int64_t)v * a.d;
+      float4* out = (float4*)(a.dwte + (int64_t)v * a.d);
 #pragma unroll
-      for (int c = 0; c < kMaxDPerLane; ++c) {
-        int j = l + c * kWave;
-        if (c < nj && j < a.d) out[j] = (a.accumulate ? out[j] : 0.f) + acc[c];
+      for (int c = 0; c < kMaxD4; ++c) {
+        const int j = l + c * kWave;
+        if (j < n4) {
+          float4 o = acc[c];
+          if (a.accumulate) {
+            const float4 p = out[j];
+            o = make_float4(p.x + o.x, p.y + o.y, p.z + o.z, p.w + o.w);
+          }
+          out[j] = o;
+        }
       }
     }
   } else {
-    const int t0 = (tile - a.v_tiles) * a.rows_per_tile, t1 = min(t0 + a.rows_per_tile, a.n_pos);
-    for (int t = t0 + w; t < t1; t += kWaves) {
-      for (int j = l; j < a.d; j += kWave) {
-        float s = 0.f;
-        if (t < a.T)
-          for (int b = 0; b < a.B; ++b) s += a.dx0[((int64_t)b * a.T + t) * a.d + j];
-        a.dwpe[(int64_t)t * a.d + j] = s;
+    // one position per wave: the sum over the batch in batch order, eight rows in flight
+    const int t = (tile - a.v_tiles) * kWaves + w;
+    if (t >= a.n_pos) return;
+    float4 acc[kMaxD4];
+#pragma unroll
+    for (int c = 0; c < kMaxD4; ++c) acc[c] = f4_zero();
+    constexpr int U = 8;
+    for (int b0 = 0; t < a.T && b0 < a.B; b0 += U) {
+      float4 x[U][kMaxD4];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int b = b0 + q;
+        const float4* row = (const float4*)(a.dx0 + ((int64_t)(b < a.B ? b : 0) * a.T + t) * a.d);
+#pragma unroll
+        for (int c = 0; c < kMaxD4; ++c) {
+          const int j = l + c * kWave;
+          x[q][c] = (b < a.B && j < n4) ? row[j] : f4_zero();
+        }
       }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        if (b0 + q >= a.B) break;
+#pragma unroll
+        for (int c = 0; c < kMaxD4; ++c) {
+          acc[c].x += x[q][c].x; acc[c].y += x[q][c].y; acc[c].z += x[q][c].z; acc[c].w += x[q][c].w;
+        }
+      }
+    }
+    float4* out = (float4*)(a.dwpe + (int64_t)t * a.d);
+#pragma unroll
+    for (int c = 0; c < kMaxD4; ++c) {
+      const int j = l + c * kWave;
+      if (j < n4) out[j] = acc[c];
     }
   }
 }

@@ -629,7 +629,7 @@ void build_train(ofa_handle* h) {
     return p;
   };
   auto ln_red = [&](int i, int dep, float* og, float* ob, float* ores, const char* nm) {
-    int p = b.add(OP_COLRED, cdiv(d, 64), nm, {dep});
+    int p = b.add(OP_COLRED, 3 * cdiv(d, 16), nm, {dep});
     ColredArgs& a = b[p].a.cr;
     a.partials = LNP(i);
     a.out[0] = og;
@@ -638,12 +638,12 @@ void build_train(ofa_handle* h) {
     a.n_parts = lnt;
     a.n_vec = 3;
     a.cols = (int)d;
-    a.cols_per_tile = 64;
+    a.cols_per_tile = 16;
     return p;
   };
   auto colsum = [&](const void* src, int64_t ld, int cols, float* part, float* out, int dep, int dep2,
                     const char* nm) {
-    int p = b.add(OP_COLSUM, w.cs_tiles * cdiv(cols, 256), nm, {dep, dep2});
+    int p = b.add(OP_COLSUM, w.cs_tiles * cdiv(cols, 512), nm, {dep, dep2});
     ColsumArgs& a = b[p].a.cs;
     a.src = src;
     a.ld = ld;
@@ -652,14 +652,14 @@ void build_train(ofa_handle* h) {
     a.cols = cols;
     a.rows_per_tile = kCsRows;
     a.dt = lp;
-    int q = b.add(OP_COLRED, cdiv(cols, 64), "bias_grad", {p});
+    int q = b.add(OP_COLRED, cdiv(cols, 16), "bias_grad", {p});
     ColredArgs& r = b[q].a.cr;
     r.partials = part;
     r.out[0] = out;
     r.n_parts = w.cs_tiles;
     r.n_vec = 1;
     r.cols = cols;
-    r.cols_per_tile = 64;
+    r.cols_per_tile = 16;
     return q;
   };
   int p_lnf_b = ln_bwd(2 * (int)L, h->lay.lnf_g, -1, {p_head_dx}, "lnf_bwd");
@@ -738,7 +738,7 @@ void build_train(ofa_handle* h) {
   }
   int v_rows = 64;
   int v_tiles = cdiv(V, v_rows);
-  int pos_tiles = c.n_pos ? cdiv(c.n_pos, v_rows) : 0;
+  int pos_tiles = c.n_pos ? cdiv(c.n_pos, kThreadsHost / 64) : 0;   // one position per wavefront
   int p_eb = b.add(OP_EMB_BWD, v_tiles + pos_tiles, "emb_bwd", {cur_dx, p_sort, p_head_dw});
   {
     EmbBwdArgs& a = b[p_eb].a.ebwd;

@@ -50,7 +50,7 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   else if constexpr (OP == OP_CE) { OFA_ARGS(ce); task_ce(a, tile, tc, smem); }
   else if constexpr (OP == OP_LOSS) { OFA_ARGS(loss); task_loss(a, tc, smem); }
   else if constexpr (OP == OP_LN_BWD) { OFA_ARGS(lnb); task_ln_bwd(a, tile, smem); }
-  else if constexpr (OP == OP_COLSUM) { OFA_ARGS(cs); task_colsum(a, tile); }
+  else if constexpr (OP == OP_COLSUM) { OFA_ARGS(cs); task_colsum(a, tile, smem); }
   else if constexpr (OP == OP_COLRED) { OFA_ARGS(cr); task_colred(a, tile, smem); }
   else if constexpr (OP == OP_ATTN_PREP) { OFA_ARGS(attn); task_attn_prep(a, tile); }
   else if constexpr (OP == OP_ATTN_BWD_KV) {
@@ -324,7 +324,8 @@ static size_t lds_for(const Phase& ph) {
     case OP_ATTN_BWD_Q:
       return ph.a.attn.impl == 1 ? attn_mfma_lds_bytes() : (size_t)kWaves * 192 * sizeof(float);
     case OP_CE: case OP_LOSS: return 64;
-    case OP_COLRED: return 4 * 64 * sizeof(float);
+    case OP_COLRED: return 16 * 16 * sizeof(float);
+    case OP_COLSUM: return (size_t)kWaves * kCsCols * sizeof(float);
     case OP_EMB_SORT: {
       int n = 1;
       while (n < ph.a.esort.BT) n <<= 1;
