@@ -227,7 +227,7 @@ __device__ __forceinline__ bf16x8_t p3_frag_t(const uint16_t* stage, int rbase, 
 }
 
 template <bool AKM, bool BKM>
-__device__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
+__device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
   GemmSmemP3& s = *(GemmSmemP3*)smem;
   // tile order: with tile_order = 1 the M index runs fastest, so tiles that run
   // at the same time share the B panel (used when B is the larger operand)
@@ -293,7 +293,7 @@ __device__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
   gemm_mfma_epilogue(g, acc, m0, n0, wm, wn, lane, (float*)smem, 128);
 }
 
-__device__ void task_gemm_p3(const GemmArgs& g, int tile, char* smem) {
+__device__ __forceinline__ void task_gemm_p3(const GemmArgs& g, int tile, char* smem) {
   if (g.a_kmajor) {
     if (g.b_kmajor) gemm_p3<true, true>(g, tile, smem); else gemm_p3<true, false>(g, tile, smem);
   } else {

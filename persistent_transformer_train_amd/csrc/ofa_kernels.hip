@@ -37,8 +37,9 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   if constexpr (OP == OP_EMBED) { OFA_ARGS(emb); task_embed(a, tile, tc); }
   else if constexpr (OP == OP_LN_FWD) { OFA_ARGS(lnf); task_ln_fwd(a, tile); }
   else if constexpr (OP == OP_GEMM) {
-    if (ph.a.gemm.impl == GEMM_P3) task_gemm_p3(ph.a.gemm, tile, smem);
-    else task_gemm_simple(ph.a.gemm, tile, smem);
+    OFA_ARGS(gemm);
+    if (a.impl == GEMM_P3) task_gemm_p3(a, tile, smem);
+    else task_gemm_simple(a, tile, smem);
   }
   else if constexpr (OP == OP_ROPE) { OFA_ARGS(rope); task_rope(a, tile, false); }
   else if constexpr (OP == OP_ATTN_FWD) {
@@ -131,9 +132,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Phase* phases, int
   extern __shared__ __align__(16) char smem[];
   const Phase& ph = phases[idx];
   const uint64_t t0 = now_ticks();
+  const GemmArgs g = ph.a.gemm;   // by value: see OFA_ARGS
   for (int tile = blockIdx.x; tile < ph.n_tiles; tile += gridDim.x) {
-    if constexpr (IMPL == GEMM_P3) task_gemm_p3(ph.a.gemm, tile, smem);
-    else task_gemm_simple(ph.a.gemm, tile, smem);
+    if constexpr (IMPL == GEMM_P3) task_gemm_p3(g, tile, smem);
+    else task_gemm_simple(g, tile, smem);
   }
   if (times && threadIdx.x == 0) {
     atomicMin((unsigned long long*)&times[idx].t0, (unsigned long long)t0);
