@@ -25,37 +25,74 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kMBM = 128, kMBN = 128;   // output tile
 
 // Epilogue through LDS: the waves park their accumulators in LDS (fp32,
-// [rows][128]), then all 256 threads walk the tile (thread -> column, rows in
-// steps of two), so each epilogue variant is one small loop with coalesced
-// stores and no per-element branching.  In bf16 mode every low-precision
-// operand of an epilogue (C, aux) is bf16.
+// [rows][128]), then all 256 threads walk the tile: thread -> four adjacent
+// columns (one 16-byte LDS read, one 8- or 16-byte global access per operand),
+// eight rows at a time.  Rows go in batches of kEpiRows per thread whose global
+// reads (residual, saved pre-activation) are issued before any store: the
+// output never aliases those inputs, and without the batching every read
+// would wait for the previous row's store.  N, ldc, ldaux, ldres and aux_off
+// are multiples of 8 (checked on the host), so every access is aligned.  In
+// bf16 mode every low-precision operand of an epilogue (C, aux) is bf16.
+constexpr int kEpiRows = 4;
+
+typedef float epi_f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t epi_u2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ epi_u2 pack_bf16x4(epi_f4 x) {
+  return epi_u2{(uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16), (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16)};
+}
+__device__ __forceinline__ epi_f4 unpack_bf16x4(epi_u2 p) {
+  return epi_f4{__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xffff0000u), __uint_as_float(p.y << 16),
+                __uint_as_float(p.y & 0xffff0000u)};
+}
+__device__ __forceinline__ epi_f4 gelu4(epi_f4 x) { return epi_f4{gelu_f(x.x), gelu_f(x.y), gelu_f(x.z), gelu_f(x.w)}; }
+__device__ __forceinline__ epi_f4 gelu_grad4(epi_f4 x) {
+  return epi_f4{gelu_grad_f(x.x), gelu_grad_f(x.y), gelu_grad_f(x.z), gelu_grad_f(x.w)};
+}
+
 template <int EPI, bool CF32>
 __device__ __forceinline__ void epi_tile(const GemmArgs& g, const float* cst, int rows, int row0, int n0) {
-  const int c = threadIdx.x & 127, col = n0 + c;
+  const int c = (threadIdx.x & 31) * 4, col = n0 + c;
   if (col >= g.N) return;
-  const float bias = g.bias ? g.bias[col] : 0.f;
+  const epi_f4 bias = g.bias ? *(const epi_f4*)(g.bias + col) : epi_f4{0.f, 0.f, 0.f, 0.f};
   const int rend = min(rows, g.M - row0);
-  for (int r = threadIdx.x >> 7; r < rend; r += 2) {
-    const int row = row0 + r;
-    const float v = cst[r * 128 + c] + bias;
-    const int64_t ci = (int64_t)row * g.ldc + col;
-    if constexpr (EPI == EPI_STORE) {
-      if constexpr (CF32) ((float*)g.C)[ci] = v;
-      else ((uint16_t*)g.C)[ci] = f2bf(v);
-    } else if constexpr (EPI == EPI_RESID) {
-      ((float*)g.C)[ci] = g.resid[(int64_t)row * g.ldres + col] + v;
-    } else if constexpr (EPI == EPI_GELU) {
-      ((uint16_t*)g.C)[ci] = f2bf(v);
-      ((uint16_t*)g.aux)[(int64_t)row * g.ldaux + col] = f2bf(gelu_f(v));
-    } else if constexpr (EPI == EPI_DGELU) {
-      const float u = bf2f(((const uint16_t*)g.aux)[(int64_t)row * g.ldaux + col]);
-      ((uint16_t*)g.C)[ci] = f2bf(v * gelu_grad_f(u));
-    } else {   // EPI_DGEGLU
-      const int64_t ai = (int64_t)row * g.ldaux + col;
-      const float gt = bf2f(((const uint16_t*)g.aux)[ai]);
-      const float up = bf2f(((const uint16_t*)g.aux)[ai + g.aux_off]);
-      ((uint16_t*)g.C)[ci] = f2bf(v * up * gelu_grad_f(gt));
-      ((uint16_t*)g.C)[ci + g.aux_off] = f2bf(v * gelu_f(gt));
+  float* Cf = (float*)g.C;
+  uint16_t* Ch = (uint16_t*)g.C;
+  const float* resid = g.resid;
+  uint16_t* aux = (uint16_t*)g.aux;
+  for (int rb = threadIdx.x >> 5; rb < rend; rb += 8 * kEpiRows) {
+    epi_f4 v[kEpiRows], a0[kEpiRows], a1[kEpiRows];
+#pragma unroll
+    for (int u = 0; u < kEpiRows; ++u) {
+      const int r = min(rb + 8 * u, rend - 1);   // rows past the end repeat the last row (not stored)
+      const int64_t row = row0 + r;
+      v[u] = *(const epi_f4*)(cst + r * 128 + c) + bias;
+      if constexpr (EPI == EPI_RESID) a0[u] = *(const epi_f4*)(resid + row * g.ldres + col);
+      if constexpr (EPI == EPI_DGELU || EPI == EPI_DGEGLU) a0[u] = unpack_bf16x4(*(const epi_u2*)(aux + row * g.ldaux + col));
+      if constexpr (EPI == EPI_DGEGLU) a1[u] = unpack_bf16x4(*(const epi_u2*)(aux + row * g.ldaux + col + g.aux_off));
+    }
+#pragma unroll
+    for (int u = 0; u < kEpiRows; ++u) {
+      const int r = rb + 8 * u;
+      if (r < rend) {
+        const int64_t row = row0 + r;
+        const int64_t ci = row * g.ldc + col;
+        const epi_f4 x = v[u];
+        if constexpr (EPI == EPI_STORE) {
+          if constexpr (CF32) *(epi_f4*)(Cf + ci) = x;
+          else *(epi_u2*)(Ch + ci) = pack_bf16x4(x);
+        } else if constexpr (EPI == EPI_RESID) {
+          *(epi_f4*)(Cf + ci) = a0[u] + x;
+        } else if constexpr (EPI == EPI_GELU) {
+          *(epi_u2*)(Ch + ci) = pack_bf16x4(x);
+          *(epi_u2*)(aux + row * g.ldaux + col) = pack_bf16x4(gelu4(x));
+        } else if constexpr (EPI == EPI_DGELU) {
+          *(epi_u2*)(Ch + ci) = pack_bf16x4(x * gelu_grad4(a0[u]));
+        } else {   // EPI_DGEGLU
+          *(epi_u2*)(Ch + ci) = pack_bf16x4(x * a1[u] * gelu_grad4(a0[u]));
+          *(epi_u2*)(Ch + ci + g.aux_off) = pack_bf16x4(x * gelu4(a0[u]));
+        }
+      }
     }
   }
 }

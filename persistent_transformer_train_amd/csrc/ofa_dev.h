@@ -36,14 +36,30 @@ __device__ __forceinline__ void stf(void* p, int64_t i, int dt, float v) {
 
 // ---------------------------------------------------------------- math
 
+// GELU in its exact erf form, GELU(u) = u Phi(u), with erf from Abramowitz &
+// Stegun, Handbook of Mathematical Functions, formula 7.1.26 (absolute error
+// at most 1.5e-7): erf(x) = 1 - t (a1 + t (a2 + ... + t a5)) exp(-x^2),
+// t = 1 / (1 + p |x|), odd in x.  exp(-x^2) with x = u / sqrt(2) is also the
+// Gaussian density's exponential, so GELU' = Phi(u) + u phi(u) takes one
+// exponential.  One base-2 exponential and one reciprocal instruction each.
+__device__ __forceinline__ float erf_as(float x, float e /* exp(-x*x) */) {
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, fabsf(x), 1.0f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f), 0.254829592f);
+  return copysignf(1.0f - poly * e, x);
+}
+
 __device__ __forceinline__ float gelu_f(float u) {
-  return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+  const float x = u * 0.70710678118654752f;
+  const float e = __builtin_amdgcn_exp2f(-x * x * 1.44269504088896341f);
+  return 0.5f * u * (1.0f + erf_as(x, e));
 }
 
 __device__ __forceinline__ float gelu_grad_f(float u) {
-  float cdf = 0.5f * (1.0f + erff(u * 0.70710678118654752f));
-  float pdf = expf(-0.5f * u * u) * 0.39894228040143268f;
-  return cdf + u * pdf;
+  const float x = u * 0.70710678118654752f;
+  const float e = __builtin_amdgcn_exp2f(-x * x * 1.44269504088896341f);
+  const float cdf = 0.5f * (1.0f + erf_as(x, e));
+  return fmaf(u * 0.39894228040143268f, e, cdf);
 }
 
 // ---------------------------------------------------------------- reductions

@@ -374,7 +374,7 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
   // contiguous dimension of a row-contiguous operand, multiples of 8) hold for
   // every bf16 configuration the validator accepts
   const bool mfma = h->cfg.precision == OFA_BF16 && a_dt == DT_BF16 && b_dt == DT_BF16 && gemm_p3_available() &&
-                    K % 8 == 0 && (a_km || M % 8 == 0) && (b_km || N % 8 == 0) && M >= 8 && N >= 8;
+                    K % 8 == 0 && (a_km || M % 8 == 0) && N % 8 == 0 && ldc % 8 == 0 && M >= 8 && N >= 8;
   g.impl = mfma ? GEMM_P3 : GEMM_SIMPLE;
   g.bm = mfma ? 128 : 64;
   g.bn = mfma ? 128 : 64;
@@ -462,7 +462,14 @@ void build_train(ofa_handle* h) {
     b[p].a.lnf.g = pf(g_off);
     b[p].a.lnf.b = pf(b_off);
   };
-  auto gemm_phase = [&](const GemmArgs& g, std::initializer_list<int> deps, const char* nm) {
+  auto gemm_phase = [&](GemmArgs g, std::initializer_list<int> deps, const char* nm) {
+    // the matrix-core epilogue accesses four columns at a time
+    if (g.impl == GEMM_P3 && (g.ldaux % 8 || g.ldres % 8 || g.aux_off % 8)) {
+      g.impl = GEMM_SIMPLE;
+      g.bm = g.bn = 64;
+      g.tiles_m = cdiv(g.M, 64);
+      g.tiles_n = cdiv(g.N, 64);
+    }
     int p = b.add(OP_GEMM, g.tiles_m * g.tiles_n, nm, deps);
     b[p].a.gemm = g;
     return p;
