@@ -44,15 +44,27 @@ __device__ __forceinline__ bf16x8_t pack_bf16(const float* v) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-// 64 rows x 64 head dims (bf16, row stride ld) -> LDS as [row][dh] and/or [dh][row]
-__device__ __forceinline__ void attn_load_block(const uint16_t* g, int64_t ld, int row0, int nvalid,
-                                                uint16_t* lds_n, uint16_t* lds_t) {
+// A block of 64 rows x 64 head dims (bf16, row stride ld) moves to LDS in two
+// steps so that the global reads of the next block overlap the current
+// block's arithmetic: attn_fetch reads it into registers (two 16-byte chunks
+// per thread), attn_stash writes them to LDS as [row][dh] and/or [dh][row].
+struct AttnChunk { uint4 v[2]; };
+
+__device__ __forceinline__ void attn_fetch(AttnChunk& c, const uint16_t* g, int64_t ld, int row0, int nvalid) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int c = threadIdx.x + i * kThreads;   // 512 chunks of 8
-    const int r = c >> 3, ch = (c & 7) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < nvalid) v = *(const uint4*)(g + (int64_t)(row0 + r) * ld + ch);
+    const int q = threadIdx.x + i * kThreads;   // 512 chunks of 8
+    const int r = q >> 3, ch = (q & 7) * 8;
+    c.v[i] = r < nvalid ? *(const uint4*)(g + (int64_t)(row0 + r) * ld + ch) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void attn_stash(const AttnChunk& c, uint16_t* lds_n, uint16_t* lds_t) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + i * kThreads;
+    const int r = q >> 3, ch = (q & 7) * 8;
+    const uint4 v = c.v[i];
     if (lds_n) *(uint4*)(lds_n + r * kAP + ch) = v;
     if (lds_t) {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -61,6 +73,11 @@ __device__ __forceinline__ void attn_load_block(const uint16_t* g, int64_t ld, i
     }
   }
 }
+
+// exp(x) as 2^(x log2 e) on the hardware base-2 exponential; callers fold
+// log2(e) into their scale factors and offsets
+constexpr float kLog2e = 1.44269504088896341f;
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // B-operand fragments of one wave's 32 rows (row stride ld) for the four 16-wide dh chunks
 __device__ __forceinline__ void attn_row_frags(bf16x8_t f[4], const uint16_t* g, int64_t ld, int row, bool valid,
@@ -87,7 +104,8 @@ __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
   const int64_t ld = 3 * (int64_t)a.d;
   const uint16_t* base = (const uint16_t*)a.qkv + (int64_t)b * a.T * ld + h * a.dh;
   const int q0 = qblk * 128, qw = q0 + 32 * w, q = qw + (lane & 31);
-  const float scale = 1.0f / sqrtf((float)a.dh);
+  // scores are kept in the base-2 domain: s2 = (q.k) scale log2(e)
+  const float scale2 = kLog2e / sqrtf((float)a.dh);
   bf16x8_t qf[4];
   attn_row_frags(qf, base, ld, q, q < a.T, lane);
   f32x16_t oacc[2];
@@ -96,10 +114,17 @@ __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
   float m = -INFINITY, lsum = 0.f;
   const int kend = min(q0 + 128, a.T);
   const int nkb = (kend + 63) / 64;
+  AttnChunk kc, vc;
+  attn_fetch(kc, base + a.d, ld, 0, min(64, a.T));
+  attn_fetch(vc, base + 2 * a.d, ld, 0, min(64, a.T));
   for (int kb = 0; kb < nkb; ++kb) {
     __syncthreads();
-    attn_load_block(base + a.d, ld, kb * 64, min(64, a.T - kb * 64), Ks, nullptr);
-    attn_load_block(base + 2 * a.d, ld, kb * 64, min(64, a.T - kb * 64), nullptr, Vt);
+    attn_stash(kc, Ks, nullptr);
+    attn_stash(vc, nullptr, Vt);
+    if (kb + 1 < nkb) {
+      attn_fetch(kc, base + a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
+      attn_fetch(vc, base + 2 * a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
+    }
     __syncthreads();
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -117,17 +142,17 @@ __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kbase + acc_row(r, lane);
-        const float v = (key <= q && key < a.T) ? s[r] * scale : -INFINITY;
+        const float v = (key <= q && key < a.T) ? s[r] * scale2 : -INFINITY;
         s[r] = v;
         mx = fmaxf(mx, v);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mnew = fmaxf(m, mx);
-      const float alpha = (m == -INFINITY) ? 0.f : expf(m - mnew);
+      const float alpha = (m == -INFINITY) ? 0.f : exp2_hw(m - mnew);
       float p[16], rs = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = (s[r] == -INFINITY) ? 0.f : expf(s[r] - mnew);
+        p[r] = (s[r] == -INFINITY) ? 0.f : exp2_hw(s[r] - mnew);
         rs += p[r];
       }
       rs += __shfl_xor(rs, 32, 64);
@@ -160,7 +185,8 @@ __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
         uint32_t w1 = (uint32_t)f2bf(oacc[db][4 * rg + 2] * inv) | ((uint32_t)f2bf(oacc[db][4 * rg + 3] * inv) << 16);
         *(uint2*)(o + j) = make_uint2(w0, w1);
       }
-    if (g == 0) a.lse[((int64_t)b * a.H + h) * a.T + q] = m + logf(lsum);
+    // natural-log LSE: m is in base-2 units
+    if (g == 0) a.lse[((int64_t)b * a.H + h) * a.T + q] = m * 0.69314718055994531f + logf(lsum);
   }
 }
 
@@ -185,7 +211,7 @@ __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
   const float* lse = a.lse + ((int64_t)b * a.H + h) * a.T;
   const float* dsum = a.dsum + ((int64_t)b * a.H + h) * a.T;
   const int k0 = kblk * 128, kw = k0 + 32 * w, key = kw + (lane & 31);
-  const float scale = 1.0f / sqrtf((float)a.dh);
+  const float scale = 1.0f / sqrtf((float)a.dh), scale2 = scale * kLog2e;
   bf16x8_t kf[4], vf[4];
   attn_row_frags(kf, base + a.d, ld, key, key < a.T, lane);
   attn_row_frags(vf, base + 2 * a.d, ld, key, key < a.T, lane);
@@ -193,16 +219,30 @@ __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) dk[0][e] = dk[1][e] = dv[0][e] = dv[1][e] = 0.f;
   const int nqb = (a.T + 63) / 64;
-  for (int qb = k0 / 64; qb < nqb; ++qb) {
-    const int q0 = qb * 64, nv = min(64, a.T - q0);
-    __syncthreads();
-    attn_load_block(base, ld, q0, nv, Qs, Qt);
-    attn_load_block(dob, a.d, q0, nv, Ds, Dt);
+  // query blocks stream through registers one block ahead (see attn_fetch)
+  AttnChunk qc, dc;
+  float lse_r = INFINITY, dd_r = 0.f;
+  auto fetch = [&](int qb) {
+    const int q0 = qb * 64;
+    attn_fetch(qc, base, ld, q0, min(64, a.T - q0));
+    attn_fetch(dc, dob, a.d, q0, min(64, a.T - q0));
     if (threadIdx.x < 64) {
       const int qq = q0 + threadIdx.x;
-      lse_s[threadIdx.x] = qq < a.T ? lse[qq] : INFINITY;
-      dd_s[threadIdx.x] = qq < a.T ? dsum[qq] : 0.f;
+      lse_r = qq < a.T ? lse[qq] * kLog2e : INFINITY;   // base-2 units
+      dd_r = qq < a.T ? dsum[qq] : 0.f;
     }
+  };
+  if (k0 / 64 < nqb) fetch(k0 / 64);
+  for (int qb = k0 / 64; qb < nqb; ++qb) {
+    const int q0 = qb * 64;
+    __syncthreads();
+    attn_stash(qc, Qs, Qt);
+    attn_stash(dc, Ds, Dt);
+    if (threadIdx.x < 64) {
+      lse_s[threadIdx.x] = lse_r;
+      dd_s[threadIdx.x] = dd_r;
+    }
+    if (qb + 1 < nqb) fetch(qb + 1);
     __syncthreads();
     if (kw >= a.T) continue;
 #pragma unroll
@@ -225,7 +265,7 @@ __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
       for (int r = 0; r < 16; ++r) {
         const int ql = sub * 32 + acc_row(r, lane);
         const int qq = q0 + ql;
-        const float pv = (key <= qq && qq < a.T) ? expf(s[r] * scale - lse_s[ql]) : 0.f;
+        const float pv = (key <= qq && qq < a.T) ? exp2_hw(s[r] * scale2 - lse_s[ql]) : 0.f;
         p[r] = pv;
         ds[r] = pv * (dp[r] - dd_s[ql]);
       }
@@ -275,22 +315,28 @@ __device__ void task_attn_bwd_q_mfma(const AttnArgs& a, int tile, char* smem) {
   const uint16_t* dob = (const uint16_t*)a.dout + (int64_t)b * a.T * a.d + h * a.dh;
   const int q0 = qblk * 128, qw = q0 + 32 * w, q = qw + (lane & 31);
   const bool qv = q < a.T;
-  const float scale = 1.0f / sqrtf((float)a.dh);
+  const float scale = 1.0f / sqrtf((float)a.dh), scale2 = scale * kLog2e;
   bf16x8_t qf[4], df[4];
   attn_row_frags(qf, base, ld, q, qv, lane);
   attn_row_frags(df, dob, a.d, q, qv, lane);
   const int64_t st = ((int64_t)b * a.H + h) * a.T + (qv ? q : 0);
-  const float lse_q = qv ? a.lse[st] : 0.f, d_q = qv ? a.dsum[st] : 0.f;
+  const float lse_q = qv ? a.lse[st] * kLog2e : 0.f, d_q = qv ? a.dsum[st] : 0.f;
   f32x16_t dq[2];
 #pragma unroll
   for (int e = 0; e < 16; ++e) dq[0][e] = dq[1][e] = 0.f;
   const int kend = min(q0 + 128, a.T);
   const int nkb = (kend + 63) / 64;
+  AttnChunk kc, vc;
+  attn_fetch(kc, base + a.d, ld, 0, min(64, a.T));
+  attn_fetch(vc, base + 2 * a.d, ld, 0, min(64, a.T));
   for (int kb = 0; kb < nkb; ++kb) {
-    const int nv = min(64, a.T - kb * 64);
     __syncthreads();
-    attn_load_block(base + a.d, ld, kb * 64, nv, Ks, Kt);
-    attn_load_block(base + 2 * a.d, ld, kb * 64, nv, Vs, nullptr);
+    attn_stash(kc, Ks, Kt);
+    attn_stash(vc, Vs, nullptr);
+    if (kb + 1 < nkb) {
+      attn_fetch(kc, base + a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
+      attn_fetch(vc, base + 2 * a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
+    }
     __syncthreads();
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -311,7 +357,7 @@ __device__ void task_attn_bwd_q_mfma(const AttnArgs& a, int tile, char* smem) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kbase + acc_row(r, lane);
-        const float pv = (key <= q && key < a.T && qv) ? expf(s[r] * scale - lse_q) : 0.f;
+        const float pv = (key <= q && key < a.T && qv) ? exp2_hw(s[r] * scale2 - lse_q) : 0.f;
         ds[r] = pv * (dp[r] - d_q);
       }
 #pragma unroll
