@@ -97,35 +97,31 @@ __device__ __forceinline__ void epi_tile(const GemmArgs& g, const float* cst, in
   }
 }
 
-// `pass_rows` = 128 when the LDS holds the whole tile, 64 otherwise (two passes).
-__device__ __forceinline__ void gemm_mfma_epilogue(const GemmArgs& g, const f32x16_t (&acc)[2][2], int m0, int n0,
-                                                   int wm, int wn, int lane, float* cst, int pass_rows) {
-  for (int pass = 0; pass < 128 / pass_rows; ++pass) {
-    const int rbase = pass * pass_rows;
-    __syncthreads();
-    if (wm >= rbase && wm < rbase + pass_rows) {
+// The waves park their accumulators in LDS as the fp32 tile [BM][128], then
+// walk it with epi_tile.
+template <int BM>
+__device__ __forceinline__ void gemm_mfma_epilogue(const GemmArgs& g, const f32x16_t (&acc)[BM / 64][2], int m0,
+                                                   int n0, int wm, int wn, int lane, float* cst) {
+  __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < BM / 64; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = wm - rbase + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-            cst[r * 128 + wn + j * 32 + (lane & 31)] = acc[i][j][e];
-          }
-    }
-    __syncthreads();
-    const int row0 = m0 + rbase;
-    switch (g.epi) {
-      case EPI_STORE:
-        if (g.c_dt == DT_F32) epi_tile<EPI_STORE, true>(g, cst, pass_rows, row0, n0);
-        else epi_tile<EPI_STORE, false>(g, cst, pass_rows, row0, n0);
-        break;
-      case EPI_RESID: epi_tile<EPI_RESID, true>(g, cst, pass_rows, row0, n0); break;
-      case EPI_GELU: epi_tile<EPI_GELU, false>(g, cst, pass_rows, row0, n0); break;
-      case EPI_DGELU: epi_tile<EPI_DGELU, false>(g, cst, pass_rows, row0, n0); break;
-      default: epi_tile<EPI_DGEGLU, false>(g, cst, pass_rows, row0, n0); break;
-    }
+      for (int e = 0; e < 16; ++e) {
+        const int r = wm + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        cst[r * 128 + wn + j * 32 + (lane & 31)] = acc[i][j][e];
+      }
+  __syncthreads();
+  switch (g.epi) {
+    case EPI_STORE:
+      if (g.c_dt == DT_F32) epi_tile<EPI_STORE, true>(g, cst, BM, m0, n0);
+      else epi_tile<EPI_STORE, false>(g, cst, BM, m0, n0);
+      break;
+    case EPI_RESID: epi_tile<EPI_RESID, true>(g, cst, BM, m0, n0); break;
+    case EPI_GELU: epi_tile<EPI_GELU, false>(g, cst, BM, m0, n0); break;
+    case EPI_DGELU: epi_tile<EPI_DGELU, false>(g, cst, BM, m0, n0); break;
+    default: epi_tile<EPI_DGEGLU, false>(g, cst, BM, m0, n0); break;
   }
 }
 
@@ -133,11 +129,16 @@ __device__ __forceinline__ void gemm_mfma_epilogue(const GemmArgs& g, const f32x
 // GEMM tile, pipelined version (K a multiple of 8; every row-contiguous
 // operand's contiguous dimension a multiple of 8).
 //
+// Tile: BM x 128 outputs (BM = 128 or 256), four waves in a 2 x 2 grid, each
+// (BM/2) x 64 = (BM/64) x 2 MFMA blocks of 32 x 32.  The 256-row tile moves
+// 1.5x the bytes of the 128-row tile per k slice for 2x the MFMAs: the copy
+// rate of a CU, not the matrix cores, bounds the smaller tile.
+//
 // Operands stay in their memory layout in LDS: a k-contiguous operand as
-// [128 rows][64 k], a row-contiguous operand as [64 k][128 rows], both with
-// 16-byte chunks XOR-swizzled so that fragment reads avoid bank conflicts.
-// Global -> LDS copies use the direct-to-LDS loads of gfx950 into a two-stage
-// ring: the next k slice is in flight while the current one is multiplied.
+// [rows][64 k], a row-contiguous operand as [64 k][rows], both with 16-byte
+// chunks XOR-swizzled so that fragment reads avoid bank conflicts.  Global ->
+// LDS copies use the direct-to-LDS loads of gfx950 into a three-stage ring:
+// the next two k slices are in flight while the current one is multiplied.
 // Fragments of a k-contiguous operand are one 16-byte LDS read; fragments of
 // a row-contiguous operand are two transposing 8-byte reads
 // (ds_read_b64_tr_b16): within each group of 16 lanes, lane 4g+e receives
@@ -150,37 +151,39 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kP3BK = 64;
-constexpr int kP3Stage = 128 * kP3BK;   // elements of one operand stage
-
 constexpr int kP3Stages = 3;            // k slices resident in the LDS ring (two in flight)
 
-struct GemmSmemP3 {
-  uint16_t a[kP3Stages][kP3Stage];
-  uint16_t b[kP3Stages][kP3Stage];
-};
+template <int BM>
+__host__ __device__ constexpr size_t gemm_p3_lds_bytes_t() {
+  return (size_t)kP3Stages * (BM + kMBN) * kP3BK * sizeof(uint16_t);
+}
+// the largest tile shape's ring (it also holds that tile's fp32 epilogue staging)
+__host__ __device__ constexpr size_t gemm_p3_lds_bytes() { return gemm_p3_lds_bytes_t<256>(); }
+static_assert(gemm_p3_lds_bytes_t<256>() >= 256 * 128 * sizeof(float), "epilogue staging fits the ring");
+static_assert(gemm_p3_lds_bytes_t<128>() >= 128 * 128 * sizeof(float), "epilogue staging fits the ring");
 
-__host__ __device__ constexpr size_t gemm_p3_lds_bytes() { return sizeof(GemmSmemP3); }
-
-// Issue the direct-to-LDS copy of one operand's (128 rows x 64 k) slice.
-// Wave w issues the 64-lane instructions w, w+4, w+8, w+12 (16 per slice);
-// lane L of instruction i fills physical 16-byte chunk p = 64 i + L.
-template <bool KMAJOR>
+// Issue part of the direct-to-LDS copy of one operand's (ROWS rows x 64 k)
+// slice: copies q0 .. q0+NQ-1 of the ROWS/32 this wave issues.  Wave w's copy q
+// is the 64-lane instruction w + 4q; lane L of instruction i fills physical
+// 16-byte chunk p = 64 i + L.
+template <bool KMAJOR, int ROWS, int NQ>
 __device__ __forceinline__ void p3_issue(const uint16_t* base, int64_t ld, int r0, int R, int k0, uint16_t* stage,
-                                         int wave, int lane) {
-  const uint16_t* src[4];
+                                         int wave, int lane, int q0) {
+  constexpr int CPR = ROWS / 8;   // 16-byte chunks per k row
+  const uint16_t* src[NQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int p = (wave + 4 * q) * 64 + lane;
+  for (int qq = 0; qq < NQ; ++qq) {
+    const int p = (wave + 4 * (q0 + qq)) * 64 + lane;
     if (KMAJOR) {
       // physical chunk p = 8 r + (c ^ (r & 7)): row r, logical k chunk c
       const int r = p >> 3, c = (p & 7) ^ (r & 7);
       const int rr = min(r0 + r, R - 1);   // rows past the end: any valid row (their outputs are dropped)
-      src[q] = base + (int64_t)rr * ld + k0 + c * 8;
+      src[qq] = base + (int64_t)rr * ld + k0 + c * 8;
     } else {
-      // physical chunk p = 16 k + (c ^ 2(k & 7)): k row k, logical row chunk c
-      const int k = p >> 4, c = (p & 15) ^ (2 * (k & 7));
+      // physical chunk p = CPR k + (c ^ 2(k & 7)): k row k, logical row chunk c
+      const int k = p / CPR, c = (p % CPR) ^ (2 * (k & 7));
       const int col = min(r0 + c * 8, R - 8);
-      src[q] = base + (int64_t)(k0 + k) * ld + col;
+      src[qq] = base + (int64_t)(k0 + k) * ld + col;
     }
   }
   // The copies are issued as inline assembly so that the compiler does not
@@ -192,10 +195,10 @@ __device__ __forceinline__ void p3_issue(const uint16_t* base, int64_t ld, int r
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int qq = 0; qq < NQ; ++qq) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(lds_void_t*)(stage + (wave + 4 * q) * 64 * 8));   // wave-uniform
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src[q]), "s"(lds) : "memory", "m0");
+        (uint32_t)(uintptr_t)(lds_void_t*)(stage + (wave + 4 * (q0 + qq)) * 64 * 8));   // wave-uniform
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src[qq]), "s"(lds) : "memory", "m0");
   }
 #pragma clang diagnostic pop
 }
@@ -203,11 +206,12 @@ __device__ __forceinline__ void p3_issue(const uint16_t* base, int64_t ld, int r
 // The last k slice when K is not a multiple of 64: ordinary loads with zero
 // fill (K % 8 == 0, so a 16-byte chunk is either wholly inside or outside),
 // written by ds_write to the same swizzled chunk the copy would have filled.
-template <bool KMAJOR>
+template <bool KMAJOR, int ROWS>
 __device__ __forceinline__ void p3_fill_tail(const uint16_t* base, int64_t ld, int r0, int R, int k0, int K,
                                              uint16_t* stage, int wave, int lane) {
+  constexpr int NQ = ROWS / 32, CPR = ROWS / 8;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     const int p = (wave + 4 * q) * 64 + lane;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (KMAJOR) {
@@ -215,7 +219,7 @@ __device__ __forceinline__ void p3_fill_tail(const uint16_t* base, int64_t ld, i
       const int rr = min(r0 + r, R - 1), k = k0 + c * 8;
       if (k < K) v = *(const uint4*)(base + (int64_t)rr * ld + k);
     } else {
-      const int k = p >> 4, c = (p & 15) ^ (2 * (k & 7));
+      const int k = p / CPR, c = (p % CPR) ^ (2 * (k & 7));
       const int col = min(r0 + c * 8, R - 8);
       if (k0 + k < K) v = *(const uint4*)(base + (int64_t)(k0 + k) * ld + col);
     }
@@ -223,11 +227,12 @@ __device__ __forceinline__ void p3_fill_tail(const uint16_t* base, int64_t ld, i
   }
 }
 
-template <bool KMAJOR>
+// whole slice: the copies at once, or the zero-filled tail
+template <bool KMAJOR, int ROWS>
 __device__ __forceinline__ void p3_load(const uint16_t* base, int64_t ld, int r0, int R, int k0, int K, uint16_t* stage,
                                         int wave, int lane) {
-  if (k0 + kP3BK <= K) p3_issue<KMAJOR>(base, ld, r0, R, k0, stage, wave, lane);
-  else p3_fill_tail<KMAJOR>(base, ld, r0, R, k0, K, stage, wave, lane);
+  if (k0 + kP3BK <= K) p3_issue<KMAJOR, ROWS, ROWS / 32>(base, ld, r0, R, k0, stage, wave, lane, 0);
+  else p3_fill_tail<KMAJOR, ROWS>(base, ld, r0, R, k0, K, stage, wave, lane);
 }
 
 // wait until at most N of this wave's vector-memory operations are
@@ -237,16 +242,14 @@ __device__ __forceinline__ void p3_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-// this wave's LDS reads are complete, then join the workgroup barrier
-__device__ __forceinline__ void p3_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
-
 __device__ __forceinline__ bf16x8_t p3_frag_k(const uint16_t* stage, int row, int kc) {
   const int pc = kc ^ (row & 7);
   return __builtin_bit_cast(bf16x8_t, *(const uint4*)(stage + row * kP3BK + pc * 8));
 }
 
 // fragment of rows rbase..rbase+31 (lane -> row rbase + lane%32), k16 chunk kk,
-// from a [64 k][128 rows] stage
+// from a [64 k][ROWS rows] stage
+template <int ROWS>
 __device__ __forceinline__ bf16x8_t p3_frag_t(const uint16_t* stage, int rbase, int kk, int lane) {
   const int G = lane >> 4, r = lane & 15;
   const int col = rbase + 16 * (G & 1) + 4 * (r & 3);
@@ -256,29 +259,33 @@ __device__ __forceinline__ bf16x8_t p3_frag_t(const uint16_t* stage, int rbase, 
   for (int t = 0; t < 2; ++t) {
     const int kr = kk * 16 + 8 * (G >> 1) + 4 * t + (r >> 2);
     const int pc = c ^ (2 * (kr & 7));
-    v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(stage + kr * 128 + pc * 8 + sub * 4));
+    v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(stage + kr * ROWS + pc * 8 + sub * 4));
   }
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
   i16x8_t w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
-template <bool AKM, bool BKM>
+template <bool AKM, bool BKM, int BM>
 __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
-  GemmSmemP3& s = *(GemmSmemP3*)smem;
+  constexpr int WMB = BM / 64;                         // 32-row MFMA blocks per wave
+  constexpr int SA = BM * kP3BK, SB = kMBN * kP3BK;    // stage elements per operand
+  constexpr int PER_SLICE = BM / 32 + kMBN / 32;       // copies per wave per k slice
+  uint16_t* ring_a = (uint16_t*)smem;
+  uint16_t* ring_b = ring_a + kP3Stages * SA;
   // tile order: with tile_order = 1 the M index runs fastest, so tiles that run
   // at the same time share the B panel (used when B is the larger operand)
   const int tm = g.tile_order ? tile % g.tiles_m : tile / g.tiles_n;
   const int tn = g.tile_order ? tile / g.tiles_m : tile % g.tiles_n;
-  const int m0 = tm * kMBM, n0 = tn * kMBN;
+  const int m0 = tm * BM, n0 = tn * kMBN;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * 64;
   const uint16_t* A = (const uint16_t*)g.A;
   const uint16_t* B = (const uint16_t*)g.B;
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[WMB][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WMB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -290,52 +297,59 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
 #pragma unroll
   for (int q = 0; q < kP3Stages - 1; ++q)
     if (q < nk) {
-      p3_load<AKM>(A, g.lda, m0, g.M, q * kP3BK, g.K, s.a[q], w, lane);
-      p3_load<BKM>(B, g.ldb, n0, g.N, q * kP3BK, g.K, s.b[q], w, lane);
+      p3_load<AKM, BM>(A, g.lda, m0, g.M, q * kP3BK, g.K, ring_a + q * SA, w, lane);
+      p3_load<BKM, kMBN>(B, g.ldb, n0, g.N, q * kP3BK, g.K, ring_b + q * SB, w, lane);
     }
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    // slice kt+2 goes into the buffer slice kt-1 used (everyone left it at the last barrier)
+    // Slice kt landed in every wave (slice kt+1 may stay in flight; a zero-filled
+    // tail slice is loaded synchronously, which also retires every older copy).
+    // Past this barrier every wave has finished reading slice kt-1, so its
+    // buffer takes slice kt+2: one barrier per slice.
+    if (kt + 1 < nk) p3_wait_barrier<PER_SLICE>();
+    else p3_wait_barrier<0>();
     const int ahead = kt + kP3Stages - 1;
     if (ahead < nk) {
       const int buf = cur == 0 ? kP3Stages - 1 : cur - 1;
-      p3_load<AKM>(A, g.lda, m0, g.M, ahead * kP3BK, g.K, s.a[buf], w, lane);
-      p3_load<BKM>(B, g.ldb, n0, g.N, ahead * kP3BK, g.K, s.b[buf], w, lane);
-      p3_wait_barrier<16>();   // slice kt landed in every wave; kt+1 and kt+2 stay in flight
-    } else if (kt + 1 < nk) {
-      p3_wait_barrier<8>();
-    } else {
-      p3_wait_barrier<0>();
+      p3_load<AKM, BM>(A, g.lda, m0, g.M, ahead * kP3BK, g.K, ring_a + buf * SA, w, lane);
+      p3_load<BKM, kMBN>(B, g.ldb, n0, g.N, ahead * kP3BK, g.K, ring_b + buf * SB, w, lane);
     }
-    const uint16_t* sa = s.a[cur];
-    const uint16_t* sb = s.b[cur];
+    const uint16_t* sa = ring_a + cur * SA;
+    const uint16_t* sb = ring_b + cur * SB;
 #pragma unroll
     for (int kk = 0; kk < kP3BK / 16; ++kk) {
-      bf16x8_t af[2], bfr[2];
+      bf16x8_t af[WMB], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = AKM ? p3_frag_k(sa, wm + i * 32 + (lane & 31), 2 * kk + (lane >> 5)) : p3_frag_t(sa, wm + i * 32, kk, lane);
+      for (int i = 0; i < WMB; ++i)
+        af[i] = AKM ? p3_frag_k(sa, wm + i * 32 + (lane & 31), 2 * kk + (lane >> 5))
+                    : p3_frag_t<BM>(sa, wm + i * 32, kk, lane);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bfr[j] = BKM ? p3_frag_k(sb, wn + j * 32 + (lane & 31), 2 * kk + (lane >> 5)) : p3_frag_t(sb, wn + j * 32, kk, lane);
+        bfr[j] = BKM ? p3_frag_k(sb, wn + j * 32 + (lane & 31), 2 * kk + (lane >> 5))
+                     : p3_frag_t<kMBN>(sb, wn + j * 32, kk, lane);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WMB; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    p3_lds_barrier();   // every wave is done with this slice before it is refilled
     cur = cur + 1 == kP3Stages ? 0 : cur + 1;
   }
-  gemm_mfma_epilogue(g, acc, m0, n0, wm, wn, lane, (float*)smem, 128);
+  gemm_mfma_epilogue<BM>(g, acc, m0, n0, wm, wn, lane, (float*)smem);
+}
+
+template <int BM>
+__device__ __forceinline__ void task_gemm_p3_bm(const GemmArgs& g, int tile, char* smem) {
+  if (g.a_kmajor) {
+    if (g.b_kmajor) gemm_p3<true, true, BM>(g, tile, smem); else gemm_p3<true, false, BM>(g, tile, smem);
+  } else {
+    if (g.b_kmajor) gemm_p3<false, true, BM>(g, tile, smem); else gemm_p3<false, false, BM>(g, tile, smem);
+  }
 }
 
 __device__ __forceinline__ void task_gemm_p3(const GemmArgs& g, int tile, char* smem) {
-  if (g.a_kmajor) {
-    if (g.b_kmajor) gemm_p3<true, true>(g, tile, smem); else gemm_p3<true, false>(g, tile, smem);
-  } else {
-    if (g.b_kmajor) gemm_p3<false, true>(g, tile, smem); else gemm_p3<false, false>(g, tile, smem);
-  }
+  if (g.bm == 256) task_gemm_p3_bm<256>(g, tile, smem);
+  else task_gemm_p3_bm<128>(g, tile, smem);
 }
 
 }  // namespace ofa

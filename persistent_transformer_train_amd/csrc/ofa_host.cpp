@@ -376,7 +376,10 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
   const bool mfma = h->cfg.precision == OFA_BF16 && a_dt == DT_BF16 && b_dt == DT_BF16 && gemm_p3_available() &&
                     K % 8 == 0 && (a_km || M % 8 == 0) && N % 8 == 0 && ldc % 8 == 0 && M >= 8 && N >= 8;
   g.impl = mfma ? GEMM_P3 : GEMM_SIMPLE;
-  g.bm = mfma ? 128 : 64;
+  // 256-row tiles move fewer bytes per MFMA; they pay off where even they make
+  // several waves of tiles over the whole GPU (the LM-head products)
+  const bool big = (int64_t)cdiv(M, 256) * cdiv(N, 128) >= 1024 || (h->cfg.debug_flags & OFA_DEBUG_TILE256);
+  g.bm = mfma ? (big ? 256 : 128) : 64;
   g.bn = mfma ? 128 : 64;
   g.tiles_m = cdiv(M, g.bm);
   g.tiles_n = cdiv(N, g.bn);
@@ -386,8 +389,9 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
 }
 
 // tile and ticket prefix sums; a ticket groups tiles so that a large phase
-// hands out at most ~512 tickets (each ticket costs one release fence)
-constexpr int kTicketsPerPhase = 512;
+// hands out at most ~256 tickets, about one per workgroup of a whole-GPU launch
+// (each ticket costs an atomic, a release fence and a counter update)
+constexpr int kTicketsPerPhase = 256;
 
 void finish_program(std::vector<Phase>& prog) {
   int tiles = 0, tickets = 0;

@@ -133,7 +133,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Phase* phases, int
   const Phase& ph = phases[idx];
   const uint64_t t0 = now_ticks();
   const GemmArgs g = ph.a.gemm;   // by value: see OFA_ARGS
-  for (int tile = blockIdx.x; tile < ph.n_tiles; tile += gridDim.x) {
+  // one tile per workgroup (the grid is the tile count): a loop around the
+  // tile lets the compiler hoist every layout variant's addressing out of it,
+  // which spills
+  const int tile = blockIdx.x;
+  if (tile < ph.n_tiles) {
     if constexpr (IMPL == GEMM_P3) task_gemm_p3(g, tile, smem);
     else task_gemm_simple(g, tile, smem);
   }
@@ -173,6 +177,12 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
   __shared__ int s_pre;
   __shared__ int s_stop;              // this workgroup saw the stop word of its open-ended job
   __shared__ int64_t s_all_checked;   // instance whose every phase this workgroup saw complete
+  // The phases' first tickets, and per phase the latest instance this
+  // workgroup has seen complete (with an acquire at the time): a ticket whose
+  // dependencies are all known complete neither polls the counters nor
+  // repeats the acquire.
+  __shared__ int32_t s_tb[kMaxPhases];
+  __shared__ int64_t s_known[kMaxPhases];
   const int ji = (p.n_jobs > 1 && (int)blockIdx.x >= p.job[0].n_wg) ? 1 : 0;
   const PersistJob& J = p.job[ji];
   const uint64_t base = J.sched->base;
@@ -181,6 +191,12 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
     s_all_checked = -1;
     s_stop = 0;
   }
+  for (int i = threadIdx.x; i < J.n_phases; i += kThreads) {
+    s_tb[i] = J.phases[i].ticket_base;
+    s_known[i] = -1;
+  }
+  __syncthreads();
+  int pi = 0;   // phase of the previous ticket (tickets only grow, so the search starts there)
   for (;;) {
     if (threadIdx.x == 0) s_ticket = add_relaxed(&J.sched->ticket, 1) - base;
     __syncthreads();
@@ -189,13 +205,9 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
     if (t >= total) break;
     const int64_t inst = (int64_t)(t / (uint64_t)J.tickets_per_inst);
     const int r = (int)(t % (uint64_t)J.tickets_per_inst);
-    // phase owning ticket r: last phase whose ticket_base <= r
-    int lo = 0, hi = J.n_phases - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (J.phases[mid].ticket_base <= r) lo = mid; else hi = mid - 1;
-    }
-    const int pi = lo;
+    // phase owning ticket r: last phase whose first ticket <= r
+    if (s_tb[pi] > r) pi = 0;   // a later instance starts over
+    while (pi + 1 < J.n_phases && s_tb[pi + 1] <= r) ++pi;
     const Phase& ph = J.phases[pi];
     const int j = r - ph.ticket_base;
     int tile0 = j * ph.per_ticket;
@@ -233,23 +245,28 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
     }
     // wait for the dependencies (thread 0), then one acquire for the workgroup
     if (threadIdx.x == 0) {
-      bool ok = true;
+      bool ok = true, fresh = false;
+      // phase q complete for instance i (i >= 0)
+      auto need = [&](int q, int64_t i) {
+        if (s_known[q] >= i) return true;
+        fresh = true;
+        const bool done = wait_count(&J.sched->done[q], base + (uint64_t)(i + 1) * J.phases[q].n_tiles, p, J, tc);
+        if (done) s_known[q] = i;
+        return done;
+      };
       for (int d = 0; d < kMaxDeps && ok; ++d) {
         const int q = ph.dep[d];
         if (q == -2) {
           if (s_all_checked != inst) {
-            for (int qq = 0; qq < pi && ok; ++qq)
-              ok = wait_count(&J.sched->done[qq], base + (uint64_t)(inst + 1) * J.phases[qq].n_tiles, p, J, tc);
+            for (int qq = 0; qq < pi && ok; ++qq) ok = need(qq, inst);
             if (ok) s_all_checked = inst;
           }
         } else if (q >= 0) {
-          ok = wait_count(&J.sched->done[q], base + (uint64_t)(inst + 1) * J.phases[q].n_tiles, p, J, tc);
+          ok = need(q, inst);
         }
       }
-      if (ok && ph.dep_prev >= 0 && inst > 0)
-        ok = wait_count(&J.sched->done[ph.dep_prev], base + (uint64_t)inst * J.phases[ph.dep_prev].n_tiles, p, J,
-                        tc);
-      if (ok) fence_acquire_agent();
+      if (ok && ph.dep_prev >= 0 && inst > 0) ok = need(ph.dep_prev, inst - 1);
+      if (ok && fresh) fence_acquire_agent();
       s_ok = ok ? 1 : 0;
     }
     __syncthreads();

@@ -166,6 +166,22 @@ def test_determinism_and_shuffled_tickets():
     assert runs[0] == runs[2]
 
 
+def test_gemm_256_row_tile_bitwise_equal_to_128():
+    """The 256-row GEMM tile (taken by the LM-head products at full size) sums
+    each output over k in the same order as the 128-row tile: forcing it on
+    every matrix-core GEMM of m3b (ragged vocabulary, row-contiguous operands)
+    must leave losses and weights bit-identical."""
+    from persistent_transformer_train_amd import ofa
+    h1, *_, g1 = gpu_run("m3b", 3, PERSISTENT)
+    p1 = h1.get_params().cpu().numpy()
+    h2, *_, g2 = gpu_run("m3b", 3, PERSISTENT, debug_flags=ofa.OFA_DEBUG_TILE256)
+    p2 = h2.get_params().cpu().numpy()
+    assert g1.tobytes() == g2.tobytes()
+    assert p1.tobytes() == p2.tobytes()
+    h1.close()
+    h2.close()
+
+
 def test_persistent_equals_per_phase_bitwise():
     h1, *_, g1 = gpu_run("m2", 3, PERSISTENT)
     p1 = h1.get_params().cpu().numpy()
