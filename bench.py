@@ -50,6 +50,35 @@ def decode_bytes_per_token(c: dict, ctx: float) -> float:
     return 2.0 * (weights + kv)
 
 
+def kernel_sources_sha256() -> str:
+    import hashlib
+    src = os.path.join(ROOT, "persistent_transformer_train_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(profile: str):
+    """HBM-side bytes per training step of the persistent kernel, from the
+    FETCH_SIZE / WRITE_SIZE passes recorded in the committed profile summary,
+    scaled by the same counters' reading for a plain copy of known size.  None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", profile)
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic: "):
+                    rec = json.loads(line[len("traffic: "):])
+                    if rec.get("sources_sha256") == kernel_sources_sha256():
+                        return rec["bytes_per_step"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
 def cpu_baseline(cfg: dict) -> dict:
     """The oracle (numpy fp64, untuned) on a bounded sample: one full training step of
     the same model at batch 1 (512 of the step's 4,096 tokens)."""
@@ -207,7 +236,8 @@ def main():
                    "executor": args.exec_mode, "params": int(ofa.ofa_param_count(ofa.make_config(cfg)))},
         "roofline": {"bound": "mfma", "kernel": "persistent_kernel" if args.exec_mode == "persistent"
                      else "all phase kernels", "achieved": round(achieved / 1e12, 2), "peak": PEAK_BF16 / 1e12,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16, 4),
+                     "traffic": measured_traffic("persistent_kernel_c3_train.md") if args.exec_mode == "persistent" else None,
                      "flops_per_step": fl["total"], "kernel_ms_per_step": round(kernel_ms / K, 4)},
         "losses": [float(ls[0]), float(ls[-1])],
     }
