@@ -160,7 +160,8 @@ static_assert(kDecCopies == 8, "wait counts above assume 8 copies per wave per t
 // Prefetch before the dependency wait: returns the number of tiles issued.
 __device__ __forceinline__ int dec_gemv_prefetch(const DecGemvArgs& a, int t0, int t1, char* smem, bool allowed) {
   if (!allowed) return 0;
-  const char* W = (const char*)a.W + a.st->w_delta;
+  const int64_t wd = a.pre_dep >= 0 ? a.st->w_delta : 0;
+  const char* W = (const char*)a.W + wd;
   const int n = min(a.n_buf, t1 - t0);
   for (int i = 0; i < n; ++i) dec_tile_issue(a, W, t0 + i, smem, i);
   return n;
@@ -271,21 +272,22 @@ __device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0
   const int pos = tc.sc->pos;
   const int64_t gen_idx = tc.sc->gen_idx;
   float* const logits_out = a.epi == DEPI_LOGITS ? a.io->logits_out : nullptr;
-  // everything that does not come from the tiles is read now, in one round trip:
-  // input, LayerNorm parameters, bias and residual of this thread's output rows
+  // Everything that does not come from the tiles is read in one batch of
+  // loads: the input (and its first element, the LayerNorm shift), the
+  // LayerNorm parameters, and the bias and residual of this thread's output rows.
   const void* bias = a.bias ? (const void*)((const char*)a.bias + wd) : nullptr;
   const int r0 = t0 * a.rows_per_tile;
   const int nrows = min(nt * a.rows_per_tile, (a.epi == DEPI_GEGLU ? a.F : a.N) - r0);
   constexpr int kPre = 4;   // rows per thread held in registers (the rest read in the epilogue)
-  float pre_b[kPre], pre_r[kPre];
+  constexpr int kMaxK = 4;  // input elements per thread (K <= 1024)
+  float pre_b[kPre], pre_r[kPre], gv[kMaxK], bv[kMaxK], xv[kMaxK];
+  float x0 = 0.f;
 #pragma unroll
   for (int m = 0; m < kPre; ++m) {
     const int i = threadIdx.x + m * kThreads;
     pre_b[m] = (bias && i < nrows) ? ldf(bias, r0 + i, a.w_dt) : 0.f;
     pre_r[m] = (a.epi == DEPI_RESID && i < nrows) ? a.resid[r0 + i] : 0.f;
   }
-  constexpr int kMaxK = 4;   // input elements per thread (K <= 1024) for the LayerNorm
-  float gv[kMaxK], bv[kMaxK];
   if (a.ln_g) {
     const void* g = (const char*)a.ln_g + wd;
     const void* b = (const char*)a.ln_b + wd;
@@ -295,8 +297,8 @@ __device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0
       gv[m] = j < a.K ? ldf(g, j, a.w_dt) : 0.f;
       bv[m] = j < a.K ? ldf(b, j, a.w_dt) : 0.f;
     }
+    x0 = a.xin[0];
   }
-  float s = 0.f;
   if (a.attn_part) {
     // the attention output: per head, the key-range partials rescaled to their
     // common maximum, summed, and divided by the summed weights
@@ -324,29 +326,40 @@ __device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0
           num += e * oc[c];
           den += e * lc[c];
         }
-      const float v = num / den;
-      xs[j] = v;
-      s += v;
+      xs[j] = num / den;
     }
+  } else if (!a.ln_g) {
+    for (int j = threadIdx.x; j < a.K; j += kThreads) xs[j] = a.xin[j];   // any K (the MLP down product)
   } else {
-    for (int j = threadIdx.x; j < a.K; j += kThreads) {
-      float v = a.xin[j];
-      xs[j] = v;
-      s += v;
-    }
-  }
-  if (a.ln_g) {
-    const float mean = block_sum2_dpp(s, 0.f, red).x / a.K;
-    float q = 0.f;
-    for (int j = threadIdx.x; j < a.K; j += kThreads) {
-      float dv = xs[j] - mean;
-      q += dv * dv;
-    }
-    const float rstd = 1.0f / sqrtf(block_sum2_dpp(q, 0.f, red + 2 * kWaves).x / a.K + 1e-5f);
+    // LayerNorm'd input: K = d_model <= 1024, four elements per thread
 #pragma unroll
     for (int m = 0; m < kMaxK; ++m) {
       const int j = threadIdx.x + m * kThreads;
-      if (j < a.K) xs[j] = (xs[j] - mean) * rstd * gv[m] + bv[m];
+      xv[m] = j < a.K ? a.xin[j] : 0.f;
+    }
+    {
+      // one reduction for the sum and the sum of squares, both shifted by the
+      // first element (the shift keeps the variance free of cancellation when
+      // the mean is large against the spread)
+      float s0 = 0.f, q = 0.f;
+#pragma unroll
+      for (int m = 0; m < kMaxK; ++m)
+        if (threadIdx.x + m * kThreads < a.K) {
+          const float dv = xv[m] - x0;
+          s0 += dv;
+          q += dv * dv;
+        }
+      const float2 sq = block_sum2_dpp(s0, q, red);
+      const float ms = sq.x / a.K;
+      const float mean = x0 + ms;
+      const float rstd = 1.0f / sqrtf(fmaxf(sq.y / a.K - ms * ms, 0.f) + 1e-5f);
+#pragma unroll
+      for (int m = 0; m < kMaxK; ++m) xv[m] = (xv[m] - mean) * rstd * gv[m] + bv[m];
+    }
+#pragma unroll
+    for (int m = 0; m < kMaxK; ++m) {
+      const int j = threadIdx.x + m * kThreads;
+      if (j < a.K) xs[j] = xv[m];
     }
   }
   __syncthreads();

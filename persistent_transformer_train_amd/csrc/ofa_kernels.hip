@@ -86,8 +86,9 @@ __device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& t
     OFA_CASE(OP_LN_BWD) OFA_CASE(OP_COLSUM) OFA_CASE(OP_COLRED) OFA_CASE(OP_ATTN_PREP)
     OFA_CASE(OP_ATTN_BWD_KV) OFA_CASE(OP_ATTN_BWD_Q) OFA_CASE(OP_ROPE_BWD) OFA_CASE(OP_EMB_SORT)
     OFA_CASE(OP_EMB_BWD) OFA_CASE(OP_ADAMW) OFA_CASE(OP_COPY) OFA_CASE(OP_DEC_EMBED)
-    OFA_CASE(OP_DEC_GEMV) OFA_CASE(OP_DEC_ATTN) OFA_CASE(OP_DEC_ARGMAX) OFA_CASE(OP_SLOT_GUARD)
-    OFA_CASE(OP_PUBLISH)
+    OFA_CASE(OP_DEC_ATTN) OFA_CASE(OP_DEC_ARGMAX) OFA_CASE(OP_SLOT_GUARD) OFA_CASE(OP_PUBLISH)
+    // OP_DEC_GEMV runs through run_dec_gemv (whole tickets, prefetched); keeping it
+    // out of this switch keeps its registers out of every other task's call
 #undef OFA_CASE
     default: break;
   }
