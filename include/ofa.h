@@ -93,6 +93,7 @@ typedef struct {
 #define OFA_DEBUG_SHORT_WATCHDOG  2  /* device waits give up after ~1 ms instead of ~10 s */
 #define OFA_DEBUG_TRACE           4  /* persistent mode: per (instance, phase) timestamps, see ofa_trace */
 #define OFA_DEBUG_TILE256         8  /* every matrix-core GEMM takes the 256-row tile (normally only large ones) */
+#define OFA_DEBUG_OCC2           16  /* step-mode persistent training with two workgroups per CU (measured slower at c3) */
 
 /* Size in bytes of the device workspace ofa_create() needs for cfg; 0 if cfg is
  * invalid (ofa_validate_config() says why). */

@@ -151,16 +151,21 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kP3BK = 64;
-constexpr int kP3Stages = 3;            // k slices resident in the LDS ring (two in flight)
 
-template <int BM>
+// LDS of a BM-row tile with a ring of `stages` k slices (it also holds the
+// tile's fp32 epilogue staging).  One workgroup per CU: three stages (two
+// slices in flight), 128 or 256 rows.  Two workgroups per CU (half the LDS
+// each): two stages, 128 rows -- the other workgroup's MFMAs run while this
+// one waits for its copies.
+template <int BM, int STAGES>
 __host__ __device__ constexpr size_t gemm_p3_lds_bytes_t() {
-  return (size_t)kP3Stages * (BM + kMBN) * kP3BK * sizeof(uint16_t);
+  return (size_t)STAGES * (BM + kMBN) * kP3BK * sizeof(uint16_t);
 }
-// the largest tile shape's ring (it also holds that tile's fp32 epilogue staging)
-__host__ __device__ constexpr size_t gemm_p3_lds_bytes() { return gemm_p3_lds_bytes_t<256>(); }
-static_assert(gemm_p3_lds_bytes_t<256>() >= 256 * 128 * sizeof(float), "epilogue staging fits the ring");
-static_assert(gemm_p3_lds_bytes_t<128>() >= 128 * 128 * sizeof(float), "epilogue staging fits the ring");
+__host__ __device__ constexpr size_t gemm_p3_lds_bytes() { return gemm_p3_lds_bytes_t<256, 3>(); }
+__host__ __device__ constexpr size_t gemm_p3_lds_bytes_occ2() { return gemm_p3_lds_bytes_t<128, 2>(); }
+static_assert(gemm_p3_lds_bytes_t<256, 3>() >= 256 * 128 * sizeof(float), "epilogue staging fits the ring");
+static_assert(gemm_p3_lds_bytes_t<128, 3>() >= 128 * 128 * sizeof(float), "epilogue staging fits the ring");
+static_assert(gemm_p3_lds_bytes_t<128, 2>() >= 128 * 128 * sizeof(float), "epilogue staging fits the ring");
 
 // Issue part of the direct-to-LDS copy of one operand's (ROWS rows x 64 k)
 // slice: copies q0 .. q0+NQ-1 of the ROWS/32 this wave issues.  Wave w's copy q
@@ -266,7 +271,7 @@ __device__ __forceinline__ bf16x8_t p3_frag_t(const uint16_t* stage, int rbase, 
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
-template <bool AKM, bool BKM, int BM>
+template <bool AKM, bool BKM, int BM, int kP3Stages>
 __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
   constexpr int WMB = BM / 64;                         // 32-row MFMA blocks per wave
   constexpr int SA = BM * kP3BK, SB = kMBN * kP3BK;    // stage elements per operand
@@ -302,11 +307,13 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
     }
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    // Slice kt landed in every wave (slice kt+1 may stay in flight; a zero-filled
-    // tail slice is loaded synchronously, which also retires every older copy).
-    // Past this barrier every wave has finished reading slice kt-1, so its
-    // buffer takes slice kt+2: one barrier per slice.
-    if (kt + 1 < nk) p3_wait_barrier<PER_SLICE>();
+    // Slice kt landed in every wave (with three stages slice kt+1 may stay in
+    // flight; a zero-filled tail slice is loaded synchronously, which also
+    // retires every older copy).  Past this barrier every wave has finished
+    // reading slice kt-1, so its buffer takes slice kt+STAGES-1: one barrier
+    // per slice.
+    constexpr int kInFlight = kP3Stages > 2 ? PER_SLICE : 0;   // copies of slice kt+1 allowed outstanding
+    if (kP3Stages > 2 && kt + 1 < nk) p3_wait_barrier<kInFlight>();
     else p3_wait_barrier<0>();
     const int ahead = kt + kP3Stages - 1;
     if (ahead < nk) {
@@ -338,18 +345,24 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
   gemm_mfma_epilogue<BM>(g, acc, m0, n0, wm, wn, lane, (float*)smem);
 }
 
-template <int BM>
+template <int BM, int STAGES>
 __device__ __forceinline__ void task_gemm_p3_bm(const GemmArgs& g, int tile, char* smem) {
   if (g.a_kmajor) {
-    if (g.b_kmajor) gemm_p3<true, true, BM>(g, tile, smem); else gemm_p3<true, false, BM>(g, tile, smem);
+    if (g.b_kmajor) gemm_p3<true, true, BM, STAGES>(g, tile, smem); else gemm_p3<true, false, BM, STAGES>(g, tile, smem);
   } else {
-    if (g.b_kmajor) gemm_p3<false, true, BM>(g, tile, smem); else gemm_p3<false, false, BM>(g, tile, smem);
+    if (g.b_kmajor) gemm_p3<false, true, BM, STAGES>(g, tile, smem); else gemm_p3<false, false, BM, STAGES>(g, tile, smem);
   }
 }
 
+// one workgroup per CU (OCC 1) or two (OCC 2: 128-row tiles only, set by the host)
+template <int OCC = 1>
 __device__ __forceinline__ void task_gemm_p3(const GemmArgs& g, int tile, char* smem) {
-  if (g.bm == 256) task_gemm_p3_bm<256>(g, tile, smem);
-  else task_gemm_p3_bm<128>(g, tile, smem);
+  if constexpr (OCC == 2) {
+    task_gemm_p3_bm<128, 2>(g, tile, smem);
+  } else {
+    if (g.bm == 256) task_gemm_p3_bm<256, 3>(g, tile, smem);
+    else task_gemm_p3_bm<128, 3>(g, tile, smem);
+  }
 }
 
 }  // namespace ofa

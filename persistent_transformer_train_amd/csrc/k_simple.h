@@ -801,6 +801,43 @@ __device__ __forceinline__ void ce_row_loop(const CeArgs& a, int r, int y, float
   if (threadIdx.x == 0) a.loss_rows[r] = lse - a.logits[(int64_t)r * a.V + y];
 }
 
+// Two passes for rows too long to hold in registers: the maximum and the
+// rescaled sum of exponentials in one pass (each thread keeps its own running
+// pair, combined over the workgroup in thread order), then the gradient.
+__device__ __forceinline__ void ce_row_online(const CeArgs& a, int r, int y, float* red) {
+  const float4* __restrict__ z4 = (const float4*)(a.logits + (int64_t)r * a.V);
+  const int n4 = a.V / 4;
+  constexpr int U = 4;
+  float m = -INFINITY, s = 0.f;
+  for (int i0 = threadIdx.x; i0 < n4; i0 += U * kThreads) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kThreads;
+      v[u] = i < n4 ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+    float cm = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) cm = fmaxf(cm, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+    const float cl2 = cm * 1.44269504088896341f;
+    float cs = m == -INFINITY ? 0.f : s * exp_shift(m, cl2);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      cs += (exp_shift(v[u].x, cl2) + exp_shift(v[u].y, cl2)) + (exp_shift(v[u].z, cl2) + exp_shift(v[u].w, cl2));
+    m = cm;
+    s = cs;
+  }
+  const float mx = block_max(m, red);
+  const float ml2 = mx * 1.44269504088896341f;
+  const float tot = block_sum(m == -INFINITY ? 0.f : s * exp_shift(m, ml2), red + kWaves);
+  const float lse = mx + logf(tot);
+  for (int i = threadIdx.x; i < n4; i += kThreads) ce_store(a, r, i, y, lse, z4[i]);
+  if (threadIdx.x == 0) a.loss_rows[r] = lse - a.logits[(int64_t)r * a.V + y];
+}
+
+// OCC 2 (two workgroups per CU, half the registers): rows beyond 16 float4 per
+// thread take the two-pass form
+template <int OCC = 1>
 __device__ __forceinline__ void task_ce(const CeArgs& a, int tile, const TaskCtx& tc, char* smem) {
   float* red = (float*)smem;
   const int r = tile;
@@ -809,7 +846,8 @@ __device__ __forceinline__ void task_ce(const CeArgs& a, int tile, const TaskCtx
   const int n4 = a.V / 4;
   if (n4 <= 4 * kThreads) ce_row_regs<4>(a, r, y, red);
   else if (n4 <= 16 * kThreads) ce_row_regs<16>(a, r, y, red);
-  else if (n4 <= 52 * kThreads) ce_row_regs<52>(a, r, y, red);
+  else if (OCC == 1 && n4 <= 52 * kThreads) ce_row_regs<OCC == 1 ? 52 : 16>(a, r, y, red);
+  else if (OCC == 2) ce_row_online(a, r, y, red);
   else ce_row_loop(a, r, y, red);
 }
 

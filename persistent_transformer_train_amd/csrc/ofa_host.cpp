@@ -272,6 +272,7 @@ struct ofa_handle {
   char* ws = nullptr;
   int n_cu = 0;
   int serve_wgs = 0;               // workgroups that run decode (one per serve CU)
+  int train_occ = 1;               // workgroups per CU of step-mode persistent training (1 or 2)
   std::vector<Phase> train;        // one training step
   std::vector<Phase> dec;          // one decode position (with head)
   Phase* d_train = nullptr;        // device copies (inside the pinned-upload area)
@@ -378,7 +379,9 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
   g.impl = mfma ? GEMM_P3 : GEMM_SIMPLE;
   // 256-row tiles move fewer bytes per MFMA; they pay off where even they make
   // several waves of tiles over the whole GPU (the LM-head products)
-  const bool big = (int64_t)cdiv(M, 256) * cdiv(N, 128) >= 1024 || (h->cfg.debug_flags & OFA_DEBUG_TILE256);
+  // (only with one workgroup per CU: two per CU leave each half the LDS)
+  const bool big = h->train_occ == 1 &&
+                   ((int64_t)cdiv(M, 256) * cdiv(N, 128) >= 1024 || (h->cfg.debug_flags & OFA_DEBUG_TILE256));
   g.bm = mfma ? (big ? 256 : 128) : 64;
   g.bn = mfma ? 128 : 64;
   g.tiles_m = cdiv(M, g.bm);
@@ -393,12 +396,12 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
 // (each ticket costs an atomic, a release fence and a counter update)
 constexpr int kTicketsPerPhase = 256;
 
-void finish_program(std::vector<Phase>& prog) {
+void finish_program(std::vector<Phase>& prog, int max_tickets = kTicketsPerPhase) {
   int tiles = 0, tickets = 0;
   for (auto& ph : prog) {
     ph.tile_base = tiles;
     tiles += ph.n_tiles;
-    if (ph.per_ticket <= 0) ph.per_ticket = std::max(1, cdiv(ph.n_tiles, kTicketsPerPhase));
+    if (ph.per_ticket <= 0) ph.per_ticket = std::max(1, cdiv(ph.n_tiles, max_tickets));
     ph.n_tickets = cdiv(ph.n_tiles, ph.per_ticket);
     ph.ticket_base = tickets;
     tickets += ph.n_tickets;
@@ -802,7 +805,8 @@ void build_train(ofa_handle* h) {
   // the next step's forward overwrites activations this step's backward reads
   b[p_emb].dep_prev = p_adam;
   b[p_sort].dep_prev = p_adam;
-  finish_program(h->train);
+  // about one ticket per workgroup of a whole-GPU launch
+  finish_program(h->train, std::max(kTicketsPerPhase, h->n_cu) * h->train_occ);
 }
 
 // Tile plan of a decode GEMV, whose task streams weight tiles through an LDS
@@ -817,7 +821,7 @@ bool plan_gemv(Phase& ph, int G) {
   const int halves = a.epi == DEPI_GEGLU ? 2 : 1;
   const int total = a.epi == DEPI_GEGLU ? a.F : a.N;
   const bool whole_heads = a.epi == DEPI_QKV && a.rope;
-  const size_t avail = std::min(persistent_lds_bytes(), lds_limit_bytes());
+  const size_t avail = std::min(persistent_lds_bytes(1), lds_limit_bytes());
   const int nch = (int)(rb / 16);
   if (nch > 64 * 8) return false;                       // a row needs more than 8 chunks per lane
   const int lpr = nch <= 16 * 8 ? 16 : (nch <= 32 * 8 ? 32 : 64);
@@ -1077,7 +1081,7 @@ PersistJob make_job(ofa_handle* h, const std::vector<Phase>& prog, const Phase* 
 }
 
 // One persistent launch of one or two jobs.
-ofa_status launch_jobs(ofa_handle* h, PersistJob* jobs, int n_jobs) {
+ofa_status launch_jobs(ofa_handle* h, PersistJob* jobs, int n_jobs, int occ = 1) {
   const ofa_config& c = h->cfg;
   PersistParams pp;
   memset(&pp, 0, sizeof pp);
@@ -1102,20 +1106,22 @@ ofa_status launch_jobs(ofa_handle* h, PersistJob* jobs, int n_jobs) {
     h->trace_dec = j.phases == h->d_dec;
   }
   h->last_grid = grid;
-  HIP_TRY(h, launch_persistent(pp, grid, h->stream));
+  HIP_TRY(h, launch_persistent(pp, grid, h->stream, occ));
   return OFA_OK;
 }
 
-// One persistent launch of n_inst instances of a program on `cus` CUs.
+// One persistent launch of n_inst instances of a program on `cus` CUs, with
+// the kernel built for `kocc` workgroups per CU.
 ofa_status run_persistent(ofa_handle* h, const std::vector<Phase>& prog, const Phase* d_prog, const StepCtx* d_ctx,
-                          int64_t n_inst, size_t sched_off, PhaseTime* times, uint64_t* inst_end, int cus) {
-  const int occ = persistent_occupancy();
+                          int64_t n_inst, size_t sched_off, PhaseTime* times, uint64_t* inst_end, int cus,
+                          int kocc = 1) {
+  const int occ = persistent_occupancy(kocc);
   if (occ < 1) return fail(h, OFA_E_HIP, "persistent kernel does not fit a CU");
   ofa_status s = reset_sched(h, sched_off, (int)prog.size());
   if (s != OFA_OK) return s;
   if (inst_end) HIP_TRY(h, launch_fill_u64(inst_end, 0, n_inst, h->stream));
   PersistJob j = make_job(h, prog, d_prog, d_ctx, n_inst, sched_off, times, inst_end, cus * occ);
-  return launch_jobs(h, &j, 1);
+  return launch_jobs(h, &j, 1, kocc);
 }
 
 }  // namespace
@@ -1216,7 +1222,7 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
     kernels_ready = true;
   }
   // the sort of the embedding backward keeps batch*seq 64-bit keys in LDS
-  if ((size_t)h->D.BT * 8 + 64 > persistent_lds_bytes())
+  if ((size_t)h->D.BT * 8 + 64 > persistent_lds_bytes(1))
     return fail(h, OFA_E_ARG, "batch*seq %lld needs more LDS than the device allows", (long long)h->D.BT);
   int dev = 0;
   HIP_TRY(h, hipGetDevice(&dev));
@@ -1231,9 +1237,15 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
   HIP_TRY(h, hipEventCreate(&h->ev_t0));
   HIP_TRY(h, hipEventCreate(&h->ev_t1));
   {
-    const int occ = std::max(1, persistent_occupancy());
+    const int occ = std::max(1, persistent_occupancy(1));
     h->serve_wgs = (h->cfg.serve_cus > 0 ? h->cfg.serve_cus : h->n_cu) * occ;
   }
+  // Step-mode training can run two workgroups per CU where the kernel fits
+  // twice (co-resident launches keep one: both jobs share one kernel).  At c3
+  // it measured slower (16.5 against 13.7 ms: twice the tickets and fences),
+  // so it is opt-in.
+  const bool coresident_cfg = h->cfg.train_cus > 0 && h->cfg.serve_cus > 0;
+  h->train_occ = (!coresident_cfg && (h->cfg.debug_flags & OFA_DEBUG_OCC2) && persistent_occupancy(2) >= 2) ? 2 : 1;
   build_train(h);
   build_decode(h);
   if (!h->plan_ok) return fail(h, OFA_E_ARG, "a decode matrix-vector product does not fit the LDS");
@@ -1241,9 +1253,12 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
     return fail(h, OFA_E_ARG, "program too long");
   for (const auto* prog : {&h->train, &h->dec})
     for (const Phase& ph : *prog)
-      if ((size_t)ph.lds_bytes > persistent_lds_bytes() || (size_t)ph.lds_bytes > lds_limit_bytes())
+      if ((size_t)ph.lds_bytes > persistent_lds_bytes(1) || (size_t)ph.lds_bytes > lds_limit_bytes())
         return fail(h, OFA_E_ARG, "phase op %d needs %d bytes of LDS (> %zu)", ph.op, ph.lds_bytes,
-                    persistent_lds_bytes());
+                    persistent_lds_bytes(1));
+  if (h->train_occ == 2)
+    for (const Phase& ph : h->train)
+      if (phase_lds_bytes_occ(ph, 2) > persistent_lds_bytes(2)) h->train_occ = 1;   // one per CU after all
   // phase tables live in a small library-owned device buffer
   size_t tbytes = (h->train.size() + h->dec.size()) * sizeof(Phase);
   HIP_TRY(h, hipMalloc(&h->d_alloc, tbytes));
@@ -1393,7 +1408,7 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
   } else {
     int cus = c.train_cus > 0 ? c.train_cus : h->n_cu;
     s = run_persistent(h, h->train, h->d_train, d_steps, n_steps, h->cw.sched, tm,
-                       at<uint64_t>(h->ws, h->cw.inst_end), cus);
+                       at<uint64_t>(h->ws, h->cw.inst_end), cus, h->train_occ);
     if (s != OFA_OK) return s;
   }
   HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
@@ -1444,7 +1459,7 @@ ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_
     s = run_launch_per_phase(h, h->dec, h->d_dec, d_dsteps, n_inst, 0, true);
   else
     s = run_persistent(h, h->dec, h->d_dec, d_dsteps, n_inst, h->cw.dsched, dtm, nullptr,
-                       h->serve_wgs / std::max(1, persistent_occupancy()));
+                       h->serve_wgs / std::max(1, persistent_occupancy(1)));
   if (s != OFA_OK) return s;
   HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
   h->timed = true;
@@ -1508,7 +1523,7 @@ ofa_status ofa_train_and_serve(ofa_handle* h, const int32_t* dev_tokens, int32_t
   HIP_TRY(h, launch_fill_u32((uint32_t*)&st->serving, 1, 1, h->stream));
   HIP_TRY(h, launch_fill_u64(&st->version, h->version, 1, h->stream));
   if (dev_n_generated) HIP_TRY(h, launch_fill_u64(dev_n_generated, 0, 1, h->stream));
-  const int occ = persistent_occupancy();
+  const int occ = persistent_occupancy(1);
   if (occ < 1) return fail(h, OFA_E_HIP, "persistent kernel does not fit a CU");
   PhaseTime* tm = at<PhaseTime>(ws, w.times);
   PhaseTime* dtm = at<PhaseTime>(ws, w.dtimes);

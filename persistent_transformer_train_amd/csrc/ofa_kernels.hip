@@ -32,13 +32,13 @@ namespace ofa {
 // out that the loop's stores change them), and every such reload waits for all
 // outstanding memory operations, the streaming copies included.
 #define OFA_ARGS(FIELD) const auto a = ph.a.FIELD
-template <int OP>
+template <int OP, int OCC = 1>
 __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCtx& tc, char* smem) {
   if constexpr (OP == OP_EMBED) { OFA_ARGS(emb); task_embed(a, tile, tc); }
   else if constexpr (OP == OP_LN_FWD) { OFA_ARGS(lnf); task_ln_fwd(a, tile); }
   else if constexpr (OP == OP_GEMM) {
     OFA_ARGS(gemm);
-    if (a.impl == GEMM_P3) task_gemm_p3(a, tile, smem);
+    if (a.impl == GEMM_P3) task_gemm_p3<OCC>(a, tile, smem);
     else task_gemm_simple(a, tile, smem);
   }
   else if constexpr (OP == OP_ROPE) { OFA_ARGS(rope); task_rope(a, tile, false); }
@@ -48,7 +48,7 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
     else task_attn_fwd_simple(a, tile, smem);
   }
   else if constexpr (OP == OP_GEGLU_FWD) { OFA_ARGS(geglu); task_geglu_fwd(a, tile); }
-  else if constexpr (OP == OP_CE) { OFA_ARGS(ce); task_ce(a, tile, tc, smem); }
+  else if constexpr (OP == OP_CE) { OFA_ARGS(ce); task_ce<OCC>(a, tile, tc, smem); }
   else if constexpr (OP == OP_LOSS) { OFA_ARGS(loss); task_loss(a, tc, smem); }
   else if constexpr (OP == OP_LN_BWD) { OFA_ARGS(lnb); task_ln_bwd(a, tile, smem); }
   else if constexpr (OP == OP_COLSUM) { OFA_ARGS(cs); task_colsum(a, tile, smem); }
@@ -78,9 +78,10 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
 }
 #undef OFA_ARGS
 
+template <int OCC>
 __device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& tc, char* smem) {
   switch (ph.op) {
-#define OFA_CASE(X) case X: run_task<X>(ph, tile, tc, smem); break;
+#define OFA_CASE(X) case X: run_task<X, OCC>(ph, tile, tc, smem); break;
     OFA_CASE(OP_EMBED) OFA_CASE(OP_LN_FWD) OFA_CASE(OP_GEMM) OFA_CASE(OP_ROPE)
     OFA_CASE(OP_ATTN_FWD) OFA_CASE(OP_GEGLU_FWD) OFA_CASE(OP_CE) OFA_CASE(OP_LOSS)
     OFA_CASE(OP_LN_BWD) OFA_CASE(OP_COLSUM) OFA_CASE(OP_COLRED) OFA_CASE(OP_ATTN_PREP)
@@ -171,7 +172,11 @@ __device__ __forceinline__ bool wait_count(const uint64_t* ctr, uint64_t need, c
   }
 }
 
-__global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
+// OCC: workgroups per CU the launch is built for.  OCC 2 (training only: two
+// workgroups share a CU's LDS and registers, so one's MFMAs run while the
+// other waits on memory) leaves out the decode tasks.
+template <int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams p) {
   extern __shared__ __align__(16) char smem[];
   __shared__ uint64_t s_ticket;
   __shared__ int s_ok;
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
     // a decode GEMV starts streaming its weights before its dependencies are
     // met; with two weight slots only once this token's version is known
     int npre = 0;
-    if (ph.op == OP_DEC_GEMV) {
+    if (OCC == 1 && ph.op == OP_DEC_GEMV) {
       const DecGemvArgs& a = ph.a.dgemv;
       bool allow = !(a.epi == DEPI_LOGITS && !(tc.sc->head & 1));
       if (allow && a.pre_dep >= 0) {
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
         __syncthreads();
         allow = __builtin_amdgcn_readfirstlane(s_pre) != 0;
       }
-      npre = prefetch_dec_gemv(ph, tile0, tile1, smem, allow);
+      if constexpr (OCC == 1) npre = prefetch_dec_gemv(ph, tile0, tile1, smem, allow);
     }
     // An open-ended job stops at an instance boundary once the other job has
     // finished: the workgroup holding an instance's first ticket checks the
@@ -281,15 +286,21 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(PersistParams p) {
       atomicMax((unsigned long long*)&J.trace[4 * (inst * J.n_phases + pi)], ~(unsigned long long)t0);
       atomicMax((unsigned long long*)&J.trace[4 * (inst * J.n_phases + pi) + 1], (unsigned long long)t0);
     }
-    if (ph.op == OP_DEC_GEMV) run_dec_gemv(ph, tile0, tile1, tc, smem, npre);
-    else for (int tile = tile0; tile < tile1; ++tile) {
+    bool gemv = false;
+    if constexpr (OCC == 1) {
+      if (ph.op == OP_DEC_GEMV) {
+        run_dec_gemv(ph, tile0, tile1, tc, smem, npre);
+        gemv = true;
+      }
+    }
+    if (!gemv) for (int tile = tile0; tile < tile1; ++tile) {
       int tl = tile;
       if (p.shuffle && ph.n_tiles > 1) {
         // reversal after a rotation: a permutation of the phase's tiles
         const int rot = (int)(((uint64_t)inst * 977u + 31u) % (uint64_t)ph.n_tiles);
         tl = ph.n_tiles - 1 - (tile + rot) % ph.n_tiles;
       }
-      run_any(ph, tl, tc, smem);
+      run_any<OCC>(ph, tl, tc, smem);
     }
     // publish: the barrier makes every wave's stores complete; one agent-scope
     // release fence then makes them visible before the counter moves
@@ -360,13 +371,21 @@ static size_t lds_for(const Phase& ph) {
 
 size_t phase_lds_bytes(const Phase& ph) { return lds_for(ph); }
 
+// LDS a phase needs in the persistent kernel built for occ workgroups per CU
+// (the matrix-core GEMM tile keeps a two-slice ring there)
+size_t phase_lds_bytes_occ(const Phase& ph, int occ) {
+  if (occ == 2 && ph.op == OP_GEMM && ph.a.gemm.impl == GEMM_P3) return gemm_p3_lds_bytes_occ2();
+  return lds_for(ph);
+}
+
 // Dynamic LDS: every phase fits 64 KB.  The pipelined GEMM uses exactly
 // 64 KB, which together with the kernels' own static LDS needs the raised
 // per-kernel limit; without it that GEMM is not used.
 static size_t g_lds_limit = 60 * 1024;
 static size_t g_persist_lds = 60 * 1024;
+static size_t g_persist_lds2 = 0;   // OCC 2 kernel: half of a CU's LDS (0: not available)
 static bool g_p3_ok = false;
-size_t persistent_lds_bytes() { return g_persist_lds; }
+size_t persistent_lds_bytes(int occ) { return occ == 2 ? g_persist_lds2 : g_persist_lds; }
 bool gemm_p3_available() { return g_p3_ok; }
 
 // Dynamic LDS of the persistent kernel (and of the kernels whose phases need
@@ -381,11 +400,11 @@ hipError_t init_kernels() {
   (void)hipGetLastError();
   hipFuncAttributes fa;
   size_t stat = 2048;
-  if (hipFuncGetAttributes(&fa, (const void*)persistent_kernel) == hipSuccess) stat = fa.sharedSizeBytes;
+  if (hipFuncGetAttributes(&fa, (const void*)persistent_kernel<1>) == hipSuccess) stat = fa.sharedSizeBytes;
   (void)hipGetLastError();
   size_t want = max_blk > (int)stat ? ((size_t)max_blk - stat) / 1024 * 1024 : 0;
   if (want < gemm_p3_lds_bytes()) return hipSuccess;   // pipelined GEMM unavailable; small tiles only
-  const void* big[] = {(const void*)gemm_kernel<GEMM_P3>, (const void*)persistent_kernel,
+  const void* big[] = {(const void*)gemm_kernel<GEMM_P3>, (const void*)persistent_kernel<1>,
                        (const void*)phase_kernel<OP_DEC_GEMV>};
   bool ok = true;
   for (const void* f : big)
@@ -396,14 +415,30 @@ hipError_t init_kernels() {
     g_lds_limit = want;
     g_persist_lds = want;
   }
+  // the two-per-CU kernel: half of the CU's LDS, less its own static LDS
+  size_t stat2 = stat;
+  if (hipFuncGetAttributes(&fa, (const void*)persistent_kernel<2>) == hipSuccess) stat2 = fa.sharedSizeBytes;
+  (void)hipGetLastError();
+  const size_t half = (size_t)max_blk / 2;
+  const size_t want2 = half > stat2 ? (half - stat2) / 1024 * 1024 : 0;
+  if (ok && want2 >= gemm_p3_lds_bytes_occ2() &&
+      hipFuncSetAttribute((const void*)persistent_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)want2) ==
+          hipSuccess)
+    g_persist_lds2 = want2;
+  (void)hipGetLastError();
   return hipSuccess;
 }
 
 size_t lds_limit_bytes() { return g_lds_limit; }
 
-int persistent_occupancy() {
+int persistent_occupancy(int occ) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, persistent_kernel, kThreads, g_persist_lds) != hipSuccess) {
+  if (occ == 2 && g_persist_lds2 == 0) return 0;
+  const hipError_t e = occ == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, persistent_kernel<2>, kThreads,
+                                                                              g_persist_lds2)
+                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, persistent_kernel<1>, kThreads,
+                                                                              g_persist_lds);
+  if (e != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -439,10 +474,13 @@ hipError_t launch_phase(const Phase& h, const Phase* d_phases, int idx, const St
   return hipGetLastError();
 }
 
-hipError_t launch_persistent(const PersistParams& p, int grid, hipStream_t s) {
+hipError_t launch_persistent(const PersistParams& p, int grid, hipStream_t s, int occ) {
   (void)hipGetLastError();
   void* args[] = {(void*)&p};
-  return hipLaunchCooperativeKernel((const void*)persistent_kernel, dim3(grid), dim3(kThreads), args,
+  if (occ == 2)
+    return hipLaunchCooperativeKernel((const void*)persistent_kernel<2>, dim3(grid), dim3(kThreads), args,
+                                      g_persist_lds2, s);
+  return hipLaunchCooperativeKernel((const void*)persistent_kernel<1>, dim3(grid), dim3(kThreads), args,
                                     g_persist_lds, s);
 }
 

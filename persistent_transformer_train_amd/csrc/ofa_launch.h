@@ -39,14 +39,15 @@ struct PersistParams {
 
 hipError_t init_kernels();
 size_t phase_lds_bytes(const Phase& ph);   // dynamic LDS a phase needs
-size_t persistent_lds_bytes();             // dynamic LDS of the persistent kernel
+size_t phase_lds_bytes_occ(const Phase& ph, int occ);   // the same in the persistent kernel built for occ
+size_t persistent_lds_bytes(int occ);      // dynamic LDS of the persistent kernel built for occ workgroups per CU (0: none)
 size_t lds_limit_bytes();                  // dynamic LDS a per-phase kernel may use
 bool gemm_p3_available();                  // the pipelined GEMM tile can be launched
-int persistent_occupancy();                // workgroups per CU for the persistent kernel
+int persistent_occupancy(int occ);         // workgroups per CU of the persistent kernel built for occ (1 or 2)
 
 hipError_t launch_phase(const Phase& host_ph, const Phase* dev_phases, int idx, const StepCtx* dev_sc,
                         DevStatus* status, PhaseTime* times, int64_t step, hipStream_t s);
-hipError_t launch_persistent(const PersistParams& p, int grid, hipStream_t s);
+hipError_t launch_persistent(const PersistParams& p, int grid, hipStream_t s, int occ);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t v, int64_t n, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 // p[2i] = a, p[2i+1] = b for i < n_pairs

@@ -182,6 +182,22 @@ def test_gemm_256_row_tile_bitwise_equal_to_128():
     h2.close()
 
 
+def test_two_workgroups_per_cu_bitwise_equal_to_one():
+    """Step-mode persistent training with two workgroups per CU (OFA_DEBUG_OCC2:
+    the GEMM tile then keeps a two-slice ring) must give bit-identical losses
+    and weights to the default one workgroup per CU."""
+    from persistent_transformer_train_amd import ofa
+    h1, *_, g1 = gpu_run("m3b", 3, PERSISTENT, debug_flags=ofa.OFA_DEBUG_OCC2)
+    p1 = h1.get_params().cpu().numpy()
+    h2, *_, g2 = gpu_run("m3b", 3, PERSISTENT)
+    p2 = h2.get_params().cpu().numpy()
+    assert h1.sync().grid == 2 * h2.sync().grid
+    assert g1.tobytes() == g2.tobytes()
+    assert p1.tobytes() == p2.tobytes()
+    h1.close()
+    h2.close()
+
+
 def test_persistent_equals_per_phase_bitwise():
     h1, *_, g1 = gpu_run("m2", 3, PERSISTENT)
     p1 = h1.get_params().cpu().numpy()
