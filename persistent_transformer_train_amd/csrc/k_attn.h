@@ -28,12 +28,27 @@ __device__ __forceinline__ bf16x8_t frag16(const uint16_t* base, int row, int k)
   return __builtin_bit_cast(bf16x8_t, *(const uint4*)(base + row * kAP + k));
 }
 
-// A fragment over k chunk c (16 wide) with the accumulator's k permutation
-__device__ __forceinline__ bf16x8_t frag_kperm(const uint16_t* base, int row, int c, int g) {
-  const uint16_t* p = base + row * kAP + 16 * c + 4 * g;
-  uint2 a = *(const uint2*)p;
-  uint2 b = *(const uint2*)(p + 8);
-  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+// An A fragment over k chunk c (16 wide) with the accumulator's k permutation,
+// read from an untransposed block [key][dh] (pitch kAP) with
+// the transposing LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane 4g+e receives element e of the 4-element pieces addressed by
+// lanes g, g+4, g+8, g+12, so lane r addressing key k0 + r/4 at head dims
+// c0 + 4(r%4) leaves lane L with keys k0..k0+3 of head dim c0 + L.  Two reads
+// (keys 16c + 4g + 0..3 and 16c + 8 + 4g + 0..3) give the accumulator's k
+// permutation.  dbase: first head dim of the 32-row block; kbase: 16c plus the
+// block's first key.
+__device__ __forceinline__ bf16x8_t frag_kperm_tr(const uint16_t* blk, int dbase, int kbase, int lane) {
+  const int G = lane >> 4, r = lane & 15;
+  const int col = dbase + 16 * (G & 1) + 4 * (r & 3);
+  i16x4_t v[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int key = kbase + 8 * t + 4 * (G >> 1) + (r >> 2);
+    v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(blk + key * kAP + col));
+  }
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  i16x8_t w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+  return __builtin_bit_cast(bf16x8_t, w);
 }
 
 // eight fp32 values (accumulator elements 8c..8c+7) -> bf16 B operand
@@ -47,7 +62,8 @@ __device__ __forceinline__ bf16x8_t pack_bf16(const float* v) {
 // A block of 64 rows x 64 head dims (bf16, row stride ld) moves to LDS in two
 // steps so that the global reads of the next block overlap the current
 // block's arithmetic: attn_fetch reads it into registers (two 16-byte chunks
-// per thread), attn_stash writes them to LDS as [row][dh] and/or [dh][row].
+// per thread), attn_stash writes them to LDS as [row][dh]; operands that need
+// the block as [dh][row] read it back with the transposing LDS read.
 struct AttnChunk { uint4 v[2]; };
 
 __device__ __forceinline__ void attn_fetch(AttnChunk& c, const uint16_t* g, int64_t ld, int row0, int nvalid) {
@@ -59,18 +75,12 @@ __device__ __forceinline__ void attn_fetch(AttnChunk& c, const uint16_t* g, int6
   }
 }
 
-__device__ __forceinline__ void attn_stash(const AttnChunk& c, uint16_t* lds_n, uint16_t* lds_t) {
+__device__ __forceinline__ void attn_stash(const AttnChunk& c, uint16_t* lds) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int q = threadIdx.x + i * kThreads;
     const int r = q >> 3, ch = (q & 7) * 8;
-    const uint4 v = c.v[i];
-    if (lds_n) *(uint4*)(lds_n + r * kAP + ch) = v;
-    if (lds_t) {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lds_t[(ch + j) * kAP + r] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
-    }
+    *(uint4*)(lds + r * kAP + ch) = c.v[i];
   }
 }
 
@@ -90,14 +100,14 @@ __device__ __forceinline__ void attn_row_frags(bf16x8_t f[4], const uint16_t* g,
   }
 }
 
-__host__ __device__ constexpr size_t attn_mfma_lds_bytes() { return 4 * 64 * kAP * 2 + 2 * 64 * 4; }
+__host__ __device__ constexpr size_t attn_mfma_lds_bytes() { return 2 * 64 * kAP * 2 + 2 * 64 * 4; }
 
 // ---------------------------------------------------------------- forward
 // tile = (b, h, block of 128 queries), largest blocks first; wave w owns 32 queries.
 
 __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
   uint16_t* Ks = (uint16_t*)smem;        // [64 keys][dh]
-  uint16_t* Vt = Ks + 64 * kAP;          // [dh][64 keys]
+  uint16_t* Vs = Ks + 64 * kAP;          // [64 keys][dh]
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, g = lane >> 5;
   const int BH = a.B * a.H, nqb = (a.T + 127) / 128;
   const int qblk = nqb - 1 - tile / BH, bh = tile % BH, b = bh / a.H, h = bh % a.H;
@@ -119,8 +129,8 @@ __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
   attn_fetch(vc, base + 2 * a.d, ld, 0, min(64, a.T));
   for (int kb = 0; kb < nkb; ++kb) {
     __syncthreads();
-    attn_stash(kc, Ks, nullptr);
-    attn_stash(vc, nullptr, Vt);
+    attn_stash(kc, Ks);
+    attn_stash(vc, Vs);
     if (kb + 1 < nkb) {
       attn_fetch(kc, base + a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
       attn_fetch(vc, base + 2 * a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
@@ -168,7 +178,7 @@ __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
         const bf16x8_t pb = pack_bf16(p + 8 * c);
 #pragma unroll
         for (int db = 0; db < 2; ++db)
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm(Vt + sub * 32, db * 32 + (lane & 31), c, g),
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm_tr(Vs, db * 32, sub * 32 + 16 * c, lane),
                                                              pb, oacc[db], 0, 0, 0);
       }
     }
@@ -197,10 +207,8 @@ __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
 
 __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
   uint16_t* Qs = (uint16_t*)smem;        // [64 q][dh]
-  uint16_t* Qt = Qs + 64 * kAP;          // [dh][64 q]
-  uint16_t* Ds = Qt + 64 * kAP;          // dO [64 q][dh]
-  uint16_t* Dt = Ds + 64 * kAP;          // dO^T [dh][64 q]
-  float* lse_s = (float*)(Dt + 64 * kAP);
+  uint16_t* Ds = Qs + 64 * kAP;          // dO [64 q][dh]
+  float* lse_s = (float*)(Ds + 64 * kAP);
   float* dd_s = lse_s + 64;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, g = lane >> 5;
   const int BH = a.B * a.H;
@@ -236,8 +244,8 @@ __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
   for (int qb = k0 / 64; qb < nqb; ++qb) {
     const int q0 = qb * 64;
     __syncthreads();
-    attn_stash(qc, Qs, Qt);
-    attn_stash(dc, Ds, Dt);
+    attn_stash(qc, Qs);
+    attn_stash(dc, Ds);
     if (threadIdx.x < 64) {
       lse_s[threadIdx.x] = lse_r;
       dd_s[threadIdx.x] = dd_r;
@@ -274,9 +282,9 @@ __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
         const bf16x8_t pb = pack_bf16(p + 8 * c), sb = pack_bf16(ds + 8 * c);
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm(Dt + sub * 32, db * 32 + (lane & 31), c, g), pb,
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm_tr(Ds, db * 32, sub * 32 + 16 * c, lane), pb,
                                                            dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm(Qt + sub * 32, db * 32 + (lane & 31), c, g), sb,
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm_tr(Qs, db * 32, sub * 32 + 16 * c, lane), sb,
                                                            dk[db], 0, 0, 0);
         }
       }
@@ -306,7 +314,6 @@ __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
 __device__ void task_attn_bwd_q_mfma(const AttnArgs& a, int tile, char* smem) {
   uint16_t* Ks = (uint16_t*)smem;        // [64 keys][dh]
   uint16_t* Vs = Ks + 64 * kAP;          // [64 keys][dh]
-  uint16_t* Kt = Vs + 64 * kAP;          // [dh][64 keys]
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, g = lane >> 5;
   const int BH = a.B * a.H, nqb = (a.T + 127) / 128;
   const int qblk = nqb - 1 - tile / BH, bh = tile % BH, b = bh / a.H, h = bh % a.H;
@@ -331,8 +338,8 @@ __device__ void task_attn_bwd_q_mfma(const AttnArgs& a, int tile, char* smem) {
   attn_fetch(vc, base + 2 * a.d, ld, 0, min(64, a.T));
   for (int kb = 0; kb < nkb; ++kb) {
     __syncthreads();
-    attn_stash(kc, Ks, Kt);
-    attn_stash(vc, Vs, nullptr);
+    attn_stash(kc, Ks);
+    attn_stash(vc, Vs);
     if (kb + 1 < nkb) {
       attn_fetch(kc, base + a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
       attn_fetch(vc, base + 2 * a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
@@ -365,7 +372,7 @@ __device__ void task_attn_bwd_q_mfma(const AttnArgs& a, int tile, char* smem) {
         const bf16x8_t sb = pack_bf16(ds + 8 * c);
 #pragma unroll
         for (int db = 0; db < 2; ++db)
-          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm(Kt + sub * 32, db * 32 + (lane & 31), c, g), sb,
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_kperm_tr(Ks, db * 32, sub * 32 + 16 * c, lane), sb,
                                                            dq[db], 0, 0, 0);
       }
     }
