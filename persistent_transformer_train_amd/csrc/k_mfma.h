@@ -278,10 +278,8 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
   constexpr int PER_SLICE = BM / 32 + kMBN / 32;       // copies per wave per k slice
   uint16_t* ring_a = (uint16_t*)smem;
   uint16_t* ring_b = ring_a + kP3Stages * SA;
-  // tile order: with tile_order = 1 the M index runs fastest, so tiles that run
-  // at the same time share the B panel (used when B is the larger operand)
-  const int tm = g.tile_order ? tile % g.tiles_m : tile / g.tiles_n;
-  const int tn = g.tile_order ? tile / g.tiles_m : tile % g.tiles_n;
+  int tm, tn;
+  gemm_tile_rc(g, tile, tm, tn);
   const int m0 = tm * BM, n0 = tn * kMBN;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int wm = (w >> 1) * (BM / 2), wn = (w & 1) * 64;

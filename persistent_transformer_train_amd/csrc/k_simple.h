@@ -397,8 +397,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, int m, int n, f
 
 __device__ __forceinline__ void task_gemm_simple(const GemmArgs& g, int tile, char* smem) {
   GemmSmemSimple& s = *(GemmSmemSimple*)smem;
-  const int tm = g.tile_order ? tile % g.tiles_m : tile / g.tiles_n;
-  const int tn = g.tile_order ? tile / g.tiles_m : tile % g.tiles_n;
+  int tm, tn;
+  gemm_tile_rc(g, tile, tm, tn);
   const int m0 = tm * 64, n0 = tn * 64;
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
   float acc[4][4];

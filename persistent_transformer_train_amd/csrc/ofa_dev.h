@@ -143,6 +143,39 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return s;
 }
 
+// ---------------------------------------------------------------- tile placement
+
+// GEMM tile index -> (tile row, tile column).  tile_order 0 walks a row of
+// tiles at a time, 1 a column of tiles; 2 walks bands of `group` tile rows,
+// each band column by column, so a run of consecutive tiles covers a compact
+// rectangle of C: the A panels of the band's rows and a few B panels.
+__device__ __forceinline__ void gemm_tile_rc(const GemmArgs& g, int tile, int& tm, int& tn) {
+  if (g.tile_order == 2) {
+    const int r0 = tile / (g.group * g.tiles_n) * g.group;
+    const int rows = min(g.group, g.tiles_m - r0);
+    const int in = tile - r0 * g.tiles_n;
+    tm = r0 + in % rows;
+    tn = in / rows;
+  } else if (g.tile_order == 1) {
+    tm = tile % g.tiles_m;
+    tn = tile / g.tiles_m;
+  } else {
+    tm = tile / g.tiles_n;
+    tn = tile % g.tiles_n;
+  }
+}
+
+// The hardware hands the workgroups of a launch to the eight accelerator
+// dies (XCDs, each with its own L2) in turn: workgroup b runs on die b % 8.
+// xcd_block maps b to a tile so that each die gets one contiguous run of the
+// n tiles (die x: tiles [x q + min(x, r), ...) with q = n / 8, r = n % 8), and
+// neighbouring tiles share that die's L2.  A bijection on [0, n).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_block(int b, int n) {
+  const int x = b % kXcds, i = b / kXcds, q = n / kXcds, r = n % kXcds;
+  return x * q + min(x, r) + i;
+}
+
 // ---------------------------------------------------------------- atomics
 
 __device__ __forceinline__ uint64_t ld_acquire(const uint64_t* p) {

@@ -386,8 +386,16 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
   g.bn = mfma ? 128 : 64;
   g.tiles_m = cdiv(M, g.bm);
   g.tiles_n = cdiv(N, g.bn);
-  // walk the smaller operand fastest so the larger one is streamed about once
-  g.tile_order = (int64_t)N > (int64_t)M ? 1 : 0;
+  if (h->cfg.debug_flags & OFA_DEBUG_PLAIN_TILES) {
+    // walk the smaller operand fastest so the larger one is streamed about once
+    g.tile_order = (int64_t)N > (int64_t)M ? 1 : 0;
+  } else {
+    // bands of eight tile rows: a die's run of tiles (or a window of tickets)
+    // covers a compact block of C, whose operand panels its L2 can hold
+    g.tile_order = 2;
+    g.group = 8;
+    g.xcd = 1;
+  }
   return g;
 }
 

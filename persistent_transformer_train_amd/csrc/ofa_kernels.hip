@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const Phase* phases, int
   // one tile per workgroup (the grid is the tile count): a loop around the
   // tile lets the compiler hoist every layout variant's addressing out of it,
   // which spills
-  const int tile = blockIdx.x;
+  const int tile = g.xcd ? xcd_block(blockIdx.x, ph.n_tiles) : (int)blockIdx.x;
   if (tile < ph.n_tiles) {
     if constexpr (IMPL == GEMM_P3) task_gemm_p3(g, tile, smem);
     else task_gemm_simple(g, tile, smem);

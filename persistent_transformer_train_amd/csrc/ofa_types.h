@@ -75,7 +75,9 @@ struct GemmArgs {
   int32_t tiles_m, tiles_n;
   int32_t aux_off;
   int32_t bm, bn;     // tile shape (rows of C, columns of C)
-  int32_t tile_order; // 0: N index fastest; 1: M index fastest
+  int32_t tile_order; // 0: N index fastest; 1: M index fastest; 2: bands of `group` tile rows, M index fastest
+  int32_t group;      // tile rows per band (tile_order 2)
+  int32_t xcd;        // one-launch-per-phase executor: give each die a contiguous run of tiles
 };
 
 struct LnFwdArgs {

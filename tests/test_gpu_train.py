@@ -198,6 +198,23 @@ def test_two_workgroups_per_cu_bitwise_equal_to_one():
     h2.close()
 
 
+@pytest.mark.parametrize("exec_mode", [PER_PHASE, PERSISTENT], ids=["per_phase", "persistent"])
+def test_die_aware_tile_placement_bitwise_equal_to_plain(exec_mode):
+    """Where a GEMM tile runs (banded tile order, each die's launch blocks on a
+    contiguous run of tiles) changes no arithmetic: m3b (ragged vocabulary,
+    partial bands) with OFA_DEBUG_PLAIN_TILES must give bit-identical losses
+    and weights."""
+    from persistent_transformer_train_amd import ofa
+    h1, *_, g1 = gpu_run("m3b", 3, exec_mode)
+    p1 = h1.get_params().cpu().numpy()
+    h2, *_, g2 = gpu_run("m3b", 3, exec_mode, debug_flags=ofa.OFA_DEBUG_PLAIN_TILES)
+    p2 = h2.get_params().cpu().numpy()
+    assert g1.tobytes() == g2.tobytes()
+    assert p1.tobytes() == p2.tobytes()
+    h1.close()
+    h2.close()
+
+
 def test_persistent_equals_per_phase_bitwise():
     h1, *_, g1 = gpu_run("m2", 3, PERSISTENT)
     p1 = h1.get_params().cpu().numpy()
