@@ -55,7 +55,7 @@ __device__ __forceinline__ bf16x8_t frag_kperm_tr(const uint16_t* blk, int dbase
 __device__ __forceinline__ bf16x8_t pack_bf16(const float* v) {
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) w[i] = f2bf2(v[2 * i], v[2 * i + 1]);
   return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
@@ -191,8 +191,8 @@ __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int j = db * 32 + acc_row(4 * rg, lane);   // 4 consecutive head dims
-        uint32_t w0 = (uint32_t)f2bf(oacc[db][4 * rg] * inv) | ((uint32_t)f2bf(oacc[db][4 * rg + 1] * inv) << 16);
-        uint32_t w1 = (uint32_t)f2bf(oacc[db][4 * rg + 2] * inv) | ((uint32_t)f2bf(oacc[db][4 * rg + 3] * inv) << 16);
+        uint32_t w0 = f2bf2(oacc[db][4 * rg] * inv, oacc[db][4 * rg + 1] * inv);
+        uint32_t w1 = f2bf2(oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv);
         *(uint2*)(o + j) = make_uint2(w0, w1);
       }
     // natural-log LSE: m is in base-2 units
@@ -297,11 +297,11 @@ __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int j = db * 32 + acc_row(4 * rg, lane);
-        uint32_t k0w = (uint32_t)f2bf(dk[db][4 * rg] * scale) | ((uint32_t)f2bf(dk[db][4 * rg + 1] * scale) << 16);
-        uint32_t k1w = (uint32_t)f2bf(dk[db][4 * rg + 2] * scale) | ((uint32_t)f2bf(dk[db][4 * rg + 3] * scale) << 16);
+        uint32_t k0w = f2bf2(dk[db][4 * rg] * scale, dk[db][4 * rg + 1] * scale);
+        uint32_t k1w = f2bf2(dk[db][4 * rg + 2] * scale, dk[db][4 * rg + 3] * scale);
         *(uint2*)(out + a.d + j) = make_uint2(k0w, k1w);
-        uint32_t v0w = (uint32_t)f2bf(dv[db][4 * rg]) | ((uint32_t)f2bf(dv[db][4 * rg + 1]) << 16);
-        uint32_t v1w = (uint32_t)f2bf(dv[db][4 * rg + 2]) | ((uint32_t)f2bf(dv[db][4 * rg + 3]) << 16);
+        uint32_t v0w = f2bf2(dv[db][4 * rg], dv[db][4 * rg + 1]);
+        uint32_t v1w = f2bf2(dv[db][4 * rg + 2], dv[db][4 * rg + 3]);
         *(uint2*)(out + 2 * a.d + j) = make_uint2(v0w, v1w);
       }
   }
@@ -384,8 +384,8 @@ __device__ void task_attn_bwd_q_mfma(const AttnArgs& a, int tile, char* smem) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int j = db * 32 + acc_row(4 * rg, lane);
-        uint32_t w0 = (uint32_t)f2bf(dq[db][4 * rg] * scale) | ((uint32_t)f2bf(dq[db][4 * rg + 1] * scale) << 16);
-        uint32_t w1 = (uint32_t)f2bf(dq[db][4 * rg + 2] * scale) | ((uint32_t)f2bf(dq[db][4 * rg + 3] * scale) << 16);
+        uint32_t w0 = f2bf2(dq[db][4 * rg] * scale, dq[db][4 * rg + 1] * scale);
+        uint32_t w1 = f2bf2(dq[db][4 * rg + 2] * scale, dq[db][4 * rg + 3] * scale);
         *(uint2*)(out + j) = make_uint2(w0, w1);
       }
   }

@@ -34,12 +34,13 @@ constexpr int kMBM = 128, kMBN = 128;   // output tile
 // are multiples of 8 (checked on the host), so every access is aligned.  In
 // bf16 mode every low-precision operand of an epilogue (C, aux) is bf16.
 constexpr int kEpiRows = 4;
+constexpr int kEpiPitch = 128 + 4;   // floats per parked row
 
 typedef float epi_f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t epi_u2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ epi_u2 pack_bf16x4(epi_f4 x) {
-  return epi_u2{(uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16), (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16)};
+  return epi_u2{f2bf2(x.x, x.y), f2bf2(x.z, x.w)};
 }
 __device__ __forceinline__ epi_f4 unpack_bf16x4(epi_u2 p) {
   return epi_f4{__uint_as_float(p.x << 16), __uint_as_float(p.x & 0xffff0000u), __uint_as_float(p.y << 16),
@@ -66,7 +67,7 @@ __device__ __forceinline__ void epi_tile(const GemmArgs& g, const float* cst, in
     for (int u = 0; u < kEpiRows; ++u) {
       const int r = min(rb + 8 * u, rend - 1);   // rows past the end repeat the last row (not stored)
       const int64_t row = row0 + r;
-      v[u] = *(const epi_f4*)(cst + r * 128 + c) + bias;
+      v[u] = *(const epi_f4*)(cst + r * kEpiPitch + c) + bias;
       if constexpr (EPI == EPI_RESID) a0[u] = *(const epi_f4*)(resid + row * g.ldres + col);
       if constexpr (EPI == EPI_DGELU || EPI == EPI_DGEGLU) a0[u] = unpack_bf16x4(*(const epi_u2*)(aux + row * g.ldaux + col));
       if constexpr (EPI == EPI_DGEGLU) a1[u] = unpack_bf16x4(*(const epi_u2*)(aux + row * g.ldaux + col + g.aux_off));
@@ -97,8 +98,13 @@ __device__ __forceinline__ void epi_tile(const GemmArgs& g, const float* cst, in
   }
 }
 
-// The waves park their accumulators in LDS as the fp32 tile [BM][128], then
-// walk it with epi_tile.
+// The waves park their accumulators in LDS as the fp32 tile [BM][kEpiPitch],
+// then walk it with epi_tile.  The accumulators hold transposed 32 x 32 blocks
+// (the MFMA takes the B fragment as its first operand): element e of lane l
+// is C[l % 32][8 (e / 4) + 4 (l / 32) + e % 4] of the block, so each group of
+// four is four adjacent columns of one row, parked with one 16-byte write.
+// The pitch (128 + 4 floats) spreads the 32 rows a write touches over all
+// banks.
 template <int BM>
 __device__ __forceinline__ void gemm_mfma_epilogue(const GemmArgs& g, const f32x16_t (&acc)[BM / 64][2], int m0,
                                                    int n0, int wm, int wn, int lane, float* cst) {
@@ -108,9 +114,10 @@ __device__ __forceinline__ void gemm_mfma_epilogue(const GemmArgs& g, const f32x
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = wm + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        cst[r * 128 + wn + j * 32 + (lane & 31)] = acc[i][j][e];
+      for (int q = 0; q < 4; ++q) {
+        const int r = wm + i * 32 + (lane & 31), cc = wn + j * 32 + 8 * q + 4 * (lane >> 5);
+        *(epi_f4*)(cst + r * kEpiPitch + cc) =
+            epi_f4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
       }
   __syncthreads();
   switch (g.epi) {
@@ -159,13 +166,12 @@ constexpr int kP3BK = 64;
 // one waits for its copies.
 template <int BM, int STAGES>
 __host__ __device__ constexpr size_t gemm_p3_lds_bytes_t() {
-  return (size_t)STAGES * (BM + kMBN) * kP3BK * sizeof(uint16_t);
+  const size_t ring = (size_t)STAGES * (BM + kMBN) * kP3BK * sizeof(uint16_t);
+  const size_t park = (size_t)BM * kEpiPitch * sizeof(float);
+  return ring > park ? ring : park;
 }
 __host__ __device__ constexpr size_t gemm_p3_lds_bytes() { return gemm_p3_lds_bytes_t<256, 3>(); }
 __host__ __device__ constexpr size_t gemm_p3_lds_bytes_occ2() { return gemm_p3_lds_bytes_t<128, 2>(); }
-static_assert(gemm_p3_lds_bytes_t<256, 3>() >= 256 * 128 * sizeof(float), "epilogue staging fits the ring");
-static_assert(gemm_p3_lds_bytes_t<128, 3>() >= 128 * 128 * sizeof(float), "epilogue staging fits the ring");
-static_assert(gemm_p3_lds_bytes_t<128, 2>() >= 128 * 128 * sizeof(float), "epilogue staging fits the ring");
 
 // Issue part of the direct-to-LDS copy of one operand's (ROWS rows x 64 k)
 // slice: copies q0 .. q0+NQ-1 of the ROWS/32 this wave issues.  Wave w's copy q
@@ -273,6 +279,7 @@ __device__ __forceinline__ bf16x8_t p3_frag_t(const uint16_t* stage, int rbase, 
 
 template <bool AKM, bool BKM, int BM, int kP3Stages>
 __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem) {
+  static_assert(kP3Stages >= 2 && kP3Stages <= 4, "ring of two to four slices");
   constexpr int WMB = BM / 64;                         // 32-row MFMA blocks per wave
   constexpr int SA = BM * kP3BK, SB = kMBN * kP3BK;    // stage elements per operand
   constexpr int PER_SLICE = BM / 32 + kMBN / 32;       // copies per wave per k slice
@@ -305,13 +312,13 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
     }
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    // Slice kt landed in every wave (with three stages slice kt+1 may stay in
-    // flight; a zero-filled tail slice is loaded synchronously, which also
-    // retires every older copy).  Past this barrier every wave has finished
-    // reading slice kt-1, so its buffer takes slice kt+STAGES-1: one barrier
-    // per slice.
-    constexpr int kInFlight = kP3Stages > 2 ? PER_SLICE : 0;   // copies of slice kt+1 allowed outstanding
-    if (kP3Stages > 2 && kt + 1 < nk) p3_wait_barrier<kInFlight>();
+    // Slice kt landed in every wave (the copies of the up to STAGES-2 slices
+    // after it may stay in flight; a zero-filled tail slice is loaded
+    // synchronously, which also retires every older copy).  Past this barrier
+    // every wave has finished reading slice kt-1, so its buffer takes slice
+    // kt+STAGES-1: one barrier per slice.
+    if (kP3Stages > 3 && kt + 2 < nk) p3_wait_barrier<2 * PER_SLICE>();
+    else if (kP3Stages > 2 && kt + 1 < nk) p3_wait_barrier<PER_SLICE>();
     else p3_wait_barrier<0>();
     const int ahead = kt + kP3Stages - 1;
     if (ahead < nk) {
@@ -336,7 +343,7 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
       for (int i = 0; i < WMB; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
     cur = cur + 1 == kP3Stages ? 0 : cur + 1;
   }

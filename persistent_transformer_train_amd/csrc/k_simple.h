@@ -51,8 +51,8 @@ __device__ __forceinline__ float4 f4_zero() { return make_float4(0.f, 0.f, 0.f, 
 
 __device__ __forceinline__ void st_row4(void* y, int64_t e, int dt, float4 v) {
   if (dt == DT_BF16) {
-    const uint32_t w0 = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
-    const uint32_t w1 = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    const uint32_t w0 = f2bf2(v.x, v.y);
+    const uint32_t w1 = f2bf2(v.z, v.w);
     *(uint2*)((uint16_t*)y + e) = make_uint2(w0, w1);
   } else {
     *(float4*)((float*)y + e) = v;
@@ -719,8 +719,8 @@ __device__ __forceinline__ void ce_store(const CeArgs& a, int r, int i, int y, f
   for (int e = 0; e < 4; ++e) p[e] = (p[e] - (v0 + e == y ? 1.f : 0.f)) * a.inv_rows;
   const int64_t o = (int64_t)r * a.V + v0;
   if (a.dt == DT_BF16) {
-    const uint32_t w0 = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
-    const uint32_t w1 = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
+    const uint32_t w0 = f2bf2(p[0], p[1]);
+    const uint32_t w1 = f2bf2(p[2], p[3]);
     *(uint2*)((uint16_t*)a.dz + o) = make_uint2(w0, w1);
   } else {
     *(float4*)((float*)a.dz + o) = make_float4(p[0], p[1], p[2], p[3]);
@@ -771,8 +771,8 @@ __device__ __forceinline__ void ce_row_regs(const CeArgs& a, int r, int y, float
     for (int e = 0; e < 4; ++e) p[e] = (p[e] - (v0 + e == y ? 1.f : 0.f)) * a.inv_rows;
     const int64_t o = (int64_t)r * a.V + v0;
     if (a.dt == DT_BF16) {
-      const uint32_t w0 = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
-      const uint32_t w1 = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
+      const uint32_t w0 = f2bf2(p[0], p[1]);
+      const uint32_t w1 = f2bf2(p[2], p[3]);
       *(uint2*)((uint16_t*)a.dz + o) = make_uint2(w0, w1);
     } else {
       *(float4*)((float*)a.dz + o) = make_float4(p[0], p[1], p[2], p[3]);
@@ -1061,8 +1061,8 @@ __device__ void task_adamw(const AdamArgs& a, int tile, const TaskCtx& tc) {
     if (a.wc || pub) {
       const int64_t e = i0 + 4 * j;
       if (a.wc_dt == DT_BF16) {
-        const uint32_t w0 = (uint32_t)f2bf(p.x) | ((uint32_t)f2bf(p.y) << 16);
-        const uint32_t w1 = (uint32_t)f2bf(p.z) | ((uint32_t)f2bf(p.w) << 16);
+        const uint32_t w0 = f2bf2(p.x, p.y);
+        const uint32_t w1 = f2bf2(p.z, p.w);
         if (a.wc) *(uint2*)((uint16_t*)a.wc + e) = make_uint2(w0, w1);
         if (pub) *(uint2*)((uint16_t*)pub + e) = make_uint2(w0, w1);
       } else {

@@ -17,12 +17,14 @@ constexpr int kWaves = kThreads / kWave;
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// round to nearest even; NaN stays a (quiet) NaN
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, rounding to nearest even (NaN stays a quiet NaN): gfx950's
+// conversion instruction (v_cvt_pk_bf16_f32, two values per instruction)
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two values packed into one word, a in the low half
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  const bf16x2_v v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float ldf(const void* p, int64_t i, int dt) {
