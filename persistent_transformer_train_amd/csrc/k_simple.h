@@ -1026,54 +1026,76 @@ __device__ void task_emb_bwd(const EmbBwdArgs& a, int tile, const TaskCtx& tc) {
 // p <- p(1 - lr wd); m <- b1 m + (1-b1) g; v <- b2 v + (1-b2) g^2;
 // p <- p - lr (m/bc1) / (sqrt(v/bc2) + eps); compute copy <- p.
 
-__device__ __forceinline__ void adamw_one(float& p, float& m, float& v, float g, float decay, float lr, float bc1,
-                                          float bc2, const AdamArgs& a) {
+// ibc1, ibc2: the reciprocals of the bias corrections (one per step)
+__device__ __forceinline__ void adamw_one(float& p, float& m, float& v, float g, float decay, float lr, float ibc1,
+                                          float ibc2, const AdamArgs& a) {
   p *= decay;
   m = a.beta1 * m + (1.0f - a.beta1) * g;
   v = a.beta2 * v + (1.0f - a.beta2) * g * g;
-  p -= lr * (m / bc1) / (sqrtf(v / bc2) + a.eps);
+  p -= lr * (m * ibc1) / (sqrtf(v * ibc2) + a.eps);
 }
 
-// per_tile is a multiple of 1024 and n of 8 (checked on the host): float4 access,
-// the tail of the last tile element-wise
+// per_tile is a multiple of 1024 and n of 8 (checked on the host): float4
+// access, kAdamU groups per thread with every load issued before the
+// arithmetic (a streaming kernel needs many bytes in flight); the tail of the
+// last tile element-wise
+constexpr int kAdamU = 4;
 __device__ void task_adamw(const AdamArgs& a, int tile, const TaskCtx& tc) {
-  const float lr = tc.sc->lr, bc1 = tc.sc->bc1, bc2 = tc.sc->bc2;
+  const float lr = tc.sc->lr, ibc1 = 1.0f / tc.sc->bc1, ibc2 = 1.0f / tc.sc->bc2;
   const int64_t i0 = (int64_t)tile * a.per_tile;
   const int64_t i1 = min(i0 + (int64_t)a.per_tile, a.n);
   const float decay = 1.0f - lr * a.wd;
   const int64_t n4 = (i1 - i0) / 4;
   // co-resident mode: the serve slot of this step's version
   void* pub = a.pub ? (void*)((char*)a.pub + (int64_t)(tc.sc->tag & 1) * a.pub_slot_bytes) : nullptr;
-  float4* P = (float4*)(a.p + i0);
-  float4* M = (float4*)(a.m + i0);
-  float4* Vv = (float4*)(a.v + i0);
-  const float4* G = (const float4*)(a.g + i0);
-  for (int64_t j = threadIdx.x; j < n4; j += kThreads) {
-    float4 p = P[j], m = M[j], v = Vv[j];
-    const float4 g = G[j];
-    adamw_one(p.x, m.x, v.x, g.x, decay, lr, bc1, bc2, a);
-    adamw_one(p.y, m.y, v.y, g.y, decay, lr, bc1, bc2, a);
-    adamw_one(p.z, m.z, v.z, g.z, decay, lr, bc1, bc2, a);
-    adamw_one(p.w, m.w, v.w, g.w, decay, lr, bc1, bc2, a);
-    P[j] = p;
-    M[j] = m;
-    Vv[j] = v;
-    if (a.wc || pub) {
-      const int64_t e = i0 + 4 * j;
-      if (a.wc_dt == DT_BF16) {
-        const uint32_t w0 = f2bf2(p.x, p.y);
-        const uint32_t w1 = f2bf2(p.z, p.w);
-        if (a.wc) *(uint2*)((uint16_t*)a.wc + e) = make_uint2(w0, w1);
-        if (pub) *(uint2*)((uint16_t*)pub + e) = make_uint2(w0, w1);
-      } else {
-        if (a.wc) *(float4*)((float*)a.wc + e) = p;
-        if (pub) *(float4*)((float*)pub + e) = p;
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  f4v* P = (f4v*)(a.p + i0);
+  f4v* M = (f4v*)(a.m + i0);
+  f4v* Vv = (f4v*)(a.v + i0);
+  const f4v* G = (const f4v*)(a.g + i0);
+  for (int64_t j0 = threadIdx.x; j0 < n4; j0 += kAdamU * kThreads) {
+    f4v p[kAdamU], m[kAdamU], v[kAdamU], g[kAdamU];
+#pragma unroll
+    for (int u = 0; u < kAdamU; ++u) {
+      const int64_t j = j0 + (int64_t)u * kThreads;
+      if (j < n4) {
+        p[u] = P[j];
+        m[u] = M[j];
+        v[u] = Vv[j];
+        g[u] = G[j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kAdamU; ++u) {
+      const int64_t j = j0 + (int64_t)u * kThreads;
+      if (j >= n4) continue;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float pc = p[u][c], mc = m[u][c], vc = v[u][c];
+        adamw_one(pc, mc, vc, g[u][c], decay, lr, ibc1, ibc2, a);
+        p[u][c] = pc;
+        m[u][c] = mc;
+        v[u][c] = vc;
+      }
+      P[j] = p[u];
+      M[j] = m[u];
+      Vv[j] = v[u];
+      if (a.wc || pub) {
+        const int64_t e = i0 + 4 * j;
+        if (a.wc_dt == DT_BF16) {
+          const uint2 w = make_uint2(f2bf2(p[u][0], p[u][1]), f2bf2(p[u][2], p[u][3]));
+          if (a.wc) *(uint2*)((uint16_t*)a.wc + e) = w;
+          if (pub) *(uint2*)((uint16_t*)pub + e) = w;
+        } else {
+          if (a.wc) *(f4v*)((float*)a.wc + e) = p[u];
+          if (pub) *(f4v*)((float*)pub + e) = p[u];
+        }
       }
     }
   }
   for (int64_t i = i0 + 4 * n4 + threadIdx.x; i < i1; i += kThreads) {
     float p = a.p[i], m = a.m[i], v = a.v[i];
-    adamw_one(p, m, v, a.g[i], decay, lr, bc1, bc2, a);
+    adamw_one(p, m, v, a.g[i], decay, lr, ibc1, ibc2, a);
     a.p[i] = p;
     a.m[i] = m;
     a.v[i] = v;

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -277,6 +278,11 @@ struct ofa_handle {
   std::vector<Phase> dec;          // one decode position (with head)
   Phase* d_train = nullptr;        // device copies (inside the pinned-upload area)
   Phase* d_dec = nullptr;
+  // per-partition ticket tables (see PersistJob::part_tb): the training
+  // program split into kMaxParts partitions, and both programs unsplit
+  int32_t* d_train_pt = nullptr;
+  int32_t* d_train_pt1 = nullptr;
+  int32_t* d_dec_pt1 = nullptr;
   std::vector<char> phase_names;   // for phase_times
   std::vector<std::string> train_names;
   std::vector<std::string> dec_names;
@@ -415,6 +421,23 @@ void finish_program(std::vector<Phase>& prog, int max_tickets = kTicketsPerPhase
     tickets += ph.n_tickets;
     ph.lds_bytes = (int)phase_lds_bytes(ph);
   }
+}
+
+// per-partition first tickets of each phase (PersistJob::part_tb): partition
+// s of P owns a phase's tickets s, s + P, ...
+std::vector<int32_t> part_table(const std::vector<Phase>& prog, int P) {
+  const size_t n = prog.size();
+  std::vector<int32_t> t((size_t)P * (n + 1));
+  for (int s = 0; s < P; ++s) {
+    int32_t acc = 0;
+    for (size_t i = 0; i < n; ++i) {
+      t[s * (n + 1) + i] = acc;
+      const int T = prog[i].n_tickets;
+      acc += T > s ? (T - s + P - 1) / P : 0;
+    }
+    t[s * (n + 1) + n] = acc;
+  }
+  return t;
 }
 
 void build_train(ofa_handle* h) {
@@ -562,6 +585,7 @@ void build_train(ofa_handle* h) {
       p_pre_attn = p;
     }
     int p_att = b.add(OP_ATTN_FWD, attn_tiles, "attn_fwd", {p_pre_attn});
+    b[p_att].per_ticket = 1;   // causal tiles differ in work: one per ticket, largest first
     b[p_att].a.attn = attn_args(l);
     g = gemm(h, (int)BT, (int)d, (int)d, O(l), d, 1, lp, wc(lo.w_o), d, 1, lp, X(2 * l + 1), d, DT_F32, EPI_RESID);
     g.bias = pf(lo.b_o);
@@ -737,8 +761,10 @@ void build_train(ofa_handle* h) {
     b[p_prep].a.attn = attn_args(l);
     b[p_prep].a.attn.block = 16;
     int p_kv = b.add(OP_ATTN_BWD_KV, attn_tiles, "attn_bwd_kv", {p_prep});
+    b[p_kv].per_ticket = 1;
     b[p_kv].a.attn = attn_args(l);
     int p_q = b.add(OP_ATTN_BWD_Q, attn_tiles, "attn_bwd_q", {p_prep});
+    b[p_q].per_ticket = 1;
     b[p_q].a.attn = attn_args(l);
     int p_dqkv = p_q;
     if (c.n_pos == 0) {
@@ -1067,6 +1093,7 @@ ofa_status reset_sched(ofa_handle* h, size_t sched_off, int n_phases) {
   HIP_TRY(h, launch_fill_u64(&sc->base, base, 1, h->stream));
   HIP_TRY(h, launch_fill_u64(&sc->abort, 0, 3, h->stream));   // abort, exited, stop
   HIP_TRY(h, launch_fill_u64(&sc->limit, ~0ull, 1, h->stream));
+  HIP_TRY(h, launch_fill_u64(sc->part_ticket, base, kMaxParts * kPartStride, h->stream));
   HIP_TRY(h, launch_fill_u64(sc->done, base, n_phases, h->stream));
   return OFA_OK;
 }
@@ -1078,6 +1105,15 @@ PersistJob make_job(ofa_handle* h, const std::vector<Phase>& prog, const Phase* 
   j.phases = d_prog;
   j.n_phases = (int)prog.size();
   j.tickets_per_inst = prog.back().ticket_base + prog.back().n_tickets;
+  // training claims tickets per die (eight partitions: 32 workgroups per
+  // counter instead of 256); decode keeps one counter
+  if (&prog == &h->train && n_wg >= kMaxParts) {
+    j.n_parts = kMaxParts;
+    j.part_tb = h->d_train_pt;
+  } else {
+    j.n_parts = 1;
+    j.part_tb = &prog == &h->train ? h->d_train_pt1 : h->d_dec_pt1;
+  }
   j.n_inst = n_inst;
   j.steps = d_ctx;
   j.period = n_inst;
@@ -1268,12 +1304,20 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
     for (const Phase& ph : h->train)
       if (phase_lds_bytes_occ(ph, 2) > persistent_lds_bytes(2)) h->train_occ = 1;   // one per CU after all
   // phase tables live in a small library-owned device buffer
-  size_t tbytes = (h->train.size() + h->dec.size()) * sizeof(Phase);
+  const std::vector<int32_t> pt = part_table(h->train, kMaxParts), pt1 = part_table(h->train, 1),
+                             dpt1 = part_table(h->dec, 1);
+  size_t tbytes = (h->train.size() + h->dec.size()) * sizeof(Phase) + (pt.size() + pt1.size() + dpt1.size()) * 4;
   HIP_TRY(h, hipMalloc(&h->d_alloc, tbytes));
   h->d_train = (Phase*)h->d_alloc;
   h->d_dec = h->d_train + h->train.size();
+  h->d_train_pt = (int32_t*)(h->d_dec + h->dec.size());
+  h->d_train_pt1 = h->d_train_pt + pt.size();
+  h->d_dec_pt1 = h->d_train_pt1 + pt1.size();
   HIP_TRY(h, hipMemcpy(h->d_train, h->train.data(), h->train.size() * sizeof(Phase), hipMemcpyHostToDevice));
   HIP_TRY(h, hipMemcpy(h->d_dec, h->dec.data(), h->dec.size() * sizeof(Phase), hipMemcpyHostToDevice));
+  HIP_TRY(h, hipMemcpy(h->d_train_pt, pt.data(), pt.size() * 4, hipMemcpyHostToDevice));
+  HIP_TRY(h, hipMemcpy(h->d_train_pt1, pt1.data(), pt1.size() * 4, hipMemcpyHostToDevice));
+  HIP_TRY(h, hipMemcpy(h->d_dec_pt1, dpt1.data(), dpt1.size() * 4, hipMemcpyHostToDevice));
   // state
   char* ws = h->ws;
   const Carve& w = h->cw;
@@ -1585,9 +1629,10 @@ ofa_status ofa_status_sync(ofa_handle* h, ofa_stats* out) {
     out->err_phase = ds.code ? ds.phase : -1;
     out->err_step = ds.step;
     out->err_info = ds.info;
-    Sched sc;
-    HIP_TRY(h, hipMemcpy(&sc, h->ws + h->cw.sched, 32, hipMemcpyDeviceToHost));
-    out->tickets_claimed = sc.ticket - h->cfg.debug_counter_base;
+    uint64_t pt[kMaxParts * kPartStride];
+    HIP_TRY(h, hipMemcpy(pt, h->ws + h->cw.sched + offsetof(Sched, part_ticket), sizeof pt, hipMemcpyDeviceToHost));
+    out->tickets_claimed = 0;
+    for (int i = 0; i < kMaxParts; ++i) out->tickets_claimed += pt[i * kPartStride] - h->cfg.debug_counter_base;
     out->steps_done = h->steps_done;
     out->version = h->version;
     out->last_call_ms = h->last_ms;

@@ -192,30 +192,36 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
   const int ji = (p.n_jobs > 1 && (int)blockIdx.x >= p.job[0].n_wg) ? 1 : 0;
   const PersistJob& J = p.job[ji];
   const uint64_t base = J.sched->base;
-  const uint64_t total = (uint64_t)J.n_inst * (uint64_t)J.tickets_per_inst;
+  // this workgroup's ticket partition: its counter, and its first ticket of each phase
+  const int part = (int)(blockIdx.x % (unsigned)J.n_parts);
+  uint64_t* part_ctr = &J.sched->part_ticket[part * kPartStride];
+  const int32_t* ptb = J.part_tb + part * (J.n_phases + 1);
+  const int tpi = ptb[J.n_phases];   // this partition's tickets per instance
+  const uint64_t total = (uint64_t)J.n_inst * (uint64_t)tpi;
   if (threadIdx.x == 0) {
     s_all_checked = -1;
     s_stop = 0;
   }
   for (int i = threadIdx.x; i < J.n_phases; i += kThreads) {
-    s_tb[i] = J.phases[i].ticket_base;
+    s_tb[i] = ptb[i];
     s_known[i] = -1;
   }
   __syncthreads();
   int pi = 0;   // phase of the previous ticket (tickets only grow, so the search starts there)
   for (;;) {
-    if (threadIdx.x == 0) s_ticket = add_relaxed(&J.sched->ticket, 1) - base;
+    if (threadIdx.x == 0) s_ticket = add_relaxed(part_ctr, 1) - base;
     __syncthreads();
     // wave-uniform copy, so the phase table is read with scalar loads
     const uint64_t t = readfirstlane_u64(s_ticket);
     if (t >= total) break;
-    const int64_t inst = (int64_t)(t / (uint64_t)J.tickets_per_inst);
-    const int r = (int)(t % (uint64_t)J.tickets_per_inst);
-    // phase owning ticket r: last phase whose first ticket <= r
+    const int64_t inst = (int64_t)(t / (uint64_t)tpi);
+    const int r = (int)(t % (uint64_t)tpi);
+    // phase owning the partition's ticket r: last phase whose first ticket
+    // <= r (a phase with fewer tickets than partitions may have none here)
     if (s_tb[pi] > r) pi = 0;   // a later instance starts over
     while (pi + 1 < J.n_phases && s_tb[pi + 1] <= r) ++pi;
     const Phase& ph = J.phases[pi];
-    const int j = r - ph.ticket_base;
+    const int j = (r - s_tb[pi]) * J.n_parts + part;   // the phase's ticket
     int tile0 = j * ph.per_ticket;
     const int tile1 = min(tile0 + ph.per_ticket, ph.n_tiles);
     const int64_t period_idx = inst / J.period;

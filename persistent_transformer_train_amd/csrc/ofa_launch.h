@@ -12,6 +12,14 @@ struct PersistJob {
   const Phase* phases;       // one program instance's phase table
   int32_t n_phases;
   int32_t tickets_per_inst;  // sum of n_tickets over the phases
+  // Tickets are claimed per partition: workgroup b belongs to partition
+  // b % n_parts (its die when n_parts is 8) and claims from that partition's
+  // counter.  Partition s owns tickets s, s + n_parts, s + 2 n_parts, ... of
+  // every phase; part_tb[s (n_phases + 1) + i] is the partition's first ticket
+  // of phase i inside one instance, and [s (n_phases + 1) + n_phases] its
+  // tickets per instance.  Every partition has at least one workgroup.
+  const int32_t* part_tb;
+  int32_t n_parts;
   int64_t n_inst;            // instances to run (open-ended jobs: a bound no run reaches)
   const StepCtx* steps;      // instance i runs steps[i % period]
   int64_t period;

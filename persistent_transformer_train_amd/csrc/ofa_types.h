@@ -313,8 +313,11 @@ struct StepCtx {
 
 constexpr int kMaxPhases = 512;
 
+constexpr int kMaxParts = 8;        // ticket partitions of a job (one per die)
+constexpr int kPartStride = 16;     // uint64 words between partition counters (one 128-byte line each)
+
 struct Sched {                       // persistent-kernel scheduler block of one job (device)
-  uint64_t ticket;                   // next ticket to hand out
+  uint64_t ticket;                   // unused (each partition has its own counter below)
   uint64_t base;                     // debug counter base (added to every counter)
   uint64_t abort;                    // non-zero: every role stops (the first job's word is shared)
   uint64_t exited;                   // workgroups that left the loop
@@ -322,6 +325,7 @@ struct Sched {                       // persistent-kernel scheduler block of one
   uint64_t limit;                    // open-ended job: instances >= limit are not run (~0 = none yet)
   uint64_t pad[2];
   uint64_t done[kMaxPhases];         // completed tiles per phase, summed over instances
+  uint64_t part_ticket[kMaxParts * kPartStride];   // next ticket of partition s at [s * kPartStride]
 };
 
 struct DevStatus {
