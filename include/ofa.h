@@ -95,6 +95,7 @@ typedef struct {
 #define OFA_DEBUG_TILE256         8  /* every matrix-core GEMM takes the 256-row tile (normally only large ones) */
 #define OFA_DEBUG_OCC2           16  /* step-mode persistent training with two workgroups per CU (measured slower at c3) */
 #define OFA_DEBUG_PLAIN_TILES    32  /* GEMM tiles in plain row / column order, not placed by die (for comparison) */
+#define OFA_DEBUG_WG_RELEASE     64  /* persistent training: every workgroup writes its die's L2 back after each ticket */
 
 /* Size in bytes of the device workspace ofa_create() needs for cfg; 0 if cfg is
  * invalid (ofa_validate_config() says why). */

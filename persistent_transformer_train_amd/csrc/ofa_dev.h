@@ -204,6 +204,16 @@ __device__ __forceinline__ void fence_acquire_agent() {
 __device__ __forceinline__ void fence_release_agent() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 }
+// orders this workgroup's earlier stores (complete in its die's L2) before its later atomics
+__device__ __forceinline__ void fence_release_workgroup() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+}
+// the accelerator die (XCD) this wave runs on
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
+}
 
 __device__ __forceinline__ uint64_t now_ticks() { return wall_clock64(); }
 

@@ -283,6 +283,7 @@ struct ofa_handle {
   int32_t* d_train_pt = nullptr;
   int32_t* d_train_pt1 = nullptr;
   int32_t* d_dec_pt1 = nullptr;
+  int32_t* d_train_ptiles = nullptr;   // tiles per partition and phase of the training program
   std::vector<char> phase_names;   // for phase_times
   std::vector<std::string> train_names;
   std::vector<std::string> dec_names;
@@ -421,6 +422,16 @@ void finish_program(std::vector<Phase>& prog, int max_tickets = kTicketsPerPhase
     tickets += ph.n_tickets;
     ph.lds_bytes = (int)phase_lds_bytes(ph);
   }
+}
+
+// tiles of each phase owned by each of P partitions (PersistJob::part_tiles)
+std::vector<int32_t> part_tile_table(const std::vector<Phase>& prog, int P) {
+  const size_t n = prog.size();
+  std::vector<int32_t> t((size_t)P * n, 0);
+  for (size_t i = 0; i < n; ++i)
+    for (int j = 0; j < prog[i].n_tickets; ++j)
+      t[(j % P) * n + i] += std::min(prog[i].per_ticket, prog[i].n_tiles - j * prog[i].per_ticket);
+  return t;
 }
 
 // per-partition first tickets of each phase (PersistJob::part_tb): partition
@@ -1094,6 +1105,7 @@ ofa_status reset_sched(ofa_handle* h, size_t sched_off, int n_phases) {
   HIP_TRY(h, launch_fill_u64(&sc->abort, 0, 3, h->stream));   // abort, exited, stop
   HIP_TRY(h, launch_fill_u64(&sc->limit, ~0ull, 1, h->stream));
   HIP_TRY(h, launch_fill_u64(sc->part_ticket, base, kMaxParts * kPartStride, h->stream));
+  HIP_TRY(h, launch_fill_u64(sc->part_done, base, (int64_t)n_phases * kMaxParts, h->stream));
   HIP_TRY(h, launch_fill_u64(sc->done, base, n_phases, h->stream));
   return OFA_OK;
 }
@@ -1110,6 +1122,10 @@ PersistJob make_job(ofa_handle* h, const std::vector<Phase>& prog, const Phase* 
   if (&prog == &h->train && n_wg >= kMaxParts) {
     j.n_parts = kMaxParts;
     j.part_tb = h->d_train_pt;
+    // the hardware hands workgroup b to die b % 8, so partition s is die s
+    // (each workgroup checks this on the device)
+    j.die_release = (h->cfg.debug_flags & OFA_DEBUG_WG_RELEASE) ? 0 : 1;
+    j.part_tiles = h->d_train_ptiles;
   } else {
     j.n_parts = 1;
     j.part_tb = &prog == &h->train ? h->d_train_pt1 : h->d_dec_pt1;
@@ -1305,19 +1321,22 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
       if (phase_lds_bytes_occ(ph, 2) > persistent_lds_bytes(2)) h->train_occ = 1;   // one per CU after all
   // phase tables live in a small library-owned device buffer
   const std::vector<int32_t> pt = part_table(h->train, kMaxParts), pt1 = part_table(h->train, 1),
-                             dpt1 = part_table(h->dec, 1);
-  size_t tbytes = (h->train.size() + h->dec.size()) * sizeof(Phase) + (pt.size() + pt1.size() + dpt1.size()) * 4;
+                             dpt1 = part_table(h->dec, 1), ptl = part_tile_table(h->train, kMaxParts);
+  size_t tbytes = (h->train.size() + h->dec.size()) * sizeof(Phase) +
+                  (pt.size() + pt1.size() + dpt1.size() + ptl.size()) * 4;
   HIP_TRY(h, hipMalloc(&h->d_alloc, tbytes));
   h->d_train = (Phase*)h->d_alloc;
   h->d_dec = h->d_train + h->train.size();
   h->d_train_pt = (int32_t*)(h->d_dec + h->dec.size());
   h->d_train_pt1 = h->d_train_pt + pt.size();
   h->d_dec_pt1 = h->d_train_pt1 + pt1.size();
+  h->d_train_ptiles = h->d_dec_pt1 + dpt1.size();
   HIP_TRY(h, hipMemcpy(h->d_train, h->train.data(), h->train.size() * sizeof(Phase), hipMemcpyHostToDevice));
   HIP_TRY(h, hipMemcpy(h->d_dec, h->dec.data(), h->dec.size() * sizeof(Phase), hipMemcpyHostToDevice));
   HIP_TRY(h, hipMemcpy(h->d_train_pt, pt.data(), pt.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(h, hipMemcpy(h->d_train_pt1, pt1.data(), pt1.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(h, hipMemcpy(h->d_dec_pt1, dpt1.data(), dpt1.size() * 4, hipMemcpyHostToDevice));
+  HIP_TRY(h, hipMemcpy(h->d_train_ptiles, ptl.data(), ptl.size() * 4, hipMemcpyHostToDevice));
   // state
   char* ws = h->ws;
   const Carve& w = h->cw;

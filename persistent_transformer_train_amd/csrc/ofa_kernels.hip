@@ -201,6 +201,11 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
   if (threadIdx.x == 0) {
     s_all_checked = -1;
     s_stop = 0;
+    // the once-per-die release relies on partition == die; a workgroup elsewhere stops the run
+    if (J.die_release && xcc_id() != (uint32_t)part) {
+      raise_status(p.status, -2 /*OFA_E_HIP*/, -1, 0, (int64_t)xcc_id());
+      st_release(p.abort, 1);
+    }
   }
   for (int i = threadIdx.x; i < J.n_phases; i += kThreads) {
     s_tb[i] = ptb[i];
@@ -314,8 +319,20 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
     if (threadIdx.x == 0) {
       if (J.trace && inst < J.trace_inst)
         atomicMax((unsigned long long*)&J.trace[4 * (inst * J.n_phases + pi) + 2], (unsigned long long)now_ticks());
-      fence_release_agent();
-      add_relaxed(&J.sched->done[pi], (uint64_t)(tile1 - tile0));
+      if (J.die_release) {
+        // this die's share of the phase completes with this ticket: one
+        // write-back of the die's L2 covers every workgroup of the die
+        fence_release_workgroup();
+        const uint64_t share = (uint64_t)J.part_tiles[part * J.n_phases + pi];
+        const uint64_t prev = add_relaxed(&J.sched->part_done[pi * kMaxParts + part], (uint64_t)(tile1 - tile0));
+        if (prev + (uint64_t)(tile1 - tile0) - base == (uint64_t)(inst + 1) * share) {
+          fence_release_agent();
+          add_relaxed(&J.sched->done[pi], share);
+        }
+      } else {
+        fence_release_agent();
+        add_relaxed(&J.sched->done[pi], (uint64_t)(tile1 - tile0));
+      }
       if (J.times) {
         atomicMin((unsigned long long*)&J.times[pi].t0, (unsigned long long)t0);
         atomicMax((unsigned long long*)&J.times[pi].t1, (unsigned long long)now_ticks());

@@ -20,6 +20,13 @@ struct PersistJob {
   // tickets per instance.  Every partition has at least one workgroup.
   const int32_t* part_tb;
   int32_t n_parts;
+  // Release once per die and phase (n_parts == 8, partition s = die s): each
+  // workgroup's stores reach its die's L2, it counts its tiles in
+  // sched->part_done, and the workgroup completing the die's share
+  // (part_tiles[s n_phases + i] tiles of phase i per instance) writes that
+  // L2 back and moves the phase counter by the whole share.
+  int32_t die_release;
+  const int32_t* part_tiles;
   int64_t n_inst;            // instances to run (open-ended jobs: a bound no run reaches)
   const StepCtx* steps;      // instance i runs steps[i % period]
   int64_t period;

@@ -326,6 +326,7 @@ struct Sched {                       // persistent-kernel scheduler block of one
   uint64_t pad[2];
   uint64_t done[kMaxPhases];         // completed tiles per phase, summed over instances
   uint64_t part_ticket[kMaxParts * kPartStride];   // next ticket of partition s at [s * kPartStride]
+  uint64_t part_done[kMaxPhases * kMaxParts];      // tiles of phase i done by partition s at [i * kMaxParts + s]
 };
 
 struct DevStatus {

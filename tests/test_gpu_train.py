@@ -215,6 +215,21 @@ def test_die_aware_tile_placement_bitwise_equal_to_plain(exec_mode):
     h2.close()
 
 
+def test_release_per_workgroup_bitwise_equal_to_per_die():
+    """The persistent executor's once-per-die L2 write-back (default) and a
+    write-back after every ticket (OFA_DEBUG_WG_RELEASE) publish the same
+    data: losses and weights bit-identical on m3b."""
+    from persistent_transformer_train_amd import ofa
+    h1, *_, g1 = gpu_run("m3b", 3, PERSISTENT)
+    p1 = h1.get_params().cpu().numpy()
+    h2, *_, g2 = gpu_run("m3b", 3, PERSISTENT, debug_flags=ofa.OFA_DEBUG_WG_RELEASE)
+    p2 = h2.get_params().cpu().numpy()
+    assert g1.tobytes() == g2.tobytes()
+    assert p1.tobytes() == p2.tobytes()
+    h1.close()
+    h2.close()
+
+
 def test_persistent_equals_per_phase_bitwise():
     h1, *_, g1 = gpu_run("m2", 3, PERSISTENT)
     p1 = h1.get_params().cpu().numpy()
