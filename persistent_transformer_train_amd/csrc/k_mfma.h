@@ -310,6 +310,10 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
       p3_load<AKM, BM>(A, g.lda, m0, g.M, q * kP3BK, g.K, ring_a + q * SA, w, lane);
       p3_load<BKM, kMBN>(B, g.ldb, n0, g.N, q * kP3BK, g.K, ring_b + q * SB, w, lane);
     }
+  // copy instructions per wave for one slice, and how many go between the
+  // MFMAs of each 16-wide k step (all of them are issued within the slice)
+  constexpr int NQA = BM / 32, NQB = kMBN / 32, NC = NQA + NQB, CPK = (NC + 3) / 4;
+  static_assert(CPK <= WMB * 2, "a k step has room for its copies");
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
     // Slice kt landed in every wave (the copies of the up to STAGES-2 slices
@@ -321,29 +325,42 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
     else if (kP3Stages > 2 && kt + 1 < nk) p3_wait_barrier<PER_SLICE>();
     else p3_wait_barrier<0>();
     const int ahead = kt + kP3Stages - 1;
-    if (ahead < nk) {
-      const int buf = cur == 0 ? kP3Stages - 1 : cur - 1;
-      p3_load<AKM, BM>(A, g.lda, m0, g.M, ahead * kP3BK, g.K, ring_a + buf * SA, w, lane);
-      p3_load<BKM, kMBN>(B, g.ldb, n0, g.N, ahead * kP3BK, g.K, ring_b + buf * SB, w, lane);
+    const int buf = cur == 0 ? kP3Stages - 1 : cur - 1;
+    // a whole slice ahead is copied between the MFMAs below; a partial one now
+    const bool copy_ahead = ahead < nk && (ahead + 1) * kP3BK <= g.K;
+    if (ahead < nk && !copy_ahead) {
+      p3_fill_tail<AKM, BM>(A, g.lda, m0, g.M, ahead * kP3BK, g.K, ring_a + buf * SA, w, lane);
+      p3_fill_tail<BKM, kMBN>(B, g.ldb, n0, g.N, ahead * kP3BK, g.K, ring_b + buf * SB, w, lane);
     }
     const uint16_t* sa = ring_a + cur * SA;
     const uint16_t* sb = ring_b + cur * SB;
-#pragma unroll
-    for (int kk = 0; kk < kP3BK / 16; ++kk) {
-      bf16x8_t af[WMB], bfr[2];
+    // fragments double-buffered: step kk+1's LDS reads go out before step kk's MFMAs
+    bf16x8_t af[2][WMB], bfr[2][2];
+    auto frags = [&](int kk, int slot) {
 #pragma unroll
       for (int i = 0; i < WMB; ++i)
-        af[i] = AKM ? p3_frag_k(sa, wm + i * 32 + (lane & 31), 2 * kk + (lane >> 5))
-                    : p3_frag_t<BM>(sa, wm + i * 32, kk, lane);
+        af[slot][i] = AKM ? p3_frag_k(sa, wm + i * 32 + (lane & 31), 2 * kk + (lane >> 5))
+                          : p3_frag_t<BM>(sa, wm + i * 32, kk, lane);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bfr[j] = BKM ? p3_frag_k(sb, wn + j * 32 + (lane & 31), 2 * kk + (lane >> 5))
-                     : p3_frag_t<kMBN>(sb, wn + j * 32, kk, lane);
+        bfr[slot][j] = BKM ? p3_frag_k(sb, wn + j * 32 + (lane & 31), 2 * kk + (lane >> 5))
+                           : p3_frag_t<kMBN>(sb, wn + j * 32, kk, lane);
+    };
+    frags(0, 0);
 #pragma unroll
-      for (int i = 0; i < WMB; ++i)
+    for (int kk = 0; kk < kP3BK / 16; ++kk) {
+      const int s0 = kk & 1;
+      if (kk + 1 < kP3BK / 16) frags(kk + 1, s0 ^ 1);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      for (int m = 0; m < WMB * 2; ++m) {
+        const int i = m >> 1, j = m & 1;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s0][j], af[s0][i], acc[i][j], 0, 0, 0);
+        const int c = kk * CPK + m;
+        if (copy_ahead && m < CPK && c < NC) {
+          if (c < NQA) p3_issue<AKM, BM, 1>(A, g.lda, m0, g.M, ahead * kP3BK, ring_a + buf * SA, w, lane, c);
+          else p3_issue<BKM, kMBN, 1>(B, g.ldb, n0, g.N, ahead * kP3BK, ring_b + buf * SB, w, lane, c - NQA);
+        }
+      }
     }
     cur = cur + 1 == kP3Stages ? 0 : cur + 1;
   }
