@@ -284,6 +284,8 @@ struct ofa_handle {
   int32_t* d_train_pt1 = nullptr;
   int32_t* d_dec_pt1 = nullptr;
   int32_t* d_train_ptiles = nullptr;   // tiles per partition and phase of the training program
+  int32_t* d_dec_pt = nullptr;         // the decode program's, split into kMaxParts partitions
+  int32_t* d_dec_ptiles = nullptr;
   std::vector<char> phase_names;   // for phase_times
   std::vector<std::string> train_names;
   std::vector<std::string> dec_names;
@@ -1111,24 +1113,27 @@ ofa_status reset_sched(ofa_handle* h, size_t sched_off, int n_phases) {
 }
 
 PersistJob make_job(ofa_handle* h, const std::vector<Phase>& prog, const Phase* d_prog, const StepCtx* d_ctx,
-                    int64_t n_inst, size_t sched_off, PhaseTime* times, uint64_t* inst_end, int n_wg) {
+                    int64_t n_inst, size_t sched_off, PhaseTime* times, uint64_t* inst_end, int n_wg,
+                    bool open_ended = false) {
   PersistJob j;
   memset(&j, 0, sizeof j);
   j.phases = d_prog;
   j.n_phases = (int)prog.size();
   j.tickets_per_inst = prog.back().ticket_base + prog.back().n_tickets;
-  // training claims tickets per die (eight partitions: 32 workgroups per
-  // counter instead of 256); decode keeps one counter
-  if (&prog == &h->train && n_wg >= kMaxParts) {
+  // tickets are claimed per die (eight partitions: 32 workgroups per counter
+  // instead of 256 for training); an open-ended job (co-resident decode, whose
+  // stopping rule needs one counter) or a grid under eight keeps one
+  const bool tr = &prog == &h->train;
+  if (n_wg >= kMaxParts && !open_ended) {
     j.n_parts = kMaxParts;
-    j.part_tb = h->d_train_pt;
+    j.part_tb = tr ? h->d_train_pt : h->d_dec_pt;
     // the hardware hands workgroup b to die b % 8, so partition s is die s
     // (each workgroup checks this on the device)
     j.die_release = (h->cfg.debug_flags & OFA_DEBUG_WG_RELEASE) ? 0 : 1;
-    j.part_tiles = h->d_train_ptiles;
+    j.part_tiles = tr ? h->d_train_ptiles : h->d_dec_ptiles;
   } else {
     j.n_parts = 1;
-    j.part_tb = &prog == &h->train ? h->d_train_pt1 : h->d_dec_pt1;
+    j.part_tb = tr ? h->d_train_pt1 : h->d_dec_pt1;
   }
   j.n_inst = n_inst;
   j.steps = d_ctx;
@@ -1321,9 +1326,10 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
       if (phase_lds_bytes_occ(ph, 2) > persistent_lds_bytes(2)) h->train_occ = 1;   // one per CU after all
   // phase tables live in a small library-owned device buffer
   const std::vector<int32_t> pt = part_table(h->train, kMaxParts), pt1 = part_table(h->train, 1),
-                             dpt1 = part_table(h->dec, 1), ptl = part_tile_table(h->train, kMaxParts);
+                             dpt1 = part_table(h->dec, 1), ptl = part_tile_table(h->train, kMaxParts),
+                             dpt = part_table(h->dec, kMaxParts), dptl = part_tile_table(h->dec, kMaxParts);
   size_t tbytes = (h->train.size() + h->dec.size()) * sizeof(Phase) +
-                  (pt.size() + pt1.size() + dpt1.size() + ptl.size()) * 4;
+                  (pt.size() + pt1.size() + dpt1.size() + ptl.size() + dpt.size() + dptl.size()) * 4;
   HIP_TRY(h, hipMalloc(&h->d_alloc, tbytes));
   h->d_train = (Phase*)h->d_alloc;
   h->d_dec = h->d_train + h->train.size();
@@ -1331,12 +1337,16 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
   h->d_train_pt1 = h->d_train_pt + pt.size();
   h->d_dec_pt1 = h->d_train_pt1 + pt1.size();
   h->d_train_ptiles = h->d_dec_pt1 + dpt1.size();
+  h->d_dec_pt = h->d_train_ptiles + ptl.size();
+  h->d_dec_ptiles = h->d_dec_pt + dpt.size();
   HIP_TRY(h, hipMemcpy(h->d_train, h->train.data(), h->train.size() * sizeof(Phase), hipMemcpyHostToDevice));
   HIP_TRY(h, hipMemcpy(h->d_dec, h->dec.data(), h->dec.size() * sizeof(Phase), hipMemcpyHostToDevice));
   HIP_TRY(h, hipMemcpy(h->d_train_pt, pt.data(), pt.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(h, hipMemcpy(h->d_train_pt1, pt1.data(), pt1.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(h, hipMemcpy(h->d_dec_pt1, dpt1.data(), dpt1.size() * 4, hipMemcpyHostToDevice));
   HIP_TRY(h, hipMemcpy(h->d_train_ptiles, ptl.data(), ptl.size() * 4, hipMemcpyHostToDevice));
+  HIP_TRY(h, hipMemcpy(h->d_dec_pt, dpt.data(), dpt.size() * 4, hipMemcpyHostToDevice));
+  HIP_TRY(h, hipMemcpy(h->d_dec_ptiles, dptl.data(), dptl.size() * 4, hipMemcpyHostToDevice));
   // state
   char* ws = h->ws;
   const Carve& w = h->cw;
@@ -1606,7 +1616,8 @@ ofa_status ofa_train_and_serve(ofa_handle* h, const int32_t* dev_tokens, int32_t
   if (s != OFA_OK) return s;
   PersistJob jobs[2];
   // job 0: decode on the serve workgroups, open-ended, stopped by training's end
-  jobs[0] = make_job(h, h->dec, h->d_dec, d_dsteps, (int64_t)1 << 40, w.dsched, dtm, nullptr, c.serve_cus * occ);
+  jobs[0] = make_job(h, h->dec, h->d_dec, d_dsteps, (int64_t)1 << 40, w.dsched, dtm, nullptr, c.serve_cus * occ,
+                     true);
   jobs[0].period = period;
   jobs[0].gen_per_period = per_gen;
   jobs[0].open_ended = 1;
