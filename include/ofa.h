@@ -55,7 +55,8 @@ typedef struct ofa_handle ofa_handle;   /* opaque, owned by the library */
 typedef enum {
   OFA_OK = 0,
   OFA_E_ARG = -1,        /* invalid argument or configuration */
-  OFA_E_HIP = -2,        /* a HIP runtime call failed (code kept in the handle) */
+  OFA_E_HIP = -2,        /* a HIP runtime call failed (code kept in the handle), or a persistent
+                            workgroup ran on another die than its ticket partition assumes */
   OFA_E_NONFINITE = -3,  /* a step produced a non-finite loss */
   OFA_E_TIMEOUT = -4,    /* a device-side wait exceeded its watchdog deadline */
   OFA_E_OVERFLOW = -5,   /* a requested budget does not fit its counters */
@@ -95,7 +96,7 @@ typedef struct {
 #define OFA_DEBUG_TILE256         8  /* every matrix-core GEMM takes the 256-row tile (normally only large ones) */
 #define OFA_DEBUG_OCC2           16  /* step-mode persistent training with two workgroups per CU (measured slower at c3) */
 #define OFA_DEBUG_PLAIN_TILES    32  /* GEMM tiles in plain row / column order, not placed by die (for comparison) */
-#define OFA_DEBUG_WG_RELEASE     64  /* persistent training: every workgroup writes its die's L2 back after each ticket */
+#define OFA_DEBUG_WG_RELEASE     64  /* persistent launches: every workgroup writes its die's L2 back after each ticket */
 
 /* Size in bytes of the device workspace ofa_create() needs for cfg; 0 if cfg is
  * invalid (ofa_validate_config() says why). */
