@@ -1049,20 +1049,22 @@ __device__ void task_adamw(const AdamArgs& a, int tile, const TaskCtx& tc) {
   // co-resident mode: the serve slot of this step's version
   void* pub = a.pub ? (void*)((char*)a.pub + (int64_t)(tc.sc->tag & 1) * a.pub_slot_bytes) : nullptr;
   typedef float f4v __attribute__((ext_vector_type(4)));
-  f4v* P = (f4v*)(a.p + i0);
-  f4v* M = (f4v*)(a.m + i0);
-  f4v* Vv = (f4v*)(a.v + i0);
-  const f4v* G = (const f4v*)(a.g + i0);
+  typedef __attribute__((address_space(1))) f4v gf4v;   // global memory: plain global (not flat) accesses
+  gf4v* P = (gf4v*)(a.p + i0);
+  gf4v* M = (gf4v*)(a.m + i0);
+  gf4v* Vv = (gf4v*)(a.v + i0);
+  const gf4v* G = (const gf4v*)(a.g + i0);
   for (int64_t j0 = threadIdx.x; j0 < n4; j0 += kAdamU * kThreads) {
     f4v p[kAdamU], m[kAdamU], v[kAdamU], g[kAdamU];
 #pragma unroll
     for (int u = 0; u < kAdamU; ++u) {
       const int64_t j = j0 + (int64_t)u * kThreads;
       if (j < n4) {
-        p[u] = P[j];
-        m[u] = M[j];
-        v[u] = Vv[j];
-        g[u] = G[j];
+        // every byte is touched once per step: non-temporal (streaming) accesses
+        p[u] = __builtin_nontemporal_load(P + j);
+        m[u] = __builtin_nontemporal_load(M + j);
+        v[u] = __builtin_nontemporal_load(Vv + j);
+        g[u] = __builtin_nontemporal_load(G + j);
       }
     }
 #pragma unroll
@@ -1077,9 +1079,9 @@ __device__ void task_adamw(const AdamArgs& a, int tile, const TaskCtx& tc) {
         m[u][c] = mc;
         v[u][c] = vc;
       }
-      P[j] = p[u];
-      M[j] = m[u];
-      Vv[j] = v[u];
+      __builtin_nontemporal_store(p[u], P + j);
+      __builtin_nontemporal_store(m[u], M + j);
+      __builtin_nontemporal_store(v[u], Vv + j);
       if (a.wc || pub) {
         const int64_t e = i0 + 4 * j;
         if (a.wc_dt == DT_BF16) {
