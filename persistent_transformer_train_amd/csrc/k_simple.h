@@ -735,15 +735,21 @@ __device__ __forceinline__ float exp_shift(float x, float ml2) {
 
 // The row stays in registers: softmax numerators overwrite the logits, so each
 // element takes one exponential.
+// the logits are read once and d logits written once: non-temporal global accesses
+typedef float ce_f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t ce_u2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) ce_f4 ce_gf4;
+typedef __attribute__((address_space(1))) ce_u2 ce_gu2;
+
 template <int NR>
 __device__ __forceinline__ void ce_row_regs(const CeArgs& a, int r, int y, float* red) {
-  const float4* __restrict__ z4 = (const float4*)(a.logits + (int64_t)r * a.V);
+  const ce_gf4* z4 = (const ce_gf4*)(a.logits + (int64_t)r * a.V);
   const int n4 = a.V / 4;
-  float4 v[NR];
+  ce_f4 v[NR];
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
     const int i = threadIdx.x + u * kThreads;
-    v[u] = i < n4 ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    v[u] = i < n4 ? __builtin_nontemporal_load(z4 + i) : ce_f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -771,11 +777,9 @@ __device__ __forceinline__ void ce_row_regs(const CeArgs& a, int r, int y, float
     for (int e = 0; e < 4; ++e) p[e] = (p[e] - (v0 + e == y ? 1.f : 0.f)) * a.inv_rows;
     const int64_t o = (int64_t)r * a.V + v0;
     if (a.dt == DT_BF16) {
-      const uint32_t w0 = f2bf2(p[0], p[1]);
-      const uint32_t w1 = f2bf2(p[2], p[3]);
-      *(uint2*)((uint16_t*)a.dz + o) = make_uint2(w0, w1);
+      __builtin_nontemporal_store(ce_u2{f2bf2(p[0], p[1]), f2bf2(p[2], p[3])}, (ce_gu2*)((uint16_t*)a.dz + o));
     } else {
-      *(float4*)((float*)a.dz + o) = make_float4(p[0], p[1], p[2], p[3]);
+      __builtin_nontemporal_store(ce_f4{p[0], p[1], p[2], p[3]}, (ce_gf4*)((float*)a.dz + o));
     }
   }
   if (threadIdx.x == 0) a.loss_rows[r] = mx + logf(s) - a.logits[(int64_t)r * a.V + y];
