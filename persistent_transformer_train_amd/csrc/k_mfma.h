@@ -69,7 +69,8 @@ __device__ __forceinline__ void epi_tile(const GemmArgs& g, const float* cst, in
       const int64_t row = row0 + r;
       v[u] = *(const epi_f4*)(cst + r * kEpiPitch + c) + bias;
       if constexpr (EPI == EPI_RESID) a0[u] = *(const epi_f4*)(resid + row * g.ldres + col);
-      if constexpr (EPI == EPI_DGELU || EPI == EPI_DGEGLU) a0[u] = unpack_bf16x4(*(const epi_u2*)(aux + row * g.ldaux + col));
+      if constexpr (EPI == EPI_DGELU || EPI == EPI_DGEGLU || EPI == EPI_DSUM)
+        a0[u] = unpack_bf16x4(*(const epi_u2*)(aux + row * g.ldaux + col));
       if constexpr (EPI == EPI_DGEGLU) a1[u] = unpack_bf16x4(*(const epi_u2*)(aux + row * g.ldaux + col + g.aux_off));
     }
 #pragma unroll
@@ -89,9 +90,26 @@ __device__ __forceinline__ void epi_tile(const GemmArgs& g, const float* cst, in
           *(epi_u2*)(aux + row * g.ldaux + col) = pack_bf16x4(gelu4(x));
         } else if constexpr (EPI == EPI_DGELU) {
           *(epi_u2*)(Ch + ci) = pack_bf16x4(x * gelu_grad4(a0[u]));
-        } else {   // EPI_DGEGLU
+        } else if constexpr (EPI == EPI_DGEGLU) {
           *(epi_u2*)(Ch + ci) = pack_bf16x4(x * a1[u] * gelu_grad4(a0[u]));
           *(epi_u2*)(Ch + ci + g.aux_off) = pack_bf16x4(x * gelu4(a0[u]));
+        }
+      }
+      if constexpr (EPI == EPI_DSUM) {
+        // dO rounded as stored, times O, summed over the head's 64 columns: the
+        // 16 threads of a row's head (lanes 16k .. 16k+15, one row per 32 lanes)
+        const epi_u2 pk = pack_bf16x4(v[u]);
+        if (r < rend) *(epi_u2*)(Ch + (int64_t)(row0 + r) * g.ldc + col) = pk;
+        const epi_f4 d = unpack_bf16x4(pk);
+        float sm = d.x * a0[u].x + d.y * a0[u].y + d.z * a0[u].z + d.w * a0[u].w;
+        sm += __shfl_xor(sm, 1);
+        sm += __shfl_xor(sm, 2);
+        sm += __shfl_xor(sm, 4);
+        sm += __shfl_xor(sm, 8);
+        if (r < rend && (threadIdx.x & 15) == 0) {
+          const int64_t row = row0 + r;
+          const int64_t bb = row / g.dsum_T, t = row % g.dsum_T;
+          g.dsum[(bb * g.dsum_H + col / 64) * g.dsum_T + t] = sm;
         }
       }
     }
@@ -128,6 +146,7 @@ __device__ __forceinline__ void gemm_mfma_epilogue(const GemmArgs& g, const f32x
     case EPI_RESID: epi_tile<EPI_RESID, true>(g, cst, BM, m0, n0); break;
     case EPI_GELU: epi_tile<EPI_GELU, false>(g, cst, BM, m0, n0); break;
     case EPI_DGELU: epi_tile<EPI_DGELU, false>(g, cst, BM, m0, n0); break;
+    case EPI_DSUM: epi_tile<EPI_DSUM, false>(g, cst, BM, m0, n0); break;
     default: epi_tile<EPI_DGEGLU, false>(g, cst, BM, m0, n0); break;
   }
 }

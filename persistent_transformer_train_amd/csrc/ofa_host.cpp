@@ -767,12 +767,28 @@ void build_train(ofa_handle* h) {
     ln_red(2 * l + 1, p_ln2b, gf(lo.ln2_g), gf(lo.ln2_b), c.has_bias ? gf(lo.b_o) : nullptr, "ln2_params");
     void* dxm = DXLP(2 * l + 1);
     g = gemm(h, (int)BT, (int)d, (int)d, dxm, d, 1, lp, wc(lo.w_o), d, 0, lp, DOUT(l), d, lp, EPI_STORE);
+    // With the matrix-core tile and 64-wide heads the attention backward's row
+    // sums D = rowsum(dO * O) come out of this product's epilogue (a 128-column
+    // tile holds two whole heads); otherwise a separate phase computes them.
+    const bool fused_prep = attn_impl == 1 && g.impl == GEMM_P3 && d % 128 == 0;
+    if (fused_prep) {
+      g.epi = EPI_DSUM;
+      g.aux = O(l);
+      g.ldaux = d;
+      g.aux_dt = lp;
+      g.dsum = DSUM(l);
+      g.dsum_T = (int)D.T;
+      g.dsum_H = (int)D.H;
+    }
     int p_odx = gemm_phase(g, {p_ln2b}, "attn_out_dx");
     g = gemm(h, (int)d, (int)d, (int)BT, dxm, d, 0, lp, O(l), d, 0, lp, gf(lo.w_o), d, DT_F32, EPI_STORE);
     gemm_phase(g, {p_ln2b}, "attn_out_dw");
-    int p_prep = b.add(OP_ATTN_PREP, cdiv(BT, 16), "attn_prep", {p_odx});
-    b[p_prep].a.attn = attn_args(l);
-    b[p_prep].a.attn.block = 16;
+    int p_prep = p_odx;
+    if (!fused_prep) {
+      p_prep = b.add(OP_ATTN_PREP, cdiv(BT, 16), "attn_prep", {p_odx});
+      b[p_prep].a.attn = attn_args(l);
+      b[p_prep].a.attn.block = 16;
+    }
     int p_kv = b.add(OP_ATTN_BWD_KV, attn_tiles, "attn_bwd_kv", {p_prep});
     b[p_kv].per_ticket = 1;
     b[p_kv].a.attn = attn_args(l);

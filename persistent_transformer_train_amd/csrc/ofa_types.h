@@ -54,6 +54,9 @@ enum Epi : int32_t {
   EPI_GELU = 2,    // u = acc (+ bias) -> C;  GELU(u) -> aux
   EPI_DGELU = 3,   // C = acc * GELU'(aux)
   EPI_DGEGLU = 4,  // aux = [g | up] (ld ldaux, up at +aux_off); C[:, n] = acc*up*GELU'(g), C[:, n+aux_off] = acc*GELU(g)
+  EPI_DSUM = 5,    // attention output gradient: C = dO = acc (bf16), and with aux = O (bf16) the
+                   // attention backward's row sums dsum[b][h][t] = sum over head h's 64 columns of dO O
+                   // (matrix-core tile only; N a multiple of 128, 64-wide heads)
 };
 
 enum GemmImpl : int32_t { GEMM_SIMPLE = 0, GEMM_P3 = 2 };
@@ -78,6 +81,8 @@ struct GemmArgs {
   int32_t tile_order; // 0: N index fastest; 1: M index fastest; 2: bands of `group` tile rows, M index fastest
   int32_t group;      // tile rows per band (tile_order 2)
   int32_t xcd;        // one-launch-per-phase executor: give each die a contiguous run of tiles
+  float* dsum;        // EPI_DSUM: [B][H][T] row sums; T and H of its indexing
+  int32_t dsum_T, dsum_H;
 };
 
 struct LnFwdArgs {
