@@ -59,6 +59,7 @@ __device__ __forceinline__ void st_row4(void* y, int64_t e, int dt, float4 v) {
   }
 }
 
+constexpr int kLnQ = 4;   // LayerNorm forward: rows per wave in flight
 __device__ void task_ln_fwd(const LnFwdArgs& a, int tile) {
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int r0 = tile * a.rows_per_tile;
@@ -74,11 +75,12 @@ __device__ void task_ln_fwd(const LnFwdArgs& a, int tile) {
     gv[c] = j < n4 ? g4[j] : f4_zero();
     bv[c] = j < n4 ? b4[j] : f4_zero();
   }
-  for (int r = r0 + w; r < r1; r += 2 * kWaves) {
-    float4 v[2][kMaxD4];
-    float mean[2], rstd[2];
+  // kLnQ rows per wave in flight: a 16-row tile is one pass
+  for (int r = r0 + w; r < r1; r += kLnQ * kWaves) {
+    float4 v[kLnQ][kMaxD4];
+    float mean[kLnQ], rstd[kLnQ];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kLnQ; ++q) {
       const int rr = r + q * kWaves;
 #pragma unroll
       for (int c = 0; c < kMaxD4; ++c) {
@@ -87,7 +89,7 @@ __device__ void task_ln_fwd(const LnFwdArgs& a, int tile) {
       }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kLnQ; ++q) {
       float s = 0.f;
 #pragma unroll
       for (int c = 0; c < kMaxD4; ++c) s += (v[q][c].x + v[q][c].y) + (v[q][c].z + v[q][c].w);
@@ -104,7 +106,7 @@ __device__ void task_ln_fwd(const LnFwdArgs& a, int tile) {
       rstd[q] = 1.0f / sqrtf(wave_sum(ss) / a.d + 1e-5f);
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kLnQ; ++q) {
       const int rr = r + q * kWaves;
       if (rr >= r1) break;
 #pragma unroll
