@@ -132,6 +132,9 @@ __device__ void task_ln_fwd(const LnFwdArgs& a, int tile) {
 
 // dx = rstd * (gy - mean(gy) - xhat * mean(gy*xhat)), gy = g*dy; dx_out = dx_in + dx.
 // Column partial sums of the tile (fixed order): dy*xhat, dy, dx_out.
+// kLnBwdQ: rows per wave in flight (four with the whole register file of one
+// workgroup per CU; two where two workgroups share it)
+template <int kLnBwdQ = 4>
 __device__ void task_ln_bwd(const LnBwdArgs& a, int tile, char* smem) {
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int r0 = tile * a.rows_per_tile;
@@ -148,11 +151,13 @@ __device__ void task_ln_bwd(const LnBwdArgs& a, int tile, char* smem) {
     gv[c] = j < n4 ? ((const float4*)a.g)[j] : f4_zero();
     pg[c] = pb[c] = px[c] = f4_zero();
   }
-  for (int r = r0 + w; r < r1; r += 2 * kWaves) {
-    float4 xh[2][kMaxD4], dyv[2][kMaxD4], din[2][kMaxD4];
-    float rs[2], m1[2], m2[2];
+  // kLnBwdQ rows per wave in flight (a wave's rows are accumulated in the same
+  // order whatever the count)
+  for (int r = r0 + w; r < r1; r += kLnBwdQ * kWaves) {
+    float4 xh[kLnBwdQ][kMaxD4], dyv[kLnBwdQ][kMaxD4], din[kLnBwdQ][kMaxD4];
+    float rs[kLnBwdQ], m1[kLnBwdQ], m2[kLnBwdQ];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kLnBwdQ; ++q) {
       const int rr = r + q * kWaves;
       const bool okr = rr < r1;
 #pragma unroll
@@ -166,7 +171,7 @@ __device__ void task_ln_bwd(const LnBwdArgs& a, int tile, char* smem) {
       }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kLnBwdQ; ++q) {
       const int rr = r + q * kWaves;
       const float mean = rr < r1 ? a.mean[rr] : 0.f;
       rs[q] = rr < r1 ? a.rstd[rr] : 0.f;
@@ -189,7 +194,7 @@ __device__ void task_ln_bwd(const LnBwdArgs& a, int tile, char* smem) {
       m2[q] = wave_sum(s2) / a.d;
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kLnBwdQ; ++q) {
       const int rr = r + q * kWaves;
       if (rr >= r1) break;
 #pragma unroll

@@ -50,7 +50,7 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   else if constexpr (OP == OP_GEGLU_FWD) { OFA_ARGS(geglu); task_geglu_fwd(a, tile); }
   else if constexpr (OP == OP_CE) { OFA_ARGS(ce); task_ce<OCC>(a, tile, tc, smem); }
   else if constexpr (OP == OP_LOSS) { OFA_ARGS(loss); task_loss(a, tc, smem); }
-  else if constexpr (OP == OP_LN_BWD) { OFA_ARGS(lnb); task_ln_bwd(a, tile, smem); }
+  else if constexpr (OP == OP_LN_BWD) { OFA_ARGS(lnb); task_ln_bwd<OCC == 1 ? 4 : 2>(a, tile, smem); }
   else if constexpr (OP == OP_COLSUM) { OFA_ARGS(cs); task_colsum(a, tile, smem); }
   else if constexpr (OP == OP_COLRED) { OFA_ARGS(cr); task_colred(a, tile, smem); }
   else if constexpr (OP == OP_ATTN_PREP) { OFA_ARGS(attn); task_attn_prep(a, tile); }
