@@ -100,14 +100,16 @@ __device__ __forceinline__ void attn_row_frags(bf16x8_t f[4], const uint16_t* g,
   }
 }
 
-__host__ __device__ constexpr size_t attn_mfma_lds_bytes() { return 2 * 64 * kAP * 2 + 2 * 64 * 4; }
+constexpr int kAttnFwdKeys = 128;   // keys per block of the forward and query-side passes (one stash, two barriers)
+__host__ __device__ constexpr size_t attn_mfma_lds_bytes() { return 2 * kAttnFwdKeys * kAP * 2 + 2 * 64 * 4; }
 
 // ---------------------------------------------------------------- forward
 // tile = (b, h, block of 128 queries), largest blocks first; wave w owns 32 queries.
 
 __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
-  uint16_t* Ks = (uint16_t*)smem;        // [64 keys][dh]
-  uint16_t* Vs = Ks + 64 * kAP;          // [64 keys][dh]
+  constexpr int KB = kAttnFwdKeys;
+  uint16_t* Ks = (uint16_t*)smem;        // [KB keys][dh]
+  uint16_t* Vs = Ks + KB * kAP;          // [KB keys][dh]
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, g = lane >> 5;
   const int BH = a.B * a.H, nqb = (a.T + 127) / 128;
   const int qblk = nqb - 1 - tile / BH, bh = tile % BH, b = bh / a.H, h = bh % a.H;
@@ -123,22 +125,30 @@ __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
   for (int e = 0; e < 16; ++e) oacc[0][e] = oacc[1][e] = 0.f;
   float m = -INFINITY, lsum = 0.f;
   const int kend = min(q0 + 128, a.T);
-  const int nkb = (kend + 63) / 64;
-  AttnChunk kc, vc;
-  attn_fetch(kc, base + a.d, ld, 0, min(64, a.T));
-  attn_fetch(vc, base + 2 * a.d, ld, 0, min(64, a.T));
+  const int nkb = (kend + KB - 1) / KB;
+  // a KB-key block in 64-row halves: attn_fetch / attn_stash move 64 rows
+  AttnChunk kc[KB / 64], vc[KB / 64];
+  auto fetch_block = [&](int kb) {
+#pragma unroll
+    for (int hh = 0; hh < KB / 64; ++hh) {
+      const int r0 = kb * KB + hh * 64;
+      attn_fetch(kc[hh], base + a.d, ld, r0, min(64, a.T - r0));
+      attn_fetch(vc[hh], base + 2 * a.d, ld, r0, min(64, a.T - r0));
+    }
+  };
+  fetch_block(0);
   for (int kb = 0; kb < nkb; ++kb) {
     __syncthreads();
-    attn_stash(kc, Ks);
-    attn_stash(vc, Vs);
-    if (kb + 1 < nkb) {
-      attn_fetch(kc, base + a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
-      attn_fetch(vc, base + 2 * a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
+#pragma unroll
+    for (int hh = 0; hh < KB / 64; ++hh) {
+      attn_stash(kc[hh], Ks + hh * 64 * kAP);
+      attn_stash(vc[hh], Vs + hh * 64 * kAP);
     }
+    if (kb + 1 < nkb) fetch_block(kb + 1);
     __syncthreads();
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kbase = kb * 64 + sub * 32;
+    for (int sub = 0; sub < KB / 32; ++sub) {
+      const int kbase = kb * KB + sub * 32;
       if (kbase > qw + 31 || kbase >= a.T) continue;   // wave-uniform: causal / past the end
       f32x16_t s;
 #pragma unroll
@@ -312,8 +322,9 @@ __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
 // S^T = K Q^T with lanes on queries: dS^T comes out as the B operand of dQ^T += K^T dS^T.
 
 __device__ void task_attn_bwd_q_mfma(const AttnArgs& a, int tile, char* smem) {
-  uint16_t* Ks = (uint16_t*)smem;        // [64 keys][dh]
-  uint16_t* Vs = Ks + 64 * kAP;          // [64 keys][dh]
+  constexpr int KB = kAttnFwdKeys;       // keys per block, as in the forward
+  uint16_t* Ks = (uint16_t*)smem;        // [KB keys][dh]
+  uint16_t* Vs = Ks + KB * kAP;          // [KB keys][dh]
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, g = lane >> 5;
   const int BH = a.B * a.H, nqb = (a.T + 127) / 128;
   const int qblk = nqb - 1 - tile / BH, bh = tile % BH, b = bh / a.H, h = bh % a.H;
@@ -332,22 +343,30 @@ __device__ void task_attn_bwd_q_mfma(const AttnArgs& a, int tile, char* smem) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) dq[0][e] = dq[1][e] = 0.f;
   const int kend = min(q0 + 128, a.T);
-  const int nkb = (kend + 63) / 64;
-  AttnChunk kc, vc;
-  attn_fetch(kc, base + a.d, ld, 0, min(64, a.T));
-  attn_fetch(vc, base + 2 * a.d, ld, 0, min(64, a.T));
+  const int nkb = (kend + KB - 1) / KB;
+  // a KB-key block in 64-row halves: attn_fetch / attn_stash move 64 rows
+  AttnChunk kc[KB / 64], vc[KB / 64];
+  auto fetch_block = [&](int kb) {
+#pragma unroll
+    for (int hh = 0; hh < KB / 64; ++hh) {
+      const int r0 = kb * KB + hh * 64;
+      attn_fetch(kc[hh], base + a.d, ld, r0, min(64, a.T - r0));
+      attn_fetch(vc[hh], base + 2 * a.d, ld, r0, min(64, a.T - r0));
+    }
+  };
+  fetch_block(0);
   for (int kb = 0; kb < nkb; ++kb) {
     __syncthreads();
-    attn_stash(kc, Ks);
-    attn_stash(vc, Vs);
-    if (kb + 1 < nkb) {
-      attn_fetch(kc, base + a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
-      attn_fetch(vc, base + 2 * a.d, ld, (kb + 1) * 64, min(64, a.T - (kb + 1) * 64));
+#pragma unroll
+    for (int hh = 0; hh < KB / 64; ++hh) {
+      attn_stash(kc[hh], Ks + hh * 64 * kAP);
+      attn_stash(vc[hh], Vs + hh * 64 * kAP);
     }
+    if (kb + 1 < nkb) fetch_block(kb + 1);
     __syncthreads();
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kbase = kb * 64 + sub * 32;
+    for (int sub = 0; sub < KB / 32; ++sub) {
+      const int kbase = kb * KB + sub * 32;
       if (kbase > qw + 31 || kbase >= a.T) continue;
       f32x16_t s, dp;
 #pragma unroll
