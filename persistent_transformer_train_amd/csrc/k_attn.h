@@ -100,8 +100,8 @@ __device__ __forceinline__ void attn_row_frags(bf16x8_t f[4], const uint16_t* g,
   }
 }
 
-constexpr int kAttnFwdKeys = 128;   // keys per block of the forward and query-side passes (one stash, two barriers)
-__host__ __device__ constexpr size_t attn_mfma_lds_bytes() { return 2 * kAttnFwdKeys * kAP * 2 + 2 * 64 * 4; }
+constexpr int kAttnFwdKeys = 128;   // keys (queries on the key side) per streamed block: one stash, two barriers
+__host__ __device__ constexpr size_t attn_mfma_lds_bytes() { return 2 * kAttnFwdKeys * kAP * 2 + 2 * kAttnFwdKeys * 4; }
 
 // ---------------------------------------------------------------- forward
 // tile = (b, h, block of 128 queries), largest blocks first; wave w owns 32 queries.
@@ -216,10 +216,11 @@ __device__ void task_attn_fwd_mfma(const AttnArgs& a, int tile, char* smem) {
 // dV^T += dO^T P and dK^T += Q^T dS.
 
 __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
-  uint16_t* Qs = (uint16_t*)smem;        // [64 q][dh]
-  uint16_t* Ds = Qs + 64 * kAP;          // dO [64 q][dh]
-  float* lse_s = (float*)(Ds + 64 * kAP);
-  float* dd_s = lse_s + 64;
+  constexpr int QB = kAttnFwdKeys;       // queries per streamed block
+  uint16_t* Qs = (uint16_t*)smem;        // [QB q][dh]
+  uint16_t* Ds = Qs + QB * kAP;          // dO [QB q][dh]
+  float* lse_s = (float*)(Ds + QB * kAP);
+  float* dd_s = lse_s + QB;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave, g = lane >> 5;
   const int BH = a.B * a.H;
   const int kblk = tile / BH, bh = tile % BH, b = bh / a.H, h = bh % a.H;
@@ -236,27 +237,34 @@ __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
   f32x16_t dk[2], dv[2];
 #pragma unroll
   for (int e = 0; e < 16; ++e) dk[0][e] = dk[1][e] = dv[0][e] = dv[1][e] = 0.f;
-  const int nqb = (a.T + 63) / 64;
-  // query blocks stream through registers one block ahead (see attn_fetch)
-  AttnChunk qc, dc;
+  const int nqb = (a.T + QB - 1) / QB;
+  // query blocks stream through registers one block ahead (see attn_fetch),
+  // in 64-row halves
+  AttnChunk qc[QB / 64], dc[QB / 64];
   float lse_r = INFINITY, dd_r = 0.f;
   auto fetch = [&](int qb) {
-    const int q0 = qb * 64;
-    attn_fetch(qc, base, ld, q0, min(64, a.T - q0));
-    attn_fetch(dc, dob, a.d, q0, min(64, a.T - q0));
-    if (threadIdx.x < 64) {
+    const int q0 = qb * QB;
+#pragma unroll
+    for (int hh = 0; hh < QB / 64; ++hh) {
+      attn_fetch(qc[hh], base, ld, q0 + hh * 64, min(64, a.T - q0 - hh * 64));
+      attn_fetch(dc[hh], dob, a.d, q0 + hh * 64, min(64, a.T - q0 - hh * 64));
+    }
+    if (threadIdx.x < QB) {
       const int qq = q0 + threadIdx.x;
       lse_r = qq < a.T ? lse[qq] * kLog2e : INFINITY;   // base-2 units
       dd_r = qq < a.T ? dsum[qq] : 0.f;
     }
   };
-  if (k0 / 64 < nqb) fetch(k0 / 64);
-  for (int qb = k0 / 64; qb < nqb; ++qb) {
-    const int q0 = qb * 64;
+  if (k0 / QB < nqb) fetch(k0 / QB);
+  for (int qb = k0 / QB; qb < nqb; ++qb) {
+    const int q0 = qb * QB;
     __syncthreads();
-    attn_stash(qc, Qs);
-    attn_stash(dc, Ds);
-    if (threadIdx.x < 64) {
+#pragma unroll
+    for (int hh = 0; hh < QB / 64; ++hh) {
+      attn_stash(qc[hh], Qs + hh * 64 * kAP);
+      attn_stash(dc[hh], Ds + hh * 64 * kAP);
+    }
+    if (threadIdx.x < QB) {
       lse_s[threadIdx.x] = lse_r;
       dd_s[threadIdx.x] = dd_r;
     }
@@ -264,7 +272,7 @@ __device__ void task_attn_bwd_kv_mfma(const AttnArgs& a, int tile, char* smem) {
     __syncthreads();
     if (kw >= a.T) continue;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < QB / 32; ++sub) {
       const int qs0 = q0 + sub * 32;
       if (qs0 + 31 < kw || qs0 >= a.T) continue;   // every query of the chunk precedes the wave's keys
       f32x16_t s, dp;
