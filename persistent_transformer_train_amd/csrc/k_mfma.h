@@ -6,14 +6,15 @@
 // step's time goes", tiled products table) puts 40% of its step in these
 // products.
 //
-// Tile: 128 x 128 outputs per workgroup, 4 wavefronts in a 2 x 2 grid, each
-// wavefront 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.  K advances 32 at a time
-// through two LDS buffers (the next tile's global loads are in flight while
-// the current tile is multiplied).  Both operands are staged in LDS as
-// [row][k] with k contiguous, so every MFMA operand fragment is one 16-byte
-// LDS read.  An operand whose contraction index is strided in memory (the
-// weight-gradient products, where k runs over tokens) is transposed while it
-// is written to LDS.
+// Tile: BM x 128 outputs per workgroup (BM = 128, or 256 for the LM-head
+// products), four wavefronts in a 2 x 2 grid, each (BM/2) x 64 in MFMA blocks
+// of 32 x 32.  K advances 64 at a time through a three-slice LDS ring filled
+// by direct-to-LDS copies issued between the MFMAs; operands keep their memory
+// layout in LDS (XOR-swizzled 16-byte chunks), and an operand whose
+// contraction index is strided in memory (weight gradients, where k runs over
+// tokens) is read with the transposing LDS read.  The epilogue parks the
+// accumulators in LDS and applies bias / residual / GELU / GELU' / gated-GELU'
+// / attention row sums on the way out (details below).
 #pragma once
 #include "k_simple.h"
 

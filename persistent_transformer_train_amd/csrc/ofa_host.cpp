@@ -410,7 +410,8 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
 
 // tile and ticket prefix sums; a ticket groups tiles so that a large phase
 // hands out at most ~256 tickets, about one per workgroup of a whole-GPU launch
-// (each ticket costs an atomic, a release fence and a counter update)
+// (each ticket costs an atomic and a counter update, and a release fence per
+// ticket or, with die partitions, per die and phase)
 constexpr int kTicketsPerPhase = 256;
 
 void finish_program(std::vector<Phase>& prog, int max_tickets = kTicketsPerPhase) {

@@ -4,16 +4,20 @@
 //    order supplies the dependencies.  Used for debugging and per-kernel
 //    profiles.
 // 2. persistent: one cooperative launch; every workgroup loops claiming 64-bit
-//    tickets from one counter.  Ticket t names (instance, phase, tile) in
-//    program order, so a workgroup only ever waits on tiles with smaller
-//    tickets, all of which are already held by running workgroups: the loop
-//    cannot deadlock.  A finished tile is published with a release increment
-//    of its phase's completion counter; a dependent tile acquire-reads the
-//    counters it needs.  This is the claim / fence-then-count / acquire-wait
-//    scheme of "How one persistent kernel runs three jobs" (review page,
-//    section of the same name), with every counter 64-bit after the 32-bit
-//    budget overflow described on the A100 reproduction page ("A longer run
-//    exposed a scheduler overflow").
+//    tickets from its partition's counter (one partition per die when the job
+//    has eight or more workgroups; partition s owns every eighth ticket of a
+//    phase).  Tickets name (instance, phase, tiles) in program order, and a
+//    partition's tickets are claimed in order, so the lowest unfinished phase
+//    always has its tickets held by running workgroups or claimable: the loop
+//    cannot deadlock.  A finished tile is published with a release, then an
+//    increment of its phase's completion counter (with partitions, the last
+//    workgroup of a die to finish its share writes that die's L2 back once and
+//    adds the share); a dependent tile acquire-reads the counters it needs.
+//    This is the claim / fence-then-count / acquire-wait scheme of "How one
+//    persistent kernel runs three jobs" (review page, section of the same
+//    name), with every counter 64-bit after the 32-bit budget overflow
+//    described on the A100 reproduction page ("A longer run exposed a
+//    scheduler overflow").
 #include <hip/hip_runtime.h>
 
 #include "k_simple.h"
@@ -313,8 +317,9 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
       }
       run_any<OCC>(ph, tl, tc, smem);
     }
-    // publish: the barrier makes every wave's stores complete; one agent-scope
-    // release fence then makes them visible before the counter moves
+    // publish: the barrier makes every wave's stores complete; an agent-scope
+    // release fence (per ticket, or once per die and phase) then makes them
+    // visible before the counter moves
     __syncthreads();
     if (threadIdx.x == 0) {
       if (J.trace && inst < J.trace_inst)
