@@ -115,3 +115,16 @@ def test_decode_after_training_reads_published_weights():
     assert np.all(vers.cpu().numpy() == 1)
     check_against_oracle(cfg, trained, prompt, toks.cpu().numpy(), logits.cpu().numpy(), np.float64, 1e-4)
     h.close()
+
+
+def test_full_size_decode_c4():
+    # The decode workload the benchmark times: the 162M model with a 512-token
+    # window and a 32-token prompt, one persistent launch on 48 CUs; the oracle
+    # recomputes the 162M model's logits along the GPU's tokens (bf16 weights).
+    n_new = 48
+    h, cfg, init, prompt, toks, logits, vers = run_decode("c4", n_new, exec_mode=0)
+    assert np.all(vers == 1)
+    w_bf16 = torch.tensor(init).to(torch.bfloat16).to(torch.float32).numpy()
+    checked = check_against_oracle(cfg, w_bf16, prompt, toks, logits, np.float64, 2e-2)
+    assert checked >= n_new // 2
+    h.close()
