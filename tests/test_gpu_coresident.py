@@ -119,3 +119,41 @@ def test_coresident_publish_without_serving():
     h.sync()
     assert np.all(vers.cpu().numpy() == 3)
     h.close()
+
+
+def test_full_size_coresident_c5():
+    """The co-resident launch the benchmark times (the 162M model, 208 training and
+    48 serving CUs), with restarts every 8 tokens so several periods start: training
+    equals step mode bit for bit, and decoded tokens match the oracle at the version
+    they read."""
+    n_steps = 12
+    log("co-resident c5: 208 train CUs, 48 serve CUs, 12 steps")
+    cfg, stream, init, co = run_coresident("c5", n_steps, train_cus=208, serve_cus=48, restart_every=8)
+    ref_losses, snaps = step_mode_snapshots("c5", n_steps, cfg)
+    log("losses co-resident", co["losses"][[0, -1]], "step mode", ref_losses[[0, -1]])
+    assert co["losses"].tobytes() == ref_losses.tobytes()
+    assert co["params"].tobytes() == snaps[-1].tobytes()
+    assert co["version"] == n_steps
+    n = co["n_gen"]
+    assert 1 <= n <= 4096
+    toks, vers = co["tokens"][:n], co["versions"][:n]
+    assert np.all((toks >= 0) & (toks < cfg["vocab"]))
+    assert np.all(np.diff(vers) >= 0)
+    s = spec_from_cfg(cfg)
+    per = cfg["restart_every"]
+    checked = 0
+    for k in range(0, (n + per - 1) // per):
+        tk, vk = toks[k * per:(k + 1) * per], vers[k * per:(k + 1) * per]
+        same = int(np.argmax(vk != vk[0])) if np.any(vk != vk[0]) else len(vk)
+        if same == 0:
+            continue
+        w = torch.tensor(snaps[int(vk[0])]).to(torch.bfloat16).to(torch.float32).numpy()
+        P = gpt.unflatten(s, np.asarray(w, np.float64))
+        z = decode.teacher_forced_logits(s, P, co["prompt"], tk[:same], cfg["decode_window"], cfg["prompt_len"])
+        for i in range(same):
+            if decode.top2_margin(z[i]) > 1e-2:
+                assert tk[i] == decode.argmax_lowest(z[i]), (k, i, tk[i], decode.argmax_lowest(z[i]))
+                checked += 1
+    log(f"decode: {n} tokens, {checked} checked against the oracle at their version, "
+        f"{len(np.unique(vers))} distinct versions read")
+    assert checked >= 1
