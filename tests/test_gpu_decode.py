@@ -117,12 +117,14 @@ def test_decode_after_training_reads_published_weights():
     h.close()
 
 
-def test_full_size_decode_c4():
-    # The decode workload the benchmark times: the 162M model with a 512-token
-    # window and a 32-token prompt, one persistent launch on 48 CUs; the oracle
-    # recomputes the 162M model's logits along the GPU's tokens (bf16 weights).
+@pytest.mark.parametrize("name", ["c4", "c2"])
+def test_full_size_decode(name):
+    # Full-size models, one persistent launch on 48 CUs, 48 tokens after a
+    # 32-token prompt: c4 is the decode workload the benchmark times (the 162M
+    # model, 512-token window); c2 takes the rotary, gated-MLP, tied-head path.
+    # The oracle recomputes the logits along the GPU's tokens (bf16 weights).
     n_new = 48
-    h, cfg, init, prompt, toks, logits, vers = run_decode("c4", n_new, exec_mode=0)
+    h, cfg, init, prompt, toks, logits, vers = run_decode(name, n_new, exec_mode=0, serve_cus=48)
     assert np.all(vers == 1)
     w_bf16 = torch.tensor(init).to(torch.bfloat16).to(torch.float32).numpy()
     checked = check_against_oracle(cfg, w_bf16, prompt, toks, logits, np.float64, 2e-2)
