@@ -296,3 +296,37 @@ def test_full_size_first_step(name):
     assert abs(gl - float(loss)) <= 2e-2
     assert cos >= 0.999
     assert worst[1] >= 0.99
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_full_size_loss_along_trajectory(name):
+    """The bf16 loss bar over the first 100 steps of the full-size workloads, in the
+    launch configuration bench.py times, read along the GPU's own trajectory: at
+    steps 1, 50 and 100 the oracle (fp32) evaluates loss and gradient at the master
+    weights the GPU holds before that step, on that step's tokens."""
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of(name, exec_mode=PERSISTENT)
+    stream = stream_of(name, cfg)
+    init = init_of(name, cfg)
+    s = spec_from_cfg(cfg)
+    h = ofa.Handle(cfg, init)
+    l1 = torch.zeros(1, dtype=torch.float32, device="cuda")
+    worst_d, worst_cos = 0.0, 1.0
+    for step in range(100):
+        check = step in (0, 49, 99)
+        if check:
+            p_now = h.get_params().cpu().numpy()
+        h.train_step(torch.from_numpy(stream.batches(step, 1)).cuda(), l1)
+        h.sync()
+        assert np.isfinite(l1.item())
+        if not check:
+            continue
+        g_gpu = h.get_grads().cpu().numpy()
+        lo, go = gpt.loss_and_grads(s, gpt.unflatten(s, p_now), stream.batch(step), dtype=np.float32)
+        d = abs(float(l1.item()) - float(lo))
+        cos = cosine(g_gpu, gpt.flatten(s, go, dtype=np.float32))
+        log(f"{name} step {step + 1}: gpu {l1.item():.5f} oracle {float(lo):.5f} |d| {d:.2e} grad cosine {cos:.6f}")
+        worst_d, worst_cos = max(worst_d, d), min(worst_cos, cos)
+    h.close()
+    assert worst_d <= 2e-2
+    assert worst_cos >= 0.999
