@@ -223,6 +223,16 @@ def causal_attention_backward(do, q, k, v, p):
     return dq, dk, dv
 
 
+def prediction_entropy(z):
+    """Entropy in nats of softmax(z) over the last axis: -sum_i p_i log p_i.
+
+    "Coppelius training on the RTX 3090", "Prediction entropy": the next-token
+    entropy of a row, ln V when every token is equally likely.
+    """
+    logp, _ = log_softmax_rows(z)
+    return -(np.exp(logp) * logp).sum(axis=-1)
+
+
 def log_softmax_rows(z):
     m = z.max(axis=-1, keepdims=True)
     lse = m + np.log(np.exp(z - m).sum(axis=-1, keepdims=True))

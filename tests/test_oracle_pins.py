@@ -318,3 +318,111 @@ def test_window_rule_segments():
 def test_argmax_tie_lowest_id():
     assert decode.argmax_lowest(np.array([0.5, 2.0, 1.0, 2.0])) == 1
     assert decode.top2_margin(np.array([0.5, 2.0, 1.0, 2.0])) == 0.0
+
+
+def test_rope_second_frequency():
+    # theta_i = 10000^(-2i/dh): with dh = 8 the second pair turns by 10000^(-1/4) = 0.1 rad per
+    # position (writing the exponent as -i/dh would give 0.316 rad)
+    T, dh = 6, 8
+    cos, sin = gpt.rope_tables(T, dh)
+    e = np.zeros(dh)
+    e[1] = 1.0
+    E = gpt.rope(np.tile(e, (T, 1)), cos, sin)
+    np.testing.assert_allclose(E[3, 1], math.cos(0.3), atol=1e-14)
+    np.testing.assert_allclose(E[3, 1 + dh // 2], math.sin(0.3), atol=1e-14)
+    # at the full head width of the rotary workload (dh = 64): pair 16 turns by 10000^(-1/2)
+    cos64, sin64 = gpt.rope_tables(8, 64)
+    np.testing.assert_allclose(math.atan2(sin64[5, 16], cos64[5, 16]), 5 * 0.01, atol=1e-14)
+    # a later start position continues the same angles
+    c2, s2 = gpt.rope_tables(3, dh, start=3)
+    np.testing.assert_allclose(c2, cos[3:6], atol=1e-15)
+    np.testing.assert_allclose(s2, sin[3:6], atol=1e-15)
+
+
+# ---------------------------------------------------------------- training loop
+
+def _seeded(name, cid, kind):
+    from persistent_transformer_train_amd import synth
+    s = ORACLE_CONFIGS[name]
+    init = synth.init_params([(int(np.prod(sh)), k) for _, sh, k in gpt.param_layout(s)], cid)
+    return s, init, synth.TokenStream(kind, cid, s.vocab, s.batch, s.seq)
+
+
+def test_trainer_first_two_steps_closed_form():
+    """Trainer.step against what AdamW reduces to on its first steps: at t = 1 the
+    bias-corrected moments are g and g^2, so p1 = p0 (1 - lr0 wd) - lr0 g / (|g| + eps)
+    with lr0 the rate of 0-based step 0.  A cosine schedule over 10 steps makes the
+    rate of step 1 differ from step 0 by 2.4%, and the second step's bias correction
+    uses t = 2: an off-by-one in either index fails here.  Gradients come from the
+    finite-difference-pinned loss_and_grads."""
+    s = TINY.replace(lr_schedule="cosine", total_steps=10, lr=1e-2)
+    flat0 = gpt.flatten(s, rand_params(s, 50, scale=0.2))
+    tok0, tok1 = rand_tokens(s, 51), rand_tokens(s, 52)
+    tr = optim.Trainer(s, flat0)
+    loss0 = tr.step(tok0)
+    l_ref, g0 = gpt.loss_and_grads(s, gpt.unflatten(s, flat0.copy()), tok0)
+    g0 = gpt.flatten(s, g0)
+    assert loss0 == pytest.approx(float(l_ref), rel=1e-15)
+    lr0 = 1e-2                      # cosine at step 0 is the peak rate
+    p1 = flat0 * (1 - lr0 * s.weight_decay) - lr0 * g0 / (np.abs(g0) + s.eps)
+    np.testing.assert_allclose(tr.flat, p1, rtol=0, atol=1e-15)
+    # second step: rate of step 1, bias corrections 1 - b^2
+    _, g1 = gpt.loss_and_grads(s, gpt.unflatten(s, p1.copy()), tok1)
+    g1 = gpt.flatten(s, g1)
+    tr.step(tok1)
+    lr1 = 1e-2 * 0.5 * (1 + math.cos(math.pi / 10))
+    b1, b2 = s.beta1, s.beta2
+    mhat = (b1 * (1 - b1) * g0 + (1 - b1) * g1) / (1 - b1 * b1)
+    vhat = (b2 * (1 - b2) * g0 ** 2 + (1 - b2) * g1 ** 2) / (1 - b2 * b2)
+    p2 = p1 * (1 - lr1 * s.weight_decay) - lr1 * mhat / (np.sqrt(vhat) + s.eps)
+    np.testing.assert_allclose(tr.flat, p2, rtol=0, atol=1e-10)
+    assert tr.steps_done == 2
+
+
+def test_c1_training_finite_falling_and_initial_loss():
+    """The tiny workload trained by the oracle for its 10 steps: every loss finite,
+    the last below the first, the first within 0.1 of ln 256 (a model that knows
+    nothing) and within 0.03 of ln V + 0.0002 d = 5.558 (logits ~ N(0, 0.0004 d)
+    after the final LayerNorm with N(0, 0.02) head weights), and no loss below the
+    data's entropy rate (the Markov chain's sum_i pi_i H(P_i), 3.70 nats)."""
+    s, init, stream = _seeded("c1", 1, "markov1")
+    tr = optim.Trainer(s, init)
+    ls = np.array([tr.step(stream.batch(i)) for i in range(10)])
+    assert np.all(np.isfinite(ls))
+    assert ls[-1] < ls[0]
+    assert ls[-3:].mean() < ls[:3].mean()
+    assert abs(ls[0] - math.log(256)) < 0.1
+    assert abs(ls[0] - (math.log(256) + 0.0002 * 64)) < 0.03
+    P = stream.table
+    pi = np.full(256, 1 / 256)
+    for _ in range(2000):
+        pi = pi @ P
+    rate = float(pi @ -(P * np.log(np.where(P > 0, P, 1))).sum(axis=1))
+    assert 3.0 < rate < 5.0
+    assert ls.min() > rate
+
+
+@pytest.mark.slow
+def test_c3_initial_loss_closed_form():
+    """The 162M workload's first loss in fp32 at its seeded init: within 0.03 of
+    ln 50304 + 0.0002 * 768 = 10.979 (untied head, N(0, 0.02) weights)."""
+    s, init, stream = _seeded("c3", 3, "markov2")
+    loss, _ = gpt.forward(s, gpt.unflatten(s, init), stream.batch(0), dtype=np.float32, keep=False)
+    assert np.isfinite(loss)
+    assert abs(float(loss) - (math.log(50304) + 0.0002 * 768)) < 0.03
+
+
+def test_prediction_entropy():
+    # equal logits: ln V; a dominant logit: ~0; two equal logits far above the rest: ln 2
+    assert gpt.prediction_entropy(np.zeros(11)) == pytest.approx(math.log(11), rel=1e-14)
+    z = np.full(7, -40.0)
+    z[2] = 40.0
+    assert gpt.prediction_entropy(z) < 1e-30 + 1e-32 * 0 + 1e-25
+    z[5] = 40.0
+    assert gpt.prediction_entropy(z) == pytest.approx(math.log(2), rel=1e-12)
+    # brute force on a small row: p = e^z / sum e^z, H = -sum p log p
+    z = np.array([0.3, -1.2, 2.5, 0.0])
+    p = np.exp(z) / np.exp(z).sum()
+    assert gpt.prediction_entropy(z) == pytest.approx(float(-(p * np.log(p)).sum()), rel=1e-13)
+    # shift invariance
+    assert gpt.prediction_entropy(z + 100.0) == pytest.approx(gpt.prediction_entropy(z), rel=1e-12)
