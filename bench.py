@@ -179,6 +179,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--co-steps", type=int, default=40, help="co-resident (c5) training steps; 0 = skip")
+    ap.add_argument("--dump-phases", default="", help="write the training program's phase names (launch order) here")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -208,6 +209,9 @@ def main():
     elapsed = time.perf_counter() - t0
     st = h.sync()
     kernel_ms = st.last_call_ms   # HIP events around the launch(es) on the handle's stream
+    if args.dump_phases:
+        with open(args.dump_phases, "w") as f:
+            json.dump([nm for nm, _, _ in h.phase_times()], f)
     ls = losses[:K].cpu().numpy()
     assert np.all(np.isfinite(ls)), ls
 

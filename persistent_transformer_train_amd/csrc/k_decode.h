@@ -667,6 +667,50 @@ __device__ void task_dec_argmax(const DecArgmaxArgs& a, int tile, const TaskCtx&
   __syncthreads();
 }
 
+// ---------------------------------------------------------------- evaluation probe
+
+// What the model predicts after row r of an evaluated context ("Coppelius
+// training on the RTX 3090", "Prompt probe" and "Prediction entropy"): the
+// most likely next token (lowest id on exact ties) and the entropy of the
+// softmax of the logits, H = log(sum e^(z - m)) - sum e^(z - m) (z - m) / sum e^(z - m)
+// with m the row maximum.  One probed row per tile.
+__device__ void task_probe(const ProbeArgs& a, int tile, const TaskCtx& tc, char* smem) {
+  const StepCtx* sc = tc.sc;
+  if (tile >= sc->n_probe || !sc->probe_rows) return;
+  float* red = (float*)smem;   // [32]
+  const int r = sc->probe_rows[tile];
+  if (r < 0 || r >= a.rows) {
+    if (threadIdx.x == 0) raise_status(tc.status, -1 /*OFA_E_ARG*/, tc.phase, tc.step, r);
+    return;
+  }
+  const float* z = a.logits + (int64_t)r * a.V;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < a.V; i += kThreads) {
+    const float v = z[i];
+    if (v > bv) {   // ascending i: a thread keeps its first maximum
+      bv = v;
+      bi = i;
+    }
+  }
+  argmax_combine_block(bv, bi, red);
+  const float m = bv;
+  float s = 0.f, t = 0.f;
+  for (int i = threadIdx.x; i < a.V; i += kThreads) {
+    const float d = z[i] - m;
+    const float e = expf(d);
+    s += e;
+    t += e * d;
+  }
+  s = block_sum(s, red + 16);
+  t = block_sum(t, red + 24);
+  if (threadIdx.x == 0) {
+    if (sc->probe_argmax) sc->probe_argmax[tile] = bi;
+    if (sc->probe_entropy) sc->probe_entropy[tile] = logf(s) - t / s;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- co-resident training
 
 // The training step about to write serve slot (tag & 1) waits until the
@@ -690,8 +734,10 @@ __device__ void task_slot_guard(const GuardArgs& a, const TaskCtx& tc) {
 
 // The step's weights (written to slot tag & 1 by AdamW, complete: this phase
 // depends on it) become version tag.
+// A step whose update was skipped after an error publishes nothing.
 __device__ void task_publish(const PublishArgs& a, const TaskCtx& tc) {
-  if (threadIdx.x == 0) st_release(a.published, tc.sc->tag);
+  if (threadIdx.x == 0 && !__hip_atomic_load(&tc.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    st_release(a.published, tc.sc->tag);
 }
 
 }  // namespace ofa

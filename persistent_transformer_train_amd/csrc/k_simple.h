@@ -777,7 +777,7 @@ __device__ __forceinline__ void ce_row_regs(const CeArgs& a, int r, int y, float
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
     const int i = threadIdx.x + u * kThreads;
-    if (i >= n4) continue;
+    if (i >= n4 || !a.dz) continue;
     float p[4] = {v[u].x * inv_s, v[u].y * inv_s, v[u].z * inv_s, v[u].w * inv_s};
     const int v0 = 4 * i;
 #pragma unroll
@@ -808,7 +808,8 @@ __device__ __forceinline__ void ce_row_loop(const CeArgs& a, int r, int y, float
   }
   s = block_sum(s, red + kWaves);
   const float lse = mx + logf(s);
-  for (int i = threadIdx.x; i < n4; i += kThreads) ce_store(a, r, i, y, lse, z4[i]);
+  if (a.dz)
+    for (int i = threadIdx.x; i < n4; i += kThreads) ce_store(a, r, i, y, lse, z4[i]);
   if (threadIdx.x == 0) a.loss_rows[r] = lse - a.logits[(int64_t)r * a.V + y];
 }
 
@@ -842,7 +843,8 @@ __device__ __forceinline__ void ce_row_online(const CeArgs& a, int r, int y, flo
   const float ml2 = mx * 1.44269504088896341f;
   const float tot = block_sum(m == -INFINITY ? 0.f : s * exp_shift(m, ml2), red + kWaves);
   const float lse = mx + logf(tot);
-  for (int i = threadIdx.x; i < n4; i += kThreads) ce_store(a, r, i, y, lse, z4[i]);
+  if (a.dz)
+    for (int i = threadIdx.x; i < n4; i += kThreads) ce_store(a, r, i, y, lse, z4[i]);
   if (threadIdx.x == 0) a.loss_rows[r] = lse - a.logits[(int64_t)r * a.V + y];
 }
 
@@ -880,6 +882,8 @@ __device__ void task_loss(const LossArgs& a, const TaskCtx& tc, char* smem) {
     if (tc.sc->loss_out) *tc.sc->loss_out = loss;
     if (!isfinite(loss)) raise_status(tc.status, -3 /*OFA_E_NONFINITE*/, tc.phase, tc.step, 0);
   }
+  if (float* out = tc.sc->rows_out)
+    for (int i = threadIdx.x; i < a.rows; i += kThreads) out[i] = a.loss_rows[i];
   __syncthreads();
 }
 
@@ -1052,6 +1056,15 @@ __device__ __forceinline__ void adamw_one(float& p, float& m, float& v, float g,
 // last tile element-wise
 constexpr int kAdamU = 4;
 __device__ void task_adamw(const AdamArgs& a, int tile, const TaskCtx& tc) {
+  // An error raised earlier in this step (a token out of range, a non-finite
+  // loss) or anywhere else in the launch leaves the weights, the moments and
+  // the compute copy untouched.  Every earlier phase of the step completed
+  // before this one (acquired through its dependency), so their status writes
+  // are visible; one thread reads the word so the whole tile takes one decision.
+  __shared__ int s_err;
+  if (threadIdx.x == 0) s_err = __hip_atomic_load(&tc.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_err) return;
   const float lr = tc.sc->lr, ibc1 = 1.0f / tc.sc->bc1, ibc2 = 1.0f / tc.sc->bc2;
   const int64_t i0 = (int64_t)tile * a.per_tile;
   const int64_t i1 = min(i0 + (int64_t)a.per_tile, a.n);

@@ -31,6 +31,10 @@ constexpr size_t kMiscBytes = 4096;    // one Phase (offset 0) and the DecIO blo
 constexpr size_t kMiscDecIO = 2048;
 constexpr int kMaxAttnSplit = 8;        // key ranges per head in decode attention
 constexpr int kThreadsHost = 256;       // threads of every workgroup
+// the device copies of the two programs' phase tables and their per-partition
+// ticket tables live in the workspace (the library allocates no device memory)
+constexpr size_t kTableBytes = 3 * (size_t)512 * 320 + 9 * (size_t)8 * 513 * 4 + 4096;
+constexpr int kMaxProbe = 64;          // rows one evaluation call may probe
 
 // ---------------------------------------------------------------- parameter layout
 
@@ -151,11 +155,21 @@ struct Bump {
   }
 };
 
+// One program's device tables: the phase table, its per-partition first
+// tickets split into kMaxParts partitions and unsplit (PersistJob::part_tb),
+// and tiles per partition and phase (PersistJob::part_tiles).
+struct DevProg {
+  Phase* ph = nullptr;
+  int32_t* pt8 = nullptr;
+  int32_t* pt1 = nullptr;
+  int32_t* tiles8 = nullptr;
+};
+
 struct Carve {
   // offsets (bytes) into the workspace
   size_t p, g, m, v, wc, serve, xres, ln_mean, ln_rstd, h, qkv, o, lse, mlp1, mlp2, logits, dz, loss_rows;
   size_t dxres, dxlp, dln, dmlp, dout, dsum, dqkv, ln_part, cs_fc, cs_qkv, esorted, efirst;
-  size_t sched, status, times, inst_end, steps, published, trace;
+  size_t sched, status, times, inst_end, steps, published, trace, tables;
   size_t kv, ctx_tok, dstate, dx, dq, dapart, dmlp_v, dlogits, dsteps, dtimes, misc, dsched, dpart_v, dpart_i, dprompt;
   size_t total;
   int n_slots;
@@ -252,6 +266,7 @@ Carve carve(const ofa_config& c, const Layout& lay) {
   w.dpart_v = b.take(D.V * f4);
   w.dpart_i = b.take(D.V * 4);
   w.misc = b.take(kMiscBytes);
+  w.tables = b.take(kTableBytes);
   w.trace = (c.debug_flags & OFA_DEBUG_TRACE) ? b.take((size_t)OFA_TRACE_INSTANCES * kMaxPhases * 32) : 0;
   w.total = (b.off + kAlign - 1) / kAlign * kAlign;
   return w;
@@ -276,16 +291,14 @@ struct ofa_handle {
   int train_occ = 1;               // workgroups per CU of step-mode persistent training (1 or 2)
   std::vector<Phase> train;        // one training step
   std::vector<Phase> dec;          // one decode position (with head)
-  Phase* d_train = nullptr;        // device copies (inside the pinned-upload area)
+  std::vector<Phase> eval;         // forward, loss and probe of one evaluated batch
+  // device copies of the three programs (in the workspace) and their ticket tables
+  DevProg dp_train, dp_dec, dp_eval;
+  Phase* d_train = nullptr;
   Phase* d_dec = nullptr;
   // per-partition ticket tables (see PersistJob::part_tb): the training
   // program split into kMaxParts partitions, and both programs unsplit
-  int32_t* d_train_pt = nullptr;
-  int32_t* d_train_pt1 = nullptr;
-  int32_t* d_dec_pt1 = nullptr;
-  int32_t* d_train_ptiles = nullptr;   // tiles per partition and phase of the training program
-  int32_t* d_dec_pt = nullptr;         // the decode program's, split into kMaxParts partitions
-  int32_t* d_dec_ptiles = nullptr;
+  uint8_t lineage[32] = {};         // SHA-256 of the checkpoint this state last came from or went to
   std::vector<char> phase_names;   // for phase_times
   std::vector<std::string> train_names;
   std::vector<std::string> dec_names;
@@ -310,7 +323,8 @@ struct ofa_handle {
   // decode host mirror of the context rule
   int64_t dec_ctx_len = 0, dec_processed = 0;
   bool dec_started = false;
-  void* d_alloc = nullptr;         // library-owned device memory for phase tables (small)
+  bool die_map = false;            // workgroup b of a launch runs on die b % 8 (probed at create)
+  bool unpublished = false;        // compute weights set by ofa_set_params since the last publication
 };
 
 namespace {
@@ -873,6 +887,40 @@ void build_train(ofa_handle* h) {
   finish_program(h->train, std::max(kTicketsPerPhase, h->n_cu) * h->train_occ);
 }
 
+// Evaluation program of one batch: the training program's forward phases
+// through the mean loss (no backward, no update) with the cross-entropy's
+// gradient write left out, then the probe of chosen rows.  The embedding sort
+// (needed by the backward only) becomes an empty phase, so phase indices and
+// dependencies stay those of the training program.
+void build_eval(ofa_handle* h) {
+  h->eval.clear();
+  int p_loss = -1, p_head = -1;
+  for (size_t i = 0; i < h->train.size() && p_loss < 0; ++i) {
+    Phase ph = h->train[i];
+    if (ph.op == OP_EMB_SORT) {
+      ph.op = OP_NOP;
+      ph.n_tiles = 0;
+      ph.per_ticket = 1;
+    }
+    if (ph.op == OP_CE) {
+      ph.a.ce.dz = nullptr;
+      p_head = ph.dep[0];
+    }
+    if (ph.op == OP_LOSS) p_loss = (int)i;
+    h->eval.push_back(ph);
+  }
+  Builder b{&h->eval, nullptr};
+  const int p_probe = b.add(OP_PROBE, kMaxProbe, "probe", {p_head, p_loss});
+  b[p_probe].a.probe.logits = at<float>(h->ws, h->cw.logits);
+  b[p_probe].a.probe.rows = (int)h->D.BT;
+  b[p_probe].a.probe.V = (int)h->D.V;
+  b[p_probe].per_ticket = 1;
+  // the next batch's forward overwrites what this batch's loss and probe read
+  h->eval[0].dep_prev = p_probe;
+  h->eval[1].dep_prev = -1;
+  finish_program(h->eval, std::max(kTicketsPerPhase, h->n_cu) * h->train_occ);
+}
+
 // Tile plan of a decode GEMV, whose task streams weight tiles through an LDS
 // ring of fixed-size buffers: rows per tile chosen so that each of the G serve
 // workgroups gets one ticket of whole tiles, up to four tiles in flight where
@@ -1072,9 +1120,9 @@ ofa_status mark_upload(ofa_handle* h) {
 }
 
 ofa_status run_launch_per_phase(ofa_handle* h, const std::vector<Phase>& prog, const Phase* d_prog,
-                                const StepCtx* d_ctx, int64_t n_inst, int64_t step0, bool dec_head_gate) {
+                                const StepCtx* d_ctx, int64_t n_inst, int64_t step0, bool dec_head_gate,
+                                PhaseTime* tm) {
   DevStatus* st = at<DevStatus>(h->ws, h->cw.status);
-  PhaseTime* tm = at<PhaseTime>(h->ws, dec_head_gate ? h->cw.dtimes : h->cw.times);
   for (int64_t s = 0; s < n_inst; ++s) {
     const bool head = dec_head_gate ? (h->h_dsteps[s].head & 1) != 0 : true;
     for (size_t i = 0; i < prog.size(); ++i) {
@@ -1140,17 +1188,17 @@ PersistJob make_job(ofa_handle* h, const std::vector<Phase>& prog, const Phase* 
   // tickets are claimed per die (eight partitions: 32 workgroups per counter
   // instead of 256 for training); an open-ended job (co-resident decode, whose
   // stopping rule needs one counter) or a grid under eight keeps one
-  const bool tr = &prog == &h->train;
+  const DevProg& dp = &prog == &h->train ? h->dp_train : &prog == &h->eval ? h->dp_eval : h->dp_dec;
   if (n_wg >= kMaxParts && !open_ended) {
     j.n_parts = kMaxParts;
-    j.part_tb = tr ? h->d_train_pt : h->d_dec_pt;
+    j.part_tb = dp.pt8;
     // the hardware hands workgroup b to die b % 8, so partition s is die s
     // (each workgroup checks this on the device)
-    j.die_release = (h->cfg.debug_flags & OFA_DEBUG_WG_RELEASE) ? 0 : 1;
-    j.part_tiles = tr ? h->d_train_ptiles : h->d_dec_ptiles;
+    j.die_release = (h->die_map && !(h->cfg.debug_flags & OFA_DEBUG_WG_RELEASE)) ? 1 : 0;
+    j.part_tiles = dp.tiles8;
   } else {
     j.n_parts = 1;
-    j.part_tb = tr ? h->d_train_pt1 : h->d_dec_pt1;
+    j.part_tb = dp.pt1;
   }
   j.n_inst = n_inst;
   j.steps = d_ctx;
@@ -1329,9 +1377,10 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
   const bool coresident_cfg = h->cfg.train_cus > 0 && h->cfg.serve_cus > 0;
   h->train_occ = (!coresident_cfg && (h->cfg.debug_flags & OFA_DEBUG_OCC2) && persistent_occupancy(2) >= 2) ? 2 : 1;
   build_train(h);
+  build_eval(h);
   build_decode(h);
   if (!h->plan_ok) return fail(h, OFA_E_ARG, "a decode matrix-vector product does not fit the LDS");
-  if (h->train.size() > (size_t)kMaxPhases || h->dec.size() > (size_t)kMaxPhases)
+  if (h->train.size() > (size_t)kMaxPhases || h->dec.size() > (size_t)kMaxPhases || h->eval.size() > (size_t)kMaxPhases)
     return fail(h, OFA_E_ARG, "program too long");
   for (const auto* prog : {&h->train, &h->dec})
     for (const Phase& ph : *prog)
@@ -1341,32 +1390,58 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
   if (h->train_occ == 2)
     for (const Phase& ph : h->train)
       if (phase_lds_bytes_occ(ph, 2) > persistent_lds_bytes(2)) h->train_occ = 1;   // one per CU after all
-  // phase tables live in a small library-owned device buffer
-  const std::vector<int32_t> pt = part_table(h->train, kMaxParts), pt1 = part_table(h->train, 1),
-                             dpt1 = part_table(h->dec, 1), ptl = part_tile_table(h->train, kMaxParts),
-                             dpt = part_table(h->dec, kMaxParts), dptl = part_tile_table(h->dec, kMaxParts);
-  size_t tbytes = (h->train.size() + h->dec.size()) * sizeof(Phase) +
-                  (pt.size() + pt1.size() + dpt1.size() + ptl.size() + dpt.size() + dptl.size()) * 4;
-  HIP_TRY(h, hipMalloc(&h->d_alloc, tbytes));
-  h->d_train = (Phase*)h->d_alloc;
-  h->d_dec = h->d_train + h->train.size();
-  h->d_train_pt = (int32_t*)(h->d_dec + h->dec.size());
-  h->d_train_pt1 = h->d_train_pt + pt.size();
-  h->d_dec_pt1 = h->d_train_pt1 + pt1.size();
-  h->d_train_ptiles = h->d_dec_pt1 + dpt1.size();
-  h->d_dec_pt = h->d_train_ptiles + ptl.size();
-  h->d_dec_ptiles = h->d_dec_pt + dpt.size();
-  HIP_TRY(h, hipMemcpy(h->d_train, h->train.data(), h->train.size() * sizeof(Phase), hipMemcpyHostToDevice));
-  HIP_TRY(h, hipMemcpy(h->d_dec, h->dec.data(), h->dec.size() * sizeof(Phase), hipMemcpyHostToDevice));
-  HIP_TRY(h, hipMemcpy(h->d_train_pt, pt.data(), pt.size() * 4, hipMemcpyHostToDevice));
-  HIP_TRY(h, hipMemcpy(h->d_train_pt1, pt1.data(), pt1.size() * 4, hipMemcpyHostToDevice));
-  HIP_TRY(h, hipMemcpy(h->d_dec_pt1, dpt1.data(), dpt1.size() * 4, hipMemcpyHostToDevice));
-  HIP_TRY(h, hipMemcpy(h->d_train_ptiles, ptl.data(), ptl.size() * 4, hipMemcpyHostToDevice));
-  HIP_TRY(h, hipMemcpy(h->d_dec_pt, dpt.data(), dpt.size() * 4, hipMemcpyHostToDevice));
-  HIP_TRY(h, hipMemcpy(h->d_dec_ptiles, dptl.data(), dptl.size() * 4, hipMemcpyHostToDevice));
-  // state
+  // phase tables: uploaded into their slot of the caller's workspace
+  // (pageable host sources: the stream is synchronised before they go out of scope)
+  std::vector<std::vector<int32_t>> keep;
+  size_t toff = h->cw.tables;
+  auto put = [&](size_t bytes) -> void* {
+    toff = (toff + 15) / 16 * 16;
+    void* dst = h->ws + toff;
+    toff += bytes;
+    return toff - h->cw.tables <= kTableBytes ? dst : nullptr;
+  };
+  for (auto [prog, dp] : {std::pair<std::vector<Phase>*, DevProg*>{&h->train, &h->dp_train}, {&h->dec, &h->dp_dec},
+                          {&h->eval, &h->dp_eval}}) {
+    keep.push_back(part_table(*prog, kMaxParts));
+    keep.push_back(part_table(*prog, 1));
+    keep.push_back(part_tile_table(*prog, kMaxParts));
+    const size_t k = keep.size();
+    dp->ph = (Phase*)put(prog->size() * sizeof(Phase));
+    dp->pt8 = (int32_t*)put(keep[k - 3].size() * 4);
+    dp->pt1 = (int32_t*)put(keep[k - 2].size() * 4);
+    dp->tiles8 = (int32_t*)put(keep[k - 1].size() * 4);
+    if (!dp->ph || !dp->pt8 || !dp->pt1 || !dp->tiles8) return fail(h, OFA_E_ARG, "phase tables exceed their slot");
+    HIP_TRY(h, hipMemcpyAsync(dp->ph, prog->data(), prog->size() * sizeof(Phase), hipMemcpyHostToDevice, h->stream));
+    HIP_TRY(h, hipMemcpyAsync(dp->pt8, keep[k - 3].data(), keep[k - 3].size() * 4, hipMemcpyHostToDevice, h->stream));
+    HIP_TRY(h, hipMemcpyAsync(dp->pt1, keep[k - 2].data(), keep[k - 2].size() * 4, hipMemcpyHostToDevice, h->stream));
+    HIP_TRY(h, hipMemcpyAsync(dp->tiles8, keep[k - 1].data(), keep[k - 1].size() * 4, hipMemcpyHostToDevice,
+                              h->stream));
+  }
+  static_assert(sizeof(Phase) <= 320, "phase table slot");
+  h->d_train = h->dp_train.ph;
+  h->d_dec = h->dp_dec.ph;
   char* ws = h->ws;
   const Carve& w = h->cw;
+  // Once per device: does workgroup b of a launch run on die b % 8?  The
+  // persistent executor's once-per-die release needs it; without it every
+  // ticket is released on its own (the probe writes into the misc block).
+  static int die_map_of[64];   // 0 = not probed, 1 = b % 8, 2 = another mapping
+  if (dev < 0 || dev >= 64 || die_map_of[dev] == 0) {
+    const int n = std::min<int>((int)(kMiscBytes / 4), std::max(kMaxParts, h->n_cu * std::max(1, persistent_occupancy(1))));
+    uint32_t* probe = at<uint32_t>(ws, w.misc);
+    std::vector<uint32_t> ids(n);
+    HIP_TRY(h, launch_xcc_probe(probe, n, h->stream));
+    HIP_TRY(h, hipMemcpyAsync(ids.data(), probe, (size_t)n * 4, hipMemcpyDeviceToHost, h->stream));
+    HIP_TRY(h, hipStreamSynchronize(h->stream));
+    bool ok = true;
+    for (int i = 0; i < n; ++i) ok = ok && ids[i] == (uint32_t)(i % kMaxParts);
+    if (dev >= 0 && dev < 64) die_map_of[dev] = ok ? 1 : 2;
+    h->die_map = ok;
+  } else {
+    h->die_map = die_map_of[dev] == 1;
+  }
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  // state
   const size_t P = h->D.P;
   HIP_TRY(h, hipMemcpyAsync(ws + w.p, dev_init_params, P * 4, hipMemcpyDeviceToDevice, h->stream));
   HIP_TRY(h, launch_fill_u32(at<uint32_t>(ws, w.m), 0, (int64_t)P, h->stream));
@@ -1379,7 +1454,10 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
   ofa_status s = ofa_set_params(h, at<float>(ws, w.p));
   if (s != OFA_OK) return s;
   h->version = 0;   // the initial weights are version 0
-  return publish(h);
+  s = publish(h);
+  if (s != OFA_OK) return s;
+  h->unpublished = false;
+  return OFA_OK;
 }
 
 ofa_status ofa_destroy(ofa_handle* h) {
@@ -1391,7 +1469,6 @@ ofa_status ofa_destroy(ofa_handle* h) {
   if (h->ev_upload) (void)hipEventDestroy(h->ev_upload);
   if (h->ev_t0) (void)hipEventDestroy(h->ev_t0);
   if (h->ev_t1) (void)hipEventDestroy(h->ev_t1);
-  if (h->d_alloc) (void)hipFree(h->d_alloc);
   delete h;
   return OFA_OK;
 }
@@ -1429,6 +1506,7 @@ ofa_status ofa_set_params(ofa_handle* h, const float* dev_params) {
   const int64_t P = h->D.P;
   if ((const char*)dev_params != ws + h->cw.p)
     HIP_TRY(h, hipMemcpyAsync(ws + h->cw.p, dev_params, P * 4, hipMemcpyDeviceToDevice, h->stream));
+  h->unpublished = true;
   if (h->cfg.precision == OFA_BF16) return copy_flat(h, ws + h->cw.p, DT_F32, ws + h->cw.wc, DT_BF16, P);
   return OFA_OK;
 }
@@ -1446,9 +1524,11 @@ ofa_status ofa_get_grads(ofa_handle* h, float* dev_grads) {
 }
 
 // serve copy <- compute weights, then the published version number
+// (two slots: version v lives in slot v & 1)
 static ofa_status publish(ofa_handle* h) {
   char* ws = h->ws;
-  ofa_status s = copy_flat(h, ws + h->cw.wc, h->D.lp_dt, ws + h->cw.serve, h->D.lp_dt, h->D.P);
+  const size_t slot = h->cw.n_slots > 1 ? (size_t)(h->version & 1) * (size_t)h->D.P * h->D.lp : 0;
+  ofa_status s = copy_flat(h, ws + h->cw.wc, h->D.lp_dt, ws + h->cw.serve + slot, h->D.lp_dt, h->D.P);
   if (s != OFA_OK) return s;
   HIP_TRY(h, launch_fill_u64(at<uint64_t>(ws, h->cw.published), h->version, 1, h->stream));
   return OFA_OK;
@@ -1458,13 +1538,15 @@ ofa_status ofa_publish_weights(ofa_handle* h, uint64_t* version_out) {
   if (!h) return OFA_E_ARG;
   ofa_status s = check_sticky(h);
   if (s != OFA_OK) return s;
-  if (h->cw.n_slots > 1) {   // co-resident configuration: every training step has published already
+  if (h->cw.n_slots > 1 && !h->unpublished) {
+    // co-resident configuration: every training step has published its weights already
     if (version_out) *version_out = h->version;
     return OFA_OK;
   }
   h->version += 1;
   s = publish(h);
   if (s != OFA_OK) return s;
+  h->unpublished = false;
   if (version_out) *version_out = h->version;
   return OFA_OK;
 }
@@ -1488,7 +1570,8 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
     sc.bc1 = (float)(1.0 - std::pow((double)c.beta1, (double)t));
     sc.bc2 = (float)(1.0 - std::pow((double)c.beta2, (double)t));
     sc.step_in_call = i;
-    sc.tag = t;
+    // co-resident configurations: the tag is the weight version the step publishes
+    sc.tag = h->cw.n_slots > 1 ? h->version + i + 1 : t;
   }
   StepCtx* d_steps = at<StepCtx>(h->ws, h->cw.steps);
   s = upload(h, d_steps, h->h_steps, sizeof(StepCtx) * n_steps);
@@ -1501,7 +1584,7 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
   HIP_TRY(h, launch_fill_pairs((uint64_t*)tm, ~0ull, 0ull, np, h->stream));
   HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
   if (c.exec_mode == OFA_EXEC_LAUNCH_PER_PHASE) {
-    s = run_launch_per_phase(h, h->train, h->d_train, d_steps, n_steps, (int64_t)h->steps_done, false);
+    s = run_launch_per_phase(h, h->train, h->d_train, d_steps, n_steps, (int64_t)h->steps_done, false, tm);
     if (s != OFA_OK) return s;
   } else {
     int cus = c.train_cus > 0 ? c.train_cus : h->n_cu;
@@ -1512,7 +1595,10 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
   HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
   h->timed = true;
   h->steps_done += n_steps;
-  if (h->cw.n_slots > 1) h->version = h->steps_done;   // co-resident configuration: each step published
+  if (h->cw.n_slots > 1) {   // co-resident configuration: each step published
+    h->version += n_steps;
+    h->unpublished = false;
+  }
   return OFA_OK;
 }
 
@@ -1554,7 +1640,7 @@ ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_
   HIP_TRY(h, launch_fill_pairs((uint64_t*)dtm, ~0ull, 0ull, (int64_t)h->dec.size(), h->stream));
   HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
   if (h->cfg.exec_mode == OFA_EXEC_LAUNCH_PER_PHASE)
-    s = run_launch_per_phase(h, h->dec, h->d_dec, d_dsteps, n_inst, 0, true);
+    s = run_launch_per_phase(h, h->dec, h->d_dec, d_dsteps, n_inst, 0, true, dtm);
   else
     s = run_persistent(h, h->dec, h->d_dec, d_dsteps, n_inst, h->cw.dsched, dtm, nullptr,
                        h->serve_wgs / std::max(1, persistent_occupancy(1)));
@@ -1593,7 +1679,8 @@ ofa_status ofa_train_and_serve(ofa_handle* h, const int32_t* dev_tokens, int32_t
     sc.bc1 = (float)(1.0 - std::pow((double)c.beta1, (double)t));
     sc.bc2 = (float)(1.0 - std::pow((double)c.beta2, (double)t));
     sc.step_in_call = i;
-    sc.tag = t;
+    // co-resident configurations: the tag is the weight version the step publishes
+    sc.tag = h->cw.n_slots > 1 ? h->version + i + 1 : t;
   }
   // decode: one restart period = the prompt reloaded, then restart_every tokens
   const int per_gen = c.restart_every > 0 ? c.restart_every : 512;
@@ -1650,7 +1737,251 @@ ofa_status ofa_train_and_serve(ofa_handle* h, const int32_t* dev_tokens, int32_t
   HIP_TRY(h, launch_fill_u32((uint32_t*)&st->serving, 0, 1, h->stream));
   h->timed = true;
   h->steps_done += n_steps;
-  h->version = h->steps_done;   // every step published its weights
+  h->version += n_steps;   // every step published its weights
+  h->unpublished = false;
+  return OFA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- SHA-256 (FIPS 180-4)
+
+namespace {
+
+// The hash's constants are the first 32 bits of the fractional parts of the
+// square roots (initial state, first 8 primes) and cube roots (round
+// constants, first 64 primes) of the primes, FIPS 180-4 sections 4.2.2 and
+// 5.3.3; they are derived here rather than tabulated.
+struct Sha256Consts {
+  uint32_t k[64], h0[8];
+  Sha256Consts() {
+    int primes[64], n = 0;
+    for (int c = 2; n < 64; ++c) {
+      bool prime = true;
+      for (int d = 2; d * d <= c; ++d) prime = prime && c % d;
+      if (prime) primes[n++] = c;
+    }
+    auto frac32 = [](long double x) { return (uint32_t)((x - std::floor(x)) * 4294967296.0L); };
+    for (int i = 0; i < 64; ++i) k[i] = frac32(std::cbrt((long double)primes[i]));
+    for (int i = 0; i < 8; ++i) h0[i] = frac32(std::sqrt((long double)primes[i]));
+  }
+};
+
+struct Sha256 {
+  uint32_t st[8];
+  uint8_t buf[64];
+  size_t fill = 0;
+  uint64_t total = 0;
+  static const Sha256Consts& K() {
+    static const Sha256Consts c;
+    return c;
+  }
+  Sha256() { memcpy(st, K().h0, sizeof st); }
+  static uint32_t rotr(uint32_t x, int n) { return (x >> n) | (x << (32 - n)); }
+  void block(const uint8_t* p) {
+    uint32_t w[64];
+    for (int i = 0; i < 16; ++i) w[i] = (uint32_t)p[4 * i] << 24 | (uint32_t)p[4 * i + 1] << 16 | (uint32_t)p[4 * i + 2] << 8 | p[4 * i + 3];
+    for (int i = 16; i < 64; ++i) {
+      const uint32_t s0 = rotr(w[i - 15], 7) ^ rotr(w[i - 15], 18) ^ (w[i - 15] >> 3);
+      const uint32_t s1 = rotr(w[i - 2], 17) ^ rotr(w[i - 2], 19) ^ (w[i - 2] >> 10);
+      w[i] = w[i - 16] + s0 + w[i - 7] + s1;
+    }
+    uint32_t a = st[0], b = st[1], c = st[2], d = st[3], e = st[4], f = st[5], g = st[6], hh = st[7];
+    for (int i = 0; i < 64; ++i) {
+      const uint32_t t1 = hh + (rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25)) + ((e & f) ^ (~e & g)) + K().k[i] + w[i];
+      const uint32_t t2 = (rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22)) + ((a & b) ^ (a & c) ^ (b & c));
+      hh = g; g = f; f = e; e = d + t1; d = c; c = b; b = a; a = t1 + t2;
+    }
+    st[0] += a; st[1] += b; st[2] += c; st[3] += d; st[4] += e; st[5] += f; st[6] += g; st[7] += hh;
+  }
+  void update(const void* data, size_t n) {
+    const uint8_t* p = (const uint8_t*)data;
+    total += n;
+    while (n) {
+      if (fill == 0 && n >= 64) {   // whole blocks straight from the input
+        block(p);
+        p += 64;
+        n -= 64;
+        continue;
+      }
+      const size_t take = std::min(n, 64 - fill);
+      memcpy(buf + fill, p, take);
+      fill += take;
+      p += take;
+      n -= take;
+      if (fill == 64) {
+        block(buf);
+        fill = 0;
+      }
+    }
+  }
+  void final(uint8_t out[32]) {
+    const uint64_t bits = total * 8;
+    const uint8_t one = 0x80, zero = 0;
+    update(&one, 1);
+    while (fill != 56) update(&zero, 1);
+    uint8_t len[8];
+    for (int i = 0; i < 8; ++i) len[i] = (uint8_t)(bits >> (56 - 8 * i));
+    update(len, 8);
+    for (int i = 0; i < 8; ++i)
+      for (int j = 0; j < 4; ++j) out[4 * i + j] = (uint8_t)(st[i] >> (24 - 8 * j));
+  }
+};
+
+// Checkpoint blob: this header, then the fp32 master weights, the AdamW first
+// and second moments (ofa_param_count scalars each).
+constexpr char kCkptMagic[8] = {'O', 'F', 'A', 'C', 'K', 'P', 'T', '1'};
+static_assert(sizeof(ofa_checkpoint_header) == 256, "checkpoint header size");
+
+// SHA-256 over the values that define the model and its optimizer (the state
+// a checkpoint holds is only meaningful for these)
+void model_fingerprint(const ofa_config& c, uint8_t out[32]) {
+  const int32_t iv[] = {c.n_layer, c.d_model, c.n_head, c.d_ff, c.vocab, c.n_pos, c.mlp_gated, c.tied_head,
+                        c.has_bias, c.precision, c.lr_schedule, c.total_steps};
+  const float fv[] = {c.lr, c.beta1, c.beta2, c.eps, c.weight_decay};
+  Sha256 sh;
+  sh.update(iv, sizeof iv);
+  sh.update(fv, sizeof fv);
+  sh.final(out);
+}
+
+// SHA-256 of n bytes of device memory (the stream is synchronised first)
+ofa_status sha256_device(ofa_handle* h, const void* dev, size_t n, uint8_t out[32]) {
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  std::vector<uint8_t> host(std::min<size_t>(n, (size_t)64 << 20));
+  Sha256 sh;
+  for (size_t off = 0; off < n; off += host.size()) {
+    const size_t len = std::min(host.size(), n - off);
+    HIP_TRY(h, hipMemcpy(host.data(), (const char*)dev + off, len, hipMemcpyDeviceToHost));
+    sh.update(host.data(), len);
+  }
+  sh.final(out);
+  return OFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ofa_status ofa_sha256(const void* host_data, size_t n, uint8_t* out32) {
+  if ((!host_data && n) || !out32) return OFA_E_ARG;
+  Sha256 sh;
+  sh.update(host_data, n);
+  sh.final(out32);
+  return OFA_OK;
+}
+
+size_t ofa_checkpoint_bytes(const ofa_config* cfg) {
+  const int64_t P = ofa_param_count(cfg);
+  return P < 0 ? 0 : sizeof(ofa_checkpoint_header) + 3 * (size_t)P * 4;
+}
+
+ofa_status ofa_checkpoint_save(ofa_handle* h, void* dev_ckpt, const uint8_t* note32, uint8_t* sha256_out) {
+  if (!h || !dev_ckpt) return fail(h, OFA_E_ARG, "bad arguments");
+  // allowed after a device error too: the state can be read back for inspection
+  ofa_status s = staging_ready(h);
+  if (s != OFA_OK) return s;
+  ofa_checkpoint_header hd;
+  memset(&hd, 0, sizeof hd);
+  memcpy(hd.magic, kCkptMagic, 8);
+  hd.n_params = (uint64_t)h->D.P;
+  hd.steps_done = h->steps_done;
+  hd.version = h->version;
+  model_fingerprint(h->cfg, hd.model_sha256);
+  memcpy(hd.parent_sha256, h->lineage, 32);
+  if (note32) memcpy(hd.note, note32, 32);
+  static_assert(sizeof hd <= kMiscDecIO, "staging");
+  memcpy(h->h_misc, &hd, sizeof hd);
+  char* dst = (char*)dev_ckpt;
+  s = upload(h, dst, h->h_misc, sizeof hd);
+  if (s != OFA_OK) return s;
+  s = mark_upload(h);
+  if (s != OFA_OK) return s;
+  const size_t pb = (size_t)h->D.P * 4;
+  const size_t src[3] = {h->cw.p, h->cw.m, h->cw.v};
+  for (int i = 0; i < 3; ++i)
+    HIP_TRY(h, hipMemcpyAsync(dst + sizeof hd + i * pb, h->ws + src[i], pb, hipMemcpyDeviceToDevice, h->stream));
+  uint8_t sha[32];
+  s = sha256_device(h, dst, sizeof hd + 3 * pb, sha);
+  if (s != OFA_OK) return s;
+  memcpy(h->lineage, sha, 32);
+  if (sha256_out) memcpy(sha256_out, sha, 32);
+  return OFA_OK;
+}
+
+ofa_status ofa_checkpoint_load(ofa_handle* h, const void* dev_ckpt, uint8_t* sha256_out) {
+  if (!h || !dev_ckpt) return fail(h, OFA_E_ARG, "bad arguments");
+  ofa_status s = check_sticky(h);
+  if (s != OFA_OK) return s;
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  ofa_checkpoint_header hd;
+  HIP_TRY(h, hipMemcpy(&hd, dev_ckpt, sizeof hd, hipMemcpyDeviceToHost));
+  uint8_t fp[32];
+  model_fingerprint(h->cfg, fp);
+  if (memcmp(hd.magic, kCkptMagic, 8)) return fail(h, OFA_E_ARG, "not a checkpoint of this library");
+  if (hd.n_params != (uint64_t)h->D.P) return fail(h, OFA_E_ARG, "checkpoint holds %llu parameters, model has %lld",
+                                                   (unsigned long long)hd.n_params, (long long)h->D.P);
+  if (memcmp(hd.model_sha256, fp, 32)) return fail(h, OFA_E_ARG, "checkpoint of another model or optimizer configuration");
+  const size_t pb = (size_t)h->D.P * 4;
+  uint8_t sha[32];
+  s = sha256_device(h, dev_ckpt, sizeof hd + 3 * pb, sha);
+  if (s != OFA_OK) return s;
+  const char* src = (const char*)dev_ckpt + sizeof hd;
+  const size_t dst[3] = {h->cw.p, h->cw.m, h->cw.v};
+  for (int i = 0; i < 3; ++i)
+    HIP_TRY(h, hipMemcpyAsync(h->ws + dst[i], src + i * pb, pb, hipMemcpyDeviceToDevice, h->stream));
+  h->steps_done = hd.steps_done;
+  s = ofa_set_params(h, at<float>(h->ws, h->cw.p));   // the compute copy
+  if (s != OFA_OK) return s;
+  h->version = hd.version;
+  s = publish(h);
+  if (s != OFA_OK) return s;
+  h->unpublished = false;
+  memcpy(h->lineage, sha, 32);
+  if (sha256_out) memcpy(sha256_out, sha, 32);
+  return OFA_OK;
+}
+
+ofa_status ofa_evaluate(ofa_handle* h, const int32_t* dev_tokens, int32_t n_batches, float* dev_losses,
+                        float* dev_row_losses, const int32_t* dev_probe_rows, int32_t n_probe,
+                        int32_t* dev_probe_argmax, float* dev_probe_entropy) {
+  if (!h || !dev_tokens || !dev_losses || n_batches < 1 || n_probe < 0 || (n_probe && !dev_probe_rows))
+    return fail(h, OFA_E_ARG, "bad arguments");
+  if (n_batches > kMaxSteps) return fail(h, OFA_E_ARG, "n_batches %d > %d", n_batches, kMaxSteps);
+  if (n_probe > kMaxProbe) return fail(h, OFA_E_ARG, "n_probe %d > %d", n_probe, kMaxProbe);
+  ofa_status s = check_sticky(h);
+  if (s != OFA_OK) return s;
+  s = staging_ready(h);
+  if (s != OFA_OK) return s;
+  const int64_t per = h->D.B * (h->D.T + 1), BT = h->D.BT;
+  for (int i = 0; i < n_batches; ++i) {
+    StepCtx& sc = h->h_steps[i];
+    memset(&sc, 0, sizeof sc);
+    sc.tokens = dev_tokens + per * i;
+    sc.loss_out = dev_losses + i;
+    sc.step_in_call = i;
+    sc.rows_out = dev_row_losses ? dev_row_losses + BT * i : nullptr;
+    sc.n_probe = n_probe;
+    sc.probe_rows = n_probe ? dev_probe_rows : nullptr;
+    sc.probe_argmax = dev_probe_argmax ? dev_probe_argmax + (int64_t)n_probe * i : nullptr;
+    sc.probe_entropy = dev_probe_entropy ? dev_probe_entropy + (int64_t)n_probe * i : nullptr;
+  }
+  StepCtx* d_steps = at<StepCtx>(h->ws, h->cw.steps);
+  s = upload(h, d_steps, h->h_steps, sizeof(StepCtx) * n_batches);
+  if (s != OFA_OK) return s;
+  s = mark_upload(h);
+  if (s != OFA_OK) return s;
+  HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
+  if (h->cfg.exec_mode == OFA_EXEC_LAUNCH_PER_PHASE) {
+    s = run_launch_per_phase(h, h->eval, h->dp_eval.ph, d_steps, n_batches, 0, false, nullptr);
+  } else {
+    const int cus = h->cfg.train_cus > 0 ? h->cfg.train_cus : h->n_cu;
+    s = run_persistent(h, h->eval, h->dp_eval.ph, d_steps, n_batches, h->cw.sched, nullptr, nullptr, cus,
+                       h->train_occ);
+  }
+  if (s != OFA_OK) return s;
+  HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
+  h->timed = true;
   return OFA_OK;
 }
 

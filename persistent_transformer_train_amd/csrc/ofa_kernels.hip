@@ -79,6 +79,7 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   else if constexpr (OP == OP_DEC_ARGMAX) { OFA_ARGS(dargmax); task_dec_argmax(a, tile, tc, smem); }
   else if constexpr (OP == OP_SLOT_GUARD) { OFA_ARGS(guard); task_slot_guard(a, tc); }
   else if constexpr (OP == OP_PUBLISH) { OFA_ARGS(publish); task_publish(a, tc); }
+  else if constexpr (OP == OP_PROBE) { OFA_ARGS(probe); task_probe(a, tile, tc, smem); }
 }
 #undef OFA_ARGS
 
@@ -92,6 +93,7 @@ __device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& t
     OFA_CASE(OP_ATTN_BWD_KV) OFA_CASE(OP_ATTN_BWD_Q) OFA_CASE(OP_ROPE_BWD) OFA_CASE(OP_EMB_SORT)
     OFA_CASE(OP_EMB_BWD) OFA_CASE(OP_ADAMW) OFA_CASE(OP_COPY) OFA_CASE(OP_DEC_EMBED)
     OFA_CASE(OP_DEC_ATTN) OFA_CASE(OP_DEC_ARGMAX) OFA_CASE(OP_SLOT_GUARD) OFA_CASE(OP_PUBLISH)
+    OFA_CASE(OP_PROBE)
     // OP_DEC_GEMV runs through run_dec_gemv (whole tickets, prefetched); keeping it
     // out of this switch keeps its registers out of every other task's call
 #undef OFA_CASE
@@ -317,16 +319,21 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
       }
       run_any<OCC>(ph, tl, tc, smem);
     }
-    // publish: the barrier makes every wave's stores complete; an agent-scope
-    // release fence (per ticket, or once per die and phase) then makes them
-    // visible before the counter moves
+    // publish: an agent-scope release fence (per ticket, or once per die and
+    // phase) makes the tile's stores visible before the counter moves.  With
+    // the once-per-die release every wave first waits until its own stores are
+    // complete in the die's L2 (vmcnt counts a store until the L2 has taken
+    // it); the barrier then puts all of them before thread 0's counter add.
+    if (J.die_release) asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
       if (J.trace && inst < J.trace_inst)
         atomicMax((unsigned long long*)&J.trace[4 * (inst * J.n_phases + pi) + 2], (unsigned long long)now_ticks());
       if (J.die_release) {
-        // this die's share of the phase completes with this ticket: one
-        // write-back of the die's L2 covers every workgroup of the die
+        // Every workgroup of the die had its stores in the die's L2 before its
+        // add; the add that completes the die's share of the phase comes after
+        // all of them, so one write-back of that L2 (the agent-scope release)
+        // by that workgroup covers the whole share.
         fence_release_workgroup();
         const uint64_t share = (uint64_t)J.part_tiles[part * J.n_phases + pi];
         const uint64_t prev = add_relaxed(&J.sched->part_done[pi * kMaxParts + part], (uint64_t)(tile1 - tile0));
@@ -354,6 +361,11 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
 }
 
 // ---------------------------------------------------------------- small utility kernels
+
+// out[b] = the die (XCD) workgroup b runs on
+__global__ void xcc_probe_kernel(uint32_t* out, int n) {
+  if (threadIdx.x == 0 && (int)blockIdx.x < n) out[blockIdx.x] = xcc_id();
+}
 
 __global__ void fill_u64_kernel(uint64_t* p, uint64_t v, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
@@ -393,6 +405,7 @@ static size_t lds_for(const Phase& ph) {
     case OP_DEC_GEMV: return dec_gemv_lds_bytes(ph.a.dgemv);
     case OP_DEC_ATTN: return dec_attn_lds_bytes(ph.a.dattn);
     case OP_DEC_ARGMAX: return 2048;
+    case OP_PROBE: return 256;
     default: return 0;
   }
 }
@@ -495,21 +508,31 @@ hipError_t launch_phase(const Phase& h, const Phase* d_phases, int idx, const St
     OFA_LAUNCH(OP_ATTN_BWD_KV) OFA_LAUNCH(OP_ATTN_BWD_Q) OFA_LAUNCH(OP_ROPE_BWD) OFA_LAUNCH(OP_EMB_SORT)
     OFA_LAUNCH(OP_EMB_BWD) OFA_LAUNCH(OP_ADAMW) OFA_LAUNCH(OP_COPY) OFA_LAUNCH(OP_DEC_EMBED)
     OFA_LAUNCH(OP_DEC_GEMV) OFA_LAUNCH(OP_DEC_ATTN) OFA_LAUNCH(OP_DEC_ARGMAX) OFA_LAUNCH(OP_SLOT_GUARD)
-    OFA_LAUNCH(OP_PUBLISH)
+    OFA_LAUNCH(OP_PUBLISH) OFA_LAUNCH(OP_PROBE)
 #undef OFA_LAUNCH
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// Cooperative launches: every workgroup is resident at once, and (measured)
+// workgroup b runs on die b % 8.  A plain launch of the same kernel did not keep
+// that placement (a 32-workgroup launch put a workgroup on another die), and the
+// once-per-die release depends on it.
 hipError_t launch_persistent(const PersistParams& p, int grid, hipStream_t s, int occ) {
   (void)hipGetLastError();
   void* args[] = {(void*)&p};
-  if (occ == 2)
-    return hipLaunchCooperativeKernel((const void*)persistent_kernel<2>, dim3(grid), dim3(kThreads), args,
-                                      g_persist_lds2, s);
-  return hipLaunchCooperativeKernel((const void*)persistent_kernel<1>, dim3(grid), dim3(kThreads), args,
-                                    g_persist_lds, s);
+  const void* fn = occ == 2 ? (const void*)persistent_kernel<2> : (const void*)persistent_kernel<1>;
+  const size_t lds = occ == 2 ? g_persist_lds2 : g_persist_lds;
+  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, lds, s);
+}
+
+// the same kind of launch as the persistent kernel's
+hipError_t launch_xcc_probe(uint32_t* out, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  (void)hipGetLastError();
+  void* args[] = {(void*)&out, (void*)&n};
+  return hipLaunchCooperativeKernel((const void*)xcc_probe_kernel, dim3(n), dim3(kThreads), args, 0, s);
 }
 
 hipError_t launch_fill_u64(uint64_t* p, uint64_t v, int64_t n, hipStream_t s) {

@@ -43,6 +43,7 @@ enum Op : int32_t {
   OP_DEC_ARGMAX,   // decode: argmax over the logits, emit the token
   OP_SLOT_GUARD,   // co-resident training: wait until decode no longer reads the slot AdamW writes
   OP_PUBLISH,      // co-resident training: release the step's weights as a new version
+  OP_PROBE,        // evaluation: argmax and prediction entropy of the logits at chosen rows
   OP_COUNT
 };
 
@@ -146,14 +147,19 @@ struct GegluArgs {
 
 struct CeArgs {
   const float* logits;  // [rows][V]
-  void* dz;             // [rows][V] (dt)
+  void* dz;             // [rows][V] (dt); null: loss only (evaluation)
   float* loss_rows;     // [rows]
   int32_t rows, V, T, dt;
   float inv_rows;
 };
 
 struct LossArgs {
-  const float* loss_rows; int32_t rows;
+  const float* loss_rows; int32_t rows;   // per-row losses also go to StepCtx::rows_out when set
+};
+
+struct ProbeArgs {
+  const float* logits;  // [rows][V]; the rows probed come from StepCtx::probe_rows
+  int32_t rows, V;
 };
 
 struct EmbSortArgs {
@@ -281,7 +287,7 @@ union PhaseArgs {
   EmbedArgs emb; AttnArgs attn; RopeArgs rope; GegluArgs geglu; CeArgs ce;
   LossArgs loss; EmbSortArgs esort; EmbBwdArgs ebwd; AdamArgs adam; CopyArgs copy;
   DecEmbedArgs dembed; DecGemvArgs dgemv; DecAttnArgs dattn; DecArgmaxArgs dargmax;
-  GuardArgs guard; PublishArgs publish;
+  GuardArgs guard; PublishArgs publish; ProbeArgs probe;
 };
 
 constexpr int kMaxDeps = 4;
@@ -313,7 +319,14 @@ struct StepCtx {
                            // bit 1 = first position of a token (acquire the newest weights),
                            // bit 2 = restart: reload the saved prompt as the context
   int32_t gen_idx;         // decode: index of the emitted token in the call
-  int32_t pad;
+  int32_t n_probe;         // evaluation: rows probed (entries of probe_rows)
+  // evaluation outputs of this instance (each nullable): per-row losses [rows],
+  // and at probe_rows[i]: the argmax token (lowest id on ties) and the entropy
+  // of the predicted distribution in nats
+  float* rows_out;
+  const int32_t* probe_rows;
+  int32_t* probe_argmax;
+  float* probe_entropy;
 };
 
 constexpr int kMaxPhases = 512;

@@ -43,6 +43,14 @@ class ofa_config(C.Structure):
     ]
 
 
+class ofa_checkpoint_header(C.Structure):
+    _fields_ = [
+        ("magic", C.c_char * 8), ("n_params", C.c_uint64), ("steps_done", C.c_uint64), ("version", C.c_uint64),
+        ("model_sha256", C.c_uint8 * 32), ("parent_sha256", C.c_uint8 * 32), ("note", C.c_uint8 * 32),
+        ("reserved", C.c_uint8 * 128),
+    ]
+
+
 class ofa_stats(C.Structure):
     _fields_ = [
         ("status", C.c_int32), ("err_phase", C.c_int32), ("err_step", C.c_int64), ("err_info", C.c_int64),
@@ -77,6 +85,11 @@ _sig = {
     "ofa_trace": (C.c_int, [_H, C.c_int32, C.POINTER(C.c_uint64), C.c_int64, C.POINTER(C.c_int64),
                             C.POINTER(C.c_int32)]),
     "ofa_task_budget": (C.c_int, [C.c_uint64, C.c_uint64, C.POINTER(C.c_uint64)]),
+    "ofa_evaluate": (C.c_int, [_H, _P, C.c_int32, _P, _P, _P, C.c_int32, _P, _P]),
+    "ofa_checkpoint_bytes": (C.c_size_t, [C.POINTER(ofa_config)]),
+    "ofa_checkpoint_save": (C.c_int, [_H, _P, C.c_char_p, C.c_char_p]),
+    "ofa_checkpoint_load": (C.c_int, [_H, _P, C.c_char_p]),
+    "ofa_sha256": (C.c_int, [C.c_char_p, C.c_size_t, C.c_char_p]),
     "ofa_last_error": (C.c_char_p, [_H]),
     "ofa_status_string": (C.c_char_p, [C.c_int]),
     "ofa_destroy": (C.c_int, [_H]),
@@ -185,6 +198,31 @@ class Handle:
                                         0 if versions_ring is None else versions_ring.data_ptr(),
                                         tokens_ring.numel(), 0 if n_generated is None else n_generated.data_ptr()))
 
+    def evaluate(self, tokens, losses, row_losses=None, probe_rows=None, probe_argmax=None, probe_entropy=None):
+        """Forward-only scoring of tokens [n][B][T+1]: mean loss per batch into losses [n],
+        per-row losses into row_losses [n][B*T], and at the flat rows probe_rows [k] the
+        argmax token and prediction entropy into probe_argmax / probe_entropy [n][k]."""
+        assert tokens.dtype == self.torch.int32 and tokens.is_cuda and tokens.is_contiguous()
+        k = 0 if probe_rows is None else probe_rows.numel()
+        p = lambda t: 0 if t is None else t.data_ptr()
+        self._check(ofa_evaluate(self.h, tokens.data_ptr(), tokens.shape[0], losses.data_ptr(), p(row_losses),
+                                 p(probe_rows), k, p(probe_argmax), p(probe_entropy)))
+
+    def checkpoint_bytes(self) -> int:
+        return ofa_checkpoint_bytes(C.byref(self.cfg))
+
+    def checkpoint_save(self, dev_buf, note: bytes = None) -> bytes:
+        """Training state into the uint8 device tensor dev_buf; returns its SHA-256."""
+        assert dev_buf.is_cuda and dev_buf.numel() * dev_buf.element_size() >= self.checkpoint_bytes()
+        out = C.create_string_buffer(32)
+        self._check(ofa_checkpoint_save(self.h, dev_buf.data_ptr(), note, out))
+        return out.raw
+
+    def checkpoint_load(self, dev_buf) -> bytes:
+        out = C.create_string_buffer(32)
+        self._check(ofa_checkpoint_load(self.h, dev_buf.data_ptr(), out))
+        return out.raw
+
     def get_params(self):
         out = self.torch.empty(self.n_params, dtype=self.torch.float32, device=self.device)
         self._check(ofa_get_params(self.h, out.data_ptr()))
@@ -242,3 +280,12 @@ class Handle:
             self.close()
         except Exception:
             pass
+
+
+def sha256(data: bytes) -> bytes:
+    """The library's SHA-256 of a host byte string."""
+    out = C.create_string_buffer(32)
+    rc = ofa_sha256(data, len(data), out)
+    if rc != OFA_OK:
+        raise OfaError(rc, "sha256")
+    return out.raw

@@ -67,3 +67,16 @@ def cosine(a, b) -> float:
     a = np.asarray(a, np.float64).ravel()
     b = np.asarray(b, np.float64).ravel()
     return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
+
+
+def rel_err(a, b) -> float:
+    """||a - b|| / ||b|| in float64 (0 when both are zero)."""
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
+
+
+def per_tensor_rel_err(layout, g_gpu, g_or):
+    """{tensor name: relative error} over the canonical layout."""
+    return {n: rel_err(g_gpu[o:o + k], g_or[o:o + k]) for n, o, k, _ in layout}

@@ -1,0 +1,197 @@
+"""Checkpoint / resume with SHA-256 lineage, forward-only evaluation and the
+prompt probe, through the C ABI.
+
+"Coppelius training on the RTX 3090": each invocation resumes the checkpoint
+the one before wrote ("Checkpoint lineage"); the first step of an invocation is
+scored on a context the model has not trained on ("Loss"); per-row losses
+("Sampled rows", "Per-row spread"); the most likely next token at chosen rows
+("Prompt probe") and its entropy ("Prediction entropy").
+"""
+
+import ctypes as C
+
+import numpy as np
+import pytest
+
+from gpu_common import cfg_of, init_of, log, spec_from_cfg, stream_of
+from oracle import decode, gpt
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+PER_PHASE, PERSISTENT = 1, 0
+
+
+def header_of(buf):
+    from persistent_transformer_train_amd import ofa
+    raw = buf[:256].cpu().numpy().tobytes()
+    return ofa.ofa_checkpoint_header.from_buffer_copy(raw)
+
+
+@pytest.mark.parametrize("name", ["c1", "m3"])
+@pytest.mark.parametrize("exec_mode", [PER_PHASE, PERSISTENT], ids=["per_phase", "persistent"])
+def test_resume_is_bit_identical_and_lineage_chains(name, exec_mode):
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of(name, exec_mode=exec_mode)
+    stream = stream_of(name, cfg)
+    init = np.asarray(init_of(name, cfg), np.float32)
+    toks = torch.from_numpy(stream.batches(0, 6)).cuda()
+    # uninterrupted: 6 steps
+    a = ofa.Handle(cfg, init)
+    la = torch.zeros(6, dtype=torch.float32, device="cuda")
+    a.train_step(toks, la)
+    a.sync()
+    ck_a = torch.zeros(a.checkpoint_bytes(), dtype=torch.uint8, device="cuda")
+    a.checkpoint_save(ck_a)
+    # interrupted: 3 steps, checkpoint, a new handle from other weights, load, 3 steps
+    b = ofa.Handle(cfg, init)
+    lb = torch.zeros(6, dtype=torch.float32, device="cuda")
+    b.train_step(toks[:3].contiguous(), lb[:3])
+    ck = torch.zeros(b.checkpoint_bytes(), dtype=torch.uint8, device="cuda")
+    note = bytes(range(32))
+    sha1 = b.checkpoint_save(ck, note)
+    b.close()
+    hd = header_of(ck)
+    assert hd.magic == b"OFACKPT1" and hd.steps_done == 3 and hd.n_params == len(init)
+    assert bytes(hd.parent_sha256) == bytes(32) and bytes(hd.note) == note
+    import hashlib
+    assert hashlib.sha256(ck.cpu().numpy().tobytes()).digest() == sha1
+    c = ofa.Handle(cfg, (init * 0.5).astype(np.float32))
+    assert c.checkpoint_load(ck) == sha1
+    c.train_step(toks[3:].contiguous(), lb[3:])
+    c.sync()
+    log(f"{name}: uninterrupted {la.cpu().numpy()[3:]}, resumed {lb.cpu().numpy()[3:]}")
+    assert la.cpu().numpy().tobytes() == lb.cpu().numpy().tobytes()
+    assert c.get_params().cpu().numpy().tobytes() == a.get_params().cpu().numpy().tobytes()
+    # the whole state (weights and both moments) equals the uninterrupted run's
+    ck_c = torch.zeros(c.checkpoint_bytes(), dtype=torch.uint8, device="cuda")
+    sha2 = c.checkpoint_save(ck_c)
+    assert torch.equal(ck_c[256:], ck_a[256:])
+    hd2 = header_of(ck_c)
+    assert bytes(hd2.parent_sha256) == sha1 and hd2.steps_done == 6
+    assert sha2 != sha1
+    # the loaded weights were published: decode reads the checkpoint's version
+    assert c.publish() == hd2.version + 1
+    a.close()
+    c.close()
+
+
+def test_checkpoint_of_another_model_is_rejected():
+    from persistent_transformer_train_amd import ofa
+    c1 = cfg_of("c1", exec_mode=PERSISTENT)
+    h = ofa.Handle(c1, init_of("c1", c1))
+    ck = torch.zeros(h.checkpoint_bytes(), dtype=torch.uint8, device="cuda")
+    h.checkpoint_save(ck)
+    h.close()
+    other = dict(c1, lr=2e-3)      # same shapes, another optimizer setting
+    g = ofa.Handle(other, init_of("c1", other))
+    with pytest.raises(ofa.OfaError) as e:
+        g.checkpoint_load(ck)
+    assert e.value.code == ofa.OFA_E_ARG
+    g.close()
+
+
+def test_bad_token_leaves_weights_and_moments_untouched():
+    """A token out of range sets OFA_E_ARG and the step's update is skipped: the
+    master weights and both AdamW moments are bit-identical before and after."""
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of("c1", exec_mode=PERSISTENT)
+    stream = stream_of("c1", cfg)
+    h = ofa.Handle(cfg, init_of("c1", cfg))
+    losses = torch.zeros(2, dtype=torch.float32, device="cuda")
+    h.train_step(torch.from_numpy(stream.batches(0, 2)).cuda(), losses)   # moments are non-zero now
+    h.sync()
+    before = torch.zeros(h.checkpoint_bytes(), dtype=torch.uint8, device="cuda")
+    h.checkpoint_save(before)
+    tok = stream.batches(2, 2)
+    tok[0, 2, 7] = -3
+    h.train_step(torch.from_numpy(tok).cuda(), losses)
+    with pytest.raises(ofa.OfaError) as e:
+        h.sync()
+    assert e.value.code == ofa.OFA_E_ARG
+    after = torch.zeros_like(before)
+    h.checkpoint_save(after)
+    assert torch.equal(before[256:], after[256:])
+    h.close()
+
+
+def oracle_eval(cfg, params, tokens):
+    s = spec_from_cfg(cfg)
+    loss, cache = gpt.forward(s, gpt.unflatten(s, np.asarray(params, np.float64)), tokens, keep=False)
+    return float(loss), cache["nll"], cache["z"]
+
+
+@pytest.mark.parametrize("name,tol", [("c1", 1e-4), ("m3", 2e-2), ("m2", 2e-2)])
+@pytest.mark.parametrize("exec_mode", [PER_PHASE, PERSISTENT], ids=["per_phase", "persistent"])
+def test_evaluate_matches_oracle_and_training_loss(name, tol, exec_mode):
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of(name, exec_mode=exec_mode)
+    stream = stream_of(name, cfg)
+    h = ofa.Handle(cfg, init_of(name, cfg))
+    l = torch.zeros(3, dtype=torch.float32, device="cuda")
+    h.train_step(torch.from_numpy(stream.batches(0, 3)).cuda(), l)     # some training first
+    h.sync()
+    p = h.get_params().cpu().numpy()
+    BT = cfg["batch"] * cfg["seq"]
+    rows = np.array([0, BT // 3, BT // 2 + 1, BT - 1], np.int32)
+    n = 2
+    toks = torch.from_numpy(stream.batches(3, n)).cuda()                # unseen batches
+    losses = torch.zeros(n, dtype=torch.float32, device="cuda")
+    row_l = torch.zeros(n, BT, dtype=torch.float32, device="cuda")
+    am = torch.zeros(n, len(rows), dtype=torch.int32, device="cuda")
+    ent = torch.zeros(n, len(rows), dtype=torch.float32, device="cuda")
+    h.evaluate(toks, losses, row_l, torch.from_numpy(rows).cuda(), am, ent)
+    h.sync()
+    # evaluation changes nothing
+    assert h.get_params().cpu().numpy().tobytes() == p.tobytes()
+    for i in range(n):
+        lo, nll, z = oracle_eval(cfg, p, stream.batch(3 + i))
+        dl = abs(float(losses[i]) - lo)
+        dr = np.abs(row_l[i].cpu().numpy() - nll).max()
+        de = np.abs(ent[i].cpu().numpy() - gpt.prediction_entropy(z[rows])).max()
+        log(f"{name} batch {i}: loss gpu {float(losses[i]):.6f} oracle {lo:.6f}; max row err {dr:.3g}; "
+            f"max entropy err {de:.3g}")
+        assert dl <= (tol * abs(lo) if tol < 1e-3 else tol)
+        assert dr <= (1e-3 if tol < 1e-3 else 0.1)
+        assert de <= (1e-3 if tol < 1e-3 else 0.05)
+        for k, r in enumerate(rows):
+            if decode.top2_margin(z[r]) > (1e-4 if tol < 1e-3 else 1e-1):
+                assert int(am[i, k]) == decode.argmax_lowest(z[r]), (i, k, r)
+    # the training step's loss on the next batch equals the evaluation of that batch
+    # at the same weights, bit for bit (same forward kernels)
+    h.train_step(toks[:1].contiguous(), l)
+    h.sync()
+    assert float(l[0]) == float(losses[0])
+    h.close()
+
+
+def test_full_size_evaluate_c3_probe_rows():
+    """The 162M workload's evaluation at its seeded init on an unseen batch, with the
+    probe at rows 255 and 511 of the first two sequences (the RTX 3090 page probes
+    rows 255, 511 and 1023 of its one 1,024-token context): loss and entropies
+    against the oracle's fp32 forward, argmax where the oracle's margin is clear."""
+    from persistent_transformer_train_amd import ofa
+    cfg = cfg_of("c3", exec_mode=PERSISTENT)
+    stream = stream_of("c3", cfg)
+    init = init_of("c3", cfg)
+    h = ofa.Handle(cfg, init)
+    rows = np.array([255, 511, 512 + 255, 512 + 511], np.int32)
+    toks = torch.from_numpy(stream.batches(7, 1)).cuda()
+    losses = torch.zeros(1, dtype=torch.float32, device="cuda")
+    am = torch.zeros(1, 4, dtype=torch.int32, device="cuda")
+    ent = torch.zeros(1, 4, dtype=torch.float32, device="cuda")
+    h.evaluate(toks, losses, None, torch.from_numpy(rows).cuda(), am, ent)
+    h.sync()
+    h.close()
+    s = spec_from_cfg(cfg)
+    lo, cache = gpt.forward(s, gpt.unflatten(s, np.asarray(init, np.float32)), stream.batch(7), dtype=np.float32,
+                            keep=False)
+    z = cache["z"][rows].astype(np.float64)
+    H = gpt.prediction_entropy(z)
+    log(f"c3 eval: loss gpu {float(losses[0]):.5f} oracle {float(lo):.5f}; entropy gpu {ent.cpu().numpy()} "
+        f"oracle {H}; argmax gpu {am.cpu().numpy()} oracle {z.argmax(1)}")
+    assert abs(float(losses[0]) - float(lo)) <= 2e-2
+    assert np.abs(ent[0].cpu().numpy() - H).max() <= 2e-2
+    for k in range(4):
+        if decode.top2_margin(z[k]) > 5e-2:
+            assert int(am[0, k]) == int(z[k].argmax())

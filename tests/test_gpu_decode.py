@@ -119,14 +119,20 @@ def test_decode_after_training_reads_published_weights():
 
 @pytest.mark.parametrize("name", ["c4", "c2"])
 def test_full_size_decode(name):
-    # Full-size models, one persistent launch on 48 CUs, 48 tokens after a
+    # Full-size models, one persistent launch on 48 CUs, all 512 tokens after a
     # 32-token prompt: c4 is the decode workload the benchmark times (the 162M
-    # model, 512-token window); c2 takes the rotary, gated-MLP, tied-head path.
-    # The oracle recomputes the logits along the GPU's tokens (bf16 weights).
-    n_new = 48
+    # model, 512-token window: after 480 generated tokens the context restarts
+    # from its last 32 tokens, so the re-prefill and 32 tokens after it are
+    # checked too); c2 takes the rotary, gated-MLP, tied-head path.  The oracle
+    # recomputes the logits along the GPU's tokens (bf16 weights).
+    n_new = 512
     h, cfg, init, prompt, toks, logits, vers = run_decode(name, n_new, exec_mode=0, serve_cus=48)
     assert np.all(vers == 1)
     w_bf16 = torch.tensor(init).to(torch.bfloat16).to(torch.float32).numpy()
     checked = check_against_oracle(cfg, w_bf16, prompt, toks, logits, np.float64, 2e-2)
     assert checked >= n_new // 2
+    if name == "c4":
+        # tokens after the window restart were checked as well
+        segs = list(decode.windows(prompt, toks, cfg["decode_window"], cfg["prompt_len"]))
+        assert len(segs) == 2 and len(segs[1][1]) == n_new - (cfg["decode_window"] - cfg["prompt_len"])
     h.close()

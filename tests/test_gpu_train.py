@@ -8,7 +8,7 @@ fp32 trajectory over 100 steps, whole-gradient cosine >= 0.999.
 import numpy as np
 import pytest
 
-from gpu_common import cfg_of, cosine, init_of, log, spec_from_cfg, stream_of
+from gpu_common import cfg_of, cosine, init_of, log, per_tensor_rel_err, spec_from_cfg, stream_of
 from oracle import gpt, optim
 
 pytestmark = pytest.mark.gpu
@@ -74,7 +74,7 @@ def test_c1_fp32_gradients_elementwise(exec_mode):
     h.close()
 
 
-@pytest.mark.parametrize("name", ["m2", "m3"])
+@pytest.mark.parametrize("name", ["m2", "m3", "m3b"])
 @pytest.mark.parametrize("exec_mode", [PER_PHASE, PERSISTENT], ids=["per_phase", "persistent"])
 def test_bf16_mini_loss_100_steps(name, exec_mode):
     log(f"{name} bf16 100 steps exec_mode={exec_mode}")
@@ -147,11 +147,12 @@ def test_bf16_mini_gradient_cosine(name):
         loss, grads = gpt.loss_and_grads(s, gpt.unflatten(s, p_now), stream.batch(step))
         g_or = gpt.flatten(s, grads)
         cos = cosine(g_gpu, g_or)
-        per = {n: cosine(g_gpu[o:o + k], g_or[o:o + k]) for n, o, k, _ in ofa.layout(h.cfg)}
-        worst = min(per.items(), key=lambda kv: kv[1])
-        log(f"{name} step {step + 1}: grad cosine {cos:.6f}, worst tensor {worst}")
+        per = per_tensor_rel_err(ofa.layout(h.cfg), g_gpu, g_or)
+        worst = max(per.items(), key=lambda kv: kv[1])
+        log(f"{name} step {step + 1}: grad cosine {cos:.6f}, worst tensor relative error {worst}")
         assert cos >= 0.999
-        assert worst[1] >= 0.99
+        # every tensor, however small (LayerNorm gains, biases), within 3% of the oracle's
+        assert worst[1] <= 3e-2
     h.close()
 
 
@@ -257,11 +258,14 @@ def test_bad_token_reports_arg_error():
     tok = np.zeros((1, cfg["batch"], cfg["seq"] + 1), np.int32)
     tok[0, 1, 5] = cfg["vocab"] + 7
     losses = torch.zeros(1, dtype=torch.float32, device="cuda")
+    before = h.get_params().cpu().numpy()
     h.train_step(torch.from_numpy(tok).cuda(), losses)
     with pytest.raises(ofa.OfaError) as e:
         h.sync()
     assert e.value.code == ofa.OFA_E_ARG
     assert h.last_stats.err_info == cfg["vocab"] + 7
+    # the step's update was skipped: the master weights are bit-identical
+    assert h.get_params().cpu().numpy().tobytes() == before.tobytes()
     # the handle stays in the error state
     with pytest.raises(ofa.OfaError):
         h.train_step(torch.from_numpy(tok).cuda(), losses)
@@ -289,13 +293,14 @@ def test_full_size_first_step(name):
                                      dtype=np.float32)
     g_or = gpt.flatten(s, grads, dtype=np.float32)
     cos = cosine(g_gpu, g_or)
-    per = {n: cosine(g_gpu[o:o + k], g_or[o:o + k]) for n, o, k, _ in ofa.layout(ofa.make_config(cfg))}
-    worst = min(per.items(), key=lambda kv: kv[1])
+    per = per_tensor_rel_err(ofa.layout(ofa.make_config(cfg)), g_gpu, g_or)
+    worst = max(per.items(), key=lambda kv: kv[1])
     gl = float(losses.cpu().numpy()[0])
-    log(f"{name}: loss gpu {gl:.5f} oracle {float(loss):.5f}; grad cosine {cos:.6f}, worst tensor {worst}")
+    log(f"{name}: loss gpu {gl:.5f} oracle {float(loss):.5f}; grad cosine {cos:.6f}, "
+        f"worst tensor relative error {worst}")
     assert abs(gl - float(loss)) <= 2e-2
     assert cos >= 0.999
-    assert worst[1] >= 0.99
+    assert worst[1] <= 3e-2
 
 
 @pytest.mark.parametrize("name", ["c2", "c3"])
@@ -330,3 +335,38 @@ def test_full_size_loss_along_trajectory(name):
     h.close()
     assert worst_d <= 2e-2
     assert worst_cos >= 0.999
+
+
+def golden_losses(name):
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", f"{name}_fp32_free_running.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    return np.array([float(r[1]) for r in rows])
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_full_size_free_running_100_steps(name):
+    """Reading A19 of the bf16 bar at full size, in the launch configuration the
+    benchmark times: the GPU trains 100 steps from the seeded init in bf16 mode, the
+    oracle's own fp32 trajectory from the same init and tokens (stored under
+    tests/golden/ by tests/golden/make_free_running.py, which calls only the oracle
+    and the input generators) is never synced to it, and every step's loss must be
+    within 2e-2."""
+    from persistent_transformer_train_amd import ofa
+    ref = golden_losses(name)
+    assert len(ref) == 100
+    cfg = cfg_of(name, exec_mode=PERSISTENT)
+    stream = stream_of(name, cfg)
+    h = ofa.Handle(cfg, init_of(name, cfg))
+    toks = torch.from_numpy(stream.batches(0, 100)).cuda()
+    losses = torch.zeros(100, dtype=torch.float32, device="cuda")
+    h.train_step(toks, losses)
+    h.sync()
+    gl = losses.cpu().numpy()
+    h.close()
+    d = np.abs(gl - ref)
+    log(f"{name}: max |dloss| {d.max():.3g} at step {int(d.argmax()) + 1}; first {gl[0]:.5f}/{ref[0]:.5f} "
+        f"last {gl[-1]:.5f}/{ref[-1]:.5f}")
+    assert np.all(np.isfinite(gl))
+    assert d.max() <= 2e-2
+    assert gl[-10:].mean() < gl[:10].mean()

@@ -24,7 +24,7 @@ def ofa():
 def header_functions():
     src = open(os.path.join(ROOT, "include", "ofa.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ofa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(ofa_[a-z_0-9]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol(ofa):
@@ -147,3 +147,25 @@ def test_init_params_layout_kinds(ofa):
             assert np.all(seg == 0)
         else:
             assert abs(seg.std() - 0.02) < 0.004
+
+
+def test_sha256_fips_vectors_and_random_buffers(ofa):
+    """The library's SHA-256 against the FIPS 180-4 example digests of "abc" and of
+    the 448-bit two-block message, the empty string's digest, and Python's hashlib
+    on buffers of every length around the 55/56/64-byte padding boundaries."""
+    import hashlib
+    assert ofa.sha256(b"abc").hex() == "ba7816bf8f01cfea414140de5dae2223b00361a396177a9cb410ff61f20015ad"
+    two = b"abcdbcdecdefdefgefghfghighijhijkijkljklmklmnlmnomnopnopq"
+    assert ofa.sha256(two).hex() == "248d6a61d20638b8e5c026930c3e6039a33ce45964ff2167f6ecedd419db06c1"
+    assert ofa.sha256(b"").hex() == "e3b0c44298fc1c149afbf4c8996fb92427ae41e4649b934ca495991b7852b855"
+    rng = np.random.default_rng(5)
+    for n in list(range(50, 140)) + [4096, 100003]:
+        data = rng.integers(0, 256, n, dtype=np.uint8).tobytes()
+        assert ofa.sha256(data) == hashlib.sha256(data).digest(), n
+
+
+def test_checkpoint_header_and_size(ofa):
+    assert C.sizeof(ofa.ofa_checkpoint_header) == 256
+    cfg = ofa.make_config(configs.CONFIGS["c1"])
+    P = ofa.ofa_param_count(C.byref(cfg))
+    assert ofa.ofa_checkpoint_bytes(C.byref(cfg)) == 256 + 12 * P
