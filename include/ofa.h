@@ -130,6 +130,26 @@ ofa_status ofa_param_tensor(const ofa_config *cfg, int32_t i, int64_t *offset, i
 ofa_status ofa_create(const ofa_config *cfg, void *dev_workspace, size_t ws_bytes,
                       const float *dev_init_params, void *hip_stream, ofa_handle **out);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): ofa_create
+ * with the library's own static workspace instead of the caller's.  Every
+ * device the library runs on holds one static array of 64 MiB
+ * (OFA_STATIC_WORKSPACE_BYTES) until the process ends, and one handle that uses
+ * it: this call (re)creates that handle for the current device and returns it
+ * (every call on a device returns the same handle, which then holds the new
+ * model; the previous model's state is gone).  Calls on one device that
+ * overlap race on the array.  A model whose ofa_workspace_bytes exceeds the
+ * array is rejected with OFA_E_ARG (ofa_last_error(*out) says why).  The call
+ * allocates no device memory and no pinned host memory and creates no events:
+ * its staging areas are static host arrays, uploads wait for the stream, and
+ * last_call_ms stays 0.  Every other call works on the handle as on one from
+ * ofa_create; ofa_destroy waits for the stream and retires the handle until the
+ * next ofa_create_static on its device.  The caller still owns dev_init_params
+ * and every buffer it passes to later calls. */
+#define OFA_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+ofa_status ofa_create_static(const ofa_config *cfg, const float *dev_init_params, void *hip_stream,
+                             ofa_handle **out);
+
 /* Runs n_steps >= 1 training steps: forward, backward and the AdamW update
  * ([A100] "What ran"), each step one pass over one batch; persistent mode runs
  * all n_steps in one kernel launch with no host launch between forward,

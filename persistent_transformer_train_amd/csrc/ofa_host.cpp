@@ -325,6 +325,8 @@ struct ofa_handle {
   bool dec_started = false;
   bool die_map = false;            // workgroup b of a launch runs on die b % 8 (probed at create)
   bool unpublished = false;        // compute weights set by ofa_set_params since the last publication
+  bool is_static = false;          // made by ofa_create_static: workspace = the device's static array,
+                                   // staging in static host arrays, no events
 };
 
 namespace {
@@ -1095,7 +1097,14 @@ double lr_at(const ofa_config& c, uint64_t step) {
 }
 
 ofa_status check_sticky(ofa_handle* h) {
+  if (!h->ws) return fail(h, OFA_E_STATE, "the handle was destroyed");
   if (h->sticky) return fail(h, (ofa_status)h->sticky, "an earlier call left device status %d", h->sticky);
+  return OFA_OK;
+}
+
+// device-time stamp of a call (handles without events record nothing)
+ofa_status record(ofa_handle* h, hipEvent_t ev) {
+  if (ev) HIP_TRY(h, hipEventRecord(ev, h->stream));
   return OFA_OK;
 }
 
@@ -1114,6 +1123,10 @@ ofa_status staging_ready(ofa_handle* h) {
 }
 
 ofa_status mark_upload(ofa_handle* h) {
+  if (!h->ev_upload) {   // static handle: the staging area is reused once the stream has consumed it
+    HIP_TRY(h, hipStreamSynchronize(h->stream));
+    return OFA_OK;
+  }
   HIP_TRY(h, hipEventRecord(h->ev_upload, h->stream));
   h->upload_pending = true;
   return OFA_OK;
@@ -1328,6 +1341,19 @@ const char* ofa_status_string(ofa_status s) {
 
 const char* ofa_last_error(const ofa_handle* h) { return h ? h->err.c_str() : "null handle"; }
 
+}  // extern "C"
+
+namespace {
+
+// Everything ofa_create and ofa_create_static share, on a handle whose config,
+// layout, dims, carve, workspace and stream are set (and, for a static handle,
+// whose staging pointers point at the static host arrays).
+ofa_status init_handle(ofa_handle* h, const float* dev_init_params);
+
+}  // namespace
+
+extern "C" {
+
 ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_bytes, const float* dev_init_params,
                       void* hip_stream, ofa_handle** out) {
   if (!cfg || !out || !dev_workspace || !dev_init_params) return OFA_E_ARG;
@@ -1346,6 +1372,23 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
   h->ws = (char*)dev_workspace;
   h->stream = (hipStream_t)hip_stream;
   *out = h;
+  return init_handle(h, dev_init_params);
+}
+
+}  // extern "C"
+
+namespace {
+
+// One handle per device for ofa_create_static, with its host staging arrays.
+struct StaticSlot {
+  ofa_handle h;
+  StepCtx steps[kMaxSteps];
+  StepCtx dsteps[kMaxDecInst];
+  alignas(64) char misc[kMiscBytes];
+};
+StaticSlot g_static_slot[kStaticMaxDevices];
+
+ofa_status init_handle(ofa_handle* h, const float* dev_init_params) {
   static bool kernels_ready = false;
   if (!kernels_ready) {
     HIP_TRY(h, init_kernels());
@@ -1360,12 +1403,14 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
   if (h->cfg.train_cus > h->n_cu || h->cfg.serve_cus > h->n_cu || h->cfg.train_cus + h->cfg.serve_cus > h->n_cu)
     return fail(h, OFA_E_ARG, "CU partition %d + %d exceeds the device's %d CUs", h->cfg.train_cus,
                 h->cfg.serve_cus, h->n_cu);
-  HIP_TRY(h, hipHostMalloc((void**)&h->h_steps, sizeof(StepCtx) * kMaxSteps, hipHostMallocDefault));
-  HIP_TRY(h, hipHostMalloc((void**)&h->h_dsteps, sizeof(StepCtx) * kMaxDecInst, hipHostMallocDefault));
-  HIP_TRY(h, hipHostMalloc((void**)&h->h_misc, kMiscBytes, hipHostMallocDefault));
-  HIP_TRY(h, hipEventCreateWithFlags(&h->ev_upload, hipEventDisableTiming));
-  HIP_TRY(h, hipEventCreate(&h->ev_t0));
-  HIP_TRY(h, hipEventCreate(&h->ev_t1));
+  if (!h->is_static) {
+    HIP_TRY(h, hipHostMalloc((void**)&h->h_steps, sizeof(StepCtx) * kMaxSteps, hipHostMallocDefault));
+    HIP_TRY(h, hipHostMalloc((void**)&h->h_dsteps, sizeof(StepCtx) * kMaxDecInst, hipHostMallocDefault));
+    HIP_TRY(h, hipHostMalloc((void**)&h->h_misc, kMiscBytes, hipHostMallocDefault));
+    HIP_TRY(h, hipEventCreateWithFlags(&h->ev_upload, hipEventDisableTiming));
+    HIP_TRY(h, hipEventCreate(&h->ev_t0));
+    HIP_TRY(h, hipEventCreate(&h->ev_t1));
+  }
   {
     const int occ = std::max(1, persistent_occupancy(1));
     h->serve_wgs = (h->cfg.serve_cus > 0 ? h->cfg.serve_cus : h->n_cu) * occ;
@@ -1460,9 +1505,52 @@ ofa_status ofa_create(const ofa_config* cfg, void* dev_workspace, size_t ws_byte
   return OFA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+ofa_status ofa_create_static(const ofa_config* cfg, const float* dev_init_params, void* hip_stream,
+                             ofa_handle** out) {
+  if (!cfg || !out || !dev_init_params) return OFA_E_ARG;
+  *out = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStaticMaxDevices) {
+    (void)hipGetLastError();
+    return OFA_E_HIP;
+  }
+  StaticSlot& slot = g_static_slot[dev];
+  ofa_handle* h = &slot.h;
+  if (h->ws) (void)hipStreamSynchronize(h->stream);   // the earlier model's work is done with the array
+  *h = ofa_handle();
+  h->is_static = true;
+  h->h_steps = slot.steps;
+  h->h_dsteps = slot.dsteps;
+  h->h_misc = slot.misc;
+  *out = h;
+  std::string e = validate(*cfg);
+  if (!e.empty()) return fail(h, OFA_E_ARG, "%s", e.c_str());
+  h->cfg = *cfg;
+  h->lay = make_layout(*cfg);
+  h->D = dims_of(*cfg, h->lay);
+  h->cw = carve(*cfg, h->lay);
+  if (h->cw.total > kStaticScratchBytes)
+    return fail(h, OFA_E_ARG, "this model needs a %zu-byte workspace; the static one holds %zu bytes", h->cw.total,
+                kStaticScratchBytes);
+  void* ws = nullptr;
+  HIP_TRY(h, static_scratch(&ws));
+  h->ws = (char*)ws;
+  h->stream = (hipStream_t)hip_stream;
+  return init_handle(h, dev_init_params);
+}
+
+
 ofa_status ofa_destroy(ofa_handle* h) {
   if (!h) return OFA_E_ARG;
   (void)hipStreamSynchronize(h->stream);
+  if (h->is_static) {   // the device's static handle stays; it only stops working
+    h->ws = nullptr;
+    return OFA_OK;
+  }
   if (h->h_steps) (void)hipHostFree(h->h_steps);
   if (h->h_dsteps) (void)hipHostFree(h->h_dsteps);
   if (h->h_misc) (void)hipHostFree(h->h_misc);
@@ -1502,6 +1590,7 @@ static ofa_status copy_flat(ofa_handle* h, const void* src, int sdt, void* dst, 
 
 ofa_status ofa_set_params(ofa_handle* h, const float* dev_params) {
   if (!h || !dev_params) return OFA_E_ARG;
+  if (!h->ws) return fail(h, OFA_E_STATE, "the handle was destroyed");
   char* ws = h->ws;
   const int64_t P = h->D.P;
   if ((const char*)dev_params != ws + h->cw.p)
@@ -1513,12 +1602,14 @@ ofa_status ofa_set_params(ofa_handle* h, const float* dev_params) {
 
 ofa_status ofa_get_params(ofa_handle* h, float* dev_params) {
   if (!h || !dev_params) return OFA_E_ARG;
+  if (!h->ws) return fail(h, OFA_E_STATE, "the handle was destroyed");
   HIP_TRY(h, hipMemcpyAsync(dev_params, h->ws + h->cw.p, h->D.P * 4, hipMemcpyDeviceToDevice, h->stream));
   return OFA_OK;
 }
 
 ofa_status ofa_get_grads(ofa_handle* h, float* dev_grads) {
   if (!h || !dev_grads) return OFA_E_ARG;
+  if (!h->ws) return fail(h, OFA_E_STATE, "the handle was destroyed");
   HIP_TRY(h, hipMemcpyAsync(dev_grads, h->ws + h->cw.g, h->D.P * 4, hipMemcpyDeviceToDevice, h->stream));
   return OFA_OK;
 }
@@ -1582,7 +1673,7 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
   // phase times: t0 <- max, t1 <- 0
   PhaseTime* tm = at<PhaseTime>(h->ws, h->cw.times);
   HIP_TRY(h, launch_fill_pairs((uint64_t*)tm, ~0ull, 0ull, np, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
+  { ofa_status rs = record(h, h->ev_t0); if (rs != OFA_OK) return rs; }
   if (c.exec_mode == OFA_EXEC_LAUNCH_PER_PHASE) {
     s = run_launch_per_phase(h, h->train, h->d_train, d_steps, n_steps, (int64_t)h->steps_done, false, tm);
     if (s != OFA_OK) return s;
@@ -1592,8 +1683,8 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
                        at<uint64_t>(h->ws, h->cw.inst_end), cus, h->train_occ);
     if (s != OFA_OK) return s;
   }
-  HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
-  h->timed = true;
+  { ofa_status rs = record(h, h->ev_t1); if (rs != OFA_OK) return rs; }
+  h->timed = h->ev_t0 != nullptr;
   h->steps_done += n_steps;
   if (h->cw.n_slots > 1) {   // co-resident configuration: each step published
     h->version += n_steps;
@@ -1638,15 +1729,15 @@ ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_
   if (s != OFA_OK) return s;
   PhaseTime* dtm = at<PhaseTime>(ws, h->cw.dtimes);
   HIP_TRY(h, launch_fill_pairs((uint64_t*)dtm, ~0ull, 0ull, (int64_t)h->dec.size(), h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
+  { ofa_status rs = record(h, h->ev_t0); if (rs != OFA_OK) return rs; }
   if (h->cfg.exec_mode == OFA_EXEC_LAUNCH_PER_PHASE)
     s = run_launch_per_phase(h, h->dec, h->d_dec, d_dsteps, n_inst, 0, true, dtm);
   else
     s = run_persistent(h, h->dec, h->d_dec, d_dsteps, n_inst, h->cw.dsched, dtm, nullptr,
                        h->serve_wgs / std::max(1, persistent_occupancy(1)));
   if (s != OFA_OK) return s;
-  HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
-  h->timed = true;
+  { ofa_status rs = record(h, h->ev_t1); if (rs != OFA_OK) return rs; }
+  h->timed = h->ev_t0 != nullptr;
   return OFA_OK;
 }
 
@@ -1730,12 +1821,12 @@ ofa_status ofa_train_and_serve(ofa_handle* h, const int32_t* dev_tokens, int32_t
                      c.train_cus * occ);
   jobs[1].raise_stop = &at<Sched>(ws, w.dsched)->stop;
   HIP_TRY(h, launch_fill_u64(jobs[1].inst_end, 0, n_steps, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
+  { ofa_status rs = record(h, h->ev_t0); if (rs != OFA_OK) return rs; }
   s = launch_jobs(h, jobs, 2);
   if (s != OFA_OK) return s;
-  HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
+  { ofa_status rs = record(h, h->ev_t1); if (rs != OFA_OK) return rs; }
   HIP_TRY(h, launch_fill_u32((uint32_t*)&st->serving, 0, 1, h->stream));
-  h->timed = true;
+  h->timed = h->ev_t0 != nullptr;
   h->steps_done += n_steps;
   h->version += n_steps;   // every step published its weights
   h->unpublished = false;
@@ -1878,6 +1969,7 @@ size_t ofa_checkpoint_bytes(const ofa_config* cfg) {
 
 ofa_status ofa_checkpoint_save(ofa_handle* h, void* dev_ckpt, const uint8_t* note32, uint8_t* sha256_out) {
   if (!h || !dev_ckpt) return fail(h, OFA_E_ARG, "bad arguments");
+  if (!h->ws) return fail(h, OFA_E_STATE, "the handle was destroyed");
   // allowed after a device error too: the state can be read back for inspection
   ofa_status s = staging_ready(h);
   if (s != OFA_OK) return s;
@@ -1971,7 +2063,7 @@ ofa_status ofa_evaluate(ofa_handle* h, const int32_t* dev_tokens, int32_t n_batc
   if (s != OFA_OK) return s;
   s = mark_upload(h);
   if (s != OFA_OK) return s;
-  HIP_TRY(h, hipEventRecord(h->ev_t0, h->stream));
+  { ofa_status rs = record(h, h->ev_t0); if (rs != OFA_OK) return rs; }
   if (h->cfg.exec_mode == OFA_EXEC_LAUNCH_PER_PHASE) {
     s = run_launch_per_phase(h, h->eval, h->dp_eval.ph, d_steps, n_batches, 0, false, nullptr);
   } else {
@@ -1980,13 +2072,14 @@ ofa_status ofa_evaluate(ofa_handle* h, const int32_t* dev_tokens, int32_t n_batc
                        h->train_occ);
   }
   if (s != OFA_OK) return s;
-  HIP_TRY(h, hipEventRecord(h->ev_t1, h->stream));
-  h->timed = true;
+  { ofa_status rs = record(h, h->ev_t1); if (rs != OFA_OK) return rs; }
+  h->timed = h->ev_t0 != nullptr;
   return OFA_OK;
 }
 
 ofa_status ofa_status_sync(ofa_handle* h, ofa_stats* out) {
   if (!h) return OFA_E_ARG;
+  if (!h->ws) return fail(h, OFA_E_STATE, "the handle was destroyed");
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   DevStatus ds;
   HIP_TRY(h, hipMemcpy(&ds, h->ws + h->cw.status, sizeof ds, hipMemcpyDeviceToHost));
@@ -2025,6 +2118,7 @@ ofa_status ofa_status_sync(ofa_handle* h, ofa_stats* out) {
 static ofa_status phase_times_of(ofa_handle* h, const std::vector<std::string>& nm, size_t off, uint64_t* host_t,
                                  int32_t n, int32_t* n_out, char* names, size_t name_stride) {
   if (!h || !host_t || !n_out) return OFA_E_ARG;
+  if (!h->ws) return fail(h, OFA_E_STATE, "the handle was destroyed");
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   int np = std::min<int>(n, (int)nm.size());
   HIP_TRY(h, hipMemcpy(host_t, h->ws + off, np * sizeof(PhaseTime), hipMemcpyDeviceToHost));
@@ -2045,6 +2139,7 @@ ofa_status ofa_phase_times(ofa_handle* h, uint64_t* host_t, int32_t n, int32_t* 
 
 ofa_status ofa_trace(ofa_handle* h, int32_t decode, uint64_t* host_t, int64_t n, int64_t* n_out, int32_t* n_phases) {
   if (!h || !host_t || !n_out || !n_phases) return OFA_E_ARG;
+  if (!h->ws) return fail(h, OFA_E_STATE, "the handle was destroyed");
   if (!(h->cfg.debug_flags & OFA_DEBUG_TRACE)) return fail(h, OFA_E_STATE, "tracing is off in this configuration");
   if (!h->trace_n_phases || h->trace_dec != (decode != 0)) return fail(h, OFA_E_STATE, "no traced call of that kind");
   HIP_TRY(h, hipStreamSynchronize(h->stream));

@@ -360,6 +360,31 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
   }
 }
 
+// ---------------------------------------------------------------- static workspace
+
+// The workspace of handles made by ofa_create_static: one array per device,
+// held until the process ends.  Host code never uses the array's name as an
+// address (on the host it is a stand-in, not device memory): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept here.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+static void* g_scratch_ptr[kStaticMaxDevices];
+
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kStaticMaxDevices) return hipErrorInvalidDevice;
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 // ---------------------------------------------------------------- small utility kernels
 
 // out[b] = the die (XCD) workgroup b runs on

@@ -52,6 +52,12 @@ struct PersistParams {
   int32_t shuffle;           // debug: permute tiles inside a phase
 };
 
+// The static workspace of ofa_create_static: kStaticScratchBytes of device
+// memory per device, whose address static_scratch returns for the current device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;   // OFA_STATIC_WORKSPACE_BYTES
+constexpr int kStaticMaxDevices = 8;
+hipError_t static_scratch(void** ptr);
+
 hipError_t init_kernels();
 size_t phase_lds_bytes(const Phase& ph);   // dynamic LDS a phase needs
 size_t phase_lds_bytes_occ(const Phase& ph, int occ);   // the same in the persistent kernel built for occ

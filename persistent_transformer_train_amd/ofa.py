@@ -70,6 +70,7 @@ _sig = {
     "ofa_param_tensor": (C.c_int, [C.POINTER(ofa_config), C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_int64),
                                    C.POINTER(C.c_int32), C.c_char_p, C.c_size_t]),
     "ofa_create": (C.c_int, [C.POINTER(ofa_config), _P, C.c_size_t, _P, _P, C.POINTER(_H)]),
+    "ofa_create_static": (C.c_int, [C.POINTER(ofa_config), _P, _P, C.POINTER(_H)]),
     "ofa_train_step": (C.c_int, [_H, _P, C.c_int32, _P]),
     "ofa_publish_weights": (C.c_int, [_H, C.POINTER(C.c_uint64)]),
     "ofa_decode_token": (C.c_int, [_H, _P, C.c_int32, C.c_int32, _P, _P, _P]),
@@ -136,7 +137,13 @@ def layout(cfg: ofa_config):
 class Handle:
     """One model on one GPU: owns the torch-allocated workspace and the ofa handle."""
 
-    def __init__(self, cfg_dict: dict, init_params, device="cuda:0"):
+    # device -> the wrapper whose model the device's static handle holds: only that
+    # wrapper retires it (an older wrapper of the same handle must not)
+    _static_owner = {}
+
+    def __init__(self, cfg_dict: dict, init_params, device="cuda:0", static=False):
+        """static=True: ofa_create_static (the library's own workspace; no torch allocation
+        of a workspace, and the device's one static handle is re-created)."""
         import torch
         self.torch = torch
         self.cfg_dict = dict(cfg_dict)
@@ -146,17 +153,23 @@ class Handle:
             raise OfaError(OFA_E_ARG, buf.value.decode())
         self.device = torch.device(device)
         self.n_params = ofa_param_count(C.byref(self.cfg))
-        ws_bytes = ofa_workspace_bytes(C.byref(self.cfg))
-        self.ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=self.device)
-        base = self.ws.data_ptr()
-        self.ws_ptr = (base + 255) // 256 * 256
-        self.ws_bytes = ws_bytes
         init = torch.as_tensor(init_params, dtype=torch.float32).to(self.device).contiguous()
         assert init.numel() == self.n_params, (init.numel(), self.n_params)
         self.stream = torch.cuda.current_stream(self.device)
         self.h = _H()
-        rc = ofa_create(C.byref(self.cfg), self.ws_ptr, ws_bytes, init.data_ptr(), self.stream.cuda_stream,
-                        C.byref(self.h))
+        self.static = static
+        if static:
+            self.ws = None
+            rc = ofa_create_static(C.byref(self.cfg), init.data_ptr(), self.stream.cuda_stream, C.byref(self.h))
+            Handle._static_owner[self.device] = id(self)
+        else:
+            ws_bytes = ofa_workspace_bytes(C.byref(self.cfg))
+            self.ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=self.device)
+            base = self.ws.data_ptr()
+            self.ws_ptr = (base + 255) // 256 * 256
+            self.ws_bytes = ws_bytes
+            rc = ofa_create(C.byref(self.cfg), self.ws_ptr, ws_bytes, init.data_ptr(), self.stream.cuda_stream,
+                            C.byref(self.h))
         if rc != OFA_OK:
             msg = ofa_last_error(self.h).decode() if self.h.value else "create failed"
             raise OfaError(rc, msg)
@@ -272,7 +285,9 @@ class Handle:
 
     def close(self):
         if self.h:
-            ofa_destroy(self.h)
+            if not getattr(self, "static", False) or Handle._static_owner.get(self.device) == id(self):
+                ofa_destroy(self.h)
+                Handle._static_owner.pop(self.device, None) if getattr(self, "static", False) else None
             self.h = _H()
 
     def __del__(self):
