@@ -80,28 +80,31 @@ def measured_traffic(profile: str):
 
 
 def cpu_baseline(cfg: dict) -> dict:
-    """The oracle (numpy fp64, untuned) on a bounded sample: one full training step of
-    the same model at batch 1 (512 of the step's 4,096 tokens)."""
+    """The oracle (numpy, untuned) on one full training step of the same workload:
+    the 162M model on all 8 x 512 = 4,096 tokens of a step (forward, hand-derived
+    backward, AdamW), in float32 as the parity runs use it, on the host's cores."""
     from oracle import gpt, optim
     from persistent_transformer_train_amd import configs, synth
     spec = gpt.Spec(n_layer=cfg["n_layer"], d_model=cfg["d_model"], n_head=cfg["n_head"], d_ff=cfg["d_ff"],
                     vocab=cfg["vocab"], n_pos=cfg["n_pos"], mlp_gated=bool(cfg["mlp_gated"]),
-                    tied_head=bool(cfg["tied_head"]), has_bias=bool(cfg["has_bias"]), batch=1, seq=cfg["seq"],
-                    lr=cfg["lr"], beta1=cfg["beta1"], beta2=cfg["beta2"], eps=cfg["eps"],
+                    tied_head=bool(cfg["tied_head"]), has_bias=bool(cfg["has_bias"]), batch=cfg["batch"],
+                    seq=cfg["seq"], lr=cfg["lr"], beta1=cfg["beta1"], beta2=cfg["beta2"], eps=cfg["eps"],
                     weight_decay=cfg["weight_decay"],
                     lr_schedule="cosine" if cfg["lr_schedule"] == configs.LR_COSINE else "constant",
                     total_steps=cfg["total_steps"])
     lay = gpt.param_layout(spec)
     init = synth.init_params([(int(np.prod(sh)), k) for _, sh, k in lay], 3)
-    stream = synth.TokenStream("markov2", 3, cfg["vocab"], 1, cfg["seq"])
-    tr = optim.Trainer(spec, init, dtype=np.float64)
+    stream = synth.TokenStream("markov2", 3, cfg["vocab"], cfg["batch"], cfg["seq"])
+    tr = optim.Trainer(spec, init, dtype=np.float32)
     t0 = time.perf_counter()
     tr.step(stream.batch(0))
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
-    return {"value": round(cfg["seq"] / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"one fp64 training step (fwd+bwd+AdamW) of the same model at batch 1 "
-                      f"({cfg['seq']} tokens), {dt:.2f} s, numpy BLAS threads = affinity cores"}
+    tokens = cfg["batch"] * cfg["seq"]
+    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one float32 training step (forward, backward, AdamW) of the 162M model on the full "
+                      f"{cfg['batch']} x {cfg['seq']} = {tokens}-token batch: {dt:.2f} s; numpy BLAS threads = "
+                      f"the {cores} cores of the process's affinity"}
 
 
 def bench_decode(init, stream, args) -> dict:
@@ -180,6 +183,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--co-steps", type=int, default=40, help="co-resident (c5) training steps; 0 = skip")
     ap.add_argument("--dump-phases", default="", help="write the training program's phase names (launch order) here")
+    ap.add_argument("--debug-flags", type=int, default=0, help="OFA_DEBUG_* bits for the training handle (experiments)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -189,7 +193,7 @@ def main():
     import torch
     from persistent_transformer_train_amd import configs, ofa, synth
 
-    cfg = configs.get("c3", exec_mode=0 if args.exec_mode == "persistent" else 1)
+    cfg = configs.get("c3", exec_mode=0 if args.exec_mode == "persistent" else 1, debug_flags=args.debug_flags)
     lay = ofa.layout(ofa.make_config(cfg))
     init = synth.init_params([(n, k) for _, _, n, k in lay], 3)
     stream = synth.TokenStream("markov2", 3, cfg["vocab"], cfg["batch"], cfg["seq"])

@@ -91,7 +91,7 @@ typedef struct {
 #define OFA_DEBUG_SHORT_WATCHDOG  2  /* device waits give up after ~1 ms instead of ~10 s */
 #define OFA_DEBUG_TRACE           4  /* persistent mode: per (instance, phase) timestamps, see ofa_trace */
 #define OFA_DEBUG_TILE256         8  /* every matrix-core GEMM takes the 256-row tile (normally only large ones) */
-#define OFA_DEBUG_OCC2           16  /* step-mode persistent training with two workgroups per CU (measured slower at c3) */
+#define OFA_DEBUG_OCC1           16  /* step-mode persistent training with one workgroup per CU (default: two where they fit) */
 #define OFA_DEBUG_PLAIN_TILES    32  /* GEMM tiles in plain row / column order, not placed by die (for comparison) */
 #define OFA_DEBUG_WG_RELEASE     64  /* persistent launches: every workgroup writes its die's L2 back after each ticket */
 
@@ -332,6 +332,26 @@ ofa_status ofa_trace(ofa_handle *h, int32_t decode, uint64_t *host_t, int64_t n,
  * scheduler, after [A100] "A longer run exposed a scheduler overflow" (a
  * 32-bit budget of 4,194,304 x 2,225 wrapped). */
 ofa_status ofa_task_budget(uint64_t iterations, uint64_t tasks_per_unit, uint64_t *out);
+
+/* Host-only model check of the persistent scheduler's protocol ([Review]:
+ * tickets claim work, a finished phase is fenced then counted, dependents
+ * acquire-read the count; [A100] "A longer run exposed a scheduler
+ * overflow": counter widths).  Builds the phase tables of cfg's training
+ * program (program 0) or evaluation program (program 1) for a device of n_cu
+ * CUs without touching a GPU, then runs n_inst instances with n_workers host
+ * threads standing in for workgroups (worker b in ticket partition b % 8):
+ * 64-bit ticket claims in order per partition, waits on the completion counters
+ * of each phase's dependencies, and the release either once per partition and
+ * phase (per_die != 0, the share accounting of the once-per-die write-back) or
+ * per ticket (per_die == 2 injects a protocol error, the count before the work,
+ * which the check must catch).  Every counter starts at counter_base; seed varies the random
+ * delays.  OFA_OK if every tile ran exactly once and only after all tiles of
+ * its dependencies had finished, every ticket was claimed once and every
+ * counter ends at base + instances x tiles; else OFA_E_STATE (or OFA_E_ARG),
+ * with the reason in msg (NUL-terminated, at most msg_len bytes). */
+ofa_status ofa_sched_selftest(const ofa_config *cfg, int32_t program, int32_t n_workers, int32_t n_cu,
+                              int64_t n_inst, uint64_t counter_base, int32_t per_die, uint64_t seed,
+                              char *msg, size_t msg_len);
 
 /* The handle's last error message (owned by the handle), and a fixed name of a
  * status code. */

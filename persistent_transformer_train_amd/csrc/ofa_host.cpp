@@ -8,7 +8,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
+#include <random>
+#include <thread>
 #include <cstddef>
 #include <cstdarg>
 #include <cstdio>
@@ -325,6 +329,8 @@ struct ofa_handle {
   bool dec_started = false;
   bool die_map = false;            // workgroup b of a launch runs on die b % 8 (probed at create)
   bool unpublished = false;        // compute weights set by ofa_set_params since the last publication
+  bool host_model = false;         // built by ofa_sched_selftest: programs only, no device (the
+                                   // matrix-core tiles are assumed available)
   bool is_static = false;          // made by ofa_create_static: workspace = the device's static array,
                                    // staging in static host arrays, no events
 };
@@ -399,7 +405,8 @@ GemmArgs gemm(const ofa_handle* h, int M, int N, int K, const void* A, int64_t l
   // bf16 operands take the matrix-core tile; its shape limits (K, and the
   // contiguous dimension of a row-contiguous operand, multiples of 8) hold for
   // every bf16 configuration the validator accepts
-  const bool mfma = h->cfg.precision == OFA_BF16 && a_dt == DT_BF16 && b_dt == DT_BF16 && gemm_p3_available() &&
+  const bool mfma = h->cfg.precision == OFA_BF16 && a_dt == DT_BF16 && b_dt == DT_BF16 &&
+                    (h->host_model || gemm_p3_available()) &&
                     K % 8 == 0 && (a_km || M % 8 == 0) && N % 8 == 0 && ldc % 8 == 0 && M >= 8 && N >= 8;
   g.impl = mfma ? GEMM_P3 : GEMM_SIMPLE;
   // 256-row tiles move fewer bytes per MFMA; they pay off where even they make
@@ -1415,12 +1422,12 @@ ofa_status init_handle(ofa_handle* h, const float* dev_init_params) {
     const int occ = std::max(1, persistent_occupancy(1));
     h->serve_wgs = (h->cfg.serve_cus > 0 ? h->cfg.serve_cus : h->n_cu) * occ;
   }
-  // Step-mode training can run two workgroups per CU where the kernel fits
-  // twice (co-resident launches keep one: both jobs share one kernel).  At c3
-  // it measured slower (16.5 against 13.7 ms: twice the tickets and fences),
-  // so it is opt-in.
+  // Step-mode training runs two workgroups per CU where the kernel fits twice
+  // (co-resident launches keep one: both jobs share one kernel): one workgroup's
+  // matrix-core work then overlaps the other's epilogue, copies and waits.  At c3
+  // this measured 10.24 against 10.71 ms a step (OFA_DEBUG_OCC1 keeps one).
   const bool coresident_cfg = h->cfg.train_cus > 0 && h->cfg.serve_cus > 0;
-  h->train_occ = (!coresident_cfg && (h->cfg.debug_flags & OFA_DEBUG_OCC2) && persistent_occupancy(2) >= 2) ? 2 : 1;
+  h->train_occ = (!coresident_cfg && !(h->cfg.debug_flags & OFA_DEBUG_OCC1) && persistent_occupancy(2) >= 2) ? 2 : 1;
   build_train(h);
   build_eval(h);
   build_decode(h);
@@ -1472,7 +1479,8 @@ ofa_status init_handle(ofa_handle* h, const float* dev_init_params) {
   // ticket is released on its own (the probe writes into the misc block).
   static int die_map_of[64];   // 0 = not probed, 1 = b % 8, 2 = another mapping
   if (dev < 0 || dev >= 64 || die_map_of[dev] == 0) {
-    const int n = std::min<int>((int)(kMiscBytes / 4), std::max(kMaxParts, h->n_cu * std::max(1, persistent_occupancy(1))));
+    const int occ = std::max({1, persistent_occupancy(1), persistent_occupancy(2)});
+    const int n = std::min<int>((int)(kMiscBytes / 4), std::max(kMaxParts, h->n_cu * occ));
     uint32_t* probe = at<uint32_t>(ws, w.misc);
     std::vector<uint32_t> ids(n);
     HIP_TRY(h, launch_xcc_probe(probe, n, h->stream));
@@ -2074,6 +2082,152 @@ ofa_status ofa_evaluate(ofa_handle* h, const int32_t* dev_tokens, int32_t n_batc
   if (s != OFA_OK) return s;
   { ofa_status rs = record(h, h->ev_t1); if (rs != OFA_OK) return rs; }
   h->timed = h->ev_t0 != nullptr;
+  return OFA_OK;
+}
+
+ofa_status ofa_sched_selftest(const ofa_config* cfg, int32_t program, int32_t n_workers, int32_t n_cu, int64_t n_inst,
+                              uint64_t counter_base, int32_t per_die, uint64_t seed, char* msg, size_t msg_len) {
+  auto say = [&](const std::string& m) {
+    if (msg && msg_len) {
+      strncpy(msg, m.c_str(), msg_len - 1);
+      msg[msg_len - 1] = 0;
+    }
+  };
+  if (!cfg || n_workers < kMaxParts || n_cu < 1 || n_inst < 1 || program < 0 || program > 1) {
+    say("bad arguments");
+    return OFA_E_ARG;
+  }
+  std::string e = validate(*cfg);
+  if (!e.empty()) {
+    say(e);
+    return OFA_E_ARG;
+  }
+  // the programs of a handle over a workspace that is never touched
+  ofa_handle hh;
+  ofa_handle* h = &hh;
+  h->host_model = true;
+  h->cfg = *cfg;
+  h->lay = make_layout(*cfg);
+  h->D = dims_of(*cfg, h->lay);
+  h->cw = carve(*cfg, h->lay);
+  h->ws = (char*)(uintptr_t)0x100000000ull;   // addresses only: nothing dereferences them
+  h->n_cu = n_cu;
+  h->serve_wgs = n_cu;
+  build_train(h);
+  build_eval(h);
+  const std::vector<Phase>& prog = program == 0 ? h->train : h->eval;
+  const int np = (int)prog.size();
+  const int P = kMaxParts;
+  const std::vector<int32_t> ptb = part_table(prog, P), ptiles = part_tile_table(prog, P);
+  // the scheduler block, as on the device: 64-bit counters starting at the base
+  std::vector<std::atomic<uint64_t>> part_ticket(P), done(np), part_done((size_t)np * P);
+  for (auto& c : part_ticket) c = counter_base;
+  for (auto& c : done) c = counter_base;
+  for (auto& c : part_done) c = counter_base;
+  // shadow state: tiles of (instance, phase) finished, tickets claimed
+  std::vector<std::atomic<int32_t>> finished((size_t)n_inst * np), claimed((size_t)n_inst * (prog.back().ticket_base + prog.back().n_tickets));
+  for (auto& c : finished) c = 0;
+  for (auto& c : claimed) c = 0;
+  std::atomic<int> failed{0};
+  std::string fail_msg;
+  std::atomic<bool> msg_taken{false};
+  auto bad = [&](const std::string& m) {
+    if (!msg_taken.exchange(true)) fail_msg = m;
+    failed = 1;
+  };
+  const auto deadline = std::chrono::steady_clock::now() + std::chrono::seconds(120);
+  auto worker = [&](int b) {
+    std::mt19937_64 rng(seed * 1000003u + (uint64_t)b);
+    const int part = b % P;
+    const int32_t* tb = ptb.data() + part * (np + 1);
+    const int tpi = tb[np];
+    const uint64_t total = (uint64_t)n_inst * (uint64_t)tpi;
+    int pi = 0;
+    for (;;) {
+      if (failed) return;
+      const uint64_t t = part_ticket[part].fetch_add(1) - counter_base;
+      if (t >= total) return;
+      const int64_t inst = (int64_t)(t / (uint64_t)tpi);
+      const int r = (int)(t % (uint64_t)tpi);
+      if (tb[pi] > r) pi = 0;
+      while (pi + 1 < np && tb[pi + 1] <= r) ++pi;
+      const Phase& ph = prog[pi];
+      const int j = (r - tb[pi]) * P + part;
+      const int tile0 = j * ph.per_ticket, tile1 = std::min(tile0 + ph.per_ticket, ph.n_tiles);
+      if (j >= ph.n_tickets || tile0 >= tile1) {
+        bad("ticket maps outside its phase: phase " + std::to_string(pi) + " ticket " + std::to_string(j));
+        return;
+      }
+      claimed[(size_t)inst * (prog.back().ticket_base + prog.back().n_tickets) + ph.ticket_base + j]++;
+      // dependencies: completion counters reach base + (instance + 1) * tiles
+      auto need = [&](int q, int64_t i) {
+        const uint64_t want = counter_base + (uint64_t)(i + 1) * (uint64_t)prog[q].n_tiles;
+        while (done[q].load(std::memory_order_acquire) < want) {
+          if (failed) return false;
+          if (std::chrono::steady_clock::now() > deadline) {
+            bad("wait timed out: phase " + std::to_string(pi) + " waits on " + std::to_string(q));
+            return false;
+          }
+          std::this_thread::yield();
+        }
+        if (finished[(size_t)i * np + q].load() != prog[q].n_tiles) {
+          bad("counter complete before every tile finished: phase " + std::to_string(q));
+          return false;
+        }
+        return true;
+      };
+      bool ok = true;
+      for (int d = 0; d < kMaxDeps && ok; ++d) {
+        const int q = ph.dep[d];
+        if (q == -2)
+          for (int qq = 0; qq < pi && ok; ++qq) ok = need(qq, inst);
+        else if (q >= 0)
+          ok = need(q, inst);
+      }
+      if (ok && ph.dep_prev >= 0 && inst > 0) ok = need(ph.dep_prev, inst - 1);
+      if (!ok) return;
+      const uint64_t n = (uint64_t)(tile1 - tile0);
+      if (per_die == 2) done[pi].fetch_add(n, std::memory_order_release);   // injected error: count, then work
+      if (rng() % 4 == 0) std::this_thread::sleep_for(std::chrono::microseconds(rng() % 50));
+      finished[(size_t)inst * np + pi] += tile1 - tile0;   // the work
+      if (per_die == 2) continue;
+      if (per_die) {
+        const uint64_t share = (uint64_t)ptiles[part * np + pi];
+        const uint64_t prev = part_done[(size_t)pi * P + part].fetch_add(n);
+        if (prev + n - counter_base == (uint64_t)(inst + 1) * share) done[pi].fetch_add(share, std::memory_order_release);
+      } else {
+        done[pi].fetch_add(n, std::memory_order_release);
+      }
+    }
+  };
+  std::vector<std::thread> th;
+  for (int b = 0; b < n_workers; ++b) th.emplace_back(worker, b);
+  for (auto& x : th) x.join();
+  if (failed) {
+    say(fail_msg);
+    return OFA_E_STATE;
+  }
+  const int tps = prog.back().ticket_base + prog.back().n_tickets;
+  for (int64_t i = 0; i < n_inst; ++i) {
+    for (int q = 0; q < np; ++q)
+      if (finished[(size_t)i * np + q] != prog[q].n_tiles) {
+        say("instance " + std::to_string(i) + " phase " + std::to_string(q) + " ran " +
+            std::to_string(finished[(size_t)i * np + q].load()) + " of " + std::to_string(prog[q].n_tiles) + " tiles");
+        return OFA_E_STATE;
+      }
+    for (int k = 0; k < tps; ++k)
+      if (claimed[(size_t)i * tps + k] != 1) {
+        say("ticket " + std::to_string(k) + " of instance " + std::to_string(i) + " claimed " +
+            std::to_string(claimed[(size_t)i * tps + k].load()) + " times");
+        return OFA_E_STATE;
+      }
+  }
+  for (int q = 0; q < np; ++q)
+    if (done[q] != counter_base + (uint64_t)n_inst * prog[q].n_tiles) {
+      say("phase " + std::to_string(q) + " counter ends at the wrong value");
+      return OFA_E_STATE;
+    }
+  say("ok: " + std::to_string(np) + " phases, " + std::to_string(tps) + " tickets per instance");
   return OFA_OK;
 }
 

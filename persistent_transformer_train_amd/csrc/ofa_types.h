@@ -58,6 +58,9 @@ enum Epi : int32_t {
   EPI_DSUM = 5,    // attention output gradient: C = dO = acc (bf16), and with aux = O (bf16) the
                    // attention backward's row sums dsum[b][h][t] = sum over head h's 64 columns of dO O
                    // (matrix-core tile only; N a multiple of 128, 64-wide heads)
+  EPI_CE = 6,      // LM head fused with the softmax statistics (matrix-core tile, bf16 C): for each
+                   // row of the 128-column tile tn, m = max over its columns of the logits z,
+                   // C = exp(z - m) (bf16), stats[row * stats_ld + tn] = (m, sum of exp(z - m))
 };
 
 enum GemmImpl : int32_t { GEMM_SIMPLE = 0, GEMM_P3 = 2 };
@@ -84,6 +87,8 @@ struct GemmArgs {
   int32_t xcd;        // one-launch-per-phase executor: give each die a contiguous run of tiles
   float* dsum;        // EPI_DSUM: [B][H][T] row sums; T and H of its indexing
   int32_t dsum_T, dsum_H;
+  float* stats;       // EPI_CE: [M][stats_ld] (max, sum) pairs
+  int32_t stats_ld;
 };
 
 struct LnFwdArgs {
@@ -151,6 +156,13 @@ struct CeArgs {
   float* loss_rows;     // [rows]
   int32_t rows, V, T, dt;
   float inv_rows;
+  // fused with the LM head (EPI_CE): dz holds exp(z - m_t) per 128-column tile t
+  // (bf16) and stats the per-tile (m_t, s_t); the target logit is recomputed as
+  // h[row] . w[y] (bf16 inputs, d wide); logits is unused
+  int32_t fused, n_stats, d;
+  const float* stats;
+  const void* h;
+  const void* w;
 };
 
 struct LossArgs {

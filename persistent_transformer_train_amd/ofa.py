@@ -21,7 +21,7 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 OFA_OK, OFA_E_ARG, OFA_E_HIP, OFA_E_NONFINITE, OFA_E_TIMEOUT, OFA_E_OVERFLOW, OFA_E_STATE = 0, -1, -2, -3, -4, -5, -6
-OFA_DEBUG_SHUFFLE_TICKETS, OFA_DEBUG_SHORT_WATCHDOG, OFA_DEBUG_TRACE, OFA_DEBUG_TILE256, OFA_DEBUG_OCC2 = 1, 2, 4, 8, 16
+OFA_DEBUG_SHUFFLE_TICKETS, OFA_DEBUG_SHORT_WATCHDOG, OFA_DEBUG_TRACE, OFA_DEBUG_TILE256, OFA_DEBUG_OCC1 = 1, 2, 4, 8, 16
 OFA_DEBUG_PLAIN_TILES, OFA_DEBUG_WG_RELEASE = 32, 64
 OFA_TRACE_INSTANCES = 1024
 
@@ -91,6 +91,8 @@ _sig = {
     "ofa_checkpoint_save": (C.c_int, [_H, _P, C.c_char_p, C.c_char_p]),
     "ofa_checkpoint_load": (C.c_int, [_H, _P, C.c_char_p]),
     "ofa_sha256": (C.c_int, [C.c_char_p, C.c_size_t, C.c_char_p]),
+    "ofa_sched_selftest": (C.c_int, [C.POINTER(ofa_config), C.c_int32, C.c_int32, C.c_int32, C.c_int64, C.c_uint64,
+                                     C.c_int32, C.c_uint64, C.c_char_p, C.c_size_t]),
     "ofa_last_error": (C.c_char_p, [_H]),
     "ofa_status_string": (C.c_char_p, [C.c_int]),
     "ofa_destroy": (C.c_int, [_H]),

@@ -48,7 +48,9 @@ def step_mode_snapshots(name, n_steps, cfg, keep=None):
     from persistent_transformer_train_amd import ofa
     stream = stream_of(name, cfg)
     init = init_of(name, cfg)
-    h = ofa.Handle(dict(cfg, train_cus=0, serve_cus=0), init)
+    # the co-resident launch runs one workgroup per CU: the step-mode reference too
+    h = ofa.Handle(dict(cfg, train_cus=0, serve_cus=0, debug_flags=cfg.get("debug_flags", 0) | ofa.OFA_DEBUG_OCC1),
+                   init)
     snaps = [np.asarray(init, np.float32)]
     losses = torch.zeros(1, dtype=torch.float32, device="cuda")
     out = []

@@ -168,14 +168,14 @@ def test_determinism_and_shuffled_tickets():
 
 
 def test_gemm_256_row_tile_bitwise_equal_to_128():
-    """The 256-row GEMM tile (taken by the LM-head products at full size) sums
-    each output over k in the same order as the 128-row tile: forcing it on
-    every matrix-core GEMM of m3b (ragged vocabulary, row-contiguous operands)
-    must leave losses and weights bit-identical."""
+    """The 256-row GEMM tile (one workgroup per CU only) sums each output over k
+    in the same order as the 128-row tile: forcing it on every matrix-core GEMM
+    of m3b (ragged vocabulary, row-contiguous operands) must leave losses and
+    weights bit-identical."""
     from persistent_transformer_train_amd import ofa
-    h1, *_, g1 = gpu_run("m3b", 3, PERSISTENT)
+    h1, *_, g1 = gpu_run("m3b", 3, PERSISTENT, debug_flags=ofa.OFA_DEBUG_OCC1)
     p1 = h1.get_params().cpu().numpy()
-    h2, *_, g2 = gpu_run("m3b", 3, PERSISTENT, debug_flags=ofa.OFA_DEBUG_TILE256)
+    h2, *_, g2 = gpu_run("m3b", 3, PERSISTENT, debug_flags=ofa.OFA_DEBUG_TILE256 | ofa.OFA_DEBUG_OCC1)
     p2 = h2.get_params().cpu().numpy()
     assert g1.tobytes() == g2.tobytes()
     assert p1.tobytes() == p2.tobytes()
@@ -184,13 +184,13 @@ def test_gemm_256_row_tile_bitwise_equal_to_128():
 
 
 def test_two_workgroups_per_cu_bitwise_equal_to_one():
-    """Step-mode persistent training with two workgroups per CU (OFA_DEBUG_OCC2:
+    """Step-mode persistent training with two workgroups per CU (the default;
     the GEMM tile then keeps a two-slice ring) must give bit-identical losses
-    and weights to the default one workgroup per CU."""
+    and weights to one workgroup per CU (OFA_DEBUG_OCC1)."""
     from persistent_transformer_train_amd import ofa
-    h1, *_, g1 = gpu_run("m3b", 3, PERSISTENT, debug_flags=ofa.OFA_DEBUG_OCC2)
+    h1, *_, g1 = gpu_run("m3b", 3, PERSISTENT)
     p1 = h1.get_params().cpu().numpy()
-    h2, *_, g2 = gpu_run("m3b", 3, PERSISTENT)
+    h2, *_, g2 = gpu_run("m3b", 3, PERSISTENT, debug_flags=ofa.OFA_DEBUG_OCC1)
     p2 = h2.get_params().cpu().numpy()
     assert h1.sync().grid == 2 * h2.sync().grid
     assert g1.tobytes() == g2.tobytes()

@@ -169,3 +169,33 @@ def test_checkpoint_header_and_size(ofa):
     cfg = ofa.make_config(configs.CONFIGS["c1"])
     P = ofa.ofa_param_count(C.byref(cfg))
     assert ofa.ofa_checkpoint_bytes(C.byref(cfg)) == 256 + 12 * P
+
+
+def _selftest(ofa, cfg, program, workers, n_inst, base, per_die, seed=3):
+    msg = C.create_string_buffer(256)
+    rc = ofa.ofa_sched_selftest(C.byref(ofa.make_config(cfg)), program, workers, 256, n_inst, base, per_die, seed,
+                                msg, 256)
+    return rc, msg.value.decode()
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("per_die", [1, 0], ids=["per_die_release", "per_ticket_release"])
+def test_scheduler_protocol_on_cpu_threads(ofa, name, per_die):
+    """The persistent scheduler's protocol on host threads with the real phase
+    tables of each workload's training step (a 256-CU device): every tile runs
+    once, after every tile of its dependencies; counters start just below 2^32
+    so a 32-bit counter would wrap inside the run."""
+    cfg = configs.CONFIGS[name]
+    rc, msg = _selftest(ofa, cfg, 0, 40, 2, 2 ** 32 - 10, per_die)
+    assert rc == ofa.OFA_OK, msg
+    rc, msg = _selftest(ofa, cfg, 1, 24, 2, 2 ** 32 - 3, per_die)   # the evaluation program
+    assert rc == ofa.OFA_OK, msg
+
+
+def test_scheduler_selftest_catches_an_early_count(ofa):
+    """A release that counts a tile before its work is done must be caught."""
+    caught = 0
+    for seed in range(4):
+        rc, msg = _selftest(ofa, configs.CONFIGS["c1"], 0, 32, 3, 0, 2, seed)
+        caught += rc == ofa.OFA_E_STATE and "before every tile finished" in msg
+    assert caught >= 1
