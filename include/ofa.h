@@ -94,6 +94,7 @@ typedef struct {
 #define OFA_DEBUG_OCC1           16  /* step-mode persistent training with one workgroup per CU (default: two where they fit) */
 #define OFA_DEBUG_PLAIN_TILES    32  /* GEMM tiles in plain row / column order, not placed by die (for comparison) */
 #define OFA_DEBUG_WG_RELEASE     64  /* persistent launches: every workgroup writes its die's L2 back after each ticket */
+#define OFA_DEBUG_CE_UNFUSED    128  /* bf16: LM head writes fp32 logits and a separate cross-entropy reads them */
 
 /* Size in bytes of the device workspace ofa_create() needs for cfg; 0 if cfg is
  * invalid (ofa_validate_config() says why).  Host only. */

@@ -117,6 +117,40 @@ __device__ __forceinline__ void epi_tile(const GemmArgs& g, const float* cst, in
   }
 }
 
+// EPI_CE, the LM head fused with the softmax statistics: every row of the
+// tile keeps its logits z only as p = exp(z - m) in bf16, with m the row's
+// maximum over the tile's valid columns, and writes (m, sum of p) for the
+// cross-entropy to combine over the row's tiles ("Coppelius training on the
+// RTX 3090", "Where a step's time goes": the output product, cross-entropy and
+// its backward).  The 32 threads of a 32-lane half hold one row (four columns
+// each) and reduce with shuffles inside that half, in a fixed order.
+__device__ __forceinline__ void epi_ce_tile(const GemmArgs& g, const float* cst, int rows, int row0, int n0) {
+  const int c = (threadIdx.x & 31) * 4, col = n0 + c;
+  const bool valid = col < g.N;   // N % 8 == 0: a group of four columns is wholly in or out
+  const int rend = min(rows, g.M - row0);
+  uint16_t* Ch = (uint16_t*)g.C;
+  const int tn = n0 / kMBN;
+  constexpr float kLog2e = 1.44269504088896341f;
+  for (int r = threadIdx.x >> 5; r < rend; r += 8) {
+    const epi_f4 v = valid ? *(const epi_f4*)(cst + r * kEpiPitch + c) : epi_f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float m = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float ml2 = m * kLog2e;
+    const epi_f4 pz = epi_f4{__builtin_amdgcn_exp2f(fmaf(v.x, kLog2e, -ml2)), __builtin_amdgcn_exp2f(fmaf(v.y, kLog2e, -ml2)),
+                             __builtin_amdgcn_exp2f(fmaf(v.z, kLog2e, -ml2)), __builtin_amdgcn_exp2f(fmaf(v.w, kLog2e, -ml2))};
+    float sm = (pz.x + pz.y) + (pz.z + pz.w);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
+    const int64_t row = row0 + r;
+    if (valid) *(epi_u2*)(Ch + row * g.ldc + col) = pack_bf16x4(pz);
+    if ((threadIdx.x & 31) == 0) {
+      g.stats[2 * (row * g.stats_ld + tn)] = m;
+      g.stats[2 * (row * g.stats_ld + tn) + 1] = sm;
+    }
+  }
+}
+
 // The waves park their accumulators in LDS as the fp32 tile [BM][kEpiPitch],
 // then walk it with epi_tile.  The accumulators hold transposed 32 x 32 blocks
 // (the MFMA takes the B fragment as its first operand): element e of lane l
@@ -148,6 +182,7 @@ __device__ __forceinline__ void gemm_mfma_epilogue(const GemmArgs& g, const f32x
     case EPI_GELU: epi_tile<EPI_GELU, false>(g, cst, BM, m0, n0); break;
     case EPI_DGELU: epi_tile<EPI_DGELU, false>(g, cst, BM, m0, n0); break;
     case EPI_DSUM: epi_tile<EPI_DSUM, false>(g, cst, BM, m0, n0); break;
+    case EPI_CE: epi_ce_tile(g, cst, BM, m0, n0); break;
     default: epi_tile<EPI_DGEGLU, false>(g, cst, BM, m0, n0); break;
   }
 }

@@ -745,6 +745,7 @@ __device__ __forceinline__ float exp_shift(float x, float ml2) {
 // the logits are read once and d logits written once: non-temporal global accesses
 typedef float ce_f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t ce_u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t ce_u4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) ce_f4 ce_gf4;
 typedef __attribute__((address_space(1))) ce_u2 ce_gu2;
 
@@ -848,6 +849,53 @@ __device__ __forceinline__ void ce_row_online(const CeArgs& a, int r, int y, flo
   if (threadIdx.x == 0) a.loss_rows[r] = lse - a.logits[(int64_t)r * a.V + y];
 }
 
+// Cross-entropy of one row fused with the LM head (EPI_CE): the row's tiles
+// left p = exp(z - m_t) in dz and (m_t, s_t) in stats.  Then
+//   lse = M + log sum_t s_t exp(m_t - M),  M = max_t m_t,
+//   loss = lse - z_y,  z_y = h[row] . w[y] (the target logit, recomputed),
+//   dz = (p exp(m_t - lse) - [v == y]) / rows, written over p.
+// Reductions run in a fixed order (per-thread strided sums, then the block).
+__device__ __forceinline__ void ce_row_fused(const CeArgs& a, int r, int y, float* red) {
+  constexpr float kLog2e = 1.44269504088896341f;
+  float* cs = red + 16;   // [n_stats] per-tile scales
+  const float* st = a.stats + (int64_t)r * a.n_stats * 2;
+  float m = -INFINITY;
+  for (int t = threadIdx.x; t < a.n_stats; t += kThreads) m = fmaxf(m, st[2 * t]);
+  m = block_max(m, red);
+  float s = 0.f;
+  for (int t = threadIdx.x; t < a.n_stats; t += kThreads) s += st[2 * t + 1] * __builtin_amdgcn_exp2f((st[2 * t] - m) * kLog2e);
+  s = block_sum(s, red + kWaves);
+  const float lse = m + logf(s);
+  // target logit: the final-LN row against the head row of the target
+  const uint16_t* hr = (const uint16_t*)a.h + (int64_t)r * a.d;
+  const uint16_t* wr = (const uint16_t*)a.w + (int64_t)y * a.d;
+  float zy = 0.f;
+  for (int j = threadIdx.x * 8; j < a.d; j += kThreads * 8) {
+    const uint4 hv = *(const uint4*)(hr + j), wv = *(const uint4*)(wr + j);
+    zy += bf2f(hv.x & 0xffff) * bf2f(wv.x & 0xffff) + bf2f(hv.x >> 16) * bf2f(wv.x >> 16) +
+          bf2f(hv.y & 0xffff) * bf2f(wv.y & 0xffff) + bf2f(hv.y >> 16) * bf2f(wv.y >> 16) +
+          bf2f(hv.z & 0xffff) * bf2f(wv.z & 0xffff) + bf2f(hv.z >> 16) * bf2f(wv.z >> 16) +
+          bf2f(hv.w & 0xffff) * bf2f(wv.w & 0xffff) + bf2f(hv.w >> 16) * bf2f(wv.w >> 16);
+  }
+  zy = block_sum(zy, red + 2 * kWaves);
+  if (threadIdx.x == 0) a.loss_rows[r] = lse - zy;
+  for (int t = threadIdx.x; t < a.n_stats; t += kThreads)
+    cs[t] = __builtin_amdgcn_exp2f((st[2 * t] - lse) * kLog2e) * a.inv_rows;
+  __syncthreads();
+  // every 8-column chunk lies in one 128-column tile (V % 8 == 0)
+  typedef __attribute__((address_space(1))) ce_u4 ce_gu4;
+  ce_gu4* zp = (ce_gu4*)((uint16_t*)a.dz + (int64_t)r * a.V);
+  for (int i = threadIdx.x; i < a.V / 8; i += kThreads) {
+    const ce_u4 u = __builtin_nontemporal_load(zp + i);
+    const float c = cs[(8 * i) >> 7];
+    float p[8] = {bf2f(u.x & 0xffff), bf2f(u.x >> 16), bf2f(u.y & 0xffff), bf2f(u.y >> 16),
+                  bf2f(u.z & 0xffff), bf2f(u.z >> 16), bf2f(u.w & 0xffff), bf2f(u.w >> 16)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = p[e] * c - (8 * i + e == y ? a.inv_rows : 0.f);
+    __builtin_nontemporal_store(ce_u4{f2bf2(p[0], p[1]), f2bf2(p[2], p[3]), f2bf2(p[4], p[5]), f2bf2(p[6], p[7])}, zp + i);
+  }
+}
+
 // OCC 2 (two workgroups per CU, half the registers): rows beyond 16 float4 per
 // thread take the two-pass form
 template <int OCC = 1>
@@ -856,6 +904,10 @@ __device__ __forceinline__ void task_ce(const CeArgs& a, int tile, const TaskCtx
   const int r = tile;
   const int b = r / a.T, t = r % a.T;
   const int y = token_at(tc.sc, b, t + 1, a.T, a.V, tc);
+  if (a.fused) {
+    ce_row_fused(a, r, y, red);
+    return;
+  }
   const int n4 = a.V / 4;
   if (n4 <= 4 * kThreads) ce_row_regs<4>(a, r, y, red);
   else if (n4 <= 16 * kThreads) ce_row_regs<16>(a, r, y, red);

@@ -171,7 +171,7 @@ struct DevProg {
 
 struct Carve {
   // offsets (bytes) into the workspace
-  size_t p, g, m, v, wc, serve, xres, ln_mean, ln_rstd, h, qkv, o, lse, mlp1, mlp2, logits, dz, loss_rows;
+  size_t p, g, m, v, wc, serve, xres, ln_mean, ln_rstd, h, qkv, o, lse, mlp1, mlp2, logits, dz, loss_rows, ce_stats;
   size_t dxres, dxlp, dln, dmlp, dout, dsum, dqkv, ln_part, cs_fc, cs_qkv, esorted, efirst;
   size_t sched, status, times, inst_end, steps, published, trace, tables;
   size_t kv, ctx_tok, dstate, dx, dq, dapart, dmlp_v, dlogits, dsteps, dtimes, misc, dsched, dpart_v, dpart_i, dprompt;
@@ -237,6 +237,7 @@ Carve carve(const ofa_config& c, const Layout& lay) {
   w.logits = b.take(D.BT * D.V * f4);
   w.dz = b.take(D.BT * D.V * lp);
   w.loss_rows = b.take(D.BT * f4);
+  w.ce_stats = b.take(D.BT * ((D.V + 127) / 128) * 2 * f4);   // per row and 128-column tile: (max, sum)
   w.dxres = b.take(R * D.BT * D.d * f4);
   w.dxlp = bf ? b.take(R * D.BT * D.d * lp) : w.dxres;
   w.dln = b.take(R * D.BT * D.d * f4);
@@ -670,6 +671,17 @@ void build_train(ofa_handle* h) {
   const int64_t w_lm = c.tied_head ? h->lay.wte : h->lay.w_lm;
   GemmArgs g = gemm(h, (int)BT, (int)V, (int)d, Hh(2 * L), d, 1, lp, wc(w_lm), d, 1, lp, at<float>(ws, w.logits), V,
                     DT_F32, EPI_STORE);
+  // bf16 with the matrix-core tile: the LM head is fused with the softmax
+  // statistics (EPI_CE) and no fp32 logits are written; the cross-entropy then
+  // combines the per-tile statistics and turns exp(z - m_t) into dz in place
+  const bool fused_ce = g.impl == GEMM_P3 && lp == DT_BF16 && g.bn == 128 && !(c.debug_flags & OFA_DEBUG_CE_UNFUSED);
+  if (fused_ce) {
+    g.C = ws + w.dz;
+    g.c_dt = lp;
+    g.epi = EPI_CE;
+    g.stats = at<float>(ws, w.ce_stats);
+    g.stats_ld = g.tiles_n;
+  }
   int p_head = gemm_phase(g, {p_lnf}, "lm_head");
   int p_ce = b.add(OP_CE, (int)BT, "cross_entropy", {p_head});
   {
@@ -682,6 +694,14 @@ void build_train(ofa_handle* h) {
     a.T = (int)D.T;
     a.dt = lp;
     a.inv_rows = 1.0f / (float)BT;
+    if (fused_ce && b[p_head].a.gemm.epi == EPI_CE) {
+      a.fused = 1;
+      a.n_stats = g.tiles_n;
+      a.d = (int)d;
+      a.stats = at<float>(ws, w.ce_stats);
+      a.h = Hh(2 * L);
+      a.w = wc(w_lm);
+    }
   }
   int p_loss = b.add(OP_LOSS, 1, "loss", {p_ce});
   b[p_loss].a.loss.loss_rows = at<float>(ws, w.loss_rows);
@@ -912,8 +932,16 @@ void build_eval(ofa_handle* h) {
       ph.per_ticket = 1;
     }
     if (ph.op == OP_CE) {
-      ph.a.ce.dz = nullptr;
+      // the LM head writes full fp32 logits here (the probe reads them) and the
+      // cross-entropy only takes the loss
       p_head = ph.dep[0];
+      ph.a.ce.dz = nullptr;
+      ph.a.ce.fused = 0;
+      GemmArgs& g = h->eval[p_head].a.gemm;
+      g.epi = EPI_STORE;
+      g.C = at<float>(h->ws, h->cw.logits);
+      g.c_dt = DT_F32;
+      g.ldc = h->D.V;
     }
     if (ph.op == OP_LOSS) p_loss = (int)i;
     h->eval.push_back(ph);

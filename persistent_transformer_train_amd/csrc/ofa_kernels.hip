@@ -419,7 +419,8 @@ static size_t lds_for(const Phase& ph) {
       return ph.a.attn.impl == 1 ? attn_mfma_lds_bytes() : (size_t)kWaves * 256 * sizeof(float);
     case OP_ATTN_BWD_Q:
       return ph.a.attn.impl == 1 ? attn_mfma_lds_bytes() : (size_t)kWaves * 192 * sizeof(float);
-    case OP_CE: case OP_LOSS: return 64;
+    case OP_CE: return ph.a.ce.fused ? (size_t)(16 + ph.a.ce.n_stats) * sizeof(float) : 64;
+    case OP_LOSS: return 64;
     case OP_COLRED: return 16 * 16 * sizeof(float);
     case OP_COLSUM: return (size_t)kWaves * kCsCols * sizeof(float);
     case OP_EMB_SORT: {

@@ -22,7 +22,7 @@ _lib = C.CDLL(LIB_PATH)
 
 OFA_OK, OFA_E_ARG, OFA_E_HIP, OFA_E_NONFINITE, OFA_E_TIMEOUT, OFA_E_OVERFLOW, OFA_E_STATE = 0, -1, -2, -3, -4, -5, -6
 OFA_DEBUG_SHUFFLE_TICKETS, OFA_DEBUG_SHORT_WATCHDOG, OFA_DEBUG_TRACE, OFA_DEBUG_TILE256, OFA_DEBUG_OCC1 = 1, 2, 4, 8, 16
-OFA_DEBUG_PLAIN_TILES, OFA_DEBUG_WG_RELEASE = 32, 64
+OFA_DEBUG_PLAIN_TILES, OFA_DEBUG_WG_RELEASE, OFA_DEBUG_CE_UNFUSED = 32, 64, 128
 OFA_TRACE_INSTANCES = 1024
 
 

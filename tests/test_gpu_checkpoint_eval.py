@@ -158,10 +158,15 @@ def test_evaluate_matches_oracle_and_training_loss(name, tol, exec_mode):
             if decode.top2_margin(z[r]) > (1e-4 if tol < 1e-3 else 1e-1):
                 assert int(am[i, k]) == decode.argmax_lowest(z[r]), (i, k, r)
     # the training step's loss on the next batch equals the evaluation of that batch
-    # at the same weights, bit for bit (same forward kernels)
+    # at the same weights: bit for bit in fp32 mode (same kernels); in bf16 mode
+    # training fuses the LM head with the softmax statistics while evaluation keeps
+    # the fp32 logits for the probe, so the two sums differ in rounding only
     h.train_step(toks[:1].contiguous(), l)
     h.sync()
-    assert float(l[0]) == float(losses[0])
+    if tol < 1e-3:
+        assert float(l[0]) == float(losses[0])
+    else:
+        assert abs(float(l[0]) - float(losses[0])) <= 1e-5 * abs(float(losses[0]))
     h.close()
 
 
