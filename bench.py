@@ -138,6 +138,37 @@ def bench_decode(init, stream, args) -> dict:
                          "unit": "GB/s", "frac": round(bpt * rate / PEAK_HBM, 4), "bytes_per_token": bpt}}
 
 
+def bench_decode_batch(init, stream, args, nseq: int = 8) -> dict:
+    """Serving variant: nseq prompts of 32 tokens decoded together on the 48 serve
+    CUs (each weight tile streamed once per position for all sequences); the
+    first call (prefill + first token) is not timed.  Aggregate tokens/s."""
+    import torch
+    from persistent_transformer_train_amd import configs, ofa
+    dcfg = configs.get("c4", decode_batch=nseq, exec_mode=0 if args.exec_mode == "persistent" else 1)
+    h = ofa.Handle(dcfg, init)
+    prompts = torch.from_numpy(stream.prompts(nseq, dcfg["prompt_len"])).cuda().contiguous()
+    n = args.decode_tokens
+    toks = torch.zeros(n, nseq, dtype=torch.int32, device="cuda")
+    h.decode(prompts, 1, toks)
+    h.sync()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    h.decode(None, n - 1, toks[1:])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = h.sync()
+    h.close()
+    avg_ctx = (dcfg["prompt_len"] + dcfg["decode_window"]) / 2
+    one = decode_bytes_per_token(dcfg, avg_ctx)
+    kv = 2.0 * dcfg["n_layer"] * 2 * dcfg["d_model"] * avg_ctx
+    bytes_per_position = one + (nseq - 1) * kv   # weights once, every sequence's KV
+    return {"metric": f"batch-{nseq} greedy decode tokens/s (all sequences)", "value": round(nseq * (n - 1) / dt, 1),
+            "unit": "tokens/s", "sequences": nseq, "positions": n - 1, "kernel_ms": round(st.last_call_ms, 3),
+            "roofline": {"bound": "hbm", "achieved": round(bytes_per_position * (n - 1) / dt / 1e9, 1),
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": round(bytes_per_position * (n - 1) / dt / PEAK_HBM, 4)}}
+
+
 def bench_coresident(init, stream, args) -> dict:
     """c5: the training step on 208 CUs and batch-1 decode on 48 CUs in one
     persistent launch; decode restarts from the seeded prompt every 512 tokens
@@ -253,6 +284,7 @@ def main():
     h.close()
     if not args.no_decode and args.decode_tokens > 1:
         out["decode"] = bench_decode(init, stream, args)
+        out["decode_batch"] = bench_decode_batch(init, stream, args)
     if args.co_steps > 0 and args.exec_mode == "persistent":
         out["coresident"] = bench_coresident(init, stream, args)
 

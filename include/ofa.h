@@ -84,7 +84,8 @@ typedef struct {
   int32_t exec_mode;      /* ofa_exec_mode */
   uint64_t debug_counter_base;  /* start value of every ticket/phase counter (tests) */
   int32_t debug_flags;          /* OFA_DEBUG_* bits (tests only) */
-  int32_t reserved[7];          /* must be zero */
+  int32_t decode_batch;   /* sequences ofa_decode_token decodes together (0 or 1: one; at most 8) */
+  int32_t reserved[6];          /* must be zero */
 } ofa_config;
 
 #define OFA_DEBUG_SHUFFLE_TICKETS 1  /* persistent mode: permute tile order inside a phase */

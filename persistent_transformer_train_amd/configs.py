@@ -26,7 +26,7 @@ _BASE = dict(
     lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
     lr_schedule=LR_CONSTANT, total_steps=1,
     train_cus=0, serve_cus=0, decode_window=0, prompt_len=0, restart_every=0,
-    exec_mode=EXEC_PERSISTENT, debug_counter_base=0, debug_flags=0,
+    exec_mode=EXEC_PERSISTENT, debug_counter_base=0, debug_flags=0, decode_batch=0,
 )
 
 

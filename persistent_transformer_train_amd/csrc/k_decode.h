@@ -22,13 +22,14 @@ __device__ __forceinline__ const T* slot_ptr(const void* p, const DecState* st) 
 // ---------------------------------------------------------------- embedding
 
 __device__ void task_dec_embed(const DecEmbedArgs& a, int tile, const TaskCtx& tc) {
-  __shared__ int s_tok;
+  __shared__ int s_tok[8];   // one per sequence (nseq <= 8)
   const int pos = tc.sc->pos;
   if (threadIdx.x == 0) {
     DecState* st = a.st;
     if (tc.sc->head & 4) {    // restart: the saved prompt becomes the context again
       const int n = st->prompt_len;
-      for (int i = 0; i < n; ++i) a.ctx_tok[i] = a.prompt[i];
+      for (int q = 0; q < a.nseq; ++q)
+        for (int i = 0; i < n; ++i) a.ctx_tok[q * a.cap + i] = a.prompt[q * a.cap + i];
       st->ctx_len = n;
     }
     if (tc.sc->head & 2) {    // first position of a token: acquire the newest weights
@@ -39,20 +40,24 @@ __device__ void task_dec_embed(const DecEmbedArgs& a, int tile, const TaskCtx& t
       // that acquires this value overwrites that slot
       st_release(&st->version, ver);
     }
-    int tok = a.ctx_tok[pos];
-    if (tok < 0 || tok >= a.V) {
-      raise_status(tc.status, -1, tc.phase, tc.step, tok);
-      tok = 0;
+    for (int q = 0; q < a.nseq; ++q) {
+      int tok = a.ctx_tok[q * a.cap + pos];
+      if (tok < 0 || tok >= a.V) {
+        raise_status(tc.status, -1, tc.phase, tc.step, tok);
+        tok = 0;
+      }
+      s_tok[q] = tok;
     }
-    s_tok = tok;
   }
   __syncthreads();
-  const int tok = s_tok;
   const DecState* st = a.st;
-  for (int j = threadIdx.x; j < a.d; j += kThreads) {
-    float v = ldf((const char*)a.wte + st->w_delta, (int64_t)tok * a.d + j, a.w_dt);
-    if (a.wpe) v += ldf((const char*)a.wpe + st->w_delta, (int64_t)pos * a.d + j, a.w_dt);
-    a.x[j] = v;
+  for (int q = 0; q < a.nseq; ++q) {
+    const int tok = s_tok[q];
+    for (int j = threadIdx.x; j < a.d; j += kThreads) {
+      float v = ldf((const char*)a.wte + st->w_delta, (int64_t)tok * a.d + j, a.w_dt);
+      if (a.wpe) v += ldf((const char*)a.wpe + st->w_delta, (int64_t)pos * a.d + j, a.w_dt);
+      a.x[(int64_t)q * a.d + j] = v;
+    }
   }
 }
 
@@ -110,8 +115,10 @@ __host__ __device__ inline int dec_tile_rows_all(const DecGemvArgs& a) {
   return (a.epi == DEPI_GEGLU ? 2 : 1) * a.rows_per_tile;
 }
 
+// LDS: [ring n_buf x kDecTile][xs: nseq K fp32][ys: nseq ys_rows][ys2: nseq ys_rows][64 scratch]
+__host__ __device__ inline int dec_nseq(const DecGemvArgs& a) { return a.nseq > 1 ? a.nseq : 1; }
 __host__ __device__ inline size_t dec_gemv_lds_bytes(const DecGemvArgs& a) {
-  return (size_t)a.n_buf * kDecTile + (size_t)(a.K + 2 * a.ys_rows + 64) * sizeof(float);
+  return (size_t)a.n_buf * kDecTile + (size_t)(dec_nseq(a) * (a.K + 2 * a.ys_rows) + 64) * sizeof(float);
 }
 
 __device__ __forceinline__ int dec_row_bytes(const DecGemvArgs& a) { return a.K * (a.w_dt == DT_BF16 ? 2 : 4); }
@@ -250,17 +257,23 @@ __device__ __forceinline__ void dec_tile_dot(const DecGemvArgs& a, const char* t
 }
 
 // Tiles [t0, t1) of one GEMV; tiles [t0, t0 + npre) were issued by the prefetch.
-__device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0, int t1, const TaskCtx& tc,
-                                                    char* smem, int npre) {
+// Every sequence's rows are dot products against the same LDS tiles, in the
+// same lane order as for one sequence.
+// MULTI = false: one sequence, known at compile time (the loops over sequences
+// fold away and the input chunks stay in registers for the whole ticket).
+template <bool MULTI>
+__device__ __forceinline__ void task_dec_gemv_range_t(const DecGemvArgs& a, int t0, int t1, const TaskCtx& tc,
+                                                      char* smem, int npre) {
   if (a.epi == DEPI_LOGITS && !(tc.sc->head & 1)) {   // prefill position: no logits needed
     if (npre) vm_wait_barrier(0);                      // drain the prefetched copies
     return;
   }
+  const int ns = MULTI ? dec_nseq(a) : 1;
   char* ring = smem;
-  float* xs = (float*)(smem + (size_t)a.n_buf * kDecTile);   // [K]
-  float* ys = xs + a.K;                                        // [ys_rows]
-  float* ys2 = ys + a.ys_rows;                                 // [ys_rows] (gated: up half)
-  float* red = ys2 + a.ys_rows;                                // [64]
+  float* xs = (float*)(smem + (size_t)a.n_buf * kDecTile);   // [ns][K]
+  float* ys = xs + (size_t)ns * a.K;                          // [ns][ys_rows]
+  float* ys2 = ys + (size_t)ns * a.ys_rows;                   // [ns][ys_rows] (gated: up half)
+  float* red = ys2 + (size_t)ns * a.ys_rows;                  // [64]
   const DecState* st = a.st;
   // with one weight slot the offset is always 0 (no dependent load)
   const int64_t wd = a.pre_dep >= 0 ? st->w_delta : 0;
@@ -274,14 +287,14 @@ __device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0
   float* const logits_out = a.epi == DEPI_LOGITS ? a.io->logits_out : nullptr;
   // Everything that does not come from the tiles is read in one batch of
   // loads: the input (and its first element, the LayerNorm shift), the
-  // LayerNorm parameters, and the bias and residual of this thread's output rows.
+  // LayerNorm parameters, and the bias and residual of this thread's output
+  // rows (sequence 0; further sequences read theirs in the epilogue).
   const void* bias = a.bias ? (const void*)((const char*)a.bias + wd) : nullptr;
   const int r0 = t0 * a.rows_per_tile;
   const int nrows = min(nt * a.rows_per_tile, (a.epi == DEPI_GEGLU ? a.F : a.N) - r0);
   constexpr int kPre = 4;   // rows per thread held in registers (the rest read in the epilogue)
   constexpr int kMaxK = 4;  // input elements per thread (K <= 1024)
   float pre_b[kPre], pre_r[kPre], gv[kMaxK], bv[kMaxK], xv[kMaxK];
-  float x0 = 0.f;
 #pragma unroll
   for (int m = 0; m < kPre; ++m) {
     const int i = threadIdx.x + m * kThreads;
@@ -297,75 +310,82 @@ __device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0
       gv[m] = j < a.K ? ldf(g, j, a.w_dt) : 0.f;
       bv[m] = j < a.K ? ldf(b, j, a.w_dt) : 0.f;
     }
-    x0 = a.xin[0];
   }
-  if (a.attn_part) {
-    // the attention output: per head, the key-range partials rescaled to their
-    // common maximum, summed, and divided by the summed weights
-    const int Wd = a.dh + 2;
-    constexpr int kSplitMax = 8;
-    for (int j = threadIdx.x; j < a.K; j += kThreads) {
-      const float* ph = a.attn_part + (int64_t)(j / a.dh) * a.attn_split * Wd;
-      float mc[kSplitMax], lc[kSplitMax], oc[kSplitMax];
+  for (int q = 0; q < ns; ++q) {
+    float* xq = xs + (size_t)q * a.K;
+    if (a.attn_part) {
+      // the attention output: per head, the key-range partials rescaled to their
+      // common maximum, summed, and divided by the summed weights
+      const float* apq = a.attn_part + (int64_t)q * a.attn_ss;
+      const int Wd = a.dh + 2;
+      constexpr int kSplitMax = 8;
+      for (int j = threadIdx.x; j < a.K; j += kThreads) {
+        const float* ph = apq + (int64_t)(j / a.dh) * a.attn_split * Wd;
+        float mc[kSplitMax], lc[kSplitMax], oc[kSplitMax];
 #pragma unroll
-      for (int c = 0; c < kSplitMax; ++c)   // all loads first: one round trip
-        if (c < a.attn_split) {
-          mc[c] = ph[c * Wd + a.dh];
-          lc[c] = ph[c * Wd + a.dh + 1];
-          oc[c] = ph[c * Wd + j % a.dh];
-        }
-      float m = -INFINITY;
+        for (int c = 0; c < kSplitMax; ++c)   // all loads first: one round trip
+          if (c < a.attn_split) {
+            mc[c] = ph[c * Wd + a.dh];
+            lc[c] = ph[c * Wd + a.dh + 1];
+            oc[c] = ph[c * Wd + j % a.dh];
+          }
+        float m = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < kSplitMax; ++c)
-        if (c < a.attn_split) m = fmaxf(m, mc[c]);
-      float num = 0.f, den = 0.f;
+        for (int c = 0; c < kSplitMax; ++c)
+          if (c < a.attn_split) m = fmaxf(m, mc[c]);
+        float num = 0.f, den = 0.f;
 #pragma unroll
-      for (int c = 0; c < kSplitMax; ++c)
-        if (c < a.attn_split && mc[c] != -INFINITY) {   // an empty key range adds nothing
-          const float e = expf(mc[c] - m);
-          num += e * oc[c];
-          den += e * lc[c];
-        }
-      xs[j] = num / den;
-    }
-  } else if (!a.ln_g) {
-    for (int j = threadIdx.x; j < a.K; j += kThreads) xs[j] = a.xin[j];   // any K (the MLP down product)
-  } else {
-    // LayerNorm'd input: K = d_model <= 1024, four elements per thread
+        for (int c = 0; c < kSplitMax; ++c)
+          if (c < a.attn_split && mc[c] != -INFINITY) {   // an empty key range adds nothing
+            const float e = expf(mc[c] - m);
+            num += e * oc[c];
+            den += e * lc[c];
+          }
+        xq[j] = num / den;
+      }
+    } else if (!a.ln_g) {
+      const float* xin = a.xin + (int64_t)q * a.xin_ss;
+      for (int j = threadIdx.x; j < a.K; j += kThreads) xq[j] = xin[j];   // any K (the MLP down product)
+    } else {
+      // LayerNorm'd input: K = d_model <= 1024, four elements per thread
+      const float* xin = a.xin + (int64_t)q * a.xin_ss;
+      const float x0 = xin[0];
 #pragma unroll
-    for (int m = 0; m < kMaxK; ++m) {
-      const int j = threadIdx.x + m * kThreads;
-      xv[m] = j < a.K ? a.xin[j] : 0.f;
-    }
-    {
-      // one reduction for the sum and the sum of squares, both shifted by the
-      // first element (the shift keeps the variance free of cancellation when
-      // the mean is large against the spread)
-      float s0 = 0.f, q = 0.f;
+      for (int m = 0; m < kMaxK; ++m) {
+        const int j = threadIdx.x + m * kThreads;
+        xv[m] = j < a.K ? xin[j] : 0.f;
+      }
+      {
+        // one reduction for the sum and the sum of squares, both shifted by the
+        // first element (the shift keeps the variance free of cancellation when
+        // the mean is large against the spread)
+        float s0 = 0.f, qq = 0.f;
 #pragma unroll
-      for (int m = 0; m < kMaxK; ++m)
-        if (threadIdx.x + m * kThreads < a.K) {
-          const float dv = xv[m] - x0;
-          s0 += dv;
-          q += dv * dv;
-        }
-      const float2 sq = block_sum2_dpp(s0, q, red);
-      const float ms = sq.x / a.K;
-      const float mean = x0 + ms;
-      const float rstd = 1.0f / sqrtf(fmaxf(sq.y / a.K - ms * ms, 0.f) + 1e-5f);
+        for (int m = 0; m < kMaxK; ++m)
+          if (threadIdx.x + m * kThreads < a.K) {
+            const float dv = xv[m] - x0;
+            s0 += dv;
+            qq += dv * dv;
+          }
+        const float2 sq = block_sum2_dpp(s0, qq, red);
+        const float ms = sq.x / a.K;
+        const float mean = x0 + ms;
+        const float rstd = 1.0f / sqrtf(fmaxf(sq.y / a.K - ms * ms, 0.f) + 1e-5f);
 #pragma unroll
-      for (int m = 0; m < kMaxK; ++m) xv[m] = (xv[m] - mean) * rstd * gv[m] + bv[m];
-    }
+        for (int m = 0; m < kMaxK; ++m) xv[m] = (xv[m] - mean) * rstd * gv[m] + bv[m];
+      }
 #pragma unroll
-    for (int m = 0; m < kMaxK; ++m) {
-      const int j = threadIdx.x + m * kThreads;
-      if (j < a.K) xs[j] = xv[m];
+      for (int m = 0; m < kMaxK; ++m) {
+        const int j = threadIdx.x + m * kThreads;
+        if (j < a.K) xq[j] = xv[m];
+      }
     }
   }
   __syncthreads();
-  // this lane's input chunks, in registers for the whole ticket
+  // this lane's input chunks of one sequence, in registers
   float xr[kDecMaxChunks][8];
-  {
+  auto load_xr = [&](int q) {
+    const float* xq = xs + (size_t)q * a.K;
     const int li = threadIdx.x % a.lpr;
     const bool bf = a.w_dt == DT_BF16;
     const int nch = dec_row_bytes(a) / 16;
@@ -375,16 +395,17 @@ __device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0
       float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
       if (c < nch) {
         if (bf) {
-          lo = *(const float4*)(xs + c * 8);
-          hi = *(const float4*)(xs + c * 8 + 4);
+          lo = *(const float4*)(xq + c * 8);
+          hi = *(const float4*)(xq + c * 8 + 4);
         } else {
-          lo = *(const float4*)(xs + c * 4);
+          lo = *(const float4*)(xq + c * 4);
         }
       }
       xr[j][0] = lo.x; xr[j][1] = lo.y; xr[j][2] = lo.z; xr[j][3] = lo.w;
       xr[j][4] = hi.x; xr[j][5] = hi.y; xr[j][6] = hi.z; xr[j][7] = hi.w;
     }
-  }
+  };
+  if (ns == 1) load_xr(0);   // one sequence: loaded once for the whole ticket
   for (int i = 0; i < nt; ++i) {
     // tile i landed in every wave, and every wave is done with tile i - 1's buffer
     dec_wait_tile(issued - i - 1);
@@ -392,8 +413,11 @@ __device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0
       dec_tile_issue(a, W, t0 + issued, ring, issued % a.n_buf);
       ++issued;
     }
-    dec_tile_dot(a, ring + (size_t)(i % a.n_buf) * kDecTile, dec_tile_rows(a, t0 + i), xr,
-                 ys + i * a.rows_per_tile, ys2 + i * a.rows_per_tile);
+    for (int q = 0; q < ns; ++q) {
+      if (ns > 1) load_xr(q);
+      dec_tile_dot(a, ring + (size_t)(i % a.n_buf) * kDecTile, dec_tile_rows(a, t0 + i), xr,
+                   ys + (size_t)q * a.ys_rows + i * a.rows_per_tile, ys2 + (size_t)q * a.ys_rows + i * a.rows_per_tile);
+    }
     if (a.n_buf == 1 && issued < nt) {   // one buffer: refill once every wave has read it
       __syncthreads();
       dec_tile_issue(a, W, t0 + issued, ring, 0);
@@ -401,72 +425,86 @@ __device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0
     }
   }
   __syncthreads();
-  // epilogue over the ticket's rows
-  for (int i = threadIdx.x, m = 0; i < nrows; i += kThreads, ++m) {
-    const int n = r0 + i;
-    float v = ys[i];
-    float rv = 0.f;
-    if (m < kPre) {
+  // epilogue over the ticket's rows, sequence by sequence
+  for (int q = 0; q < ns; ++q) {
+    const float* ysq = ys + (size_t)q * a.ys_rows;
+    const float* ys2q = ys2 + (size_t)q * a.ys_rows;
+    float* yq = a.y + (int64_t)q * a.y_ss;
+    const float* rq = a.resid ? a.resid + (int64_t)q * a.resid_ss : nullptr;
+    void* kvq = a.kv ? (void*)((char*)a.kv + (size_t)q * a.kv_ss * (a.kv_dt == DT_BF16 ? 2 : 4)) : nullptr;
+    for (int i = threadIdx.x, m = 0; i < nrows; i += kThreads, ++m) {
+      const int n = r0 + i;
+      float v = ysq[i];
+      float rv = 0.f;
+      if (m < kPre) {
 #pragma unroll
-      for (int q = 0; q < kPre; ++q)
-        if (q == m) {
-          v += pre_b[q];
-          rv = pre_r[q];
-        }
-    } else {
-      if (bias) v += ldf(bias, n, a.w_dt);
-      if (a.epi == DEPI_RESID) rv = a.resid[n];
-    }
-    switch (a.epi) {
-      case DEPI_STORE: a.y[n] = v; break;
-      case DEPI_RESID: a.y[n] = rv + v; break;
-      case DEPI_GELU: a.y[n] = gelu_f(v); break;
-      case DEPI_GEGLU: a.y[n] = gelu_f(v) * ys2[i]; break;
-      case DEPI_LOGITS:
-        a.y[n] = v;
-        if (logits_out) logits_out[gen_idx * a.N + n] = v;
-        break;
-      case DEPI_QKV: {
-        // a ticket covers whole heads when the rotation is on (host plan)
-        const int part = n / a.d, h = (n % a.d) / a.dh, j = n % a.dh;
-        float out = v;
-        if (a.rope && part < 2) {
-          const int hl = a.dh / 2;
-          const int jj = j < hl ? j : j - hl;
-          const double ang = (double)pos * pow(10000.0, -2.0 * jj / a.dh);
-          const float c = (float)cos(ang), sn = (float)sin(ang);
-          const int io = j < hl ? i + hl : i - hl;
-          float other = ys[io];
-          if (bias) other += ldf(bias, r0 + io, a.w_dt);
-          out = j < hl ? v * c - other * sn : other * sn + v * c;
-        }
-        if (part == 0) {
-          a.y[n] = out;
-        } else {
-          const int64_t ci = (((int64_t)(part - 1) * a.H + h) * a.cap + pos) * a.dh + j;
-          stf(a.kv, ci, a.kv_dt, out);
-        }
-      } break;
-    }
-  }
-  if (a.epi == DEPI_LOGITS) {
-    // this ticket's (max, first index): ascending per thread, then lowest index
-    // among equal maxima; a NaN never wins
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int i = threadIdx.x; i < nrows; i += kThreads)
-      if (ys[i] > bv) {
-        bv = ys[i];
-        bi = r0 + i;
+        for (int u = 0; u < kPre; ++u)
+          if (u == m) {
+            v += pre_b[u];
+            rv = pre_r[u];
+          }
+        if (q > 0 && a.epi == DEPI_RESID) rv = rq[n];
+      } else {
+        if (bias) v += ldf(bias, n, a.w_dt);
+        if (a.epi == DEPI_RESID) rv = rq[n];
       }
-    argmax_combine_block(bv, bi, red);
-    if (threadIdx.x == 0) {
-      const int ticket = t0 / a.per_ticket;
-      a.part_val[ticket] = bv;
-      a.part_idx[ticket] = bi;
+      switch (a.epi) {
+        case DEPI_STORE: yq[n] = v; break;
+        case DEPI_RESID: yq[n] = rv + v; break;
+        case DEPI_GELU: yq[n] = gelu_f(v); break;
+        case DEPI_GEGLU: yq[n] = gelu_f(v) * ys2q[i]; break;
+        case DEPI_LOGITS:
+          yq[n] = v;
+          if (logits_out) logits_out[(gen_idx * ns + q) * a.N + n] = v;
+          break;
+        case DEPI_QKV: {
+          // a ticket covers whole heads when the rotation is on (host plan)
+          const int part = n / a.d, h = (n % a.d) / a.dh, j = n % a.dh;
+          float out = v;
+          if (a.rope && part < 2) {
+            const int hl = a.dh / 2;
+            const int jj = j < hl ? j : j - hl;
+            const double ang = (double)pos * pow(10000.0, -2.0 * jj / a.dh);
+            const float c = (float)cos(ang), sn = (float)sin(ang);
+            const int io = j < hl ? i + hl : i - hl;
+            float other = ysq[io];
+            if (bias) other += ldf(bias, r0 + io, a.w_dt);
+            out = j < hl ? v * c - other * sn : other * sn + v * c;
+          }
+          if (part == 0) {
+            yq[n] = out;
+          } else {
+            const int64_t ci = (((int64_t)(part - 1) * a.H + h) * a.cap + pos) * a.dh + j;
+            stf(kvq, ci, a.kv_dt, out);
+          }
+        } break;
+      }
+    }
+    if (a.epi == DEPI_LOGITS) {
+      // this ticket's (max, first index): ascending per thread, then lowest index
+      // among equal maxima; a NaN never wins
+      float bvv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int i = threadIdx.x; i < nrows; i += kThreads)
+        if (ysq[i] > bvv) {
+          bvv = ysq[i];
+          bi = r0 + i;
+        }
+      argmax_combine_block(bvv, bi, red);
+      if (threadIdx.x == 0) {
+        const int ticket = t0 / a.per_ticket;
+        a.part_val[(int64_t)q * a.part_ss + ticket] = bvv;
+        a.part_idx[(int64_t)q * a.part_ss + ticket] = bi;
+      }
     }
   }
   __syncthreads();
+}
+
+__device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0, int t1, const TaskCtx& tc, char* smem,
+                                                    int npre) {
+  if (a.nseq > 1) task_dec_gemv_range_t<true>(a, t0, t1, tc, smem, npre);
+  else task_dec_gemv_range_t<false>(a, t0, t1, tc, smem, npre);
 }
 
 __device__ void task_dec_gemv(const DecGemvArgs& a, int tile, const TaskCtx& tc, char* smem) {
@@ -508,8 +546,11 @@ template <int ept>
 __device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc, char* smem) {
   constexpr int kKMax = 64 / ept;   // chunks of a key row (head size <= 64)
   constexpr int kVPre = 4;          // value rows per thread read ahead
-  const int h = tile / a.split, c = tile % a.split;
+  const int sq = tile / (a.H * a.split);
+  const int h = (tile / a.split) % a.H, c = tile % a.split;
   const int pos = tc.sc->pos;
+  const float* qv_base = a.q + (int64_t)sq * a.H * a.dh;
+  const void* kvq = (const char*)a.kv + (size_t)sq * a.kv_ss * (a.kv_dt == DT_BF16 ? 2 : 4);
   const int n_keys = pos + 1;
   const int cl = (n_keys + a.split - 1) / a.split;
   const int s0 = min(c * cl, n_keys), s1 = min(s0 + cl, n_keys);
@@ -518,7 +559,7 @@ __device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc,
   float* acc2 = qs + a.dh;                          // [row slots][dh]
   const int lpr = a.dh / ept, slots = kThreads / lpr;
   float* red = acc2 + slots * a.dh;                 // [16]
-  float* out = a.part + (int64_t)tile * (a.dh + 2);
+  float* out = a.part + (int64_t)sq * a.part_ss + (int64_t)(tile % (a.H * a.split)) * (a.dh + 2);
   const float scale = 1.0f / sqrtf((float)a.dh);
   const int64_t kbase = (int64_t)h * a.cap * a.dh;
   const int64_t vbase = ((int64_t)a.H + h) * a.cap * a.dh;
@@ -526,17 +567,17 @@ __device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc,
   const int slot = threadIdx.x / lpr, ci = threadIdx.x % lpr;
   // every load that does not depend on another is issued first: the query, this
   // thread's first key row and its first value chunks
-  const float qv = threadIdx.x < a.dh ? a.q[h * a.dh + threadIdx.x] : 0.f;
+  const float qv = threadIdx.x < a.dh ? qv_base[h * a.dh + threadIdx.x] : 0.f;
   const int s_k = s0 + threadIdx.x;
   float kr[kKMax][ept];
 #pragma unroll
   for (int j = 0; j < kKMax; ++j)
-    if (j < nkc && s_k < s1) kv_chunk(a.kv, kbase + (int64_t)s_k * a.dh + j * ept, a.kv_dt, ept, kr[j]);
+    if (j < nkc && s_k < s1) kv_chunk(kvq, kbase + (int64_t)s_k * a.dh + j * ept, a.kv_dt, ept, kr[j]);
   float vr[kVPre][ept];
 #pragma unroll
   for (int m = 0; m < kVPre; ++m) {
     const int s = s0 + slot + m * slots;
-    if (s < s1) kv_chunk(a.kv, vbase + (int64_t)s * a.dh + ci * ept, a.kv_dt, ept, vr[m]);
+    if (s < s1) kv_chunk(kvq, vbase + (int64_t)s * a.dh + ci * ept, a.kv_dt, ept, vr[m]);
   }
   if (threadIdx.x < a.dh) qs[threadIdx.x] = qv * scale;
   __syncthreads();
@@ -565,7 +606,7 @@ __device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc,
     float acc = 0.f;
     for (int j = 0; j < a.dh; j += ept) {
       float k[8];
-      kv_chunk(a.kv, kbase + (int64_t)s * a.dh + j, a.kv_dt, ept, k);
+      kv_chunk(kvq, kbase + (int64_t)s * a.dh + j, a.kv_dt, ept, k);
 #pragma unroll
       for (int e = 0; e < ept; ++e) acc += qs[j + e] * k[e];
     }
@@ -595,7 +636,7 @@ __device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc,
   }
   for (int s = s0 + slot + kVPre * slots; s < s1; s += slots) {
     float v[8];
-    kv_chunk(a.kv, vbase + (int64_t)s * a.dh + ci * ept, a.kv_dt, ept, v);
+    kv_chunk(kvq, vbase + (int64_t)s * a.dh + ci * ept, a.kv_dt, ept, v);
     const float p = sc[s - s0];
 #pragma unroll
     for (int e = 0; e < ept; ++e) o[e] += p * v[e];
@@ -628,40 +669,47 @@ __device__ void task_dec_attn(const DecAttnArgs& a, int tile, const TaskCtx& tc,
 __device__ void task_dec_argmax(const DecArgmaxArgs& a, int tile, const TaskCtx& tc, char* smem) {
   if (!(tc.sc->head & 1)) return;
   float* red = (float*)smem;   // [16]
-  float best = -INFINITY;
-  int idx = 0x7fffffff;
-  for (int i = threadIdx.x; i < a.n_part; i += kThreads) {
-    const float z = a.part_val[i];
-    const int zi = a.part_idx[i];
-    if (z > best || (z == best && zi < idx)) {
-      best = z;
-      idx = zi;
+  int* ys = (int*)(red + 16);  // [nseq] chosen tokens
+  for (int q = 0; q < a.nseq; ++q) {
+    float best = -INFINITY;
+    int idx = 0x7fffffff;
+    for (int i = threadIdx.x; i < a.n_part; i += kThreads) {
+      const float z = a.part_val[q * a.part_ss + i];
+      const int zi = a.part_idx[q * a.part_ss + i];
+      if (z > best || (z == best && zi < idx)) {
+        best = z;
+        idx = zi;
+      }
     }
+    argmax_combine_block(best, idx, red);
+    if (threadIdx.x == 0) ys[q] = idx;
   }
-  argmax_combine_block(best, idx, red);
+  __syncthreads();
   if (threadIdx.x == 0) {
-    int y = idx;
-    if (y < 0 || y >= a.V) {   // every logit was NaN
-      raise_status(tc.status, -3 /*OFA_E_NONFINITE*/, tc.phase, tc.step, 0);
-      y = 0;
-    }
     DecState* st = a.st;
     const int gi = tc.sc->gen_idx;
     const int64_t g = tc.gen_base + gi;   // tokens emitted before this one
     const int64_t slot = g % a.io->ring_len;
-    a.io->tokens_out[slot] = y;
+    const int L = st->ctx_len;
+    for (int q = 0; q < a.nseq; ++q) {
+      int y = ys[q];
+      if (y < 0 || y >= a.V) {   // every logit was NaN
+        raise_status(tc.status, -3 /*OFA_E_NONFINITE*/, tc.phase, tc.step, 0);
+        y = 0;
+      }
+      a.io->tokens_out[slot * a.nseq + q] = y;
+      int32_t* ctx = a.ctx_tok + q * a.cap;
+      if (L + 1 > a.cap) {
+        // context full: keep the most recent `keep` tokens (the new one included) at 0..keep-1
+        for (int i = 0; i < a.keep - 1; ++i) ctx[i] = ctx[L - a.keep + 1 + i];
+        ctx[a.keep - 1] = y;
+      } else {
+        ctx[L] = y;
+      }
+    }
     if (a.io->versions_out) a.io->versions_out[slot] = st->version;
     if (a.io->n_generated) st_release(a.io->n_generated, (uint64_t)(g + 1));
-    int L = st->ctx_len;
-    if (L + 1 > a.cap) {
-      // context full: keep the most recent `keep` tokens (the new one included) at 0..keep-1
-      for (int i = 0; i < a.keep - 1; ++i) a.ctx_tok[i] = a.ctx_tok[L - a.keep + 1 + i];
-      a.ctx_tok[a.keep - 1] = y;
-      st->ctx_len = a.keep;
-    } else {
-      a.ctx_tok[L] = y;
-      st->ctx_len = L + 1;
-    }
+    st->ctx_len = L + 1 > a.cap ? a.keep : L + 1;
     st->n_gen = gi + 1;
   }
   __syncthreads();

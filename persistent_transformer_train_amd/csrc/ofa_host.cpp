@@ -35,6 +35,7 @@ constexpr size_t kMiscBytes = 4096;    // one Phase (offset 0) and the DecIO blo
 constexpr size_t kMiscDecIO = 2048;
 constexpr int kMaxAttnSplit = 8;        // key ranges per head in decode attention
 constexpr int kThreadsHost = 256;       // threads of every workgroup
+constexpr int kMaxDecSeq = 8;           // sequences one decode call decodes together
 // the device copies of the two programs' phase tables and their per-partition
 // ticket tables live in the workspace (the library allocates no device memory)
 constexpr size_t kTableBytes = 3 * (size_t)512 * 320 + 9 * (size_t)8 * 513 * 4 + 4096;
@@ -142,6 +143,9 @@ std::string validate(const ofa_config& c) {
   const int keep = c.prompt_len ? c.prompt_len : 1;
   if (keep < 1 || keep > win) return bad("prompt_len %d invalid for window %d", keep, win);
   if (c.train_cus < 0 || c.serve_cus < 0) return bad("negative CU count");
+  if (c.decode_batch < 0 || c.decode_batch > kMaxDecSeq) return bad("decode_batch %d out of [0, %d]", c.decode_batch, kMaxDecSeq);
+  if (c.decode_batch > 1 && c.train_cus > 0 && c.serve_cus > 0)
+    return bad("co-resident decode runs one sequence (decode_batch %d)", c.decode_batch);
   for (int r : c.reserved)
     if (r) return bad("reserved fields must be zero");
   return "";
@@ -181,7 +185,7 @@ struct Carve {
 };
 
 struct Dims {
-  int64_t B, T, BT, d, H, dh, F, V, L, P, win, keep, mlp1_cols;
+  int64_t B, T, BT, d, H, dh, F, V, L, P, win, keep, mlp1_cols, nseq;
   int lp_dt;
   size_t lp;   // bytes per low-precision element
 };
@@ -201,6 +205,7 @@ Dims dims_of(const ofa_config& c, const Layout& lay) {
   D.win = c.decode_window ? c.decode_window : (c.n_pos ? c.n_pos : c.seq);
   D.keep = c.prompt_len ? c.prompt_len : 1;
   D.mlp1_cols = c.mlp_gated ? 2 * D.F : D.F;
+  D.nseq = c.decode_batch > 1 ? c.decode_batch : 1;
   D.lp_dt = c.precision == OFA_BF16 ? DT_BF16 : DT_F32;
   D.lp = c.precision == OFA_BF16 ? 2 : 4;
   return D;
@@ -257,19 +262,20 @@ Carve carve(const ofa_config& c, const Layout& lay) {
   w.inst_end = b.take(kMaxSteps * 8);
   w.steps = b.take(kMaxSteps * sizeof(StepCtx));
   w.published = b.take(64);
-  w.kv = b.take(D.L * 2 * D.H * D.win * D.dh * lp);
-  w.ctx_tok = b.take(D.win * 4);
+  // decode: per sequence s of nseq, [s][...] blocks (vectors: [point][s][d])
+  w.kv = b.take(D.nseq * D.L * 2 * D.H * D.win * D.dh * lp);
+  w.ctx_tok = b.take(D.nseq * D.win * 4);
   w.dstate = b.take(sizeof(DecState));
-  w.dx = b.take(R * D.d * f4);
-  w.dq = b.take(D.d * f4);
-  w.dapart = b.take(D.L * D.H * kMaxAttnSplit * (D.dh + 2) * f4);
-  w.dmlp_v = b.take(D.L * D.F * f4);
-  w.dlogits = b.take(D.V * f4);
+  w.dx = b.take(R * D.nseq * D.d * f4);
+  w.dq = b.take(D.nseq * D.d * f4);
+  w.dapart = b.take(D.L * D.nseq * D.H * kMaxAttnSplit * (D.dh + 2) * f4);
+  w.dmlp_v = b.take(D.L * D.nseq * D.F * f4);
+  w.dlogits = b.take(D.nseq * D.V * f4);
   w.dsteps = b.take((size_t)kMaxDecInst * sizeof(StepCtx));
   w.dsched = b.take(sizeof(Sched));
-  w.dprompt = b.take(D.win * 4);
-  w.dpart_v = b.take(D.V * f4);
-  w.dpart_i = b.take(D.V * 4);
+  w.dprompt = b.take(D.nseq * D.win * 4);
+  w.dpart_v = b.take(D.nseq * D.V * f4);
+  w.dpart_i = b.take(D.nseq * D.V * 4);
   w.misc = b.take(kMiscBytes);
   w.tables = b.take(kTableBytes);
   w.trace = (c.debug_flags & OFA_DEBUG_TRACE) ? b.take((size_t)OFA_TRACE_INSTANCES * kMaxPhases * 32) : 0;
@@ -1017,7 +1023,11 @@ void build_decode(ofa_handle* h) {
   char* S = ws + w.serve;   // slot 0
   auto sw = [&](int64_t off) -> const void* { return off < 0 ? nullptr : S + off * D.lp; };
   float* dx = at<float>(ws, w.dx);
-  auto XV = [&](int i) { return dx + (int64_t)i * d; };
+  const int64_t ns = D.nseq;
+  auto XV = [&](int i) { return dx + (int64_t)i * ns * d; };   // [point][sequence][d]
+  // per-sequence blocks: KV cache of all layers, attention partials of one layer
+  const int64_t kv_ss = D.L * 2 * D.H * D.win * D.dh;
+  const int64_t attn_ss = D.H * kMaxAttnSplit * (D.dh + 2);
   DecState* st = at<DecState>(ws, w.dstate);
   const int64_t slot_bytes = w.n_slots > 1 ? D.P * D.lp : 0;
   int p_emb = b.add(OP_DEC_EMBED, 1, "dec_embed");
@@ -1028,6 +1038,8 @@ void build_decode(ofa_handle* h) {
     a.ctx_tok = at<int32_t>(ws, w.ctx_tok);
     a.prompt = at<int32_t>(ws, w.dprompt);
     a.x = XV(0);
+    a.nseq = (int)ns;
+    a.cap = (int)D.win;
     a.st = st;
     a.published = at<uint64_t>(ws, w.published);
     a.slot_bytes = slot_bytes;
@@ -1036,10 +1048,17 @@ void build_decode(ofa_handle* h) {
     a.w_dt = lp;
   }
   auto gemv = [&](const char* nm, int dep, const void* W, const void* bias, const float* xin, const void* lg, const void* lb, float* y,
-                  int N, int K, int epi, int rpt) {
+                  int N, int K, int epi, int rpt, int64_t xin_ss, int64_t y_ss) {
     (void)rpt;
     int p = b.add(OP_DEC_GEMV, 1, nm, {dep});
     DecGemvArgs& a = b[p].a.dgemv;
+    a.nseq = (int)ns;
+    a.xin_ss = xin_ss;
+    a.y_ss = y_ss;
+    a.resid_ss = d;
+    a.kv_ss = kv_ss;
+    a.attn_ss = attn_ss;
+    a.part_ss = V;
     a.W = W;
     a.bias = bias;
     a.xin = xin;
@@ -1069,16 +1088,19 @@ void build_decode(ofa_handle* h) {
     const LayerOff& lo = h->lay.layer[l];
     void* kv = ws + w.kv + (size_t)l * 2 * D.H * D.win * D.dh * D.lp;
     int p_qkv = gemv("dec_qkv", last, sw(lo.w_qkv), sw(lo.b_qkv), XV(2 * l), sw(lo.ln1_g), sw(lo.ln1_b), at<float>(ws, w.dq),
-                     (int)(3 * d), (int)d, DEPI_QKV, (int)D.dh);
+                     (int)(3 * d), (int)d, DEPI_QKV, (int)D.dh, d, d);
     b[p_qkv].a.dgemv.kv = kv;
     const int split = std::max(1, std::min(kMaxAttnSplit, h->serve_wgs / (int)D.H));
-    float* apart = at<float>(ws, w.dapart) + (int64_t)l * D.H * kMaxAttnSplit * (D.dh + 2);
-    int p_att = b.add(OP_DEC_ATTN, (int)D.H * split, "dec_attn", {p_qkv});
+    float* apart = at<float>(ws, w.dapart) + (int64_t)l * ns * attn_ss;
+    int p_att = b.add(OP_DEC_ATTN, (int)(ns * D.H * split), "dec_attn", {p_qkv});
     {
       DecAttnArgs& a = b[p_att].a.dattn;
       a.q = at<float>(ws, w.dq);
       a.kv = kv;
       a.part = apart;
+      a.nseq = (int)ns;
+      a.kv_ss = kv_ss;
+      a.part_ss = attn_ss;
       a.H = (int)D.H;
       a.dh = (int)D.dh;
       a.cap = (int)D.win;
@@ -1086,26 +1108,26 @@ void build_decode(ofa_handle* h) {
       a.split = split;
     }
     int p_o = gemv("dec_attn_out", p_att, sw(lo.w_o), sw(lo.b_o), nullptr, nullptr, nullptr, XV(2 * l + 1),
-                   (int)d, (int)d, DEPI_RESID, 16);
+                   (int)d, (int)d, DEPI_RESID, 16, 0, d);
     b[p_o].a.dgemv.attn_part = apart;
     b[p_o].a.dgemv.attn_split = split;
     b[p_o].a.dgemv.resid = XV(2 * l);
-    float* act = at<float>(ws, w.dmlp_v) + l * F;
+    float* act = at<float>(ws, w.dmlp_v) + l * ns * F;
     int p_fc;
     if (c.mlp_gated)
       p_fc = gemv("dec_fc", p_o, sw(lo.w_gate), nullptr, XV(2 * l + 1), sw(lo.ln2_g), sw(lo.ln2_b), act, (int)(2 * F), (int)d,
-                  DEPI_GEGLU, 16);
+                  DEPI_GEGLU, 16, d, F);
     else
       p_fc = gemv("dec_fc", p_o, sw(lo.w_fc), sw(lo.b_fc), XV(2 * l + 1), sw(lo.ln2_g), sw(lo.ln2_b), act, (int)F, (int)d,
-                  DEPI_GELU, 16);
+                  DEPI_GELU, 16, d, F);
     int p_pr = gemv("dec_proj", p_fc, sw(c.mlp_gated ? lo.w_down : lo.w_proj), sw(lo.b_proj), act, nullptr, nullptr,
-                    XV(2 * l + 2), (int)d, (int)F, DEPI_RESID, 16);
+                    XV(2 * l + 2), (int)d, (int)F, DEPI_RESID, 16, F, d);
     b[p_pr].a.dgemv.resid = XV(2 * l + 1);
     last = p_pr;
   }
   const int64_t w_lm = c.tied_head ? h->lay.wte : h->lay.w_lm;
   int p_lm = gemv("dec_lm_head", last, sw(w_lm), nullptr, XV(2 * (int)D.L), sw(h->lay.lnf_g), sw(h->lay.lnf_b),
-                  at<float>(ws, w.dlogits), (int)V, (int)d, DEPI_LOGITS, 16);
+                  at<float>(ws, w.dlogits), (int)V, (int)d, DEPI_LOGITS, 16, d, V);
   b[p_lm].a.dgemv.part_val = at<float>(ws, w.dpart_v);
   b[p_lm].a.dgemv.part_idx = at<int32_t>(ws, w.dpart_i);
   int p_am = b.add(OP_DEC_ARGMAX, 1, "dec_argmax", {p_lm});
@@ -1120,6 +1142,8 @@ void build_decode(ofa_handle* h) {
     a.V = (int)V;
     a.cap = (int)D.win;
     a.keep = (int)D.keep;
+    a.nseq = (int)ns;
+    a.part_ss = V;
   }
   b[p_emb].dep_prev = p_am;
   finish_program(h->dec);
@@ -1741,7 +1765,9 @@ ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_
   DecState* st = at<DecState>(ws, h->cw.dstate);
   if (n_prompt > 0) {
     if (!dev_prompt) return fail(h, OFA_E_ARG, "null prompt");
-    HIP_TRY(h, hipMemcpyAsync(ws + h->cw.ctx_tok, dev_prompt, n_prompt * 4, hipMemcpyDeviceToDevice, h->stream));
+    // sequence q's prompt dev_prompt[q][0..n_prompt) -> its context ctx_tok[q][0..)
+    HIP_TRY(h, hipMemcpy2DAsync(ws + h->cw.ctx_tok, (size_t)D.win * 4, dev_prompt, (size_t)n_prompt * 4,
+                                (size_t)n_prompt * 4, (size_t)D.nseq, hipMemcpyDeviceToDevice, h->stream));
     // ctx_len = n_prompt, n_gen = 0 (DecState: version, w_delta, ctx_len, n_gen)
     HIP_TRY(h, launch_fill_u32((uint32_t*)&st->ctx_len, (uint32_t)n_prompt, 1, h->stream));
     HIP_TRY(h, launch_fill_u32((uint32_t*)&st->n_gen, 0, 1, h->stream));

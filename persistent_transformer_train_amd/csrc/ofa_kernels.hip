@@ -101,9 +101,15 @@ __device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& t
   }
 }
 
-__device__ __noinline__ void run_dec_gemv(const Phase& ph, int t0, int t1, const TaskCtx& tc, char* smem, int npre) {
+// one non-inlined function per form, so the one-sequence form keeps its own
+// register allocation
+__device__ __noinline__ void run_dec_gemv1(const Phase& ph, int t0, int t1, const TaskCtx& tc, char* smem, int npre) {
   const DecGemvArgs a = ph.a.dgemv;
-  task_dec_gemv_range(a, t0, t1, tc, smem, npre);
+  task_dec_gemv_range_t<false>(a, t0, t1, tc, smem, npre);
+}
+__device__ __noinline__ void run_dec_gemvN(const Phase& ph, int t0, int t1, const TaskCtx& tc, char* smem, int npre) {
+  const DecGemvArgs a = ph.a.dgemv;
+  task_dec_gemv_range_t<true>(a, t0, t1, tc, smem, npre);
 }
 
 __device__ __noinline__ int prefetch_dec_gemv(const Phase& ph, int t0, int t1, char* smem, bool allowed) {
@@ -306,7 +312,8 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
     bool gemv = false;
     if constexpr (OCC == 1) {
       if (ph.op == OP_DEC_GEMV) {
-        run_dec_gemv(ph, tile0, tile1, tc, smem, npre);
+        if (ph.a.dgemv.nseq > 1) run_dec_gemvN(ph, tile0, tile1, tc, smem, npre);
+        else run_dec_gemv1(ph, tile0, tile1, tc, smem, npre);
         gemv = true;
       }
     }

@@ -241,15 +241,19 @@ struct DecIO {               // per-call output pointers of a decode call
   int64_t ring_len;
 };
 
+// Decode runs nseq sequences in lock-step (equal prompt lengths, one position
+// per program instance for all of them); per-sequence data sit at fixed
+// strides from sequence 0's.
 struct DecEmbedArgs {
   const void* wte; const void* wpe;   // slot-0 pointers (wpe nullable)
-  int32_t* ctx_tok;
+  int32_t* ctx_tok;                   // [nseq][cap]
   const int32_t* prompt;              // saved prompt a restart reloads (co-resident decode)
   float* x;
   DecState* st;
   const uint64_t* published;          // published version (co-resident: slot = version & 1)
   int64_t slot_bytes;                 // distance between the two slots (0 = one slot)
   int32_t d, V, w_dt;
+  int32_t nseq, cap;                  // sequences; context capacity (ctx_tok / prompt stride)
 };
 
 struct DecGemvArgs {
@@ -276,22 +280,29 @@ struct DecGemvArgs {
   int32_t per_ticket;        // tiles per ticket (the ticket of tile t is t / per_ticket)
   // input = the attention partials [H][attn_split][dh + 2] combined (nullable; xin unused then)
   const float* attn_part; int32_t attn_split;
+  // sequences and the strides between their data: input / output / residual
+  // vectors (floats), KV cache (elements), attention partials (floats), argmax
+  // partials (entries)
+  int32_t nseq;
+  int64_t xin_ss, y_ss, resid_ss, kv_ss, attn_ss, part_ss;
 };
 
 struct DecAttnArgs {
-  const float* q;            // [d]
-  const void* kv;            // this layer's cache [2][H][cap][dh]
-  float* part;               // [H][split][dh + 2]: unnormalised output, running max, sum of weights
-  int32_t H, dh, cap, kv_dt, split;
+  const float* q;            // [nseq][d]
+  const void* kv;            // this layer's cache [2][H][cap][dh] of sequence 0 (stride kv_ss elements)
+  float* part;               // [nseq][H][split][dh + 2]: unnormalised output, running max, sum of weights
+  int32_t H, dh, cap, kv_dt, split, nseq;
+  int64_t kv_ss, part_ss;    // tile t: sequence t / (H split), head (t / split) % H, key range t % split
 };
 
 struct DecArgmaxArgs {
-  const float* part_val; const int32_t* part_idx;   // per-ticket maxima of the LM-head GEMV
+  const float* part_val; const int32_t* part_idx;   // per-ticket maxima of the LM-head GEMV, [nseq][part_ss]
   int32_t n_part;
-  int32_t* ctx_tok;
+  int32_t* ctx_tok;          // [nseq][cap]
   DecState* st;
-  const DecIO* io;
-  int32_t V, cap, keep;
+  const DecIO* io;           // tokens_out[slot][nseq], logits_out[gen][nseq][V]
+  int32_t V, cap, keep, nseq;
+  int64_t part_ss;
 };
 
 union PhaseArgs {

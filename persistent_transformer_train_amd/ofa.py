@@ -39,7 +39,7 @@ class ofa_config(C.Structure):
         ("decode_window", C.c_int32), ("prompt_len", C.c_int32), ("restart_every", C.c_int32),
         ("exec_mode", C.c_int32),
         ("debug_counter_base", C.c_uint64), ("debug_flags", C.c_int32),
-        ("reserved", C.c_int32 * 7),
+        ("decode_batch", C.c_int32), ("reserved", C.c_int32 * 6),
     ]
 
 
@@ -195,7 +195,10 @@ class Handle:
         return v.value
 
     def decode(self, prompt, n_new, tokens_out, logits_out=None, versions_out=None):
-        n_prompt = 0 if prompt is None else prompt.numel()
+        """prompt: int32 cuda [n_prompt], or [decode_batch][n_prompt] for several sequences
+        (None continues); tokens_out [n_new] or [n_new][decode_batch]; logits_out
+        [n_new][decode_batch][vocab]."""
+        n_prompt = 0 if prompt is None else prompt.shape[-1]
         self._check(ofa_decode_token(self.h, 0 if prompt is None else prompt.data_ptr(), n_prompt, n_new,
                                      tokens_out.data_ptr(), 0 if logits_out is None else logits_out.data_ptr(),
                                      0 if versions_out is None else versions_out.data_ptr()))

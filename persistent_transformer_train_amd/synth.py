@@ -127,6 +127,10 @@ class TokenStream:
         """Decode prompt: the first ``length`` tokens of the stream drawn with purpose 3."""
         return self.rows(3, 0, 1, length)[0]
 
+    def prompts(self, n: int, length: int) -> np.ndarray:
+        """n decode prompts of ``length`` tokens ([n][length], purpose 3, step 1)."""
+        return self.rows(3, 1, n, length)
+
 
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
