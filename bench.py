@@ -169,6 +169,27 @@ def bench_decode_batch(init, stream, args, nseq: int = 8) -> dict:
                          "frac": round(bytes_per_position * (n - 1) / dt / PEAK_HBM, 4)}}
 
 
+def bench_doorbell(init, stream, args, n_new: int = 64) -> dict:
+    """Host doorbell to wake-up: a batch-1 decode of the c4 model on the 48 serve CUs
+    in which the host rings for every token; per token, the host clock's ring-to-token
+    time and the device clock's wake-to-token time (their difference: the doorbell's
+    trip to the device plus the progress word's trip back)."""
+    import torch
+    from persistent_transformer_train_amd import configs, ofa
+    dcfg = configs.get("c4")
+    h = ofa.Handle(dcfg, init)
+    prompt = torch.from_numpy(stream.prompt(dcfg["prompt_len"])).cuda()
+    toks = torch.zeros(n_new, dtype=torch.int32, device="cuda")
+    host_us, dev_us = h.decode_doorbell(prompt, n_new, toks)
+    h.close()
+    host_us, dev_us = np.array(host_us[1:]), np.array(dev_us[1:])   # the first token includes the prefill
+    trip = host_us - dev_us
+    return {"metric": "host doorbell to token (batch-1 decode, c4 model, 48 CUs)", "tokens": n_new - 1,
+            "ring_to_token_us": {"median": round(float(np.median(host_us)), 1), "max": round(float(host_us.max()), 1)},
+            "device_wake_to_token_us": {"median": round(float(np.median(dev_us)), 1), "max": round(float(dev_us.max()), 1)},
+            "doorbell_round_trip_us": {"median": round(float(np.median(trip)), 1), "max": round(float(trip.max()), 1)}}
+
+
 def bench_coresident(init, stream, args) -> dict:
     """c5: the training step on 208 CUs and batch-1 decode on 48 CUs in one
     persistent launch; decode restarts from the seeded prompt every 512 tokens
@@ -285,6 +306,8 @@ def main():
     if not args.no_decode and args.decode_tokens > 1:
         out["decode"] = bench_decode(init, stream, args)
         out["decode_batch"] = bench_decode_batch(init, stream, args)
+        if args.exec_mode == "persistent":
+            out["doorbell"] = bench_doorbell(init, stream, args)
     if args.co_steps > 0 and args.exec_mode == "persistent":
         out["coresident"] = bench_coresident(init, stream, args)
 

@@ -199,6 +199,24 @@ ofa_status ofa_decode_token(ofa_handle *h, const int32_t *dev_prompt, int32_t n_
                             int32_t n_new, int32_t *dev_tokens_out, float *dev_logits_out,
                             uint64_t *dev_versions_out);
 
+/* Host doorbell to wake-up ([3090] "Host doorbell to wake-up": per
+ * invocation, over the host-stamped submissions).  A batch-1 decode of n_new
+ * (<= 4096) tokens from dev_prompt (as ofa_decode_token starts a context) in
+ * which every token waits, on the device, until the host rings for it: the
+ * library launches the decode, then for token k writes k + 1 into a coherent
+ * pinned host word, spins until the decode's progress word (also pinned host
+ * memory, written by the device at system scope) reaches k + 1, and moves on.
+ * host_ring_to_token_us[k] (host, may be NULL): ring to token k seen by the host,
+ * host clock; dev_wake_to_token_us[k] (host, may be NULL): the device saw the
+ * ring to token k emitted, device clock.  Their difference is the doorbell's
+ * trip to the device plus the progress word's trip back.  Synchronous.  Needs
+ * the persistent executor and a handle from ofa_create (OFA_E_STATE
+ * otherwise); a token not back within 10 s gives OFA_E_TIMEOUT (the device
+ * side stops waiting after 5 s). */
+ofa_status ofa_decode_doorbell(ofa_handle *h, const int32_t *dev_prompt, int32_t n_prompt, int32_t n_new,
+                               int32_t *dev_tokens_out, double *host_ring_to_token_us,
+                               double *dev_wake_to_token_us);
+
 /* Co-resident mode ([A100] "What ran": training and serving share one
  * persistent kernel on static SM partitions; [Review]).  Needs train_cus > 0,
  * serve_cus > 0 and the persistent executor (else OFA_E_STATE).  One persistent

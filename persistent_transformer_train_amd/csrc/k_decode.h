@@ -32,6 +32,19 @@ __device__ void task_dec_embed(const DecEmbedArgs& a, int tile, const TaskCtx& t
         for (int i = 0; i < n; ++i) a.ctx_tok[q * a.cap + i] = a.prompt[q * a.cap + i];
       st->ctx_len = n;
     }
+    if ((tc.sc->head & 2) && a.io->doorbell) {
+      // doorbell mode: the token starts once the host has rung for it (a bounded wait)
+      const uint64_t g = (uint64_t)(tc.gen_base + tc.sc->gen_idx);
+      const uint64_t start = now_ticks();
+      for (int spins = 0; __hip_atomic_load(a.io->doorbell, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) <= g; ++spins) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((spins & 63) == 63 && now_ticks() - start > 500000000ull) {   // 5 s
+          raise_status(tc.status, -4 /*OFA_E_TIMEOUT*/, tc.phase, tc.step, (int64_t)g);
+          break;
+        }
+      }
+      if (a.io->ticks && (int64_t)g < a.io->n_ticks) a.io->ticks[2 * g] = now_ticks();
+    }
     if (tc.sc->head & 2) {    // first position of a token: acquire the newest weights
       uint64_t ver = ld_acquire(a.published);
       st->w_delta = a.slot_bytes ? (int64_t)(ver & 1) * a.slot_bytes : 0;
@@ -708,7 +721,9 @@ __device__ void task_dec_argmax(const DecArgmaxArgs& a, int tile, const TaskCtx&
       }
     }
     if (a.io->versions_out) a.io->versions_out[slot] = st->version;
-    if (a.io->n_generated) st_release(a.io->n_generated, (uint64_t)(g + 1));
+    if (a.io->ticks && g < a.io->n_ticks) a.io->ticks[2 * g + 1] = now_ticks();
+    // system scope: the count may live in host memory the host polls
+    if (a.io->n_generated) __hip_atomic_store(a.io->n_generated, (uint64_t)(g + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     st->ctx_len = L + 1 > a.cap ? a.keep : L + 1;
     st->n_gen = gi + 1;
   }

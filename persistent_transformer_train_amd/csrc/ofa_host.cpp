@@ -40,6 +40,7 @@ constexpr int kMaxDecSeq = 8;           // sequences one decode call decodes tog
 // ticket tables live in the workspace (the library allocates no device memory)
 constexpr size_t kTableBytes = 3 * (size_t)512 * 320 + 9 * (size_t)8 * 513 * 4 + 4096;
 constexpr int kMaxProbe = 64;          // rows one evaluation call may probe
+constexpr int kMaxBell = 4096;         // tokens of one doorbell decode call
 
 // ---------------------------------------------------------------- parameter layout
 
@@ -177,7 +178,7 @@ struct Carve {
   // offsets (bytes) into the workspace
   size_t p, g, m, v, wc, serve, xres, ln_mean, ln_rstd, h, qkv, o, lse, mlp1, mlp2, logits, dz, loss_rows, ce_stats;
   size_t dxres, dxlp, dln, dmlp, dout, dsum, dqkv, ln_part, cs_fc, cs_qkv, esorted, efirst;
-  size_t sched, status, times, inst_end, steps, published, trace, tables;
+  size_t sched, status, times, inst_end, steps, published, trace, tables, bell_ticks;
   size_t kv, ctx_tok, dstate, dx, dq, dapart, dmlp_v, dlogits, dsteps, dtimes, misc, dsched, dpart_v, dpart_i, dprompt;
   size_t total;
   int n_slots;
@@ -277,6 +278,7 @@ Carve carve(const ofa_config& c, const Layout& lay) {
   w.dpart_v = b.take(D.nseq * D.V * f4);
   w.dpart_i = b.take(D.nseq * D.V * 4);
   w.misc = b.take(kMiscBytes);
+  w.bell_ticks = b.take((size_t)kMaxBell * 16);
   w.tables = b.take(kTableBytes);
   w.trace = (c.debug_flags & OFA_DEBUG_TRACE) ? b.take((size_t)OFA_TRACE_INSTANCES * kMaxPhases * 32) : 0;
   w.total = (b.off + kAlign - 1) / kAlign * kAlign;
@@ -309,7 +311,8 @@ struct ofa_handle {
   Phase* d_dec = nullptr;
   // per-partition ticket tables (see PersistJob::part_tb): the training
   // program split into kMaxParts partitions, and both programs unsplit
-  uint8_t lineage[32] = {};         // SHA-256 of the checkpoint this state last came from or went to
+  uint8_t lineage[32] = {};
+  uint64_t* h_bell = nullptr;      // coherent pinned host words: doorbell at [0], progress at [8]         // SHA-256 of the checkpoint this state last came from or went to
   std::vector<char> phase_names;   // for phase_times
   std::vector<std::string> train_names;
   std::vector<std::string> dec_names;
@@ -1033,6 +1036,7 @@ void build_decode(ofa_handle* h) {
   int p_emb = b.add(OP_DEC_EMBED, 1, "dec_embed");
   {
     DecEmbedArgs& a = b[p_emb].a.dembed;
+    a.io = at<DecIO>(ws, w.misc + kMiscDecIO);
     a.wte = sw(h->lay.wte);
     a.wpe = sw(h->lay.wpe);
     a.ctx_tok = at<int32_t>(ws, w.ctx_tok);
@@ -1469,6 +1473,7 @@ ofa_status init_handle(ofa_handle* h, const float* dev_init_params) {
     HIP_TRY(h, hipEventCreateWithFlags(&h->ev_upload, hipEventDisableTiming));
     HIP_TRY(h, hipEventCreate(&h->ev_t0));
     HIP_TRY(h, hipEventCreate(&h->ev_t1));
+    HIP_TRY(h, hipHostMalloc((void**)&h->h_bell, 128, hipHostMallocCoherent));
   }
   {
     const int occ = std::max(1, persistent_occupancy(1));
@@ -1617,6 +1622,7 @@ ofa_status ofa_destroy(ofa_handle* h) {
   if (h->ev_upload) (void)hipEventDestroy(h->ev_upload);
   if (h->ev_t0) (void)hipEventDestroy(h->ev_t0);
   if (h->ev_t1) (void)hipEventDestroy(h->ev_t1);
+  if (h->h_bell) (void)hipHostFree(h->h_bell);
   delete h;
   return OFA_OK;
 }
@@ -1753,8 +1759,14 @@ ofa_status ofa_train_step(ofa_handle* h, const int32_t* dev_tokens, int32_t n_st
   return OFA_OK;
 }
 
-ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_prompt, int32_t n_new,
-                            int32_t* dev_tokens_out, float* dev_logits_out, uint64_t* dev_versions_out) {
+}  // extern "C"
+
+namespace {
+
+// One decode call (ofa_decode_token; with a doorbell, ofa_decode_doorbell).
+ofa_status decode_call(ofa_handle* h, const int32_t* dev_prompt, int32_t n_prompt, int32_t n_new,
+                       int32_t* dev_tokens_out, float* dev_logits_out, uint64_t* dev_versions_out,
+                       const uint64_t* doorbell, uint64_t* progress, uint64_t* ticks, int64_t n_ticks) {
   if (!h || n_new < 1 || !dev_tokens_out || n_prompt < 0) return fail(h, OFA_E_ARG, "bad arguments");
   ofa_status s = check_sticky(h);
   if (s != OFA_OK) return s;
@@ -1783,7 +1795,7 @@ ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_
   s = upload(h, d_dsteps, h->h_dsteps, sizeof(StepCtx) * n_inst);
   if (s != OFA_OK) return s;
   // outputs of this call
-  DecIO io{dev_tokens_out, dev_versions_out, dev_logits_out, nullptr, (int64_t)n_new};
+  DecIO io{dev_tokens_out, dev_versions_out, dev_logits_out, progress, (int64_t)n_new, doorbell, ticks, n_ticks};
   memcpy(h->h_misc + kMiscDecIO, &io, sizeof io);
   s = upload(h, h->ws + h->cw.misc + kMiscDecIO, h->h_misc + kMiscDecIO, sizeof io);
   if (s != OFA_OK) return s;
@@ -1800,6 +1812,62 @@ ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_
   if (s != OFA_OK) return s;
   { ofa_status rs = record(h, h->ev_t1); if (rs != OFA_OK) return rs; }
   h->timed = h->ev_t0 != nullptr;
+  return OFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ofa_status ofa_decode_token(ofa_handle* h, const int32_t* dev_prompt, int32_t n_prompt, int32_t n_new,
+                            int32_t* dev_tokens_out, float* dev_logits_out, uint64_t* dev_versions_out) {
+  return decode_call(h, dev_prompt, n_prompt, n_new, dev_tokens_out, dev_logits_out, dev_versions_out, nullptr,
+                     nullptr, nullptr, 0);
+}
+
+ofa_status ofa_decode_doorbell(ofa_handle* h, const int32_t* dev_prompt, int32_t n_prompt, int32_t n_new,
+                               int32_t* dev_tokens_out, double* host_ring_to_token_us, double* dev_wake_to_token_us) {
+  if (!h) return OFA_E_ARG;
+  if (!h->h_bell) return fail(h, OFA_E_STATE, "this handle has no doorbell (made by ofa_create_static)");
+  if (h->cfg.exec_mode != OFA_EXEC_PERSISTENT) return fail(h, OFA_E_STATE, "the doorbell needs the persistent executor");
+  if (n_new < 1 || n_new > kMaxBell) return fail(h, OFA_E_ARG, "n_new %d out of [1, %d]", n_new, kMaxBell);
+  ofa_status s = check_sticky(h);
+  if (s != OFA_OK) return s;
+  HIP_TRY(h, hipStreamSynchronize(h->stream));   // the previous call no longer reads the words
+  volatile uint64_t* bell = h->h_bell;
+  volatile uint64_t* prog = h->h_bell + 8;        // its own 64-byte line
+  *bell = 0;
+  *prog = 0;
+  std::atomic_thread_fence(std::memory_order_seq_cst);
+  uint64_t* ticks = at<uint64_t>(h->ws, h->cw.bell_ticks);
+  HIP_TRY(h, launch_fill_u64(ticks, 0, 2 * (int64_t)n_new, h->stream));
+  s = decode_call(h, dev_prompt, n_prompt, n_new, dev_tokens_out, nullptr, nullptr, h->h_bell, h->h_bell + 8, ticks,
+                  n_new);
+  if (s != OFA_OK) return s;
+  // ring for each token and wait until it is out (each wait bounded)
+  using clk = std::chrono::steady_clock;
+  bool timed_out = false;
+  for (int k = 0; k < n_new && !timed_out; ++k) {
+    const auto t0 = clk::now();
+    std::atomic_thread_fence(std::memory_order_seq_cst);
+    *bell = (uint64_t)(k + 1);
+    std::atomic_thread_fence(std::memory_order_seq_cst);
+    while (*prog < (uint64_t)(k + 1)) {
+      if (clk::now() - t0 > std::chrono::seconds(10)) {
+        timed_out = true;
+        break;
+      }
+    }
+    if (host_ring_to_token_us) host_ring_to_token_us[k] = std::chrono::duration<double, std::micro>(clk::now() - t0).count();
+  }
+  if (timed_out) *bell = (uint64_t)n_new;   // release every remaining wait
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  if (timed_out) return fail(h, OFA_E_TIMEOUT, "a doorbell token did not come back within 10 s");
+  if (dev_wake_to_token_us) {
+    std::vector<uint64_t> t(2 * (size_t)n_new);
+    HIP_TRY(h, hipMemcpy(t.data(), ticks, t.size() * 8, hipMemcpyDeviceToHost));
+    for (int k = 0; k < n_new; ++k) dev_wake_to_token_us[k] = (double)(t[2 * k + 1] - t[2 * k]) * 0.01;   // 100 MHz
+  }
   return OFA_OK;
 }
 

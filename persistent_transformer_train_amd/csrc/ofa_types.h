@@ -237,14 +237,20 @@ struct DecIO {               // per-call output pointers of a decode call
   int32_t* tokens_out;       // [ring_len]: token g goes to g % ring_len
   uint64_t* versions_out;    // [ring_len] (nullable)
   float* logits_out;         // [n_new][V] (nullable; step mode only)
-  uint64_t* n_generated;     // tokens emitted so far (nullable)
+  uint64_t* n_generated;     // tokens emitted so far (nullable; may be coherent host memory)
   int64_t ring_len;
+  // doorbell mode (nullable): token g starts once *doorbell > g (a coherent host
+  // word the host writes); ticks[2g] / ticks[2g + 1] = device time it woke / emitted
+  const uint64_t* doorbell;
+  uint64_t* ticks;
+  int64_t n_ticks;
 };
 
 // Decode runs nseq sequences in lock-step (equal prompt lengths, one position
 // per program instance for all of them); per-sequence data sit at fixed
 // strides from sequence 0's.
 struct DecEmbedArgs {
+  const DecIO* io;                    // doorbell mode: the wait before each token
   const void* wte; const void* wpe;   // slot-0 pointers (wpe nullable)
   int32_t* ctx_tok;                   // [nseq][cap]
   const int32_t* prompt;              // saved prompt a restart reloads (co-resident decode)

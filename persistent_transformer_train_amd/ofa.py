@@ -75,6 +75,8 @@ _sig = {
     "ofa_publish_weights": (C.c_int, [_H, C.POINTER(C.c_uint64)]),
     "ofa_decode_token": (C.c_int, [_H, _P, C.c_int32, C.c_int32, _P, _P, _P]),
     "ofa_train_and_serve": (C.c_int, [_H, _P, C.c_int32, _P, _P, C.c_int32, _P, _P, C.c_int32, _P]),
+    "ofa_decode_doorbell": (C.c_int, [_H, _P, C.c_int32, C.c_int32, _P, C.POINTER(C.c_double),
+                                      C.POINTER(C.c_double)]),
     "ofa_get_params": (C.c_int, [_H, _P]),
     "ofa_set_params": (C.c_int, [_H, _P]),
     "ofa_get_grads": (C.c_int, [_H, _P]),
@@ -202,6 +204,16 @@ class Handle:
         self._check(ofa_decode_token(self.h, 0 if prompt is None else prompt.data_ptr(), n_prompt, n_new,
                                      tokens_out.data_ptr(), 0 if logits_out is None else logits_out.data_ptr(),
                                      0 if versions_out is None else versions_out.data_ptr()))
+
+    def decode_doorbell(self, prompt, n_new, tokens_out):
+        """Batch-1 decode where each token waits for a host doorbell (rung inside the call);
+        returns (ring-to-token microseconds on the host clock, wake-to-token microseconds on
+        the device clock), one value per token."""
+        host = (C.c_double * n_new)()
+        dev = (C.c_double * n_new)()
+        self._check(ofa_decode_doorbell(self.h, prompt.data_ptr(), prompt.shape[-1], n_new, tokens_out.data_ptr(),
+                                        host, dev))
+        return list(host), list(dev)
 
     def train_and_serve(self, tokens, losses, prompt, tokens_ring, versions_ring=None, n_generated=None):
         """Co-resident mode: train on tokens [n][B][T+1] on the train CUs while the
