@@ -113,25 +113,77 @@ __device__ __forceinline__ void argmax_combine_block(float& bv, int& bi, float* 
 // of the tile buffer).  The weights stream through an LDS ring of n_buf
 // buffers of kDecTile bytes by direct-to-LDS copies; the persistent executor
 // issues the first ones before the ticket's dependencies are met (weights do
-// not depend on them), so weight streaming overlaps the previous phase.  Every
-// tile takes the same number of copies per wave, so every wait count is a
-// constant.  Rows are dot products of lpr lanes (16-byte chunks i, i + lpr, ...)
-// against the LayerNorm'd input held in registers, each group of lpr lanes
-// taking RPG rows per pass and reducing with DPP row operations.
-// LDS: [ring n_buf x kDecTile][x: K fp32][ys: 2 ys_rows fp32][64 fp32 scratch].
+// not depend on them), so weight streaming overlaps the wait.
+//
+// Roles: waves 1..3 issue every weight copy; wave 0 issues none and reads
+// everything else the ticket needs (the input vector, the LayerNorm
+// parameters, bias and residual rows, the attention partials).  A wave's
+// vector-memory counter completes in issue order, so a load issued behind a
+// wave's copies would wait for all of them: with the copies out of wave 0 the
+// input arrives while the weights are still streaming.  Every copy wave issues
+// the same number of copies per tile, so every wait count is a constant.
+//
+// Rows are dot products of lpr lanes (16-byte chunks i, i + lpr, ...) against
+// the LayerNorm'd input held in registers, each group of lpr lanes taking RPG
+// rows per pass and reducing with DPP row operations.  The argument block and
+// the instance's StepCtx are read through wave-uniform constant-address views
+// (scalar loads: they are fixed for the whole launch and stay off the vector
+// counter).
 
-constexpr int kDecTile = 32768;                    // bytes of one tile buffer
-constexpr int kDecCopies = kDecTile / (1024 * kWaves);   // copies per wave per tile (8)
-constexpr int kDecMaxChunks = 8;                   // 16-byte chunks of a row per lane
+constexpr int kDecCopyWaves = kWaves - 1;                     // waves 1..3 stream the weights
+constexpr int kDecCopies = 8;                                 // copies per copy wave per tile
+constexpr int kDecTile = kDecCopyWaves * kDecCopies * 1024;   // bytes of one tile buffer (24 KB)
+constexpr int kDecMaxChunks = 8;                              // 16-byte chunks of a row per lane
+
+// constant address space on the device (the host pass of the same source,
+// which emits none of this code, sees plain types)
+#if defined(__HIP_DEVICE_COMPILE__)
+#define OFA_CONST_AS __attribute__((address_space(4)))
+#else
+#define OFA_CONST_AS
+#endif
+typedef const OFA_CONST_AS DecGemvArgs DecGemvArgsC;
+typedef const OFA_CONST_AS StepCtx StepCtxC;
+
+// wave-uniform constant-address view of data that no wave writes during the launch
+template <typename C, typename T>
+__device__ __forceinline__ C* const_view(const T* p) {
+  return (C*)(uintptr_t)readfirstlane_u64((uint64_t)(uintptr_t)p);
+}
 
 __host__ __device__ inline int dec_tile_rows_all(const DecGemvArgs& a) {
   return (a.epi == DEPI_GEGLU ? 2 : 1) * a.rows_per_tile;
 }
 
-// LDS: [ring n_buf x kDecTile][xs: nseq K fp32][ys: nseq ys_rows][ys2: nseq ys_rows][64 scratch]
 __host__ __device__ inline int dec_nseq(const DecGemvArgs& a) { return a.nseq > 1 ? a.nseq : 1; }
+// attention partials of one sequence, staged for the output projection
+__host__ __device__ inline int dec_stage_floats(const DecGemvArgs& a) {
+  return a.attn_part ? a.H * a.attn_split * (a.dh + 2) : 0;
+}
+// LDS: [ring n_buf x kDecTile][xs: nseq K][ys: nseq ys_rows][ys2: nseq ys_rows, gated MLP]
+//      [eb: ys_rows bias][er: nseq ys_rows residual][stage][scl: H split range weights]
+//      [lnp: LayerNorm gain, shift]
+//      [64 scratch], all fp32
+struct DecLds {
+  int xs, ys, ys2, eb, er, stage, scl, lnp, red, total;   // float offsets after the ring
+};
+__host__ __device__ inline DecLds dec_lds_layout(const DecGemvArgs& a) {
+  const int ns = dec_nseq(a);
+  DecLds L;
+  L.xs = 0;
+  L.ys = L.xs + ((ns * a.K + 3) & ~3);
+  L.ys2 = L.ys + ns * a.ys_rows;
+  L.eb = L.ys2 + (a.epi == DEPI_GEGLU ? ns * a.ys_rows : 0);
+  L.er = L.eb + (a.bias ? a.ys_rows : 0);
+  L.stage = L.er + (a.epi == DEPI_RESID ? ns * a.ys_rows : 0);
+  L.scl = L.stage + ((dec_stage_floats(a) + 3) & ~3);
+  L.lnp = L.scl + (a.attn_part ? ((a.H * a.attn_split + 3) & ~3) : 0);
+  L.red = L.lnp + (a.ln_g ? 2 * ((a.K + 3) & ~3) : 0);
+  L.total = L.red + 64;
+  return L;
+}
 __host__ __device__ inline size_t dec_gemv_lds_bytes(const DecGemvArgs& a) {
-  return (size_t)a.n_buf * kDecTile + (size_t)(dec_nseq(a) * (a.K + 2 * a.ys_rows) + 64) * sizeof(float);
+  return (size_t)a.n_buf * kDecTile + (size_t)dec_lds_layout(a).total * sizeof(float);
 }
 
 __device__ __forceinline__ int dec_row_bytes(const DecGemvArgs& a) { return a.K * (a.w_dt == DT_BF16 ? 2 : 4); }
@@ -142,14 +194,16 @@ __device__ __forceinline__ int dec_tile_rows(const DecGemvArgs& a, int tile) {
   return min(a.rows_per_tile, total - tile * a.rows_per_tile);
 }
 
-// N copies per wave of [src, src + 4 KB N) into dst; reads past `valid` bytes
-// re-read the last valid chunk (nothing is read out of range)
+// N copies per copy wave of [src, src + 3 KB N) into dst; reads past `valid`
+// bytes re-read the last valid chunk (nothing is read out of range).  Wave 0
+// returns at once.
 template <int N>
 __device__ __forceinline__ void dec_copy_n(const char* src, int valid, char* dst) {
-  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave - 1, lane = threadIdx.x % kWave;
+  if (w < 0) return;
 #pragma unroll
   for (int j = 0; j < N; ++j) {
-    const int blk = j * kWaves + w;
+    const int blk = j * kDecCopyWaves + w;
     dma16_to_lds(src + min(blk * 1024 + lane * 16, valid - 16), dst + blk * 1024);
   }
 }
@@ -168,24 +222,14 @@ __device__ __forceinline__ void dec_tile_issue(const DecGemvArgs& a, const char*
 }
 
 // wait until tile i has landed while `later` (0..3) later tiles stay in flight,
-// then join the workgroup barrier
+// then join the workgroup barrier (wave 0 has no copies: its waits pass)
 __device__ __forceinline__ void dec_wait_tile(int later) {
   if (later >= 3) asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" : : : "memory");
   else if (later == 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" : : : "memory");
   else if (later == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" : : : "memory");
   else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
 }
-static_assert(kDecCopies == 8, "wait counts above assume 8 copies per wave per tile");
-
-// Prefetch before the dependency wait: returns the number of tiles issued.
-__device__ __forceinline__ int dec_gemv_prefetch(const DecGemvArgs& a, int t0, int t1, char* smem, bool allowed) {
-  if (!allowed) return 0;
-  const int64_t wd = a.pre_dep >= 0 ? a.st->w_delta : 0;
-  const char* W = (const char*)a.W + wd;
-  const int n = min(a.n_buf, t1 - t0);
-  for (int i = 0; i < n; ++i) dec_tile_issue(a, W, t0 + i, smem, i);
-  return n;
-}
+static_assert(kDecCopies == 8, "wait counts above assume 8 copies per copy wave per tile");
 
 // sum over groups of lpr lanes (16, 32 or 64) with DPP; the sum lands in the
 // group's last lane
@@ -203,69 +247,345 @@ __device__ __forceinline__ float dpp_group_sum(float v, int lpr) {
   return v;
 }
 
+// Products of bf16 weights with an fp32 input: the input is carried as two
+// bf16 terms, hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in fp32, so
+// hi + lo matches x to about 2^-17 relative), and each 16-byte chunk of a row
+// takes eight bf16 pair dot products with fp32 accumulation (v_dot2 on gfx950)
+// instead of eight conversions and eight fused multiply-adds.
+typedef __bf16 ofa_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t w2, uint32_t x2, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(ofa_bf16x2, w2), __builtin_bit_cast(ofa_bf16x2, x2), c, false);
+}
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);   // round to nearest even
+}
+// 8 fp32 inputs -> 4 packed hi pairs in out[0..3], 4 packed lo pairs in out[4..7]
+__device__ __forceinline__ void dec_split_x(const float4& a, const float4& b, float* out) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = bf16_bits(v[2 * i]), h1 = bf16_bits(v[2 * i + 1]);
+    const uint32_t l0 = bf16_bits(v[2 * i] - __uint_as_float(h0 << 16));
+    const uint32_t l1 = bf16_bits(v[2 * i + 1] - __uint_as_float(h1 << 16));
+    out[i] = __uint_as_float(h0 | (h1 << 16));
+    out[4 + i] = __uint_as_float(l0 | (l1 << 16));
+  }
+}
+
 // Dot products of one LDS tile's rows with the input chunks in xr; row rr of
 // the tile (GEGLU: rows R.. are the up half) lands in ys[rr] or ys2[rr - R].
+// A lane reads all chunks of a row before it uses one; cpl (whole chunks per
+// lane) is wave-uniform, so only a ragged row's last chunk is lane-masked.
 template <int RPG, bool BF16>
-__device__ __forceinline__ void dec_dot_rows(const DecGemvArgs& a, const char* tilep, int rows,
+__device__ __forceinline__ void dec_dot_rows(const char* tilep, int lpr, int rb, int R, int TR, int rows,
                                              const float (&xr)[kDecMaxChunks][8], float* ys, float* ys2) {
-  const int lpr = a.lpr, ng = kThreads / lpr;
+  const int ng = kThreads / lpr;
   const int grp = threadIdx.x / lpr, li = threadIdx.x % lpr;
-  const int R = a.rows_per_tile, TR = dec_tile_rows_all(a);
-  const int rb = dec_row_bytes(a);
   const int nch = rb / 16;
-  const int half = kDecTile / 2;
-  int off[RPG];
+  const int cpl = nch / lpr;
+  const bool ragged = cpl * lpr != nch;
+  const bool tail = li + cpl * lpr < nch;
+  constexpr int half = kDecTile / 2;
 #pragma unroll
   for (int k = 0; k < RPG; ++k) {
     const int rr = grp + k * ng;
-    off[k] = (rr < TR && rr % R < rows) ? (rr / R) * half + (rr % R) * rb : 0;
-  }
-  float acc[RPG];
+    const bool ok = rr < TR && rr % R < rows;
+    const char* rowp = tilep + (ok ? (rr / R) * half + (rr % R) * rb : 0) + li * 16;
+    uint4 u[kDecMaxChunks];
 #pragma unroll
-  for (int k = 0; k < RPG; ++k) acc[k] = 0.f;
+    for (int j = 0; j < kDecMaxChunks; ++j) {
+      u[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (j < cpl) u[j] = *(const uint4*)(rowp + j * lpr * 16);
+    }
+    if (ragged) {
 #pragma unroll
-  for (int j = 0; j < kDecMaxChunks; ++j) {
-    const int c = li + j * lpr;
-    if (j * lpr < nch && c < nch) {
-      if constexpr (BF16) {
-        uint4 u[RPG];
+      for (int j = 0; j < kDecMaxChunks; ++j)
+        if (j == cpl && tail) u[j] = *(const uint4*)(rowp + j * lpr * 16);
+    }
+    float acc = 0.f;
 #pragma unroll
-        for (int k = 0; k < RPG; ++k) u[k] = *(const uint4*)(tilep + off[k] + c * 16);
-#pragma unroll
-        for (int k = 0; k < RPG; ++k)
-          acc[k] += bf2f(u[k].x & 0xffff) * xr[j][0] + bf2f(u[k].x >> 16) * xr[j][1] +
-                    bf2f(u[k].y & 0xffff) * xr[j][2] + bf2f(u[k].y >> 16) * xr[j][3] +
-                    bf2f(u[k].z & 0xffff) * xr[j][4] + bf2f(u[k].z >> 16) * xr[j][5] +
-                    bf2f(u[k].w & 0xffff) * xr[j][6] + bf2f(u[k].w >> 16) * xr[j][7];
-      } else {
-        float4 u[RPG];
-#pragma unroll
-        for (int k = 0; k < RPG; ++k) u[k] = *(const float4*)(tilep + off[k] + c * 16);
-#pragma unroll
-        for (int k = 0; k < RPG; ++k)
-          acc[k] += u[k].x * xr[j][0] + u[k].y * xr[j][1] + u[k].z * xr[j][2] + u[k].w * xr[j][3];
+    for (int j = 0; j < kDecMaxChunks; ++j) {
+      if (j < cpl || (ragged && j == cpl)) {
+        if constexpr (BF16) {
+          float ah = 0.f, al = 0.f;
+          ah = dot2_bf16(u[j].x, __float_as_uint(xr[j][0]), ah);
+          al = dot2_bf16(u[j].x, __float_as_uint(xr[j][4]), al);
+          ah = dot2_bf16(u[j].y, __float_as_uint(xr[j][1]), ah);
+          al = dot2_bf16(u[j].y, __float_as_uint(xr[j][5]), al);
+          ah = dot2_bf16(u[j].z, __float_as_uint(xr[j][2]), ah);
+          al = dot2_bf16(u[j].z, __float_as_uint(xr[j][6]), al);
+          ah = dot2_bf16(u[j].w, __float_as_uint(xr[j][3]), ah);
+          al = dot2_bf16(u[j].w, __float_as_uint(xr[j][7]), al);
+          acc += ah + al;
+        } else {
+          acc += __uint_as_float(u[j].x) * xr[j][0] + __uint_as_float(u[j].y) * xr[j][1] +
+                 __uint_as_float(u[j].z) * xr[j][2] + __uint_as_float(u[j].w) * xr[j][3];
+        }
       }
     }
-  }
-#pragma unroll
-  for (int k = 0; k < RPG; ++k) {
-    const float v = dpp_group_sum(acc[k], lpr);
-    const int rr = grp + k * ng;
-    if (li == lpr - 1 && rr < TR && rr % R < rows) {
+    const float v = dpp_group_sum(acc, lpr);
+    if (li == lpr - 1 && ok) {
       if (rr < R) ys[rr] = v;
       else ys2[rr - R] = v;
     }
   }
 }
 
-__device__ __forceinline__ void dec_tile_dot(const DecGemvArgs& a, const char* tilep, int rows,
+// The same with the chunk count fixed at compile time and no ragged chunk:
+// straight-line loads, then the products (the shape of every large model's rows).
+template <bool BF16, int CPL>
+__device__ __forceinline__ void dec_dot_rows_fixed(const char* tilep, int lpr, int rb, int R, int TR, int rows,
+                                                   const float (&xr)[kDecMaxChunks][8], float* ys, float* ys2) {
+  const int lg = __builtin_ctz(lpr);
+  const int grp = threadIdx.x >> lg, li = threadIdx.x & (lpr - 1);
+  const int hsel = grp >= R ? 1 : 0;   // gated MLP: second half of the tile
+  const int rw = grp - hsel * R;
+  const bool ok = grp < TR && rw < rows;
+  const char* rowp = tilep + (ok ? hsel * (kDecTile / 2) + rw * rb : 0) + li * 16;
+  uint4 u[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) u[j] = *(const uint4*)(rowp + j * lpr * 16);
+  float acc = 0.f;
+  if constexpr (BF16) {
+    // two-term bf16 input (high and low parts, see dec_split_x): bf16 pair dot
+    // products with fp32 accumulation, one chain per part
+    float ah[2] = {0.f, 0.f}, al[2] = {0.f, 0.f};   // four independent chains
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      float& h = ah[j & 1];
+      float& l = al[j & 1];
+      h = dot2_bf16(u[j].x, __float_as_uint(xr[j][0]), h);
+      l = dot2_bf16(u[j].x, __float_as_uint(xr[j][4]), l);
+      h = dot2_bf16(u[j].y, __float_as_uint(xr[j][1]), h);
+      l = dot2_bf16(u[j].y, __float_as_uint(xr[j][5]), l);
+      h = dot2_bf16(u[j].z, __float_as_uint(xr[j][2]), h);
+      l = dot2_bf16(u[j].z, __float_as_uint(xr[j][6]), l);
+      h = dot2_bf16(u[j].w, __float_as_uint(xr[j][3]), h);
+      l = dot2_bf16(u[j].w, __float_as_uint(xr[j][7]), l);
+    }
+    acc = (ah[0] + ah[1]) + (al[0] + al[1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+      acc += __uint_as_float(u[j].x) * xr[j][0] + __uint_as_float(u[j].y) * xr[j][1] +
+             __uint_as_float(u[j].z) * xr[j][2] + __uint_as_float(u[j].w) * xr[j][3];
+  }
+  const float v = dpp_group_sum(acc, lpr);
+  if (li == lpr - 1 && ok) {
+    if (hsel == 0) ys[rw] = v;
+    else ys2[rw] = v;
+  }
+}
+
+// CPL > 0: the fixed-count dot (chunks per lane known at compile time);
+// CPL == 0: the general one
+template <bool BF16, int CPL>
+__device__ __forceinline__ void dec_tile_dot(int rpg, const char* tilep, int lpr, int rb, int R, int TR, int rows,
                                              const float (&xr)[kDecMaxChunks][8], float* ys, float* ys2) {
-  const bool bf = a.w_dt == DT_BF16;
-  switch (a.rpg) {
-    case 1: bf ? dec_dot_rows<1, true>(a, tilep, rows, xr, ys, ys2) : dec_dot_rows<1, false>(a, tilep, rows, xr, ys, ys2); break;
-    case 2: bf ? dec_dot_rows<2, true>(a, tilep, rows, xr, ys, ys2) : dec_dot_rows<2, false>(a, tilep, rows, xr, ys, ys2); break;
-    case 4: bf ? dec_dot_rows<4, true>(a, tilep, rows, xr, ys, ys2) : dec_dot_rows<4, false>(a, tilep, rows, xr, ys, ys2); break;
-    default: bf ? dec_dot_rows<8, true>(a, tilep, rows, xr, ys, ys2) : dec_dot_rows<8, false>(a, tilep, rows, xr, ys, ys2); break;
+  if constexpr (CPL > 0) {
+    dec_dot_rows_fixed<BF16, CPL>(tilep, lpr, rb, R, TR, rows, xr, ys, ys2);
+  } else {
+    switch (rpg) {
+      case 1: dec_dot_rows<1, BF16>(tilep, lpr, rb, R, TR, rows, xr, ys, ys2); break;
+      case 2: dec_dot_rows<2, BF16>(tilep, lpr, rb, R, TR, rows, xr, ys, ys2); break;
+      case 4: dec_dot_rows<4, BF16>(tilep, lpr, rb, R, TR, rows, xr, ys, ys2); break;
+      default: dec_dot_rows<8, BF16>(tilep, lpr, rb, R, TR, rows, xr, ys, ys2); break;
+    }
+  }
+}
+
+// this lane's input chunks of one sequence (xq: K fp32 in LDS), in registers;
+// bf16 weights take the input as split high / low bf16 pairs
+template <bool BF16>
+__device__ __forceinline__ void dec_load_xr(const float* xq, int lpr, int rb, float (&xr)[kDecMaxChunks][8]) {
+  const int li = threadIdx.x % lpr;
+  const int nch = rb / 16;
+#pragma unroll
+  for (int j = 0; j < kDecMaxChunks; ++j) {
+    const int c = li + j * lpr;
+    float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+    if (c < nch) {
+      if (BF16) {
+        lo = *(const float4*)(xq + c * 8);
+        hi = *(const float4*)(xq + c * 8 + 4);
+      } else {
+        lo = *(const float4*)(xq + c * 4);
+      }
+    }
+    if constexpr (BF16) {
+      dec_split_x(lo, hi, xr[j]);
+    } else {
+      xr[j][0] = lo.x; xr[j][1] = lo.y; xr[j][2] = lo.z; xr[j][3] = lo.w;
+      xr[j][4] = hi.x; xr[j][5] = hi.y; xr[j][6] = hi.z; xr[j][7] = hi.w;
+    }
+  }
+}
+
+// The tiles of one ticket: wait for tile i, refill the ring, dot products of
+// every sequence.  Returns nothing; ys / ys2 hold the ticket's row sums.
+template <bool MULTI, bool BF16, int CPL>
+__device__ __forceinline__ void dec_tiles(const DecGemvArgs& a, const char* W, char* ring, int t0, int nt, int issued,
+                                          const float* xs, float* ys, float* ys2) {
+  const int ns = MULTI ? dec_nseq(a) : 1;
+  const int lpr = a.lpr, rb = dec_row_bytes(a), R = a.rows_per_tile, TR = dec_tile_rows_all(a), rpg = a.rpg;
+  float xr[kDecMaxChunks][8];
+  if (ns == 1) dec_load_xr<BF16>(xs, lpr, rb, xr);   // one sequence: loaded once for the whole ticket
+  for (int i = 0; i < nt; ++i) {
+    // tile i landed in every wave, and every wave is done with tile i - 1's buffer
+    dec_wait_tile(issued - i - 1);
+    if (a.n_buf > 1 && i >= 1 && issued < nt) {   // refill the buffer tile i - 1 used
+      dec_tile_issue(a, W, t0 + issued, ring, issued % a.n_buf);
+      ++issued;
+    }
+    const int rows = dec_tile_rows(a, t0 + i);
+    for (int q = 0; q < ns; ++q) {
+      if (ns > 1) dec_load_xr<BF16>(xs + (size_t)q * a.K, lpr, rb, xr);
+      dec_tile_dot<BF16, CPL>(rpg, ring + (size_t)(i % a.n_buf) * kDecTile, lpr, rb, R, TR, rows, xr,
+                              ys + (size_t)q * a.ys_rows + i * R, ys2 + (size_t)q * a.ys_rows + i * R);
+    }
+    if (a.n_buf == 1 && issued < nt) {   // one buffer: refill once every wave has read it
+      __syncthreads();
+      dec_tile_issue(a, W, t0 + issued, ring, 0);
+      ++issued;
+    }
+  }
+}
+
+// Wave 0: n weights (bf16 or fp32) at src[0..n) into dst as fp32, 16 per lane per round.
+template <bool BF16>
+__device__ __forceinline__ void w0_load_w(const void* src, int n, float* dst) {
+  const int lane = threadIdx.x;
+  for (int b = 0; b < n; b += 16 * kWave) {
+    float v[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {   // clamped index: every load is issued, one wait for all
+      const int i = min(b + lane + m * kWave, n - 1);
+      v[m] = BF16 ? bf2f(((const uint16_t*)src)[i]) : ((const float*)src)[i];
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int i = b + lane + m * kWave;
+      if (i < n) dst[i] = v[m];
+    }
+  }
+}
+
+// Wave 0: n fp32 values at src into dst.  16-byte loads (16 per lane, 4096
+// values per round) when src is 16-byte aligned and n a multiple of 4, else
+// 16 single loads per lane per round.
+__device__ __forceinline__ void w0_load_f(const float* src, int n, float* dst) {
+  const int lane = threadIdx.x;
+  if ((((uintptr_t)src | (uintptr_t)dst) & 15) == 0 && (n & 3) == 0) {
+    const int n4 = n / 4;
+    for (int b = 0; b < n4; b += 16 * kWave) {
+      float4 v[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) v[m] = ((const float4*)src)[min(b + lane + m * kWave, n4 - 1)];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const int i = b + lane + m * kWave;
+        if (i < n4) ((float4*)dst)[i] = v[m];
+      }
+    }
+    return;
+  }
+  for (int b = 0; b < n; b += 16 * kWave) {
+    float v[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) v[m] = src[min(b + lane + m * kWave, n - 1)];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int i = b + lane + m * kWave;
+      if (i < n) dst[i] = v[m];
+    }
+  }
+}
+
+// Wave 0: LayerNorm of x[0..K) (K <= 1024) with parameters g, b (fp32, in LDS) into dst.
+// One reduction for the sum and the sum of squares, both shifted by the first
+// element (the shift keeps the variance free of cancellation when the mean is
+// large against the spread).
+__device__ __forceinline__ void w0_layernorm(const float* x, const float* g, const float* b, int K, float* dst) {
+  constexpr int kPer = 16;   // elements per lane (K <= 1024)
+  const int lane = threadIdx.x;
+  float xv[kPer], gv[kPer], bv[kPer];
+  const float x0 = x[0];
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {   // clamped index: every load is issued, one wait for all
+    const int j = min(lane + m * kWave, K - 1);
+    xv[m] = x[j];
+    gv[m] = g[j];
+    bv[m] = b[j];
+  }
+  float s0 = 0.f, qq = 0.f;
+#pragma unroll
+  for (int m = 0; m < kPer; ++m)
+    if (lane + m * kWave < K) {
+      const float dv = xv[m] - x0;
+      s0 += dv;
+      qq += dv * dv;
+    }
+  s0 = wave_sum_dpp(s0);
+  qq = wave_sum_dpp(qq);
+  const float ms = s0 / K;
+  const float mean = x0 + ms;
+  const float rstd = 1.0f / sqrtf(fmaxf(qq / K - ms * ms, 0.f) + 1e-5f);
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+    const int j = lane + m * kWave;
+    if (j < K) dst[j] = (xv[m] - mean) * rstd * gv[m] + bv[m];
+  }
+}
+
+// Wave 0: the ticket's weights other than the matrix (bias rows, LayerNorm
+// gain and shift) into their LDS areas, as fp32.
+template <bool BF16>
+__device__ __forceinline__ void dec_stage_params(const DecGemvArgs& a, int64_t wd, int r0, int nrows, float* fl) {
+  const DecLds L = dec_lds_layout(a);
+  if (a.bias) w0_load_w<BF16>((const char*)a.bias + wd + (size_t)r0 * (BF16 ? 2 : 4), nrows, fl + L.eb);
+  if (a.ln_g) {
+    w0_load_w<BF16>((const char*)a.ln_g + wd, a.K, fl + L.lnp);
+    w0_load_w<BF16>((const char*)a.ln_b + wd, a.K, fl + L.lnp + ((a.K + 3) & ~3));
+  }
+}
+
+// Prefetch before the dependency wait (the weights do not depend on the
+// ticket's inputs): the copy waves issue the first tiles of the ring; wave 0
+// issues nothing (it polls the dependencies).  Returns the number of tiles issued.
+__device__ __forceinline__ int dec_gemv_prefetch(const DecGemvArgs* ap, int t0, int t1, char* smem, bool allowed) {
+  if (!allowed) return 0;
+  const DecGemvArgs a = *const_view<DecGemvArgsC>(ap);
+  // the token's weight slot (written by this launch's embedding phase: a vector load)
+  const int64_t wd = a.pre_dep >= 0 ? a.st->w_delta : 0;
+  const char* W = (const char*)a.W + wd;
+  const int n = min(a.n_buf, t1 - t0);
+  for (int i = 0; i < n; ++i) dec_tile_issue(a, W, t0 + i, smem, i);
+  return n;
+}
+
+// Wave 0: LayerNorm of x (K <= 1024, element lane + 64 m in x[m]) with gain g
+// and shift b held the same way, into dst.  The same arithmetic as w0_layernorm.
+__device__ __forceinline__ void w0_layernorm_regs(const float (&xv)[16], const float (&gv)[16], const float (&bv)[16],
+                                                  int K, float* dst) {
+  const int lane = threadIdx.x;
+  const float x0 = __shfl(xv[0], 0, kWave);
+  float s0 = 0.f, qq = 0.f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m)
+    if (lane + m * kWave < K) {
+      const float dv = xv[m] - x0;
+      s0 += dv;
+      qq += dv * dv;
+    }
+  s0 = wave_sum_dpp(s0);
+  qq = wave_sum_dpp(qq);
+  const float ms = s0 / K;
+  const float mean = x0 + ms;
+  const float rstd = 1.0f / sqrtf(fmaxf(qq / K - ms * ms, 0.f) + 1e-5f);
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int j = lane + m * kWave;
+    if (j < K) dst[j] = (xv[m] - mean) * rstd * gv[m] + bv[m];
   }
 }
 
@@ -274,196 +594,181 @@ __device__ __forceinline__ void dec_tile_dot(const DecGemvArgs& a, const char* t
 // same lane order as for one sequence.
 // MULTI = false: one sequence, known at compile time (the loops over sequences
 // fold away and the input chunks stay in registers for the whole ticket).
-template <bool MULTI>
-__device__ __forceinline__ void task_dec_gemv_range_t(const DecGemvArgs& a, int t0, int t1, const TaskCtx& tc,
-                                                      char* smem, int npre) {
-  if (a.epi == DEPI_LOGITS && !(tc.sc->head & 1)) {   // prefill position: no logits needed
-    if (npre) vm_wait_barrier(0);                      // drain the prefetched copies
+template <bool MULTI, bool BF16>
+__device__ __forceinline__ void dec_gemv_body(const DecGemvArgs& a, int t0, int t1, const StepCtx* scp, char* smem,
+                                              int npre) {
+  StepCtxC* sc = const_view<StepCtxC>(scp);
+  const int head = sc->head;
+  if (a.epi == DEPI_LOGITS && !(head & 1)) {   // prefill position: no logits needed
+    if (npre) vm_wait_barrier(0);               // drain the prefetched copies
     return;
   }
   const int ns = MULTI ? dec_nseq(a) : 1;
+  const DecLds L = dec_lds_layout(a);
   char* ring = smem;
-  float* xs = (float*)(smem + (size_t)a.n_buf * kDecTile);   // [ns][K]
-  float* ys = xs + (size_t)ns * a.K;                          // [ns][ys_rows]
-  float* ys2 = ys + (size_t)ns * a.ys_rows;                   // [ns][ys_rows] (gated: up half)
-  float* red = ys2 + (size_t)ns * a.ys_rows;                  // [64]
-  const DecState* st = a.st;
+  float* fl = (float*)(smem + (size_t)a.n_buf * kDecTile);
+  float* xs = fl + L.xs;     // [ns][K]
+  float* ys = fl + L.ys;     // [ns][ys_rows]
+  float* ys2 = fl + L.ys2;   // [ns][ys_rows] (gated: up half)
+  float* eb = fl + L.eb;     // [ys_rows] bias of the ticket's rows
+  float* er = fl + L.er;     // [ns][ys_rows] residual of the ticket's rows
+  float* stage = fl + L.stage;
+  float* red = fl + L.red;   // [64]
+  const int pos = sc->pos;
+  const int64_t gen_idx = sc->gen_idx;
+  const int wave = threadIdx.x / kWave;
   // with one weight slot the offset is always 0 (no dependent load)
-  const int64_t wd = a.pre_dep >= 0 ? st->w_delta : 0;
+  const int64_t wd = a.pre_dep >= 0 ? a.st->w_delta : 0;
   const char* W = (const char*)a.W + wd;
   const int nt = t1 - t0;
   for (int i = npre; i < min(a.n_buf, nt); ++i) dec_tile_issue(a, W, t0 + i, ring, i);
   int issued = min(a.n_buf, nt);
-  // per-position values the epilogue needs, read now rather than after the tiles
-  const int pos = tc.sc->pos;
-  const int64_t gen_idx = tc.sc->gen_idx;
-  float* const logits_out = a.epi == DEPI_LOGITS ? a.io->logits_out : nullptr;
-  // Everything that does not come from the tiles is read in one batch of
-  // loads: the input (and its first element, the LayerNorm shift), the
-  // LayerNorm parameters, and the bias and residual of this thread's output
-  // rows (sequence 0; further sequences read theirs in the epilogue).
-  const void* bias = a.bias ? (const void*)((const char*)a.bias + wd) : nullptr;
   const int r0 = t0 * a.rows_per_tile;
   const int nrows = min(nt * a.rows_per_tile, (a.epi == DEPI_GEGLU ? a.F : a.N) - r0);
-  constexpr int kPre = 4;   // rows per thread held in registers (the rest read in the epilogue)
-  constexpr int kMaxK = 4;  // input elements per thread (K <= 1024)
-  float pre_b[kPre], pre_r[kPre], gv[kMaxK], bv[kMaxK], xv[kMaxK];
+  const void* bias = a.bias ? (const void*)((const char*)a.bias + wd) : nullptr;
+  // one sequence, shapes within one round per lane: every input of the ticket
+  // is read in a single batch of loads (one memory round trip)
+  const int K4 = (a.K + 3) & ~3;
+  const bool one_batch = !MULTI && nrows <= 16 * kWave && (a.ln_g ? a.K <= 16 * kWave : (a.K & 3) == 0 && a.K <= 64 * kWave) &&
+                         (!a.attn_part || ((dec_stage_floats(a) & 3) == 0 && dec_stage_floats(a) <= 64 * kWave)) &&
+                         ((uintptr_t)(a.attn_part ? (const void*)a.attn_part : (const void*)a.xin) & 15) == 0;
+  if (wave == 0 && one_batch) {
+    const int lane = threadIdx.x;
+    const bool resid = a.epi == DEPI_RESID;
+    float bv[16], rv[16], xv[16], gv[16], hv[16];
+    float4 v4[16];
+    // every load first, none under a condition (indices clamped; an absent
+    // bias or residual reads the weight matrix instead and is not used), so
+    // the batch costs one memory round trip
+    const void* bsrc = bias ? bias : a.W;
+    const float* rsrc = resid ? a.resid : (const float*)a.W;
 #pragma unroll
-  for (int m = 0; m < kPre; ++m) {
-    const int i = threadIdx.x + m * kThreads;
-    pre_b[m] = (bias && i < nrows) ? ldf(bias, r0 + i, a.w_dt) : 0.f;
-    pre_r[m] = (a.epi == DEPI_RESID && i < nrows) ? a.resid[r0 + i] : 0.f;
-  }
-  if (a.ln_g) {
-    const void* g = (const char*)a.ln_g + wd;
-    const void* b = (const char*)a.ln_b + wd;
-#pragma unroll
-    for (int m = 0; m < kMaxK; ++m) {
-      const int j = threadIdx.x + m * kThreads;
-      gv[m] = j < a.K ? ldf(g, j, a.w_dt) : 0.f;
-      bv[m] = j < a.K ? ldf(b, j, a.w_dt) : 0.f;
+    for (int m = 0; m < 16; ++m) {
+      const int i = r0 + min(lane + m * kWave, nrows - 1);
+      bv[m] = BF16 ? bf2f(((const uint16_t*)bsrc)[i]) : ((const float*)bsrc)[i];
+      rv[m] = rsrc[i];
     }
-  }
-  for (int q = 0; q < ns; ++q) {
-    float* xq = xs + (size_t)q * a.K;
-    if (a.attn_part) {
-      // the attention output: per head, the key-range partials rescaled to their
-      // common maximum, summed, and divided by the summed weights
-      const float* apq = a.attn_part + (int64_t)q * a.attn_ss;
-      const int Wd = a.dh + 2;
-      constexpr int kSplitMax = 8;
-      for (int j = threadIdx.x; j < a.K; j += kThreads) {
-        const float* ph = apq + (int64_t)(j / a.dh) * a.attn_split * Wd;
-        float mc[kSplitMax], lc[kSplitMax], oc[kSplitMax];
+    if (a.ln_g) {
+      const void* g = (const char*)a.ln_g + wd;
+      const void* b = (const char*)a.ln_b + wd;
 #pragma unroll
-        for (int c = 0; c < kSplitMax; ++c)   // all loads first: one round trip
-          if (c < a.attn_split) {
-            mc[c] = ph[c * Wd + a.dh];
-            lc[c] = ph[c * Wd + a.dh + 1];
-            oc[c] = ph[c * Wd + j % a.dh];
-          }
+      for (int m = 0; m < 16; ++m) {
+        const int j = min(lane + m * kWave, a.K - 1);
+        xv[m] = a.xin[j];
+        gv[m] = BF16 ? bf2f(((const uint16_t*)g)[j]) : ((const float*)g)[j];
+        hv[m] = BF16 ? bf2f(((const uint16_t*)b)[j]) : ((const float*)b)[j];
+      }
+    } else {
+      const float4* src = (const float4*)(a.attn_part ? a.attn_part : a.xin);
+      const int n4 = (a.attn_part ? dec_stage_floats(a) : a.K) / 4;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) v4[m] = src[min(lane + m * kWave, n4 - 1)];
+    }
+    // then the stores and the LayerNorm
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int i = lane + m * kWave;
+      if (i < nrows) {
+        if (bias) eb[i] = bv[m];
+        if (resid) er[i] = rv[m];
+      }
+    }
+    if (a.ln_g) {
+      w0_layernorm_regs(xv, gv, hv, a.K, xs);
+    } else {
+      float4* dst = (float4*)(a.attn_part ? stage : xs);
+      const int n4 = (a.attn_part ? dec_stage_floats(a) : a.K) / 4;
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+        if (lane + m * kWave < n4) dst[lane + m * kWave] = v4[m];
+    }
+  } else if (wave == 0) {
+    // general shapes: the same in rounds
+    dec_stage_params<BF16>(a, wd, r0, nrows, fl);
+    const float* lg = fl + L.lnp;
+    const float* lb = lg + K4;
+    for (int q = 0; q < ns; ++q) {
+      if (a.attn_part) continue;
+      const float* xin = a.xin + (int64_t)q * a.xin_ss;
+      if (a.ln_g) w0_layernorm(xin, lg, lb, a.K, xs + (size_t)q * a.K);
+      else w0_load_f(xin, a.K, xs + (size_t)q * a.K);
+    }
+    if (a.epi == DEPI_RESID)
+      for (int q = 0; q < ns; ++q) w0_load_f(a.resid + (int64_t)q * a.resid_ss + r0, nrows, er + (size_t)q * a.ys_rows);
+  }
+  if (a.attn_part) {
+    // the attention output: per head, the key-range partials rescaled to their
+    // common maximum, summed, and divided by the summed weights; one sequence's
+    // partials at a time pass through the staging area
+    const int Wd = a.dh + 2;
+    const int S = a.attn_split;
+    constexpr int kSplitMax = 8;
+    float* scl = fl + L.scl;   // [H][S] weights of the key ranges
+    for (int q = 0; q < ns; ++q) {
+      if (wave == 0 && !one_batch) w0_load_f(a.attn_part + (int64_t)q * a.attn_ss, dec_stage_floats(a), stage);
+      __syncthreads();
+      // range c of head h weighs exp(m_c - m) / sum_c' exp(m_c' - m) l_c', m the
+      // largest range maximum; an empty range (m_c = -inf) weighs 0
+      for (int t = threadIdx.x; t < a.H * S; t += kThreads) {
+        const int h = t / S, c = t % S;
+        const float* ph = stage + h * S * Wd;
         float m = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < kSplitMax; ++c)
-          if (c < a.attn_split) m = fmaxf(m, mc[c]);
-        float num = 0.f, den = 0.f;
+        for (int k = 0; k < kSplitMax; ++k)
+          if (k < S) m = fmaxf(m, ph[k * Wd + a.dh]);
+        float den = 0.f;
 #pragma unroll
-        for (int c = 0; c < kSplitMax; ++c)
-          if (c < a.attn_split && mc[c] != -INFINITY) {   // an empty key range adds nothing
-            const float e = expf(mc[c] - m);
-            num += e * oc[c];
-            den += e * lc[c];
+        for (int k = 0; k < kSplitMax; ++k)
+          if (k < S) {
+            const float mk = ph[k * Wd + a.dh];
+            if (mk != -INFINITY) den += expf(mk - m) * ph[k * Wd + a.dh + 1];
           }
-        xq[j] = num / den;
+        const float mc = ph[c * Wd + a.dh];
+        scl[t] = mc != -INFINITY ? expf(mc - m) / den : 0.f;
       }
-    } else if (!a.ln_g) {
-      const float* xin = a.xin + (int64_t)q * a.xin_ss;
-      for (int j = threadIdx.x; j < a.K; j += kThreads) xq[j] = xin[j];   // any K (the MLP down product)
-    } else {
-      // LayerNorm'd input: K = d_model <= 1024, four elements per thread
-      const float* xin = a.xin + (int64_t)q * a.xin_ss;
-      const float x0 = xin[0];
-#pragma unroll
-      for (int m = 0; m < kMaxK; ++m) {
-        const int j = threadIdx.x + m * kThreads;
-        xv[m] = j < a.K ? xin[j] : 0.f;
-      }
-      {
-        // one reduction for the sum and the sum of squares, both shifted by the
-        // first element (the shift keeps the variance free of cancellation when
-        // the mean is large against the spread)
-        float s0 = 0.f, qq = 0.f;
-#pragma unroll
-        for (int m = 0; m < kMaxK; ++m)
-          if (threadIdx.x + m * kThreads < a.K) {
-            const float dv = xv[m] - x0;
-            s0 += dv;
-            qq += dv * dv;
-          }
-        const float2 sq = block_sum2_dpp(s0, qq, red);
-        const float ms = sq.x / a.K;
-        const float mean = x0 + ms;
-        const float rstd = 1.0f / sqrtf(fmaxf(sq.y / a.K - ms * ms, 0.f) + 1e-5f);
-#pragma unroll
-        for (int m = 0; m < kMaxK; ++m) xv[m] = (xv[m] - mean) * rstd * gv[m] + bv[m];
-      }
-#pragma unroll
-      for (int m = 0; m < kMaxK; ++m) {
-        const int j = threadIdx.x + m * kThreads;
-        if (j < a.K) xq[j] = xv[m];
-      }
-    }
-  }
-  __syncthreads();
-  // this lane's input chunks of one sequence, in registers
-  float xr[kDecMaxChunks][8];
-  auto load_xr = [&](int q) {
-    const float* xq = xs + (size_t)q * a.K;
-    const int li = threadIdx.x % a.lpr;
-    const bool bf = a.w_dt == DT_BF16;
-    const int nch = dec_row_bytes(a) / 16;
-#pragma unroll
-    for (int j = 0; j < kDecMaxChunks; ++j) {
-      const int c = li + j * a.lpr;
-      float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
-      if (c < nch) {
-        if (bf) {
-          lo = *(const float4*)(xq + c * 8);
-          hi = *(const float4*)(xq + c * 8 + 4);
-        } else {
-          lo = *(const float4*)(xq + c * 4);
-        }
-      }
-      xr[j][0] = lo.x; xr[j][1] = lo.y; xr[j][2] = lo.z; xr[j][3] = lo.w;
-      xr[j][4] = hi.x; xr[j][5] = hi.y; xr[j][6] = hi.z; xr[j][7] = hi.w;
-    }
-  };
-  if (ns == 1) load_xr(0);   // one sequence: loaded once for the whole ticket
-  for (int i = 0; i < nt; ++i) {
-    // tile i landed in every wave, and every wave is done with tile i - 1's buffer
-    dec_wait_tile(issued - i - 1);
-    if (a.n_buf > 1 && i >= 1 && issued < nt) {   // refill the buffer tile i - 1 used
-      dec_tile_issue(a, W, t0 + issued, ring, issued % a.n_buf);
-      ++issued;
-    }
-    for (int q = 0; q < ns; ++q) {
-      if (ns > 1) load_xr(q);
-      dec_tile_dot(a, ring + (size_t)(i % a.n_buf) * kDecTile, dec_tile_rows(a, t0 + i), xr,
-                   ys + (size_t)q * a.ys_rows + i * a.rows_per_tile, ys2 + (size_t)q * a.ys_rows + i * a.rows_per_tile);
-    }
-    if (a.n_buf == 1 && issued < nt) {   // one buffer: refill once every wave has read it
       __syncthreads();
-      dec_tile_issue(a, W, t0 + issued, ring, 0);
-      ++issued;
+      float* xq = xs + (size_t)q * a.K;
+      for (int j = threadIdx.x; j < a.K; j += kThreads) {
+        const int h = j / a.dh;
+        const float* ph = stage + h * S * Wd + j % a.dh;
+        float v = 0.f;
+#pragma unroll
+        for (int c = 0; c < kSplitMax; ++c)
+          if (c < S) v += scl[h * S + c] * ph[c * Wd];
+        xq[j] = v;
+      }
+      __syncthreads();
+    }
+  } else {
+    __syncthreads();
+  }
+  {
+    // one dispatch per ticket on the row shape
+    const int nch = dec_row_bytes(a) / 16;
+    const int cpl = (BF16 && a.rpg == 1 && nch % a.lpr == 0 && nch / a.lpr <= kDecMaxChunks) ? nch / a.lpr : 0;
+    switch (cpl) {
+#define OFA_TILES(C) case C: dec_tiles<MULTI, BF16, C>(a, W, ring, t0, nt, issued, xs, ys, ys2); break;
+      OFA_TILES(1) OFA_TILES(2) OFA_TILES(3) OFA_TILES(4) OFA_TILES(5) OFA_TILES(6) OFA_TILES(7) OFA_TILES(8)
+#undef OFA_TILES
+      default: dec_tiles<MULTI, BF16, 0>(a, W, ring, t0, nt, issued, xs, ys, ys2); break;
     }
   }
   __syncthreads();
+  float* const logits_out = a.epi == DEPI_LOGITS ? a.io->logits_out : nullptr;
   // epilogue over the ticket's rows, sequence by sequence
   for (int q = 0; q < ns; ++q) {
     const float* ysq = ys + (size_t)q * a.ys_rows;
     const float* ys2q = ys2 + (size_t)q * a.ys_rows;
+    const float* erq = er + (size_t)q * a.ys_rows;
     float* yq = a.y + (int64_t)q * a.y_ss;
-    const float* rq = a.resid ? a.resid + (int64_t)q * a.resid_ss : nullptr;
     void* kvq = a.kv ? (void*)((char*)a.kv + (size_t)q * a.kv_ss * (a.kv_dt == DT_BF16 ? 2 : 4)) : nullptr;
-    for (int i = threadIdx.x, m = 0; i < nrows; i += kThreads, ++m) {
+    for (int i = threadIdx.x; i < nrows; i += kThreads) {
       const int n = r0 + i;
       float v = ysq[i];
-      float rv = 0.f;
-      if (m < kPre) {
-#pragma unroll
-        for (int u = 0; u < kPre; ++u)
-          if (u == m) {
-            v += pre_b[u];
-            rv = pre_r[u];
-          }
-        if (q > 0 && a.epi == DEPI_RESID) rv = rq[n];
-      } else {
-        if (bias) v += ldf(bias, n, a.w_dt);
-        if (a.epi == DEPI_RESID) rv = rq[n];
-      }
+      if (bias) v += eb[i];
       switch (a.epi) {
         case DEPI_STORE: yq[n] = v; break;
-        case DEPI_RESID: yq[n] = rv + v; break;
+        case DEPI_RESID: yq[n] = erq[i] + v; break;
         case DEPI_GELU: yq[n] = gelu_f(v); break;
         case DEPI_GEGLU: yq[n] = gelu_f(v) * ys2q[i]; break;
         case DEPI_LOGITS:
@@ -481,7 +786,7 @@ __device__ __forceinline__ void task_dec_gemv_range_t(const DecGemvArgs& a, int 
             const float c = (float)cos(ang), sn = (float)sin(ang);
             const int io = j < hl ? i + hl : i - hl;
             float other = ysq[io];
-            if (bias) other += ldf(bias, r0 + io, a.w_dt);
+            if (bias) other += eb[io];
             out = j < hl ? v * c - other * sn : other * sn + v * c;
           }
           if (part == 0) {
@@ -514,14 +819,18 @@ __device__ __forceinline__ void task_dec_gemv_range_t(const DecGemvArgs& a, int 
   __syncthreads();
 }
 
-__device__ __forceinline__ void task_dec_gemv_range(const DecGemvArgs& a, int t0, int t1, const TaskCtx& tc, char* smem,
-                                                    int npre) {
-  if (a.nseq > 1) task_dec_gemv_range_t<true>(a, t0, t1, tc, smem, npre);
-  else task_dec_gemv_range_t<false>(a, t0, t1, tc, smem, npre);
+// ap points at the phase's argument block in the phase table (global memory)
+template <bool MULTI>
+__device__ __forceinline__ void task_dec_gemv_range_t(const DecGemvArgs* ap, int t0, int t1, const StepCtx* sc,
+                                                      char* smem, int npre) {
+  const DecGemvArgs a = *const_view<DecGemvArgsC>(ap);
+  if (a.w_dt == DT_BF16) dec_gemv_body<MULTI, true>(a, t0, t1, sc, smem, npre);
+  else dec_gemv_body<MULTI, false>(a, t0, t1, sc, smem, npre);
 }
 
-__device__ void task_dec_gemv(const DecGemvArgs& a, int tile, const TaskCtx& tc, char* smem) {
-  task_dec_gemv_range(a, tile, tile + 1, tc, smem, 0);
+__device__ __forceinline__ void task_dec_gemv(const DecGemvArgs* ap, int tile, const StepCtx* sc, char* smem) {
+  if (const_view<DecGemvArgsC>(ap)->nseq > 1) task_dec_gemv_range_t<true>(ap, tile, tile + 1, sc, smem, 0);
+  else task_dec_gemv_range_t<false>(ap, tile, tile + 1, sc, smem, 0);
 }
 
 // ---------------------------------------------------------------- attention
@@ -540,13 +849,14 @@ __host__ __device__ inline size_t dec_attn_lds_bytes(const DecAttnArgs& a) {
   return (size_t)(a.cap + a.dh + (kThreads / (a.dh / ept)) * a.dh + 16) * sizeof(float);
 }
 
-// elements [e0, e0 + ept) of a cache row, as fp32
-__device__ __forceinline__ void kv_chunk(const void* kv, int64_t e0, int dt, int ept, float* out) {
-  if (dt == DT_BF16) {
+// elements [e0, e0 + ept) of a cache row, as fp32 (ept 8: bf16 cache; 4 or 2: fp32)
+template <int ept>
+__device__ __forceinline__ void kv_chunk(const void* kv, int64_t e0, float* out) {
+  if constexpr (ept == 8) {
     const uint4 u = *(const uint4*)((const uint16_t*)kv + e0);
     out[0] = bf2f(u.x & 0xffff); out[1] = bf2f(u.x >> 16); out[2] = bf2f(u.y & 0xffff); out[3] = bf2f(u.y >> 16);
     out[4] = bf2f(u.z & 0xffff); out[5] = bf2f(u.z >> 16); out[6] = bf2f(u.w & 0xffff); out[7] = bf2f(u.w >> 16);
-  } else if (ept == 4) {
+  } else if constexpr (ept == 4) {
     const float4 u = *(const float4*)((const float*)kv + e0);
     out[0] = u.x; out[1] = u.y; out[2] = u.z; out[3] = u.w;
   } else {
@@ -555,13 +865,16 @@ __device__ __forceinline__ void kv_chunk(const void* kv, int64_t e0, int dt, int
   }
 }
 
+typedef const OFA_CONST_AS DecAttnArgs DecAttnArgsC;
+
 template <int ept>
-__device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc, char* smem) {
+__device__ void dec_attn_tile(const DecAttnArgs* ap, int tile, const StepCtx* scp, char* smem) {
+  const DecAttnArgs a = *const_view<DecAttnArgsC>(ap);
   constexpr int kKMax = 64 / ept;   // chunks of a key row (head size <= 64)
   constexpr int kVPre = 4;          // value rows per thread read ahead
   const int sq = tile / (a.H * a.split);
   const int h = (tile / a.split) % a.H, c = tile % a.split;
-  const int pos = tc.sc->pos;
+  const int pos = const_view<StepCtxC>(scp)->pos;
   const float* qv_base = a.q + (int64_t)sq * a.H * a.dh;
   const void* kvq = (const char*)a.kv + (size_t)sq * a.kv_ss * (a.kv_dt == DT_BF16 ? 2 : 4);
   const int n_keys = pos + 1;
@@ -580,17 +893,20 @@ __device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc,
   const int slot = threadIdx.x / lpr, ci = threadIdx.x % lpr;
   // every load that does not depend on another is issued first: the query, this
   // thread's first key row and its first value chunks
-  const float qv = threadIdx.x < a.dh ? qv_base[h * a.dh + threadIdx.x] : 0.f;
+  // indices clamped into the range, so no load sits under a lane condition and
+  // the batch costs one memory round trip (an empty range reads key 0: unused)
+  const float qv = qv_base[h * a.dh + min((int)threadIdx.x, a.dh - 1)];
   const int s_k = s0 + threadIdx.x;
+  const int s_kc = max(min(s_k, s1 - 1), 0);
   float kr[kKMax][ept];
 #pragma unroll
   for (int j = 0; j < kKMax; ++j)
-    if (j < nkc && s_k < s1) kv_chunk(kvq, kbase + (int64_t)s_k * a.dh + j * ept, a.kv_dt, ept, kr[j]);
+    if (j < nkc) kv_chunk<ept>(kvq, kbase + (int64_t)s_kc * a.dh + j * ept, kr[j]);
   float vr[kVPre][ept];
 #pragma unroll
   for (int m = 0; m < kVPre; ++m) {
-    const int s = s0 + slot + m * slots;
-    if (s < s1) kv_chunk(kvq, vbase + (int64_t)s * a.dh + ci * ept, a.kv_dt, ept, vr[m]);
+    const int s = max(min(s0 + slot + m * slots, s1 - 1), 0);
+    kv_chunk<ept>(kvq, vbase + (int64_t)s * a.dh + ci * ept, vr[m]);
   }
   if (threadIdx.x < a.dh) qs[threadIdx.x] = qv * scale;
   __syncthreads();
@@ -619,7 +935,7 @@ __device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc,
     float acc = 0.f;
     for (int j = 0; j < a.dh; j += ept) {
       float k[8];
-      kv_chunk(kvq, kbase + (int64_t)s * a.dh + j, a.kv_dt, ept, k);
+      kv_chunk<ept>(kvq, kbase + (int64_t)s * a.dh + j, k);
 #pragma unroll
       for (int e = 0; e < ept; ++e) acc += qs[j + e] * k[e];
     }
@@ -649,7 +965,7 @@ __device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc,
   }
   for (int s = s0 + slot + kVPre * slots; s < s1; s += slots) {
     float v[8];
-    kv_chunk(kvq, vbase + (int64_t)s * a.dh + ci * ept, a.kv_dt, ept, v);
+    kv_chunk<ept>(kvq, vbase + (int64_t)s * a.dh + ci * ept, v);
     const float p = sc[s - s0];
 #pragma unroll
     for (int e = 0; e < ept; ++e) o[e] += p * v[e];
@@ -669,11 +985,13 @@ __device__ void dec_attn_tile(const DecAttnArgs& a, int tile, const TaskCtx& tc,
   __syncthreads();
 }
 
-__device__ void task_dec_attn(const DecAttnArgs& a, int tile, const TaskCtx& tc, char* smem) {
+// ap points at the phase's argument block in the phase table (global memory)
+__device__ void task_dec_attn(const DecAttnArgs* ap, int tile, const StepCtx* sc, char* smem) {
+  const DecAttnArgs a = *const_view<DecAttnArgsC>(ap);
   switch (dec_attn_ept(a)) {
-    case 8: dec_attn_tile<8>(a, tile, tc, smem); break;
-    case 4: dec_attn_tile<4>(a, tile, tc, smem); break;
-    default: dec_attn_tile<2>(a, tile, tc, smem); break;
+    case 8: dec_attn_tile<8>(ap, tile, sc, smem); break;
+    case 4: dec_attn_tile<4>(ap, tile, sc, smem); break;
+    default: dec_attn_tile<2>(ap, tile, sc, smem); break;
   }
 }
 

@@ -971,7 +971,7 @@ void build_eval(ofa_handle* h) {
 // ring of fixed-size buffers: rows per tile chosen so that each of the G serve
 // workgroups gets one ticket of whole tiles, up to four tiles in flight where
 // the LDS allows.  With the rotation on, a ticket covers whole heads.
-constexpr int kDecTileHost = 32768;   // bytes of one tile buffer (the task's kDecTile)
+constexpr int kDecTileHost = 24576;   // bytes of one tile buffer (the task's kDecTile)
 
 bool plan_gemv(Phase& ph, int G) {
   DecGemvArgs& a = ph.a.dgemv;

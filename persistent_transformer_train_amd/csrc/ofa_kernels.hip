@@ -74,8 +74,9 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   else if constexpr (OP == OP_ADAMW) { OFA_ARGS(adam); task_adamw(a, tile, tc); }
   else if constexpr (OP == OP_COPY) { OFA_ARGS(copy); task_copy(a, tile); }
   else if constexpr (OP == OP_DEC_EMBED) { OFA_ARGS(dembed); task_dec_embed(a, tile, tc); }
-  else if constexpr (OP == OP_DEC_GEMV) { OFA_ARGS(dgemv); task_dec_gemv(a, tile, tc, smem); }
-  else if constexpr (OP == OP_DEC_ATTN) { OFA_ARGS(dattn); task_dec_attn(a, tile, tc, smem); }
+  // the decode GEMV and attention read their arguments through a scalar view of the phase table
+  else if constexpr (OP == OP_DEC_GEMV) { task_dec_gemv(&ph.a.dgemv, tile, tc.sc, smem); }
+  else if constexpr (OP == OP_DEC_ATTN) { task_dec_attn(&ph.a.dattn, tile, tc.sc, smem); }
   else if constexpr (OP == OP_DEC_ARGMAX) { OFA_ARGS(dargmax); task_dec_argmax(a, tile, tc, smem); }
   else if constexpr (OP == OP_SLOT_GUARD) { OFA_ARGS(guard); task_slot_guard(a, tc); }
   else if constexpr (OP == OP_PUBLISH) { OFA_ARGS(publish); task_publish(a, tc); }
@@ -103,18 +104,21 @@ __device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& t
 
 // one non-inlined function per form, so the one-sequence form keeps its own
 // register allocation
-__device__ __noinline__ void run_dec_gemv1(const Phase& ph, int t0, int t1, const TaskCtx& tc, char* smem, int npre) {
-  const DecGemvArgs a = ph.a.dgemv;
-  task_dec_gemv_range_t<false>(a, t0, t1, tc, smem, npre);
+// ap and sc are addresses in the phase and step tables (read through scalar views)
+__device__ __noinline__ void run_dec_gemv1(const DecGemvArgs* ap, int t0, int t1, const StepCtx* sc, char* smem,
+                                           int npre) {
+  task_dec_gemv_range_t<false>(ap, t0, t1, sc, smem, npre);
 }
-__device__ __noinline__ void run_dec_gemvN(const Phase& ph, int t0, int t1, const TaskCtx& tc, char* smem, int npre) {
-  const DecGemvArgs a = ph.a.dgemv;
-  task_dec_gemv_range_t<true>(a, t0, t1, tc, smem, npre);
+__device__ __noinline__ void run_dec_gemvN(const DecGemvArgs* ap, int t0, int t1, const StepCtx* sc, char* smem,
+                                           int npre) {
+  task_dec_gemv_range_t<true>(ap, t0, t1, sc, smem, npre);
+}
+__device__ __noinline__ void run_dec_attn(const DecAttnArgs* ap, int tile, const StepCtx* sc, char* smem) {
+  task_dec_attn(ap, tile, sc, smem);
 }
 
-__device__ __noinline__ int prefetch_dec_gemv(const Phase& ph, int t0, int t1, char* smem, bool allowed) {
-  const DecGemvArgs a = ph.a.dgemv;
-  return dec_gemv_prefetch(a, t0, t1, smem, allowed);
+__device__ __noinline__ int prefetch_dec_gemv(const DecGemvArgs* ap, int t0, int t1, char* smem, bool allowed) {
+  return dec_gemv_prefetch(ap, t0, t1, smem, allowed);
 }
 
 // ---------------------------------------------------------------- executor 1: one launch per phase
@@ -128,9 +132,10 @@ __global__ __launch_bounds__(kThreads) void phase_kernel(const Phase* phases, in
   const uint64_t t0 = now_ticks();
   if constexpr (OP == OP_DEC_GEMV) {
     // one workgroup per ticket, as the persistent executor hands them out
-    const DecGemvArgs a = ph.a.dgemv;
-    for (int t = blockIdx.x; t < ph.n_tickets; t += gridDim.x)
-      task_dec_gemv_range(a, t * ph.per_ticket, min((t + 1) * ph.per_ticket, ph.n_tiles), tc, smem, 0);
+    for (int t = blockIdx.x; t < ph.n_tickets; t += gridDim.x) {
+      if (ph.a.dgemv.nseq > 1) task_dec_gemv_range_t<true>(&ph.a.dgemv, t * ph.per_ticket, min((t + 1) * ph.per_ticket, ph.n_tiles), sc, smem, 0);
+      else task_dec_gemv_range_t<false>(&ph.a.dgemv, t * ph.per_ticket, min((t + 1) * ph.per_ticket, ph.n_tiles), sc, smem, 0);
+    }
   } else {
     for (int tile = blockIdx.x; tile < ph.n_tiles; tile += gridDim.x) run_task<OP>(ph, tile, tc, smem);
   }
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
         __syncthreads();
         allow = __builtin_amdgcn_readfirstlane(s_pre) != 0;
       }
-      if constexpr (OCC == 1) npre = prefetch_dec_gemv(ph, tile0, tile1, smem, allow);
+      if constexpr (OCC == 1) npre = prefetch_dec_gemv(&ph.a.dgemv, tile0, tile1, smem, allow);
     }
     // An open-ended job stops at an instance boundary once the other job has
     // finished: the workgroup holding an instance's first ticket checks the
@@ -312,8 +317,8 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
     bool gemv = false;
     if constexpr (OCC == 1) {
       if (ph.op == OP_DEC_GEMV) {
-        if (ph.a.dgemv.nseq > 1) run_dec_gemvN(ph, tile0, tile1, tc, smem, npre);
-        else run_dec_gemv1(ph, tile0, tile1, tc, smem, npre);
+        if (ph.a.dgemv.nseq > 1) run_dec_gemvN(&ph.a.dgemv, tile0, tile1, tc.sc, smem, npre);
+        else run_dec_gemv1(&ph.a.dgemv, tile0, tile1, tc.sc, smem, npre);
         gemv = true;
       }
     }
@@ -324,7 +329,8 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
         const int rot = (int)(((uint64_t)inst * 977u + 31u) % (uint64_t)ph.n_tiles);
         tl = ph.n_tiles - 1 - (tile + rot) % ph.n_tiles;
       }
-      run_any<OCC>(ph, tl, tc, smem);
+      if (OCC == 1 && ph.op == OP_DEC_ATTN) run_dec_attn(&ph.a.dattn, tl, tc.sc, smem);
+      else run_any<OCC>(ph, tl, tc, smem);
     }
     // publish: an agent-scope release fence (per ticket, or once per die and
     // phase) makes the tile's stores visible before the counter moves.  With
