@@ -161,24 +161,28 @@ __host__ __device__ inline int dec_stage_floats(const DecGemvArgs& a) {
   return a.attn_part ? a.H * a.attn_split * (a.dh + 2) : 0;
 }
 // LDS: [ring n_buf x kDecTile][xs: nseq K][ys: nseq ys_rows][ys2: nseq ys_rows, gated MLP]
-//      [eb: ys_rows bias][er: nseq ys_rows residual][stage][scl: H split range weights]
-//      [lnp: LayerNorm gain, shift]
-//      [64 scratch], all fp32
+//      [eb: ys_rows bias][er: nseq ys_rows residual][stage: attention partials]
+//      [scl: H split range weights][lnp: LayerNorm gain, shift][braw: bias as stored]
+//      [xraw: LayerNorm input][64 scratch]
 struct DecLds {
-  int xs, ys, ys2, eb, er, stage, scl, lnp, red, total;   // float offsets after the ring
+  int xs, ys, ys2, eb, er, stage, scl, lnp, braw, xraw, red, total;   // float offsets after the ring
 };
+// areas that wave 0 fills by direct-to-LDS copies are whole 1 KB blocks
+__host__ __device__ inline int dec_pad1k(int nfloats) { return (nfloats + 255) & ~255; }
 __host__ __device__ inline DecLds dec_lds_layout(const DecGemvArgs& a) {
   const int ns = dec_nseq(a);
   DecLds L;
   L.xs = 0;
-  L.ys = L.xs + ((ns * a.K + 3) & ~3);
+  L.ys = L.xs + dec_pad1k(ns * a.K);
   L.ys2 = L.ys + ns * a.ys_rows;
   L.eb = L.ys2 + (a.epi == DEPI_GEGLU ? ns * a.ys_rows : 0);
   L.er = L.eb + (a.bias ? a.ys_rows : 0);
-  L.stage = L.er + (a.epi == DEPI_RESID ? ns * a.ys_rows : 0);
-  L.scl = L.stage + ((dec_stage_floats(a) + 3) & ~3);
+  L.stage = L.er + (a.epi == DEPI_RESID ? dec_pad1k(ns * a.ys_rows) : 0);
+  L.scl = L.stage + (a.attn_part ? dec_pad1k(dec_stage_floats(a)) : 0);
   L.lnp = L.scl + (a.attn_part ? ((a.H * a.attn_split + 3) & ~3) : 0);
-  L.red = L.lnp + (a.ln_g ? 2 * ((a.K + 3) & ~3) : 0);
+  L.braw = L.lnp + (a.ln_g ? 2 * dec_pad1k(a.K) : 0);
+  L.xraw = L.braw + (a.bias ? dec_pad1k(a.ys_rows) : 0);
+  L.red = L.xraw + (a.ln_g ? dec_pad1k(a.K) : 0);
   L.total = L.red + 64;
   return L;
 }
@@ -545,7 +549,7 @@ __device__ __forceinline__ void dec_stage_params(const DecGemvArgs& a, int64_t w
   if (a.bias) w0_load_w<BF16>((const char*)a.bias + wd + (size_t)r0 * (BF16 ? 2 : 4), nrows, fl + L.eb);
   if (a.ln_g) {
     w0_load_w<BF16>((const char*)a.ln_g + wd, a.K, fl + L.lnp);
-    w0_load_w<BF16>((const char*)a.ln_b + wd, a.K, fl + L.lnp + ((a.K + 3) & ~3));
+    w0_load_w<BF16>((const char*)a.ln_b + wd, a.K, fl + L.lnp + dec_pad1k(a.K));
   }
 }
 
@@ -563,12 +567,25 @@ __device__ __forceinline__ int dec_gemv_prefetch(const DecGemvArgs* ap, int t0, 
   return n;
 }
 
-// Wave 0: LayerNorm of x (K <= 1024, element lane + 64 m in x[m]) with gain g
-// and shift b held the same way, into dst.  The same arithmetic as w0_layernorm.
-__device__ __forceinline__ void w0_layernorm_regs(const float (&xv)[16], const float (&gv)[16], const float (&bv)[16],
-                                                  int K, float* dst) {
+// Wave 0: nbytes (a multiple of 16, at least 16) at src (16-byte aligned)
+// into LDS at dst by direct-to-LDS copies, 1 KB per instruction; the last
+// block's lanes past the end re-read the last 16 bytes (nothing is read out of
+// range; dst has room for whole blocks).  Completion: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void w0_dma(const void* src, int nbytes, void* dst) {
   const int lane = threadIdx.x;
-  const float x0 = __shfl(xv[0], 0, kWave);
+  for (int off = 0; off < nbytes; off += 1024)
+    dma16_to_lds((const char*)src + min(off + lane * 16, nbytes - 16), (char*)dst + off);
+}
+
+// Wave 0: LayerNorm of x (K <= 1024 fp32, in LDS) with gain g and shift b as
+// stored (bf16 or fp32, in LDS) into dst; the arithmetic of w0_layernorm.
+template <bool BF16>
+__device__ __forceinline__ void w0_layernorm_lds(const float* x, const float* g, const float* b, int K, float* dst) {
+  const int lane = threadIdx.x;
+  float xv[16];
+  const float x0 = x[0];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) xv[m] = x[min(lane + m * kWave, K - 1)];
   float s0 = 0.f, qq = 0.f;
 #pragma unroll
   for (int m = 0; m < 16; ++m)
@@ -585,7 +602,11 @@ __device__ __forceinline__ void w0_layernorm_regs(const float (&xv)[16], const f
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
     const int j = lane + m * kWave;
-    if (j < K) dst[j] = (xv[m] - mean) * rstd * gv[m] + bv[m];
+    if (j < K) {
+      const float gj = BF16 ? bf2f(((const uint16_t*)g)[j]) : g[j];
+      const float bj = BF16 ? bf2f(((const uint16_t*)b)[j]) : b[j];
+      dst[j] = (xv[m] - mean) * rstd * gj + bj;
+    }
   }
 }
 
@@ -626,67 +647,39 @@ __device__ __forceinline__ void dec_gemv_body(const DecGemvArgs& a, int t0, int 
   const int r0 = t0 * a.rows_per_tile;
   const int nrows = min(nt * a.rows_per_tile, (a.epi == DEPI_GEGLU ? a.F : a.N) - r0);
   const void* bias = a.bias ? (const void*)((const char*)a.bias + wd) : nullptr;
-  // one sequence, shapes within one round per lane: every input of the ticket
-  // is read in a single batch of loads (one memory round trip)
-  const int K4 = (a.K + 3) & ~3;
-  const bool one_batch = !MULTI && nrows <= 16 * kWave && (a.ln_g ? a.K <= 16 * kWave : (a.K & 3) == 0 && a.K <= 64 * kWave) &&
-                         (!a.attn_part || ((dec_stage_floats(a) & 3) == 0 && dec_stage_floats(a) <= 64 * kWave)) &&
-                         ((uintptr_t)(a.attn_part ? (const void*)a.attn_part : (const void*)a.xin) & 15) == 0;
-  if (wave == 0 && one_batch) {
-    const int lane = threadIdx.x;
-    const bool resid = a.epi == DEPI_RESID;
-    float bv[16], rv[16], xv[16], gv[16], hv[16];
-    float4 v4[16];
-    // every load first, none under a condition (indices clamped; an absent
-    // bias or residual reads the weight matrix instead and is not used), so
-    // the batch costs one memory round trip
-    const void* bsrc = bias ? bias : a.W;
-    const float* rsrc = resid ? a.resid : (const float*)a.W;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int i = r0 + min(lane + m * kWave, nrows - 1);
-      bv[m] = BF16 ? bf2f(((const uint16_t*)bsrc)[i]) : ((const float*)bsrc)[i];
-      rv[m] = rsrc[i];
-    }
+  // One sequence with 16-byte aligned pieces: wave 0 copies every input of the
+  // ticket straight into LDS (no registers held, one wait for all of them),
+  // then converts the bias and normalises.
+  const int es = BF16 ? 2 : 4;
+  auto al16 = [](const void* p, int64_t off) { return (((uintptr_t)p + off) & 15) == 0; };
+  const bool dma_in = !MULTI && (a.ln_g ? a.K <= 16 * kWave && (a.K * es) % 16 == 0 && al16(a.ln_g, wd) && al16(a.ln_b, wd)
+                                        : (a.K % 4) == 0) &&
+                      al16(a.attn_part ? (const void*)a.attn_part : (const void*)a.xin, 0) &&
+                      (!a.attn_part || dec_stage_floats(a) % 4 == 0) &&
+                      (!bias || ((nrows * es) % 16 == 0 && al16(bias, (int64_t)r0 * es))) &&
+                      (a.epi != DEPI_RESID || (nrows % 4 == 0 && al16(a.resid, (int64_t)r0 * 4)));
+  if (wave == 0 && dma_in) {
+    if (bias) w0_dma((const char*)bias + (size_t)r0 * es, nrows * es, fl + L.braw);
+    if (a.epi == DEPI_RESID) w0_dma(a.resid + r0, nrows * 4, er);
     if (a.ln_g) {
-      const void* g = (const char*)a.ln_g + wd;
-      const void* b = (const char*)a.ln_b + wd;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const int j = min(lane + m * kWave, a.K - 1);
-        xv[m] = a.xin[j];
-        gv[m] = BF16 ? bf2f(((const uint16_t*)g)[j]) : ((const float*)g)[j];
-        hv[m] = BF16 ? bf2f(((const uint16_t*)b)[j]) : ((const float*)b)[j];
-      }
+      w0_dma((const char*)a.ln_g + wd, a.K * es, fl + L.lnp);
+      w0_dma((const char*)a.ln_b + wd, a.K * es, fl + L.lnp + dec_pad1k(a.K));
+      w0_dma(a.xin, a.K * 4, fl + L.xraw);
+    } else if (a.attn_part) {
+      w0_dma(a.attn_part, dec_stage_floats(a) * 4, stage);
     } else {
-      const float4* src = (const float4*)(a.attn_part ? a.attn_part : a.xin);
-      const int n4 = (a.attn_part ? dec_stage_floats(a) : a.K) / 4;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) v4[m] = src[min(lane + m * kWave, n4 - 1)];
+      w0_dma(a.xin, a.K * 4, xs);
     }
-    // then the stores and the LayerNorm
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int i = lane + m * kWave;
-      if (i < nrows) {
-        if (bias) eb[i] = bv[m];
-        if (resid) er[i] = rv[m];
-      }
-    }
-    if (a.ln_g) {
-      w0_layernorm_regs(xv, gv, hv, a.K, xs);
-    } else {
-      float4* dst = (float4*)(a.attn_part ? stage : xs);
-      const int n4 = (a.attn_part ? dec_stage_floats(a) : a.K) / 4;
-#pragma unroll
-      for (int m = 0; m < 16; ++m)
-        if (lane + m * kWave < n4) dst[lane + m * kWave] = v4[m];
-    }
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // every copy of this wave has landed
+    if (bias)
+      for (int i = threadIdx.x; i < nrows; i += kWave)
+        eb[i] = BF16 ? bf2f(((const uint16_t*)(fl + L.braw))[i]) : fl[L.braw + i];
+    if (a.ln_g) w0_layernorm_lds<BF16>(fl + L.xraw, fl + L.lnp, fl + L.lnp + dec_pad1k(a.K), a.K, xs);
   } else if (wave == 0) {
     // general shapes: the same in rounds
     dec_stage_params<BF16>(a, wd, r0, nrows, fl);
     const float* lg = fl + L.lnp;
-    const float* lb = lg + K4;
+    const float* lb = lg + dec_pad1k(a.K);
     for (int q = 0; q < ns; ++q) {
       if (a.attn_part) continue;
       const float* xin = a.xin + (int64_t)q * a.xin_ss;
@@ -705,7 +698,7 @@ __device__ __forceinline__ void dec_gemv_body(const DecGemvArgs& a, int t0, int 
     constexpr int kSplitMax = 8;
     float* scl = fl + L.scl;   // [H][S] weights of the key ranges
     for (int q = 0; q < ns; ++q) {
-      if (wave == 0 && !one_batch) w0_load_f(a.attn_part + (int64_t)q * a.attn_ss, dec_stage_floats(a), stage);
+      if (wave == 0 && !dma_in) w0_load_f(a.attn_part + (int64_t)q * a.attn_ss, dec_stage_floats(a), stage);
       __syncthreads();
       // range c of head h weighs exp(m_c - m) / sum_c' exp(m_c' - m) l_c', m the
       // largest range maximum; an empty range (m_c = -inf) weighs 0
@@ -868,7 +861,7 @@ __device__ __forceinline__ void kv_chunk(const void* kv, int64_t e0, float* out)
 typedef const OFA_CONST_AS DecAttnArgs DecAttnArgsC;
 
 template <int ept>
-__device__ void dec_attn_tile(const DecAttnArgs* ap, int tile, const StepCtx* scp, char* smem) {
+__device__ __forceinline__ void dec_attn_tile(const DecAttnArgs* ap, int tile, const StepCtx* scp, char* smem) {
   const DecAttnArgs a = *const_view<DecAttnArgsC>(ap);
   constexpr int kKMax = 64 / ept;   // chunks of a key row (head size <= 64)
   constexpr int kVPre = 4;          // value rows per thread read ahead
@@ -986,7 +979,7 @@ __device__ void dec_attn_tile(const DecAttnArgs* ap, int tile, const StepCtx* sc
 }
 
 // ap points at the phase's argument block in the phase table (global memory)
-__device__ void task_dec_attn(const DecAttnArgs* ap, int tile, const StepCtx* sc, char* smem) {
+__device__ __forceinline__ void task_dec_attn(const DecAttnArgs* ap, int tile, const StepCtx* sc, char* smem) {
   const DecAttnArgs a = *const_view<DecAttnArgsC>(ap);
   switch (dec_attn_ept(a)) {
     case 8: dec_attn_tile<8>(ap, tile, sc, smem); break;

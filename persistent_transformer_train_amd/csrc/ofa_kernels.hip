@@ -30,6 +30,13 @@ namespace ofa {
 
 // ---------------------------------------------------------------- dispatch
 
+// decode attention reached through the generic dispatch (launch-per-phase
+// executor, or the training kernel's switch): out of line, so its registers
+// stay out of the callers' allocation
+__device__ __noinline__ void task_dec_attn_call(const DecAttnArgs* ap, int tile, const StepCtx* sc, char* smem) {
+  task_dec_attn(ap, tile, sc, smem);
+}
+
 // Each task receives a by-value copy of its argument block, read once when the
 // task starts: arguments read through the phase-table reference inside the
 // tasks' loops would be reloaded on every iteration (the compiler cannot rule
@@ -76,7 +83,7 @@ __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCt
   else if constexpr (OP == OP_DEC_EMBED) { OFA_ARGS(dembed); task_dec_embed(a, tile, tc); }
   // the decode GEMV and attention read their arguments through a scalar view of the phase table
   else if constexpr (OP == OP_DEC_GEMV) { task_dec_gemv(&ph.a.dgemv, tile, tc.sc, smem); }
-  else if constexpr (OP == OP_DEC_ATTN) { task_dec_attn(&ph.a.dattn, tile, tc.sc, smem); }
+  else if constexpr (OP == OP_DEC_ATTN) { task_dec_attn_call(&ph.a.dattn, tile, tc.sc, smem); }
   else if constexpr (OP == OP_DEC_ARGMAX) { OFA_ARGS(dargmax); task_dec_argmax(a, tile, tc, smem); }
   else if constexpr (OP == OP_SLOT_GUARD) { OFA_ARGS(guard); task_slot_guard(a, tc); }
   else if constexpr (OP == OP_PUBLISH) { OFA_ARGS(publish); task_publish(a, tc); }
@@ -104,16 +111,20 @@ __device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& t
 
 // one non-inlined function per form, so the one-sequence form keeps its own
 // register allocation
-// ap and sc are addresses in the phase and step tables (read through scalar views)
-__device__ __noinline__ void run_dec_gemv1(const DecGemvArgs* ap, int t0, int t1, const StepCtx* sc, char* smem,
-                                           int npre) {
+// ap and sc are addresses in the phase and step tables (read through scalar
+// views).  The one-sequence GEMV and the attention are inlined into the
+// decode kernel: a call would save and restore the callee-saved registers
+// through scratch memory on every ticket, stores that the per-phase L2
+// write-back then carries to HBM.
+__device__ __forceinline__ void run_dec_gemv1(const DecGemvArgs* ap, int t0, int t1, const StepCtx* sc, char* smem,
+                                              int npre) {
   task_dec_gemv_range_t<false>(ap, t0, t1, sc, smem, npre);
 }
 __device__ __noinline__ void run_dec_gemvN(const DecGemvArgs* ap, int t0, int t1, const StepCtx* sc, char* smem,
                                            int npre) {
   task_dec_gemv_range_t<true>(ap, t0, t1, sc, smem, npre);
 }
-__device__ __noinline__ void run_dec_attn(const DecAttnArgs* ap, int tile, const StepCtx* sc, char* smem) {
+__device__ __forceinline__ void run_dec_attn(const DecAttnArgs* ap, int tile, const StepCtx* sc, char* smem) {
   task_dec_attn(ap, tile, sc, smem);
 }
 
@@ -329,8 +340,19 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
         const int rot = (int)(((uint64_t)inst * 977u + 31u) % (uint64_t)ph.n_tiles);
         tl = ph.n_tiles - 1 - (tile + rot) % ph.n_tiles;
       }
-      if (OCC == 1 && ph.op == OP_DEC_ATTN) run_dec_attn(&ph.a.dattn, tl, tc.sc, smem);
-      else run_any<OCC>(ph, tl, tc, smem);
+      if constexpr (OCC == 1) {
+        if (ph.op == OP_DEC_ATTN) {
+          run_dec_attn(&ph.a.dattn, tl, tc.sc, smem);
+        } else {
+          // run_any takes the context by reference, so it lives in scratch
+          // memory for the call; built here, the decode tickets that make no
+          // call (the GEMVs and attention) write none
+          const TaskCtx tcc = tc;
+          run_any<OCC>(ph, tl, tcc, smem);
+        }
+      } else {
+        run_any<OCC>(ph, tl, tc, smem);
+      }
     }
     // publish: an agent-scope release fence (per ticket, or once per die and
     // phase) makes the tile's stores visible before the counter moves.  With
