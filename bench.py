@@ -130,12 +130,28 @@ def bench_decode(init, stream, args) -> dict:
     rate = (n - 1) / dt
     avg_ctx = (dcfg["prompt_len"] + dcfg["decode_window"]) / 2
     bpt = decode_bytes_per_token(dcfg, avg_ctx)
+    ceiling = read_ceiling(dcfg["serve_cus"], bpt)
     return {"metric": "batch-1 greedy decode tokens/s", "value": round(rate, 1), "unit": "tokens/s",
             "tokens": n - 1, "prompt": dcfg["prompt_len"], "window": dcfg["decode_window"],
             "cus": dcfg["serve_cus"] if args.exec_mode == "persistent" else "all (launch per phase)",
             "kernel_ms": round(st.last_call_ms, 3),
             "roofline": {"bound": "hbm", "achieved": round(bpt * rate / 1e9, 1), "peak": PEAK_HBM / 1e9,
-                         "unit": "GB/s", "frac": round(bpt * rate / PEAK_HBM, 4), "bytes_per_token": bpt}}
+                         "unit": "GB/s", "frac": round(bpt * rate / PEAK_HBM, 4), "bytes_per_token": bpt},
+            "read_ceiling": dict(ceiling, frac=round(bpt * rate / 1e9 / ceiling["GBps"], 4))}
+
+
+def read_ceiling(n_wg: int, nbytes: float) -> dict:
+    """The streaming-read ceiling of the decode weight stream on n_wg workgroups
+    (ofa_read_ceiling): a buffer of the token's bytes, copied through LDS as the
+    GEMV tickets copy their weights."""
+    import torch
+    from persistent_transformer_train_amd import ofa
+    buf = torch.zeros(int(nbytes) // 16 * 16, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(n_wg, dtype=torch.int32, device="cuda")
+    gbps, us = ofa.read_ceiling(n_wg, buf, sink, reps=5)
+    del buf
+    return {"workgroups": n_wg, "bytes": int(nbytes), "GBps": round(gbps, 1), "best_us": round(us, 1),
+            "tokens_per_s_at_ceiling": round(gbps * 1e9 / nbytes, 1)}
 
 
 def bench_decode_batch(init, stream, args, nseq: int = 8) -> dict:

@@ -441,6 +441,43 @@ __global__ void fill_pairs_kernel(uint64_t* p, uint64_t a, uint64_t b, int64_t n
   }
 }
 
+// ---------------------------------------------------------------- streaming-read ceiling
+
+// The read ceiling of the decode GEMV's weight stream: workgroup b copies its
+// share of the buffer (`per_wg` bytes, whole 24 KB tiles, from b * per_wg)
+// into a four-tile LDS ring exactly as the GEMV streams a ticket's weights
+// (waves 1..3 issue eight 1 KB direct-to-LDS copies per tile, a tile's buffer
+// refilled once every wave is past it).  Wave 0 folds one word of every tile
+// into `sink` so the copies cannot be dropped.
+__global__ __launch_bounds__(kThreads) void read_ceiling_kernel(const char* buf, int64_t per_wg, uint32_t* sink) {
+  extern __shared__ __align__(16) char ring[];
+  const char* src = buf + (int64_t)blockIdx.x * per_wg;
+  const int nt = (int)(per_wg / kDecTile);
+  const int nb = min(4, nt);
+  uint32_t acc = 0;
+  for (int i = 0; i < nb; ++i) dec_copy_n<kDecCopies>(src + (int64_t)i * kDecTile, kDecTile, ring + i * kDecTile);
+  int issued = nb;
+  for (int i = 0; i < nt; ++i) {
+    dec_wait_tile(issued - i - 1);
+    if (threadIdx.x == 0) acc += *(const uint32_t*)(ring + (i % 4) * kDecTile + (i & 255) * 16);
+    if (i >= 1 && issued < nt) {   // refill the buffer tile i - 1 used (every wave is past it)
+      dec_copy_n<kDecCopies>(src + (int64_t)issued * kDecTile, kDecTile, ring + (issued % 4) * kDecTile);
+      ++issued;
+    }
+  }
+  vm_wait_barrier(0);
+  if (threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
+hipError_t launch_read_ceiling(const void* buf, int64_t per_wg, int n_wg, uint32_t* sink, hipStream_t s) {
+  const int lds = 4 * kDecTile;
+  hipError_t e = hipFuncSetAttribute((const void*)read_ceiling_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(read_ceiling_kernel, dim3(n_wg), dim3(kThreads), lds, s, (const char*)buf, per_wg, sink);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- host side
 
 static size_t lds_for(const Phase& ph) {

@@ -93,6 +93,8 @@ _sig = {
     "ofa_checkpoint_save": (C.c_int, [_H, _P, C.c_char_p, C.c_char_p]),
     "ofa_checkpoint_load": (C.c_int, [_H, _P, C.c_char_p]),
     "ofa_sha256": (C.c_int, [C.c_char_p, C.c_size_t, C.c_char_p]),
+    "ofa_read_ceiling": (C.c_int, [C.c_int32, _P, C.c_int64, _P, C.c_int32, C.POINTER(C.c_double),
+                                   C.POINTER(C.c_double)]),
     "ofa_sched_selftest": (C.c_int, [C.POINTER(ofa_config), C.c_int32, C.c_int32, C.c_int32, C.c_int64, C.c_uint64,
                                      C.c_int32, C.c_uint64, C.c_char_p, C.c_size_t]),
     "ofa_last_error": (C.c_char_p, [_H]),
@@ -312,6 +314,17 @@ class Handle:
             self.close()
         except Exception:
             pass
+
+
+def read_ceiling(n_wg: int, buf, sink, reps: int = 5):
+    """ofa_read_ceiling over a device tensor buf (any dtype, only read) with a
+    device int32 tensor sink of n_wg elements: (GB/s, fastest launch in us)."""
+    g, us = C.c_double(), C.c_double()
+    rc = ofa_read_ceiling(n_wg, C.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                          C.c_void_p(sink.data_ptr()), reps, C.byref(g), C.byref(us))
+    if rc != OFA_OK:
+        raise OfaError(rc, "read_ceiling")
+    return g.value, us.value
 
 
 def sha256(data: bytes) -> bytes:

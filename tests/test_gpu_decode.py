@@ -138,3 +138,21 @@ def test_full_size_decode(name):
         segs = list(decode.windows(prompt, toks, cfg["decode_window"], cfg["prompt_len"]))
         assert len(segs) == 2 and len(segs[1][1]) == n_new - (cfg["decode_window"] - cfg["prompt_len"] + 1)
     h.close()
+
+
+def test_read_ceiling_helper():
+    """ofa_read_ceiling streams whole decode tiles on the given workgroups and
+    rejects arguments it cannot use."""
+    from persistent_transformer_train_amd import ofa
+    buf = torch.zeros(48 * 24576 * 8 + 1000, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(48, dtype=torch.int32, device="cuda")
+    gbps, us = ofa.read_ceiling(48, buf, sink, reps=2)
+    log(f"read ceiling on 48 workgroups over {buf.numel()} bytes: {gbps:.1f} GB/s ({us:.1f} us)")
+    assert gbps > 0 and us > 0
+    small = torch.zeros(1000, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ofa.OfaError) as e:
+        ofa.read_ceiling(48, small, sink, reps=1)
+    assert e.value.code == ofa.OFA_E_ARG
+    with pytest.raises(ofa.OfaError) as e:
+        ofa.read_ceiling(0, buf, sink, reps=1)
+    assert e.value.code == ofa.OFA_E_ARG
