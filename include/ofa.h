@@ -292,13 +292,13 @@ ofa_status ofa_checkpoint_load(ofa_handle *h, const void *dev_ckpt, uint8_t *sha
  * on n_wg workgroups (one per CU; the pages' serving share, "Open Flapping
  * Airplanes ... A100 reproduction", "What ran", is 48 of the GPU's compute
  * units).  Workgroup b copies bytes [b s, (b + 1) s) of dev_buf through LDS
- * exactly as a decode GEMV ticket streams its weights, s the largest whole
- * number of 24 KB tiles with n_wg s <= bytes; one word per workgroup goes to
- * dev_sink (device, n_wg uint32).  Runs on the null stream: one warm-up launch,
- * then reps timed launches; *gbps_out = n_wg s / (fastest launch), and
- * *best_us_out (may be NULL) that launch's duration.  dev_buf is only read.
- * OFA_E_ARG for a null pointer, n_wg or reps <= 0, or less than one tile per
- * workgroup. */
+ * eight times over, exactly as a decode GEMV ticket streams its weights (decode
+ * re-reads the same weights every token), s the largest whole number of 24 KB
+ * tiles with n_wg s <= bytes; one word per workgroup goes to dev_sink (device,
+ * n_wg uint32).  Runs on the null stream: one warm-up launch, then reps timed
+ * launches; *gbps_out = 8 n_wg s / (fastest launch), and *best_us_out (may be
+ * NULL) that launch's duration.  dev_buf is only read.  OFA_E_ARG for a null
+ * pointer, n_wg or reps <= 0, or less than one tile per workgroup. */
 ofa_status ofa_read_ceiling(int32_t n_wg, const void *dev_buf, int64_t bytes, uint32_t *dev_sink, int32_t reps,
                             double *gbps_out, double *best_us_out);
 

@@ -2084,6 +2084,8 @@ ofa_status sha256_device(ofa_handle* h, const void* dev, size_t n, uint8_t out[3
 
 extern "C" {
 
+constexpr int kCeilingPasses = 8;   // passes over the buffer per timed launch
+
 ofa_status ofa_read_ceiling(int32_t n_wg, const void* dev_buf, int64_t bytes, uint32_t* dev_sink, int32_t reps,
                             double* gbps_out, double* best_us_out) {
   if (n_wg <= 0 || !dev_buf || !dev_sink || bytes <= 0 || reps <= 0 || !gbps_out) return OFA_E_ARG;
@@ -2097,7 +2099,7 @@ ofa_status ofa_read_ceiling(int32_t n_wg, const void* dev_buf, int64_t bytes, ui
   ofa_status st = OFA_OK;
   float best = -1.f;
   for (int r = 0; r <= reps && st == OFA_OK; ++r) {   // the first launch warms up
-    if (hipEventRecord(e0, 0) != hipSuccess || launch_read_ceiling(dev_buf, per, n_wg, dev_sink, 0) != hipSuccess ||
+    if (hipEventRecord(e0, 0) != hipSuccess || launch_read_ceiling(dev_buf, per, kCeilingPasses, n_wg, dev_sink, 0) != hipSuccess ||
         hipEventRecord(e1, 0) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {
       st = OFA_E_HIP;
       break;
@@ -2109,7 +2111,7 @@ ofa_status ofa_read_ceiling(int32_t n_wg, const void* dev_buf, int64_t bytes, ui
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   if (st != OFA_OK) return st;
-  *gbps_out = (double)per * n_wg / (best * 1e-3) / 1e9;
+  *gbps_out = (double)per * n_wg * kCeilingPasses / (best * 1e-3) / 1e9;
   if (best_us_out) *best_us_out = best * 1e3;
   return OFA_OK;
 }

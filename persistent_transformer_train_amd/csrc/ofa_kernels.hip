@@ -113,9 +113,11 @@ __device__ __noinline__ void run_any(const Phase& ph, int tile, const TaskCtx& t
 // register allocation
 // ap and sc are addresses in the phase and step tables (read through scalar
 // views).  The one-sequence GEMV and the attention are inlined into the
-// decode kernel: a call would save and restore the callee-saved registers
-// through scratch memory on every ticket, stores that the per-phase L2
-// write-back then carries to HBM.
+// decode kernel: a call saves and restores the callee-saved registers through
+// scratch memory on every ticket, stores that the per-phase L2 write-back
+// then carries to HBM.  The batch GEMV stays a call (about 150 MB of such
+// writes per position at eight sequences): inlined as well, its registers
+// slow the one-sequence path by 7% and the batch path by 3%.
 __device__ __forceinline__ void run_dec_gemv1(const DecGemvArgs* ap, int t0, int t1, const StepCtx* sc, char* smem,
                                               int npre) {
   task_dec_gemv_range_t<false>(ap, t0, t1, sc, smem, npre);
@@ -445,23 +447,27 @@ __global__ void fill_pairs_kernel(uint64_t* p, uint64_t a, uint64_t b, int64_t n
 
 // The read ceiling of the decode GEMV's weight stream: workgroup b copies its
 // share of the buffer (`per_wg` bytes, whole 24 KB tiles, from b * per_wg)
-// into a four-tile LDS ring exactly as the GEMV streams a ticket's weights
-// (waves 1..3 issue eight 1 KB direct-to-LDS copies per tile, a tile's buffer
-// refilled once every wave is past it).  Wave 0 folds one word of every tile
+// `passes` times into a four-tile LDS ring exactly as the GEMV streams a
+// ticket's weights (waves 1..3 issue eight 1 KB direct-to-LDS copies per tile,
+// a tile's buffer refilled once every wave is past it); repeated passes over
+// the same bytes are what decode does token after token, and they make the
+// launch long against its own start-up.  Wave 0 folds one word of every tile
 // into `sink` so the copies cannot be dropped.
-__global__ __launch_bounds__(kThreads) void read_ceiling_kernel(const char* buf, int64_t per_wg, uint32_t* sink) {
+__global__ __launch_bounds__(kThreads) void read_ceiling_kernel(const char* buf, int64_t per_wg, int passes,
+                                                                uint32_t* sink) {
   extern __shared__ __align__(16) char ring[];
   const char* src = buf + (int64_t)blockIdx.x * per_wg;
-  const int nt = (int)(per_wg / kDecTile);
+  const int per = (int)(per_wg / kDecTile);
+  const int nt = per * passes;   // tile t is tile t % per of the share
   const int nb = min(4, nt);
   uint32_t acc = 0;
-  for (int i = 0; i < nb; ++i) dec_copy_n<kDecCopies>(src + (int64_t)i * kDecTile, kDecTile, ring + i * kDecTile);
+  for (int i = 0; i < nb; ++i) dec_copy_n<kDecCopies>(src + (int64_t)(i % per) * kDecTile, kDecTile, ring + i * kDecTile);
   int issued = nb;
   for (int i = 0; i < nt; ++i) {
     dec_wait_tile(issued - i - 1);
     if (threadIdx.x == 0) acc += *(const uint32_t*)(ring + (i % 4) * kDecTile + (i & 255) * 16);
     if (i >= 1 && issued < nt) {   // refill the buffer tile i - 1 used (every wave is past it)
-      dec_copy_n<kDecCopies>(src + (int64_t)issued * kDecTile, kDecTile, ring + (issued % 4) * kDecTile);
+      dec_copy_n<kDecCopies>(src + (int64_t)(issued % per) * kDecTile, kDecTile, ring + (issued % 4) * kDecTile);
       ++issued;
     }
   }
@@ -469,12 +475,12 @@ __global__ __launch_bounds__(kThreads) void read_ceiling_kernel(const char* buf,
   if (threadIdx.x == 0) sink[blockIdx.x] = acc;
 }
 
-hipError_t launch_read_ceiling(const void* buf, int64_t per_wg, int n_wg, uint32_t* sink, hipStream_t s) {
+hipError_t launch_read_ceiling(const void* buf, int64_t per_wg, int passes, int n_wg, uint32_t* sink, hipStream_t s) {
   const int lds = 4 * kDecTile;
   hipError_t e = hipFuncSetAttribute((const void*)read_ceiling_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(read_ceiling_kernel, dim3(n_wg), dim3(kThreads), lds, s, (const char*)buf, per_wg, sink);
+  hipLaunchKernelGGL(read_ceiling_kernel, dim3(n_wg), dim3(kThreads), lds, s, (const char*)buf, per_wg, passes, sink);
   return hipGetLastError();
 }
 

@@ -72,8 +72,8 @@ hipError_t launch_phase(const Phase& host_ph, const Phase* dev_phases, int idx, 
 hipError_t launch_persistent(const PersistParams& p, int grid, hipStream_t s, int occ);
 // out[b] (device, n words) = the die workgroup b of an n-workgroup launch runs on
 hipError_t launch_xcc_probe(uint32_t* out, int n, hipStream_t s);
-// n_wg workgroups each stream per_wg bytes (whole decode tiles) of buf through LDS
-hipError_t launch_read_ceiling(const void* buf, int64_t per_wg, int n_wg, uint32_t* sink, hipStream_t s);
+// n_wg workgroups each stream per_wg bytes (whole decode tiles) of buf through LDS, passes times
+hipError_t launch_read_ceiling(const void* buf, int64_t per_wg, int passes, int n_wg, uint32_t* sink, hipStream_t s);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t v, int64_t n, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
 // p[2i] = a, p[2i+1] = b for i < n_pairs
