@@ -398,8 +398,8 @@ __device__ __forceinline__ void dec_tile_dot(int rpg, const char* tilep, int lpr
   }
 }
 
-// this lane's input chunks of one sequence (xq: K fp32 in LDS), in registers;
-// bf16 weights take the input as split high / low bf16 pairs
+// this lane's input chunks of one sequence (xq: K values in LDS), in registers;
+// for bf16 weights xq holds the split high / low bf16 pairs of dec_split_xs
 template <bool BF16>
 __device__ __forceinline__ void dec_load_xr(const float* xq, int lpr, int rb, float (&xr)[kDecMaxChunks][8]) {
   const int li = threadIdx.x % lpr;
@@ -416,12 +416,22 @@ __device__ __forceinline__ void dec_load_xr(const float* xq, int lpr, int rb, fl
         lo = *(const float4*)(xq + c * 4);
       }
     }
-    if constexpr (BF16) {
-      dec_split_x(lo, hi, xr[j]);
-    } else {
-      xr[j][0] = lo.x; xr[j][1] = lo.y; xr[j][2] = lo.z; xr[j][3] = lo.w;
-      xr[j][4] = hi.x; xr[j][5] = hi.y; xr[j][6] = hi.z; xr[j][7] = hi.w;
-    }
+    // bf16 weights: the chunk already holds its split pairs (dec_split_xs)
+    xr[j][0] = lo.x; xr[j][1] = lo.y; xr[j][2] = lo.z; xr[j][3] = lo.w;
+    xr[j][4] = hi.x; xr[j][5] = hi.y; xr[j][6] = hi.z; xr[j][7] = hi.w;
+  }
+}
+
+// bf16 weights: every 8-element chunk of the inputs xs[0 .. n) (n a multiple of
+// 8) replaced in place by its split form (four hi pairs, then four lo pairs),
+// once per ticket, so the tile loop only reads it
+__device__ __forceinline__ void dec_split_xs(float* xs, int n) {
+  for (int c = threadIdx.x; c < n / 8; c += kThreads) {
+    float4* p = (float4*)(xs + c * 8);
+    float out[8];
+    dec_split_x(p[0], p[1], out);
+    p[0] = make_float4(out[0], out[1], out[2], out[3]);
+    p[1] = make_float4(out[4], out[5], out[6], out[7]);
   }
 }
 
@@ -733,6 +743,10 @@ __device__ __forceinline__ void dec_gemv_body(const DecGemvArgs& a, int t0, int 
       __syncthreads();
     }
   } else {
+    __syncthreads();
+  }
+  if constexpr (BF16) {
+    dec_split_xs(xs, ns * a.K);
     __syncthreads();
   }
   {
