@@ -367,8 +367,12 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
     }
   // copy instructions per wave for one slice, and how many go between the
   // MFMAs of each 16-wide k step (all of them are issued within the slice)
+  // With a ring of two the buffer being refilled is free from the slice's
+  // barrier on, and the copies have only this slice's MFMAs to land in: all of
+  // them go out at its start.  Longer rings spread them over the k steps.
   constexpr int NQA = BM / 32, NQB = kMBN / 32, NC = NQA + NQB, CPK = (NC + 3) / 4;
-  static_assert(CPK <= WMB * 2, "a k step has room for its copies");
+  constexpr bool kIssueFirst = kP3Stages == 2;
+  static_assert(kIssueFirst || CPK <= WMB * 2, "a k step has room for its copies");
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
     // Slice kt landed in every wave (the copies of the up to STAGES-2 slices
@@ -402,6 +406,10 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
                            : p3_frag_t<kMBN>(sb, wn + j * 32, kk, lane);
     };
     frags(0, 0);
+    if (kIssueFirst && copy_ahead) {
+      p3_issue<AKM, BM, NQA>(A, g.lda, m0, g.M, ahead * kP3BK, ring_a + buf * SA, w, lane, 0);
+      p3_issue<BKM, kMBN, NQB>(B, g.ldb, n0, g.N, ahead * kP3BK, ring_b + buf * SB, w, lane, 0);
+    }
 #pragma unroll
     for (int kk = 0; kk < kP3BK / 16; ++kk) {
       const int s0 = kk & 1;
@@ -411,7 +419,7 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
         const int i = m >> 1, j = m & 1;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s0][j], af[s0][i], acc[i][j], 0, 0, 0);
         const int c = kk * CPK + m;
-        if (copy_ahead && m < CPK && c < NC) {
+        if (!kIssueFirst && copy_ahead && m < CPK && c < NC) {
           if (c < NQA) p3_issue<AKM, BM, 1>(A, g.lda, m0, g.M, ahead * kP3BK, ring_a + buf * SA, w, lane, c);
           else p3_issue<BKM, kMBN, 1>(B, g.ldb, n0, g.N, ahead * kP3BK, ring_b + buf * SB, w, lane, c - NQA);
         }

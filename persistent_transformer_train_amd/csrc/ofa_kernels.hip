@@ -190,9 +190,13 @@ __device__ __forceinline__ bool wait_count(const uint64_t* ctr, uint64_t need, c
   if (ld_relaxed(ctr) >= need) return true;
   const uint64_t start = now_ticks();
   for (int spins = 0;; ++spins) {
-    if (ld_relaxed(ctr) >= need) return true;
-    if (ld_relaxed(p.abort)) return false;
-    if (J.open_ended && ld_relaxed(&J.sched->limit) <= (uint64_t)tc.step) return false;
+    // the counter and the stop words are read together: one memory round trip per poll
+    const uint64_t c = ld_relaxed(ctr);
+    const uint64_t ab = ld_relaxed(p.abort);
+    const uint64_t lim = J.open_ended ? ld_relaxed(&J.sched->limit) : ~0ull;
+    if (c >= need) return true;
+    if (ab) return false;
+    if (lim <= (uint64_t)tc.step) return false;
     __builtin_amdgcn_s_sleep(1);
     if ((spins & 63) == 63 && now_ticks() - start > p.watchdog_ticks) {
       raise_status(p.status, -4 /*OFA_E_TIMEOUT*/, tc.phase, tc.step, (int64_t)need);
