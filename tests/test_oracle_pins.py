@@ -426,3 +426,28 @@ def test_prediction_entropy():
     assert gpt.prediction_entropy(z) == pytest.approx(float(-(p * np.log(p)).sum()), rel=1e-13)
     # shift invariance
     assert gpt.prediction_entropy(z + 100.0) == pytest.approx(gpt.prediction_entropy(z), rel=1e-12)
+
+
+def _golden(fname):
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", fname)
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    return np.array([float(r[1]) for r in rows])
+
+
+def test_c3_trajectory_amplifies_a_rounding_level_start_difference():
+    """The oracle's own c3 run in fp32 (100 steps from the seeded init) against
+    the same run started from the init rounded to bf16 (both stored by
+    tests/golden/make_free_running.py, which calls only the oracle): the two
+    agree to 2e-4 over the first 51 steps, then differ by more than 5e-2 within
+    steps 54-62 and come back together after.  A difference of the size bf16
+    rounding makes is amplified there by the training itself, with no GPU
+    involved, so a bf16 run cannot be held to 2e-2 of the fp32 trajectory in
+    that window."""
+    a = _golden("c3_fp32_free_running.txt")
+    b = _golden("c3_fp32_bf16init_free_running.txt")
+    assert len(a) == 100 and len(b) == 66
+    d = np.abs(a[:66] - b)
+    assert d[:51].max() <= 2e-4
+    assert d[54:63].max() > 5e-2
+    assert d[63:].max() <= 5e-3
