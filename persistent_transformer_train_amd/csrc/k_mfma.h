@@ -367,12 +367,12 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
     }
   // copy instructions per wave for one slice, and how many go between the
   // MFMAs of each 16-wide k step (all of them are issued within the slice)
-  // With a ring of two the buffer being refilled is free from the slice's
-  // barrier on, and the copies have only this slice's MFMAs to land in: all of
-  // them go out at its start.  Longer rings spread them over the k steps.
-  constexpr int NQA = BM / 32, NQB = kMBN / 32, NC = NQA + NQB, CPK = (NC + 3) / 4;
-  constexpr bool kIssueFirst = kP3Stages == 2;
-  static_assert(kIssueFirst || CPK <= WMB * 2, "a k step has room for its copies");
+  // The buffer being refilled is free from the slice's barrier on: every copy
+  // of the slice ahead goes out at the start of the slice, so it has the whole
+  // slice's MFMAs to land in (measured against spreading the copies over the k
+  // steps: 9.37 against 10.09 ms per c3 step with a ring of two, 11.06 against
+  // 11.22 with three).
+  constexpr int NQA = BM / 32, NQB = kMBN / 32;
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
     // Slice kt landed in every wave (the copies of the up to STAGES-2 slices
@@ -385,7 +385,7 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
     else p3_wait_barrier<0>();
     const int ahead = kt + kP3Stages - 1;
     const int buf = cur == 0 ? kP3Stages - 1 : cur - 1;
-    // a whole slice ahead is copied between the MFMAs below; a partial one now
+    // a whole slice ahead is copied after the first fragment reads below; a partial one now
     const bool copy_ahead = ahead < nk && (ahead + 1) * kP3BK <= g.K;
     if (ahead < nk && !copy_ahead) {
       p3_fill_tail<AKM, BM>(A, g.lda, m0, g.M, ahead * kP3BK, g.K, ring_a + buf * SA, w, lane);
@@ -406,7 +406,7 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
                            : p3_frag_t<kMBN>(sb, wn + j * 32, kk, lane);
     };
     frags(0, 0);
-    if (kIssueFirst && copy_ahead) {
+    if (copy_ahead) {
       p3_issue<AKM, BM, NQA>(A, g.lda, m0, g.M, ahead * kP3BK, ring_a + buf * SA, w, lane, 0);
       p3_issue<BKM, kMBN, NQB>(B, g.ldb, n0, g.N, ahead * kP3BK, ring_b + buf * SB, w, lane, 0);
     }
@@ -418,11 +418,6 @@ __device__ __forceinline__ void gemm_p3(const GemmArgs& g, int tile, char* smem)
       for (int m = 0; m < WMB * 2; ++m) {
         const int i = m >> 1, j = m & 1;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s0][j], af[s0][i], acc[i][j], 0, 0, 0);
-        const int c = kk * CPK + m;
-        if (!kIssueFirst && copy_ahead && m < CPK && c < NC) {
-          if (c < NQA) p3_issue<AKM, BM, 1>(A, g.lda, m0, g.M, ahead * kP3BK, ring_a + buf * SA, w, lane, c);
-          else p3_issue<BKM, kMBN, 1>(B, g.ldb, n0, g.N, ahead * kP3BK, ring_b + buf * SB, w, lane, c - NQA);
-        }
       }
     }
     cur = cur + 1 == kP3Stages ? 0 : cur + 1;
