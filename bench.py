@@ -79,19 +79,27 @@ def measured_traffic(profile: str):
     return None
 
 
-def cpu_baseline(cfg: dict) -> dict:
-    """The oracle (numpy, untuned) on one full training step of the same workload:
-    the 162M model on all 8 x 512 = 4,096 tokens of a step (forward, hand-derived
-    backward, AdamW), in float32 as the parity runs use it, on the host's cores."""
-    from oracle import gpt, optim
-    from persistent_transformer_train_amd import configs, synth
-    spec = gpt.Spec(n_layer=cfg["n_layer"], d_model=cfg["d_model"], n_head=cfg["n_head"], d_ff=cfg["d_ff"],
+def oracle_spec(cfg: dict):
+    """The oracle's description of the benchmarked model (test infrastructure: used
+    only by the CPU baselines)."""
+    from oracle import gpt
+    from persistent_transformer_train_amd import configs
+    return gpt.Spec(n_layer=cfg["n_layer"], d_model=cfg["d_model"], n_head=cfg["n_head"], d_ff=cfg["d_ff"],
                     vocab=cfg["vocab"], n_pos=cfg["n_pos"], mlp_gated=bool(cfg["mlp_gated"]),
                     tied_head=bool(cfg["tied_head"]), has_bias=bool(cfg["has_bias"]), batch=cfg["batch"],
                     seq=cfg["seq"], lr=cfg["lr"], beta1=cfg["beta1"], beta2=cfg["beta2"], eps=cfg["eps"],
                     weight_decay=cfg["weight_decay"],
                     lr_schedule="cosine" if cfg["lr_schedule"] == configs.LR_COSINE else "constant",
                     total_steps=cfg["total_steps"])
+
+
+def cpu_baseline(cfg: dict) -> dict:
+    """The oracle (numpy, untuned) on one full training step of the same workload:
+    the 162M model on all 8 x 512 = 4,096 tokens of a step (forward, hand-derived
+    backward, AdamW), in float32 as the parity runs use it, on the host's cores."""
+    from oracle import gpt, optim
+    from persistent_transformer_train_amd import synth
+    spec = oracle_spec(cfg)
     lay = gpt.param_layout(spec)
     init = synth.init_params([(int(np.prod(sh)), k) for _, sh, k in lay], 3)
     stream = synth.TokenStream("markov2", 3, cfg["vocab"], cfg["batch"], cfg["seq"])
@@ -105,6 +113,28 @@ def cpu_baseline(cfg: dict) -> dict:
             "sample": f"one float32 training step (forward, backward, AdamW) of the 162M model on the full "
                       f"{cfg['batch']} x {cfg['seq']} = {tokens}-token batch: {dt:.2f} s; numpy BLAS threads = "
                       f"the {cores} cores of the process's affinity"}
+
+
+def cpu_baseline_decode(cfg: dict, init, stream, n_tok: int = 4) -> dict:
+    """The oracle's batch-1 greedy decode of the same model: every token by a full
+    causal forward of its whole context (the oracle keeps no KV cache), float32,
+    on the host's cores; n_tok tokens from a context of the decode run's average
+    length ((prompt + window) / 2 = 272 tokens of the seeded prompt chain)."""
+    from oracle import decode, gpt
+    from persistent_transformer_train_amd import configs
+    spec = oracle_spec(cfg)
+    P = gpt.unflatten(spec, np.asarray(init, np.float32))
+    dcfg = configs.get("c4")
+    n_ctx = (dcfg["prompt_len"] + dcfg["decode_window"]) // 2
+    ctx = stream.prompt(n_ctx)
+    t0 = time.perf_counter()
+    decode.greedy(spec, P, ctx, n_tok, dcfg["decode_window"], dcfg["prompt_len"], dtype=np.float32)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(n_tok / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_tok} greedy tokens from a {n_ctx}-token context (the decode run's average), each by a "
+                      f"full float32 forward of its context (no KV cache): {dt:.2f} s; numpy BLAS threads = the "
+                      f"{cores} cores"}
 
 
 def bench_decode(init, stream, args) -> dict:
@@ -329,6 +359,8 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
+        if "decode" in out:
+            out["decode"]["cpu_baseline"] = cpu_baseline_decode(cfg, init, stream)
     print(json.dumps(out), flush=True)
 
 
