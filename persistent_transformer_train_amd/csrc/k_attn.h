@@ -20,12 +20,30 @@
 
 namespace ofa {
 
-constexpr int kAP = 72;   // LDS pitch (bf16 elements) of a 64-wide block: 144 bytes
+// A 64-wide block row in LDS: 64 bf16 (128 bytes), its eight 16-byte chunks
+// XOR-swizzled: chunk c of row r at c ^ s(r), s permuting the bits of
+// (r >> 1) & 7 so that bit 0 moves to bit 2.  The LDS serves 64 banks of 4
+// bytes a cycle (16 lanes of a 16-byte read, 32 lanes of an 8-byte one):
+// * fragment reads, 16 consecutive rows at one chunk: rows of equal parity get
+//   distinct chunk slots, the parity picks the bank half;
+// * transposing reads, 4 consecutive keys x 4 aligned chunks x 2 halves: keys 2
+//   apart differ in bit 2 of s, so their aligned groups of four chunk slots are
+//   disjoint;
+// * stash writes, two whole rows: any s.
+// (A padded pitch of 72 elements measured 0.2 conflict cycles per access.)
+constexpr int kAP = 64;   // LDS pitch (bf16 elements) of a 64-wide block
+__device__ __forceinline__ int attn_swz(int r) {
+  const int y = (r >> 1) & 7;
+  return ((y & 1) << 2) | ((y >> 1) & 1) | (((y >> 2) & 1) << 1);
+}
+// element offset of chunk c (8 elements) of block row r
+__device__ __forceinline__ int attn_off(int r, int c) { return r * kAP + ((c ^ attn_swz(r)) << 3); }
 
 __device__ __forceinline__ int acc_row(int r, int lane) { return ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3); }
 
+// k: a multiple of 8 (one chunk)
 __device__ __forceinline__ bf16x8_t frag16(const uint16_t* base, int row, int k) {
-  return __builtin_bit_cast(bf16x8_t, *(const uint4*)(base + row * kAP + k));
+  return __builtin_bit_cast(bf16x8_t, *(const uint4*)(base + attn_off(row, k >> 3)));
 }
 
 // An A fragment over k chunk c (16 wide) with the accumulator's k permutation,
@@ -44,7 +62,7 @@ __device__ __forceinline__ bf16x8_t frag_kperm_tr(const uint16_t* blk, int dbase
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int key = kbase + 8 * t + 4 * (G >> 1) + (r >> 2);
-    v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(blk + key * kAP + col));
+    v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(blk + attn_off(key, col >> 3) + (col & 7)));
   }
   typedef short i16x8_t __attribute__((ext_vector_type(8)));
   i16x8_t w = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
@@ -79,8 +97,7 @@ __device__ __forceinline__ void attn_stash(const AttnChunk& c, uint16_t* lds) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int q = threadIdx.x + i * kThreads;
-    const int r = q >> 3, ch = (q & 7) * 8;
-    *(uint4*)(lds + r * kAP + ch) = c.v[i];
+    *(uint4*)(lds + attn_off(q >> 3, q & 7)) = c.v[i];
   }
 }
 
