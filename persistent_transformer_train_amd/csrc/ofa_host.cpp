@@ -777,8 +777,76 @@ void build_train(ofa_handle* h) {
   int p_lnf_b = ln_bwd(2 * (int)L, h->lay.lnf_g, -1, {p_head_dx}, "lnf_bwd");
   // colsum(dx at the last residual point) is the last MLP output bias gradient
   float* last_bias = c.has_bias ? gf(h->lay.layer[L - 1].b_proj) : nullptr;
-  ln_red(2 * (int)L, p_lnf_b, gf(h->lay.lnf_g), gf(h->lay.lnf_b), last_bias, "lnf_params");
+  const int p_lnf_red = ln_red(2 * (int)L, p_lnf_b, gf(h->lay.lnf_g), gf(h->lay.lnf_b), last_bias, "lnf_params");
   int cur_dx = p_lnf_b;   // phase that produced dx at the current residual point
+
+  // AdamW in parameter ranges, each started as soon as its gradients are final
+  // (a layer's weight-gradient products, bias and LayerNorm-parameter sums, and
+  // its input-gradient products, which read its compute copy), so most of the
+  // update runs beside the rest of the backward instead of after it.  A range
+  // is placed one layer later in ticket order than its last producer, so the
+  // workgroups that claim its tickets seldom wait.  The embedding tables and
+  // the first layer stay in a last range after every other phase.  Every range
+  // also waits for the loss (a non-finite loss leaves the weights untouched)
+  // and, co-resident, for the slot guard.
+  const int adam_chunk = 16384;
+  const bool coresident = w.n_slots > 1;
+  int p_guard = -1;
+  std::vector<std::vector<int>> grad_prod(L);   // per layer: the phases that write its gradients
+  std::vector<int> ln1_red(L, -1);
+  auto adam_range = [&](int64_t lo, int64_t hi, std::vector<int> deps, const char* nm) {
+    int p = b.add(OP_ADAMW, (int)cdiv(hi - lo, adam_chunk), nm);
+    AdamArgs& a = b[p].a.adam;
+    a.p = P + lo;
+    a.g = G + lo;
+    a.m = at<float>(ws, w.m) + lo;
+    a.v = at<float>(ws, w.v) + lo;
+    a.wc = c.precision == OFA_BF16 ? (void*)(ws + w.wc + lo * D.lp) : nullptr;
+    a.wc_dt = lp;
+    a.n = hi - lo;
+    a.per_tile = adam_chunk;
+    a.beta1 = c.beta1;
+    a.beta2 = c.beta2;
+    a.eps = c.eps;
+    a.wd = c.weight_decay;
+    if (coresident) {
+      a.pub = ws + w.serve + lo * D.lp;
+      a.pub_slot_bytes = D.P * D.lp;
+    }
+    for (int i = 0; i < kMaxDeps; ++i) b[p].dep[i] = i < (int)deps.size() ? deps[i] : -1;
+    return p;
+  };
+  // an early range: joins (one tile, no work) fold the producers into at most
+  // three dependencies, the guard being the fourth
+  auto adam_early = [&](int64_t lo, int64_t hi, std::vector<int> deps, const char* nm) {
+    deps.push_back(p_loss);
+    while (deps.size() > 3) {
+      int j = b.add(OP_NOP, 1, "grad_join");
+      for (int i = 0; i < kMaxDeps; ++i) b[j].dep[i] = deps[i];
+      deps.erase(deps.begin(), deps.begin() + kMaxDeps);
+      deps.insert(deps.begin(), j);
+    }
+    if (coresident) {
+      if (p_guard < 0) {
+        // before any range overwrites serve slot (tag & 1) the decoder must have left the version it holds
+        p_guard = b.add(OP_SLOT_GUARD, 1, "slot_guard", {-2});
+        b[p_guard].a.guard.st = at<DecState>(ws, w.dstate);
+      }
+      deps.push_back(p_guard);
+    }
+    // four tiles (65,536 parameters) per ticket: a ticket takes a workgroup
+    // off the backward for a while, and ticket order is priority; measured per
+    // c3 step with one, two, three, four, six, eight, sixteen and thirty-two
+    // tiles per ticket: 9.37, 9.29, 9.23, 9.11, 9.14, 9.15, 9.30 and 9.63 ms
+    // (9.30 with the update in one range at the end)
+    const int pr = adam_range(lo, hi, deps, nm);
+    b[pr].per_ticket = 4;
+    return pr;
+  };
+  // ranges start on 16-byte boundaries (vector accesses); otherwise one range for everything
+  auto layer_lo = [&](int l) { return l < (int)L ? h->lay.layer[l].ln1_g : h->lay.lnf_g; };
+  bool split_adam = true;
+  for (int l = 0; l <= (int)L; ++l) split_adam = split_adam && layer_lo(l) % 4 == 0;
   for (int l = (int)L - 1; l >= 0; --l) {
     const LayerOff& lo = h->lay.layer[l];
     const int ri = 2 * l + 2;   // residual point after the MLP
@@ -792,13 +860,14 @@ void build_train(ofa_handle* h) {
       g.aux_off = (int)F;
       int p_ddx = gemm_phase(g, {cur_dx}, "down_dx");
       g = gemm(h, (int)d, (int)F, (int)BT, dxo, d, 0, lp, M2(l), F, 0, lp, gf(lo.w_down), F, DT_F32, EPI_STORE);
-      gemm_phase(g, {cur_dx}, "down_dw");
+      grad_prod[l].push_back(gemm_phase(g, {cur_dx}, "down_dw"));
       g = gemm(h, (int)BT, (int)d, (int)(2 * F), DM(l), 2 * F, 1, lp, wc(lo.w_gate), d, 0, lp, DLN(2 * l + 1), d,
                DT_F32, EPI_STORE);
       p_mdx = gemm_phase(g, {p_ddx}, "gate_up_dx");
       g = gemm(h, (int)(2 * F), (int)d, (int)BT, DM(l), 2 * F, 0, lp, Hh(2 * l + 1), d, 0, lp, gf(lo.w_gate), d,
                DT_F32, EPI_STORE);
       p_mdw2 = gemm_phase(g, {p_ddx}, "gate_up_dw");
+      grad_prod[l].push_back(p_mdw2);
     } else {
       g = gemm(h, (int)BT, (int)F, (int)d, dxo, d, 1, lp, wc(lo.w_proj), F, 0, lp, DM(l), F, lp, EPI_DGELU);
       g.aux = M1(l);
@@ -806,18 +875,20 @@ void build_train(ofa_handle* h) {
       g.aux_dt = lp;
       int p_pdx = gemm_phase(g, {cur_dx}, "proj_dx");
       g = gemm(h, (int)d, (int)F, (int)BT, dxo, d, 0, lp, M2(l), F, 0, lp, gf(lo.w_proj), F, DT_F32, EPI_STORE);
-      gemm_phase(g, {cur_dx}, "proj_dw");
+      grad_prod[l].push_back(gemm_phase(g, {cur_dx}, "proj_dw"));
       g = gemm(h, (int)BT, (int)d, (int)F, DM(l), F, 1, lp, wc(lo.w_fc), d, 0, lp, DLN(2 * l + 1), d, DT_F32,
                EPI_STORE);
       p_mdx = gemm_phase(g, {p_pdx}, "fc_dx");
       g = gemm(h, (int)F, (int)d, (int)BT, DM(l), F, 0, lp, Hh(2 * l + 1), d, 0, lp, gf(lo.w_fc), d, DT_F32,
                EPI_STORE);
       p_mdw2 = gemm_phase(g, {p_pdx}, "fc_dw");
-      if (c.has_bias) colsum(DM(l), F, (int)F, CSF(l), gf(lo.b_fc), p_pdx, -1, "fc_bias_sum");
+      grad_prod[l].push_back(p_mdw2);
+      if (c.has_bias) grad_prod[l].push_back(colsum(DM(l), F, (int)F, CSF(l), gf(lo.b_fc), p_pdx, -1, "fc_bias_sum"));
     }
     (void)p_mdw2;
     int p_ln2b = ln_bwd(2 * l + 1, lo.ln2_g, ri, {p_mdx}, "ln2_bwd");
-    ln_red(2 * l + 1, p_ln2b, gf(lo.ln2_g), gf(lo.ln2_b), c.has_bias ? gf(lo.b_o) : nullptr, "ln2_params");
+    grad_prod[l].push_back(ln_red(2 * l + 1, p_ln2b, gf(lo.ln2_g), gf(lo.ln2_b), c.has_bias ? gf(lo.b_o) : nullptr,
+                                  "ln2_params"));
     void* dxm = DXLP(2 * l + 1);
     g = gemm(h, (int)BT, (int)d, (int)d, dxm, d, 1, lp, wc(lo.w_o), d, 0, lp, DOUT(l), d, lp, EPI_STORE);
     // With the matrix-core tile and 64-wide heads the attention backward's row
@@ -835,7 +906,7 @@ void build_train(ofa_handle* h) {
     }
     int p_odx = gemm_phase(g, {p_ln2b}, "attn_out_dx");
     g = gemm(h, (int)d, (int)d, (int)BT, dxm, d, 0, lp, O(l), d, 0, lp, gf(lo.w_o), d, DT_F32, EPI_STORE);
-    gemm_phase(g, {p_ln2b}, "attn_out_dw");
+    grad_prod[l].push_back(gemm_phase(g, {p_ln2b}, "attn_out_dw"));
     int p_prep = p_odx;
     if (!fused_prep) {
       p_prep = b.add(OP_ATTN_PREP, cdiv(BT, 16), "attn_prep", {p_odx});
@@ -859,12 +930,31 @@ void build_train(ofa_handle* h) {
     int p_qdx = gemm_phase(g, {p_dqkv, p_kv}, "qkv_dx");
     g = gemm(h, (int)(3 * d), (int)d, (int)BT, DQKV(l), 3 * d, 0, lp, Hh(2 * l), d, 0, lp, gf(lo.w_qkv), d, DT_F32,
              EPI_STORE);
-    gemm_phase(g, {p_dqkv, p_kv}, "qkv_dw");
-    if (c.has_bias) colsum(DQKV(l), 3 * d, (int)(3 * d), CSQ(l), gf(lo.b_qkv), p_dqkv, p_kv, "qkv_bias_sum");
+    grad_prod[l].push_back(gemm_phase(g, {p_dqkv, p_kv}, "qkv_dw"));
+    if (c.has_bias)
+      grad_prod[l].push_back(colsum(DQKV(l), 3 * d, (int)(3 * d), CSQ(l), gf(lo.b_qkv), p_dqkv, p_kv, "qkv_bias_sum"));
     int p_ln1b = ln_bwd(2 * l, lo.ln1_g, 2 * l + 1, {p_qdx}, "ln1_bwd");
     float* prev_bias = (c.has_bias && l > 0) ? gf(h->lay.layer[l - 1].b_proj) : nullptr;
-    ln_red(2 * l, p_ln1b, gf(lo.ln1_g), gf(lo.ln1_b), prev_bias, "ln1_params");
+    // ln1_params also writes the previous layer's MLP output bias gradient; it
+    // completes after every input-gradient product of this layer
+    ln1_red[l] = ln_red(2 * l, p_ln1b, gf(lo.ln1_g), gf(lo.ln1_b), prev_bias, "ln1_params");
     cur_dx = p_ln1b;
+    if (split_adam) {
+      if (l == (int)L - 1) {
+        // final LayerNorm and LM head (untied): their gradients and the head's input gradient
+        std::vector<int> deps = {p_head_dx, p_lnf_red};
+        if (!c.tied_head) deps.push_back(p_head_dw);
+        adam_early(h->lay.lnf_g, D.P, deps, "adamw_head");
+      }
+      if (l + 1 < (int)L) {
+        // layer l + 1: its producers, its own ln1_params (input gradients done) and
+        // the phase that wrote its MLP output bias gradient
+        std::vector<int> deps = grad_prod[l + 1];
+        deps.push_back(ln1_red[l + 1]);
+        deps.push_back(l + 2 < (int)L ? ln1_red[l + 2] : p_lnf_red);
+        adam_early(layer_lo(l + 1), layer_lo(l + 2), deps, "adamw_layer");
+      }
+    }
   }
   int v_rows = 64;
   int v_tiles = cdiv(V, v_rows);
@@ -886,34 +976,13 @@ void build_train(ofa_handle* h) {
     a.rows_per_tile = v_rows;
     a.v_tiles = v_tiles;
   }
-  const int adam_chunk = 16384;
-  // co-resident mode: before AdamW overwrites serve slot (tag & 1) the decoder
-  // must have left the version that slot holds; after it, the step is published
-  const bool coresident = w.n_slots > 1;
-  if (coresident) {
-    int p_guard = b.add(OP_SLOT_GUARD, 1, "slot_guard", {-2});
+  // the last range: every earlier phase (the embedding tables' gradients come
+  // last; co-resident, the slot guard is among the earlier phases)
+  if (coresident && p_guard < 0) {
+    p_guard = b.add(OP_SLOT_GUARD, 1, "slot_guard", {-2});
     b[p_guard].a.guard.st = at<DecState>(ws, w.dstate);
   }
-  int p_adam = b.add(OP_ADAMW, cdiv(D.P, adam_chunk), "adamw", {-2});
-  {
-    AdamArgs& a = b[p_adam].a.adam;
-    a.p = P;
-    a.g = G;
-    a.m = at<float>(ws, w.m);
-    a.v = at<float>(ws, w.v);
-    a.wc = c.precision == OFA_BF16 ? (void*)(ws + w.wc) : nullptr;
-    a.wc_dt = lp;
-    a.n = D.P;
-    a.per_tile = adam_chunk;
-    a.beta1 = c.beta1;
-    a.beta2 = c.beta2;
-    a.eps = c.eps;
-    a.wd = c.weight_decay;
-    if (coresident) {
-      a.pub = ws + w.serve;
-      a.pub_slot_bytes = D.P * D.lp;
-    }
-  }
+  int p_adam = adam_range(0, split_adam ? layer_lo(1) : D.P, {-2}, "adamw");
   if (coresident) {
     int p_pub = b.add(OP_PUBLISH, 1, "publish", {p_adam});
     b[p_pub].a.publish.published = at<uint64_t>(ws, w.published);

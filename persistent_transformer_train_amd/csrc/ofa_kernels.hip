@@ -216,7 +216,9 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
   __shared__ int s_ok;
   __shared__ int s_pre;
   __shared__ int s_stop;              // this workgroup saw the stop word of its open-ended job
-  __shared__ int64_t s_all_checked;   // instance whose every phase this workgroup saw complete
+  // instance s_all_inst: phases [0, s_all_upto) this workgroup saw complete
+  __shared__ int64_t s_all_inst;
+  __shared__ int32_t s_all_upto;
   // The phases' first tickets, and per phase the latest instance this
   // workgroup has seen complete (with an acquire at the time): a ticket whose
   // dependencies are all known complete neither polls the counters nor
@@ -233,7 +235,8 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
   const int tpi = ptb[J.n_phases];   // this partition's tickets per instance
   const uint64_t total = (uint64_t)J.n_inst * (uint64_t)tpi;
   if (threadIdx.x == 0) {
-    s_all_checked = -1;
+    s_all_inst = -1;
+    s_all_upto = 0;
     s_stop = 0;
     // the once-per-die release relies on partition == die; a workgroup elsewhere stops the run
     if (J.die_release && xcc_id() != (uint32_t)part) {
@@ -308,10 +311,12 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
       for (int d = 0; d < kMaxDeps && ok; ++d) {
         const int q = ph.dep[d];
         if (q == -2) {
-          if (s_all_checked != inst) {
-            for (int qq = 0; qq < pi && ok; ++qq) ok = need(qq, inst);
-            if (ok) s_all_checked = inst;
+          if (s_all_inst != inst) {
+            s_all_inst = inst;
+            s_all_upto = 0;
           }
+          for (int qq = s_all_upto; qq < pi && ok; ++qq) ok = need(qq, inst);
+          if (ok && s_all_upto < pi) s_all_upto = pi;
         } else if (q >= 0) {
           ok = need(q, inst);
         }
@@ -596,7 +601,8 @@ int persistent_occupancy(int occ) {
 
 hipError_t launch_phase(const Phase& h, const Phase* d_phases, int idx, const StepCtx* d_sc, DevStatus* st,
                         PhaseTime* tm, int64_t step, hipStream_t s) {
-  if (h.n_tiles <= 0) return hipSuccess;
+  // a join phase has no work: in stream order its dependencies already hold
+  if (h.n_tiles <= 0 || h.op == OP_NOP) return hipSuccess;
   (void)hipGetLastError();   // report this launch's error, not a stale one
   const int grid = h.op == OP_DEC_GEMV ? h.n_tickets : h.n_tiles;
   const size_t lds = lds_for(h);
