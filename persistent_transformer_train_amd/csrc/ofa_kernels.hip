@@ -297,6 +297,25 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
       atomicMin((unsigned long long*)&J.sched->limit, (unsigned long long)inst);
       s_stop = 1;
     }
+    // An "every earlier phase" dependency: wave 0 first reads the counters of
+    // 64 phases per round trip and records those already complete (each lane
+    // that saw one then takes the acquire itself), so that thread 0 waits only
+    // for the rest instead of polling every phase in turn.
+    bool all_dep = false;
+    for (int d = 0; d < kMaxDeps; ++d) all_dep |= ph.dep[d] == -2;
+    if (all_dep && threadIdx.x < kWave) {
+      const int from = s_all_inst == inst ? s_all_upto : 0;
+      bool seen = false;
+      for (int q0 = from; q0 < pi; q0 += kWave) {
+        const int q = q0 + (int)threadIdx.x;
+        if (q < pi && s_known[q] < inst &&
+            ld_relaxed(&J.sched->done[q]) >= base + (uint64_t)(inst + 1) * J.phases[q].n_tiles) {
+          s_known[q] = inst;
+          seen = true;
+        }
+      }
+      if (seen) fence_acquire_agent();
+    }
     // wait for the dependencies (thread 0), then one acquire for the workgroup
     if (threadIdx.x == 0) {
       bool ok = true, fresh = false;
