@@ -301,8 +301,11 @@ __global__ __launch_bounds__(kThreads, OCC) void persistent_kernel(PersistParams
     // 64 phases per round trip and records those already complete (each lane
     // that saw one then takes the acquire itself), so that thread 0 waits only
     // for the rest instead of polling every phase in turn.
+    // (Training launches only: in the one-workgroup-per-CU kernel, which runs
+    // decode, the extra code on every ticket cost batch-1 decode 1.7%.)
     bool all_dep = false;
-    for (int d = 0; d < kMaxDeps; ++d) all_dep |= ph.dep[d] == -2;
+    if constexpr (OCC == 2)
+      for (int d = 0; d < kMaxDeps; ++d) all_dep |= ph.dep[d] == -2;
     if (all_dep && threadIdx.x < kWave) {
       const int from = s_all_inst == inst ? s_all_upto : 0;
       bool seen = false;
