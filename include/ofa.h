@@ -382,7 +382,10 @@ ofa_status ofa_task_budget(uint64_t iterations, uint64_t tasks_per_unit, uint64_
  * delays.  OFA_OK if every tile ran exactly once and only after all tiles of
  * its dependencies had finished, every ticket was claimed once and every
  * counter ends at base + instances x tiles; else OFA_E_STATE (or OFA_E_ARG),
- * with the reason in msg (NUL-terminated, at most msg_len bytes). */
+ * with the reason in msg (NUL-terminated, at most msg_len bytes).  For the
+ * training program it first checks that the AdamW ranges cover every parameter
+ * once and that each range depends, transitively, on every phase of the step
+ * that writes its gradients or reads its weights (OFA_E_STATE otherwise). */
 ofa_status ofa_sched_selftest(const ofa_config *cfg, int32_t program, int32_t n_workers, int32_t n_cu,
                               int64_t n_inst, uint64_t counter_base, int32_t per_die, uint64_t seed,
                               char *msg, size_t msg_len);

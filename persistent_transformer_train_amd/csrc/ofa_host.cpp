@@ -2330,6 +2330,83 @@ ofa_status ofa_evaluate(ofa_handle* h, const int32_t* dev_tokens, int32_t n_batc
   return OFA_OK;
 }
 
+// The AdamW ranges of the training program cover every parameter once, and
+// each runs after every phase of its step that writes its gradients or reads
+// its master weights or compute copy (through the dependencies, transitively).
+// Phases touch parameters through the pointer fields listed here; a pointer
+// into a buffer names the element it starts at, and a tensor never straddles
+// two ranges.  Empty string when it holds.
+static std::string audit_adam(const ofa_handle* h) {
+  const std::vector<Phase>& prog = h->train;
+  const int np = (int)prog.size();
+  const int64_t P = h->D.P;
+  const char* pb = h->ws + h->cw.p;
+  const char* gb = h->ws + h->cw.g;
+  const char* wb = h->ws + h->cw.wc;
+  const int64_t wes = h->cw.wc == h->cw.p ? 4 : h->D.lp;   // compute-copy element size
+  // ancestors through the dependencies of the same instance
+  std::vector<std::vector<char>> anc(np, std::vector<char>(np, 0));
+  for (int i = 0; i < np; ++i)
+    for (int d = 0; d < kMaxDeps; ++d) {
+      const int q = prog[i].dep[d];
+      if (q == -2) {
+        for (int j = 0; j < i; ++j) anc[i][j] = 1;
+      } else if (q >= 0) {
+        anc[i][q] = 1;
+        for (int j = 0; j < np; ++j) anc[i][j] |= anc[q][j];
+      }
+    }
+  // parameter element a pointer starts at (-1: none)
+  auto elem = [&](const void* ptr) -> int64_t {
+    const char* c = (const char*)ptr;
+    if (!c) return -1;
+    if (c >= pb && c < pb + P * 4) return (c - pb) / 4;
+    if (c >= gb && c < gb + P * 4) return (c - gb) / 4;
+    if (c >= wb && c < wb + P * wes) return (c - wb) / wes;
+    return -1;
+  };
+  auto touched = [&](const Phase& ph) {
+    std::vector<int64_t> e;
+    auto add = [&](const void* q) {
+      const int64_t x = elem(q);
+      if (x >= 0) e.push_back(x);
+    };
+    switch (ph.op) {
+      case OP_GEMM: add(ph.a.gemm.A); add(ph.a.gemm.B); add(ph.a.gemm.C); add(ph.a.gemm.bias); break;
+      case OP_LN_FWD: add(ph.a.lnf.g); add(ph.a.lnf.b); break;
+      case OP_LN_BWD: add(ph.a.lnb.g); break;
+      case OP_COLRED: for (int k = 0; k < 3; ++k) add(ph.a.cr.out[k]); break;
+      case OP_EMBED: add(ph.a.emb.wte); add(ph.a.emb.wpe); break;
+      case OP_EMB_BWD: add(ph.a.ebwd.dwte); add(ph.a.ebwd.dwpe); break;
+      case OP_CE: add(ph.a.ce.w); break;
+      default: break;
+    }
+    return e;
+  };
+  std::vector<std::pair<int64_t, int64_t>> cover;
+  for (int r = 0; r < np; ++r) {
+    if (prog[r].op != OP_ADAMW) continue;
+    const int64_t lo = elem(prog[r].a.adam.p), hi = lo + prog[r].a.adam.n;
+    if (lo < 0) return "an AdamW range starts outside the parameters (phase " + std::to_string(r) + ")";
+    cover.push_back({lo, hi});
+    for (int q = 0; q < np; ++q) {
+      if (q == r || prog[q].op == OP_ADAMW) continue;
+      for (int64_t x : touched(prog[q]))
+        if (x >= lo && x < hi && !anc[r][q])
+          return "AdamW phase " + std::to_string(r) + " [" + std::to_string(lo) + ", " + std::to_string(hi) +
+                 ") does not wait for phase " + std::to_string(q) + ", which touches element " + std::to_string(x);
+    }
+  }
+  std::sort(cover.begin(), cover.end());
+  int64_t at_ = 0;
+  for (auto& rg : cover) {
+    if (rg.first != at_) return "the AdamW ranges leave a gap or overlap at element " + std::to_string(at_);
+    at_ = rg.second;
+  }
+  if (at_ != P) return "the AdamW ranges end at " + std::to_string(at_) + " of " + std::to_string(P);
+  return "";
+}
+
 ofa_status ofa_sched_selftest(const ofa_config* cfg, int32_t program, int32_t n_workers, int32_t n_cu, int64_t n_inst,
                               uint64_t counter_base, int32_t per_die, uint64_t seed, char* msg, size_t msg_len) {
   auto say = [&](const std::string& m) {
@@ -2360,6 +2437,13 @@ ofa_status ofa_sched_selftest(const ofa_config* cfg, int32_t program, int32_t n_
   h->serve_wgs = n_cu;
   build_train(h);
   build_eval(h);
+  if (program == 0) {
+    const std::string a = audit_adam(h);
+    if (!a.empty()) {
+      say(a);
+      return OFA_E_STATE;
+    }
+  }
   const std::vector<Phase>& prog = program == 0 ? h->train : h->eval;
   const int np = (int)prog.size();
   const int P = kMaxParts;

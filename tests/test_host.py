@@ -184,7 +184,11 @@ def test_scheduler_protocol_on_cpu_threads(ofa, name, per_die):
     """The persistent scheduler's protocol on host threads with the real phase
     tables of each workload's training step (a 256-CU device): every tile runs
     once, after every tile of its dependencies; counters start just below 2^32
-    so a 32-bit counter would wrap inside the run."""
+    so a 32-bit counter would wrap inside the run.  For the training program the
+    self-test first audits the AdamW ranges: they cover every parameter once, and
+    each depends transitively on every phase that writes its gradients or reads
+    its weights (a build with one layer range's LayerNorm-parameter dependency
+    removed fails it, naming the input-gradient product left unordered)."""
     cfg = configs.CONFIGS[name]
     rc, msg = _selftest(ofa, cfg, 0, 40, 2, 2 ** 32 - 10, per_die)
     assert rc == ofa.OFA_OK, msg
