@@ -124,6 +124,18 @@ __device__ __forceinline__ void epi_tile(const GemmArgs& g, const float* cst, in
 // RTX 3090", "Where a step's time goes": the output product, cross-entropy and
 // its backward).  The 32 threads of a 32-lane half hold one row (four columns
 // each) and reduce with shuffles inside that half, in a fixed order.
+// The value of the lane whose index differs from this one in bit log2(O) of
+// its 32-lane group (what __shfl_xor(v, O) returns there): O = 16, 8, 4 by a
+// swizzle (no address operand), O = 2, 1 by a DPP quad permutation (no LDS).
+template <int O>
+__device__ __forceinline__ float xor_peer32(float v) {
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16, "a lane bit of the 32-lane group");
+  if constexpr (O >= 4)
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (O << 10)));
+  else
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), O == 1 ? 0xb1 : 0x4e, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ void epi_ce_tile(const GemmArgs& g, const float* cst, int rows, int row0, int n0) {
   const int c = (threadIdx.x & 31) * 4, col = n0 + c;
   const bool valid = col < g.N;   // N % 8 == 0: a group of four columns is wholly in or out
@@ -131,22 +143,58 @@ __device__ __forceinline__ void epi_ce_tile(const GemmArgs& g, const float* cst,
   uint16_t* Ch = (uint16_t*)g.C;
   const int tn = n0 / kMBN;
   constexpr float kLog2e = 1.44269504088896341f;
-  for (int r = threadIdx.x >> 5; r < rend; r += 8) {
-    const epi_f4 v = valid ? *(const epi_f4*)(cst + r * kEpiPitch + c) : epi_f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    float m = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+  // four rows per pass, so their shuffle chains overlap (each row's arithmetic
+  // and reduction order as for one row at a time); rows past the end repeat
+  // the last row and store nothing
+  constexpr int U = 4;
+  for (int rb = threadIdx.x >> 5; rb < rend; rb += 8 * U) {
+    epi_f4 v[U];
+    float m[U], sm[U];
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    const float ml2 = m * kLog2e;
-    const epi_f4 pz = epi_f4{__builtin_amdgcn_exp2f(fmaf(v.x, kLog2e, -ml2)), __builtin_amdgcn_exp2f(fmaf(v.y, kLog2e, -ml2)),
-                             __builtin_amdgcn_exp2f(fmaf(v.z, kLog2e, -ml2)), __builtin_amdgcn_exp2f(fmaf(v.w, kLog2e, -ml2))};
-    float sm = (pz.x + pz.y) + (pz.z + pz.w);
+    for (int u = 0; u < U; ++u) {
+      const int r = min(rb + 8 * u, rend - 1);
+      v[u] = valid ? *(const epi_f4*)(cst + r * kEpiPitch + c) : epi_f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      m[u] = fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w));
+    }
+    // butterfly over the 32 lanes of the row, partners in bit 4, 3, 2, 1, 0
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
-    const int64_t row = row0 + r;
-    if (valid) *(epi_u2*)(Ch + row * g.ldc + col) = pack_bf16x4(pz);
-    if ((threadIdx.x & 31) == 0) {
-      g.stats[2 * (row * g.stats_ld + tn)] = m;
-      g.stats[2 * (row * g.stats_ld + tn) + 1] = sm;
+    for (int u = 0; u < U; ++u) m[u] = fmaxf(m[u], xor_peer32<16>(m[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) m[u] = fmaxf(m[u], xor_peer32<8>(m[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) m[u] = fmaxf(m[u], xor_peer32<4>(m[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) m[u] = fmaxf(m[u], xor_peer32<2>(m[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) m[u] = fmaxf(m[u], xor_peer32<1>(m[u]));
+    epi_f4 pz[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float ml2 = m[u] * kLog2e;
+      pz[u] = epi_f4{__builtin_amdgcn_exp2f(fmaf(v[u].x, kLog2e, -ml2)), __builtin_amdgcn_exp2f(fmaf(v[u].y, kLog2e, -ml2)),
+                     __builtin_amdgcn_exp2f(fmaf(v[u].z, kLog2e, -ml2)), __builtin_amdgcn_exp2f(fmaf(v[u].w, kLog2e, -ml2))};
+      sm[u] = (pz[u].x + pz[u].y) + (pz[u].z + pz[u].w);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) sm[u] += xor_peer32<16>(sm[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) sm[u] += xor_peer32<8>(sm[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) sm[u] += xor_peer32<4>(sm[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) sm[u] += xor_peer32<2>(sm[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) sm[u] += xor_peer32<1>(sm[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = rb + 8 * u;
+      if (r >= rend) break;
+      const int64_t row = row0 + r;
+      if (valid) *(epi_u2*)(Ch + row * g.ldc + col) = pack_bf16x4(pz[u]);
+      if ((threadIdx.x & 31) == 0) {
+        g.stats[2 * (row * g.stats_ld + tn)] = m[u];
+        g.stats[2 * (row * g.stats_ld + tn) + 1] = sm[u];
+      }
     }
   }
 }
