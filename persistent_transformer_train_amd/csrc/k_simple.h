@@ -859,40 +859,60 @@ __device__ __forceinline__ void ce_row_fused(const CeArgs& a, int r, int y, floa
   constexpr float kLog2e = 1.44269504088896341f;
   float* cs = red + 16;   // [n_stats] per-tile scales
   const float* st = a.stats + (int64_t)r * a.n_stats * 2;
+  // target logit: the final-LN row against the head row of the target; its
+  // operands are requested first so that their round trip overlaps the
+  // statistics (d <= 1024: at most one 8-element chunk per thread)
+  const uint16_t* hr = (const uint16_t*)a.h + (int64_t)r * a.d;
+  const uint16_t* wr = (const uint16_t*)a.w + (int64_t)y * a.d;
+  const int j = threadIdx.x * 8;
+  uint4 hv = make_uint4(0u, 0u, 0u, 0u), wv = hv;
+  if (j < a.d) {
+    hv = *(const uint4*)(hr + j);
+    wv = *(const uint4*)(wr + j);
+  }
   float m = -INFINITY;
   for (int t = threadIdx.x; t < a.n_stats; t += kThreads) m = fmaxf(m, st[2 * t]);
   m = block_max(m, red);
   float s = 0.f;
   for (int t = threadIdx.x; t < a.n_stats; t += kThreads) s += st[2 * t + 1] * __builtin_amdgcn_exp2f((st[2 * t] - m) * kLog2e);
-  s = block_sum(s, red + kWaves);
-  const float lse = m + logf(s);
-  // target logit: the final-LN row against the head row of the target
-  const uint16_t* hr = (const uint16_t*)a.h + (int64_t)r * a.d;
-  const uint16_t* wr = (const uint16_t*)a.w + (int64_t)y * a.d;
   float zy = 0.f;
-  for (int j = threadIdx.x * 8; j < a.d; j += kThreads * 8) {
-    const uint4 hv = *(const uint4*)(hr + j), wv = *(const uint4*)(wr + j);
+  if (j < a.d)
     zy += bf2f(hv.x & 0xffff) * bf2f(wv.x & 0xffff) + bf2f(hv.x >> 16) * bf2f(wv.x >> 16) +
           bf2f(hv.y & 0xffff) * bf2f(wv.y & 0xffff) + bf2f(hv.y >> 16) * bf2f(wv.y >> 16) +
           bf2f(hv.z & 0xffff) * bf2f(wv.z & 0xffff) + bf2f(hv.z >> 16) * bf2f(wv.z >> 16) +
           bf2f(hv.w & 0xffff) * bf2f(wv.w & 0xffff) + bf2f(hv.w >> 16) * bf2f(wv.w >> 16);
-  }
-  zy = block_sum(zy, red + 2 * kWaves);
-  if (threadIdx.x == 0) a.loss_rows[r] = lse - zy;
+  const float2 sz = block_sum2(s, zy, red + kWaves);
+  const float lse = m + logf(sz.x);
+  if (threadIdx.x == 0) a.loss_rows[r] = lse - sz.y;
   for (int t = threadIdx.x; t < a.n_stats; t += kThreads)
     cs[t] = __builtin_amdgcn_exp2f((st[2 * t] - lse) * kLog2e) * a.inv_rows;
   __syncthreads();
-  // every 8-column chunk lies in one 128-column tile (V % 8 == 0)
+  // every 8-column chunk lies in one 128-column tile (V % 8 == 0); eight
+  // chunks per thread are requested before any is rewritten, so that enough
+  // reads are in flight to cover the memory latency
   typedef __attribute__((address_space(1))) ce_u4 ce_gu4;
   ce_gu4* zp = (ce_gu4*)((uint16_t*)a.dz + (int64_t)r * a.V);
-  for (int i = threadIdx.x; i < a.V / 8; i += kThreads) {
-    const ce_u4 u = __builtin_nontemporal_load(zp + i);
-    const float c = cs[(8 * i) >> 7];
-    float p[8] = {bf2f(u.x & 0xffff), bf2f(u.x >> 16), bf2f(u.y & 0xffff), bf2f(u.y >> 16),
-                  bf2f(u.z & 0xffff), bf2f(u.z >> 16), bf2f(u.w & 0xffff), bf2f(u.w >> 16)};
+  const int n8 = a.V / 8;
+  constexpr int U = 8;
+  for (int i0 = threadIdx.x; i0 < n8; i0 += U * kThreads) {
+    ce_u4 u[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = p[e] * c - (8 * i + e == y ? a.inv_rows : 0.f);
-    __builtin_nontemporal_store(ce_u4{f2bf2(p[0], p[1]), f2bf2(p[2], p[3]), f2bf2(p[4], p[5]), f2bf2(p[6], p[7])}, zp + i);
+    for (int k = 0; k < U; ++k) {
+      const int i = i0 + k * kThreads;
+      u[k] = i < n8 ? __builtin_nontemporal_load(zp + i) : ce_u4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int i = i0 + k * kThreads;
+      if (i >= n8) break;
+      const float c = cs[(8 * i) >> 7];
+      float p[8] = {bf2f(u[k].x & 0xffff), bf2f(u[k].x >> 16), bf2f(u[k].y & 0xffff), bf2f(u[k].y >> 16),
+                    bf2f(u[k].z & 0xffff), bf2f(u[k].z >> 16), bf2f(u[k].w & 0xffff), bf2f(u[k].w >> 16)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = p[e] * c - (8 * i + e == y ? a.inv_rows : 0.f);
+      __builtin_nontemporal_store(ce_u4{f2bf2(p[0], p[1]), f2bf2(p[2], p[3]), f2bf2(p[4], p[5]), f2bf2(p[6], p[7])},
+                                  zp + i);
+    }
   }
 }
 

@@ -120,6 +120,27 @@ __device__ __forceinline__ float2 block_sum2_dpp(float a, float b, float* red) {
   return r;
 }
 
+// workgroup sums of two values with one barrier pair, each in block_sum's
+// order (so each equals block_sum of it); red must hold 2 kWaves floats
+__device__ __forceinline__ float2 block_sum2(float a, float b, float* red) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) {
+    red[w] = a;
+    red[kWaves + w] = b;
+  }
+  __syncthreads();
+  float2 r = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    r.x += red[i];
+    r.y += red[kWaves + i];
+  }
+  return r;
+}
+
 // workgroup sum, fixed order (deterministic); red must hold kWaves floats
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
