@@ -272,6 +272,23 @@ def test_bad_token_reports_arg_error():
     h.close()
 
 
+def test_full_size_persistent_bitwise_deterministic():
+    """c3 in the launch configuration bench.py times (persistent executor, two
+    workgroups per CU, once-per-die release), six steps in one launch, twice
+    from the same weights and tokens: losses and all weights bit-identical.
+    Several steps per launch put each step's start right behind the previous
+    step's final AdamW range, where an ordering or visibility gap between steps
+    would show."""
+    runs = []
+    for k in range(2):
+        log(f"c3 persistent 6 steps, run {k}")
+        h, *_, gl = gpu_run("c3", 6, PERSISTENT)
+        runs.append((gl, h.get_params().cpu().numpy()))
+        h.close()
+    assert runs[0][0].tobytes() == runs[1][0].tobytes(), (runs[0][0], runs[1][0])
+    assert runs[0][1].tobytes() == runs[1][1].tobytes()
+
+
 @pytest.mark.parametrize("name", ["c2", "c3"])
 def test_full_size_first_step(name):
     """Full-size workloads in the launch configuration bench.py times (persistent
