@@ -309,10 +309,8 @@ struct ofa_handle {
   DevProg dp_train, dp_dec, dp_eval;
   Phase* d_train = nullptr;
   Phase* d_dec = nullptr;
-  // per-partition ticket tables (see PersistJob::part_tb): the training
-  // program split into kMaxParts partitions, and both programs unsplit
-  uint8_t lineage[32] = {};
-  uint64_t* h_bell = nullptr;      // coherent pinned host words: doorbell at [0], progress at [8]         // SHA-256 of the checkpoint this state last came from or went to
+  uint8_t lineage[32] = {};        // SHA-256 of the checkpoint this state last came from or went to
+  uint64_t* h_bell = nullptr;      // coherent pinned host words: doorbell at [0], progress at [8]
   std::vector<char> phase_names;   // for phase_times
   std::vector<std::string> train_names;
   std::vector<std::string> dec_names;
