@@ -59,7 +59,9 @@ __device__ __forceinline__ void st_row4(void* y, int64_t e, int dt, float4 v) {
   }
 }
 
-constexpr int kLnQ = 4;   // LayerNorm forward: rows per wave in flight
+// kLnQ rows per wave in flight (a 16-row tile is one pass); COMB: the residual
+// combine, whose extra operands leave room for two
+template <int kLnQ, bool COMB>
 __device__ void task_ln_fwd(const LnFwdArgs& a, int tile) {
   const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
   const int r0 = tile * a.rows_per_tile;
@@ -68,14 +70,16 @@ __device__ void task_ln_fwd(const LnFwdArgs& a, int tile) {
   const float4* __restrict__ x4 = (const float4*)a.x;
   const float4* __restrict__ g4 = (const float4*)a.g;
   const float4* __restrict__ b4 = (const float4*)a.b;
-  float4 gv[kMaxD4], bv[kMaxD4];
+  const float4* __restrict__ k4 = (const float4*)a.kp;
+  const int64_t khalf = (int64_t)a.rows * n4;
+  float4 gv[kMaxD4], bv[kMaxD4], kbv[kMaxD4];
 #pragma unroll
   for (int c = 0; c < kMaxD4; ++c) {
     const int j = l + c * kWave;
     gv[c] = j < n4 ? g4[j] : f4_zero();
     bv[c] = j < n4 ? b4[j] : f4_zero();
+    if constexpr (COMB) kbv[c] = (j < n4 && a.kb) ? ((const float4*)a.kb)[j] : f4_zero();
   }
-  // kLnQ rows per wave in flight: a 16-row tile is one pass
   for (int r = r0 + w; r < r1; r += kLnQ * kWaves) {
     float4 v[kLnQ][kMaxD4];
     float mean[kLnQ], rstd[kLnQ];
@@ -85,7 +89,18 @@ __device__ void task_ln_fwd(const LnFwdArgs& a, int tile) {
 #pragma unroll
       for (int c = 0; c < kMaxD4; ++c) {
         const int j = l + c * kWave;
-        v[q][c] = (rr < r1 && j < n4) ? x4[(int64_t)rr * n4 + j] : f4_zero();
+        const int64_t e = (int64_t)rr * n4 + j;
+        v[q][c] = (rr < r1 && j < n4) ? x4[e] : f4_zero();
+        if constexpr (COMB) {
+          if (rr < r1 && j < n4) {
+            const float4 p0 = k4[e], p1 = k4[khalf + e];
+            // residual + (sum + bias), in the order of the product's own epilogue
+            float4 t = make_float4(p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w);
+            t = make_float4(t.x + kbv[c].x, t.y + kbv[c].y, t.z + kbv[c].z, t.w + kbv[c].w);
+            v[q][c] = make_float4(v[q][c].x + t.x, v[q][c].y + t.y, v[q][c].z + t.z, v[q][c].w + t.w);
+            ((float4*)a.x_out)[e] = v[q][c];
+          }
+        }
       }
     }
 #pragma unroll

@@ -177,7 +177,7 @@ struct DevProg {
 struct Carve {
   // offsets (bytes) into the workspace
   size_t p, g, m, v, wc, serve, xres, ln_mean, ln_rstd, h, qkv, o, lse, mlp1, mlp2, logits, dz, loss_rows, ce_stats;
-  size_t dxres, dxlp, dln, dmlp, dout, dsum, dqkv, ln_part, cs_fc, cs_qkv, esorted, efirst;
+  size_t dxres, dxlp, dln, dmlp, dout, dsum, dqkv, ln_part, cs_fc, cs_qkv, esorted, efirst, kpart;
   size_t sched, status, times, inst_end, steps, published, trace, tables, bell_ticks;
   size_t kv, ctx_tok, dstate, dx, dq, dapart, dmlp_v, dlogits, dsteps, dtimes, misc, dsched, dpart_v, dpart_i, dprompt;
   size_t total;
@@ -255,6 +255,7 @@ Carve carve(const ofa_config& c, const Layout& lay) {
   w.cs_fc = b.take(D.L * w.cs_tiles * D.F * f4);
   w.cs_qkv = b.take(D.L * w.cs_tiles * 3 * D.d * f4);
   w.esorted = b.take(D.BT * 4);
+  w.kpart = b.take(2 * D.BT * D.d * f4);   // two k-half partial sums of a residual product
   w.efirst = b.take(D.V * 8);
   w.sched = b.take(sizeof(Sched));
   w.status = b.take(sizeof(DevStatus));
@@ -557,6 +558,41 @@ void build_train(ofa_handle* h) {
     b[p].a.gemm = g;
     return p;
   };
+  // A residual product with fewer tiles than half the workgroups and a long k
+  // (the MLP's second product) runs as two phases over the two k halves, each
+  // writing fp32 partial sums; the LayerNorm that reads its output adds them to
+  // the residual (and the bias) as the product's epilogue would, and writes the
+  // sum.  Twice the tiles, each half as long.  Matrix-core bf16 path only, with
+  // 16-byte aligned halves.
+  float* KP = at<float>(ws, w.kpart);
+  struct Pending { const float* resid; const float* bias; int p0, p1; } pend_comb{nullptr, nullptr, -1, -1};
+  auto split_resid = [&](const GemmArgs& g, std::initializer_list<int> deps, const char* nm) -> bool {
+    const int hk = g.K / 2;
+    if (g.impl != GEMM_P3 || g.a_dt != DT_BF16 || g.b_dt != DT_BF16 || g.a_kmajor != 1 || g.b_kmajor != 1 ||
+        g.K % 16 || hk < 256 || g.epi != EPI_RESID ||
+        2 * g.tiles_m * g.tiles_n > h->n_cu * h->train_occ)
+      return false;
+    GemmArgs g0 = gemm(h, g.M, g.N, hk, g.A, g.lda, 1, DT_BF16, g.B, g.ldb, 1, DT_BF16, KP, g.N, DT_F32, EPI_STORE);
+    GemmArgs g1 = gemm(h, g.M, g.N, hk, (const char*)g.A + 2 * (int64_t)hk, g.lda, 1, DT_BF16,
+                       (const char*)g.B + 2 * (int64_t)hk, g.ldb, 1, DT_BF16, KP + (int64_t)g.M * g.N, g.N, DT_F32,
+                       EPI_STORE);
+    const int p0 = gemm_phase(g0, deps, nm);
+    const int p1 = gemm_phase(g1, deps, "k_half");
+    pend_comb = {g.resid, g.bias, p0, p1};
+    return true;
+  };
+  // the LayerNorm at residual point i takes a pending split product's sum
+  auto take_comb = [&](int p, int i) {
+    if (pend_comb.p0 < 0) return;
+    LnFwdArgs& a = b[p].a.lnf;
+    a.x = pend_comb.resid;
+    a.kp = KP;
+    a.kb = pend_comb.bias;
+    a.x_out = X(i);
+    b[p].dep[0] = pend_comb.p0;
+    b[p].dep[1] = pend_comb.p1;
+    pend_comb = {nullptr, nullptr, -1, -1};
+  };
   auto attn_args = [&](int l) {
     AttnArgs a;
     memset(&a, 0, sizeof a);
@@ -619,6 +655,10 @@ void build_train(ofa_handle* h) {
     const LayerOff& lo = h->lay.layer[l];
     int p_ln1 = ln_fwd(2 * l, last_x, "ln1");
     set_ln_params(p_ln1, lo.ln1_g, lo.ln1_b);
+    if (pend_comb.p0 >= 0) {
+      take_comb(p_ln1, 2 * l);
+      last_x = p_ln1;   // the residual X(2l) is now written here
+    }
     GemmArgs g = gemm(h, (int)BT, (int)(3 * d), (int)d, Hh(2 * l), d, 1, lp, wc(lo.w_qkv), d, 1, lp, QKV(l), 3 * d, lp,
                       EPI_STORE);
     g.bias = pf(lo.b_qkv);
@@ -656,7 +696,7 @@ void build_train(ofa_handle* h) {
                EPI_RESID);
       g.resid = X(2 * l + 1);
       g.ldres = d;
-      p_down = gemm_phase(g, {p_gg, p_o}, "down");
+      p_down = split_resid(g, {p_gg, p_o}, "down") ? -1 : gemm_phase(g, {p_gg, p_o}, "down");
     } else {
       g = gemm(h, (int)BT, (int)F, (int)d, Hh(2 * l + 1), d, 1, lp, wc(lo.w_fc), d, 1, lp, M1(l), F, lp, EPI_GELU);
       g.bias = pf(lo.b_fc);
@@ -669,12 +709,13 @@ void build_train(ofa_handle* h) {
       g.bias = pf(lo.b_proj);
       g.resid = X(2 * l + 1);
       g.ldres = d;
-      p_down = gemm_phase(g, {p_fc, p_o}, "proj");
+      p_down = split_resid(g, {p_fc, p_o}, "proj") ? -1 : gemm_phase(g, {p_fc, p_o}, "proj");
     }
     last_x = p_down;
   }
   int p_lnf = ln_fwd(2 * (int)L, last_x, "lnf");
   set_ln_params(p_lnf, h->lay.lnf_g, h->lay.lnf_b);
+  take_comb(p_lnf, 2 * (int)L);
   const int64_t w_lm = c.tied_head ? h->lay.wte : h->lay.w_lm;
   GemmArgs g = gemm(h, (int)BT, (int)V, (int)d, Hh(2 * L), d, 1, lp, wc(w_lm), d, 1, lp, at<float>(ws, w.logits), V,
                     DT_F32, EPI_STORE);
@@ -2371,7 +2412,7 @@ static std::string audit_adam(const ofa_handle* h) {
     };
     switch (ph.op) {
       case OP_GEMM: add(ph.a.gemm.A); add(ph.a.gemm.B); add(ph.a.gemm.C); add(ph.a.gemm.bias); break;
-      case OP_LN_FWD: add(ph.a.lnf.g); add(ph.a.lnf.b); break;
+      case OP_LN_FWD: add(ph.a.lnf.g); add(ph.a.lnf.b); add(ph.a.lnf.kb); break;
       case OP_LN_BWD: add(ph.a.lnb.g); break;
       case OP_COLRED: for (int k = 0; k < 3; ++k) add(ph.a.cr.out[k]); break;
       case OP_EMBED: add(ph.a.emb.wte); add(ph.a.emb.wpe); break;

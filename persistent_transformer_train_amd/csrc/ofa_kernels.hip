@@ -46,7 +46,11 @@ __device__ __noinline__ void task_dec_attn_call(const DecAttnArgs* ap, int tile,
 template <int OP, int OCC = 1>
 __device__ __forceinline__ void run_task(const Phase& ph, int tile, const TaskCtx& tc, char* smem) {
   if constexpr (OP == OP_EMBED) { OFA_ARGS(emb); task_embed(a, tile, tc); }
-  else if constexpr (OP == OP_LN_FWD) { OFA_ARGS(lnf); task_ln_fwd(a, tile); }
+  else if constexpr (OP == OP_LN_FWD) {
+    OFA_ARGS(lnf);
+    if (a.kp) task_ln_fwd<2, true>(a, tile);
+    else task_ln_fwd<4, false>(a, tile);
+  }
   else if constexpr (OP == OP_GEMM) {
     OFA_ARGS(gemm);
     if (a.impl == GEMM_P3) task_gemm_p3<OCC>(a, tile, smem);

@@ -94,6 +94,10 @@ struct GemmArgs {
 struct LnFwdArgs {
   const float* x; const float* g; const float* b;
   void* y; float* mean; float* rstd;
+  // residual combine (kp non-null): the LN input is x + ((kp[e] + kp[rows d + e])
+  // + kb[col]), a product's two k-half partial sums added to the residual as
+  // its epilogue would (kb nullable), and is also written to x_out
+  const float* kp; const float* kb; float* x_out;
   int32_t rows, d, y_dt, rows_per_tile;
 };
 
