@@ -1393,9 +1393,12 @@ PersistJob make_job(ofa_handle* h, const std::vector<Phase>& prog, const Phase* 
   j.tickets_per_inst = prog.back().ticket_base + prog.back().n_tickets;
   // tickets are claimed per die (eight partitions: 32 workgroups per counter
   // instead of 256 for training); an open-ended job (co-resident decode, whose
-  // stopping rule needs one counter) or a grid under eight keeps one
+  // stopping rule needs one counter) or a grid under eight keeps one, and so
+  // does decode, with a release per ticket: its phases have few tickets each
+  // and follow one another, and the workgroup finishing a phase then makes one
+  // counter round trip instead of two (its die's share, then the phase)
   const DevProg& dp = &prog == &h->train ? h->dp_train : &prog == &h->eval ? h->dp_eval : h->dp_dec;
-  if (n_wg >= kMaxParts && !open_ended) {
+  if (n_wg >= kMaxParts && !open_ended && &prog != &h->dec) {
     j.n_parts = kMaxParts;
     j.part_tb = dp.pt8;
     // the hardware hands workgroup b to die b % 8, so partition s is die s
