@@ -171,9 +171,9 @@ def test_checkpoint_header_and_size(ofa):
     assert ofa.ofa_checkpoint_bytes(C.byref(cfg)) == 256 + 12 * P
 
 
-def _selftest(ofa, cfg, program, workers, n_inst, base, per_die, seed=3):
+def _selftest(ofa, cfg, program, workers, n_inst, base, per_die, seed=3, n_cu=256):
     msg = C.create_string_buffer(256)
-    rc = ofa.ofa_sched_selftest(C.byref(ofa.make_config(cfg)), program, workers, 256, n_inst, base, per_die, seed,
+    rc = ofa.ofa_sched_selftest(C.byref(ofa.make_config(cfg)), program, workers, n_cu, n_inst, base, per_die, seed,
                                 msg, 256)
     return rc, msg.value.decode()
 
@@ -194,6 +194,21 @@ def test_scheduler_protocol_on_cpu_threads(ofa, name, per_die):
     assert rc == ofa.OFA_OK, msg
     rc, msg = _selftest(ofa, cfg, 1, 24, 2, 2 ** 32 - 3, per_die)   # the evaluation program
     assert rc == ofa.OFA_OK, msg
+
+
+@pytest.mark.parametrize("per_die", [1, 0], ids=["per_die_release", "per_ticket_release"])
+def test_scheduler_protocol_with_split_products(ofa, per_die):
+    """c3 with 512 workgroup slots, as two workgroups per CU on 256 CUs: the
+    program then runs the MLP's second product as two k-half phases whose
+    partial sums the next LayerNorm adds (one more phase per layer than with 256
+    slots).  Protocol and AdamW audit as above, on that program."""
+    cfg = configs.CONFIGS["c3"]
+    rc, msg = _selftest(ofa, cfg, 0, 40, 2, 2 ** 32 - 10, per_die, n_cu=512)
+    assert rc == ofa.OFA_OK, msg
+    rc0, msg0 = _selftest(ofa, cfg, 0, 40, 1, 0, per_die)
+    assert rc0 == ofa.OFA_OK, msg0
+    n_split, n_plain = (int(m.split()[1]) for m in (msg, msg0))
+    assert n_split == n_plain + cfg["n_layer"], (msg, msg0)
 
 
 def test_scheduler_selftest_catches_an_early_count(ofa):
