@@ -284,7 +284,7 @@ def main():
     ap.add_argument("--debug-flags", type=int, default=0, help="OFA_DEBUG_* bits for the training handle (experiments)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(collectives and sharding are design-only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
