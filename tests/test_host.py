@@ -198,14 +198,14 @@ def test_scheduler_protocol_on_cpu_threads(ofa, name, per_die):
 
 @pytest.mark.parametrize("per_die", [1, 0], ids=["per_die_release", "per_ticket_release"])
 def test_scheduler_protocol_with_split_products(ofa, per_die):
-    """c3 with 512 workgroup slots, as two workgroups per CU on 256 CUs: the
-    program then runs the MLP's second product as two k-half phases whose
-    partial sums the next LayerNorm adds (one more phase per layer than with 256
-    slots).  Protocol and AdamW audit as above, on that program."""
+    """c3 on 256 CUs runs the MLP's second product (192 tiles) as two k-half
+    phases whose partial sums the next LayerNorm adds; on a 128-CU device it
+    stays one phase (one phase per layer fewer).  Protocol and AdamW audit as
+    above, on both programs."""
     cfg = configs.CONFIGS["c3"]
-    rc, msg = _selftest(ofa, cfg, 0, 40, 2, 2 ** 32 - 10, per_die, n_cu=512)
+    rc, msg = _selftest(ofa, cfg, 0, 40, 2, 2 ** 32 - 10, per_die, n_cu=256)
     assert rc == ofa.OFA_OK, msg
-    rc0, msg0 = _selftest(ofa, cfg, 0, 40, 1, 0, per_die)
+    rc0, msg0 = _selftest(ofa, cfg, 0, 40, 2, 2 ** 32 - 10, per_die, n_cu=128)
     assert rc0 == ofa.OFA_OK, msg0
     n_split, n_plain = (int(m.split()[1]) for m in (msg, msg0))
     assert n_split == n_plain + cfg["n_layer"], (msg, msg0)
